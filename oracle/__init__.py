@@ -1,0 +1,165 @@
+"""fp64 CPU oracle -- TEST INFRASTRUCTURE ONLY.
+
+The plain, slow, definition-level reference the GPU library is checked against
+(``vjsd_oracle.c``, built with gcc into ``liboracle.so``), plus a pure-Python
+brute force for tiny inputs (``oracle.brute``).  Only the tests, the smoke check
+and the benchmark's CPU-baseline leg may import this package; the product path
+never does, and this package imports nothing from the product.
+
+Page keys: [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel
+generalized JSD with Triton kernels"; [OPS-PR] DeepSpeed PR #8791 "Add
+vocabulary-parallel logprobs, entropy and KL ops".
+
+Every function takes CPU torch tensors holding the exact stored input values
+(float32, float16 or bfloat16; 2-D ``[N, V]`` with unit column stride), evaluates
+the listed rows in fp64 and returns numpy float64 arrays packed by position in
+``rows``.  ``widths`` splits the vocabulary into consecutive shards (default: one).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vjsd_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point the loader at another build of the same source (a planted-mistake
+# variant) to show that the pins catch it.
+_LIB_OVERRIDE = os.environ.get("VJSD_ORACLE_LIB")
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the C oracle with gcc (fp64, IEEE semantics, OpenMP over rows)."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-std=gnu11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                    "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            lib = ctypes.CDLL(_LIB)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        D = ctypes.c_double
+        lib.or_stats.argtypes = [P, I, I64, I64, P, I, P, I64, P, P]
+        lib.or_jsd.argtypes = [P, P, I, I64, I64, P, I, D, P, I64, P, P, P, P, P, P]
+        lib.or_entropy.argtypes = [P, I, I64, I64, P, I, P, I64, P, P, P]
+        lib.or_logprobs.argtypes = [P, I, I64, I64, P, I, P, I64, P, I, I64, P, P, P, P]
+        lib.or_num_threads.restype = I
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs with."""
+    return _load().or_num_threads()
+
+
+def _mat(x: torch.Tensor):
+    if x.device.type != "cpu":
+        raise ValueError("oracle inputs must be CPU tensors")
+    if x.dim() != 2 or (x.size(1) > 1 and x.stride(1) != 1):
+        raise ValueError("oracle inputs must be 2-D with unit column stride")
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    return x.data_ptr(), _DT[x.dtype], x.stride(0) if x.size(0) > 1 else x.size(1)
+
+
+def _common(x, widths, rows):
+    V = x.size(1)
+    w = np.asarray([V] if widths is None else list(widths), dtype=np.int64)
+    if w.sum() != V or (w < 0).any():
+        raise ValueError("shard widths must be >= 0 and sum to V")
+    r = np.arange(x.size(0), dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    if r.size and (r.min() < 0 or r.max() >= x.size(0)):
+        raise ValueError("row index out of range")
+    return V, np.ascontiguousarray(w), np.ascontiguousarray(r)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def stats(x, widths=None, rows=None):
+    """Per-row (max, ln sum exp(x - max)) through the cross-shard merge."""
+    ptr, dt, ld = _mat(x)
+    V, w, r = _common(x, widths, rows)
+    m = np.empty(r.size)
+    lz = np.empty(r.size)
+    _load().or_stats(ptr, dt, ld, V, _p(w), w.size, _p(r), r.size, _p(m), _p(lz))
+    return m, lz
+
+
+def jsd(s, t, beta, widths=None, rows=None, gout=None, grads=True):
+    """Generalized JSD per row; beta 0 / 1 are the forward / reverse KL branches.
+
+    Returns dict(loss, kt, ks, gs, gt) with kt = KL(p_t||M), ks = KL(p_s||M)
+    (M = p_s at beta 0, p_t at beta 1), gradients of ``gout[q] * loss[q]``.
+    """
+    if s.shape != t.shape or s.dtype != t.dtype:
+        raise ValueError("student and teacher must match in shape and dtype")
+    if _mat(s)[2] != _mat(t)[2]:  # the C side takes one row stride for both
+        s, t = s.contiguous(), t.contiguous()
+    ps_, dt, ld = _mat(s)
+    pt_ = _mat(t)[0]
+    V, w, r = _common(s, widths, rows)
+    g = None if gout is None else np.ascontiguousarray(gout, dtype=np.float64)
+    loss, kt, ks = np.empty(r.size), np.empty(r.size), np.empty(r.size)
+    gs = np.empty((r.size, V)) if grads else None
+    gt = np.empty((r.size, V)) if grads else None
+    _load().or_jsd(ps_, pt_, dt, ld, V, _p(w), w.size, float(beta), _p(r), r.size, _p(g),
+                   _p(loss), _p(kt), _p(ks), _p(gs), _p(gt))
+    return dict(loss=loss, kt=kt, ks=ks, gs=gs, gt=gt)
+
+
+def kl_div(s, t, reverse=False, **kw):
+    """KL(p_t||p_s), or KL(p_s||p_t) with reverse=True: the beta = 0 / 1 branches."""
+    return jsd(s, t, 1.0 if reverse else 0.0, **kw)
+
+
+def entropy(x, widths=None, rows=None, gout=None, grads=True):
+    ptr, dt, ld = _mat(x)
+    V, w, r = _common(x, widths, rows)
+    g = None if gout is None else np.ascontiguousarray(gout, dtype=np.float64)
+    H = np.empty(r.size)
+    gx = np.empty((r.size, V)) if grads else None
+    _load().or_entropy(ptr, dt, ld, V, _p(w), w.size, _p(r), r.size, _p(g), _p(H), _p(gx))
+    return dict(ent=H, gx=gx)
+
+
+def logprobs(x, ids, ignore_index=-100, widths=None, rows=None, gout=None, grads=True):
+    """Log-probabilities of ``ids[q, k]`` (global vocabulary ids) for each listed row.
+
+    ``ids`` has one row of K ids per listed row.  Raises ValueError on an id outside
+    [0, V) that is not ``ignore_index``.
+    """
+    ptr, dt, ld = _mat(x)
+    V, w, r = _common(x, widths, rows)
+    idv = np.ascontiguousarray(np.asarray(ids, dtype=np.int64).reshape(r.size, -1))
+    K = idv.shape[1]
+    g = None if gout is None else np.ascontiguousarray(
+        np.asarray(gout, np.float64).reshape(r.size, K))
+    out = np.empty((r.size, K))
+    gx = np.empty((r.size, V)) if grads else None
+    if grads and g is None:
+        g = np.ones((r.size, K))
+    err = ctypes.c_int(0)
+    _load().or_logprobs(ptr, dt, ld, V, _p(w), w.size, _p(r), r.size, _p(idv), K,
+                        int(ignore_index), _p(g), _p(out), _p(gx), ctypes.byref(err))
+    if err.value:
+        raise ValueError("logprobs: an id is outside [0, V) and is not ignore_index")
+    return dict(out=out, gx=gx)
