@@ -1,0 +1,226 @@
+/*
+ * vjsd.h -- C ABI of libvjsd: per-token softmax statistics, generalized
+ * Jensen-Shannon divergence, KL, entropy and log-probabilities over a vocabulary
+ * split into logical shards, for AMD Instinct MI355X (gfx950).
+ *
+ * Page keys used in the citations:
+ *   [JSD-PR] DeepSpeed PR #8958, "[VocabTP] Add vocabulary-parallel generalized JSD
+ *            with Triton kernels".
+ *   [OPS-PR] DeepSpeed PR #8791, "Add vocabulary-parallel logprobs, entropy and KL
+ *            ops", and its review thread.
+ *
+ * ---------------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ *
+ * Rows.  N tokens ("rows") are processed; each row holds V vocabulary logits split
+ * into S >= 1 consecutive shards.  Shard k covers the global vocabulary ids
+ * [vocab_start_k, vocab_start_k + width_k); shards are ordered and contiguous
+ * (vocab_start_{k+1} = vocab_start_k + width_k) and a width may be 0 (an empty
+ * shard joins the merge as (max, sum-exp) = (-inf, 0), [OPS-PR, review: empty
+ * shards]).  One GPU stands in for the tensor-parallel ranks of the pages: a
+ * shard's statistics are reduced locally and merged on the device where the pages
+ * all-reduce them [OPS-PR, How].
+ *
+ * Views.  A shard's student / teacher logits (and its gradients) are views with
+ * unit column stride.  Row r of a view is at element
+ *     rows_per_batch == 0:  r * row_stride
+ *     rows_per_batch  > 0:  (r / rows_per_batch) * batch_stride
+ *                           + (r % rows_per_batch) * row_stride
+ * relative to p, so the causal-shift slices [B, T-1, V] of a [B, T, V] tensor are
+ * taken without a copy [JSD-PR, Changes].  Strides count elements.  Student,
+ * teacher and both gradients share the same dtype and shard layout [JSD-PR, Scope
+ * and limitations].  Pointers are device pointers and must be aligned to their
+ * element size; 16-byte alignment of every row (same offset in all views of a
+ * shard) selects the vector path, any other alignment runs a slower scalar path.
+ *
+ * Dtypes.  Inputs are fp32, fp16 or bf16 (vjsd_dtype) and are widened to fp32 in
+ * registers; all arithmetic is fp32 with fp64 per-row bookkeeping.  Per-token
+ * outputs are fp32 [JSD-PR, Changes]; gradients are written in the input dtype,
+ * rounded to nearest even.
+ *
+ * Statistics.  `stats` is double[N][4] = (m_s, lnZ_s, m_t, lnZ_t): the row max of
+ * the student / teacher logits and ln sum_j exp(x_j - m), kept apart so that a large
+ * common offset costs no precision [OPS-PR, How].  One-input ops use (m_s, lnZ_s)
+ * and leave the teacher half unspecified.  An undefined row (all -inf) has
+ * m = -inf, lnZ = -inf.
+ *
+ * Workspace.  `part` is caller-owned device memory of vjsd_workspace_bytes(N, S)
+ * bytes holding per-shard partial results between the launches of one call (and
+ * between vjsd_stats and vjsd_merge).  Its contents are otherwise unspecified.
+ *
+ * Ownership and streams.  The caller owns every buffer.  The library allocates no
+ * memory, keeps no state between calls and is reentrant; every call only enqueues
+ * kernels on `stream` (a hipStream_t; NULL is the null stream) and returns without
+ * synchronising.  Buffers must stay valid until the enqueued work completes.
+ * Outputs must not alias inputs.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued; an
+ * invalid call returns a negative VJSD_ERR_* code and enqueues nothing.  N == 0 is
+ * valid and enqueues nothing [JSD-PR, Validation: empty token batches].  A launch
+ * failure returns VJSD_ERR_HIP.  A row that is -inf everywhere is not an error: its
+ * per-token value is NaN and every gradient in it is exactly 0, whatever the
+ * upstream gradient [OPS-PR, review: NaN gradients of fully masked rows].
+ * ---------------------------------------------------------------------------------
+ */
+#ifndef VJSD_H
+#define VJSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Entry points are the library's only exported symbols. */
+#if defined(__GNUC__) || defined(__clang__)
+#define VJSD_API __attribute__((visibility("default")))
+#else
+#define VJSD_API
+#endif
+
+typedef enum { VJSD_F32 = 0, VJSD_F16 = 1, VJSD_BF16 = 2 } vjsd_dtype;
+
+enum {
+    VJSD_OK = 0,
+    VJSD_ERR_ARG = -1,         /* null pointer, negative size, bad stride, misaligned pointer */
+    VJSD_ERR_DTYPE = -2,       /* dtype not one of vjsd_dtype */
+    VJSD_ERR_BETA = -3,        /* beta NaN or outside [0, 1] */
+    VJSD_ERR_LAYOUT = -4,      /* shards not ordered/contiguous, or vocabulary size mismatch */
+    VJSD_ERR_EMPTY_SHARD = -5, /* a shard of width 0 given to the log-probability op */
+    VJSD_ERR_HIP = -6          /* the HIP runtime refused a launch */
+};
+
+/* Read-only view of one shard of one input (see "Views"). */
+typedef struct {
+    const void *p;
+    int64_t row_stride;
+    int64_t rows_per_batch;
+    int64_t batch_stride;
+} vjsd_view;
+
+/* Writable view; p == NULL means "this output is not wanted". */
+typedef struct {
+    void *p;
+    int64_t row_stride;
+    int64_t rows_per_batch;
+    int64_t batch_stride;
+} vjsd_mview;
+
+/* One logical vocabulary shard. */
+typedef struct {
+    int64_t vocab_start; /* first global vocabulary id of the shard */
+    int64_t width;       /* number of vocabulary columns, >= 0 */
+    vjsd_view s;         /* student logits; the one input of entropy / logprobs */
+    vjsd_view t;         /* teacher logits; ignored by one-input ops */
+    vjsd_mview gs;       /* gradient w.r.t. s, written by the backward entry points */
+    vjsd_mview gt;       /* gradient w.r.t. t, written by the backward entry points */
+} vjsd_shard;
+
+/* Human-readable text of a VJSD_* code (static storage). */
+VJSD_API const char *vjsd_strerror(int code);
+
+/* Bytes of the `part` workspace for N rows and S shards. */
+VJSD_API size_t vjsd_workspace_bytes(int64_t N, int S);
+
+/*
+ * Per-shard paired softmax statistics [JSD-PR, Changes: fused paired softmax
+ * statistics; OPS-PR, How].  For every shard k and row r, and for the inputs
+ * selected by `which` (1 = student, 2 = teacher, 3 = both), computes the shard's
+ * max and sum of exponentials into `part`.  This is the first input pass.
+ */
+VJSD_API int vjsd_stats(const vjsd_shard *shards, int S, int64_t N, int dtype, int which,
+               float *part, void *stream);
+
+/*
+ * Cross-shard merge [OPS-PR, How: MAX then SUM of the [N] statistics]: the global
+ * max is the max of the shard maxima and each shard's sum-exp is rescaled to it;
+ * shards with max -inf add nothing [OPS-PR, review: empty shards].  Reads `part` as
+ * left by vjsd_stats with the same S, N, which; writes stats[N][4] (only the halves
+ * selected by `which`).
+ */
+VJSD_API int vjsd_merge(const float *part, int S, int64_t N, int which, double *stats, void *stream);
+
+/*
+ * Generalized JSD forward [JSD-PR, Motivation and Changes]: with
+ * M = beta p_t + (1 - beta) p_s, writes per token
+ *     kl[r]   = (KL(p_t || M), KL(p_s || M))   (float[N][2], saved for backward)
+ *     loss[r] = beta KL(p_t || M) + (1 - beta) KL(p_s || M)   for 0 < beta < 1,
+ *               KL(p_t || p_s)  (forward KL) for beta == 0,
+ *               KL(p_s || p_t)  (reverse KL) for beta == 1,
+ * the endpoints being exact branches, not limits [JSD-PR, Changes].  At beta == 0
+ * kl[r][1] is 0 and at beta == 1 kl[r][0] is 0.  KL is +inf when the target puts
+ * mass on a token the other side masked, decided on the logits [OPS-PR, Tests].
+ * `stats` must hold both halves (vjsd_stats/vjsd_merge with which = 3).  This is the
+ * second input pass; shard partials go through `part` and are summed in shard order.
+ */
+VJSD_API int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
+             double beta, float *part, float *kl, float *loss, void *stream);
+
+/*
+ * Generalized JSD backward, closed form and local [JSD-PR, Changes: recompute
+ * probabilities in registers; OPS-PR, How: no communication].  With g = grad_loss[r]:
+ *   interior: d/ds = g (1-beta) p_s (lp_s - lM - KS),  d/dt = g beta p_t (lp_t - lM - KT)
+ *   beta = 0: d/ds = g (p_s - p_t),                   d/dt = g p_t (lp_t - lp_s - KT)
+ *   beta = 1: d/ds = g p_s (lp_s - lp_t - KS),         d/dt = g (p_t - p_s)
+ * written into each shard's gs / gt views; a NULL gs.p (gt.p) skips that gradient
+ * (teacher or student detached) [JSD-PR, Changes].  A -inf logit's own term is 0.
+ * In a row whose KL is +inf the target-side gradient is not finite.  Reads the
+ * inputs, stats and kl of the forward.  This is the third input pass.
+ */
+VJSD_API int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
+             const float *kl, double beta, const float *grad_loss, void *stream);
+
+/*
+ * KL divergence [OPS-PR, What]: KL(p_t || p_s), or KL(p_s || p_t) when reverse != 0,
+ * with the forward computed in a single input pass by online accumulation (as the
+ * single-pass KL forward of [JSD-PR, Scope and limitations]).  Writes stats[N][4]
+ * (both halves), kl[N][2] in the layout of vjsd_fwd at beta = 0 (reverse = 0) or
+ * beta = 1 (reverse != 0), and loss[N].
+ */
+VJSD_API int vkl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse, float *part,
+            double *stats, float *kl, float *loss, void *stream);
+
+/* KL backward: vjsd_bwd at beta = 0 (reverse = 0) or beta = 1 (reverse != 0). */
+VJSD_API int vkl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse,
+            const double *stats, const float *kl, const float *grad_loss, void *stream);
+
+/*
+ * Entropy [OPS-PR, What]: ent[r] = -sum_j p_j lp_j over the student view, single
+ * input pass.  Writes stats (student half) and ent[N].
+ */
+VJSD_API int ventropy_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, float *part,
+                 double *stats, float *ent, void *stream);
+
+/* Entropy backward: d/dx_j = -g p_j (lp_j + H), into each shard's gs view. */
+VJSD_API int ventropy_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
+                 const float *ent, const float *grad, void *stream);
+
+/*
+ * Log-probabilities of K ids per row [OPS-PR, What]: out[r][k] = lp(ids[r][k]),
+ * ids being global vocabulary ids in [0, vocab_global); out is exactly 0 where
+ * ids[r][k] == ignore_index.  The shards must cover [0, vocab_global) and none may
+ * be empty (VJSD_ERR_EMPTY_SHARD) [OPS-PR, review: empty shards].  An id outside the
+ * range that is not ignore_index cannot be seen on the host: the kernels set
+ * *dev_err (device int32, caller-zeroed) to 1, and the caller must check it after
+ * synchronising and treat the call as failed [OPS-PR, review: the index range check
+ * runs every call].  Writes stats (student half) and out[N][K].
+ */
+VJSD_API int vlogprobs_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                  const int64_t *ids, int K, int64_t ignore_index, float *part, double *stats,
+                  float *out, int32_t *dev_err, void *stream);
+
+/*
+ * Log-probabilities backward: d/dx_j = sum_{k valid} g_k [j == ids_k]
+ *   - (sum_{k valid} g_k) p_j, with g = grad[N][K]; repeated ids accumulate.  Writes
+ * each shard's gs view.  Out-of-range ids are skipped (the forward reported them).
+ */
+VJSD_API int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                  const double *stats, const int64_t *ids, int K, int64_t ignore_index,
+                  const float *grad, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VJSD_H */

@@ -1,0 +1,165 @@
+"""The C ABI on the host (CPU only): the library loads, exports every entry point
+``include/vjsd.h`` declares, and rejects invalid arguments before anything is
+enqueued.  No call here reaches a GPU: every call either fails validation or has
+N == 0, which returns before any HIP call.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vjsd.h")
+
+abi = pytest.importorskip("vocab_sharded_softmax_amd._abi")
+lib = abi.lib
+Shard, View = abi.Shard, abi.View
+
+OK, ARG, DTYPE, BETA, LAYOUT, EMPTY = 0, -1, -2, -3, -4, -5
+FAKE = 0x10000  # a well-aligned address that is never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"VJSD_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_every_declared_entry_point_is_exported():
+    names = declared_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+    # and nothing else of the library's own code is exported
+    out = os.popen(f"nm -D --defined-only {abi.LIB_PATH}").read().split("\n")
+    own = {ln.split()[-1] for ln in out if ln.strip() and (" T " in ln)}
+    own = {n for n in own if n.startswith(("vjsd", "vkl", "ventropy", "vlogprobs"))}
+    assert own == set(names)
+
+
+def test_strerror_and_workspace():
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
+        assert isinstance(lib.vjsd_strerror(code), bytes)
+    assert lib.vjsd_workspace_bytes(0, 4) == 0
+    assert lib.vjsd_workspace_bytes(8192, 1) == 8192 * 8 * 4
+    assert lib.vjsd_workspace_bytes(4096, 4) == 4096 * 4 * 8 * 4
+
+
+def shards(widths, ptr=FAKE, rs=None, start=0, es=2, grads=False):
+    arr = (Shard * len(widths))()
+    c = start
+    V = sum(widths)
+    for k, w in enumerate(widths):
+        p = ptr + c * es if ptr else None
+        v = View(p, V if rs is None else rs, 0, 0)
+        g = View(p + (1 << 30) if (grads and p) else None, V if rs is None else rs, 0, 0)
+        arr[k] = Shard(c, w, v, v, g, g)
+        c += w
+    return arr
+
+
+def fwd(arr, S, N, dt=2, beta=0.5, stats=FAKE, part=FAKE, kl=FAKE, loss=FAKE):
+    return lib.vjsd_fwd(arr, S, N, dt, stats, beta, part, kl, loss, None)
+
+
+def test_empty_batch_is_valid_and_enqueues_nothing():
+    a = shards([5, 0, 7])
+    assert lib.vjsd_stats(a, 3, 0, 2, 3, None, None) == OK
+    assert lib.vjsd_merge(None, 3, 0, 3, None, None) == OK
+    assert fwd(a, 3, 0, stats=None, part=None, kl=None, loss=None) == OK
+    assert lib.vjsd_bwd(a, 3, 0, 2, None, None, 0.5, None, None) == OK
+    assert lib.vkl_fwd(a, 3, 0, 2, 0, None, None, None, None, None) == OK
+    assert lib.ventropy_fwd(a, 3, 0, 2, None, None, None, None) == OK
+    b = shards([5, 7])
+    assert lib.vlogprobs_fwd(b, 2, 0, 2, 12, None, 4, -100, None, None, None, None, None) == OK
+
+
+@pytest.mark.parametrize("beta", [-0.1, 1.0000001, math.nan, math.inf, -math.inf])
+def test_beta_outside_unit_interval_is_rejected(beta):
+    a = shards([10])
+    assert fwd(a, 1, 4, beta=beta) == BETA
+    assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, beta, FAKE, None) == BETA
+
+
+def test_dtype_and_sizes_are_checked():
+    a = shards([10])
+    assert fwd(a, 1, 4, dt=3) == DTYPE
+    assert fwd(a, 1, 4, dt=-1) == DTYPE
+    assert fwd(a, 1, -1) == ARG
+    assert fwd(a, 0, 4) == ARG
+    assert fwd(None, 1, 4) == ARG
+    assert fwd(a, 1, 1 << 31) == ARG
+    assert lib.vjsd_stats(a, 1, 4, 2, 0, FAKE, None) == ARG
+    assert lib.vjsd_stats(a, 1, 4, 2, 4, FAKE, None) == ARG
+    assert lib.vjsd_merge(FAKE, 1, 4, 5, FAKE, None) == ARG
+
+
+def test_null_buffers_are_rejected():
+    a = shards([10])
+    assert fwd(a, 1, 4, stats=None) == ARG
+    assert fwd(a, 1, 4, kl=None) == ARG
+    assert fwd(a, 1, 4, loss=None) == ARG
+    assert lib.vjsd_stats(a, 1, 4, 2, 3, None, None) == ARG
+    a2 = shards([5, 5])
+    assert fwd(a2, 2, 4, part=None) == ARG  # several shards need the workspace
+    assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, 0.5, None, None) == ARG
+    assert lib.vjsd_merge(None, 1, 4, 3, FAKE, None) == ARG
+
+
+def test_views_are_checked():
+    assert fwd(shards([10], ptr=None), 1, 4) == ARG  # null logits with width > 0
+    assert fwd(shards([10], ptr=FAKE + 1), 1, 4) == ARG  # not element-aligned
+    assert fwd(shards([10], rs=9), 1, 4) == ARG  # overlapping rows
+    assert fwd(shards([10], rs=-10), 1, 4) == ARG
+    a = shards([10])
+    a[0].s.rows_per_batch = 3
+    a[0].s.batch_stride = 25  # batches overlap: needs >= 2 * 10 + 10
+    assert fwd(a, 1, 6) == ARG
+    # an empty shard may carry a null pointer
+    b = shards([4, 0, 6])
+    b[1].s.p = None
+    b[1].t.p = None
+    assert fwd(b, 3, 0) == OK
+
+
+def test_shards_must_be_ordered_and_contiguous():
+    a = shards([4, 6])
+    a[1].vocab_start = 5
+    assert fwd(a, 2, 4) == LAYOUT
+    a[1].vocab_start = 3
+    assert fwd(a, 2, 4) == LAYOUT
+    a = shards([4, 6])
+    a[0].width = -1
+    assert fwd(a, 2, 4) == ARG
+
+
+def test_logprobs_rejects_empty_shards_and_bad_vocabulary():
+    a = shards([5, 0, 7])
+    assert lib.vlogprobs_fwd(a, 3, 4, 2, 12, FAKE, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == EMPTY
+    assert lib.vlogprobs_bwd(a, 3, 4, 2, 12, FAKE, FAKE, 3, -100, FAKE, None) == EMPTY
+    b = shards([5, 7])
+    assert lib.vlogprobs_fwd(b, 2, 4, 2, 13, FAKE, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == LAYOUT
+    c = shards([5, 7], start=1)
+    assert lib.vlogprobs_fwd(c, 2, 4, 2, 13, FAKE, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == LAYOUT
+    assert lib.vlogprobs_fwd(b, 2, 4, 2, 12, None, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == ARG
+    assert lib.vlogprobs_fwd(b, 2, 4, 2, 12, FAKE, -1, -100, FAKE, FAKE, FAKE, FAKE, None) == ARG
+    assert lib.vlogprobs_fwd(b, 2, 4, 2, 12, FAKE, 3, -100, FAKE, FAKE, FAKE, None, None) == ARG
+
+
+def test_entropy_and_kl_check_their_arguments():
+    a = shards([10])
+    assert lib.ventropy_fwd(a, 1, 4, 7, FAKE, FAKE, FAKE, None) == DTYPE
+    assert lib.ventropy_fwd(a, 1, 4, 2, None, FAKE, FAKE, None) == ARG
+    assert lib.ventropy_bwd(a, 1, 4, 2, FAKE, FAKE, None, None) == ARG
+    assert lib.vkl_fwd(a, 1, 4, 2, 1, FAKE, FAKE, None, FAKE, None) == ARG
+    assert lib.vkl_bwd(a, 1, 4, 2, 1, FAKE, FAKE, None, None) == ARG
+
+
+def test_default_split_matches_the_pages_uneven_example():
+    """101 columns over two ranks give 51 / 50 (DeepSpeed PR #8309 timeline)."""
+    import synth
+
+    assert synth.default_split(101, 2) == [51, 50]
+    assert synth.default_split(128256, 8) == [16032] * 8
+    assert synth.default_split(5, 8) == [1, 1, 1, 1, 1, 0, 0, 0]

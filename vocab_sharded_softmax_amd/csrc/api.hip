@@ -1,0 +1,306 @@
+// api.hip -- the extern "C" entry points of libvjsd: argument validation on the host,
+// then one launch per shard per pass on the caller's stream.  The library allocates
+// nothing and keeps no state.  The operations and their citations are documented in
+// include/vjsd.h.
+#include <math.h>
+#include <string.h>
+
+#include "kernels.hpp"
+#include "vjsd.h"
+
+using vjsd::Shard;
+
+namespace {
+
+constexpr int MAX_SHARDS = 4096;
+constexpr int64_t MAX_ROWS = 0x7fffffff;  // one workgroup per row: grid.x limit
+
+int esize(int dt) { return dt == VJSD_F32 ? 4 : 2; }
+
+// A view is valid when its rows are element-aligned and do not overlap.
+bool view_ok(const void *p, int64_t rs, int64_t rpb, int64_t bs, int64_t N, int64_t w, int es) {
+    if (N == 0 || w == 0) return true;
+    if (!p || (reinterpret_cast<uintptr_t>(p) % es) != 0) return false;
+    if (rs < 0 || rpb < 0 || bs < 0) return false;
+    const int64_t rows_in_batch = rpb > 0 ? (rpb < N ? rpb : N) : N;
+    if (rows_in_batch > 1 && rs < w) return false;
+    if (rpb > 0 && N > rpb && bs < (rpb - 1) * rs + w) return false;
+    return true;
+}
+
+int check_common(const vjsd_shard *shards, int S, int64_t N, int dtype) {
+    if (dtype != VJSD_F32 && dtype != VJSD_F16 && dtype != VJSD_BF16) return VJSD_ERR_DTYPE;
+    if (N < 0 || N > MAX_ROWS || S < 1 || S > MAX_SHARDS || !shards) return VJSD_ERR_ARG;
+    for (int k = 0; k < S; ++k) {
+        if (shards[k].width < 0 || shards[k].vocab_start < 0) return VJSD_ERR_ARG;
+        if (k > 0 && shards[k].vocab_start != shards[k - 1].vocab_start + shards[k - 1].width)
+            return VJSD_ERR_LAYOUT;
+    }
+    return VJSD_OK;
+}
+
+// Inputs: student always, teacher when `two`; gradients when `grads` (a NULL gradient
+// pointer means "not wanted" and is allowed).
+int check_views(const vjsd_shard *shards, int S, int64_t N, int dtype, bool two, bool grads) {
+    const int es = esize(dtype);
+    for (int k = 0; k < S; ++k) {
+        const vjsd_shard &h = shards[k];
+        const int64_t w = h.width;
+        if (!view_ok(h.s.p, h.s.row_stride, h.s.rows_per_batch, h.s.batch_stride, N, w, es))
+            return VJSD_ERR_ARG;
+        if (two && !view_ok(h.t.p, h.t.row_stride, h.t.rows_per_batch, h.t.batch_stride, N, w, es))
+            return VJSD_ERR_ARG;
+        if (grads) {
+            if (h.gs.p && !view_ok(h.gs.p, h.gs.row_stride, h.gs.rows_per_batch,
+                                   h.gs.batch_stride, N, w, es))
+                return VJSD_ERR_ARG;
+            if (two && h.gt.p && !view_ok(h.gt.p, h.gt.row_stride, h.gt.rows_per_batch,
+                                          h.gt.batch_stride, N, w, es))
+                return VJSD_ERR_ARG;
+        }
+    }
+    return VJSD_OK;
+}
+
+Shard convert(const vjsd_shard &h, bool two, bool grads) {
+    Shard s;
+    s.start = h.vocab_start;
+    s.width = h.width;
+    s.s = {h.s.p, h.s.row_stride, h.s.rows_per_batch, h.s.batch_stride};
+    if (two) s.t = {h.t.p, h.t.row_stride, h.t.rows_per_batch, h.t.batch_stride};
+    else s.t = s.s;
+    if (grads) {
+        s.gs = {h.gs.p, h.gs.row_stride, h.gs.rows_per_batch, h.gs.batch_stride};
+        if (two) s.gt = {h.gt.p, h.gt.row_stride, h.gt.rows_per_batch, h.gt.batch_stride};
+        else s.gt = {nullptr, 0, 0, 0};
+    } else {
+        s.gs = {nullptr, 0, 0, 0};
+        s.gt = {nullptr, 0, 0, 0};
+    }
+    return s;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VJSD_OK : VJSD_ERR_HIP; }
+
+float *part_of(float *part, int k, int64_t N) {
+    return part + (size_t)k * (size_t)N * vjsd::PART_STRIDE;
+}
+
+int mode_of(double beta) {
+    return beta == 0.0 ? vjsd::FWD_KL : (beta == 1.0 ? vjsd::REV_KL : vjsd::INTERIOR);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *vjsd_strerror(int code) {
+    switch (code) {
+        case VJSD_OK: return "success";
+        case VJSD_ERR_ARG: return "invalid argument (null pointer, size, stride or alignment)";
+        case VJSD_ERR_DTYPE: return "unsupported dtype";
+        case VJSD_ERR_BETA: return "beta must be a number in [0, 1]";
+        case VJSD_ERR_LAYOUT: return "shards must be ordered and contiguous in the vocabulary";
+        case VJSD_ERR_EMPTY_SHARD: return "log-probabilities need every vocabulary shard non-empty";
+        case VJSD_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown vjsd status";
+    }
+}
+
+size_t vjsd_workspace_bytes(int64_t N, int S) {
+    if (N <= 0 || S <= 0) return 0;
+    return (size_t)N * (size_t)S * vjsd::PART_STRIDE * sizeof(float);
+}
+
+int vjsd_stats(const vjsd_shard *shards, int S, int64_t N, int dtype, int which, float *part,
+               void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (which < 1 || which > 3) return VJSD_ERR_ARG;
+    for (int k = 0; k < S; ++k) {  // only the selected inputs are read
+        const vjsd_shard &h = shards[k];
+        if ((which & 1) && !view_ok(h.s.p, h.s.row_stride, h.s.rows_per_batch, h.s.batch_stride,
+                                    N, h.width, esize(dtype)))
+            return VJSD_ERR_ARG;
+        if ((which & 2) && !view_ok(h.t.p, h.t.row_stride, h.t.rows_per_batch, h.t.batch_stride,
+                                    N, h.width, esize(dtype)))
+            return VJSD_ERR_ARG;
+    }
+    if (N == 0) return VJSD_OK;
+    if (!part) return VJSD_ERR_ARG;
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], true, false);
+        if ((e = hip_status(vjsd::launch_stats(dtype, which, sh, N, part_of(part, k, N),
+                                               (hipStream_t)stream))))
+            return e;
+    }
+    return VJSD_OK;
+}
+
+int vjsd_merge(const float *part, int S, int64_t N, int which, double *stats, void *stream) {
+    if (N < 0 || N > MAX_ROWS || S < 1 || S > MAX_SHARDS || which < 1 || which > 3)
+        return VJSD_ERR_ARG;
+    if (N == 0) return VJSD_OK;
+    if (!part || !stats) return VJSD_ERR_ARG;
+    return hip_status(vjsd::launch_merge(part, S, N, which, stats, (hipStream_t)stream));
+}
+
+int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
+             double beta, float *part, float *kl, float *loss, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    if ((e = check_views(shards, S, N, dtype, true, false))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!stats || !kl || !loss || (S > 1 && !part)) return VJSD_ERR_ARG;
+    const int mode = mode_of(beta);
+    hipStream_t st = (hipStream_t)stream;
+    if (S == 1) {
+        Shard sh = convert(shards[0], true, false);
+        return hip_status(vjsd::launch_div(dtype, mode, sh, N, stats, beta, nullptr, kl, loss, st));
+    }
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], true, false);
+        if ((e = hip_status(vjsd::launch_div(dtype, mode, sh, N, stats, beta, part_of(part, k, N),
+                                             nullptr, nullptr, st))))
+            return e;
+    }
+    return hip_status(vjsd::launch_div_finalize(mode, part, S, N, stats, beta, kl, loss, st));
+}
+
+int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
+             const float *kl, double beta, const float *grad_loss, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    if ((e = check_views(shards, S, N, dtype, true, true))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!stats || !kl || !grad_loss) return VJSD_ERR_ARG;
+    const int mode = mode_of(beta);
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], true, true);
+        if ((e = hip_status(vjsd::launch_bwd(dtype, mode, sh, N, stats, kl, beta, grad_loss,
+                                             (hipStream_t)stream))))
+            return e;
+    }
+    return VJSD_OK;
+}
+
+int vkl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse, float *part,
+            double *stats, float *kl, float *loss, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, true, false))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!part || !stats || !kl || !loss) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], true, false);
+        if ((e = hip_status(vjsd::launch_kl1(dtype, reverse != 0, sh, N, part_of(part, k, N), st))))
+            return e;
+    }
+    return hip_status(vjsd::launch_kl1_merge(reverse != 0, part, S, N, stats, kl, loss, st));
+}
+
+int vkl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse,
+            const double *stats, const float *kl, const float *grad_loss, void *stream) {
+    return vjsd_bwd(shards, S, N, dtype, stats, kl, reverse ? 1.0 : 0.0, grad_loss, stream);
+}
+
+int ventropy_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, float *part,
+                 double *stats, float *ent, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, false))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!part || !stats || !ent) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], false, false);
+        if ((e = hip_status(vjsd::launch_ent1(dtype, sh, N, part_of(part, k, N), st)))) return e;
+    }
+    return hip_status(vjsd::launch_ent1_merge(part, S, N, stats, ent, st));
+}
+
+int ventropy_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
+                 const float *ent, const float *grad, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, true))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!stats || !ent || !grad) return VJSD_ERR_ARG;
+    for (int k = 0; k < S; ++k) {
+        if (!shards[k].gs.p) continue;
+        Shard sh = convert(shards[k], false, true);
+        if ((e = hip_status(vjsd::launch_ent_bwd(dtype, sh, N, stats, ent, grad,
+                                                 (hipStream_t)stream))))
+            return e;
+    }
+    return VJSD_OK;
+}
+
+static int check_logprobs(const vjsd_shard *shards, int S, int64_t N, int dtype,
+                          int64_t vocab_global, const int64_t *ids, int K) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (K < 0 || (N > 0 && K > 0 && !ids)) return VJSD_ERR_ARG;
+    if (N > 0 && K > 0 && (N * (int64_t)K) / 256 > MAX_ROWS) return VJSD_ERR_ARG;
+    for (int k = 0; k < S; ++k)
+        if (shards[k].width == 0) return VJSD_ERR_EMPTY_SHARD;
+    if (shards[0].vocab_start != 0 ||
+        shards[S - 1].vocab_start + shards[S - 1].width != vocab_global)
+        return VJSD_ERR_LAYOUT;
+    return VJSD_OK;
+}
+
+int vlogprobs_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                  const int64_t *ids, int K, int64_t ignore_index, float *part, double *stats,
+                  float *out, int32_t *dev_err, void *stream) {
+    int e = check_logprobs(shards, S, N, dtype, vocab_global, ids, K);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, false))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!part || !stats || (K > 0 && (!out || !dev_err))) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], false, false);
+        if ((e = hip_status(vjsd::launch_stats(dtype, 1, sh, N, part_of(part, k, N), st)))) return e;
+    }
+    if ((e = hip_status(vjsd::launch_merge(part, S, N, 1, stats, st)))) return e;
+    if (K == 0) return VJSD_OK;
+    for (int k0 = 0; k0 < S; k0 += vjsd::LP_TABLE) {
+        vjsd::LpTable tab;
+        memset(&tab, 0, sizeof tab);
+        tab.n = (S - k0) < vjsd::LP_TABLE ? (S - k0) : vjsd::LP_TABLE;
+        for (int q = 0; q < tab.n; ++q) {
+            const vjsd_shard &h = shards[k0 + q];
+            tab.start[q] = h.vocab_start;
+            tab.width[q] = h.width;
+            tab.x[q] = {h.s.p, h.s.row_stride, h.s.rows_per_batch, h.s.batch_stride};
+        }
+        if ((e = hip_status(vjsd::launch_lp_gather(dtype, tab, k0 == 0, N, vocab_global, ids, K,
+                                                   ignore_index, stats, out, dev_err, st))))
+            return e;
+    }
+    return VJSD_OK;
+}
+
+int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                  const double *stats, const int64_t *ids, int K, int64_t ignore_index,
+                  const float *grad, void *stream) {
+    int e = check_logprobs(shards, S, N, dtype, vocab_global, ids, K);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, true))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!stats || (K > 0 && !grad)) return VJSD_ERR_ARG;
+    for (int k = 0; k < S; ++k) {
+        if (!shards[k].gs.p) continue;
+        Shard sh = convert(shards[k], false, true);
+        if ((e = hip_status(vjsd::launch_lp_bwd(dtype, sh, N, vocab_global, stats, ids, K,
+                                                ignore_index, grad, (hipStream_t)stream))))
+            return e;
+    }
+    return VJSD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,251 @@
+// device.hpp -- device-side building blocks of libvjsd (gfx950, wave64).
+//
+// Page keys: [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel
+// generalized JSD with Triton kernels"; [OPS-PR] DeepSpeed PR #8791 "Add
+// vocabulary-parallel logprobs, entropy and KL ops".
+//
+// Arithmetic model.  Every kernel works in base 2: a logit x of a row with max m
+// becomes u = x*L2E - c with c = fl32(m*L2E), evaluated by one fused multiply-add,
+// whose exact product keeps a large common offset out of the rounding (the
+// offset-robust statistics of [OPS-PR, How]).  exp and log are the hardware
+// v_exp_f32 (2^x) and v_log_f32 (log2 x).  A row's sum of 2^u is kept relative to
+// c; statistics handed between calls are (m, ln sum exp(x - m)) in fp64 and each
+// kernel rebuilds its fp32 row constants from them in fp64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vjsd {
+
+constexpr int BLOCK = 256;  // 4 waves of 64 lanes per row-workgroup
+constexpr int NWAVE = BLOCK / 64;
+constexpr float L2E = 1.44269504088896340736f;  // log2(e), fp32
+constexpr double L2E_D = 1.44269504088896340736;
+constexpr double LN2_D = 0.69314718055994530942;
+constexpr float LN2F = 0.69314718055994530942f;
+constexpr float NINF = -__builtin_huge_valf();
+// Lower clamp of u: 2^-512 is exactly 0 in fp32, and a clamped u keeps e * u finite
+// (0 * -inf would be NaN) for masked tokens.
+constexpr float U_FLOOR = -512.0f;
+// Added inside the mixture so log2 never sees 0 (both sides underflowed or masked);
+// 2^-126 is far below any mass that can move an fp32 result.
+constexpr float W_FLOOR = 1.17549435e-38f;
+constexpr int PART_STRIDE = 8;  // floats per (shard, row) in the workspace
+
+// ---- storage formats -------------------------------------------------------------
+
+struct F32 {
+    using T = float;
+    static constexpr int VEC = 4;  // elements per 16-byte access
+};
+struct F16 {
+    using T = uint16_t;
+    static constexpr int VEC = 8;
+};
+struct BF16 {
+    using T = uint16_t;
+    static constexpr int VEC = 8;
+};
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <class D>
+__device__ __forceinline__ float load1(const typename D::T *p);
+template <>
+__device__ __forceinline__ float load1<F32>(const float *p) { return *p; }
+template <>
+__device__ __forceinline__ float load1<F16>(const uint16_t *p) {
+    return (float)__builtin_bit_cast(_Float16, *p);
+}
+template <>
+__device__ __forceinline__ float load1<BF16>(const uint16_t *p) {
+    return __uint_as_float((uint32_t)*p << 16);
+}
+
+// 16-byte load widened to fp32.
+template <class D>
+__device__ __forceinline__ void load_vec(const typename D::T *p, float (&x)[D::VEC]);
+template <>
+__device__ __forceinline__ void load_vec<F32>(const float *p, float (&x)[4]) {
+    float4 v = *reinterpret_cast<const float4 *>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load_vec<BF16>(const uint16_t *p, float (&x)[8]) {
+    uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load_vec<F16>(const uint16_t *p, float (&x)[8]) {
+    uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+        x[2 * i] = (float)h.x;
+        x[2 * i + 1] = (float)h.y;
+    }
+}
+
+// Round-to-nearest-even stores of fp32 results in the storage format.
+template <class D>
+__device__ __forceinline__ void store1(typename D::T *p, float v);
+template <>
+__device__ __forceinline__ void store1<F32>(float *p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store1<F16>(uint16_t *p, float v) {
+    *p = __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+template <>
+__device__ __forceinline__ void store1<BF16>(uint16_t *p, float v) {
+    *p = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+template <class D>
+__device__ __forceinline__ void store_vec(typename D::T *p, const float (&x)[D::VEC]);
+template <>
+__device__ __forceinline__ void store_vec<F32>(float *p, const float (&x)[4]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+template <>
+__device__ __forceinline__ void store_vec<BF16>(uint16_t *p, const float (&x)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = __builtin_bit_cast(uint32_t,
+                                  __builtin_convertvector((f32x2){x[2 * i], x[2 * i + 1]}, bf16x2));
+    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ void store_vec<F16>(uint16_t *p, const float (&x)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = __builtin_bit_cast(uint32_t,
+                                  __builtin_convertvector((f32x2){x[2 * i], x[2 * i + 1]}, f16x2));
+    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---- views and rows --------------------------------------------------------------
+
+// Row view as passed to kernels (mirrors the ABI's view; strides in elements).
+struct RowView {
+    const void *p;
+    int64_t rs, rpb, bs;
+};
+struct RowMView {
+    void *p;
+    int64_t rs, rpb, bs;
+};
+
+__device__ __forceinline__ int64_t row_offset(int64_t r, int64_t rs, int64_t rpb, int64_t bs) {
+    return rpb > 0 ? (r / rpb) * bs + (r % rpb) * rs : r * rs;
+}
+template <class T>
+__device__ __forceinline__ const T *row_ptr(const RowView &v, int64_t r) {
+    return static_cast<const T *>(v.p) + row_offset(r, v.rs, v.rpb, v.bs);
+}
+template <class T>
+__device__ __forceinline__ T *row_ptr(const RowMView &v, int64_t r) {
+    return v.p ? static_cast<T *>(v.p) + row_offset(r, v.rs, v.rpb, v.bs) : nullptr;
+}
+
+// Elements before the first 16-byte boundary of a row whose views all share the same
+// offset inside 16 bytes; if they do not, the whole row goes through the scalar path.
+template <class T>
+__device__ __forceinline__ int64_t head_len(int64_t w, const void *a, const void *b = nullptr,
+                                            const void *c = nullptr, const void *d = nullptr) {
+    const uintptr_t off = reinterpret_cast<uintptr_t>(a) & 15;
+    bool same = true;
+    if (b) same &= (reinterpret_cast<uintptr_t>(b) & 15) == off;
+    if (c) same &= (reinterpret_cast<uintptr_t>(c) & 15) == off;
+    if (d) same &= (reinterpret_cast<uintptr_t>(d) & 15) == off;
+    if (!same) return w;
+    const int64_t h = (int64_t)(((16 - off) & 15) / sizeof(T));
+    return h < w ? h : w;
+}
+
+// ---- hardware exp2 / log2 and the base-2 reference point ---------------------------
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Reference point c = fl32(m * log2 e) of a row max m (0 for an empty / masked row).
+__device__ __forceinline__ float refc(float m) { return m == NINF ? 0.0f : m * L2E; }
+
+// Row normaliser rebuilt from stored statistics: Z = sum 2^(x*L2E - c) = 2^(lnZ*log2e + res)
+// with res = m*L2E - c exact in fp64.
+__device__ __forceinline__ double z_from_stats(float m, double lnZ) {
+    const double res = (double)m * (double)L2E - (double)refc(m);
+    return exp2(lnZ * L2E_D + res);
+}
+// Inverse: ln sum exp(x - m) from Z relative to c.
+__device__ __forceinline__ double lnz_from_z(float m, double Z) {
+    const double res = (double)m * (double)L2E - (double)refc(m);
+    return (log2(Z) - res) * LN2_D;
+}
+
+// ---- workgroup reductions (fixed order: deterministic results) ----------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Online (max, sum of 2^(x*L2E - refc(max))) pair.
+struct MZ {
+    float m, z;
+};
+__device__ __forceinline__ MZ mz_combine(MZ a, MZ b) {
+    const float m = fmaxf(a.m, b.m);
+    const float c = refc(m);
+    const float za = a.m == NINF ? 0.0f : a.z * ex2(refc(a.m) - c);
+    const float zb = b.m == NINF ? 0.0f : b.z * ex2(refc(b.m) - c);
+    return {m, za + zb};
+}
+__device__ __forceinline__ MZ wave_mz(MZ v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        MZ w{__shfl_xor(v.m, o), __shfl_xor(v.z, o)};
+        // combine in lane order so that both partners compute the same value
+        v = (threadIdx.x & o) ? mz_combine(w, v) : mz_combine(v, w);
+    }
+    return v;
+}
+
+// Sum of NV floats over the workgroup; result valid in thread 0.  `red` is LDS of
+// NV * NWAVE floats.
+template <int NV>
+__device__ __forceinline__ void block_sum(float (&v)[NV], float *red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
+    if (lane == 0)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) red[i * NWAVE + wave] = v[i];
+    __syncthreads();
+    if (threadIdx.x == 0)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            float a = red[i * NWAVE];
+#pragma unroll
+            for (int k = 1; k < NWAVE; ++k) a += red[i * NWAVE + k];
+            v[i] = a;
+        }
+}
+
+}  // namespace vjsd

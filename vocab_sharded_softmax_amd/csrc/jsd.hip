@@ -1,0 +1,349 @@
+// jsd.hip -- input passes 2 and 3 of the generalized JSD and of its KL endpoints.
+//
+// [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel generalized JSD with
+// Triton kernels": section Motivation (the interior 0 < beta < 1 generalized JSD of
+// GKD-style distillation), section Changes (global normalisation reused, the two
+// KL-to-mixture expectations reduced together, probabilities recomputed in registers
+// in the backward, gradients to both inputs or one, beta = 0 / 1 as explicit forward /
+// reverse KL branches), section Scope and limitations (statistics and divergence are
+// two input passes).  [OPS-PR] DeepSpeed PR #8791 "Add vocabulary-parallel logprobs,
+// entropy and KL ops", section How (closed-form local backward; -inf tokens add
+// nothing) and section Tests (KL is +inf when target mass meets a masked token).
+//
+// Base-2 row algebra.  With u = x*L2E - c (c = fl32(m*L2E)), e = 2^u, Z = sum e:
+//   M = beta p_t + (1-beta) p_s = (beta e_t + gamma e_s) / Z_t,  gamma = (1-beta) Z_t / Z_s
+//   L = log2(beta e_t + gamma e_s),  r = log2(Z_s / Z_t)
+//   log2(p_t / M) = u_t - L,  log2(p_s / M) = u_s - L - r
+//   KT / ln2 = (1/Z_t) sum e_t (u_t - L),  KS / ln2 = (1/Z_s) sum e_s ((u_s - L) - r)
+// so the per-element work touches only O(1)-sized quantities, never log Z; u - L and
+// (u_s - L) - r are differences of nearby numbers and come out (nearly) exact.
+#include "kernels.hpp"
+#include "sweep.hpp"
+
+namespace vjsd {
+
+namespace {
+
+// Per-row constants of a two-input pass, rebuilt from the fp64 statistics.
+struct RowConst {
+    bool undefined;
+    float cs, ct;    // reference points
+    float izs, izt;  // 1 / Z
+    double Zs, Zt;
+    double r;        // log2(Z_s / Z_t)
+};
+
+__device__ __forceinline__ RowConst row_const(const double *__restrict__ stats, int64_t r) {
+    RowConst k;
+    const double *st = stats + r * 4;
+    const float ms = (float)st[0], mt = (float)st[2];
+    k.undefined = (ms == NINF) || (mt == NINF);
+    k.cs = refc(ms);
+    k.ct = refc(mt);
+    k.Zs = k.undefined ? 1.0 : z_from_stats(ms, st[1]);
+    k.Zt = k.undefined ? 1.0 : z_from_stats(mt, st[3]);
+    k.izs = (float)(1.0 / k.Zs);
+    k.izt = (float)(1.0 / k.Zt);
+    k.r = log2(k.Zs / k.Zt);
+    return k;
+}
+
+template <int MODE>
+struct OpDiv {
+    float cs, ct, bf, gam, rf;
+    float At[4] = {0, 0, 0, 0}, As[4] = {0, 0, 0, 0};
+    float F = NINF;  // max of u_t - u_s (forward KL) or u_s - u_t (reverse): +inf flags mass on a masked token
+
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
+                                        const int64_t (&)[NV]) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const float usr = fmaf(x[j][i], L2E, -cs);
+                const float utr = fmaf(y[j][i], L2E, -ct);
+                const float us = fmaxf(usr, U_FLOOR), ut = fmaxf(utr, U_FLOOR);
+                if constexpr (MODE == INTERIOR) {
+                    const float es = ex2(us), et = ex2(ut);
+                    const float L = lg2(fmaf(bf, et, fmaf(gam, es, W_FLOOR)));
+                    At[j] = fmaf(et, ut - L, At[j]);
+                    As[j] = fmaf(es, (us - L) - rf, As[j]);
+                } else if constexpr (MODE == FWD_KL) {
+                    F = fmaxf(F, utr - usr);
+                    At[j] = fmaf(ex2(ut), (ut - us) + rf, At[j]);
+                } else {
+                    F = fmaxf(F, usr - utr);
+                    As[j] = fmaf(ex2(us), (us - ut) - rf, As[j]);
+                }
+            }
+    }
+};
+
+// Final per-token values from the shard-summed partials (all in base 2, fp64).
+__device__ __forceinline__ void finalize_row(int mode, double beta, bool undefined, double pt,
+                                             double ps, float F, float *kl, float *loss) {
+    double KT, KS, l;
+    if (undefined) {
+        KT = KS = l = __builtin_nan("");
+    } else if (mode == INTERIOR) {
+        KT = pt * LN2_D;
+        KS = ps * LN2_D;
+        l = beta * KT + (1.0 - beta) * KS;
+    } else if (mode == FWD_KL) {
+        KT = F == __builtin_huge_valf() ? __builtin_inf() : pt * LN2_D;
+        KS = 0.0;
+        l = KT;
+    } else {
+        KS = F == __builtin_huge_valf() ? __builtin_inf() : ps * LN2_D;
+        KT = 0.0;
+        l = KS;
+    }
+    kl[0] = (float)KT;
+    kl[1] = (float)KS;
+    *loss = (float)l;
+}
+
+template <class D, int MODE>
+__global__ __launch_bounds__(BLOCK) void k_div(RowView sv, RowView tv, int64_t w,
+                                               const double *__restrict__ stats, double beta,
+                                               float *__restrict__ part_k, float *__restrict__ kl,
+                                               float *__restrict__ loss) {
+    using T = typename D::T;
+    __shared__ float red[3 * NWAVE];
+    const int64_t r = blockIdx.x;
+    const RowConst k = row_const(stats, r);
+    float pt = 0.0f, ps = 0.0f, F = NINF;
+    if (!k.undefined && w > 0) {
+        const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
+        OpDiv<MODE> op;
+        op.cs = k.cs;
+        op.ct = k.ct;
+        op.bf = (float)beta;
+        op.gam = (float)((1.0 - beta) * k.Zt / k.Zs);
+        op.rf = (float)k.r;
+        sweep<D, 4, true>(s, t, w, head_len<T>(w, s, t), op);
+        float v[2] = {(op.At[0] + op.At[1]) + (op.At[2] + op.At[3]),
+                      (op.As[0] + op.As[1]) + (op.As[2] + op.As[3])};
+        block_sum<2>(v, red);
+        const float f = wave_max(op.F);
+        if ((threadIdx.x & 63) == 0) red[2 * NWAVE + (threadIdx.x >> 6)] = f;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            pt = v[0] * k.izt;
+            ps = v[1] * k.izs;
+            for (int q = 0; q < NWAVE; ++q) F = fmaxf(F, red[2 * NWAVE + q]);
+        }
+    }
+    if (threadIdx.x == 0) {
+        if (loss) {
+            finalize_row(MODE, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r);
+        } else {
+            float *o = part_k + r * PART_STRIDE;
+            o[0] = pt;
+            o[1] = ps;
+            o[2] = F;
+        }
+    }
+}
+
+__global__ void k_div_finalize(int mode, const float *__restrict__ part, int S, int64_t N,
+                               const double *__restrict__ stats, double beta,
+                               float *__restrict__ kl, float *__restrict__ loss) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= N) return;
+    const RowConst k = row_const(stats, r);
+    double pt = 0.0, ps = 0.0;
+    float F = NINF;
+    for (int q = 0; q < S; ++q) {
+        const float *p = part + ((int64_t)q * N + r) * PART_STRIDE;
+        pt += p[0];
+        ps += p[1];
+        F = fmaxf(F, p[2]);
+    }
+    finalize_row(mode, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r);
+}
+
+// ---- backward ---------------------------------------------------------------------
+
+template <class D, int MODE, bool WS, bool WT>
+struct OpBwd {
+    using T = typename D::T;
+    T *gs, *gt;
+    float cs, ct, bf, gam;
+    float Cs, Ct;  // gradient scales
+    float Hs, Ht;  // per-side offsets subtracted from the log-ratio
+    float Gs, Gt;  // g / Z for the p_s - p_t terms of the endpoints
+
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
+                                        const int64_t (&col)[NV]) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            float os[W], ot[W];
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const float us = fmaxf(fmaf(x[j][i], L2E, -cs), U_FLOOR);
+                const float ut = fmaxf(fmaf(y[j][i], L2E, -ct), U_FLOOR);
+                const float es = ex2(us), et = ex2(ut);
+                if constexpr (MODE == INTERIOR) {
+                    const float L = lg2(fmaf(bf, et, fmaf(gam, es, W_FLOOR)));
+                    os[i] = (Cs * es) * ((us - L) - Hs);
+                    ot[i] = (Ct * et) * ((ut - L) - Ht);
+                } else if constexpr (MODE == FWD_KL) {
+                    os[i] = fmaf(Gs, es, -(Gt * et));
+                    ot[i] = (Ct * et) * ((ut - us) - Ht);
+                } else {
+                    os[i] = (Cs * es) * ((us - ut) - Hs);
+                    ot[i] = fmaf(Gt, et, -(Gs * es));
+                }
+            }
+            if constexpr (W == D::VEC) {
+                if (WS) store_vec<D>(gs + col[j], os);
+                if (WT) store_vec<D>(gt + col[j], ot);
+            } else {
+#pragma unroll
+                for (int i = 0; i < W; ++i) {
+                    if (WS) store1<D>(gs + col[j] + i, os[i]);
+                    if (WT) store1<D>(gt + col[j] + i, ot[i]);
+                }
+            }
+        }
+    }
+};
+
+template <class D>
+__device__ __forceinline__ void zero_row(typename D::T *p, int64_t w) {
+    if (!p) return;
+    const int64_t h = head_len<typename D::T>(w, p);
+    for (int64_t i = threadIdx.x; i < h; i += BLOCK) store1<D>(p + i, 0.0f);
+    const int64_t nv = (w - h) / D::VEC;
+    float z[D::VEC];
+#pragma unroll
+    for (int i = 0; i < D::VEC; ++i) z[i] = 0.0f;
+    for (int64_t v = threadIdx.x; v < nv; v += BLOCK) store_vec<D>(p + h + v * D::VEC, z);
+    for (int64_t i = h + nv * D::VEC + threadIdx.x; i < w; i += BLOCK) store1<D>(p + i, 0.0f);
+}
+
+template <class D, int MODE, bool WS, bool WT>
+__global__ __launch_bounds__(BLOCK) void k_bwd(RowView sv, RowView tv, RowMView gsv,
+                                               RowMView gtv, int64_t w,
+                                               const double *__restrict__ stats,
+                                               const float *__restrict__ kl, double beta,
+                                               const float *__restrict__ grad) {
+    using T = typename D::T;
+    const int64_t r = blockIdx.x;
+    if (w == 0) return;
+    T *gs = WS ? row_ptr<T>(gsv, r) : nullptr;
+    T *gt = WT ? row_ptr<T>(gtv, r) : nullptr;
+    const RowConst k = row_const(stats, r);
+    if (k.undefined) {  // no distribution: exactly zero gradient whatever g is
+        if (WS) zero_row<D>(gs, w);
+        if (WT) zero_row<D>(gt, w);
+        return;
+    }
+    const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
+    const double g = grad[r];
+    const double KT2 = (double)kl[2 * r] * L2E_D, KS2 = (double)kl[2 * r + 1] * L2E_D;
+    OpBwd<D, MODE, WS, WT> op;
+    op.gs = gs;
+    op.gt = gt;
+    op.cs = k.cs;
+    op.ct = k.ct;
+    op.bf = (float)beta;
+    op.gam = (float)((1.0 - beta) * k.Zt / k.Zs);
+    op.Gs = (float)(g / k.Zs);
+    op.Gt = (float)(g / k.Zt);
+    if (MODE == INTERIOR) {
+        op.Cs = (float)(g * (1.0 - beta) * LN2_D / k.Zs);
+        op.Ct = (float)(g * beta * LN2_D / k.Zt);
+        op.Hs = (float)(k.r + KS2);
+        op.Ht = (float)KT2;
+    } else if (MODE == FWD_KL) {  // d/dt = g p_t (lp_t - lp_s - KT), lp2_t - lp2_s = u_t - u_s + r
+        op.Ct = (float)(g * LN2_D / k.Zt);
+        op.Ht = (float)(KT2 - k.r);
+        op.Cs = 0.0f;
+        op.Hs = 0.0f;
+    } else {  // d/ds = g p_s (lp_s - lp_t - KS), lp2_s - lp2_t = u_s - u_t - r
+        op.Cs = (float)(g * LN2_D / k.Zs);
+        op.Hs = (float)(KS2 + k.r);
+        op.Ct = 0.0f;
+        op.Ht = 0.0f;
+    }
+    // the vector path needs every view of the row at the same offset inside 16 bytes
+    const int64_t h = head_len<T>(w, s, t, gs, gt);
+    sweep<D, 4, true>(s, t, w, h, op);
+}
+
+template <class D, int MODE>
+hipError_t div_dt(const Shard &sh, int64_t N, const double *stats, double beta, float *part_k,
+                  float *kl, float *loss, hipStream_t st) {
+    hipLaunchKernelGGL((k_div<D, MODE>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s, sh.t,
+                       sh.width, stats, beta, part_k, kl, loss);
+    return hipGetLastError();
+}
+
+template <class D>
+hipError_t div_mode(int mode, const Shard &sh, int64_t N, const double *stats, double beta,
+                    float *part_k, float *kl, float *loss, hipStream_t st) {
+    if (mode == INTERIOR) return div_dt<D, INTERIOR>(sh, N, stats, beta, part_k, kl, loss, st);
+    if (mode == FWD_KL) return div_dt<D, FWD_KL>(sh, N, stats, beta, part_k, kl, loss, st);
+    return div_dt<D, REV_KL>(sh, N, stats, beta, part_k, kl, loss, st);
+}
+
+template <class D, int MODE, bool WS, bool WT>
+hipError_t bwd_k(const Shard &sh, int64_t N, const double *stats, const float *kl, double beta,
+                 const float *grad, hipStream_t st) {
+    hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s,
+                       sh.t, sh.gs, sh.gt, sh.width, stats, kl, beta, grad);
+    return hipGetLastError();
+}
+
+template <class D, int MODE>
+hipError_t bwd_want(const Shard &sh, int64_t N, const double *stats, const float *kl,
+                    double beta, const float *grad, hipStream_t st) {
+    const bool ws = sh.gs.p != nullptr, wt = sh.gt.p != nullptr;
+    if (ws && wt) return bwd_k<D, MODE, true, true>(sh, N, stats, kl, beta, grad, st);
+    if (ws) return bwd_k<D, MODE, true, false>(sh, N, stats, kl, beta, grad, st);
+    if (wt) return bwd_k<D, MODE, false, true>(sh, N, stats, kl, beta, grad, st);
+    return hipSuccess;
+}
+
+template <class D>
+hipError_t bwd_mode(int mode, const Shard &sh, int64_t N, const double *stats, const float *kl,
+                    double beta, const float *grad, hipStream_t st) {
+    if (mode == INTERIOR) return bwd_want<D, INTERIOR>(sh, N, stats, kl, beta, grad, st);
+    if (mode == FWD_KL) return bwd_want<D, FWD_KL>(sh, N, stats, kl, beta, grad, st);
+    return bwd_want<D, REV_KL>(sh, N, stats, kl, beta, grad, st);
+}
+
+}  // namespace
+
+hipError_t launch_div(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
+                      double beta, float *part_k, float *kl, float *loss, hipStream_t st) {
+    switch (dtype) {
+        case 0: return div_mode<F32>(mode, sh, N, stats, beta, part_k, kl, loss, st);
+        case 1: return div_mode<F16>(mode, sh, N, stats, beta, part_k, kl, loss, st);
+        default: return div_mode<BF16>(mode, sh, N, stats, beta, part_k, kl, loss, st);
+    }
+}
+
+hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
+                               const double *stats, double beta, float *kl, float *loss,
+                               hipStream_t st) {
+    const int threads = 256;
+    hipLaunchKernelGGL(k_div_finalize, dim3((unsigned)((N + threads - 1) / threads)),
+                       dim3(threads), 0, st, mode, part, S, N, stats, beta, kl, loss);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
+                      const float *kl, double beta, const float *grad, hipStream_t st) {
+    switch (dtype) {
+        case 0: return bwd_mode<F32>(mode, sh, N, stats, kl, beta, grad, st);
+        case 1: return bwd_mode<F16>(mode, sh, N, stats, kl, beta, grad, st);
+        default: return bwd_mode<BF16>(mode, sh, N, stats, kl, beta, grad, st);
+    }
+}
+
+}  // namespace vjsd

@@ -1,0 +1,64 @@
+// kernels.hpp -- host-side launchers of libvjsd's kernels (one call per shard or per
+// row set).  Each returns the launch status; argument checking happens in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace vjsd {
+
+enum Mode { INTERIOR = 0, FWD_KL = 1, REV_KL = 2 };
+
+struct Shard {
+    int64_t start, width;
+    RowView s, t;
+    RowMView gs, gt;
+};
+
+// pass 1: per-shard (max, sum-exp) of the inputs selected by `which` (1 s, 2 t, 3 both)
+hipError_t launch_stats(int dtype, int which, const Shard &sh, int64_t N, float *part_k,
+                        hipStream_t st);
+// cross-shard merge of pass-1 partials into stats[N][4]
+hipError_t launch_merge(const float *part, int S, int64_t N, int which, double *stats,
+                        hipStream_t st);
+// pass 2 of the JSD (and its endpoint branches): per-shard divergence partials; with
+// `kl`/`loss` non-null (single shard) the row is finalised in the same launch
+hipError_t launch_div(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
+                      double beta, float *part_k, float *kl, float *loss, hipStream_t st);
+// shard-ordered sum of pass-2 partials into kl[N][2], loss[N]
+hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
+                               const double *stats, double beta, float *kl, float *loss,
+                               hipStream_t st);
+// pass 3: closed-form gradients of the JSD / KL for one shard
+hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
+                      const float *kl, double beta, const float *grad, hipStream_t st);
+
+// single-pass KL forward: per-shard online partials, then the merge into stats/kl/loss
+hipError_t launch_kl1(int dtype, int reverse, const Shard &sh, int64_t N, float *part_k,
+                      hipStream_t st);
+hipError_t launch_kl1_merge(int reverse, const float *part, int S, int64_t N, double *stats,
+                            float *kl, float *loss, hipStream_t st);
+// single-pass entropy forward and its backward
+hipError_t launch_ent1(int dtype, const Shard &sh, int64_t N, float *part_k, hipStream_t st);
+hipError_t launch_ent1_merge(const float *part, int S, int64_t N, double *stats, float *ent,
+                             hipStream_t st);
+hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const double *stats,
+                          const float *ent, const float *grad, hipStream_t st);
+
+// log-probabilities: gather of K ids per row, and the backward (stream + id fix-up)
+constexpr int LP_TABLE = 16;  // shards per gather launch
+struct LpTable {
+    int n;
+    int64_t start[LP_TABLE], width[LP_TABLE];
+    RowView x[LP_TABLE];
+};
+hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N,
+                            int64_t vocab_global, const int64_t *ids, int K, int64_t ignore,
+                            const double *stats, float *out, int32_t *dev_err, hipStream_t st);
+hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, int64_t vocab_global,
+                         const double *stats, const int64_t *ids, int K, int64_t ignore,
+                         const float *grad, hipStream_t st);
+
+}  // namespace vjsd

@@ -1,0 +1,550 @@
+// siblings.hip -- the sibling ops on the same statistics engine: single-pass KL and
+// entropy forwards, the entropy backward, and per-id / top-k log-probabilities.
+//
+// [OPS-PR] DeepSpeed PR #8791 "Add vocabulary-parallel logprobs, entropy and KL ops":
+// section What (the three ops, ignore_index positions return 0), section How (MAX and
+// SUM of [N] statistics, -inf tokens add nothing, fully -inf rows give NaN and zero
+// gradient, closed-form local backward), review thread (empty shards join the merge;
+// log-probabilities reject them; the index range check runs every call).
+// [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel generalized JSD with
+// Triton kernels", section Scope and limitations: KL's forward is a single input pass.
+//
+// Single-pass accumulation keeps every running sum relative to the running maxima and
+// rebases it when a maximum grows, so no large offset enters a sum.
+#include "kernels.hpp"
+#include "sweep.hpp"
+
+namespace vjsd {
+
+namespace {
+
+// ---- single-pass KL(p_a || p_b) ---------------------------------------------------
+// a is the target side (teacher for forward KL, student for reverse KL).
+// A = sum e_a (u_a - u_b) relative to the current reference points (c_a, c_b);
+// F = max (u_a - u_b) over raw values: +inf iff some a > -inf meets b = -inf.
+struct OpKL1 {
+    float ma = NINF, ca = 0.0f, za = 0.0f;
+    float mb = NINF, cb = 0.0f, zb = 0.0f;
+    float A = 0.0f, F = NINF;
+
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&xa)[NV][W], const float (&xb)[NV][W],
+                                        const int64_t (&)[NV]) {
+        constexpr int N = NV * W;
+        const float *a = &xa[0][0], *b = &xb[0][0];
+        float bma = a[0], bmb = b[0];
+#pragma unroll
+        for (int i = 1; i < N; ++i) {
+            bma = fmaxf(bma, a[i]);
+            bmb = fmaxf(bmb, b[i]);
+        }
+        const float nma = fmaxf(ma, bma), nmb = fmaxf(mb, bmb);
+        const float nca = refc(nma), ncb = refc(nmb);
+        const float sa = ma == NINF ? 0.0f : ex2(ca - nca);
+        const float sb = mb == NINF ? 0.0f : ex2(cb - ncb);
+        A = sa * fmaf((ca - nca) - (cb - ncb), za, A);
+        float ea[N], eb[N], pa = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float uar = fmaf(a[i], L2E, -nca), ubr = fmaf(b[i], L2E, -ncb);
+            F = fmaxf(F, uar - ubr);
+            const float ua = fmaxf(uar, U_FLOOR), ub = fmaxf(ubr, U_FLOOR);
+            ea[i] = ex2(ua);
+            eb[i] = ex2(ub);
+            pa = fmaf(ea[i], ua - ub, pa);
+        }
+#pragma unroll
+        for (int st = N / 2; st >= 1; st /= 2)
+#pragma unroll
+            for (int i = 0; i < st; ++i) {
+                ea[i] += ea[i + st];
+                eb[i] += eb[i + st];
+            }
+        za = fmaf(za, sa, ea[0]);
+        zb = fmaf(zb, sb, eb[0]);
+        A += pa;
+        ma = nma;
+        ca = nca;
+        mb = nmb;
+        cb = ncb;
+    }
+};
+
+// Combine two (m_a, z_a, m_b, z_b, A, F) partials, the first argument first.
+struct KLPart {
+    float ma, za, mb, zb, A, F;
+};
+__device__ __forceinline__ KLPart kl_combine(KLPart x, KLPart y) {
+    KLPart o;
+    o.ma = fmaxf(x.ma, y.ma);
+    o.mb = fmaxf(x.mb, y.mb);
+    const float ca = refc(o.ma), cb = refc(o.mb);
+    o.za = 0.0f;
+    o.zb = 0.0f;
+    o.A = 0.0f;
+    const KLPart *in[2] = {&x, &y};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const KLPart &p = *in[q];
+        if (p.mb != NINF) o.zb += p.zb * ex2(refc(p.mb) - cb);
+        if (p.ma != NINF) {
+            const float da = refc(p.ma) - ca;
+            const float db = p.mb == NINF ? 0.0f : refc(p.mb) - cb;
+            const float sc = ex2(da);
+            o.za += p.za * sc;
+            o.A += sc * fmaf(da - db, p.za, p.A);
+        }
+    }
+    o.F = fmaxf(x.F, y.F);
+    return o;
+}
+
+template <class D, bool REV>
+__global__ __launch_bounds__(BLOCK) void k_kl1(RowView sv, RowView tv, int64_t w,
+                                               float *__restrict__ part_k) {
+    using T = typename D::T;
+    __shared__ float red[6 * NWAVE];
+    const int64_t r = blockIdx.x;
+    KLPart p{NINF, 0.0f, NINF, 0.0f, 0.0f, NINF};
+    if (w > 0) {
+        const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
+        const T *a = REV ? s : t, *b = REV ? t : s;
+        OpKL1 op;
+        sweep<D, 4, true>(a, b, w, head_len<T>(w, a, b), op);
+        p = {op.ma, op.za, op.mb, op.zb, op.A, op.F};
+        // wave reduction in lane order, then waves in order
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            KLPart q{__shfl_xor(p.ma, o), __shfl_xor(p.za, o), __shfl_xor(p.mb, o),
+                     __shfl_xor(p.zb, o), __shfl_xor(p.A, o),  __shfl_xor(p.F, o)};
+            p = (threadIdx.x & o) ? kl_combine(q, p) : kl_combine(p, q);
+        }
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) {
+            float *d = red + 6 * wave;
+            d[0] = p.ma; d[1] = p.za; d[2] = p.mb; d[3] = p.zb; d[4] = p.A; d[5] = p.F;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            p = {red[0], red[1], red[2], red[3], red[4], red[5]};
+            for (int q = 1; q < NWAVE; ++q) {
+                const float *d = red + 6 * q;
+                p = kl_combine(p, KLPart{d[0], d[1], d[2], d[3], d[4], d[5]});
+            }
+        }
+    }
+    if (threadIdx.x == 0) {
+        float *o = part_k + r * PART_STRIDE;
+        o[0] = p.ma; o[1] = p.za; o[2] = p.mb; o[3] = p.zb; o[4] = p.A; o[5] = p.F;
+    }
+}
+
+__global__ void k_kl1_merge(int rev, const float *__restrict__ part, int S, int64_t N,
+                            double *__restrict__ stats, float *__restrict__ kl,
+                            float *__restrict__ loss) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= N) return;
+    float ma = NINF, mb = NINF, F = NINF;
+    for (int k = 0; k < S; ++k) {
+        const float *p = part + ((int64_t)k * N + r) * PART_STRIDE;
+        ma = fmaxf(ma, p[0]);
+        mb = fmaxf(mb, p[2]);
+        F = fmaxf(F, p[5]);
+    }
+    const double ca = refc(ma), cb = refc(mb);
+    double Za = 0.0, Zb = 0.0, A = 0.0;
+    for (int k = 0; k < S; ++k) {
+        const float *p = part + ((int64_t)k * N + r) * PART_STRIDE;
+        if (p[2] != NINF) Zb += (double)p[3] * exp2((double)refc(p[2]) - cb);
+        if (p[0] != NINF) {
+            const double da = (double)refc(p[0]) - ca;
+            const double db = p[2] == NINF ? 0.0 : (double)refc(p[2]) - cb;
+            const double sc = exp2(da);
+            Za += (double)p[1] * sc;
+            A += sc * ((double)p[4] + (da - db) * (double)p[1]);
+        }
+    }
+    const bool undefined = ma == NINF || mb == NINF;
+    const double lza = undefined ? 0.0 : log2(Za), lzb = undefined ? 0.0 : log2(Zb);
+    double v;
+    if (undefined) v = __builtin_nan("");
+    else if (F == __builtin_huge_valf()) v = __builtin_inf();
+    else v = (A / Za - lza + lzb) * LN2_D;  // sum p_a (lp_a - lp_b), base 2 then nats
+    // statistics: a is the teacher for forward KL, the student for reverse KL
+    const float ms = rev ? ma : mb, mt = rev ? mb : ma;
+    const double Zs = rev ? Za : Zb, Zt = rev ? Zb : Za;
+    double *o = stats + r * 4;
+    o[0] = ms;
+    o[1] = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, Zs);
+    o[2] = mt;
+    o[3] = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, Zt);
+    kl[2 * r] = rev ? 0.0f : (float)v;
+    kl[2 * r + 1] = rev ? (float)v : 0.0f;
+    if (undefined) kl[2 * r] = kl[2 * r + 1] = __builtin_nanf("");
+    loss[r] = (float)v;
+}
+
+// ---- single-pass entropy ------------------------------------------------------------
+// B = sum e u relative to the running reference point; H / ln2 = log2 Z - B / Z.
+struct OpEnt1 {
+    float m = NINF, c = 0.0f, z = 0.0f, B = 0.0f;
+
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&xa)[NV][W], const float (&)[NV][W],
+                                        const int64_t (&)[NV]) {
+        constexpr int N = NV * W;
+        const float *x = &xa[0][0];
+        float bm = x[0];
+#pragma unroll
+        for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
+        const float nm = fmaxf(m, bm), nc = refc(nm);
+        const float sc = m == NINF ? 0.0f : ex2(c - nc);
+        B = sc * fmaf(c - nc, z, B);
+        float e[N], pb = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float u = fmaxf(fmaf(x[i], L2E, -nc), U_FLOOR);
+            e[i] = ex2(u);
+            pb = fmaf(e[i], u, pb);
+        }
+#pragma unroll
+        for (int st = N / 2; st >= 1; st /= 2)
+#pragma unroll
+            for (int i = 0; i < st; ++i) e[i] += e[i + st];
+        z = fmaf(z, sc, e[0]);
+        B += pb;
+        m = nm;
+        c = nc;
+    }
+};
+
+struct EntPart {
+    float m, z, B;
+};
+__device__ __forceinline__ EntPart ent_combine(EntPart x, EntPart y) {
+    EntPart o{fmaxf(x.m, y.m), 0.0f, 0.0f};
+    const float c = refc(o.m);
+    const EntPart *in[2] = {&x, &y};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const EntPart &p = *in[q];
+        if (p.m != NINF) {
+            const float d = refc(p.m) - c;
+            const float sc = ex2(d);
+            o.z += p.z * sc;
+            o.B += sc * fmaf(d, p.z, p.B);
+        }
+    }
+    return o;
+}
+
+template <class D>
+__global__ __launch_bounds__(BLOCK) void k_ent1(RowView xv, int64_t w, float *__restrict__ part_k) {
+    using T = typename D::T;
+    __shared__ float red[3 * NWAVE];
+    const int64_t r = blockIdx.x;
+    EntPart p{NINF, 0.0f, 0.0f};
+    if (w > 0) {
+        const T *x = row_ptr<T>(xv, r);
+        OpEnt1 op;
+        sweep<D, 4, false>(x, x, w, head_len<T>(w, x), op);
+        p = {op.m, op.z, op.B};
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            EntPart q{__shfl_xor(p.m, o), __shfl_xor(p.z, o), __shfl_xor(p.B, o)};
+            p = (threadIdx.x & o) ? ent_combine(q, p) : ent_combine(p, q);
+        }
+        const int wave = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) {
+            red[3 * wave] = p.m;
+            red[3 * wave + 1] = p.z;
+            red[3 * wave + 2] = p.B;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            p = {red[0], red[1], red[2]};
+            for (int q = 1; q < NWAVE; ++q)
+                p = ent_combine(p, EntPart{red[3 * q], red[3 * q + 1], red[3 * q + 2]});
+        }
+    }
+    if (threadIdx.x == 0) {
+        float *o = part_k + r * PART_STRIDE;
+        o[0] = p.m; o[1] = p.z; o[2] = p.B;
+    }
+}
+
+__global__ void k_ent1_merge(const float *__restrict__ part, int S, int64_t N,
+                             double *__restrict__ stats, float *__restrict__ ent) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= N) return;
+    float m = NINF;
+    for (int k = 0; k < S; ++k) m = fmaxf(m, part[((int64_t)k * N + r) * PART_STRIDE]);
+    const double c = refc(m);
+    double Z = 0.0, B = 0.0;
+    for (int k = 0; k < S; ++k) {
+        const float *p = part + ((int64_t)k * N + r) * PART_STRIDE;
+        if (p[0] != NINF) {
+            const double d = (double)refc(p[0]) - c;
+            const double sc = exp2(d);
+            Z += (double)p[1] * sc;
+            B += sc * ((double)p[2] + d * (double)p[1]);
+        }
+    }
+    double *o = stats + r * 4;
+    o[0] = m;
+    if (m == NINF) {
+        o[1] = -__builtin_inf();
+        ent[r] = __builtin_nanf("");
+    } else {
+        o[1] = lnz_from_z(m, Z);
+        ent[r] = (float)((log2(Z) - B / Z) * LN2_D);
+    }
+}
+
+// d/dx = -g p (lp + H) = (-g ln2 / Z) e (u - R),  R = log2 Z - H / ln2
+template <class D>
+struct OpEntBwd {
+    using T = typename D::T;
+    T *gx;
+    float c, C, R;
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&)[NV][W],
+                                        const int64_t (&col)[NV]) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            float o[W];
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const float u = fmaxf(fmaf(x[j][i], L2E, -c), U_FLOOR);
+                o[i] = (C * ex2(u)) * (u - R);
+            }
+            if constexpr (W == D::VEC) store_vec<D>(gx + col[j], o);
+            else
+#pragma unroll
+                for (int i = 0; i < W; ++i) store1<D>(gx + col[j] + i, o[i]);
+        }
+    }
+};
+
+template <class D>
+__device__ __forceinline__ void zero_row1(typename D::T *p, int64_t w) {
+    const int64_t h = head_len<typename D::T>(w, p);
+    for (int64_t i = threadIdx.x; i < h; i += BLOCK) store1<D>(p + i, 0.0f);
+    const int64_t nv = (w - h) / D::VEC;
+    float z[D::VEC];
+#pragma unroll
+    for (int i = 0; i < D::VEC; ++i) z[i] = 0.0f;
+    for (int64_t v = threadIdx.x; v < nv; v += BLOCK) store_vec<D>(p + h + v * D::VEC, z);
+    for (int64_t i = h + nv * D::VEC + threadIdx.x; i < w; i += BLOCK) store1<D>(p + i, 0.0f);
+}
+
+template <class D>
+__global__ __launch_bounds__(BLOCK) void k_ent_bwd(RowView xv, RowMView gv, int64_t w,
+                                                   const double *__restrict__ stats,
+                                                   const float *__restrict__ ent,
+                                                   const float *__restrict__ grad) {
+    using T = typename D::T;
+    const int64_t r = blockIdx.x;
+    if (w == 0) return;
+    T *gx = row_ptr<T>(gv, r);
+    const float m = (float)stats[r * 4];
+    if (m == NINF) {
+        zero_row1<D>(gx, w);
+        return;
+    }
+    const T *x = row_ptr<T>(xv, r);
+    const double Z = z_from_stats(m, stats[r * 4 + 1]);
+    OpEntBwd<D> op;
+    op.gx = gx;
+    op.c = refc(m);
+    op.C = (float)(-(double)grad[r] * LN2_D / Z);
+    op.R = (float)(log2(Z) - (double)ent[r] * L2E_D);
+    sweep<D, 4, false>(x, x, w, head_len<T>(w, x, gx), op);
+}
+
+// ---- log-probabilities ----------------------------------------------------------------
+
+// One thread per (row, k).  The first launch of a call also resolves ignore_index
+// (exactly 0) and out-of-range ids (error flag); every launch gathers the ids its
+// table of shards owns: lp = (x - m) - lnZ in fp64.
+template <class D>
+__global__ void k_lp_gather(LpTable tab, int first, int64_t N, int64_t vocab_global,
+                            const int64_t *__restrict__ ids, int K, int64_t ignore,
+                            const double *__restrict__ stats, float *__restrict__ out,
+                            int32_t *__restrict__ dev_err) {
+    using T = typename D::T;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N * K) return;
+    const int64_t r = i / K;
+    const int64_t id = ids[i];
+    if (id == ignore) {
+        if (first) out[i] = 0.0f;
+        return;
+    }
+    if (id < 0 || id >= vocab_global) {
+        if (first) {
+            out[i] = __builtin_nanf("");
+            *dev_err = 1;
+        }
+        return;
+    }
+    for (int q = 0; q < tab.n; ++q) {
+        if (id >= tab.start[q] && id < tab.start[q] + tab.width[q]) {
+            const double m = stats[r * 4], lz = stats[r * 4 + 1];
+            if (m == -__builtin_inf()) {
+                out[i] = __builtin_nanf("");
+            } else {
+                const double x = load1<D>(row_ptr<T>(tab.x[q], r) + (id - tab.start[q]));
+                out[i] = (float)((x - m) - lz);
+            }
+            return;
+        }
+    }
+}
+
+// d/dx_j = -G p_j everywhere (G = sum of the valid upstream gradients), then the ids
+// this shard owns are rewritten as (sum of their g) - G p_j, rounded once.
+template <class D>
+struct OpLpBwd {
+    using T = typename D::T;
+    T *gx;
+    float c, C;
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&)[NV][W],
+                                        const int64_t (&col)[NV]) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            float o[W];
+#pragma unroll
+            for (int i = 0; i < W; ++i) o[i] = C * ex2(fmaxf(fmaf(x[j][i], L2E, -c), U_FLOOR));
+            if constexpr (W == D::VEC) store_vec<D>(gx + col[j], o);
+            else
+#pragma unroll
+                for (int i = 0; i < W; ++i) store1<D>(gx + col[j] + i, o[i]);
+        }
+    }
+};
+
+template <class D>
+__global__ __launch_bounds__(BLOCK) void k_lp_bwd(RowView xv, RowMView gv, int64_t start,
+                                                  int64_t w, int64_t vocab_global,
+                                                  const double *__restrict__ stats,
+                                                  const int64_t *__restrict__ ids, int K,
+                                                  int64_t ignore, const float *__restrict__ grad) {
+    using T = typename D::T;
+    const int64_t r = blockIdx.x;
+    if (w == 0) return;
+    T *gx = row_ptr<T>(gv, r);
+    const float m = (float)stats[r * 4];
+    if (m == NINF) {
+        zero_row1<D>(gx, w);
+        return;
+    }
+    const int64_t *id = ids + r * K;
+    const float *g = grad + r * K;
+    double G = 0.0;
+    for (int k = 0; k < K; ++k)
+        if (id[k] != ignore && id[k] >= 0 && id[k] < vocab_global) G += g[k];
+    const T *x = row_ptr<T>(xv, r);
+    const double Z = z_from_stats(m, stats[r * 4 + 1]);
+    OpLpBwd<D> op;
+    op.gx = gx;
+    op.c = refc(m);
+    op.C = (float)(-G / Z);
+    sweep<D, 4, false>(x, x, w, head_len<T>(w, x, gx), op);
+    __syncthreads();  // the streamed values of this row are visible to the block
+    for (int k = threadIdx.x; k < K; k += BLOCK) {
+        const int64_t j = id[k] - start;
+        if (id[k] == ignore || j < 0 || j >= w) continue;
+        float gsum = 0.0f;
+        for (int q = 0; q < K; ++q)
+            if (id[q] == id[k]) gsum += g[q];
+        const float p = ex2(fmaxf(fmaf(load1<D>(x + j), L2E, -op.c), U_FLOOR)) * (float)(1.0 / Z);
+        store1<D>(gx + j, gsum - (float)G * p);
+    }
+}
+
+template <class D>
+hipError_t kl1_dt(int rev, const Shard &sh, int64_t N, float *part_k, hipStream_t st) {
+    if (rev)
+        hipLaunchKernelGGL((k_kl1<D, true>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s, sh.t,
+                           sh.width, part_k);
+    else
+        hipLaunchKernelGGL((k_kl1<D, false>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s, sh.t,
+                           sh.width, part_k);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kl1(int dtype, int reverse, const Shard &sh, int64_t N, float *part_k,
+                      hipStream_t st) {
+    switch (dtype) {
+        case 0: return kl1_dt<F32>(reverse, sh, N, part_k, st);
+        case 1: return kl1_dt<F16>(reverse, sh, N, part_k, st);
+        default: return kl1_dt<BF16>(reverse, sh, N, part_k, st);
+    }
+}
+
+hipError_t launch_kl1_merge(int reverse, const float *part, int S, int64_t N, double *stats,
+                            float *kl, float *loss, hipStream_t st) {
+    hipLaunchKernelGGL(k_kl1_merge, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
+                       reverse, part, S, N, stats, kl, loss);
+    return hipGetLastError();
+}
+
+hipError_t launch_ent1(int dtype, const Shard &sh, int64_t N, float *part_k, hipStream_t st) {
+    const dim3 grid((unsigned)N), block(BLOCK);
+    switch (dtype) {
+        case 0: hipLaunchKernelGGL(k_ent1<F32>, grid, block, 0, st, sh.s, sh.width, part_k); break;
+        case 1: hipLaunchKernelGGL(k_ent1<F16>, grid, block, 0, st, sh.s, sh.width, part_k); break;
+        default: hipLaunchKernelGGL(k_ent1<BF16>, grid, block, 0, st, sh.s, sh.width, part_k);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_ent1_merge(const float *part, int S, int64_t N, double *stats, float *ent,
+                             hipStream_t st) {
+    hipLaunchKernelGGL(k_ent1_merge, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, part, S,
+                       N, stats, ent);
+    return hipGetLastError();
+}
+
+hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const double *stats,
+                          const float *ent, const float *grad, hipStream_t st) {
+    const dim3 grid((unsigned)N), block(BLOCK);
+    switch (dtype) {
+        case 0: hipLaunchKernelGGL(k_ent_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.width, stats, ent, grad); break;
+        case 1: hipLaunchKernelGGL(k_ent_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.width, stats, ent, grad); break;
+        default: hipLaunchKernelGGL(k_ent_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.width, stats, ent, grad);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N,
+                            int64_t vocab_global, const int64_t *ids, int K, int64_t ignore,
+                            const double *stats, float *out, int32_t *dev_err, hipStream_t st) {
+    const int64_t n = N * K;
+    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    const int f = first ? 1 : 0;
+    switch (dtype) {
+        case 0: hipLaunchKernelGGL(k_lp_gather<F32>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err); break;
+        case 1: hipLaunchKernelGGL(k_lp_gather<F16>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err); break;
+        default: hipLaunchKernelGGL(k_lp_gather<BF16>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, int64_t vocab_global,
+                         const double *stats, const int64_t *ids, int K, int64_t ignore,
+                         const float *grad, hipStream_t st) {
+    const dim3 grid((unsigned)N), block(BLOCK);
+    switch (dtype) {
+        case 0: hipLaunchKernelGGL(k_lp_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, vocab_global, stats, ids, K, ignore, grad); break;
+        case 1: hipLaunchKernelGGL(k_lp_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, vocab_global, stats, ids, K, ignore, grad); break;
+        default: hipLaunchKernelGGL(k_lp_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, vocab_global, stats, ids, K, ignore, grad);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace vjsd

@@ -1,0 +1,95 @@
+// sweep.hpp -- the row sweep every streaming kernel is built on.
+//
+// One workgroup owns one row of one shard.  The row is cut into a scalar head (up
+// to the first 16-byte boundary), a body of 16-byte vectors that consecutive lanes
+// read from consecutive addresses (a wave touches 1 KiB per load, U loads per input
+// in flight per lane) and a scalar tail.  The per-element work is an `Op` whose
+//     template <int NV, int W> void run(const float (&a)[NV][W],
+//                                       const float (&b)[NV][W],
+//                                       const int64_t (&col)[NV])
+// receives NV groups of W consecutive elements of the first and second input,
+// widened to fp32, starting at the given columns (W is the vector width, or 1 in
+// the head and tail).  One-input ops ignore `b`.
+#pragma once
+
+#include "device.hpp"
+
+namespace vjsd {
+
+template <class D, int U, bool TWO, class Op>
+__device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
+                                      const typename D::T *__restrict__ t, int64_t w, int64_t h,
+                                      Op &op) {
+    using T = typename D::T;
+    constexpr int VEC = D::VEC;
+    const int tid = threadIdx.x;
+    for (int64_t i = tid; i < h; i += BLOCK) {
+        float a[1][1], b[1][1] = {{0.0f}};
+        const int64_t c[1] = {i};
+        a[0][0] = load1<D>(s + i);
+        if (TWO) b[0][0] = load1<D>(t + i);
+        op.template run<1, 1>(a, b, c);
+    }
+    const int64_t nv = (w - h) / VEC;
+    const T *sb = s + h;
+    const T *tb = TWO ? t + h : s + h;
+    int64_t v = tid;
+    for (; v + (int64_t)(U - 1) * BLOCK < nv; v += (int64_t)U * BLOCK) {
+        float a[U][VEC], b[U][VEC];
+        int64_t c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t q = (v + (int64_t)u * BLOCK) * VEC;
+            c[u] = h + q;
+            load_vec<D>(sb + q, a[u]);
+            if (TWO) load_vec<D>(tb + q, b[u]);
+        }
+        op.template run<U, VEC>(a, b, c);
+    }
+    for (; v < nv; v += BLOCK) {
+        float a[1][VEC], b[1][VEC];
+        const int64_t q = v * VEC;
+        const int64_t c[1] = {h + q};
+        load_vec<D>(sb + q, a[0]);
+        if (TWO) load_vec<D>(tb + q, b[0]);
+        else
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) b[0][i] = 0.0f;
+        op.template run<1, VEC>(a, b, c);
+    }
+    for (int64_t i = h + nv * VEC + tid; i < w; i += BLOCK) {
+        float a[1][1], b[1][1] = {{0.0f}};
+        const int64_t c[1] = {i};
+        a[0][0] = load1<D>(s + i);
+        if (TWO) b[0][0] = load1<D>(t + i);
+        op.template run<1, 1>(a, b, c);
+    }
+}
+
+// Online (max, sum of 2^(x*L2E - c)) of one input over a batch of n elements: one
+// rescale per batch, a tree sum of the batch's exponentials.
+struct Online {
+    float m = NINF, c = 0.0f, z = 0.0f;
+
+    template <int N>
+    __device__ __forceinline__ void add(const float *x) {
+        float bm = x[0];
+#pragma unroll
+        for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
+        const float nm = fmaxf(m, bm);
+        const float nc = refc(nm);
+        const float scale = m == NINF ? 0.0f : ex2(c - nc);
+        float e[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) e[i] = ex2(fmaf(x[i], L2E, -nc));
+#pragma unroll
+        for (int st = N / 2; st >= 1; st /= 2)
+#pragma unroll
+            for (int i = 0; i < st; ++i) e[i] += e[i + st];
+        z = fmaf(z, scale, e[0]);
+        m = nm;
+        c = nc;
+    }
+};
+
+}  // namespace vjsd

@@ -1,0 +1,228 @@
+"""Autograd ops over libvjsd: per-token JSD, KL, entropy and log-probabilities.
+
+Page keys: [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel
+generalized JSD with Triton kernels"; [OPS-PR] DeepSpeed PR #8791 "Add
+vocabulary-parallel logprobs, entropy and KL ops".
+
+Logits are GPU tensors ``[N, V]`` or ``[B, T, V]`` (views with unit vocabulary
+stride, such as causal-shift slices, are taken without a copy), or a list of
+per-shard tensors ``[..., V_k]``; ``split`` cuts a whole tensor into logical
+vocabulary shards.  Outputs are fp32 per token, shaped like the leading
+dimensions.  Temperature, masking, reduction and T^2 scaling are the caller's
+[JSD-PR, Changes].  Only first-order gradients exist: a second backward raises
+[OPS-PR, Limitations].  Every step runs in libvjsd's HIP kernels.
+"""
+from __future__ import annotations
+
+import torch
+from torch.autograd.function import once_differentiable
+
+from . import _abi
+from ._abi import ShardSet
+
+__all__ = ["jsd", "kl_div", "entropy", "logprobs"]
+
+
+def _unpack(n_shards: int, tensors):
+    if n_shards == 0:
+        return tensors[0]
+    return list(tensors[:n_shards])
+
+
+def _grads_like(x, listed):
+    if listed:
+        return [torch.empty(t.shape, dtype=t.dtype, device=t.device) for t in x]
+    return torch.empty(x.shape, dtype=x.dtype, device=x.device)
+
+
+def _flat(g):
+    return g if isinstance(g, list) else [g]
+
+
+class _JSD(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, beta, split, n_shards, *tensors):
+        half = len(tensors) // 2
+        s = _unpack(n_shards, tensors[:half])
+        t = _unpack(n_shards, tensors[half:])
+        sh = ShardSet(s, t, widths=split)
+        dev = (s[0] if n_shards else s).device
+        N, S = sh.N, sh.S
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
+        loss = torch.empty((N,), dtype=torch.float32, device=dev)
+        _abi.vjsd_stats(sh, 3, part)
+        _abi.vjsd_merge(part, S, N, 3, stats)
+        _abi.vjsd_fwd(sh, stats, beta, part, kl, loss)
+        ctx.beta, ctx.split, ctx.n_shards = beta, split, n_shards
+        ctx.save_for_backward(stats, kl, *tensors)
+        return loss.view(sh.lead_shape)
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gloss):
+        stats, kl, *tensors = ctx.saved_tensors
+        half = len(tensors) // 2
+        n = ctx.n_shards
+        s = _unpack(n, tensors[:half])
+        t = _unpack(n, tensors[half:])
+        need = ctx.needs_input_grad[3:]
+        want_s, want_t = any(need[:half]), any(need[half:])
+        gs = _grads_like(s, bool(n)) if want_s else None
+        gt = _grads_like(t, bool(n)) if want_t else None
+        sh = ShardSet(s, t, widths=ctx.split, gs=gs, gt=gt)
+        g = gloss.reshape(-1).to(torch.float32).contiguous()
+        _abi.vjsd_bwd(sh, stats, kl, ctx.beta, g)
+        out_s = _flat(gs) if want_s else [None] * half
+        out_t = _flat(gt) if want_t else [None] * half
+        return (None, None, None, *out_s, *out_t)
+
+
+class _KL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, reverse, split, n_shards, *tensors):
+        half = len(tensors) // 2
+        s = _unpack(n_shards, tensors[:half])
+        t = _unpack(n_shards, tensors[half:])
+        sh = ShardSet(s, t, widths=split)
+        dev = (s[0] if n_shards else s).device
+        N, S = sh.N, sh.S
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
+        loss = torch.empty((N,), dtype=torch.float32, device=dev)
+        _abi.vkl_fwd(sh, reverse, part, stats, kl, loss)
+        ctx.reverse, ctx.split, ctx.n_shards = reverse, split, n_shards
+        ctx.save_for_backward(stats, kl, *tensors)
+        return loss.view(sh.lead_shape)
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gloss):
+        stats, kl, *tensors = ctx.saved_tensors
+        half = len(tensors) // 2
+        n = ctx.n_shards
+        s = _unpack(n, tensors[:half])
+        t = _unpack(n, tensors[half:])
+        need = ctx.needs_input_grad[3:]
+        want_s, want_t = any(need[:half]), any(need[half:])
+        gs = _grads_like(s, bool(n)) if want_s else None
+        gt = _grads_like(t, bool(n)) if want_t else None
+        sh = ShardSet(s, t, widths=ctx.split, gs=gs, gt=gt)
+        g = gloss.reshape(-1).to(torch.float32).contiguous()
+        _abi.vkl_bwd(sh, ctx.reverse, stats, kl, g)
+        out_s = _flat(gs) if want_s else [None] * half
+        out_t = _flat(gt) if want_t else [None] * half
+        return (None, None, None, *out_s, *out_t)
+
+
+class _Entropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, split, n_shards, *tensors):
+        x = _unpack(n_shards, tensors)
+        sh = ShardSet(x, widths=split)
+        dev = (x[0] if n_shards else x).device
+        N, S = sh.N, sh.S
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        ent = torch.empty((N,), dtype=torch.float32, device=dev)
+        _abi.ventropy_fwd(sh, part, stats, ent)
+        ctx.split, ctx.n_shards = split, n_shards
+        ctx.save_for_backward(stats, ent, *tensors)
+        return ent.view(sh.lead_shape)
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gent):
+        stats, ent, *tensors = ctx.saved_tensors
+        n = ctx.n_shards
+        x = _unpack(n, tensors)
+        gx = _grads_like(x, bool(n))
+        sh = ShardSet(x, widths=ctx.split, gs=gx)
+        _abi.ventropy_bwd(sh, stats, ent, gent.reshape(-1).to(torch.float32).contiguous())
+        return (None, None, *_flat(gx))
+
+
+class _Logprobs(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, ids, ignore_index, split, n_shards, *tensors):
+        x = _unpack(n_shards, tensors)
+        sh = ShardSet(x, widths=split)
+        dev = (x[0] if n_shards else x).device
+        N, S = sh.N, sh.S
+        K = ids.shape[-1]
+        idv = ids.reshape(N, K).to(torch.int64).contiguous()
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        out = torch.empty((N, K), dtype=torch.float32, device=dev)
+        err = torch.zeros((1,), dtype=torch.int32, device=dev)
+        _abi.vlogprobs_fwd(sh, sh.V, idv, ignore_index, part, stats, out, err)
+        # the range check runs every call; it needs this host synchronisation
+        if N and K and int(err.item()):
+            raise ValueError("logprobs: an index is outside [0, V) and is not ignore_index")
+        ctx.ignore_index, ctx.split, ctx.n_shards, ctx.V = ignore_index, split, n_shards, sh.V
+        ctx.save_for_backward(stats, idv, *tensors)
+        return out.view(*sh.lead_shape, K)
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gout):
+        stats, idv, *tensors = ctx.saved_tensors
+        n = ctx.n_shards
+        x = _unpack(n, tensors)
+        gx = _grads_like(x, bool(n))
+        sh = ShardSet(x, widths=ctx.split, gs=gx)
+        g = gout.reshape(idv.shape).to(torch.float32).contiguous()
+        _abi.vlogprobs_bwd(sh, ctx.V, stats, idv, ctx.ignore_index, g)
+        return (None, None, None, None, *_flat(gx))
+
+
+def _as_args(x):
+    if isinstance(x, (list, tuple)):
+        return len(x), list(x)
+    return 0, [x]
+
+
+def jsd(student, teacher, beta: float = 0.5, *, split=None) -> torch.Tensor:
+    """Per-token generalized JSD, fp32 [JSD-PR, Changes].
+
+    ``beta == 0`` is forward KL(teacher || student) and ``beta == 1`` reverse
+    KL(student || teacher), as explicit branches.  A teacher that does not require
+    grad gets none (the student-only backward).
+    """
+    beta = float(beta)
+    if not (0.0 <= beta <= 1.0):
+        raise ValueError("beta must be in [0, 1]")
+    ns, s = _as_args(student)
+    nt, t = _as_args(teacher)
+    if ns != nt or len(s) != len(t):
+        raise ValueError("student and teacher must be given the same way (tensor or shard list)")
+    return _JSD.apply(beta, None if split is None else tuple(split), ns, *s, *t)
+
+
+def kl_div(student, teacher, reverse: bool = False, *, split=None) -> torch.Tensor:
+    """Per-token KL(teacher || student), or KL(student || teacher) with ``reverse``
+    [OPS-PR, What]; the forward is a single input pass."""
+    ns, s = _as_args(student)
+    nt, t = _as_args(teacher)
+    if ns != nt or len(s) != len(t):
+        raise ValueError("student and teacher must be given the same way (tensor or shard list)")
+    return _KL.apply(bool(reverse), None if split is None else tuple(split), ns, *s, *t)
+
+
+def entropy(logits, *, split=None) -> torch.Tensor:
+    """Per-token entropy of softmax(logits) [OPS-PR, What]; single input pass."""
+    n, x = _as_args(logits)
+    return _Entropy.apply(None if split is None else tuple(split), n, *x)
+
+
+def logprobs(logits, index, *, ignore_index: int = -100, split=None) -> torch.Tensor:
+    """Log-probabilities of ``index`` (``[...]`` or top-k ``[..., K]``, global ids);
+    positions equal to ``ignore_index`` return exactly 0 [OPS-PR, What].  An index
+    outside the vocabulary raises ValueError after a host synchronisation."""
+    n, x = _as_args(logits)
+    single = index.dim() == (x[0].dim() - 1)
+    ids = index.unsqueeze(-1) if single else index
+    out = _Logprobs.apply(ids, int(ignore_index), None if split is None else tuple(split), n, *x)
+    return out.squeeze(-1) if single else out
