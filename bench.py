@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-token JSD hot path on one MI355X.
+
+One step is the whole JSD forward and backward over one batch, with inputs
+resident in HBM and outputs and workspace preallocated: paired statistics,
+on-device merge, divergence pass, closed-form backward with gradients to both
+inputs.  The workload is N=8192 tokens over a V=151936 vocabulary in bf16 with
+a per-column Zipf bias (the pages' Qwen2.5-sized vocabulary, B4 x ISL2048
+tokens); beta cycles through 0.1, 0.5, 0.9 from step to step.
+
+Printed: one JSON line with tokens/s, ms per step, the roofline of the dominant
+kernel (the backward), measured with HIP events on the stream the kernels run
+on, the fp64 CPU oracle's rate on a bounded sample of the same rows, and
+per-kernel and sibling-op timings (forward / reverse KL, entropy, top-k
+log-probabilities at N=16384, V=128256 in bf16 and fp16; the beta = 0 / 1 JSD
+branches).  The HBM traffic figure comes from committed rocprofv3 counters and
+is reported only while the kernel sources match the ones profiled.
+
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "JSD fwd+bwd tokens/s and HBM GB/s (% peak), N=8192 V=151936 bf16, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+CSRC = os.path.join(ROOT, "vocab_sharded_softmax_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def csrc_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-siblings", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="wall-clock budget of the oracle sample")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a plain 2 GiB device copy (counter calibration for rocprofv3)")
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream the library's
+    kernels are enqueued on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.spans = {}
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def add(self, name, a, b):
+        self.spans.setdefault(name, []).append((a, b))
+
+    def ms(self, name):
+        v = [a.elapsed_time(b) for a, b in self.spans.get(name, [])]
+        return sum(v) / len(v) if v else float("nan")
+
+
+def calib_copy(torch):
+    n = 1 << 31  # bytes
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 3}))
+
+
+def cpu_baseline(torch, s, t, gout, budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the timed rows."""
+    import numpy as np
+
+    import oracle
+
+    cores = oracle.num_threads()
+    chunk = 64
+    rows_done, elapsed, r0 = 0, 0.0, 0
+    N = s.shape[0]
+    while elapsed < budget_s and r0 < N:
+        rows = list(range(r0, min(N, r0 + chunk)))
+        sc, tc = s[rows].cpu(), t[rows].cpu()
+        g = gout[rows].cpu().double().numpy()
+        t0 = time.perf_counter()
+        oracle.jsd(sc, tc, 0.5, gout=g)
+        elapsed += time.perf_counter() - t0
+        rows_done += len(rows)
+        r0 += chunk
+    return {"value": rows_done / elapsed, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"JSD beta=0.5 fwd+bwd (loss and both gradients, fp64) of the first "
+                      f"{rows_done} of {N} rows of the same workload, {elapsed:.1f} s"}
+
+
+def traffic_entry(kernel_key):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("csrc_sha") != csrc_digest():
+        return None  # the kernels changed since the counters were taken
+    k = rec.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU: the op runs on one GPU's vocabulary shards with an "
+            f"on-device merge, and no multi-GPU path exists (asked for --gpus {args.gpus}).")
+        sys.exit(2)
+    import torch
+
+    if args.calib_copy:
+        calib_copy(torch)
+        return
+
+    import synth
+    import vocab_sharded_softmax_amd as vj
+
+    w = synth.WORKLOADS["full_vocab"]
+    N, V = w.N, w.V
+    log(f"drawing {w.name}: N={N} V={V} bf16")
+    b = synth.draw("full_vocab", device="cuda")
+    s, t, gout = b.s, b.t, b.gout
+    el = s.element_size()
+    part = vj.new_part(N, 1, "cuda")
+    stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
+    kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
+    loss = torch.empty((N,), dtype=torch.float32, device="cuda")
+    gs = torch.empty_like(s)
+    gt = torch.empty_like(t)
+    sh = vj.ShardSet(s, t)
+    shg = vj.ShardSet(s, t, gs=gs, gt=gt)
+    timer = Timer(torch)
+
+    def step(beta, rec):
+        e0 = timer.mark()
+        vj.vjsd_stats(sh, 3, part)
+        e1 = timer.mark()
+        vj.vjsd_merge(part, 1, N, 3, stats)
+        e2 = timer.mark()
+        vj.vjsd_fwd(sh, stats, beta, part, kl, loss)
+        e3 = timer.mark()
+        vj.vjsd_bwd(shg, stats, kl, beta, gout)
+        e4 = timer.mark()
+        if rec:
+            timer.add("stats", e0, e1)
+            timer.add("merge", e1, e2)
+            timer.add("div", e2, e3)
+            timer.add("bwd", e3, e4)
+            timer.add("step", e0, e4)
+            timer.add(f"step_beta{beta}", e0, e4)
+
+    betas = list(w.betas)
+    for i in range(args.warmup):
+        step(betas[i % 3], False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(betas[i % 3], True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    tensor_bytes = N * V * el
+    bytes_alg = 8 * tensor_bytes  # 3 input passes over s and t + 2 gradient writes
+    bytes_bwd = 4 * tensor_bytes  # read s, t; write gs, gt
+    bwd_ms = timer.ms("bwd")
+    achieved = bytes_bwd / (bwd_ms * 1e-3) / 1e9
+    per_kernel = {k: round(timer.ms(k), 4) for k in ("stats", "merge", "div", "bwd", "step")}
+    per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas}
+    log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
+
+    # the KL branches of the same engine on the same data
+    branches = {}
+    for beta in (0.0, 1.0):
+        for _ in range(2):
+            step(beta, False)
+        tm = Timer(torch)
+        for _ in range(5):
+            a = tm.mark()
+            vj.vjsd_stats(sh, 3, part)
+            vj.vjsd_merge(part, 1, N, 3, stats)
+            vj.vjsd_fwd(sh, stats, beta, part, kl, loss)
+            vj.vjsd_bwd(shg, stats, kl, beta, gout)
+            tm.add("x", a, tm.mark())
+        torch.cuda.synchronize()
+        branches[f"jsd_beta{beta:g}_fwd_bwd_ms"] = round(tm.ms("x"), 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample")
+        cpu = cpu_baseline(torch, s, t, gout, args.cpu_seconds)
+    del gs, gt, shg, sh, s, t, b
+    torch.cuda.empty_cache()
+
+    siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
+
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "full_vocab N=8192 V=151936 bf16 logits, Zipf column bias",
+                   "global_batch": N, "vocab": V, "storage_dtype": "bf16",
+                   "betas": betas, "grads": "student and teacher", "shards": 1},
+        "hbm_gbps": round(bytes_alg / (ms_step * 1e-3) / 1e9, 1),
+        "hbm_frac": round(bytes_alg / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "bytes_alg_per_step": bytes_alg,
+        "roofline": {"kernel": "k_bwd<BF16, interior, both grads>", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic_entry("bwd_bf16_interior_both"),
+                     "bytes_per_launch": bytes_bwd, "avg_launch_ms": round(bwd_ms, 4)},
+        "cpu_baseline": cpu,
+        "kernel_ms": per_kernel,
+        "step_ms_by_beta": per_beta,
+        "branches": branches,
+        "siblings": siblings,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def sibling_rows(torch, vj, synth, reps=3):
+    """Forward+backward of the sibling ops at N=16384, V=128256 (teacher detached)."""
+    res = {}
+    for dtype in (torch.bfloat16, torch.float16):
+        name = "bf16" if dtype == torch.bfloat16 else "fp16"
+        log(f"siblings {name}")
+        b = synth.draw("siblings", device="cuda", dtype=dtype)
+        N, V = b.s.shape
+        K = b.ids.shape[1]
+        tb = N * V * b.s.element_size()
+        part = vj.new_part(N, 1, "cuda")
+        stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
+        kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
+        loss = torch.empty((N,), dtype=torch.float32, device="cuda")
+        out = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        gs = torch.empty_like(b.s)
+        sh = vj.ShardSet(b.s, b.t)
+        shg = vj.ShardSet(b.s, b.t, gs=gs)
+        sx = vj.ShardSet(b.s)
+        sxg = vj.ShardSet(b.s, gs=gs)
+        ops = {
+            "fwd_kl": (lambda: (vj.vkl_fwd(sh, False, part, stats, kl, loss),
+                                vj.vkl_bwd(shg, False, stats, kl, b.gout)), 5 * tb),
+            "rev_kl": (lambda: (vj.vkl_fwd(sh, True, part, stats, kl, loss),
+                                vj.vkl_bwd(shg, True, stats, kl, b.gout)), 5 * tb),
+            "entropy": (lambda: (vj.ventropy_fwd(sx, part, stats, loss),
+                                 vj.ventropy_bwd(sxg, stats, loss, b.gout)), 3 * tb),
+            "logprobs_top20": (lambda: (vj.vlogprobs_fwd(sx, V, b.ids, -100, part, stats, out, err),
+                                        vj.vlogprobs_bwd(sxg, V, stats, b.ids, -100, b.gids)),
+                               3 * tb),
+        }
+        for op, (fn, nbytes) in ops.items():
+            fn()
+            tm = Timer(torch)
+            for _ in range(reps):
+                a = tm.mark()
+                fn()
+                tm.add("x", a, tm.mark())
+            torch.cuda.synchronize()
+            ms = tm.ms("x")
+            res[f"{op}_{name}"] = {"fwd_bwd_ms": round(ms, 4),
+                                   "tokens_per_s": round(N / (ms * 1e-3), 1),
+                                   "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del b, gs, sh, shg, sx, sxg
+        torch.cuda.empty_cache()
+    return res
+
+
+if __name__ == "__main__":
+    main()
