@@ -168,7 +168,7 @@ def main():
         e2 = timer.mark()
         vj.vjsd_fwd(sh, stats, beta, part, kl, loss)
         e3 = timer.mark()
-        vj.vjsd_bwd(shg, stats, kl, beta, gout)
+        vj.vjsd_bwd(shg, stats, kl, beta, gout, part)
         e4 = timer.mark()
         if rec:
             timer.add("stats", e0, e1)
@@ -209,7 +209,7 @@ def main():
             vj.vjsd_stats(sh, 3, part)
             vj.vjsd_merge(part, 1, N, 3, stats)
             vj.vjsd_fwd(sh, stats, beta, part, kl, loss)
-            vj.vjsd_bwd(shg, stats, kl, beta, gout)
+            vj.vjsd_bwd(shg, stats, kl, beta, gout, part)
             tm.add("x", a, tm.mark())
         torch.cuda.synchronize()
         branches[f"jsd_beta{beta:g}_fwd_bwd_ms"] = round(tm.ms("x"), 4)
@@ -279,13 +279,13 @@ def sibling_rows(torch, vj, synth, reps=3):
         sxg = vj.ShardSet(b.s, gs=gs)
         ops = {
             "fwd_kl": (lambda: (vj.vkl_fwd(sh, False, part, stats, kl, loss),
-                                vj.vkl_bwd(shg, False, stats, kl, b.gout)), 5 * tb),
+                                vj.vkl_bwd(shg, False, stats, kl, b.gout, part)), 5 * tb),
             "rev_kl": (lambda: (vj.vkl_fwd(sh, True, part, stats, kl, loss),
-                                vj.vkl_bwd(shg, True, stats, kl, b.gout)), 5 * tb),
+                                vj.vkl_bwd(shg, True, stats, kl, b.gout, part)), 5 * tb),
             "entropy": (lambda: (vj.ventropy_fwd(sx, part, stats, loss),
-                                 vj.ventropy_bwd(sxg, stats, loss, b.gout)), 3 * tb),
+                                 vj.ventropy_bwd(sxg, stats, loss, b.gout, part)), 3 * tb),
             "logprobs_top20": (lambda: (vj.vlogprobs_fwd(sx, V, b.ids, -100, part, stats, out, err),
-                                        vj.vlogprobs_bwd(sxg, V, stats, b.ids, -100, b.gids)),
+                                        vj.vlogprobs_bwd(sxg, V, stats, b.ids, -100, b.gids, part)),
                                3 * tb),
         }
         for op, (fn, nbytes) in ops.items():

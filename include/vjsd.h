@@ -45,8 +45,10 @@
  * m = -inf, lnZ = -inf.
  *
  * Workspace.  `part` is caller-owned device memory of vjsd_workspace_bytes(N, S)
- * bytes holding per-shard partial results between the launches of one call (and
- * between vjsd_stats and vjsd_merge).  Its contents are otherwise unspecified.
+ * bytes (16-byte aligned) holding per-row constants and per-shard partial results
+ * between the launches of one call, and between vjsd_stats and vjsd_merge.  Its
+ * contents are otherwise unspecified; calls that share one workspace must not
+ * overlap in time.
  *
  * Ownership and streams.  The caller owns every buffer.  The library allocates no
  * memory, keeps no state between calls and is reentrant; every call only enqueues
@@ -166,10 +168,11 @@ VJSD_API int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, con
  * written into each shard's gs / gt views; a NULL gs.p (gt.p) skips that gradient
  * (teacher or student detached) [JSD-PR, Changes].  A -inf logit's own term is 0.
  * In a row whose KL is +inf the target-side gradient is not finite.  Reads the
- * inputs, stats and kl of the forward.  This is the third input pass.
+ * inputs, stats and kl of the forward; `part` (workspace) receives per-row constants.
+ * This is the third input pass.
  */
 VJSD_API int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
-             const float *kl, double beta, const float *grad_loss, void *stream);
+             const float *kl, double beta, const float *grad_loss, float *part, void *stream);
 
 /*
  * KL divergence [OPS-PR, What]: KL(p_t || p_s), or KL(p_s || p_t) when reverse != 0,
@@ -183,7 +186,8 @@ VJSD_API int vkl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int 
 
 /* KL backward: vjsd_bwd at beta = 0 (reverse = 0) or beta = 1 (reverse != 0). */
 VJSD_API int vkl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse,
-            const double *stats, const float *kl, const float *grad_loss, void *stream);
+            const double *stats, const float *kl, const float *grad_loss, float *part,
+            void *stream);
 
 /*
  * Entropy [OPS-PR, What]: ent[r] = -sum_j p_j lp_j over the student view, single
@@ -194,7 +198,7 @@ VJSD_API int ventropy_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype,
 
 /* Entropy backward: d/dx_j = -g p_j (lp_j + H), into each shard's gs view. */
 VJSD_API int ventropy_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
-                 const float *ent, const float *grad, void *stream);
+                 const float *ent, const float *grad, float *part, void *stream);
 
 /*
  * Log-probabilities of K ids per row [OPS-PR, What]: out[r][k] = lp(ids[r][k]),
@@ -217,7 +221,7 @@ VJSD_API int vlogprobs_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype
  */
 VJSD_API int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
                   const double *stats, const int64_t *ids, int K, int64_t ignore_index,
-                  const float *grad, void *stream);
+                  const float *grad, float *part, void *stream);
 
 #ifdef __cplusplus
 }

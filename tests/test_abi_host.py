@@ -42,8 +42,11 @@ def test_strerror_and_workspace():
     for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert isinstance(lib.vjsd_strerror(code), bytes)
     assert lib.vjsd_workspace_bytes(0, 4) == 0
-    assert lib.vjsd_workspace_bytes(8192, 1) == 8192 * 8 * 4
-    assert lib.vjsd_workspace_bytes(4096, 4) == 4096 * 4 * 8 * 4
+    # per-row constants (16 floats) + per (shard, row) partials (8 floats)
+    assert lib.vjsd_workspace_bytes(8192, 1) == 8192 * (16 + 8) * 4
+    assert lib.vjsd_workspace_bytes(4096, 4) == 4096 * (16 + 4 * 8) * 4
+    for N, S in ((1, 1), (64, 3), (8192, 1), (16384, 7)):  # the binding sizes it the same way
+        assert abi.part_floats(N, S) * 4 == lib.vjsd_workspace_bytes(N, S)
 
 
 def shards(widths, ptr=FAKE, rs=None, start=0, es=2, grads=False):
@@ -68,7 +71,7 @@ def test_empty_batch_is_valid_and_enqueues_nothing():
     assert lib.vjsd_stats(a, 3, 0, 2, 3, None, None) == OK
     assert lib.vjsd_merge(None, 3, 0, 3, None, None) == OK
     assert fwd(a, 3, 0, stats=None, part=None, kl=None, loss=None) == OK
-    assert lib.vjsd_bwd(a, 3, 0, 2, None, None, 0.5, None, None) == OK
+    assert lib.vjsd_bwd(a, 3, 0, 2, None, None, 0.5, None, None, None) == OK
     assert lib.vkl_fwd(a, 3, 0, 2, 0, None, None, None, None, None) == OK
     assert lib.ventropy_fwd(a, 3, 0, 2, None, None, None, None) == OK
     b = shards([5, 7])
@@ -79,7 +82,7 @@ def test_empty_batch_is_valid_and_enqueues_nothing():
 def test_beta_outside_unit_interval_is_rejected(beta):
     a = shards([10])
     assert fwd(a, 1, 4, beta=beta) == BETA
-    assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, beta, FAKE, None) == BETA
+    assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, beta, FAKE, FAKE, None) == BETA
 
 
 def test_dtype_and_sizes_are_checked():
@@ -103,7 +106,8 @@ def test_null_buffers_are_rejected():
     assert lib.vjsd_stats(a, 1, 4, 2, 3, None, None) == ARG
     a2 = shards([5, 5])
     assert fwd(a2, 2, 4, part=None) == ARG  # several shards need the workspace
-    assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, 0.5, None, None) == ARG
+    assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, 0.5, None, FAKE, None) == ARG
+    assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, 0.5, FAKE, None, None) == ARG  # no workspace
     assert lib.vjsd_merge(None, 1, 4, 3, FAKE, None) == ARG
 
 
@@ -137,7 +141,7 @@ def test_shards_must_be_ordered_and_contiguous():
 def test_logprobs_rejects_empty_shards_and_bad_vocabulary():
     a = shards([5, 0, 7])
     assert lib.vlogprobs_fwd(a, 3, 4, 2, 12, FAKE, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == EMPTY
-    assert lib.vlogprobs_bwd(a, 3, 4, 2, 12, FAKE, FAKE, 3, -100, FAKE, None) == EMPTY
+    assert lib.vlogprobs_bwd(a, 3, 4, 2, 12, FAKE, FAKE, 3, -100, FAKE, FAKE, None) == EMPTY
     b = shards([5, 7])
     assert lib.vlogprobs_fwd(b, 2, 4, 2, 13, FAKE, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == LAYOUT
     c = shards([5, 7], start=1)
@@ -151,9 +155,10 @@ def test_entropy_and_kl_check_their_arguments():
     a = shards([10])
     assert lib.ventropy_fwd(a, 1, 4, 7, FAKE, FAKE, FAKE, None) == DTYPE
     assert lib.ventropy_fwd(a, 1, 4, 2, None, FAKE, FAKE, None) == ARG
-    assert lib.ventropy_bwd(a, 1, 4, 2, FAKE, FAKE, None, None) == ARG
+    assert lib.ventropy_bwd(a, 1, 4, 2, FAKE, FAKE, None, FAKE, None) == ARG
+    assert lib.ventropy_bwd(a, 1, 4, 2, FAKE, FAKE, FAKE, None, None) == ARG
     assert lib.vkl_fwd(a, 1, 4, 2, 1, FAKE, FAKE, None, FAKE, None) == ARG
-    assert lib.vkl_bwd(a, 1, 4, 2, 1, FAKE, FAKE, None, None) == ARG
+    assert lib.vkl_bwd(a, 1, 4, 2, 1, FAKE, FAKE, None, FAKE, None) == ARG
 
 
 def test_default_split_matches_the_pages_uneven_example():

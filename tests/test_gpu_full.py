@@ -35,7 +35,7 @@ def jsd_all(s, t, beta, widths=None, gout=None, want_t=True):
     v.vjsd_fwd(sh, stats, beta, part, kl, loss)
     gs = torch.empty_like(s)
     gt = torch.empty_like(t) if want_t else None
-    v.vjsd_bwd(v.ShardSet(s, t, widths=widths, gs=gs, gt=gt), stats, kl, beta, gout)
+    v.vjsd_bwd(v.ShardSet(s, t, widths=widths, gs=gs, gt=gt), stats, kl, beta, gout, part)
     torch.cuda.synchronize()
     return stats, kl, loss, gs, gt
 
@@ -121,7 +121,7 @@ def test_siblings_full_size(dtype):
         loss = torch.empty(N, device="cuda")
         v.vkl_fwd(sh, reverse, part, stats, kl, loss)
         gs = torch.empty_like(b.s)
-        v.vkl_bwd(v.ShardSet(b.s, b.t, gs=gs), reverse, stats, kl, b.gout)
+        v.vkl_bwd(v.ShardSet(b.s, b.t, gs=gs), reverse, stats, kl, b.gout, part)
         torch.cuda.synchronize()
         ref = oracle.kl_div(sc, tc, reverse=reverse, gout=g)
         assert_values(loss[rows].cpu(), ref["loss"], dtype, "KL")
@@ -135,7 +135,7 @@ def test_siblings_full_size(dtype):
     sh = v.ShardSet(b.s)
     v.ventropy_fwd(sh, part, stats, ent)
     gx = torch.empty_like(b.s)
-    v.ventropy_bwd(v.ShardSet(b.s, gs=gx), stats, ent, b.gout)
+    v.ventropy_bwd(v.ShardSet(b.s, gs=gx), stats, ent, b.gout, part)
     torch.cuda.synchronize()
     ref = oracle.entropy(sc, gout=g)
     assert_values(ent[rows].cpu(), ref["ent"], dtype, "entropy")
@@ -147,7 +147,7 @@ def test_siblings_full_size(dtype):
     out = torch.empty((N, K), device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     v.vlogprobs_fwd(sh, V, b.ids, -100, part, stats, out, err)
-    v.vlogprobs_bwd(v.ShardSet(b.s, gs=gx), V, stats, b.ids, -100, b.gids)
+    v.vlogprobs_bwd(v.ShardSet(b.s, gs=gx), V, stats, b.ids, -100, b.gids, part)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     ids_r = b.ids[rows].cpu().numpy()

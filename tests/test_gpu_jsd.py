@@ -44,7 +44,7 @@ def run_jsd(s, t, beta, widths=None, gout=None, want_s=True, want_t=True):
     if gout is None:
         gout = torch.ones(N, device=dev)
     shg = v.ShardSet(s, t, widths=widths, gs=gs, gt=gt)
-    v.vjsd_bwd(shg, stats, kl, beta, gout)
+    v.vjsd_bwd(shg, stats, kl, beta, gout, part)
     torch.cuda.synchronize()
     return dict(stats=stats.cpu(), kl=kl.cpu(), loss=loss.cpu(),
                 gs=None if gs is None else gs.cpu(), gt=None if gt is None else gt.cpu())

@@ -30,7 +30,7 @@ def run_kl(s, t, reverse, widths=None, gout=None, want_t=False):
     gs = torch.full_like(s, float("nan"))
     gt = torch.full_like(t, float("nan")) if want_t else None
     gout = torch.ones(N, device=s.device) if gout is None else gout
-    v.vkl_bwd(v.ShardSet(s, t, widths=widths, gs=gs, gt=gt), reverse, stats, kl, gout)
+    v.vkl_bwd(v.ShardSet(s, t, widths=widths, gs=gs, gt=gt), reverse, stats, kl, gout, part)
     torch.cuda.synchronize()
     return dict(stats=stats.cpu(), kl=kl.cpu(), loss=loss.cpu(), gs=gs.cpu(),
                 gt=None if gt is None else gt.cpu())
@@ -110,7 +110,7 @@ def run_entropy(x, widths=None, gout=None):
     v.ventropy_fwd(sh, part, stats, ent)
     gx = torch.full_like(x, float("nan"))
     gout = torch.ones(N, device=x.device) if gout is None else gout
-    v.ventropy_bwd(v.ShardSet(x, widths=widths, gs=gx), stats, ent, gout)
+    v.ventropy_bwd(v.ShardSet(x, widths=widths, gs=gx), stats, ent, gout, part)
     torch.cuda.synchronize()
     return dict(stats=stats.cpu(), ent=ent.cpu(), gx=gx.cpu())
 
@@ -159,7 +159,7 @@ def run_logprobs(x, ids, ignore=-100, widths=None, gout=None):
     v.vlogprobs_fwd(sh, sh.V, ids, ignore, part, stats, out, err)
     gx = torch.full_like(x, float("nan"))
     gout = torch.ones((N, K), device=x.device) if gout is None else gout
-    v.vlogprobs_bwd(v.ShardSet(x, widths=widths, gs=gx), sh.V, stats, ids, ignore, gout)
+    v.vlogprobs_bwd(v.ShardSet(x, widths=widths, gs=gx), sh.V, stats, ids, ignore, gout, part)
     torch.cuda.synchronize()
     return dict(stats=stats.cpu(), out=out.cpu(), gx=gx.cpu(), err=int(err.item()))
 

@@ -20,7 +20,8 @@ VJSD_OK = 0
 ERRORS = {-1: "ERR_ARG", -2: "ERR_DTYPE", -3: "ERR_BETA", -4: "ERR_LAYOUT",
           -5: "ERR_EMPTY_SHARD", -6: "ERR_HIP"}
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-PART_FLOATS = 8
+ROWC_FLOATS = 16  # per-row constants at the head of the workspace
+PART_FLOATS = 8  # per (shard, row) partials after them
 
 
 class VjsdError(RuntimeError):
@@ -56,13 +57,13 @@ def _load():
         "vjsd_stats": ([SP, I, I64, I, I, P, P], I),
         "vjsd_merge": ([P, I, I64, I, P, P], I),
         "vjsd_fwd": ([SP, I, I64, I, P, D, P, P, P, P], I),
-        "vjsd_bwd": ([SP, I, I64, I, P, P, D, P, P], I),
+        "vjsd_bwd": ([SP, I, I64, I, P, P, D, P, P, P], I),
         "vkl_fwd": ([SP, I, I64, I, I, P, P, P, P, P], I),
-        "vkl_bwd": ([SP, I, I64, I, I, P, P, P, P], I),
+        "vkl_bwd": ([SP, I, I64, I, I, P, P, P, P, P], I),
         "ventropy_fwd": ([SP, I, I64, I, P, P, P, P], I),
-        "ventropy_bwd": ([SP, I, I64, I, P, P, P, P], I),
+        "ventropy_bwd": ([SP, I, I64, I, P, P, P, P, P], I),
         "vlogprobs_fwd": ([SP, I, I64, I, I64, P, I, I64, P, P, P, P, P], I),
-        "vlogprobs_bwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P], I),
+        "vlogprobs_bwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -86,13 +87,17 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _require_gpu(x: torch.Tensor, name: str) -> None:
+    if not x.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
 def _ptr(x: torch.Tensor | None, dtype=None, numel=None, name="buffer"):
     if x is None:
         return None
     if dtype is not None and x.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
-    if not x.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+    _require_gpu(x, name)
     if not x.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if numel is not None and x.numel() < numel:
@@ -104,8 +109,7 @@ def _view(x: torch.Tensor | None) -> tuple[View, int]:
     """View of a [N, w] or [B, T, w] tensor with unit column stride; returns (view, N)."""
     if x is None:
         return View(None, 0, 0, 0), -1
-    if not x.is_cuda:
-        raise ValueError("logits and gradients must be GPU tensors")
+    _require_gpu(x, "logits and gradients")
     w = x.shape[-1]
     if x.dim() == 2:
         rs = x.stride(0)
@@ -190,67 +194,76 @@ def vjsd_workspace_bytes(N: int, S: int) -> int:
     return lib.vjsd_workspace_bytes(N, S)
 
 
+def part_floats(N: int, S: int) -> int:
+    return N * ROWC_FLOATS + N * S * PART_FLOATS
+
+
 def new_part(N: int, S: int, device) -> torch.Tensor:
-    return torch.empty(max(1, N * S * PART_FLOATS), dtype=torch.float32, device=device)
+    """Workspace of vjsd_workspace_bytes(N, S) bytes."""
+    return torch.empty(max(1, part_floats(N, S)), dtype=torch.float32, device=device)
 
 
 def vjsd_stats(sh: ShardSet, which: int, part, stream=None) -> None:
     _check(lib.vjsd_stats(sh.arr, sh.S, sh.N, sh.dtype_code, which,
-                          _ptr(part, torch.float32, sh.N * sh.S * PART_FLOATS, "part"),
+                          _ptr(part, torch.float32, part_floats(sh.N, sh.S), "part"),
                           _stream(stream)))
 
 
 def vjsd_merge(part, S: int, N: int, which: int, stats, stream=None) -> None:
-    _check(lib.vjsd_merge(_ptr(part, torch.float32, N * S * PART_FLOATS, "part"), S, N, which,
+    _check(lib.vjsd_merge(_ptr(part, torch.float32, part_floats(N, S), "part"), S, N, which,
                           _ptr(stats, torch.float64, N * 4, "stats"), _stream(stream)))
 
 
 def vjsd_fwd(sh: ShardSet, stats, beta: float, part, kl, loss, stream=None) -> None:
     N = sh.N
     _check(lib.vjsd_fwd(sh.arr, sh.S, N, sh.dtype_code, _ptr(stats, torch.float64, N * 4, "stats"),
-                        float(beta), _ptr(part, torch.float32, N * sh.S * PART_FLOATS, "part"),
+                        float(beta), _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
                         _ptr(kl, torch.float32, N * 2, "kl"), _ptr(loss, torch.float32, N, "loss"),
                         _stream(stream)))
 
 
-def vjsd_bwd(sh: ShardSet, stats, kl, beta: float, grad_loss, stream=None) -> None:
+def vjsd_bwd(sh: ShardSet, stats, kl, beta: float, grad_loss, part, stream=None) -> None:
     N = sh.N
     _check(lib.vjsd_bwd(sh.arr, sh.S, N, sh.dtype_code, _ptr(stats, torch.float64, N * 4, "stats"),
                         _ptr(kl, torch.float32, N * 2, "kl"), float(beta),
-                        _ptr(grad_loss, torch.float32, N, "grad_loss"), _stream(stream)))
+                        _ptr(grad_loss, torch.float32, N, "grad_loss"),
+                        _ptr(part, torch.float32, part_floats(N, sh.S), "part"), _stream(stream)))
 
 
 def vkl_fwd(sh: ShardSet, reverse: bool, part, stats, kl, loss, stream=None) -> None:
     N = sh.N
     _check(lib.vkl_fwd(sh.arr, sh.S, N, sh.dtype_code, int(bool(reverse)),
-                       _ptr(part, torch.float32, N * sh.S * PART_FLOATS, "part"),
+                       _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
                        _ptr(stats, torch.float64, N * 4, "stats"),
                        _ptr(kl, torch.float32, N * 2, "kl"), _ptr(loss, torch.float32, N, "loss"),
                        _stream(stream)))
 
 
-def vkl_bwd(sh: ShardSet, reverse: bool, stats, kl, grad_loss, stream=None) -> None:
+def vkl_bwd(sh: ShardSet, reverse: bool, stats, kl, grad_loss, part, stream=None) -> None:
     N = sh.N
     _check(lib.vkl_bwd(sh.arr, sh.S, N, sh.dtype_code, int(bool(reverse)),
                        _ptr(stats, torch.float64, N * 4, "stats"),
                        _ptr(kl, torch.float32, N * 2, "kl"),
-                       _ptr(grad_loss, torch.float32, N, "grad_loss"), _stream(stream)))
+                       _ptr(grad_loss, torch.float32, N, "grad_loss"),
+                       _ptr(part, torch.float32, part_floats(N, sh.S), "part"), _stream(stream)))
 
 
 def ventropy_fwd(sh: ShardSet, part, stats, ent, stream=None) -> None:
     N = sh.N
     _check(lib.ventropy_fwd(sh.arr, sh.S, N, sh.dtype_code,
-                            _ptr(part, torch.float32, N * sh.S * PART_FLOATS, "part"),
+                            _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
                             _ptr(stats, torch.float64, N * 4, "stats"),
                             _ptr(ent, torch.float32, N, "ent"), _stream(stream)))
 
 
-def ventropy_bwd(sh: ShardSet, stats, ent, grad, stream=None) -> None:
+def ventropy_bwd(sh: ShardSet, stats, ent, grad, part, stream=None) -> None:
     N = sh.N
     _check(lib.ventropy_bwd(sh.arr, sh.S, N, sh.dtype_code,
                             _ptr(stats, torch.float64, N * 4, "stats"),
                             _ptr(ent, torch.float32, N, "ent"),
-                            _ptr(grad, torch.float32, N, "grad"), _stream(stream)))
+                            _ptr(grad, torch.float32, N, "grad"),
+                            _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                            _stream(stream)))
 
 
 def vlogprobs_fwd(sh: ShardSet, vocab_global: int, ids, ignore_index: int, part, stats, out,
@@ -259,17 +272,19 @@ def vlogprobs_fwd(sh: ShardSet, vocab_global: int, ids, ignore_index: int, part,
     K = ids.shape[-1] if ids is not None and ids.dim() else 0
     _check(lib.vlogprobs_fwd(sh.arr, sh.S, N, sh.dtype_code, int(vocab_global),
                              _ptr(ids, torch.int64, N * K, "ids"), K, int(ignore_index),
-                             _ptr(part, torch.float32, N * sh.S * PART_FLOATS, "part"),
+                             _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
                              _ptr(stats, torch.float64, N * 4, "stats"),
                              _ptr(out, torch.float32, N * K, "out"),
                              _ptr(dev_err, torch.int32, 1, "dev_err"), _stream(stream)))
 
 
-def vlogprobs_bwd(sh: ShardSet, vocab_global: int, stats, ids, ignore_index: int, grad,
+def vlogprobs_bwd(sh: ShardSet, vocab_global: int, stats, ids, ignore_index: int, grad, part,
                   stream=None) -> None:
     N = sh.N
     K = ids.shape[-1] if ids is not None and ids.dim() else 0
     _check(lib.vlogprobs_bwd(sh.arr, sh.S, N, sh.dtype_code, int(vocab_global),
                              _ptr(stats, torch.float64, N * 4, "stats"),
                              _ptr(ids, torch.int64, N * K, "ids"), K, int(ignore_index),
-                             _ptr(grad, torch.float32, N * K, "grad"), _stream(stream)))
+                             _ptr(grad, torch.float32, N * K, "grad"),
+                             _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                             _stream(stream)))

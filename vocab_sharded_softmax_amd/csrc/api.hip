@@ -82,8 +82,12 @@ Shard convert(const vjsd_shard &h, bool two, bool grads) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VJSD_OK : VJSD_ERR_HIP; }
 
+// Workspace: N * ROWC floats of per-row constants, then S * N * PART_STRIDE partials.
 float *part_of(float *part, int k, int64_t N) {
-    return part + (size_t)k * (size_t)N * vjsd::PART_STRIDE;
+    return part + (size_t)N * vjsd::ROWC + (size_t)k * (size_t)N * vjsd::PART_STRIDE;
+}
+const float *part_of(const float *part, int k, int64_t N) {
+    return part + (size_t)N * vjsd::ROWC + (size_t)k * (size_t)N * vjsd::PART_STRIDE;
 }
 
 int mode_of(double beta) {
@@ -109,7 +113,7 @@ const char *vjsd_strerror(int code) {
 
 size_t vjsd_workspace_bytes(int64_t N, int S) {
     if (N <= 0 || S <= 0) return 0;
-    return (size_t)N * (size_t)S * vjsd::PART_STRIDE * sizeof(float);
+    return ((size_t)N * vjsd::ROWC + (size_t)N * (size_t)S * vjsd::PART_STRIDE) * sizeof(float);
 }
 
 int vjsd_stats(const vjsd_shard *shards, int S, int64_t N, int dtype, int which, float *part,
@@ -142,7 +146,8 @@ int vjsd_merge(const float *part, int S, int64_t N, int which, double *stats, vo
         return VJSD_ERR_ARG;
     if (N == 0) return VJSD_OK;
     if (!part || !stats) return VJSD_ERR_ARG;
-    return hip_status(vjsd::launch_merge(part, S, N, which, stats, (hipStream_t)stream));
+    return hip_status(
+        vjsd::launch_merge(part_of(part, 0, N), S, N, which, stats, (hipStream_t)stream));
 }
 
 int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
@@ -165,23 +170,25 @@ int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double
                                              nullptr, nullptr, st))))
             return e;
     }
-    return hip_status(vjsd::launch_div_finalize(mode, part, S, N, stats, beta, kl, loss, st));
+    return hip_status(
+        vjsd::launch_div_finalize(mode, part_of(part, 0, N), S, N, stats, beta, kl, loss, st));
 }
 
 int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
-             const float *kl, double beta, const float *grad_loss, void *stream) {
+             const float *kl, double beta, const float *grad_loss, float *part, void *stream) {
     int e = check_common(shards, S, N, dtype);
     if (e) return e;
     if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
     if ((e = check_views(shards, S, N, dtype, true, true))) return e;
     if (N == 0) return VJSD_OK;
-    if (!stats || !kl || !grad_loss) return VJSD_ERR_ARG;
+    if (!stats || !kl || !grad_loss || !part) return VJSD_ERR_ARG;
     const int mode = mode_of(beta);
+    hipStream_t st = (hipStream_t)stream;
+    if ((e = hip_status(vjsd::launch_bwd_prep(mode, N, stats, kl, beta, grad_loss, part, st))))
+        return e;
     for (int k = 0; k < S; ++k) {
         Shard sh = convert(shards[k], true, true);
-        if ((e = hip_status(vjsd::launch_bwd(dtype, mode, sh, N, stats, kl, beta, grad_loss,
-                                             (hipStream_t)stream))))
-            return e;
+        if ((e = hip_status(vjsd::launch_bwd(dtype, mode, sh, N, part, st)))) return e;
     }
     return VJSD_OK;
 }
@@ -199,12 +206,14 @@ int vkl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse, 
         if ((e = hip_status(vjsd::launch_kl1(dtype, reverse != 0, sh, N, part_of(part, k, N), st))))
             return e;
     }
-    return hip_status(vjsd::launch_kl1_merge(reverse != 0, part, S, N, stats, kl, loss, st));
+    return hip_status(
+        vjsd::launch_kl1_merge(reverse != 0, part_of(part, 0, N), S, N, stats, kl, loss, st));
 }
 
 int vkl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse,
-            const double *stats, const float *kl, const float *grad_loss, void *stream) {
-    return vjsd_bwd(shards, S, N, dtype, stats, kl, reverse ? 1.0 : 0.0, grad_loss, stream);
+            const double *stats, const float *kl, const float *grad_loss, float *part,
+            void *stream) {
+    return vjsd_bwd(shards, S, N, dtype, stats, kl, reverse ? 1.0 : 0.0, grad_loss, part, stream);
 }
 
 int ventropy_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, float *part,
@@ -219,22 +228,22 @@ int ventropy_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, float *p
         Shard sh = convert(shards[k], false, false);
         if ((e = hip_status(vjsd::launch_ent1(dtype, sh, N, part_of(part, k, N), st)))) return e;
     }
-    return hip_status(vjsd::launch_ent1_merge(part, S, N, stats, ent, st));
+    return hip_status(vjsd::launch_ent1_merge(part_of(part, 0, N), S, N, stats, ent, st));
 }
 
 int ventropy_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
-                 const float *ent, const float *grad, void *stream) {
+                 const float *ent, const float *grad, float *part, void *stream) {
     int e = check_common(shards, S, N, dtype);
     if (e) return e;
     if ((e = check_views(shards, S, N, dtype, false, true))) return e;
     if (N == 0) return VJSD_OK;
-    if (!stats || !ent || !grad) return VJSD_ERR_ARG;
+    if (!stats || !ent || !grad || !part) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if ((e = hip_status(vjsd::launch_ent_bwd_prep(N, stats, ent, grad, part, st)))) return e;
     for (int k = 0; k < S; ++k) {
         if (!shards[k].gs.p) continue;
         Shard sh = convert(shards[k], false, true);
-        if ((e = hip_status(vjsd::launch_ent_bwd(dtype, sh, N, stats, ent, grad,
-                                                 (hipStream_t)stream))))
-            return e;
+        if ((e = hip_status(vjsd::launch_ent_bwd(dtype, sh, N, part, st)))) return e;
     }
     return VJSD_OK;
 }
@@ -266,7 +275,7 @@ int vlogprobs_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t
         Shard sh = convert(shards[k], false, false);
         if ((e = hip_status(vjsd::launch_stats(dtype, 1, sh, N, part_of(part, k, N), st)))) return e;
     }
-    if ((e = hip_status(vjsd::launch_merge(part, S, N, 1, stats, st)))) return e;
+    if ((e = hip_status(vjsd::launch_merge(part_of(part, 0, N), S, N, 1, stats, st)))) return e;
     if (K == 0) return VJSD_OK;
     for (int k0 = 0; k0 < S; k0 += vjsd::LP_TABLE) {
         vjsd::LpTable tab;
@@ -287,17 +296,21 @@ int vlogprobs_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t
 
 int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
                   const double *stats, const int64_t *ids, int K, int64_t ignore_index,
-                  const float *grad, void *stream) {
+                  const float *grad, float *part, void *stream) {
     int e = check_logprobs(shards, S, N, dtype, vocab_global, ids, K);
     if (e) return e;
     if ((e = check_views(shards, S, N, dtype, false, true))) return e;
     if (N == 0) return VJSD_OK;
-    if (!stats || (K > 0 && !grad)) return VJSD_ERR_ARG;
+    if (!stats || !part || (K > 0 && !grad)) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if ((e = hip_status(vjsd::launch_lp_bwd_prep(N, vocab_global, stats, ids, K, ignore_index,
+                                                 grad, part, st))))
+        return e;
     for (int k = 0; k < S; ++k) {
         if (!shards[k].gs.p) continue;
         Shard sh = convert(shards[k], false, true);
-        if ((e = hip_status(vjsd::launch_lp_bwd(dtype, sh, N, vocab_global, stats, ids, K,
-                                                ignore_index, grad, (hipStream_t)stream))))
+        if ((e = hip_status(vjsd::launch_lp_bwd(dtype, sh, N, ids, K, ignore_index, grad, part,
+                                                st))))
             return e;
     }
     return VJSD_OK;

@@ -31,7 +31,14 @@ constexpr float U_FLOOR = -512.0f;
 // Added inside the mixture so log2 never sees 0 (both sides underflowed or masked);
 // 2^-126 is far below any mass that can move an fp32 result.
 constexpr float W_FLOOR = 1.17549435e-38f;
-constexpr int PART_STRIDE = 8;  // floats per (shard, row) in the workspace
+// Workspace layout: per-row constants (ROWC floats per row) for the streaming
+// backward kernels, then per-(shard, row) partials (PART_STRIDE floats each).
+constexpr int ROWC = 16;
+constexpr int PART_STRIDE = 8;
+constexpr int ROWC_UNDEFINED = 15;  // slot holding 1.0f for a row with no distribution
+// Streaming gradient kernels: one wave per workgroup, each lane one 16-byte vector of
+// a row chunk, consecutive workgroups on consecutive chunks of a row.
+constexpr int GRAD_BLOCK = 64;
 
 // ---- storage formats -------------------------------------------------------------
 

@@ -212,67 +212,79 @@ struct OpBwd {
     }
 };
 
-template <class D>
-__device__ __forceinline__ void zero_row(typename D::T *p, int64_t w) {
-    if (!p) return;
-    const int64_t h = head_len<typename D::T>(w, p);
-    for (int64_t i = threadIdx.x; i < h; i += BLOCK) store1<D>(p + i, 0.0f);
-    const int64_t nv = (w - h) / D::VEC;
-    float z[D::VEC];
-#pragma unroll
-    for (int i = 0; i < D::VEC; ++i) z[i] = 0.0f;
-    for (int64_t v = threadIdx.x; v < nv; v += BLOCK) store_vec<D>(p + h + v * D::VEC, z);
-    for (int64_t i = h + nv * D::VEC + threadIdx.x; i < w; i += BLOCK) store1<D>(p + i, 0.0f);
-}
-
-template <class D, int MODE, bool WS, bool WT>
-__global__ __launch_bounds__(BLOCK) void k_bwd(RowView sv, RowView tv, RowMView gsv,
-                                               RowMView gtv, int64_t w,
-                                               const double *__restrict__ stats,
-                                               const float *__restrict__ kl, double beta,
-                                               const float *__restrict__ grad) {
-    using T = typename D::T;
-    const int64_t r = blockIdx.x;
-    if (w == 0) return;
-    T *gs = WS ? row_ptr<T>(gsv, r) : nullptr;
-    T *gt = WT ? row_ptr<T>(gtv, r) : nullptr;
+// Per-row constants of the backward, computed once per call from the fp64 statistics:
+// rowc[r*ROWC + i] = cs, ct, beta, gamma, Cs, Ct, Hs, Ht, Gs, Gt (i = 0..9) and the
+// undefined-row flag in slot ROWC_UNDEFINED.
+__global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats,
+                           const float *__restrict__ kl, double beta,
+                           const float *__restrict__ grad, float *__restrict__ rowc) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= N) return;
     const RowConst k = row_const(stats, r);
-    if (k.undefined) {  // no distribution: exactly zero gradient whatever g is
-        if (WS) zero_row<D>(gs, w);
-        if (WT) zero_row<D>(gt, w);
-        return;
-    }
-    const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const double g = grad[r];
     const double KT2 = (double)kl[2 * r] * L2E_D, KS2 = (double)kl[2 * r + 1] * L2E_D;
+    double Cs = 0.0, Ct = 0.0, Hs = 0.0, Ht = 0.0;
+    if (mode == INTERIOR) {
+        Cs = g * (1.0 - beta) * LN2_D / k.Zs;
+        Ct = g * beta * LN2_D / k.Zt;
+        Hs = k.r + KS2;
+        Ht = KT2;
+    } else if (mode == FWD_KL) {  // d/dt = g p_t (lp_t - lp_s - KT), lp2_t - lp2_s = u_t - u_s + r
+        Ct = g * LN2_D / k.Zt;
+        Ht = KT2 - k.r;
+    } else {  // d/ds = g p_s (lp_s - lp_t - KS), lp2_s - lp2_t = u_s - u_t - r
+        Cs = g * LN2_D / k.Zs;
+        Hs = KS2 + k.r;
+    }
+    float *o = rowc + r * ROWC;
+    o[0] = k.cs;
+    o[1] = k.ct;
+    o[2] = (float)beta;
+    o[3] = (float)((1.0 - beta) * k.Zt / k.Zs);
+    o[4] = (float)Cs;
+    o[5] = (float)Ct;
+    o[6] = (float)Hs;
+    o[7] = (float)Ht;
+    o[8] = (float)(g / k.Zs);
+    o[9] = (float)(g / k.Zt);
+    o[ROWC_UNDEFINED] = k.undefined ? 1.0f : 0.0f;
+}
+
+// One wave per row chunk of cw columns; the chunks of a row are consecutive workgroups,
+// so the whole grid streams through memory in order.
+template <class D, int MODE, bool WS, bool WT>
+__global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowMView gsv,
+                                                    RowMView gtv, int64_t w, int64_t cw,
+                                                    int64_t nchunk, const float *__restrict__ rowc) {
+    using T = typename D::T;
+    const int64_t b = blockIdx.x;
+    const int64_t r = b / nchunk;
+    const int64_t c0 = (b - r * nchunk) * cw;
+    const int64_t n = w - c0 < cw ? w - c0 : cw;
+    const float *k = rowc + r * ROWC;
+    T *gs = WS ? row_ptr<T>(gsv, r) + c0 : nullptr;
+    T *gt = WT ? row_ptr<T>(gtv, r) + c0 : nullptr;
+    if (k[ROWC_UNDEFINED] != 0.0f) {  // no distribution: exactly zero gradient whatever g is
+        if (WS) zero_span<D, GRAD_BLOCK>(gs, n);
+        if (WT) zero_span<D, GRAD_BLOCK>(gt, n);
+        return;
+    }
+    const T *s = row_ptr<T>(sv, r) + c0, *t = row_ptr<T>(tv, r) + c0;
     OpBwd<D, MODE, WS, WT> op;
     op.gs = gs;
     op.gt = gt;
-    op.cs = k.cs;
-    op.ct = k.ct;
-    op.bf = (float)beta;
-    op.gam = (float)((1.0 - beta) * k.Zt / k.Zs);
-    op.Gs = (float)(g / k.Zs);
-    op.Gt = (float)(g / k.Zt);
-    if (MODE == INTERIOR) {
-        op.Cs = (float)(g * (1.0 - beta) * LN2_D / k.Zs);
-        op.Ct = (float)(g * beta * LN2_D / k.Zt);
-        op.Hs = (float)(k.r + KS2);
-        op.Ht = (float)KT2;
-    } else if (MODE == FWD_KL) {  // d/dt = g p_t (lp_t - lp_s - KT), lp2_t - lp2_s = u_t - u_s + r
-        op.Ct = (float)(g * LN2_D / k.Zt);
-        op.Ht = (float)(KT2 - k.r);
-        op.Cs = 0.0f;
-        op.Hs = 0.0f;
-    } else {  // d/ds = g p_s (lp_s - lp_t - KS), lp2_s - lp2_t = u_s - u_t - r
-        op.Cs = (float)(g * LN2_D / k.Zs);
-        op.Hs = (float)(KS2 + k.r);
-        op.Ct = 0.0f;
-        op.Ht = 0.0f;
-    }
-    // the vector path needs every view of the row at the same offset inside 16 bytes
-    const int64_t h = head_len<T>(w, s, t, gs, gt);
-    sweep<D, 4, true>(s, t, w, h, op);
+    op.cs = k[0];
+    op.ct = k[1];
+    op.bf = k[2];
+    op.gam = k[3];
+    op.Cs = k[4];
+    op.Ct = k[5];
+    op.Hs = k[6];
+    op.Ht = k[7];
+    op.Gs = k[8];
+    op.Gt = k[9];
+    // the vector path needs every view of the chunk at the same offset inside 16 bytes
+    sweep<D, 1, true, GRAD_BLOCK>(s, t, n, head_len<T>(n, s, t, gs, gt), op);
 }
 
 template <class D, int MODE>
@@ -292,29 +304,29 @@ hipError_t div_mode(int mode, const Shard &sh, int64_t N, const double *stats, d
 }
 
 template <class D, int MODE, bool WS, bool WT>
-hipError_t bwd_k(const Shard &sh, int64_t N, const double *stats, const float *kl, double beta,
-                 const float *grad, hipStream_t st) {
-    hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s,
-                       sh.t, sh.gs, sh.gt, sh.width, stats, kl, beta, grad);
+hipError_t bwd_k(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
+    const Chunks ch = grad_chunks(N, sh.width, sizeof(typename D::T));
+    if (ch.nchunk == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)(N * ch.nchunk)),
+                       dim3(GRAD_BLOCK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
+                       ch.nchunk, rowc);
     return hipGetLastError();
 }
 
 template <class D, int MODE>
-hipError_t bwd_want(const Shard &sh, int64_t N, const double *stats, const float *kl,
-                    double beta, const float *grad, hipStream_t st) {
+hipError_t bwd_want(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
     const bool ws = sh.gs.p != nullptr, wt = sh.gt.p != nullptr;
-    if (ws && wt) return bwd_k<D, MODE, true, true>(sh, N, stats, kl, beta, grad, st);
-    if (ws) return bwd_k<D, MODE, true, false>(sh, N, stats, kl, beta, grad, st);
-    if (wt) return bwd_k<D, MODE, false, true>(sh, N, stats, kl, beta, grad, st);
+    if (ws && wt) return bwd_k<D, MODE, true, true>(sh, N, rowc, st);
+    if (ws) return bwd_k<D, MODE, true, false>(sh, N, rowc, st);
+    if (wt) return bwd_k<D, MODE, false, true>(sh, N, rowc, st);
     return hipSuccess;
 }
 
 template <class D>
-hipError_t bwd_mode(int mode, const Shard &sh, int64_t N, const double *stats, const float *kl,
-                    double beta, const float *grad, hipStream_t st) {
-    if (mode == INTERIOR) return bwd_want<D, INTERIOR>(sh, N, stats, kl, beta, grad, st);
-    if (mode == FWD_KL) return bwd_want<D, FWD_KL>(sh, N, stats, kl, beta, grad, st);
-    return bwd_want<D, REV_KL>(sh, N, stats, kl, beta, grad, st);
+hipError_t bwd_mode(int mode, const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
+    if (mode == INTERIOR) return bwd_want<D, INTERIOR>(sh, N, rowc, st);
+    if (mode == FWD_KL) return bwd_want<D, FWD_KL>(sh, N, rowc, st);
+    return bwd_want<D, REV_KL>(sh, N, rowc, st);
 }
 
 }  // namespace
@@ -337,12 +349,19 @@ hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
     return hipGetLastError();
 }
 
-hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
-                      const float *kl, double beta, const float *grad, hipStream_t st) {
+hipError_t launch_bwd_prep(int mode, int64_t N, const double *stats, const float *kl,
+                           double beta, const float *grad, float *rowc, hipStream_t st) {
+    hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, mode, N,
+                       stats, kl, beta, grad, rowc);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const float *rowc,
+                      hipStream_t st) {
     switch (dtype) {
-        case 0: return bwd_mode<F32>(mode, sh, N, stats, kl, beta, grad, st);
-        case 1: return bwd_mode<F16>(mode, sh, N, stats, kl, beta, grad, st);
-        default: return bwd_mode<BF16>(mode, sh, N, stats, kl, beta, grad, st);
+        case 0: return bwd_mode<F32>(mode, sh, N, rowc, st);
+        case 1: return bwd_mode<F16>(mode, sh, N, rowc, st);
+        default: return bwd_mode<BF16>(mode, sh, N, rowc, st);
     }
 }
 

@@ -31,9 +31,24 @@ hipError_t launch_div(int dtype, int mode, const Shard &sh, int64_t N, const dou
 hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
                                const double *stats, double beta, float *kl, float *loss,
                                hipStream_t st);
-// pass 3: closed-form gradients of the JSD / KL for one shard
-hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
-                      const float *kl, double beta, const float *grad, hipStream_t st);
+// Row chunks of the streaming gradient kernels: cw columns per workgroup (a multiple
+// of GRAD_BLOCK vectors), nchunk chunks per row, N * nchunk workgroups in all.
+struct Chunks {
+    int64_t cw, nchunk;
+};
+inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
+    const int64_t vec = 16 / esize;
+    int64_t cw = GRAD_BLOCK * vec;
+    while (N * ((w + cw - 1) / cw) > 0x7fffffffLL) cw *= 2;  // grid.x limit
+    return {cw, w > 0 ? (w + cw - 1) / cw : 0};
+}
+
+// pass 3: per-row constants of the backward (once per call), then the closed-form
+// gradients of the JSD / KL for one shard
+hipError_t launch_bwd_prep(int mode, int64_t N, const double *stats, const float *kl,
+                           double beta, const float *grad, float *rowc, hipStream_t st);
+hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const float *rowc,
+                      hipStream_t st);
 
 // single-pass KL forward: per-shard online partials, then the merge into stats/kl/loss
 hipError_t launch_kl1(int dtype, int reverse, const Shard &sh, int64_t N, float *part_k,
@@ -44,8 +59,10 @@ hipError_t launch_kl1_merge(int reverse, const float *part, int S, int64_t N, do
 hipError_t launch_ent1(int dtype, const Shard &sh, int64_t N, float *part_k, hipStream_t st);
 hipError_t launch_ent1_merge(const float *part, int S, int64_t N, double *stats, float *ent,
                              hipStream_t st);
-hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const double *stats,
-                          const float *ent, const float *grad, hipStream_t st);
+hipError_t launch_ent_bwd_prep(int64_t N, const double *stats, const float *ent,
+                               const float *grad, float *rowc, hipStream_t st);
+hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const float *rowc,
+                          hipStream_t st);
 
 // log-probabilities: gather of K ids per row, and the backward (stream + id fix-up)
 constexpr int LP_TABLE = 16;  // shards per gather launch
@@ -57,8 +74,10 @@ struct LpTable {
 hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N,
                             int64_t vocab_global, const int64_t *ids, int K, int64_t ignore,
                             const double *stats, float *out, int32_t *dev_err, hipStream_t st);
-hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, int64_t vocab_global,
-                         const double *stats, const int64_t *ids, int K, int64_t ignore,
-                         const float *grad, hipStream_t st);
+hipError_t launch_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *stats,
+                              const int64_t *ids, int K, int64_t ignore, const float *grad,
+                              float *rowc, hipStream_t st);
+hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, const int64_t *ids, int K,
+                         int64_t ignore, const float *grad, const float *rowc, hipStream_t st);
 
 }  // namespace vjsd

@@ -326,40 +326,44 @@ struct OpEntBwd {
     }
 };
 
-template <class D>
-__device__ __forceinline__ void zero_row1(typename D::T *p, int64_t w) {
-    const int64_t h = head_len<typename D::T>(w, p);
-    for (int64_t i = threadIdx.x; i < h; i += BLOCK) store1<D>(p + i, 0.0f);
-    const int64_t nv = (w - h) / D::VEC;
-    float z[D::VEC];
-#pragma unroll
-    for (int i = 0; i < D::VEC; ++i) z[i] = 0.0f;
-    for (int64_t v = threadIdx.x; v < nv; v += BLOCK) store_vec<D>(p + h + v * D::VEC, z);
-    for (int64_t i = h + nv * D::VEC + threadIdx.x; i < w; i += BLOCK) store1<D>(p + i, 0.0f);
+// rowc: c, C, R and the undefined flag
+__global__ void k_ent_bwd_prep(int64_t N, const double *__restrict__ stats,
+                               const float *__restrict__ ent, const float *__restrict__ grad,
+                               float *__restrict__ rowc) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= N) return;
+    const float m = (float)stats[r * 4];
+    float *o = rowc + r * ROWC;
+    o[ROWC_UNDEFINED] = m == NINF ? 1.0f : 0.0f;
+    if (m == NINF) return;
+    const double Z = z_from_stats(m, stats[r * 4 + 1]);
+    o[0] = refc(m);
+    o[1] = (float)(-(double)grad[r] * LN2_D / Z);
+    o[2] = (float)(log2(Z) - (double)ent[r] * L2E_D);
 }
 
 template <class D>
-__global__ __launch_bounds__(BLOCK) void k_ent_bwd(RowView xv, RowMView gv, int64_t w,
-                                                   const double *__restrict__ stats,
-                                                   const float *__restrict__ ent,
-                                                   const float *__restrict__ grad) {
+__global__ __launch_bounds__(GRAD_BLOCK) void k_ent_bwd(RowView xv, RowMView gv, int64_t w,
+                                                        int64_t cw, int64_t nchunk,
+                                                        const float *__restrict__ rowc) {
     using T = typename D::T;
-    const int64_t r = blockIdx.x;
-    if (w == 0) return;
-    T *gx = row_ptr<T>(gv, r);
-    const float m = (float)stats[r * 4];
-    if (m == NINF) {
-        zero_row1<D>(gx, w);
+    const int64_t b = blockIdx.x;
+    const int64_t r = b / nchunk;
+    const int64_t c0 = (b - r * nchunk) * cw;
+    const int64_t n = w - c0 < cw ? w - c0 : cw;
+    const float *k = rowc + r * ROWC;
+    T *gx = row_ptr<T>(gv, r) + c0;
+    if (k[ROWC_UNDEFINED] != 0.0f) {
+        zero_span<D, GRAD_BLOCK>(gx, n);
         return;
     }
-    const T *x = row_ptr<T>(xv, r);
-    const double Z = z_from_stats(m, stats[r * 4 + 1]);
+    const T *x = row_ptr<T>(xv, r) + c0;
     OpEntBwd<D> op;
     op.gx = gx;
-    op.c = refc(m);
-    op.C = (float)(-(double)grad[r] * LN2_D / Z);
-    op.R = (float)(log2(Z) - (double)ent[r] * L2E_D);
-    sweep<D, 4, false>(x, x, w, head_len<T>(w, x, gx), op);
+    op.c = k[0];
+    op.C = k[1];
+    op.R = k[2];
+    sweep<D, 1, false, GRAD_BLOCK>(x, x, n, head_len<T>(n, x, gx), op);
 }
 
 // ---- log-probabilities ----------------------------------------------------------------
@@ -402,8 +406,8 @@ __global__ void k_lp_gather(LpTable tab, int first, int64_t N, int64_t vocab_glo
     }
 }
 
-// d/dx_j = -G p_j everywhere (G = sum of the valid upstream gradients), then the ids
-// this shard owns are rewritten as (sum of their g) - G p_j, rounded once.
+// d/dx_j = -G p_j everywhere (G = sum of the valid upstream gradients), then the ids a
+// chunk owns are rewritten as (sum of their g) - G p_j, rounded once.
 template <class D>
 struct OpLpBwd {
     using T = typename D::T;
@@ -425,42 +429,62 @@ struct OpLpBwd {
     }
 };
 
-template <class D>
-__global__ __launch_bounds__(BLOCK) void k_lp_bwd(RowView xv, RowMView gv, int64_t start,
-                                                  int64_t w, int64_t vocab_global,
-                                                  const double *__restrict__ stats,
-                                                  const int64_t *__restrict__ ids, int K,
-                                                  int64_t ignore, const float *__restrict__ grad) {
-    using T = typename D::T;
-    const int64_t r = blockIdx.x;
-    if (w == 0) return;
-    T *gx = row_ptr<T>(gv, r);
+// rowc: c, C = -G / Z, 1 / Z, G and the undefined flag
+__global__ void k_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *__restrict__ stats,
+                              const int64_t *__restrict__ ids, int K, int64_t ignore,
+                              const float *__restrict__ grad, float *__restrict__ rowc) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= N) return;
     const float m = (float)stats[r * 4];
-    if (m == NINF) {
-        zero_row1<D>(gx, w);
+    float *o = rowc + r * ROWC;
+    o[ROWC_UNDEFINED] = m == NINF ? 1.0f : 0.0f;
+    if (m == NINF) return;
+    double G = 0.0;
+    for (int k = 0; k < K; ++k) {
+        const int64_t id = ids[r * K + k];
+        if (id != ignore && id >= 0 && id < vocab_global) G += grad[r * K + k];
+    }
+    const double Z = z_from_stats(m, stats[r * 4 + 1]);
+    o[0] = refc(m);
+    o[1] = (float)(-G / Z);
+    o[2] = (float)(1.0 / Z);
+    o[3] = (float)G;
+}
+
+template <class D>
+__global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, int64_t start,
+                                                       int64_t w, int64_t cw, int64_t nchunk,
+                                                       const int64_t *__restrict__ ids, int K,
+                                                       int64_t ignore, const float *__restrict__ grad,
+                                                       const float *__restrict__ rowc) {
+    using T = typename D::T;
+    const int64_t b = blockIdx.x;
+    const int64_t r = b / nchunk;
+    const int64_t c0 = (b - r * nchunk) * cw;
+    const int64_t n = w - c0 < cw ? w - c0 : cw;
+    const float *k = rowc + r * ROWC;
+    T *gx = row_ptr<T>(gv, r) + c0;
+    if (k[ROWC_UNDEFINED] != 0.0f) {
+        zero_span<D, GRAD_BLOCK>(gx, n);
         return;
     }
-    const int64_t *id = ids + r * K;
-    const float *g = grad + r * K;
-    double G = 0.0;
-    for (int k = 0; k < K; ++k)
-        if (id[k] != ignore && id[k] >= 0 && id[k] < vocab_global) G += g[k];
-    const T *x = row_ptr<T>(xv, r);
-    const double Z = z_from_stats(m, stats[r * 4 + 1]);
+    const T *x = row_ptr<T>(xv, r) + c0;
     OpLpBwd<D> op;
     op.gx = gx;
-    op.c = refc(m);
-    op.C = (float)(-G / Z);
-    sweep<D, 4, false>(x, x, w, head_len<T>(w, x, gx), op);
-    __syncthreads();  // the streamed values of this row are visible to the block
-    for (int k = threadIdx.x; k < K; k += BLOCK) {
-        const int64_t j = id[k] - start;
-        if (id[k] == ignore || j < 0 || j >= w) continue;
+    op.c = k[0];
+    op.C = k[1];
+    sweep<D, 1, false, GRAD_BLOCK>(x, x, n, head_len<T>(n, x, gx), op);
+    __syncthreads();  // this chunk's streamed values land before the id fix-ups
+    const int64_t *id = ids + r * K;
+    const float *g = grad + r * K;
+    for (int q = threadIdx.x; q < K; q += GRAD_BLOCK) {
+        const int64_t j = id[q] - start - c0;
+        if (id[q] == ignore || j < 0 || j >= n) continue;
         float gsum = 0.0f;
-        for (int q = 0; q < K; ++q)
-            if (id[q] == id[k]) gsum += g[q];
-        const float p = ex2(fmaxf(fmaf(load1<D>(x + j), L2E, -op.c), U_FLOOR)) * (float)(1.0 / Z);
-        store1<D>(gx + j, gsum - (float)G * p);
+        for (int q2 = 0; q2 < K; ++q2)
+            if (id[q2] == id[q]) gsum += g[q2];
+        const float p = ex2(fmaxf(fmaf(load1<D>(x + j), L2E, -op.c), U_FLOOR)) * k[2];
+        store1<D>(gx + j, gsum - k[3] * p);
     }
 }
 
@@ -510,13 +534,22 @@ hipError_t launch_ent1_merge(const float *part, int S, int64_t N, double *stats,
     return hipGetLastError();
 }
 
-hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const double *stats,
-                          const float *ent, const float *grad, hipStream_t st) {
-    const dim3 grid((unsigned)N), block(BLOCK);
+hipError_t launch_ent_bwd_prep(int64_t N, const double *stats, const float *ent,
+                               const float *grad, float *rowc, hipStream_t st) {
+    hipLaunchKernelGGL(k_ent_bwd_prep, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, N,
+                       stats, ent, grad, rowc);
+    return hipGetLastError();
+}
+
+hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const float *rowc,
+                          hipStream_t st) {
+    const Chunks ch = grad_chunks(N, sh.width, dtype == 0 ? 4 : 2);
+    if (ch.nchunk == 0) return hipSuccess;
+    const dim3 grid((unsigned)(N * ch.nchunk)), block(GRAD_BLOCK);
     switch (dtype) {
-        case 0: hipLaunchKernelGGL(k_ent_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.width, stats, ent, grad); break;
-        case 1: hipLaunchKernelGGL(k_ent_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.width, stats, ent, grad); break;
-        default: hipLaunchKernelGGL(k_ent_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.width, stats, ent, grad);
+        case 0: hipLaunchKernelGGL(k_ent_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.width, ch.cw, ch.nchunk, rowc); break;
+        case 1: hipLaunchKernelGGL(k_ent_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.width, ch.cw, ch.nchunk, rowc); break;
+        default: hipLaunchKernelGGL(k_ent_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.width, ch.cw, ch.nchunk, rowc);
     }
     return hipGetLastError();
 }
@@ -535,14 +568,23 @@ hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N
     return hipGetLastError();
 }
 
-hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, int64_t vocab_global,
-                         const double *stats, const int64_t *ids, int K, int64_t ignore,
-                         const float *grad, hipStream_t st) {
-    const dim3 grid((unsigned)N), block(BLOCK);
+hipError_t launch_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *stats,
+                              const int64_t *ids, int K, int64_t ignore, const float *grad,
+                              float *rowc, hipStream_t st) {
+    hipLaunchKernelGGL(k_lp_bwd_prep, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, N,
+                       vocab_global, stats, ids, K, ignore, grad, rowc);
+    return hipGetLastError();
+}
+
+hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, const int64_t *ids, int K,
+                         int64_t ignore, const float *grad, const float *rowc, hipStream_t st) {
+    const Chunks ch = grad_chunks(N, sh.width, dtype == 0 ? 4 : 2);
+    if (ch.nchunk == 0) return hipSuccess;
+    const dim3 grid((unsigned)(N * ch.nchunk)), block(GRAD_BLOCK);
     switch (dtype) {
-        case 0: hipLaunchKernelGGL(k_lp_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, vocab_global, stats, ids, K, ignore, grad); break;
-        case 1: hipLaunchKernelGGL(k_lp_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, vocab_global, stats, ids, K, ignore, grad); break;
-        default: hipLaunchKernelGGL(k_lp_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, vocab_global, stats, ids, K, ignore, grad);
+        case 0: hipLaunchKernelGGL(k_lp_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, grad, rowc); break;
+        case 1: hipLaunchKernelGGL(k_lp_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, grad, rowc); break;
+        default: hipLaunchKernelGGL(k_lp_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, grad, rowc);
     }
     return hipGetLastError();
 }

@@ -16,12 +16,13 @@
 
 namespace vjsd {
 
-template <class D, int U, bool TWO, class Op>
+template <class D, int U, bool TWO, int BLK = BLOCK, class Op>
 __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
                                       const typename D::T *__restrict__ t, int64_t w, int64_t h,
                                       Op &op) {
     using T = typename D::T;
     constexpr int VEC = D::VEC;
+    constexpr int BLOCK = BLK;
     const int tid = threadIdx.x;
     for (int64_t i = tid; i < h; i += BLOCK) {
         float a[1][1], b[1][1] = {{0.0f}};
@@ -64,6 +65,19 @@ __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
         if (TWO) b[0][0] = load1<D>(t + i);
         op.template run<1, 1>(a, b, c);
     }
+}
+
+// Writes n zeros of the storage format (head / 16-byte body / tail), BLK lanes.
+template <class D, int BLK>
+__device__ __forceinline__ void zero_span(typename D::T *p, int64_t n) {
+    const int64_t h = head_len<typename D::T>(n, p);
+    for (int64_t i = threadIdx.x; i < h; i += BLK) store1<D>(p + i, 0.0f);
+    const int64_t nv = (n - h) / D::VEC;
+    float z[D::VEC];
+#pragma unroll
+    for (int i = 0; i < D::VEC; ++i) z[i] = 0.0f;
+    for (int64_t v = threadIdx.x; v < nv; v += BLK) store_vec<D>(p + h + v * D::VEC, z);
+    for (int64_t i = h + nv * D::VEC + threadIdx.x; i < n; i += BLK) store1<D>(p + i, 0.0f);
 }
 
 // Online (max, sum of 2^(x*L2E - c)) of one input over a batch of n elements: one

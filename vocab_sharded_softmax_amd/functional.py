@@ -73,7 +73,7 @@ class _JSD(torch.autograd.Function):
         gt = _grads_like(t, bool(n)) if want_t else None
         sh = ShardSet(s, t, widths=ctx.split, gs=gs, gt=gt)
         g = gloss.reshape(-1).to(torch.float32).contiguous()
-        _abi.vjsd_bwd(sh, stats, kl, ctx.beta, g)
+        _abi.vjsd_bwd(sh, stats, kl, ctx.beta, g, _abi.new_part(sh.N, sh.S, stats.device))
         out_s = _flat(gs) if want_s else [None] * half
         out_t = _flat(gt) if want_t else [None] * half
         return (None, None, None, *out_s, *out_t)
@@ -111,7 +111,7 @@ class _KL(torch.autograd.Function):
         gt = _grads_like(t, bool(n)) if want_t else None
         sh = ShardSet(s, t, widths=ctx.split, gs=gs, gt=gt)
         g = gloss.reshape(-1).to(torch.float32).contiguous()
-        _abi.vkl_bwd(sh, ctx.reverse, stats, kl, g)
+        _abi.vkl_bwd(sh, ctx.reverse, stats, kl, g, _abi.new_part(sh.N, sh.S, stats.device))
         out_s = _flat(gs) if want_s else [None] * half
         out_t = _flat(gt) if want_t else [None] * half
         return (None, None, None, *out_s, *out_t)
@@ -140,7 +140,8 @@ class _Entropy(torch.autograd.Function):
         x = _unpack(n, tensors)
         gx = _grads_like(x, bool(n))
         sh = ShardSet(x, widths=ctx.split, gs=gx)
-        _abi.ventropy_bwd(sh, stats, ent, gent.reshape(-1).to(torch.float32).contiguous())
+        _abi.ventropy_bwd(sh, stats, ent, gent.reshape(-1).to(torch.float32).contiguous(),
+                          _abi.new_part(sh.N, sh.S, stats.device))
         return (None, None, *_flat(gx))
 
 
@@ -174,7 +175,8 @@ class _Logprobs(torch.autograd.Function):
         gx = _grads_like(x, bool(n))
         sh = ShardSet(x, widths=ctx.split, gs=gx)
         g = gout.reshape(idv.shape).to(torch.float32).contiguous()
-        _abi.vlogprobs_bwd(sh, ctx.V, stats, idv, ctx.ignore_index, g)
+        _abi.vlogprobs_bwd(sh, ctx.V, stats, idv, ctx.ignore_index, g,
+                           _abi.new_part(sh.N, sh.S, stats.device))
         return (None, None, None, None, *_flat(gx))
 
 
