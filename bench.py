@@ -2,10 +2,10 @@
 """Benchmark of the per-token JSD hot path on one MI355X.
 
 One step is the whole JSD forward and backward over one batch, with inputs
-resident in HBM and outputs and workspace preallocated: paired statistics,
-on-device merge, divergence pass, closed-form backward with gradients to both
-inputs.  The workload is N=8192 tokens over a V=151936 vocabulary in bf16 with
-a per-column Zipf bias (the pages' Qwen2.5-sized vocabulary, B4 x ISL2048
+resident in HBM and outputs and workspace preallocated: the forward (paired
+statistics, merge and divergence) and the closed-form backward with gradients to
+both inputs.  The workload is N=8192 tokens over a V=151936 vocabulary in bf16
+with a per-column Zipf bias (the pages' Qwen2.5-sized vocabulary, B4 x ISL2048
 tokens); beta cycles through 0.1, 0.5, 0.9 from step to step.
 
 Printed: one JSON line with tokens/s, ms per step, the roofline of the dominant
@@ -13,7 +13,7 @@ kernel (the backward), measured with HIP events on the stream the kernels run
 on, the fp64 CPU oracle's rate on a bounded sample of the same rows, and
 per-kernel and sibling-op timings (forward / reverse KL, entropy, top-k
 log-probabilities at N=16384, V=128256 in bf16 and fp16; the beta = 0 / 1 JSD
-branches).  The HBM traffic figure comes from committed rocprofv3 counters and
+branches; the one-pass forward at one tensor-parallel rank's shard width).  The HBM traffic figure comes from committed rocprofv3 counters and
 is reported only while the kernel sources match the ones profiled.
 
     python bench.py [--gpus 1] [--steps 30] [--warmup 5]
@@ -162,21 +162,28 @@ def main():
 
     def step(beta, rec):
         e0 = timer.mark()
-        vj.vjsd_stats(sh, 3, part)
+        vj.vjsd_forward(sh, beta, part, stats, kl, loss)
         e1 = timer.mark()
-        vj.vjsd_merge(part, 1, N, 3, stats)
-        e2 = timer.mark()
-        vj.vjsd_fwd(sh, stats, beta, part, kl, loss)
-        e3 = timer.mark()
         vj.vjsd_bwd(shg, stats, kl, beta, gout, part)
-        e4 = timer.mark()
+        e2 = timer.mark()
         if rec:
-            timer.add("stats", e0, e1)
-            timer.add("merge", e1, e2)
-            timer.add("div", e2, e3)
-            timer.add("bwd", e3, e4)
-            timer.add("step", e0, e4)
-            timer.add(f"step_beta{beta}", e0, e4)
+            timer.add("forward", e0, e1)
+            timer.add("bwd", e1, e2)
+            timer.add("step", e0, e2)
+            timer.add(f"step_beta{beta}", e0, e2)
+
+    def three_launch_forward(beta, tm):
+        e0 = tm.mark()
+        vj.vjsd_stats(sh, 3, part)
+        e1 = tm.mark()
+        vj.vjsd_merge(part, 1, N, 3, stats)
+        e2 = tm.mark()
+        vj.vjsd_fwd(sh, stats, beta, part, kl, loss)
+        e3 = tm.mark()
+        tm.add("stats", e0, e1)
+        tm.add("merge", e1, e2)
+        tm.add("div", e2, e3)
+        tm.add("forward", e0, e3)
 
     betas = list(w.betas)
     for i in range(args.warmup):
@@ -194,9 +201,19 @@ def main():
     bytes_bwd = 4 * tensor_bytes  # read s, t; write gs, gt
     bwd_ms = timer.ms("bwd")
     achieved = bytes_bwd / (bwd_ms * 1e-3) / 1e9
-    per_kernel = {k: round(timer.ms(k), 4) for k in ("stats", "merge", "div", "bwd", "step")}
+    per_kernel = {k: round(timer.ms(k), 4) for k in ("forward", "bwd", "step")}
     per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas}
     log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
+
+    # the forward's three launches timed one by one (statistics, merge, divergence):
+    # at this width vjsd_forward runs exactly these
+    tm3 = Timer(torch)
+    for i in range(2):
+        three_launch_forward(betas[i % 3], Timer(torch))
+    for i in range(10):
+        three_launch_forward(betas[i % 3], tm3)
+    torch.cuda.synchronize()
+    three = {k: round(tm3.ms(k), 4) for k in ("stats", "merge", "div", "forward")}
 
     # the KL branches of the same engine on the same data
     branches = {}
@@ -206,9 +223,7 @@ def main():
         tm = Timer(torch)
         for _ in range(5):
             a = tm.mark()
-            vj.vjsd_stats(sh, 3, part)
-            vj.vjsd_merge(part, 1, N, 3, stats)
-            vj.vjsd_fwd(sh, stats, beta, part, kl, loss)
+            vj.vjsd_forward(sh, beta, part, stats, kl, loss)
             vj.vjsd_bwd(shg, stats, kl, beta, gout, part)
             tm.add("x", a, tm.mark())
         torch.cuda.synchronize()
@@ -222,6 +237,7 @@ def main():
     torch.cuda.empty_cache()
 
     siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
+    tp8 = tp8_forward(torch, vj, synth)
 
     out = {
         "metric": METRIC,
@@ -249,11 +265,51 @@ def main():
                      "bytes_per_launch": bytes_bwd, "avg_launch_ms": round(bwd_ms, 4)},
         "cpu_baseline": cpu,
         "kernel_ms": per_kernel,
+        "forward_parts_ms": three,
+        "tp8_shard": tp8,
         "step_ms_by_beta": per_beta,
         "branches": branches,
         "siblings": siblings,
     }
     print(json.dumps(out), flush=True)
+
+
+def tp8_forward(torch, vj, synth, reps=10):
+    """JSD at one tensor-parallel rank's vocabulary shard (N=8192, V=16032 bf16, one
+    shard, beta=0.5): the one-pass forward (a row per workgroup, held in registers)
+    against the same forward as three launches, and the backward."""
+    b = synth.draw("tp8_shard", device="cuda")
+    N, V = b.s.shape
+    tb = N * V * b.s.element_size()
+    part = vj.new_part(N, 1, "cuda")
+    stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
+    kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
+    loss = torch.empty((N,), dtype=torch.float32, device="cuda")
+    gs, gt = torch.empty_like(b.s), torch.empty_like(b.t)
+    sh = vj.ShardSet(b.s, b.t)
+    shg = vj.ShardSet(b.s, b.t, gs=gs, gt=gt)
+    ops = {
+        "one_pass_forward": lambda: vj.vjsd_forward(sh, 0.5, part, stats, kl, loss),
+        "three_launch_forward": lambda: (vj.vjsd_stats(sh, 3, part),
+                                         vj.vjsd_merge(part, 1, N, 3, stats),
+                                         vj.vjsd_fwd(sh, stats, 0.5, part, kl, loss)),
+        "bwd": lambda: vj.vjsd_bwd(shg, stats, kl, 0.5, b.gout, part),
+    }
+    res = {}
+    for name, fn in ops.items():
+        fn()
+        fn()
+        tm = Timer(torch)
+        for _ in range(reps):
+            a = tm.mark()
+            fn()
+            tm.add("x", a, tm.mark())
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round(tm.ms("x"), 4)
+    res["one_pass_forward_gbps"] = round(2 * tb / (res["one_pass_forward_ms"] * 1e-3) / 1e9, 1)
+    res["bwd_gbps"] = round(4 * tb / (res["bwd_ms"] * 1e-3) / 1e9, 1)
+    res["tokens_per_s"] = round(N / ((res["one_pass_forward_ms"] + res["bwd_ms"]) * 1e-3), 1)
+    return res
 
 
 def sibling_rows(torch, vj, synth, reps=3):

@@ -160,6 +160,20 @@ VJSD_API int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, con
              double beta, float *part, float *kl, float *loss, void *stream);
 
 /*
+ * The whole JSD forward in one call: vjsd_stats (both inputs), vjsd_merge and
+ * vjsd_fwd, with the same outputs (stats, kl, loss), the same semantics and the
+ * same workspace `part` [JSD-PR, Changes].  With a single shard whose rows are
+ * 16-byte aligned, a multiple of 16 bytes wide and at most 32 KiB wide (16384
+ * bf16 / fp16 or 8192 fp32 columns), one workgroup holds a row of both inputs in
+ * registers and each logit is read from HBM once; otherwise the three passes run as
+ * separate launches.  Results agree with the separate calls within rounding (the
+ * reduction order differs) and are deterministic for a given layout and device.
+ * Errors as vjsd_fwd.
+ */
+VJSD_API int vjsd_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
+                          float *part, double *stats, float *kl, float *loss, void *stream);
+
+/*
  * Generalized JSD backward, closed form and local [JSD-PR, Changes: recompute
  * probabilities in registers; OPS-PR, How: no communication].  With g = grad_loss[r]:
  *   interior: d/ds = g (1-beta) p_s (lp_s - lM - KS),  d/dt = g beta p_t (lp_t - lM - KT)

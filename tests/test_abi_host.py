@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
@@ -68,6 +68,7 @@ def fwd(arr, S, N, dt=2, beta=0.5, stats=FAKE, part=FAKE, kl=FAKE, loss=FAKE):
 
 def test_empty_batch_is_valid_and_enqueues_nothing():
     a = shards([5, 0, 7])
+    assert lib.vjsd_forward(a, 3, 0, 2, 0.5, None, None, None, None, None) == OK
     assert lib.vjsd_stats(a, 3, 0, 2, 3, None, None) == OK
     assert lib.vjsd_merge(None, 3, 0, 3, None, None) == OK
     assert fwd(a, 3, 0, stats=None, part=None, kl=None, loss=None) == OK
@@ -82,6 +83,7 @@ def test_empty_batch_is_valid_and_enqueues_nothing():
 def test_beta_outside_unit_interval_is_rejected(beta):
     a = shards([10])
     assert fwd(a, 1, 4, beta=beta) == BETA
+    assert lib.vjsd_forward(a, 1, 4, 2, beta, FAKE, FAKE, FAKE, FAKE, None) == BETA
     assert lib.vjsd_bwd(a, 1, 4, 2, FAKE, FAKE, beta, FAKE, FAKE, None) == BETA
 
 
@@ -101,6 +103,7 @@ def test_dtype_and_sizes_are_checked():
 def test_null_buffers_are_rejected():
     a = shards([10])
     assert fwd(a, 1, 4, stats=None) == ARG
+    assert lib.vjsd_forward(a, 1, 4, 2, 0.5, None, FAKE, FAKE, FAKE, None) == ARG
     assert fwd(a, 1, 4, kl=None) == ARG
     assert fwd(a, 1, 4, loss=None) == ARG
     assert lib.vjsd_stats(a, 1, 4, 2, 3, None, None) == ARG

@@ -14,8 +14,13 @@ from vocab_sharded_softmax_amd import functional  # noqa: E402
 
 
 class Recorder:
-    def __init__(self):
+    """Stands in for the library: records entry-point calls; the two pure helpers
+    (workspace size, error text) still come from the real library."""
+
+    def __init__(self, real):
         self.calls = []
+        self.vjsd_workspace_bytes = real.vjsd_workspace_bytes
+        self.vjsd_strerror = real.vjsd_strerror
 
     def __getattr__(self, name):
         if name.startswith("v"):
@@ -28,7 +33,7 @@ class Recorder:
 
 @pytest.fixture
 def rec(monkeypatch):
-    r = Recorder()
+    r = Recorder(abi.lib)
     monkeypatch.setattr(abi, "lib", r)
     monkeypatch.setattr(abi, "_require_gpu", lambda x, name: None)
     monkeypatch.setattr(abi, "_stream", lambda s: 0)
@@ -64,6 +69,7 @@ def test_wrappers_pass_sizes_and_shards(rec):
     vj.vjsd_stats(sh, 3, part)
     vj.vjsd_merge(part, 3, N, 3, stats)
     vj.vjsd_fwd(sh, stats, 0.25, part, kl, loss)
+    vj.vjsd_forward(sh, 0.25, part, stats, kl, loss)
     shg = abi.ShardSet(s, t, widths=[5, 0, 7], gs=torch.empty(B, T, V, dtype=torch.bfloat16))
     vj.vjsd_bwd(shg, stats, kl, 0.25, g, part)
     vj.vkl_fwd(sh, True, part, stats, kl, loss)
@@ -78,7 +84,7 @@ def test_wrappers_pass_sizes_and_shards(rec):
     vj.vlogprobs_bwd(abi.ShardSet(s, widths=[5, 7], gs=torch.empty(B, T, V, dtype=torch.bfloat16)),
                      V, stats, ids, -100, torch.empty(N, 3), part)
     names = [c[0] for c in rec.calls]
-    assert names == ["vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_bwd", "vkl_fwd", "vkl_bwd",
+    assert names == ["vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vkl_fwd", "vkl_bwd",
                      "ventropy_fwd", "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd"]
     args = dict(rec.calls)
     assert args["vjsd_stats"][1:5] == (3, N, 2, 3)

@@ -1,0 +1,123 @@
+"""GPU parity of the whole-forward call (vjsd_forward): against the fp64 oracle and
+against the three separate launches, over dtypes, beta branches, row widths on both
+sides of the one-workgroup-per-row limit (16384 16-bit or 8192 fp32 columns) and at
+each register-tile size below it, batch sizes, masks, offsets, and the layouts that
+must fall back to the three launches."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import assert_stats, assert_values
+
+pytestmark = pytest.mark.gpu
+
+NINF = float("-inf")
+
+
+def vj():
+    import vocab_sharded_softmax_amd as v
+    return v
+
+
+def forward(s, t, beta, widths=None, fused=True):
+    v = vj()
+    sh = v.ShardSet(s, t, widths=widths)
+    N, S = sh.N, sh.S
+    part = v.new_part(N, S, s.device)
+    stats = torch.full((N, 4), float("nan"), dtype=torch.float64, device=s.device)
+    kl = torch.full((N, 2), float("nan"), device=s.device)
+    loss = torch.full((N,), float("nan"), device=s.device)
+    if fused:
+        v.vjsd_forward(sh, beta, part, stats, kl, loss)
+    else:
+        v.vjsd_stats(sh, 3, part)
+        v.vjsd_merge(part, S, N, 3, stats)
+        v.vjsd_fwd(sh, stats, beta, part, kl, loss)
+    torch.cuda.synchronize()
+    return stats.cpu(), kl.cpu(), loss.cpu()
+
+
+def check(s, t, beta, widths=None):
+    dt = s.dtype
+    st, kl, loss = forward(s, t, beta, widths)
+    sc, tc = s.reshape(-1, s.shape[-1]).cpu(), t.reshape(-1, t.shape[-1]).cpu()
+    ref = oracle.jsd(sc, tc, beta, widths=widths, grads=False)
+    assert_stats(st, *oracle.stats(sc, widths=widths), 0, "student stats")
+    assert_stats(st, *oracle.stats(tc, widths=widths), 1, "teacher stats")
+    assert_values(loss, ref["loss"], dt, "loss")
+    assert_values(kl[:, 0], ref["kt"], dt, "KL(p_t||M)")
+    assert_values(kl[:, 1], ref["ks"], dt, "KL(p_s||M)")
+    # the three-launch path agrees within rounding
+    st3, kl3, loss3 = forward(s, t, beta, widths, fused=False)
+    fin = np.isfinite(loss.numpy())
+    np.testing.assert_allclose(loss.numpy()[fin], loss3.numpy()[fin], rtol=2e-6, atol=2e-7)
+    assert np.array_equal(np.isnan(loss.numpy()), np.isnan(loss3.numpy()))
+    assert np.array_equal(np.isinf(loss.numpy()), np.isinf(loss3.numpy()))
+    return loss
+
+
+# 1000 / 4096 / 8192 / 16032 / 16384: one workgroup per row (1, 2, 4, 8 vectors per
+# lane); 16392 and wider: the three launches
+@pytest.mark.parametrize("V", [1000, 4096, 8192, 16032, 16384, 16392, 151936])
+@pytest.mark.parametrize("beta", [0.5, 0.0, 1.0])
+def test_one_pass_forward_bf16(V, beta):
+    b = synth.draw("full_vocab", device="cuda", N=40, V=V)
+    check(b.s, b.t, beta)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.float16])
+@pytest.mark.parametrize("V", [3000, 8192, 12000, 128256])
+def test_one_pass_forward_other_dtypes(dtype, V):
+    b = synth.draw("tiny", device="cuda", N=24, V=V, dtype=dtype)
+    check(b.s, b.t, 0.3)
+
+
+@pytest.mark.parametrize("N", [1, 7, 100, 4097])
+def test_one_pass_forward_batch_sizes(N):
+    b = synth.draw("full_vocab", device="cuda", N=N, V=16032)
+    check(b.s, b.t, 0.9)
+
+
+def test_one_pass_forward_masks_offsets_undefined_rows():
+    b = synth.draw("robust", device="cuda", N=200, V=8000)  # fp32: one workgroup per row
+    s, t = b.s.clone(), b.t.clone()
+    s[7] = NINF  # student undefined
+    t[8] = NINF  # teacher undefined
+    s[9, 50:] = NINF  # partly masked
+    s[11, 123] = NINF  # forward KL of row 11 infinite
+    t[11, 123] = 1.0
+    loss = check(s, t, 0.5)
+    assert np.isnan(loss.numpy()[[7, 8]]).all()
+    lf = check(s, t, 0.0)
+    assert np.isinf(lf.numpy()[11])
+
+
+def test_one_pass_forward_full_size_sampled():
+    b = synth.draw("tp8_shard", device="cuda")
+    st, kl, loss = forward(b.s, b.t, 0.5)
+    rows = np.array([0, 1, 2, 1000, 4095, 4096, 8190, 8191])
+    ref = oracle.jsd(b.s[rows].cpu(), b.t[rows].cpu(), 0.5, grads=False)
+    assert_values(loss[rows], ref["loss"], torch.bfloat16, "loss")
+    assert torch.isfinite(loss).all()
+    st3, kl3, loss3 = forward(b.s, b.t, 0.5, fused=False)
+    np.testing.assert_allclose(loss.numpy(), loss3.numpy(), rtol=2e-6, atol=2e-7)
+
+
+def test_fallback_layouts():
+    b = synth.draw("tiny", device="cuda", N=12, V=1002, dtype=torch.bfloat16)
+    check(b.s[:, 1:1001], b.t[:, 1:1001], 0.5)  # rows not 16-byte aligned
+    check(b.s[:, :1001], b.t[:, :1001], 0.5)  # width not a multiple of 16 bytes
+    check(b.s, b.t, 0.5, widths=[500, 0, 502])  # several shards
+
+
+def test_autograd_uses_the_one_pass_forward():
+    v = vj()
+    b = synth.draw("tiny", device="cuda", N=10, V=4096, dtype=torch.bfloat16)
+    s = b.s.clone().requires_grad_()
+    loss = v.jsd(s, b.t, 0.5)
+    _, _, ref = forward(b.s, b.t, 0.5)
+    assert torch.equal(loss.detach().cpu(), ref)
+    loss.sum().backward()
+    assert torch.isfinite(s.grad.float()).all()

@@ -5,7 +5,8 @@ The compute path is libvjsd.so (hand-written HIP kernels for gfx950, C ABI in
 ``functional`` wraps them as autograd ops.  Importing the package fails if the
 library has not been built.
 """
-from ._abi import (ShardSet, VjsdArgumentError, VjsdError, new_part, vjsd_bwd, vjsd_fwd,
+from ._abi import (ShardSet, VjsdArgumentError, VjsdError, new_part, vjsd_bwd, vjsd_forward,
+                   vjsd_fwd,
                    vjsd_merge, vjsd_stats, vjsd_strerror, vjsd_workspace_bytes, ventropy_bwd,
                    ventropy_fwd, vkl_bwd, vkl_fwd, vlogprobs_bwd, vlogprobs_fwd)
 from ._abi import LIB_PATH
@@ -13,7 +14,7 @@ from .functional import entropy, jsd, kl_div, logprobs
 
 __all__ = [
     "jsd", "kl_div", "entropy", "logprobs", "ShardSet", "VjsdError", "VjsdArgumentError",
-    "vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_bwd", "vkl_fwd", "vkl_bwd", "ventropy_fwd",
+    "vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vkl_fwd", "vkl_bwd", "ventropy_fwd",
     "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd", "vjsd_strerror", "vjsd_workspace_bytes",
     "new_part", "LIB_PATH",
 ]

@@ -57,6 +57,7 @@ def _load():
         "vjsd_stats": ([SP, I, I64, I, I, P, P], I),
         "vjsd_merge": ([P, I, I64, I, P, P], I),
         "vjsd_fwd": ([SP, I, I64, I, P, D, P, P, P, P], I),
+        "vjsd_forward": ([SP, I, I64, I, D, P, P, P, P, P], I),
         "vjsd_bwd": ([SP, I, I64, I, P, P, D, P, P, P], I),
         "vkl_fwd": ([SP, I, I64, I, I, P, P, P, P, P], I),
         "vkl_bwd": ([SP, I, I64, I, I, P, P, P, P, P], I),
@@ -195,7 +196,8 @@ def vjsd_workspace_bytes(N: int, S: int) -> int:
 
 
 def part_floats(N: int, S: int) -> int:
-    return N * ROWC_FLOATS + N * S * PART_FLOATS
+    """Floats of the workspace: vjsd_workspace_bytes(N, S) / 4."""
+    return (lib.vjsd_workspace_bytes(N, S) + 3) // 4 if N > 0 and S > 0 else 0
 
 
 def new_part(N: int, S: int, device) -> torch.Tensor:
@@ -220,6 +222,15 @@ def vjsd_fwd(sh: ShardSet, stats, beta: float, part, kl, loss, stream=None) -> N
                         float(beta), _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
                         _ptr(kl, torch.float32, N * 2, "kl"), _ptr(loss, torch.float32, N, "loss"),
                         _stream(stream)))
+
+
+def vjsd_forward(sh: ShardSet, beta: float, part, stats, kl, loss, stream=None) -> None:
+    N = sh.N
+    _check(lib.vjsd_forward(sh.arr, sh.S, N, sh.dtype_code, float(beta),
+                            _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                            _ptr(stats, torch.float64, N * 4, "stats"),
+                            _ptr(kl, torch.float32, N * 2, "kl"),
+                            _ptr(loss, torch.float32, N, "loss"), _stream(stream)))
 
 
 def vjsd_bwd(sh: ShardSet, stats, kl, beta: float, grad_loss, part, stream=None) -> None:

@@ -113,7 +113,8 @@ const char *vjsd_strerror(int code) {
 
 size_t vjsd_workspace_bytes(int64_t N, int S) {
     if (N <= 0 || S <= 0) return 0;
-    return ((size_t)N * vjsd::ROWC + (size_t)N * (size_t)S * vjsd::PART_STRIDE) * sizeof(float);
+    const size_t floats = (size_t)N * vjsd::ROWC + (size_t)N * (size_t)S * vjsd::PART_STRIDE;
+    return floats * sizeof(float);
 }
 
 int vjsd_stats(const vjsd_shard *shards, int S, int64_t N, int dtype, int which, float *part,
@@ -172,6 +173,29 @@ int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double
     }
     return hip_status(
         vjsd::launch_div_finalize(mode, part_of(part, 0, N), S, N, stats, beta, kl, loss, st));
+}
+
+int vjsd_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta, float *part,
+                 double *stats, float *kl, float *loss, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    if ((e = check_views(shards, S, N, dtype, true, false))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!part || !stats || !kl || !loss) return VJSD_ERR_ARG;
+    const int mode = mode_of(beta);
+    hipStream_t st = (hipStream_t)stream;
+    if (S == 1) {
+        bool used = false;
+        Shard sh = convert(shards[0], true, false);
+        if ((e = hip_status(vjsd::launch_fwd_fused(dtype, mode, sh, N, beta, stats, kl, loss, st,
+                                                   &used))))
+            return e;
+        if (used) return VJSD_OK;
+    }
+    if ((e = vjsd_stats(shards, S, N, dtype, 3, part, stream))) return e;
+    if ((e = vjsd_merge(part, S, N, 3, stats, stream))) return e;
+    return vjsd_fwd(shards, S, N, dtype, stats, beta, part, kl, loss, stream);
 }
 
 int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,

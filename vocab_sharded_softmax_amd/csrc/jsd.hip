@@ -17,6 +17,7 @@
 //   KT / ln2 = (1/Z_t) sum e_t (u_t - L),  KS / ln2 = (1/Z_s) sum e_s ((u_s - L) - r)
 // so the per-element work touches only O(1)-sized quantities, never log Z; u - L and
 // (u_s - L) - r are differences of nearby numbers and come out (nearly) exact.
+#include "divergence.hpp"
 #include "kernels.hpp"
 #include "sweep.hpp"
 
@@ -46,62 +47,6 @@ __device__ __forceinline__ RowConst row_const(const double *__restrict__ stats, 
     k.izt = (float)(1.0 / k.Zt);
     k.r = log2(k.Zs / k.Zt);
     return k;
-}
-
-template <int MODE>
-struct OpDiv {
-    float cs, ct, bf, gam, rf;
-    float At[4] = {0, 0, 0, 0}, As[4] = {0, 0, 0, 0};
-    float F = NINF;  // max of u_t - u_s (forward KL) or u_s - u_t (reverse): +inf flags mass on a masked token
-
-    template <int NV, int W>
-    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
-                                        const int64_t (&)[NV]) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j)
-#pragma unroll
-            for (int i = 0; i < W; ++i) {
-                const float usr = fmaf(x[j][i], L2E, -cs);
-                const float utr = fmaf(y[j][i], L2E, -ct);
-                const float us = fmaxf(usr, U_FLOOR), ut = fmaxf(utr, U_FLOOR);
-                if constexpr (MODE == INTERIOR) {
-                    const float es = ex2(us), et = ex2(ut);
-                    const float L = lg2(fmaf(bf, et, fmaf(gam, es, W_FLOOR)));
-                    At[j] = fmaf(et, ut - L, At[j]);
-                    As[j] = fmaf(es, (us - L) - rf, As[j]);
-                } else if constexpr (MODE == FWD_KL) {
-                    F = fmaxf(F, utr - usr);
-                    At[j] = fmaf(ex2(ut), (ut - us) + rf, At[j]);
-                } else {
-                    F = fmaxf(F, usr - utr);
-                    As[j] = fmaf(ex2(us), (us - ut) - rf, As[j]);
-                }
-            }
-    }
-};
-
-// Final per-token values from the shard-summed partials (all in base 2, fp64).
-__device__ __forceinline__ void finalize_row(int mode, double beta, bool undefined, double pt,
-                                             double ps, float F, float *kl, float *loss) {
-    double KT, KS, l;
-    if (undefined) {
-        KT = KS = l = __builtin_nan("");
-    } else if (mode == INTERIOR) {
-        KT = pt * LN2_D;
-        KS = ps * LN2_D;
-        l = beta * KT + (1.0 - beta) * KS;
-    } else if (mode == FWD_KL) {
-        KT = F == __builtin_huge_valf() ? __builtin_inf() : pt * LN2_D;
-        KS = 0.0;
-        l = KT;
-    } else {
-        KS = F == __builtin_huge_valf() ? __builtin_inf() : ps * LN2_D;
-        KT = 0.0;
-        l = KS;
-    }
-    kl[0] = (float)KT;
-    kl[1] = (float)KS;
-    *loss = (float)l;
 }
 
 template <class D, int MODE>

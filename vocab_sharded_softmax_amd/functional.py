@@ -52,9 +52,7 @@ class _JSD(torch.autograd.Function):
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
         kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
         loss = torch.empty((N,), dtype=torch.float32, device=dev)
-        _abi.vjsd_stats(sh, 3, part)
-        _abi.vjsd_merge(part, S, N, 3, stats)
-        _abi.vjsd_fwd(sh, stats, beta, part, kl, loss)
+        _abi.vjsd_forward(sh, beta, part, stats, kl, loss)
         ctx.beta, ctx.split, ctx.n_shards = beta, split, n_shards
         ctx.save_for_backward(stats, kl, *tensors)
         return loss.view(sh.lead_shape)
