@@ -205,8 +205,8 @@ def main():
     per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas}
     log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
 
-    # the forward's three launches timed one by one (statistics, merge, divergence):
-    # at this width vjsd_forward runs exactly these
+    # the same forward as three separate launches (statistics, merge, divergence),
+    # timed one by one for comparison with the one-launch forward above
     tm3 = Timer(torch)
     for i in range(2):
         three_launch_forward(betas[i % 3], Timer(torch))

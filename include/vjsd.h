@@ -162,13 +162,15 @@ VJSD_API int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, con
 /*
  * The whole JSD forward in one call: vjsd_stats (both inputs), vjsd_merge and
  * vjsd_fwd, with the same outputs (stats, kl, loss), the same semantics and the
- * same workspace `part` [JSD-PR, Changes].  With a single shard whose rows are
- * 16-byte aligned, a multiple of 16 bytes wide and at most 32 KiB wide (16384
- * bf16 / fp16 or 8192 fp32 columns), one workgroup holds a row of both inputs in
- * registers and each logit is read from HBM once; otherwise the three passes run as
- * separate launches.  Results agree with the separate calls within rounding (the
- * reduction order differs) and are deterministic for a given layout and device.
- * Errors as vjsd_fwd.
+ * same workspace `part` [JSD-PR, Changes].  How it runs:
+ *   beta = 0 or 1   the forward / reverse KL, in one input pass (as vkl_fwd)
+ *   one shard       one launch, a workgroup per row: statistics, then divergence.
+ *                   Rows 16-byte aligned, a multiple of 16 bytes and at most
+ *                   32 KiB wide (16384 bf16 / fp16 or 8192 fp32 columns) are held
+ *                   in registers and read from HBM once; wider rows are swept twice
+ *   several shards  the three separate launches
+ * Results agree with the separate calls within rounding (the reduction order
+ * differs) and are deterministic for a given layout and device.  Errors as vjsd_fwd.
  */
 VJSD_API int vjsd_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
                           float *part, double *stats, float *kl, float *loss, void *stream);

@@ -1,8 +1,8 @@
 """GPU parity of the whole-forward call (vjsd_forward): against the fp64 oracle and
-against the three separate launches, over dtypes, beta branches, row widths on both
-sides of the one-workgroup-per-row limit (16384 16-bit or 8192 fp32 columns) and at
-each register-tile size below it, batch sizes, masks, offsets, and the layouts that
-must fall back to the three launches."""
+against the three separate launches, over dtypes, the beta = 0 / 1 branches (one-pass
+KL), row widths on both sides of the held-in-registers limit (16384 16-bit or 8192
+fp32 columns) and at each register-tile size below it, batch sizes, masks, offsets,
+unaligned rows (swept twice) and several shards (three launches)."""
 import numpy as np
 import pytest
 import torch
@@ -58,8 +58,8 @@ def check(s, t, beta, widths=None):
     return loss
 
 
-# 1000 / 4096 / 8192 / 16032 / 16384: one workgroup per row (1, 2, 4, 8 vectors per
-# lane); 16392 and wider: the three launches
+# 1000 / 4096 / 8192 / 16032 / 16384: the row held in registers (1, 2, 4, 8 vectors
+# per lane); 16392 and wider: the row swept twice
 @pytest.mark.parametrize("V", [1000, 4096, 8192, 16032, 16384, 16392, 151936])
 @pytest.mark.parametrize("beta", [0.5, 0.0, 1.0])
 def test_one_pass_forward_bf16(V, beta):
@@ -94,8 +94,9 @@ def test_one_pass_forward_masks_offsets_undefined_rows():
     assert np.isinf(lf.numpy()[11])
 
 
-def test_one_pass_forward_full_size_sampled():
-    b = synth.draw("tp8_shard", device="cuda")
+@pytest.mark.parametrize("name", ["tp8_shard", "full_vocab"])
+def test_one_pass_forward_full_size_sampled(name):
+    b = synth.draw(name, device="cuda")
     st, kl, loss = forward(b.s, b.t, 0.5)
     rows = np.array([0, 1, 2, 1000, 4095, 4096, 8190, 8191])
     ref = oracle.jsd(b.s[rows].cpu(), b.t[rows].cpu(), 0.5, grads=False)
@@ -105,11 +106,14 @@ def test_one_pass_forward_full_size_sampled():
     np.testing.assert_allclose(loss.numpy(), loss3.numpy(), rtol=2e-6, atol=2e-7)
 
 
-def test_fallback_layouts():
+def test_layouts_outside_the_register_path():
     b = synth.draw("tiny", device="cuda", N=12, V=1002, dtype=torch.bfloat16)
     check(b.s[:, 1:1001], b.t[:, 1:1001], 0.5)  # rows not 16-byte aligned
     check(b.s[:, :1001], b.t[:, :1001], 0.5)  # width not a multiple of 16 bytes
+    check(b.s[:, 1:1001], b.t[:, 2:1002], 0.5)  # student and teacher misaligned apart
     check(b.s, b.t, 0.5, widths=[500, 0, 502])  # several shards
+    c = synth.draw("tiny", device="cuda", N=6, V=20003, dtype=torch.bfloat16)
+    check(c.s[:, 3:20003], c.t[:, 1:20001], 0.3)  # wide, unaligned: swept twice
 
 
 def test_autograd_uses_the_one_pass_forward():

@@ -184,14 +184,13 @@ int vjsd_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double b
     if (N == 0) return VJSD_OK;
     if (!part || !stats || !kl || !loss) return VJSD_ERR_ARG;
     const int mode = mode_of(beta);
-    hipStream_t st = (hipStream_t)stream;
+    // the endpoints are plain KL divergences: one input pass
+    if (mode != vjsd::INTERIOR)
+        return vkl_fwd(shards, S, N, dtype, mode == vjsd::REV_KL, part, stats, kl, loss, stream);
     if (S == 1) {
-        bool used = false;
         Shard sh = convert(shards[0], true, false);
-        if ((e = hip_status(vjsd::launch_fwd_fused(dtype, mode, sh, N, beta, stats, kl, loss, st,
-                                                   &used))))
-            return e;
-        if (used) return VJSD_OK;
+        return hip_status(vjsd::launch_fwd_fused(dtype, sh, N, beta, stats, kl, loss,
+                                                 (hipStream_t)stream));
     }
     if ((e = vjsd_stats(shards, S, N, dtype, 3, part, stream))) return e;
     if ((e = vjsd_merge(part, S, N, 3, stats, stream))) return e;

@@ -237,23 +237,24 @@ __device__ __forceinline__ MZ wave_mz(MZ v) {
     return v;
 }
 
-// Sum of NV floats over the workgroup; result valid in thread 0.  `red` is LDS of
-// NV * NWAVE floats.
-template <int NV>
+// Sum of NV floats over a BLK-lane workgroup; result valid in thread 0.  `red` is LDS
+// of NV * (BLK / 64) floats.
+template <int NV, int BLK = BLOCK>
 __device__ __forceinline__ void block_sum(float (&v)[NV], float *red) {
+    constexpr int NW = BLK / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
     if (lane == 0)
 #pragma unroll
-        for (int i = 0; i < NV; ++i) red[i * NWAVE + wave] = v[i];
+        for (int i = 0; i < NV; ++i) red[i * NW + wave] = v[i];
     __syncthreads();
     if (threadIdx.x == 0)
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            float a = red[i * NWAVE];
+            float a = red[i * NW];
 #pragma unroll
-            for (int k = 1; k < NWAVE; ++k) a += red[i * NWAVE + k];
+            for (int k = 1; k < NW; ++k) a += red[i * NW + k];
             v[i] = a;
         }
 }

@@ -1,16 +1,21 @@
-// fused.hip -- the JSD forward in one HBM pass for rows that fit one workgroup.
+// fused.hip -- the interior JSD forward of a single shard in one launch.
 //
 // [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel generalized JSD with
 // Triton kernels", section Scope and limitations: the JSD needs the global normaliser
 // before the nonlinear mixture, so statistics and divergence are two passes over the
-// input.  When a whole row of both inputs fits in one workgroup's registers (256 lanes
-// x FUSED_NVT_MAX 16-byte vectors per input: up to 16384 bf16 / fp16 or 8192 fp32
-// columns), the two passes run over registers and each logit is read from HBM once;
-// the row constants are rebuilt from the fp64 statistics exactly as the separate
-// passes rebuild them.  Wider rows take the separate statistics, merge and divergence
-// launches: splitting a row over several workgroups needs a device-wide exchange per
-// row, and on MI355X the cache write-back and invalidation that a correct device-scope
-// release/acquire costs exceeds the second read it would save.
+// input.  With a single shard one workgroup owns a whole row, so both passes can run
+// in one workgroup with nothing exchanged between workgroups:
+//   k_fwd_row    a row of both inputs fits the workgroup's registers (256 lanes x
+//                FUSED_NVT_MAX 16-byte vectors per input: up to 16384 bf16 / fp16 or
+//                8192 fp32 columns, 16-byte aligned rows): one HBM read per logit
+//   k_fwd_twice  wider rows: the workgroup sweeps its row for the statistics, then
+//                sweeps it again for the divergence terms; part of the second read
+//                is served by the caches, and the merge launch and two kernel
+//                boundaries go away
+// The row constants are rebuilt from the fp64 statistics exactly as the separate
+// passes rebuild them.  Splitting a row over several workgroups would need a
+// device-wide exchange per row; on MI355X the cache write-back and invalidation that a
+// correct device-scope release/acquire costs exceeds the second read it would save.
 #include "kernels.hpp"
 #include "sweep.hpp"
 
@@ -106,7 +111,7 @@ __device__ __forceinline__ void block_sum2(float &a, float &b, float *red) {
 
 // One workgroup per row.  Lane l holds vectors l, l + FB, ... of each input; slots past
 // the row's end hold -inf, which adds exactly nothing to any sum below.
-template <class D, int MODE, int NVT>
+template <class D, int NVT>
 __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t w, double beta,
                                                 double *__restrict__ stats,
                                                 float *__restrict__ kl,
@@ -183,12 +188,12 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
         o[3] = lzt;
     }
     // ---- divergence: row constants from the stored statistics, terms from registers
-    float pt = 0.0f, ps = 0.0f, F = NINF;
+    float pt = 0.0f, ps = 0.0f;
     double Zs = 1.0, Zt = 1.0;
     if (!undefined) {
         Zs = z_from_stats(ms, lzs);
         Zt = z_from_stats(mt, lzt);
-        OpDivRegs<MODE> op;
+        OpDivRegs<INTERIOR> op;
         op.cs = cs;
         op.ct = ct;
         op.bf = (float)beta;
@@ -208,65 +213,106 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
         }
         pt = op.At;
         ps = op.As;
-        F = op.F;
     }
     block_sum2(pt, ps, red);
-    float G = NINF;
-    block_max2(F, G, red);
     if (threadIdx.x == 0)
-        finalize_row(MODE, beta, undefined, pt * (float)(1.0 / Zt), ps * (float)(1.0 / Zs), F,
-                     kl + 2 * r, loss + r);
+        finalize_row(INTERIOR, beta, undefined, pt * (float)(1.0 / Zt), ps * (float)(1.0 / Zs),
+                     NINF, kl + 2 * r, loss + r);
 }
 
-template <class D, int MODE, int NVT>
+// One workgroup per row, any alignment: statistics sweep, then divergence sweep.
+// TWICE_BLK lanes, so that two workgroups fill a CU: about 512 rows are in flight, few
+// enough that much of the second sweep is served by the caches.
+constexpr int TWICE_BLK = 512;
+
+template <class D>
+__global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv, int64_t w,
+                                                         double beta,
+                                                         double *__restrict__ stats,
+                                                         float *__restrict__ kl,
+                                                         float *__restrict__ loss) {
+    using T = typename D::T;
+    __shared__ float red[2 * (TWICE_BLK / 64)];
+    const int64_t r = blockIdx.x;
+    const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
+    const int64_t h = head_len<T>(w, s, t);
+    OpStats<3> o1;
+    sweep<D, 4, true, TWICE_BLK>(s, t, w, h, o1);
+    const MZ ms = block_mz<TWICE_BLK>(MZ{o1.a.m, o1.a.z}, red);
+    const MZ mt = block_mz<TWICE_BLK>(MZ{o1.b.m, o1.b.z}, red);
+    const bool undefined = ms.m == NINF || mt.m == NINF;
+    const double lzs = ms.m == NINF ? -__builtin_inf() : lnz_from_z(ms.m, (double)ms.z);
+    const double lzt = mt.m == NINF ? -__builtin_inf() : lnz_from_z(mt.m, (double)mt.z);
+    if (threadIdx.x == 0) {
+        double *o = stats + r * 4;
+        o[0] = ms.m;
+        o[1] = lzs;
+        o[2] = mt.m;
+        o[3] = lzt;
+    }
+    float v[2] = {0.0f, 0.0f};
+    double Zs = 1.0, Zt = 1.0;
+    if (!undefined) {
+        Zs = z_from_stats(ms.m, lzs);
+        Zt = z_from_stats(mt.m, lzt);
+        OpDiv<INTERIOR> op;
+        op.cs = refc(ms.m);
+        op.ct = refc(mt.m);
+        op.bf = (float)beta;
+        op.gam = (float)((1.0 - beta) * Zt / Zs);
+        op.rf = (float)log2(Zs / Zt);
+        sweep<D, 4, true, TWICE_BLK>(s, t, w, h, op);
+        v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
+        v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
+    }
+    block_sum<2, TWICE_BLK>(v, red);
+    if (threadIdx.x == 0)
+        finalize_row(INTERIOR, beta, undefined, v[0] * (float)(1.0 / Zt),
+                     v[1] * (float)(1.0 / Zs), NINF, kl + 2 * r, loss + r);
+}
+
+template <class D, int NVT>
 hipError_t row_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
                       float *loss, hipStream_t st) {
-    hipLaunchKernelGGL((k_fwd_row<D, MODE, NVT>), dim3((unsigned)N), dim3(FB), 0, st, sh.s, sh.t,
+    hipLaunchKernelGGL((k_fwd_row<D, NVT>), dim3((unsigned)N), dim3(FB), 0, st, sh.s, sh.t,
                        sh.width, beta, stats, kl, loss);
     return hipGetLastError();
 }
 
-template <class D, int MODE>
+// Row held in registers when the layout allows it, else the two sweeps.
+template <class D>
 hipError_t fused_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
-                        float *loss, hipStream_t st, bool *used) {
+                        float *loss, hipStream_t st) {
     constexpr int VEC = D::VEC;
-    *used = false;
     const int64_t w = sh.width;
-    if (w <= 0 || w % VEC != 0 || N <= 0 || N > 0x7fffffffLL) return hipSuccess;
     const int64_t nv = w / VEC;
-    if (nv > (int64_t)FB * FUSED_NVT_MAX) return hipSuccess;
+    bool regs = w > 0 && w % VEC == 0 && nv <= (int64_t)FB * FUSED_NVT_MAX;
     const int esize = (int)sizeof(typename D::T);
     const RowView *views[2] = {&sh.s, &sh.t};
     for (const RowView *v : views) {  // every row must start on a 16-byte boundary
-        if (reinterpret_cast<uintptr_t>(v->p) % 16 != 0) return hipSuccess;
-        if ((v->rs * esize) % 16 != 0 && N > 1) return hipSuccess;
-        if (v->rpb > 0 && (v->bs * esize) % 16 != 0) return hipSuccess;
+        if (reinterpret_cast<uintptr_t>(v->p) % 16 != 0) regs = false;
+        if ((v->rs * esize) % 16 != 0 && N > 1) regs = false;
+        if (v->rpb > 0 && (v->bs * esize) % 16 != 0) regs = false;
     }
-    hipError_t e;
-    if (nv <= FB) e = row_launch<D, MODE, 1>(sh, N, beta, stats, kl, loss, st);
-    else if (nv <= 2 * FB) e = row_launch<D, MODE, 2>(sh, N, beta, stats, kl, loss, st);
-    else if (nv <= 4 * FB) e = row_launch<D, MODE, 4>(sh, N, beta, stats, kl, loss, st);
-    else e = row_launch<D, MODE, FUSED_NVT_MAX>(sh, N, beta, stats, kl, loss, st);
-    if (e == hipSuccess) *used = true;
-    return e;
-}
-
-template <class D>
-hipError_t fused_mode(int mode, const Shard &sh, int64_t N, double beta, double *stats,
-                      float *kl, float *loss, hipStream_t st, bool *used) {
-    if (mode == INTERIOR) return fused_launch<D, INTERIOR>(sh, N, beta, stats, kl, loss, st, used);
-    if (mode == FWD_KL) return fused_launch<D, FWD_KL>(sh, N, beta, stats, kl, loss, st, used);
-    return fused_launch<D, REV_KL>(sh, N, beta, stats, kl, loss, st, used);
+    if (!regs) {
+        hipLaunchKernelGGL(k_fwd_twice<D>, dim3((unsigned)N), dim3(TWICE_BLK), 0, st, sh.s,
+                           sh.t, w, beta, stats, kl, loss);
+        return hipGetLastError();
+    }
+    if (nv <= FB) return row_launch<D, 1>(sh, N, beta, stats, kl, loss, st);
+    if (nv <= 2 * FB) return row_launch<D, 2>(sh, N, beta, stats, kl, loss, st);
+    if (nv <= 4 * FB) return row_launch<D, 4>(sh, N, beta, stats, kl, loss, st);
+    return row_launch<D, FUSED_NVT_MAX>(sh, N, beta, stats, kl, loss, st);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_fused(int dtype, int mode, const Shard &sh, int64_t N, double beta,
-                            double *stats, float *kl, float *loss, hipStream_t st, bool *used) {
+hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
+                            float *kl, float *loss, hipStream_t st) {
     switch (dtype) {
-        case 0: return fused_mode<F32>(mode, sh, N, beta, stats, kl, loss, st, used);
-        case 1: return fused_mode<F16>(mode, sh, N, beta, stats, kl, loss, st, used);
-        default: return fused_mode<BF16>(mode, sh, N, beta, stats, kl, loss, st, used);
+        case 0: return fused_launch<F32>(sh, N, beta, stats, kl, loss, st);
+        case 1: return fused_launch<F16>(sh, N, beta, stats, kl, loss, st);
+        default: return fused_launch<BF16>(sh, N, beta, stats, kl, loss, st);
     }
 }
 

@@ -30,12 +30,10 @@ hipError_t launch_div(int dtype, int mode, const Shard &sh, int64_t N, const dou
 hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
                                const double *stats, double beta, float *kl, float *loss,
                                hipStream_t st);
-// Single-HBM-pass forward (statistics + divergence) of a single shard whose rows fit
-// one workgroup.  Sets *used = false, launching nothing, when the shard is not eligible
-// (row width not a multiple of 16 bytes or wider than 256 * FUSED_NVT_MAX vectors,
-// rows not 16-byte aligned); the caller then runs the three-launch path.
-hipError_t launch_fwd_fused(int dtype, int mode, const Shard &sh, int64_t N, double beta,
-                            double *stats, float *kl, float *loss, hipStream_t st, bool *used);
+// Interior JSD forward (0 < beta < 1) of a single shard in one launch: statistics,
+// then divergence, one workgroup per row (held in registers when the row fits).
+hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
+                            float *kl, float *loss, hipStream_t st);
 
 // Row chunks of the streaming gradient kernels: cw columns per workgroup (a multiple
 // of GRAD_BLOCK vectors), nchunk chunks per row, N * nchunk workgroups in all.

@@ -13,31 +13,6 @@ namespace vjsd {
 
 namespace {
 
-template <int WHICH>
-struct OpStats {
-    Online a, b;  // first and second swept input
-    template <int NV, int W>
-    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
-                                        const int64_t (&)[NV]) {
-        a.add<NV * W>(&x[0][0]);
-        if (WHICH == 3) b.add<NV * W>(&y[0][0]);
-    }
-};
-
-__device__ __forceinline__ MZ block_mz(MZ v, float *red) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_mz(v);
-    if (lane == 0) {
-        red[2 * wave] = v.m;
-        red[2 * wave + 1] = v.z;
-    }
-    __syncthreads();
-    MZ acc{red[0], red[1]};
-    for (int k = 1; k < NWAVE; ++k) acc = mz_combine(acc, MZ{red[2 * k], red[2 * k + 1]});
-    __syncthreads();
-    return acc;
-}
-
 // One workgroup per row of the shard.  part_k[r*8 + 0..3] = (m_s, z_s, m_t, z_t) with
 // z relative to refc(m); an empty shard writes (-inf, 0).
 template <class D, int WHICH>

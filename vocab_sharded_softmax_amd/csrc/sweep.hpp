@@ -106,4 +106,35 @@ struct Online {
     }
 };
 
+// Sweep op of the statistics pass: online (max, sum-exp) of the first input, and of
+// the second when WHICH == 3.
+template <int WHICH>
+struct OpStats {
+    Online a, b;  // first and second swept input
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
+                                        const int64_t (&)[NV]) {
+        a.add<NV * W>(&x[0][0]);
+        if (WHICH == 3) b.add<NV * W>(&y[0][0]);
+    }
+};
+
+// (max, sum-exp) over a BLK-lane workgroup, combined in wave order; red holds
+// 2 * (BLK / 64) floats.  Every lane returns the result.
+template <int BLK = BLOCK>
+__device__ __forceinline__ MZ block_mz(MZ v, float *red) {
+    constexpr int NW = BLK / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_mz(v);
+    if (lane == 0) {
+        red[2 * wave] = v.m;
+        red[2 * wave + 1] = v.z;
+    }
+    __syncthreads();
+    MZ acc{red[0], red[1]};
+    for (int k = 1; k < NW; ++k) acc = mz_combine(acc, MZ{red[2 * k], red[2 * k + 1]});
+    __syncthreads();
+    return acc;
+}
+
 }  // namespace vjsd
