@@ -36,37 +36,10 @@ __device__ __forceinline__ uint32_t ninf_word<F16>() { return 0xfc00fc00u; }
 template <>
 __device__ __forceinline__ uint32_t ninf_word<BF16>() { return 0xff80ff80u; }
 
-template <class D>
-__device__ __forceinline__ void unpack(const uint4 &v, float (&x)[D::VEC]);
-template <>
-__device__ __forceinline__ void unpack<F32>(const uint4 &v, float (&x)[4]) {
-    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
-}
-template <>
-__device__ __forceinline__ void unpack<BF16>(const uint4 &v, float (&x)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-template <>
-__device__ __forceinline__ void unpack<F16>(const uint4 &v, float (&x)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f16x2 h = __builtin_bit_cast(f16x2, w[i]);
-        x[2 * i] = (float)h.x;
-        x[2 * i + 1] = (float)h.y;
-    }
-}
-
 // Empty register barrier: the compiler must assume the packed vectors changed, so it
 // re-widens them in each sweep instead of keeping NVT * 2 * VEC floats alive.
-__device__ __forceinline__ void opaque(uint4 &v) {
-    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+__device__ __forceinline__ void opaque(u32x4 &v) {
+    asm volatile("" : "+v"(v));
 }
 
 __device__ __forceinline__ void block_max2(float &a, float &b, float *red) {
@@ -122,17 +95,17 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
     const int64_t r = blockIdx.x;
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const int64_t nv = w / VEC;  // whole vectors: the host requires w % VEC == 0
-    uint4 xs[NVT], xt[NVT];
+    u32x4 xs[NVT], xt[NVT];
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
         const int64_t j = threadIdx.x + (int64_t)i * FB;
         if (j < nv) {
-            xs[i] = *reinterpret_cast<const uint4 *>(s + j * VEC);
-            xt[i] = *reinterpret_cast<const uint4 *>(t + j * VEC);
+            xs[i] = ld16<true>(s + j * VEC);
+            xt[i] = ld16<true>(t + j * VEC);
         } else {
             const uint32_t q = ninf_word<D>();
-            xs[i] = make_uint4(q, q, q, q);
-            xt[i] = make_uint4(q, q, q, q);
+            xs[i] = u32x4{q, q, q, q};
+            xt[i] = u32x4{q, q, q, q};
         }
     }
     // ---- statistics: row max, then sum of 2^(x log2e - c)
@@ -140,8 +113,8 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
         float a[VEC], b[VEC];
-        unpack<D>(xs[i], a);
-        unpack<D>(xt[i], b);
+        widen<D>(xs[i], a);
+        widen<D>(xt[i], b);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             ms = fmaxf(ms, a[e]);
@@ -159,8 +132,8 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
         float a[VEC], b[VEC], ea[VEC], eb[VEC];
-        unpack<D>(xs[i], a);
-        unpack<D>(xt[i], b);
+        widen<D>(xs[i], a);
+        widen<D>(xt[i], b);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             ea[e] = ex2(fmaf(a[e], L2E, -cs));
@@ -207,8 +180,8 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 #pragma unroll
         for (int i = 0; i < NVT; ++i) {
             float a[VEC], b[VEC];
-            unpack<D>(xs[i], a);
-            unpack<D>(xt[i], b);
+            widen<D>(xs[i], a);
+            widen<D>(xt[i], b);
             op.template add<VEC>(a, b);
         }
         pt = op.At;
@@ -222,7 +195,8 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
 // TWICE_BLK lanes, so that two workgroups fill a CU: about 512 rows are in flight, few
-// enough that much of the second sweep is served by the caches.
+// enough that much of the second sweep is served by the caches.  The first sweep reads
+// with the default cache policy (its data is wanted again), the second streams.
 constexpr int TWICE_BLK = 512;
 
 template <class D>
@@ -261,7 +235,7 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
         op.bf = (float)beta;
         op.gam = (float)((1.0 - beta) * Zt / Zs);
         op.rf = (float)log2(Zs / Zt);
-        sweep<D, 4, true, TWICE_BLK>(s, t, w, h, op);
+        sweep<D, 4, true, TWICE_BLK, true>(s, t, w, h, op);
         v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
         v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
     }

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(BLOCK) void k_div(RowView sv, RowView tv, int64_t w
         op.bf = (float)beta;
         op.gam = (float)((1.0 - beta) * k.Zt / k.Zs);
         op.rf = (float)k.r;
-        sweep<D, 4, true>(s, t, w, head_len<T>(w, s, t), op);
+        sweep<D, 4, true, BLOCK, true>(s, t, w, head_len<T>(w, s, t), op);
         float v[2] = {(op.At[0] + op.At[1]) + (op.At[2] + op.At[3]),
                       (op.As[0] + op.As[1]) + (op.As[2] + op.As[3])};
         block_sum<2>(v, red);
@@ -144,8 +144,8 @@ struct OpBwd {
                 }
             }
             if constexpr (W == D::VEC) {
-                if (WS) store_vec<D>(gs + col[j], os);
-                if (WT) store_vec<D>(gt + col[j], ot);
+                if (WS) store_vec<D, true>(gs + col[j], os);
+                if (WT) store_vec<D, true>(gt + col[j], ot);
             } else {
 #pragma unroll
                 for (int i = 0; i < W; ++i) {
@@ -228,8 +228,9 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
     op.Ht = k[7];
     op.Gs = k[8];
     op.Gt = k[9];
-    // the vector path needs every view of the chunk at the same offset inside 16 bytes
-    sweep<D, 1, true, GRAD_BLOCK>(s, t, n, head_len<T>(n, s, t, gs, gt), op);
+    // the vector path needs every view of the chunk at the same offset inside 16 bytes;
+    // inputs and gradients are touched once, so loads and stores stream
+    sweep<D, 1, true, GRAD_BLOCK, true>(s, t, n, head_len<T>(n, s, t, gs, gt), op);
 }
 
 template <class D, int MODE>

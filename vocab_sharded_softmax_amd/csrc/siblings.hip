@@ -110,7 +110,7 @@ __global__ __launch_bounds__(BLOCK) void k_kl1(RowView sv, RowView tv, int64_t w
         const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
         const T *a = REV ? s : t, *b = REV ? t : s;
         OpKL1 op;
-        sweep<D, 4, true>(a, b, w, head_len<T>(w, a, b), op);
+        sweep<D, 4, true, BLOCK, true>(a, b, w, head_len<T>(w, a, b), op);
         p = {op.ma, op.za, op.mb, op.zb, op.A, op.F};
         // wave reduction in lane order, then waves in order
 #pragma unroll
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(BLOCK) void k_ent1(RowView xv, int64_t w, float *__
     if (w > 0) {
         const T *x = row_ptr<T>(xv, r);
         OpEnt1 op;
-        sweep<D, 4, false>(x, x, w, head_len<T>(w, x), op);
+        sweep<D, 4, false, BLOCK, true>(x, x, w, head_len<T>(w, x), op);
         p = {op.m, op.z, op.B};
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
@@ -318,7 +318,7 @@ struct OpEntBwd {
                 const float u = fmaxf(fmaf(x[j][i], L2E, -c), U_FLOOR);
                 o[i] = (C * ex2(u)) * (u - R);
             }
-            if constexpr (W == D::VEC) store_vec<D>(gx + col[j], o);
+            if constexpr (W == D::VEC) store_vec<D, true>(gx + col[j], o);
             else
 #pragma unroll
                 for (int i = 0; i < W; ++i) store1<D>(gx + col[j] + i, o[i]);
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_ent_bwd(RowView xv, RowMView gv,
     op.c = k[0];
     op.C = k[1];
     op.R = k[2];
-    sweep<D, 1, false, GRAD_BLOCK>(x, x, n, head_len<T>(n, x, gx), op);
+    sweep<D, 1, false, GRAD_BLOCK, true>(x, x, n, head_len<T>(n, x, gx), op);
 }
 
 // ---- log-probabilities ----------------------------------------------------------------
@@ -421,7 +421,7 @@ struct OpLpBwd {
             float o[W];
 #pragma unroll
             for (int i = 0; i < W; ++i) o[i] = C * ex2(fmaxf(fmaf(x[j][i], L2E, -c), U_FLOOR));
-            if constexpr (W == D::VEC) store_vec<D>(gx + col[j], o);
+            if constexpr (W == D::VEC) store_vec<D, true>(gx + col[j], o);
             else
 #pragma unroll
                 for (int i = 0; i < W; ++i) store1<D>(gx + col[j] + i, o[i]);
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, 
     op.gx = gx;
     op.c = k[0];
     op.C = k[1];
-    sweep<D, 1, false, GRAD_BLOCK>(x, x, n, head_len<T>(n, x, gx), op);
+    sweep<D, 1, false, GRAD_BLOCK, true>(x, x, n, head_len<T>(n, x, gx), op);
     __syncthreads();  // this chunk's streamed values land before the id fix-ups
     const int64_t *id = ids + r * K;
     const float *g = grad + r * K;

@@ -26,13 +26,13 @@ __global__ __launch_bounds__(BLOCK) void k_stats(RowView sv, RowView tv, int64_t
         if (WHICH == 3) {
             const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
             OpStats<3> op;
-            sweep<D, 4, true>(s, t, w, head_len<T>(w, s, t), op);
+            sweep<D, 4, true, BLOCK, true>(s, t, w, head_len<T>(w, s, t), op);
             ms = {op.a.m, op.a.z};
             mt = {op.b.m, op.b.z};
         } else {
             const T *x = row_ptr<T>(WHICH == 1 ? sv : tv, r);
             OpStats<1> op;
-            sweep<D, 4, false>(x, x, w, head_len<T>(w, x), op);
+            sweep<D, 4, false, BLOCK, true>(x, x, w, head_len<T>(w, x), op);
             (WHICH == 1 ? ms : mt) = {op.a.m, op.a.z};
         }
         if (WHICH & 1) ms = block_mz(ms, red);

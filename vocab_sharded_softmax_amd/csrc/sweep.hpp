@@ -9,14 +9,15 @@
 //                                       const int64_t (&col)[NV])
 // receives NV groups of W consecutive elements of the first and second input,
 // widened to fp32, starting at the given columns (W is the vector width, or 1 in
-// the head and tail).  One-input ops ignore `b`.
+// the head and tail).  One-input ops ignore `b`.  STREAM reads the body with the
+// nontemporal cache policy (data read once).
 #pragma once
 
 #include "device.hpp"
 
 namespace vjsd {
 
-template <class D, int U, bool TWO, int BLK = BLOCK, class Op>
+template <class D, int U, bool TWO, int BLK = BLOCK, bool STREAM = false, class Op>
 __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
                                       const typename D::T *__restrict__ t, int64_t w, int64_t h,
                                       Op &op) {
@@ -42,8 +43,8 @@ __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
         for (int u = 0; u < U; ++u) {
             const int64_t q = (v + (int64_t)u * BLOCK) * VEC;
             c[u] = h + q;
-            load_vec<D>(sb + q, a[u]);
-            if (TWO) load_vec<D>(tb + q, b[u]);
+            load_vec<D, STREAM>(sb + q, a[u]);
+            if (TWO) load_vec<D, STREAM>(tb + q, b[u]);
         }
         op.template run<U, VEC>(a, b, c);
     }
@@ -51,8 +52,8 @@ __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
         float a[1][VEC], b[1][VEC];
         const int64_t q = v * VEC;
         const int64_t c[1] = {h + q};
-        load_vec<D>(sb + q, a[0]);
-        if (TWO) load_vec<D>(tb + q, b[0]);
+        load_vec<D, STREAM>(sb + q, a[0]);
+        if (TWO) load_vec<D, STREAM>(tb + q, b[0]);
         else
 #pragma unroll
             for (int i = 0; i < VEC; ++i) b[0][i] = 0.0f;
@@ -67,7 +68,8 @@ __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
     }
 }
 
-// Writes n zeros of the storage format (head / 16-byte body / tail), BLK lanes.
+// Writes n zeros of the storage format (head / 16-byte body / tail), BLK lanes; the
+// body with streaming stores.
 template <class D, int BLK>
 __device__ __forceinline__ void zero_span(typename D::T *p, int64_t n) {
     const int64_t h = head_len<typename D::T>(n, p);
@@ -76,7 +78,7 @@ __device__ __forceinline__ void zero_span(typename D::T *p, int64_t n) {
     float z[D::VEC];
 #pragma unroll
     for (int i = 0; i < D::VEC; ++i) z[i] = 0.0f;
-    for (int64_t v = threadIdx.x; v < nv; v += BLK) store_vec<D>(p + h + v * D::VEC, z);
+    for (int64_t v = threadIdx.x; v < nv; v += BLK) store_vec<D, true>(p + h + v * D::VEC, z);
     for (int64_t i = h + nv * D::VEC + threadIdx.x; i < n; i += BLK) store1<D>(p + i, 0.0f);
 }
 
