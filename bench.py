@@ -34,15 +34,22 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "JSD fwd+bwd tokens/s and HBM GB/s (% peak), N=8192 V=151936 bf16, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CSRC = os.path.join(ROOT, "vocab_sharded_softmax_amd", "csrc")
+# the sources each profiled kernel is compiled from: its counters stay valid while
+# these files are unchanged
+HEADERS = ["device.hpp", "sweep.hpp", "divergence.hpp", "kernels.hpp"]
+KERNEL_SOURCES = {
+    "bwd_bf16_interior_both": ["jsd.hip"] + HEADERS,
+    "fwd_twice_bf16": ["fused.hip"] + HEADERS,
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def csrc_digest() -> str:
+def sources_digest(names) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(names):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -57,8 +64,10 @@ def parse():
     p.add_argument("--no-siblings", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="wall-clock budget of the oracle sample")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time the step only (no per-part, branch, shard-width or sibling rows)")
     p.add_argument("--calib-copy", action="store_true",
-                   help="only run a plain 2 GiB device copy (counter calibration for rocprofv3)")
+                   help="only run a streaming 2 GiB device copy (counter calibration for rocprofv3)")
     return p.parse_args()
 
 
@@ -82,16 +91,65 @@ class Timer:
         v = [a.elapsed_time(b) for a, b in self.spans.get(name, [])]
         return sum(v) / len(v) if v else float("nan")
 
+    def spread(self, name):
+        v = sorted(a.elapsed_time(b) for a, b in self.spans.get(name, []))
+        if not v:
+            return None
+        mid = len(v) // 2
+        med = v[mid] if len(v) % 2 else 0.5 * (v[mid - 1] + v[mid])
+        return {"median": round(med, 4), "min": round(v[0], 4), "max": round(v[-1], 4)}
+
 
 def calib_copy(torch):
+    """Three streaming copies of 2 GiB (k_probe_copy): each reads and writes exactly n
+    bytes, so the byte counters of a profiled run divided by n give their scale."""
+    import vocab_sharded_softmax_amd as vj
+
     n = 1 << 31  # bytes
     src = torch.empty(n // 4, dtype=torch.float32, device="cuda").uniform_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(3):
-        dst.copy_(src)
+        vj.vjsd_membw_probe(src, dst, 1)
     torch.cuda.synchronize()
-    print(json.dumps({"calib_copy_bytes": n, "launches": 3}))
+    print(json.dumps({"calib_copy_bytes": n, "launches": 3, "kernel": "k_probe_copy"}))
+
+
+def ceilings(torch, vj, x, y, out, reps=5):
+    """Measured streaming ceilings on this GPU: a read of x and y (two launches) and
+    a copy of x into out, with the library's probe kernels."""
+    nb = x.numel() * x.element_size()
+    res = {}
+    for name, fn, moved in (("read", lambda: (vj.vjsd_membw_probe(x, out, 0),
+                                              vj.vjsd_membw_probe(y, out, 0)), 2 * nb),
+                            ("copy", lambda: vj.vjsd_membw_probe(x, out, 1), 2 * nb)):
+        fn()
+        tm = Timer(torch)
+        for _ in range(reps):
+            a = tm.mark()
+            fn()
+            tm.add("x", a, tm.mark())
+        torch.cuda.synchronize()
+        res[f"{name}_gbps"] = round(moved / (tm.ms("x") * 1e-3) / 1e9, 1)
+    res["bytes_per_launch"] = nb
+    return res
+
+
+def clock_state():
+    """Current shader and memory clock levels from sysfs, where readable."""
+    import glob
+
+    out = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
+        try:
+            with open(path) as f:
+                cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+        except OSError:
+            continue
+        key = path.split("/")[-3] + "_" + path.rsplit("_", 1)[-1]
+        if cur:
+            out[key] = cur[0]
+    return out or None
 
 
 def cpu_baseline(torch, s, t, gout, budget_s):
@@ -123,10 +181,10 @@ def traffic_entry(kernel_key):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
-    if rec.get("csrc_sha") != csrc_digest():
-        return None  # the kernels changed since the counters were taken
     k = rec.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("bytes_per_launch")
+    if k is None or k.get("sources_sha") != sources_digest(KERNEL_SOURCES[kernel_key]):
+        return None  # the kernel changed since the counters were taken
+    return k.get("bytes_per_launch")
 
 
 def main():
@@ -205,29 +263,38 @@ def main():
     per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas}
     log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
 
-    # the same forward as three separate launches (statistics, merge, divergence),
-    # timed one by one for comparison with the one-launch forward above
-    tm3 = Timer(torch)
-    for i in range(2):
-        three_launch_forward(betas[i % 3], Timer(torch))
-    for i in range(10):
-        three_launch_forward(betas[i % 3], tm3)
-    torch.cuda.synchronize()
-    three = {k: round(tm3.ms(k), 4) for k in ("stats", "merge", "div", "forward")}
-
-    # the KL branches of the same engine on the same data
-    branches = {}
-    for beta in (0.0, 1.0):
-        for _ in range(2):
-            step(beta, False)
-        tm = Timer(torch)
-        for _ in range(5):
-            a = tm.mark()
-            vj.vjsd_forward(sh, beta, part, stats, kl, loss)
-            vj.vjsd_bwd(shg, stats, kl, beta, gout, part)
-            tm.add("x", a, tm.mark())
+    three = branches = siblings = tp8 = None
+    if not args.no_extras:
+        # the same forward as three separate launches (statistics, merge, divergence),
+        # timed one by one for comparison with the one-launch forward above
+        tm3 = Timer(torch)
+        for i in range(2):
+            three_launch_forward(betas[i % 3], Timer(torch))
+        for i in range(10):
+            three_launch_forward(betas[i % 3], tm3)
         torch.cuda.synchronize()
-        branches[f"jsd_beta{beta:g}_fwd_bwd_ms"] = round(tm.ms("x"), 4)
+        three = {k: round(tm3.ms(k), 4) for k in ("stats", "merge", "div", "forward")}
+
+        # the KL branches of the same engine on the same data
+        branches = {}
+        for beta in (0.0, 1.0):
+            for _ in range(2):
+                step(beta, False)
+            tm = Timer(torch)
+            for _ in range(5):
+                a = tm.mark()
+                vj.vjsd_forward(sh, beta, part, stats, kl, loss)
+                vj.vjsd_bwd(shg, stats, kl, beta, gout, part)
+                tm.add("x", a, tm.mark())
+            torch.cuda.synchronize()
+            branches[f"jsd_beta{beta:g}_fwd_bwd_ms"] = round(tm.ms("x"), 4)
+
+    # streaming read and copy ceilings measured on the same buffers
+    ceil = ceilings(torch, vj, s, t, gs)
+    ceil["bwd_frac_of_copy"] = round(achieved / ceil["copy_gbps"], 4)
+    fwd_ms = timer.ms("forward")
+    ceil["fwd_two_reads_frac_of_read"] = round(
+        4 * tensor_bytes / (fwd_ms * 1e-3) / 1e9 / ceil["read_gbps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -236,8 +303,9 @@ def main():
     del gs, gt, shg, sh, s, t, b
     torch.cuda.empty_cache()
 
-    siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
-    tp8 = tp8_forward(torch, vj, synth)
+    if not args.no_extras:
+        siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
+        tp8 = tp8_forward(torch, vj, synth)
 
     out = {
         "metric": METRIC,
@@ -258,13 +326,20 @@ def main():
         "hbm_gbps": round(bytes_alg / (ms_step * 1e-3) / 1e9, 1),
         "hbm_frac": round(bytes_alg / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "bytes_alg_per_step": bytes_alg,
+        # one forward read and one backward read of s and t, plus the gradient writes
+        "bytes_compulsory_per_step": 6 * tensor_bytes,
+        "hbm_frac_compulsory": round(6 * tensor_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "roofline": {"kernel": "k_bwd<BF16, interior, both grads>", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic_entry("bwd_bf16_interior_both"),
                      "bytes_per_launch": bytes_bwd, "avg_launch_ms": round(bwd_ms, 4)},
         "cpu_baseline": cpu,
+        "step_ms_spread": timer.spread("step"),
         "kernel_ms": per_kernel,
+        "kernel_ms_spread": {k: timer.spread(k) for k in ("forward", "bwd")},
+        "ceiling": ceil,
+        "clocks": clock_state(),
         "forward_parts_ms": three,
         "tp8_shard": tp8,
         "step_ms_by_beta": per_beta,

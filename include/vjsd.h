@@ -239,6 +239,20 @@ VJSD_API int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype
                   const double *stats, const int64_t *ids, int K, int64_t ignore_index,
                   const float *grad, float *part, void *stream);
 
+/*
+ * Memory-bandwidth probe: the streaming ceiling the passes above are judged against
+ * (their inputs and gradients move through HBM once per pass with 16-byte
+ * streaming accesses, so a plain streaming read or copy of the same size bounds
+ * them).  op 0 reads `bytes` from src; op 1 copies `bytes` from src to dst; both use
+ * 16-byte nontemporal loads (and stores), consecutive lanes on consecutive 16-byte
+ * words.  bytes must be a positive multiple of 16 and src / dst 16-byte aligned.
+ * op 0 writes at most 16 bytes at dst (only if the data hashes to a fixed value; the
+ * write keeps the reads live); op 1 writes `bytes` at dst, which must not overlap
+ * src.  VJSD_ERR_ARG for a bad op, size or pointer; VJSD_ERR_HIP for a failed
+ * launch.
+ */
+VJSD_API int vjsd_membw_probe(const void *src, void *dst, size_t bytes, int op, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
@@ -162,6 +162,17 @@ def test_entropy_and_kl_check_their_arguments():
     assert lib.ventropy_bwd(a, 1, 4, 2, FAKE, FAKE, FAKE, None, None) == ARG
     assert lib.vkl_fwd(a, 1, 4, 2, 1, FAKE, FAKE, None, FAKE, None) == ARG
     assert lib.vkl_bwd(a, 1, 4, 2, 1, FAKE, FAKE, None, FAKE, None) == ARG
+
+
+def test_membw_probe_checks_its_arguments():
+    assert lib.vjsd_membw_probe(FAKE, 2 * FAKE, 1024, 2, None) == ARG  # unknown op
+    assert lib.vjsd_membw_probe(FAKE, 2 * FAKE, 0, 0, None) == ARG  # empty
+    assert lib.vjsd_membw_probe(FAKE, 2 * FAKE, 1000 + 4, 0, None) == ARG  # not whole words
+    assert lib.vjsd_membw_probe(FAKE + 4, 2 * FAKE, 1024, 0, None) == ARG  # misaligned src
+    assert lib.vjsd_membw_probe(FAKE, 2 * FAKE + 8, 1024, 1, None) == ARG  # misaligned dst
+    assert lib.vjsd_membw_probe(None, 2 * FAKE, 1024, 0, None) == ARG
+    assert lib.vjsd_membw_probe(FAKE, None, 1024, 1, None) == ARG
+    assert lib.vjsd_membw_probe(FAKE, FAKE + 512, 1024, 1, None) == ARG  # overlapping copy
 
 
 def test_default_split_matches_the_pages_uneven_example():

@@ -6,9 +6,9 @@ The compute path is libvjsd.so (hand-written HIP kernels for gfx950, C ABI in
 library has not been built.
 """
 from ._abi import (ShardSet, VjsdArgumentError, VjsdError, new_part, vjsd_bwd, vjsd_forward,
-                   vjsd_fwd,
-                   vjsd_merge, vjsd_stats, vjsd_strerror, vjsd_workspace_bytes, ventropy_bwd,
-                   ventropy_fwd, vkl_bwd, vkl_fwd, vlogprobs_bwd, vlogprobs_fwd)
+                   vjsd_fwd, vjsd_membw_probe, vjsd_merge, vjsd_stats, vjsd_strerror,
+                   vjsd_workspace_bytes, ventropy_bwd, ventropy_fwd, vkl_bwd, vkl_fwd,
+                   vlogprobs_bwd, vlogprobs_fwd)
 from ._abi import LIB_PATH
 from .functional import entropy, jsd, kl_div, logprobs
 
@@ -16,5 +16,5 @@ __all__ = [
     "jsd", "kl_div", "entropy", "logprobs", "ShardSet", "VjsdError", "VjsdArgumentError",
     "vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vkl_fwd", "vkl_bwd", "ventropy_fwd",
     "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd", "vjsd_strerror", "vjsd_workspace_bytes",
-    "new_part", "LIB_PATH",
+    "vjsd_membw_probe", "new_part", "LIB_PATH",
 ]

@@ -65,6 +65,7 @@ def _load():
         "ventropy_bwd": ([SP, I, I64, I, P, P, P, P, P], I),
         "vlogprobs_fwd": ([SP, I, I64, I, I64, P, I, I64, P, P, P, P, P], I),
         "vlogprobs_bwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P, P], I),
+        "vjsd_membw_probe": ([P, P, ctypes.c_size_t, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -193,6 +194,18 @@ def vjsd_strerror(code: int) -> str:
 
 def vjsd_workspace_bytes(N: int, S: int) -> int:
     return lib.vjsd_workspace_bytes(N, S)
+
+
+def vjsd_membw_probe(src: torch.Tensor, dst: torch.Tensor, op: int, stream=None) -> None:
+    """Streaming read (op 0) of all of `src`, or copy (op 1) of `src` into `dst`."""
+    for x, name in ((src, "src"), (dst, "dst")):
+        _require_gpu(x, name)
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if op == 1 and dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _check(lib.vjsd_membw_probe(src.data_ptr(), dst.data_ptr(), nbytes, op, _stream(stream)))
 
 
 def part_floats(N: int, S: int) -> int:
