@@ -11,9 +11,10 @@ generalized JSD with Triton kernels"; [OPS-PR] DeepSpeed PR #8791 "Add
 vocabulary-parallel logprobs, entropy and KL ops".
 
 Every function takes CPU torch tensors holding the exact stored input values
-(float32, float16 or bfloat16; 2-D ``[N, V]`` with unit column stride), evaluates
-the listed rows in fp64 and returns numpy float64 arrays packed by position in
-``rows``.  ``widths`` splits the vocabulary into consecutive shards (default: one).
+(float32, float16 or bfloat16; 2-D ``[N, V]`` with unit column stride; float64
+for logits already transformed in fp64), evaluates the listed rows in fp64 and
+returns numpy float64 arrays packed by position in ``rows``.  ``widths`` splits
+the vocabulary into consecutive shards (default: one).
 """
 from __future__ import annotations
 
@@ -30,7 +31,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # A test may point the loader at another build of the same source (a planted-mistake
 # variant) to show that the pins catch it.
 _LIB_OVERRIDE = os.environ.get("VJSD_ORACLE_LIB")
-_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.float64: 3}
 
 _lib = None
 
@@ -129,6 +130,54 @@ def jsd(s, t, beta, widths=None, rows=None, gout=None, grads=True):
 def kl_div(s, t, reverse=False, **kw):
     """KL(p_t||p_s), or KL(p_s||p_t) with reverse=True: the beta = 0 / 1 branches."""
     return jsd(s, t, 1.0 if reverse else 0.0, **kw)
+
+
+def jsd_loss(s, t, beta, temperature=1.0, scale_t2=False, mask=None, reduction="none",
+             grad=None, widths=None, grads=True):
+    """The distillation loss around the per-token JSD, as a caller writes it.
+
+    The callers of the pages' per-token ops divide both logits by the temperature,
+    multiply by T^2 when asked, and average over the tokens a mask keeps ([JSD-PR,
+    Changes]: temperature, T^2 scaling, masking and normalisation are the caller's;
+    DeepSpeedExamples PR #1019: the teacher-cache route keeps the token mean and the
+    T^2 scaling and divides by a temperature other than 1 first).  Here, in fp64:
+        l_r   = JSD_beta(softmax(s_r / T), softmax(t_r / T)) * (T^2 if scale_t2)
+        rows  = l_r where mask_r, else 0 (masked rows are never evaluated)
+        "sum" : sum of l_r over the kept rows
+        "mean": that sum / max(kept rows, 1)   (no kept rows: 0)
+    ``grad`` is the upstream gradient: [N] for "none", a scalar otherwise.  Returns
+    dict(rows, out, kt, ks, gs, gt); gs / gt are d(sum_r grad_r * rows_r)/d(logits)
+    for "none", d(grad * out)/d(logits) otherwise; masked rows get exactly 0.
+    """
+    N = s.shape[0]
+    keep = np.ones(N, bool) if mask is None else np.asarray(mask).astype(bool)
+    T = float(temperature)
+    fac = T * T if scale_t2 else 1.0
+    count = int(keep.sum())
+    if reduction == "none":
+        g = np.zeros(N) if grad is None else np.asarray(grad, np.float64).copy()
+    elif reduction == "sum":
+        g = np.full(N, 0.0 if grad is None else float(grad))
+    elif reduction == "mean":
+        g = np.full(N, (0.0 if grad is None else float(grad)) / max(count, 1))
+    else:
+        raise ValueError(reduction)
+    g = np.where(keep, g * fac, 0.0)
+    st = s.double() / T  # the caller's division, here exact to fp64
+    tt = t.double() / T
+    ref = jsd(st, tt, beta, widths=widths, gout=g, grads=grads)
+    rows = np.where(keep, ref["loss"] * fac, 0.0)
+    out = None
+    if reduction != "none":
+        tot = rows[keep].sum() if count else 0.0
+        out = tot / max(count, 1) if reduction == "mean" else tot
+    res = dict(rows=rows, out=out, kt=np.where(keep, ref["kt"], 0.0),
+               ks=np.where(keep, ref["ks"], 0.0), gs=None, gt=None)
+    if grads:
+        # chain rule through x / T; masked rows contribute nothing at all
+        res["gs"] = np.where(keep[:, None], ref["gs"] / T, 0.0)
+        res["gt"] = np.where(keep[:, None], ref["gt"] / T, 0.0)
+    return res
 
 
 def entropy(x, widths=None, rows=None, gout=None, grads=True):

@@ -16,7 +16,8 @@
  *
  * Conventions.
  *   Inputs are row-major matrices of fp32, fp16 or bf16 values, widened exactly to
- *   double.  Row r, column j of an input lives at element r*ld + j.  The vocabulary
+ *   double, or of doubles (logits a caller has already transformed in fp64, such as
+ *   logits divided by a distillation temperature).  Row r, column j of an input lives at element r*ld + j.  The vocabulary
  *   [0, V) is split into S consecutive shards of the given widths (a width may be
  *   0).  Only the rows listed in rows[0..nr) are evaluated; every output is packed
  *   by position in that list, so a caller can check single rows of a huge matrix.
@@ -45,7 +46,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2, OR_F64 = 3 };
 
 /* ---- exact widening of the stored input formats ------------------------------- */
 
@@ -76,6 +77,8 @@ static double bf16_bits_to_double(uint16_t b)
 
 static double elem(const void *x, int dt, int64_t i)
 {
+    if (dt == OR_F64)
+        return ((const double *)x)[i];
     if (dt == OR_F32)
         return (double)((const float *)x)[i];
     if (dt == OR_F16)
