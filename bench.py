@@ -13,7 +13,8 @@ kernel (the backward), measured with HIP events on the stream the kernels run
 on, the fp64 CPU oracle's rate on a bounded sample of the same rows, and
 per-kernel and sibling-op timings (forward / reverse KL, entropy, top-k
 log-probabilities at N=16384, V=128256 in bf16 and fp16; the beta = 0 / 1 JSD
-branches; the one-pass forward at one tensor-parallel rank's shard width).  The HBM traffic figure comes from committed rocprofv3 counters and
+branches; the distillation-loss form at temperature 2 with a token mean, all tokens
+and 3% kept; the one-pass forward at one tensor-parallel rank's shard width).  The HBM traffic figure comes from committed rocprofv3 counters and
 is reported only while the kernel sources match the ones profiled.
 
     python bench.py [--gpus 1] [--steps 30] [--warmup 5]
@@ -288,6 +289,29 @@ def main():
                 tm.add("x", a, tm.mark())
             torch.cuda.synchronize()
             branches[f"jsd_beta{beta:g}_fwd_bwd_ms"] = round(tm.ms("x"), 4)
+
+        # the distillation-loss form: temperature 2, T^2, token mean; all tokens kept,
+        # then the few-response-tokens shape of a teacher-cache caller (3% kept)
+        loss_rows = {}
+        out1 = torch.empty(1, dtype=torch.float32, device="cuda")
+        g1 = torch.ones(1, dtype=torch.float32, device="cuda")
+        gen = torch.Generator(device="cuda").manual_seed(5)
+        for name, frac in (("all_tokens", 1.0), ("3pct_tokens", 0.03)):
+            keep = (torch.rand(N, generator=gen, device="cuda") < frac).to(torch.uint8)
+            opts = vj.loss_opts(N, 2.0, True, keep, "mean")
+
+            def lstep():
+                vj.vjsd_loss_forward(sh, 0.5, opts, part, stats, kl, loss, out1)
+                vj.vjsd_loss_backward(shg, 0.5, opts, stats, kl, g1, part)
+            lstep()
+            tm = Timer(torch)
+            for _ in range(5):
+                a = tm.mark()
+                lstep()
+                tm.add("x", a, tm.mark())
+            torch.cuda.synchronize()
+            loss_rows[name] = {"kept": int(keep.sum().item()), "fwd_bwd_ms": round(tm.ms("x"), 4)}
+        branches["jsd_loss_T2_mean"] = loss_rows
 
     # streaming read and copy ceilings measured on the same buffers
     ceil = ceilings(torch, vj, s, t, gs)

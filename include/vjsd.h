@@ -176,6 +176,61 @@ VJSD_API int vjsd_forward(const vjsd_shard *shards, int S, int64_t N, int dtype,
                           float *part, double *stats, float *kl, float *loss, void *stream);
 
 /*
+ * The distillation loss around the per-token JSD: what the pages' callers do before
+ * and after the per-token op, fused into its passes.  [JSD-PR, Changes] leaves
+ * temperature, optional T^2 scaling, masking and normalisation to the caller;
+ * DeepSpeedExamples PR #1019 ("vocab-parallel KL route for OPSD") divides both
+ * logits by a temperature other than 1 in fp32 first (a full-size fp32 copy of each
+ * input), then keeps the T^2 scaling and a token mean over the response tokens.
+ *
+ *   temperature  T > 0, finite.  Both inputs are divided by T in registers: the
+ *                kernels' exponent scale log2(e) becomes fl32(log2(e) / T), so
+ *                nothing is copied.  T = 1 reproduces vjsd_forward / vjsd_bwd.
+ *   scale_t2     nonzero: per-token losses (and their gradients) carry T^2.
+ *   mask         NULL, or a device uint8_t[N]; a zero entry drops the token: its
+ *                logits are never read, its per-token loss is 0, it is left out of
+ *                the reduction and its gradients are exactly 0.
+ *   reduction    VJSD_REDUCE_NONE: per-token losses only; VJSD_REDUCE_SUM: out[0] =
+ *                their sum over kept tokens; VJSD_REDUCE_MEAN: that sum divided by
+ *                the number of kept tokens, 0 when no token is kept (the count is
+ *                clamped at 1).  The sum runs in fp64 in a fixed order; an undefined
+ *                kept token (NaN) makes the result NaN.
+ * A NULL opts pointer means T = 1, no T^2, no mask, no reduction.
+ */
+enum { VJSD_REDUCE_NONE = 0, VJSD_REDUCE_SUM = 1, VJSD_REDUCE_MEAN = 2 };
+typedef struct {
+    double temperature;
+    int scale_t2;
+    const uint8_t *mask;
+    int reduction;
+} vjsd_loss_opts;
+
+/*
+ * Forward of the distillation loss (routed like vjsd_forward).  Writes stats[N][4]
+ * (raw row maxima, lnZ of the tempered logits), kl[N][2] (the KL pair of the
+ * tempered distributions, not scaled by T^2), rows[N] (per-token losses, times T^2
+ * when scale_t2, 0 for dropped tokens) and, for a reduction, out[0] (out may be NULL
+ * for VJSD_REDUCE_NONE).  With N == 0 only out[0] = 0 is written.  Errors as
+ * vjsd_fwd, plus VJSD_ERR_ARG for a bad temperature or reduction, or a NULL out
+ * with a reduction.
+ */
+VJSD_API int vjsd_loss_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
+                               const vjsd_loss_opts *opts, float *part, double *stats, float *kl,
+                               float *rows, float *out, void *stream);
+
+/*
+ * Backward of the distillation loss: gradients w.r.t. the raw logits, into each
+ * shard's gs / gt views (NULL gs.p / gt.p skip one, as in vjsd_bwd).  grad is the
+ * upstream gradient: float[N] per token for VJSD_REDUCE_NONE, float[1] for a
+ * reduction.  Row r's upstream scale is g_r * (T^2 if scale_t2) / T (the chain rule
+ * through x / T), g_r / max(kept, 1) for a mean, and 0 for a dropped row.  Takes
+ * the forward's stats and kl and the same opts, beta and mask.  Errors as vjsd_bwd.
+ */
+VJSD_API int vjsd_loss_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
+                                const vjsd_loss_opts *opts, const double *stats, const float *kl,
+                                const float *grad, float *part, void *stream);
+
+/*
  * Generalized JSD backward, closed form and local [JSD-PR, Changes: recompute
  * probabilities in registers; OPS-PR, How: no communication].  With g = grad_loss[r]:
  *   interior: d/ds = g (1-beta) p_s (lp_s - lM - KS),  d/dt = g beta p_t (lp_t - lM - KT)

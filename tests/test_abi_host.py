@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
@@ -42,9 +42,10 @@ def test_strerror_and_workspace():
     for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert isinstance(lib.vjsd_strerror(code), bytes)
     assert lib.vjsd_workspace_bytes(0, 4) == 0
-    # per-row constants (16 floats) + per (shard, row) partials (8 floats)
-    assert lib.vjsd_workspace_bytes(8192, 1) == 8192 * (16 + 8) * 4
-    assert lib.vjsd_workspace_bytes(4096, 4) == 4096 * (16 + 4 * 8) * 4
+    # per-row constants (16 floats) + per (shard, row) partials (8 floats) + a 64-byte
+    # scalar tail (the kept-row count of a masked mean)
+    assert lib.vjsd_workspace_bytes(8192, 1) == 8192 * (16 + 8) * 4 + 64
+    assert lib.vjsd_workspace_bytes(4096, 4) == 4096 * (16 + 4 * 8) * 4 + 64
     for N, S in ((1, 1), (64, 3), (8192, 1), (16384, 7)):  # the binding sizes it the same way
         assert abi.part_floats(N, S) * 4 == lib.vjsd_workspace_bytes(N, S)
 
@@ -162,6 +163,28 @@ def test_entropy_and_kl_check_their_arguments():
     assert lib.ventropy_bwd(a, 1, 4, 2, FAKE, FAKE, FAKE, None, None) == ARG
     assert lib.vkl_fwd(a, 1, 4, 2, 1, FAKE, FAKE, None, FAKE, None) == ARG
     assert lib.vkl_bwd(a, 1, 4, 2, 1, FAKE, FAKE, None, FAKE, None) == ARG
+
+
+def _opts(T=1.0, t2=0, mask=None, red=0):
+    return ctypes.byref(abi.LossOpts(T, t2, mask, red))
+
+
+def test_loss_entry_points_check_their_options():
+    a = shards([10])
+    fwd_ = lambda o, out=FAKE, N=4: lib.vjsd_loss_forward(a, 1, N, 2, 0.5, o, FAKE, FAKE, FAKE, FAKE,
+                                                          out, None)
+    bwd_ = lambda o: lib.vjsd_loss_backward(a, 1, 4, 2, 0.5, o, FAKE, FAKE, FAKE, FAKE, None)
+    for T in (0.0, -1.0, float("nan"), float("inf")):
+        assert fwd_(_opts(T=T)) == ARG
+        assert bwd_(_opts(T=T)) == ARG
+    for red in (-1, 3):
+        assert fwd_(_opts(red=red)) == ARG
+        assert bwd_(_opts(red=red)) == ARG
+    assert fwd_(_opts(red=2), out=None) == ARG  # a reduction needs out
+    assert fwd_(None, N=0) == OK  # no reduction, no rows: nothing to do
+    assert lib.vjsd_loss_forward(a, 1, 4, 2, 1.5, None, FAKE, FAKE, FAKE, FAKE, None, None) == BETA
+    assert lib.vjsd_loss_forward(a, 1, 4, 2, 0.5, None, None, FAKE, FAKE, FAKE, None, None) == ARG
+    assert lib.vjsd_loss_backward(a, 1, 4, 2, 0.5, None, FAKE, FAKE, None, FAKE, None) == ARG
 
 
 def test_membw_probe_checks_its_arguments():

@@ -83,9 +83,19 @@ def test_wrappers_pass_sizes_and_shards(rec):
     vj.vlogprobs_fwd(sh2, V, ids, -100, part, stats, out, err)
     vj.vlogprobs_bwd(abi.ShardSet(s, widths=[5, 7], gs=torch.empty(B, T, V, dtype=torch.bfloat16)),
                      V, stats, ids, -100, torch.empty(N, 3), part)
+    mask = torch.ones(N, dtype=torch.uint8)
+    opts = abi.loss_opts(N, 2.0, True, mask, "mean")
+    assert (opts.temperature, opts.scale_t2, opts.mask, opts.reduction) == (2.0, 1, mask.data_ptr(), 2)
+    vj.vjsd_loss_forward(sh, 0.25, opts, part, stats, kl, loss, torch.empty(1))
+    vj.vjsd_loss_backward(shg, 0.25, opts, stats, kl, torch.empty(1), part)
+    with pytest.raises(ValueError):  # a per-token backward needs N upstream gradients
+        vj.vjsd_loss_backward(shg, 0.25, abi.loss_opts(N), stats, kl, torch.empty(1), part)
+    with pytest.raises(ValueError):
+        abi.loss_opts(N, reduction="avg")
     names = [c[0] for c in rec.calls]
     assert names == ["vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vkl_fwd", "vkl_bwd",
-                     "ventropy_fwd", "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd"]
+                     "ventropy_fwd", "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd",
+                     "vjsd_loss_forward", "vjsd_loss_backward"]
     args = dict(rec.calls)
     assert args["vjsd_stats"][1:5] == (3, N, 2, 3)
     assert args["vjsd_fwd"][5] == 0.25 and args["vjsd_bwd"][6] == 0.25
@@ -105,6 +115,14 @@ def test_autograd_ops_marshal_forward_and_backward(rec):
     assert s.grad.shape == s.shape and t.grad.shape == t.shape
     loss = functional.kl_div(s, t.detach(), reverse=True)
     loss.sum().backward()
+    dl = functional.jsd_loss(s, t, 0.5, temperature=2.0, scale_t2=True,
+                             mask=torch.tensor([True, False, True, True]), reduction="mean")
+    assert dl.shape == ()
+    dl.backward()
+    with pytest.raises(ValueError):
+        functional.jsd_loss(s, t, 0.5, mask=torch.ones(3, dtype=torch.bool))
+    with pytest.raises(ValueError):
+        functional.jsd_loss(s, t, 0.5, temperature=0.0)
     e = functional.entropy([s[:, :4], s[:, 4:]])
     assert e.shape == (4,)
     lp = functional.logprobs(s, torch.tensor([0, 1, 2, -100]))

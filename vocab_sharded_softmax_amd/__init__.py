@@ -5,16 +5,17 @@ The compute path is libvjsd.so (hand-written HIP kernels for gfx950, C ABI in
 ``functional`` wraps them as autograd ops.  Importing the package fails if the
 library has not been built.
 """
-from ._abi import (ShardSet, VjsdArgumentError, VjsdError, new_part, vjsd_bwd, vjsd_forward,
-                   vjsd_fwd, vjsd_membw_probe, vjsd_merge, vjsd_stats, vjsd_strerror,
-                   vjsd_workspace_bytes, ventropy_bwd, ventropy_fwd, vkl_bwd, vkl_fwd,
-                   vlogprobs_bwd, vlogprobs_fwd)
+from ._abi import (ShardSet, VjsdArgumentError, VjsdError, loss_opts, new_part, vjsd_bwd,
+                   vjsd_forward, vjsd_fwd, vjsd_loss_backward, vjsd_loss_forward,
+                   vjsd_membw_probe, vjsd_merge, vjsd_stats, vjsd_strerror, vjsd_workspace_bytes,
+                   ventropy_bwd, ventropy_fwd, vkl_bwd, vkl_fwd, vlogprobs_bwd, vlogprobs_fwd)
 from ._abi import LIB_PATH
-from .functional import entropy, jsd, kl_div, logprobs
+from .functional import entropy, jsd, jsd_loss, kl_div, logprobs
 
 __all__ = [
-    "jsd", "kl_div", "entropy", "logprobs", "ShardSet", "VjsdError", "VjsdArgumentError",
+    "jsd", "jsd_loss", "kl_div", "entropy", "logprobs", "ShardSet", "VjsdError", "VjsdArgumentError",
     "vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vkl_fwd", "vkl_bwd", "ventropy_fwd",
     "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd", "vjsd_strerror", "vjsd_workspace_bytes",
-    "vjsd_membw_probe", "new_part", "LIB_PATH",
+    "vjsd_membw_probe", "vjsd_loss_forward", "vjsd_loss_backward", "loss_opts", "new_part",
+    "LIB_PATH",
 ]

@@ -44,6 +44,14 @@ class Shard(ctypes.Structure):
                 ("s", View), ("t", View), ("gs", View), ("gt", View)]
 
 
+class LossOpts(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_double), ("scale_t2", ctypes.c_int),
+                ("mask", ctypes.c_void_p), ("reduction", ctypes.c_int)]
+
+
+REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
@@ -66,6 +74,8 @@ def _load():
         "vlogprobs_fwd": ([SP, I, I64, I, I64, P, I, I64, P, P, P, P, P], I),
         "vlogprobs_bwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P, P], I),
         "vjsd_membw_probe": ([P, P, ctypes.c_size_t, I, P], I),
+        "vjsd_loss_forward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P, P], I),
+        "vjsd_loss_backward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -252,6 +262,39 @@ def vjsd_bwd(sh: ShardSet, stats, kl, beta: float, grad_loss, part, stream=None)
                         _ptr(kl, torch.float32, N * 2, "kl"), float(beta),
                         _ptr(grad_loss, torch.float32, N, "grad_loss"),
                         _ptr(part, torch.float32, part_floats(N, sh.S), "part"), _stream(stream)))
+
+
+def loss_opts(N: int, temperature: float = 1.0, scale_t2: bool = False, mask=None,
+              reduction: str = "none") -> LossOpts:
+    """The C options of the distillation-loss entry points; ``mask`` is a GPU uint8 [N]
+    tensor (nonzero = the token counts) or None."""
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
+    mp = _ptr(mask, torch.uint8, N, "mask") if mask is not None else None
+    return LossOpts(float(temperature), int(bool(scale_t2)), mp, REDUCTIONS[reduction])
+
+
+def vjsd_loss_forward(sh: ShardSet, beta: float, opts: LossOpts, part, stats, kl, rows,
+                      out=None, stream=None) -> None:
+    N = sh.N
+    _check(lib.vjsd_loss_forward(sh.arr, sh.S, N, sh.dtype_code, float(beta), ctypes.byref(opts),
+                                 _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                                 _ptr(stats, torch.float64, N * 4, "stats"),
+                                 _ptr(kl, torch.float32, N * 2, "kl"),
+                                 _ptr(rows, torch.float32, N, "rows"),
+                                 _ptr(out, torch.float32, 1, "out"), _stream(stream)))
+
+
+def vjsd_loss_backward(sh: ShardSet, beta: float, opts: LossOpts, stats, kl, grad, part,
+                       stream=None) -> None:
+    N = sh.N
+    ng = N if opts.reduction == 0 else 1
+    _check(lib.vjsd_loss_backward(sh.arr, sh.S, N, sh.dtype_code, float(beta), ctypes.byref(opts),
+                                  _ptr(stats, torch.float64, N * 4, "stats"),
+                                  _ptr(kl, torch.float32, N * 2, "kl"),
+                                  _ptr(grad, torch.float32, ng, "grad"),
+                                  _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                                  _stream(stream)))
 
 
 def vkl_fwd(sh: ShardSet, reverse: bool, part, stats, kl, loss, stream=None) -> None:

@@ -90,6 +90,38 @@ const float *part_of(const float *part, int k, int64_t N) {
     return part + (size_t)N * vjsd::ROWC + (size_t)k * (size_t)N * vjsd::PART_STRIDE;
 }
 
+// After the partials: one double holding the kept-row count of a masked mean.
+double *count_of(float *part, int S, int64_t N) {
+    return reinterpret_cast<double *>(part + (size_t)N * vjsd::ROWC +
+                                      (size_t)S * (size_t)N * vjsd::PART_STRIDE);
+}
+
+// Options of the loss forms, validated; NULL means T = 1, no T^2, no mask, no reduction.
+struct LossCfg {
+    double T = 1.0;
+    bool t2 = false;
+    const uint8_t *mask = nullptr;
+    int red = VJSD_REDUCE_NONE;
+};
+int loss_cfg(const vjsd_loss_opts *o, LossCfg *c) {
+    *c = LossCfg();
+    if (!o) return VJSD_OK;
+    if (!(o->temperature > 0.0 && o->temperature <= 1e30)) return VJSD_ERR_ARG;  // NaN too
+    if (o->reduction < VJSD_REDUCE_NONE || o->reduction > VJSD_REDUCE_MEAN) return VJSD_ERR_ARG;
+    c->T = o->temperature;
+    c->t2 = o->scale_t2 != 0;
+    c->mask = o->mask;
+    c->red = o->reduction;
+    return VJSD_OK;
+}
+vjsd::RowOpts row_opts(const LossCfg &c) {
+    vjsd::RowOpts o;
+    o.ks = (float)(vjsd::L2E_D / c.T);
+    o.lscale = c.t2 ? (float)(c.T * c.T) : 1.0f;
+    o.mask = c.mask;
+    return o;
+}
+
 int mode_of(double beta) {
     return beta == 0.0 ? vjsd::FWD_KL : (beta == 1.0 ? vjsd::REV_KL : vjsd::INTERIOR);
 }
@@ -114,7 +146,7 @@ const char *vjsd_strerror(int code) {
 size_t vjsd_workspace_bytes(int64_t N, int S) {
     if (N <= 0 || S <= 0) return 0;
     const size_t floats = (size_t)N * vjsd::ROWC + (size_t)N * (size_t)S * vjsd::PART_STRIDE;
-    return floats * sizeof(float);
+    return floats * sizeof(float) + 64;  // + the scalar tail (kept-row count)
 }
 
 int vjsd_stats(const vjsd_shard *shards, int S, int64_t N, int dtype, int which, float *part,
@@ -195,6 +227,95 @@ int vjsd_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double b
     if ((e = vjsd_stats(shards, S, N, dtype, 3, part, stream))) return e;
     if ((e = vjsd_merge(part, S, N, 3, stats, stream))) return e;
     return vjsd_fwd(shards, S, N, dtype, stats, beta, part, kl, loss, stream);
+}
+
+int vjsd_loss_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
+                      const vjsd_loss_opts *opts, float *part, double *stats, float *kl,
+                      float *rows, float *out, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    LossCfg c;
+    if ((e = loss_cfg(opts, &c))) return e;
+    if ((e = check_views(shards, S, N, dtype, true, false))) return e;
+    if (c.red != VJSD_REDUCE_NONE && !out) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (N == 0) {
+        if (c.red != VJSD_REDUCE_NONE)
+            return hip_status(vjsd::launch_reduce_rows(nullptr, nullptr, 0, false, out, nullptr, st));
+        return VJSD_OK;
+    }
+    if (!part || !stats || !kl || !rows) return VJSD_ERR_ARG;
+    const vjsd::RowOpts ro = row_opts(c);
+    const int mode = mode_of(beta);
+    if (mode != vjsd::INTERIOR) {  // the endpoints are plain KL divergences: one input pass
+        const int rev = mode == vjsd::REV_KL;
+        for (int k = 0; k < S; ++k) {
+            Shard sh = convert(shards[k], true, false);
+            if ((e = hip_status(vjsd::launch_kl1(dtype, rev, sh, N, part_of(part, k, N), st, ro))))
+                return e;
+        }
+        if ((e = hip_status(vjsd::launch_kl1_merge(rev, part_of(part, 0, N), S, N, stats, kl,
+                                                   rows, st, ro))))
+            return e;
+    } else if (S == 1) {
+        Shard sh = convert(shards[0], true, false);
+        if ((e = hip_status(vjsd::launch_fwd_fused(dtype, sh, N, beta, stats, kl, rows, st, ro))))
+            return e;
+    } else {
+        for (int k = 0; k < S; ++k) {
+            Shard sh = convert(shards[k], true, false);
+            if ((e = hip_status(vjsd::launch_stats(dtype, 3, sh, N, part_of(part, k, N), st, ro))))
+                return e;
+        }
+        if ((e = hip_status(vjsd::launch_merge(part_of(part, 0, N), S, N, 3, stats, st, ro.ks))))
+            return e;
+        for (int k = 0; k < S; ++k) {
+            Shard sh = convert(shards[k], true, false);
+            if ((e = hip_status(vjsd::launch_div(dtype, mode, sh, N, stats, beta,
+                                                 part_of(part, k, N), nullptr, nullptr, st, ro))))
+                return e;
+        }
+        if ((e = hip_status(vjsd::launch_div_finalize(mode, part_of(part, 0, N), S, N, stats, beta,
+                                                      kl, rows, st, ro))))
+            return e;
+    }
+    if (c.red == VJSD_REDUCE_NONE) return VJSD_OK;
+    return hip_status(vjsd::launch_reduce_rows(rows, c.mask, N, c.red == VJSD_REDUCE_MEAN, out,
+                                               nullptr, st));
+}
+
+int vjsd_loss_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
+                       const vjsd_loss_opts *opts, const double *stats, const float *kl,
+                       const float *grad, float *part, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    LossCfg c;
+    if ((e = loss_cfg(opts, &c))) return e;
+    if ((e = check_views(shards, S, N, dtype, true, true))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!stats || !kl || !grad || !part) return VJSD_ERR_ARG;
+    const int mode = mode_of(beta);
+    hipStream_t st = (hipStream_t)stream;
+    vjsd::GradOpts go;
+    go.ks = row_opts(c).ks;
+    go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
+    go.scalar = c.red != VJSD_REDUCE_NONE;
+    go.mask = c.mask;
+    if (c.red == VJSD_REDUCE_MEAN) {
+        double *cnt = count_of(part, S, N);
+        if ((e = hip_status(vjsd::launch_reduce_rows(nullptr, c.mask, N, false, nullptr, cnt, st))))
+            return e;
+        go.count = cnt;
+    }
+    if ((e = hip_status(vjsd::launch_bwd_prep(mode, N, stats, kl, beta, grad, part, st, go))))
+        return e;
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], true, true);
+        if ((e = hip_status(vjsd::launch_bwd(dtype, mode, sh, N, part, st)))) return e;
+    }
+    return VJSD_OK;
 }
 
 int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,

@@ -35,6 +35,7 @@ constexpr float W_FLOOR = 1.17549435e-38f;
 // backward kernels, then per-(shard, row) partials (PART_STRIDE floats each).
 constexpr int ROWC = 16;
 constexpr int PART_STRIDE = 8;
+constexpr int ROWC_KS = 10;         // slot holding the exponent scale log2 e / T
 constexpr int ROWC_UNDEFINED = 15;  // slot holding 1.0f for a row with no distribution
 // Streaming gradient kernels: one wave per workgroup, each lane one 16-byte vector of
 // a row chunk, consecutive workgroups on consecutive chunks of a row.
@@ -215,19 +216,36 @@ __device__ __forceinline__ int64_t head_len(int64_t w, const void *a, const void
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Reference point c = fl32(m * log2 e) of a row max m (0 for an empty / masked row).
-__device__ __forceinline__ float refc(float m) { return m == NINF ? 0.0f : m * L2E; }
+// Scale of the base-2 exponent.  Logits x at temperature T enter every kernel as
+// u = x * ks - c with ks = fl32(log2 e / T): the division by T is folded into the
+// scale the exponent needs anyway (T = 1 gives ks = L2E).  Statistics keep the raw
+// row max m, and lnZ = ln sum exp((x - m) / T) of the tempered logits.
 
-// Row normaliser rebuilt from stored statistics: Z = sum 2^(x*L2E - c) = 2^(lnZ*log2e + res)
-// with res = m*L2E - c exact in fp64.
-__device__ __forceinline__ double z_from_stats(float m, double lnZ) {
-    const double res = (double)m * (double)L2E - (double)refc(m);
+// Reference point c = fl32(m * ks) of a row max m (0 for an empty / masked row).
+__device__ __forceinline__ float refc(float m, float ks = L2E) { return m == NINF ? 0.0f : m * ks; }
+
+// Row normaliser rebuilt from stored statistics: Z = sum 2^(x*ks - c) = 2^(lnZ*log2e + res)
+// with res = m*ks - c exact in fp64.
+__device__ __forceinline__ double z_from_stats(float m, double lnZ, float ks = L2E) {
+    const double res = (double)m * (double)ks - (double)refc(m, ks);
     return exp2(lnZ * L2E_D + res);
 }
-// Inverse: ln sum exp(x - m) from Z relative to c.
-__device__ __forceinline__ double lnz_from_z(float m, double Z) {
-    const double res = (double)m * (double)L2E - (double)refc(m);
+// Inverse: ln sum exp((x - m) / T) from Z relative to c.
+__device__ __forceinline__ double lnz_from_z(float m, double Z, float ks = L2E) {
+    const double res = (double)m * (double)ks - (double)refc(m, ks);
     return (log2(Z) - res) * LN2_D;
+}
+
+// Per-call options of the distillation-loss form of the forward passes (kernel
+// argument, by value): the exponent scale, the loss multiplier and the row mask.
+struct RowOpts {
+    float ks = L2E;                 // log2 e / temperature
+    float lscale = 1.0f;            // T^2 when the loss is temperature-scaled, else 1
+    const uint8_t *mask = nullptr;  // [N]; a zero entry drops the row; null keeps all
+};
+// A dropped row is never read: its outputs are zeros.
+__device__ __forceinline__ bool row_dropped(const RowOpts &o, int64_t r) {
+    return o.mask != nullptr && o.mask[r] == 0;
 }
 
 // ---- workgroup reductions (fixed order: deterministic results) ----------------------
@@ -243,23 +261,23 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-// Online (max, sum of 2^(x*L2E - refc(max))) pair.
+// Online (max, sum of 2^(x*ks - refc(max))) pair.
 struct MZ {
     float m, z;
 };
-__device__ __forceinline__ MZ mz_combine(MZ a, MZ b) {
+__device__ __forceinline__ MZ mz_combine(MZ a, MZ b, float ks = L2E) {
     const float m = fmaxf(a.m, b.m);
-    const float c = refc(m);
-    const float za = a.m == NINF ? 0.0f : a.z * ex2(refc(a.m) - c);
-    const float zb = b.m == NINF ? 0.0f : b.z * ex2(refc(b.m) - c);
+    const float c = refc(m, ks);
+    const float za = a.m == NINF ? 0.0f : a.z * ex2(refc(a.m, ks) - c);
+    const float zb = b.m == NINF ? 0.0f : b.z * ex2(refc(b.m, ks) - c);
     return {m, za + zb};
 }
-__device__ __forceinline__ MZ wave_mz(MZ v) {
+__device__ __forceinline__ MZ wave_mz(MZ v, float ks = L2E) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         MZ w{__shfl_xor(v.m, o), __shfl_xor(v.z, o)};
         // combine in lane order so that both partners compute the same value
-        v = (threadIdx.x & o) ? mz_combine(w, v) : mz_combine(v, w);
+        v = (threadIdx.x & o) ? mz_combine(w, v, ks) : mz_combine(v, w, ks);
     }
     return v;
 }

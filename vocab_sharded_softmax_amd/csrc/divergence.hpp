@@ -5,7 +5,8 @@
 // Triton kernels", sections Motivation and Changes: the generalized JSD as two
 // KL-to-mixture expectations reduced together; beta = 0 / 1 as forward / reverse KL.
 //
-// Base-2 row algebra.  With u = x*L2E - c (c = fl32(m*L2E)), e = 2^u, Z = sum e:
+// Base-2 row algebra.  With u = x*ks - c (ks = log2 e / T, c = fl32(m*ks)), e = 2^u,
+// Z = sum e:
 //   M = beta p_t + (1-beta) p_s = (beta e_t + gamma e_s) / Z_t,  gamma = (1-beta) Z_t / Z_s
 //   L = log2(beta e_t + gamma e_s),  r = log2(Z_s / Z_t)
 //   log2(p_t / M) = u_t - L,  log2(p_s / M) = (u_s - L) - r
@@ -25,14 +26,15 @@ enum Mode { INTERIOR = 0, FWD_KL = 1, REV_KL = 2 };
 template <int MODE>
 struct DivTerm {
     float cs, ct, bf, gam, rf;
+    float ks = L2E;  // log2 e / temperature
 
     // adds the element (xs, xt) to the running sums; F tracks max(u_t - u_s) (forward
     // KL) or max(u_s - u_t) (reverse KL) over raw values: +inf flags target mass on a
     // masked token
     __device__ __forceinline__ void add(float xs, float xt, float &At, float &As,
                                         float &F) const {
-        const float usr = fmaf(xs, L2E, -cs);
-        const float utr = fmaf(xt, L2E, -ct);
+        const float usr = fmaf(xs, ks, -cs);
+        const float utr = fmaf(xt, ks, -ct);
         const float us = fmaxf(usr, U_FLOOR), ut = fmaxf(utr, U_FLOOR);
         if constexpr (MODE == INTERIOR) {
             const float es = ex2(us), et = ex2(ut);
@@ -77,9 +79,11 @@ struct OpDivRegs : DivTerm<MODE> {
     }
 };
 
-// Final per-token values from the part-summed partials (base 2, fp64).
+// Final per-token values from the part-summed partials (base 2, fp64).  The loss is
+// multiplied by lscale (T^2 for a temperature-scaled loss, else 1); kl is not.
 __device__ __forceinline__ void finalize_row(int mode, double beta, bool undefined, double pt,
-                                             double ps, float F, float *kl, float *loss) {
+                                             double ps, float F, float *kl, float *loss,
+                                             float lscale = 1.0f) {
     double KT, KS, l;
     if (undefined) {
         KT = KS = l = __builtin_nan("");
@@ -98,7 +102,22 @@ __device__ __forceinline__ void finalize_row(int mode, double beta, bool undefin
     }
     kl[0] = (float)KT;
     kl[1] = (float)KS;
-    *loss = (float)l;
+    *loss = (float)(l * (double)lscale);
+}
+
+// A row the caller's mask drops: nothing evaluated, loss and KL pair 0.
+__device__ __forceinline__ void masked_row(float *kl, float *loss) {
+    kl[0] = 0.0f;
+    kl[1] = 0.0f;
+    *loss = 0.0f;
+}
+// The same from a one-pass forward, which also owns the row's statistics: they read
+// as a row with no distribution, so a backward gives it exactly zero gradients.
+__device__ __forceinline__ void dropped_row(double *st, float *kl, float *loss) {
+    if (threadIdx.x == 0) {
+        st[0] = st[1] = st[2] = st[3] = -__builtin_inf();
+        masked_row(kl, loss);
+    }
 }
 
 }  // namespace vjsd

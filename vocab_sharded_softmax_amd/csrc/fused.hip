@@ -88,11 +88,15 @@ template <class D, int NVT>
 __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t w, double beta,
                                                 double *__restrict__ stats,
                                                 float *__restrict__ kl,
-                                                float *__restrict__ loss) {
+                                                float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
     constexpr int VEC = D::VEC;
     __shared__ float red[2 * FNW];
     const int64_t r = blockIdx.x;
+    if (row_dropped(o, r)) {
+        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
+        return;
+    }
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const int64_t nv = w / VEC;  // whole vectors: the host requires w % VEC == 0
     u32x4 xs[NVT], xt[NVT];
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
             xt[i] = u32x4{q, q, q, q};
         }
     }
-    // ---- statistics: row max, then sum of 2^(x log2e - c)
+    // ---- statistics: row max, then sum of 2^(x ks - c)
     float ms = NINF, mt = NINF;
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
         opaque(xs[i]);
         opaque(xt[i]);
     }
-    const float cs = refc(ms), ct = refc(mt);
+    const float cs = refc(ms, o.ks), ct = refc(mt, o.ks);
     float zs = 0.0f, zt = 0.0f;
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
@@ -136,8 +140,8 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
         widen<D>(xt[i], b);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            ea[e] = ex2(fmaf(a[e], L2E, -cs));
-            eb[e] = ex2(fmaf(b[e], L2E, -ct));
+            ea[e] = ex2(fmaf(a[e], o.ks, -cs));
+            eb[e] = ex2(fmaf(b[e], o.ks, -ct));
         }
 #pragma unroll
         for (int st = VEC / 2; st >= 1; st /= 2)
@@ -151,8 +155,8 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
     }
     block_sum2(zs, zt, red);
     const bool undefined = ms == NINF || mt == NINF;
-    const double lzs = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, (double)zs);
-    const double lzt = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, (double)zt);
+    const double lzs = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, (double)zs, o.ks);
+    const double lzt = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, (double)zt, o.ks);
     if (threadIdx.x == 0) {
         double *o = stats + r * 4;
         o[0] = ms;
@@ -164,9 +168,10 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
     float pt = 0.0f, ps = 0.0f;
     double Zs = 1.0, Zt = 1.0;
     if (!undefined) {
-        Zs = z_from_stats(ms, lzs);
-        Zt = z_from_stats(mt, lzt);
+        Zs = z_from_stats(ms, lzs, o.ks);
+        Zt = z_from_stats(mt, lzt, o.ks);
         OpDivRegs<INTERIOR> op;
+        op.ks = o.ks;
         op.cs = cs;
         op.ct = ct;
         op.bf = (float)beta;
@@ -190,7 +195,7 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
     block_sum2(pt, ps, red);
     if (threadIdx.x == 0)
         finalize_row(INTERIOR, beta, undefined, pt * (float)(1.0 / Zt), ps * (float)(1.0 / Zs),
-                     NINF, kl + 2 * r, loss + r);
+                     NINF, kl + 2 * r, loss + r, o.lscale);
 }
 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
@@ -204,19 +209,23 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
                                                          double beta,
                                                          double *__restrict__ stats,
                                                          float *__restrict__ kl,
-                                                         float *__restrict__ loss) {
+                                                         float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
     __shared__ float red[2 * (TWICE_BLK / 64)];
     const int64_t r = blockIdx.x;
+    if (row_dropped(o, r)) {
+        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
+        return;
+    }
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const int64_t h = head_len<T>(w, s, t);
-    OpStats<3> o1;
+    OpStats<3> o1(o.ks);
     sweep<D, 4, true, TWICE_BLK>(s, t, w, h, o1);
-    const MZ ms = block_mz<TWICE_BLK>(MZ{o1.a.m, o1.a.z}, red);
-    const MZ mt = block_mz<TWICE_BLK>(MZ{o1.b.m, o1.b.z}, red);
+    const MZ ms = block_mz<TWICE_BLK>(MZ{o1.a.m, o1.a.z}, red, o.ks);
+    const MZ mt = block_mz<TWICE_BLK>(MZ{o1.b.m, o1.b.z}, red, o.ks);
     const bool undefined = ms.m == NINF || mt.m == NINF;
-    const double lzs = ms.m == NINF ? -__builtin_inf() : lnz_from_z(ms.m, (double)ms.z);
-    const double lzt = mt.m == NINF ? -__builtin_inf() : lnz_from_z(mt.m, (double)mt.z);
+    const double lzs = ms.m == NINF ? -__builtin_inf() : lnz_from_z(ms.m, (double)ms.z, o.ks);
+    const double lzt = mt.m == NINF ? -__builtin_inf() : lnz_from_z(mt.m, (double)mt.z, o.ks);
     if (threadIdx.x == 0) {
         double *o = stats + r * 4;
         o[0] = ms.m;
@@ -227,11 +236,12 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
     float v[2] = {0.0f, 0.0f};
     double Zs = 1.0, Zt = 1.0;
     if (!undefined) {
-        Zs = z_from_stats(ms.m, lzs);
-        Zt = z_from_stats(mt.m, lzt);
+        Zs = z_from_stats(ms.m, lzs, o.ks);
+        Zt = z_from_stats(mt.m, lzt, o.ks);
         OpDiv<INTERIOR> op;
-        op.cs = refc(ms.m);
-        op.ct = refc(mt.m);
+        op.ks = o.ks;
+        op.cs = refc(ms.m, o.ks);
+        op.ct = refc(mt.m, o.ks);
         op.bf = (float)beta;
         op.gam = (float)((1.0 - beta) * Zt / Zs);
         op.rf = (float)log2(Zs / Zt);
@@ -242,21 +252,21 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
     block_sum<2, TWICE_BLK>(v, red);
     if (threadIdx.x == 0)
         finalize_row(INTERIOR, beta, undefined, v[0] * (float)(1.0 / Zt),
-                     v[1] * (float)(1.0 / Zs), NINF, kl + 2 * r, loss + r);
+                     v[1] * (float)(1.0 / Zs), NINF, kl + 2 * r, loss + r, o.lscale);
 }
 
 template <class D, int NVT>
 hipError_t row_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
-                      float *loss, hipStream_t st) {
+                      float *loss, hipStream_t st, const RowOpts &o) {
     hipLaunchKernelGGL((k_fwd_row<D, NVT>), dim3((unsigned)N), dim3(FB), 0, st, sh.s, sh.t,
-                       sh.width, beta, stats, kl, loss);
+                       sh.width, beta, stats, kl, loss, o);
     return hipGetLastError();
 }
 
 // Row held in registers when the layout allows it, else the two sweeps.
 template <class D>
 hipError_t fused_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
-                        float *loss, hipStream_t st) {
+                        float *loss, hipStream_t st, const RowOpts &o) {
     constexpr int VEC = D::VEC;
     const int64_t w = sh.width;
     const int64_t nv = w / VEC;
@@ -270,23 +280,23 @@ hipError_t fused_launch(const Shard &sh, int64_t N, double beta, double *stats, 
     }
     if (!regs) {
         hipLaunchKernelGGL(k_fwd_twice<D>, dim3((unsigned)N), dim3(TWICE_BLK), 0, st, sh.s,
-                           sh.t, w, beta, stats, kl, loss);
+                           sh.t, w, beta, stats, kl, loss, o);
         return hipGetLastError();
     }
-    if (nv <= FB) return row_launch<D, 1>(sh, N, beta, stats, kl, loss, st);
-    if (nv <= 2 * FB) return row_launch<D, 2>(sh, N, beta, stats, kl, loss, st);
-    if (nv <= 4 * FB) return row_launch<D, 4>(sh, N, beta, stats, kl, loss, st);
-    return row_launch<D, FUSED_NVT_MAX>(sh, N, beta, stats, kl, loss, st);
+    if (nv <= FB) return row_launch<D, 1>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= 2 * FB) return row_launch<D, 2>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= 4 * FB) return row_launch<D, 4>(sh, N, beta, stats, kl, loss, st, o);
+    return row_launch<D, FUSED_NVT_MAX>(sh, N, beta, stats, kl, loss, st, o);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
-                            float *kl, float *loss, hipStream_t st) {
+                            float *kl, float *loss, hipStream_t st, const RowOpts &o) {
     switch (dtype) {
-        case 0: return fused_launch<F32>(sh, N, beta, stats, kl, loss, st);
-        case 1: return fused_launch<F16>(sh, N, beta, stats, kl, loss, st);
-        default: return fused_launch<BF16>(sh, N, beta, stats, kl, loss, st);
+        case 0: return fused_launch<F32>(sh, N, beta, stats, kl, loss, st, o);
+        case 1: return fused_launch<F16>(sh, N, beta, stats, kl, loss, st, o);
+        default: return fused_launch<BF16>(sh, N, beta, stats, kl, loss, st, o);
     }
 }
 

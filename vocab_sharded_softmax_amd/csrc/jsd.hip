@@ -34,15 +34,16 @@ struct RowConst {
     double r;        // log2(Z_s / Z_t)
 };
 
-__device__ __forceinline__ RowConst row_const(const double *__restrict__ stats, int64_t r) {
+__device__ __forceinline__ RowConst row_const(const double *__restrict__ stats, int64_t r,
+                                              float ks = L2E) {
     RowConst k;
     const double *st = stats + r * 4;
     const float ms = (float)st[0], mt = (float)st[2];
     k.undefined = (ms == NINF) || (mt == NINF);
-    k.cs = refc(ms);
-    k.ct = refc(mt);
-    k.Zs = k.undefined ? 1.0 : z_from_stats(ms, st[1]);
-    k.Zt = k.undefined ? 1.0 : z_from_stats(mt, st[3]);
+    k.cs = refc(ms, ks);
+    k.ct = refc(mt, ks);
+    k.Zs = k.undefined ? 1.0 : z_from_stats(ms, st[1], ks);
+    k.Zt = k.undefined ? 1.0 : z_from_stats(mt, st[3], ks);
     k.izs = (float)(1.0 / k.Zs);
     k.izt = (float)(1.0 / k.Zt);
     k.r = log2(k.Zs / k.Zt);
@@ -53,15 +54,17 @@ template <class D, int MODE>
 __global__ __launch_bounds__(BLOCK) void k_div(RowView sv, RowView tv, int64_t w,
                                                const double *__restrict__ stats, double beta,
                                                float *__restrict__ part_k, float *__restrict__ kl,
-                                               float *__restrict__ loss) {
+                                               float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
     __shared__ float red[3 * NWAVE];
     const int64_t r = blockIdx.x;
-    const RowConst k = row_const(stats, r);
+    const RowConst k = row_const(stats, r, o.ks);
     float pt = 0.0f, ps = 0.0f, F = NINF;
+    // a dropped row has statistics (-inf, ...) and so counts as undefined here
     if (!k.undefined && w > 0) {
         const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
         OpDiv<MODE> op;
+        op.ks = o.ks;
         op.cs = k.cs;
         op.ct = k.ct;
         op.bf = (float)beta;
@@ -82,7 +85,10 @@ __global__ __launch_bounds__(BLOCK) void k_div(RowView sv, RowView tv, int64_t w
     }
     if (threadIdx.x == 0) {
         if (loss) {
-            finalize_row(MODE, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r);
+            if (row_dropped(o, r))
+                masked_row(kl + 2 * r, loss + r);
+            else
+                finalize_row(MODE, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r, o.lscale);
         } else {
             float *o = part_k + r * PART_STRIDE;
             o[0] = pt;
@@ -94,10 +100,14 @@ __global__ __launch_bounds__(BLOCK) void k_div(RowView sv, RowView tv, int64_t w
 
 __global__ void k_div_finalize(int mode, const float *__restrict__ part, int S, int64_t N,
                                const double *__restrict__ stats, double beta,
-                               float *__restrict__ kl, float *__restrict__ loss) {
+                               float *__restrict__ kl, float *__restrict__ loss, RowOpts o) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= N) return;
-    const RowConst k = row_const(stats, r);
+    if (row_dropped(o, r)) {
+        masked_row(kl + 2 * r, loss + r);
+        return;
+    }
+    const RowConst k = row_const(stats, r, o.ks);
     double pt = 0.0, ps = 0.0;
     float F = NINF;
     for (int q = 0; q < S; ++q) {
@@ -106,7 +116,7 @@ __global__ void k_div_finalize(int mode, const float *__restrict__ part, int S, 
         ps += p[1];
         F = fmaxf(F, p[2]);
     }
-    finalize_row(mode, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r);
+    finalize_row(mode, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r, o.lscale);
 }
 
 // ---- backward ---------------------------------------------------------------------
@@ -115,6 +125,7 @@ template <class D, int MODE, bool WS, bool WT>
 struct OpBwd {
     using T = typename D::T;
     T *gs, *gt;
+    float ks;  // log2 e / temperature
     float cs, ct, bf, gam;
     float Cs, Ct;  // gradient scales
     float Hs, Ht;  // per-side offsets subtracted from the log-ratio
@@ -128,8 +139,8 @@ struct OpBwd {
             float os[W], ot[W];
 #pragma unroll
             for (int i = 0; i < W; ++i) {
-                const float us = fmaxf(fmaf(x[j][i], L2E, -cs), U_FLOOR);
-                const float ut = fmaxf(fmaf(y[j][i], L2E, -ct), U_FLOOR);
+                const float us = fmaxf(fmaf(x[j][i], ks, -cs), U_FLOOR);
+                const float ut = fmaxf(fmaf(y[j][i], ks, -ct), U_FLOOR);
                 const float es = ex2(us), et = ex2(ut);
                 if constexpr (MODE == INTERIOR) {
                     const float L = lg2(fmaf(bf, et, fmaf(gam, es, W_FLOOR)));
@@ -158,15 +169,20 @@ struct OpBwd {
 };
 
 // Per-row constants of the backward, computed once per call from the fp64 statistics:
-// rowc[r*ROWC + i] = cs, ct, beta, gamma, Cs, Ct, Hs, Ht, Gs, Gt (i = 0..9) and the
-// undefined-row flag in slot ROWC_UNDEFINED.
+// rowc[r*ROWC + i] = cs, ct, beta, gamma, Cs, Ct, Hs, Ht, Gs, Gt (i = 0..9), the
+// exponent scale in slot ROWC_KS and the zero-gradient flag (no distribution, or a
+// row the mask drops) in slot ROWC_UNDEFINED.
 __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats,
                            const float *__restrict__ kl, double beta,
-                           const float *__restrict__ grad, float *__restrict__ rowc) {
+                           const float *__restrict__ grad, float *__restrict__ rowc,
+                           GradOpts go) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= N) return;
-    const RowConst k = row_const(stats, r);
-    const double g = grad[r];
+    const RowConst k = row_const(stats, r, go.ks);
+    const bool dropped = go.mask != nullptr && go.mask[r] == 0;
+    double g = go.scalar ? (double)grad[0] : (double)grad[r];
+    if (go.count) g /= fmax((double)*go.count, 1.0);
+    g *= go.gmul;
     const double KT2 = (double)kl[2 * r] * L2E_D, KS2 = (double)kl[2 * r + 1] * L2E_D;
     double Cs = 0.0, Ct = 0.0, Hs = 0.0, Ht = 0.0;
     if (mode == INTERIOR) {
@@ -192,7 +208,8 @@ __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats
     o[7] = (float)Ht;
     o[8] = (float)(g / k.Zs);
     o[9] = (float)(g / k.Zt);
-    o[ROWC_UNDEFINED] = k.undefined ? 1.0f : 0.0f;
+    o[ROWC_KS] = go.ks;
+    o[ROWC_UNDEFINED] = (k.undefined || dropped) ? 1.0f : 0.0f;
 }
 
 // One wave per row chunk of cw columns; the chunks of a row are consecutive workgroups,
@@ -209,7 +226,7 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
     const float *k = rowc + r * ROWC;
     T *gs = WS ? row_ptr<T>(gsv, r) + c0 : nullptr;
     T *gt = WT ? row_ptr<T>(gtv, r) + c0 : nullptr;
-    if (k[ROWC_UNDEFINED] != 0.0f) {  // no distribution: exactly zero gradient whatever g is
+    if (k[ROWC_UNDEFINED] != 0.0f) {  // no distribution, or dropped: exactly zero gradient
         if (WS) zero_span<D, GRAD_BLOCK>(gs, n);
         if (WT) zero_span<D, GRAD_BLOCK>(gt, n);
         return;
@@ -218,6 +235,7 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
     OpBwd<D, MODE, WS, WT> op;
     op.gs = gs;
     op.gt = gt;
+    op.ks = k[ROWC_KS];
     op.cs = k[0];
     op.ct = k[1];
     op.bf = k[2];
@@ -235,18 +253,18 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
 
 template <class D, int MODE>
 hipError_t div_dt(const Shard &sh, int64_t N, const double *stats, double beta, float *part_k,
-                  float *kl, float *loss, hipStream_t st) {
+                  float *kl, float *loss, hipStream_t st, const RowOpts &o) {
     hipLaunchKernelGGL((k_div<D, MODE>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s, sh.t,
-                       sh.width, stats, beta, part_k, kl, loss);
+                       sh.width, stats, beta, part_k, kl, loss, o);
     return hipGetLastError();
 }
 
 template <class D>
 hipError_t div_mode(int mode, const Shard &sh, int64_t N, const double *stats, double beta,
-                    float *part_k, float *kl, float *loss, hipStream_t st) {
-    if (mode == INTERIOR) return div_dt<D, INTERIOR>(sh, N, stats, beta, part_k, kl, loss, st);
-    if (mode == FWD_KL) return div_dt<D, FWD_KL>(sh, N, stats, beta, part_k, kl, loss, st);
-    return div_dt<D, REV_KL>(sh, N, stats, beta, part_k, kl, loss, st);
+                    float *part_k, float *kl, float *loss, hipStream_t st, const RowOpts &o) {
+    if (mode == INTERIOR) return div_dt<D, INTERIOR>(sh, N, stats, beta, part_k, kl, loss, st, o);
+    if (mode == FWD_KL) return div_dt<D, FWD_KL>(sh, N, stats, beta, part_k, kl, loss, st, o);
+    return div_dt<D, REV_KL>(sh, N, stats, beta, part_k, kl, loss, st, o);
 }
 
 template <class D, int MODE, bool WS, bool WT>
@@ -278,27 +296,29 @@ hipError_t bwd_mode(int mode, const Shard &sh, int64_t N, const float *rowc, hip
 }  // namespace
 
 hipError_t launch_div(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
-                      double beta, float *part_k, float *kl, float *loss, hipStream_t st) {
+                      double beta, float *part_k, float *kl, float *loss, hipStream_t st,
+                      const RowOpts &o) {
     switch (dtype) {
-        case 0: return div_mode<F32>(mode, sh, N, stats, beta, part_k, kl, loss, st);
-        case 1: return div_mode<F16>(mode, sh, N, stats, beta, part_k, kl, loss, st);
-        default: return div_mode<BF16>(mode, sh, N, stats, beta, part_k, kl, loss, st);
+        case 0: return div_mode<F32>(mode, sh, N, stats, beta, part_k, kl, loss, st, o);
+        case 1: return div_mode<F16>(mode, sh, N, stats, beta, part_k, kl, loss, st, o);
+        default: return div_mode<BF16>(mode, sh, N, stats, beta, part_k, kl, loss, st, o);
     }
 }
 
 hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
                                const double *stats, double beta, float *kl, float *loss,
-                               hipStream_t st) {
+                               hipStream_t st, const RowOpts &o) {
     const int threads = 256;
     hipLaunchKernelGGL(k_div_finalize, dim3((unsigned)((N + threads - 1) / threads)),
-                       dim3(threads), 0, st, mode, part, S, N, stats, beta, kl, loss);
+                       dim3(threads), 0, st, mode, part, S, N, stats, beta, kl, loss, o);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_prep(int mode, int64_t N, const double *stats, const float *kl,
-                           double beta, const float *grad, float *rowc, hipStream_t st) {
+                           double beta, const float *grad, float *rowc, hipStream_t st,
+                           const GradOpts &g) {
     hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, mode, N,
-                       stats, kl, beta, grad, rowc);
+                       stats, kl, beta, grad, rowc, g);
     return hipGetLastError();
 }
 

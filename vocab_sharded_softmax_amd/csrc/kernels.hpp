@@ -18,22 +18,23 @@ struct Shard {
 
 // pass 1: per-shard (max, sum-exp) of the inputs selected by `which` (1 s, 2 t, 3 both)
 hipError_t launch_stats(int dtype, int which, const Shard &sh, int64_t N, float *part_k,
-                        hipStream_t st);
+                        hipStream_t st, const RowOpts &o = RowOpts());
 // cross-shard merge of pass-1 partials into stats[N][4]
 hipError_t launch_merge(const float *part, int S, int64_t N, int which, double *stats,
-                        hipStream_t st);
+                        hipStream_t st, float ks = L2E);
 // pass 2 of the JSD (and its endpoint branches): per-shard divergence partials; with
 // `kl`/`loss` non-null (single shard) the row is finalised in the same launch
 hipError_t launch_div(int dtype, int mode, const Shard &sh, int64_t N, const double *stats,
-                      double beta, float *part_k, float *kl, float *loss, hipStream_t st);
+                      double beta, float *part_k, float *kl, float *loss, hipStream_t st,
+                      const RowOpts &o = RowOpts());
 // shard-ordered sum of pass-2 partials into kl[N][2], loss[N]
 hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
                                const double *stats, double beta, float *kl, float *loss,
-                               hipStream_t st);
+                               hipStream_t st, const RowOpts &o = RowOpts());
 // Interior JSD forward (0 < beta < 1) of a single shard in one launch: statistics,
 // then divergence, one workgroup per row (held in registers when the row fits).
 hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
-                            float *kl, float *loss, hipStream_t st);
+                            float *kl, float *loss, hipStream_t st, const RowOpts &o = RowOpts());
 
 // Row chunks of the streaming gradient kernels: cw columns per workgroup (a multiple
 // of GRAD_BLOCK vectors), nchunk chunks per row, N * nchunk workgroups in all.
@@ -47,18 +48,35 @@ inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
     return {cw, w > 0 ? (w + cw - 1) / cw : 0};
 }
 
+// Upstream-gradient options of the distillation-loss form of the backward: the row
+// r's gradient scale is g_r * gmul, g_r = grad[r] (per-row) or grad[0] (reduced;
+// divided by max(*count, 1) for a mean), and 0 for a row the mask drops.
+struct GradOpts {
+    float ks = L2E;                  // log2 e / temperature
+    double gmul = 1.0;               // T^2 (if scaled) * (1/T): chain rule through x / T
+    bool scalar = false;             // grad is one value for all rows
+    const uint8_t *mask = nullptr;   // [N]; zero drops the row
+    const double *count = nullptr;   // device: kept rows, for a mean (null: no division)
+};
+
 // pass 3: per-row constants of the backward (once per call), then the closed-form
 // gradients of the JSD / KL for one shard
 hipError_t launch_bwd_prep(int mode, int64_t N, const double *stats, const float *kl,
-                           double beta, const float *grad, float *rowc, hipStream_t st);
+                           double beta, const float *grad, float *rowc, hipStream_t st,
+                           const GradOpts &g = GradOpts());
 hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const float *rowc,
                       hipStream_t st);
 
 // single-pass KL forward: per-shard online partials, then the merge into stats/kl/loss
 hipError_t launch_kl1(int dtype, int reverse, const Shard &sh, int64_t N, float *part_k,
-                      hipStream_t st);
+                      hipStream_t st, const RowOpts &o = RowOpts());
 hipError_t launch_kl1_merge(int reverse, const float *part, int S, int64_t N, double *stats,
-                            float *kl, float *loss, hipStream_t st);
+                            float *kl, float *loss, hipStream_t st, const RowOpts &o = RowOpts());
+
+// fixed-order masked reduction of per-row losses: out[0] = sum (mean: sum / max(count,
+// 1)) over the kept rows; *count = kept rows (rows may be null to count only)
+hipError_t launch_reduce_rows(const float *rows, const uint8_t *mask, int64_t N, bool mean,
+                              float *out, double *count, hipStream_t st);
 // single-pass entropy forward and its backward
 hipError_t launch_ent1(int dtype, const Shard &sh, int64_t N, float *part_k, hipStream_t st);
 hipError_t launch_ent1_merge(const float *part, int S, int64_t N, double *stats, float *ent,

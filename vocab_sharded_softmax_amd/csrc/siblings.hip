@@ -26,6 +26,7 @@ struct OpKL1 {
     float ma = NINF, ca = 0.0f, za = 0.0f;
     float mb = NINF, cb = 0.0f, zb = 0.0f;
     float A = 0.0f, F = NINF;
+    float ks = L2E;  // log2 e / temperature
 
     template <int NV, int W>
     __device__ __forceinline__ void run(const float (&xa)[NV][W], const float (&xb)[NV][W],
@@ -39,14 +40,14 @@ struct OpKL1 {
             bmb = fmaxf(bmb, b[i]);
         }
         const float nma = fmaxf(ma, bma), nmb = fmaxf(mb, bmb);
-        const float nca = refc(nma), ncb = refc(nmb);
+        const float nca = refc(nma, ks), ncb = refc(nmb, ks);
         const float sa = ma == NINF ? 0.0f : ex2(ca - nca);
         const float sb = mb == NINF ? 0.0f : ex2(cb - ncb);
         A = sa * fmaf((ca - nca) - (cb - ncb), za, A);
         float ea[N], eb[N], pa = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const float uar = fmaf(a[i], L2E, -nca), ubr = fmaf(b[i], L2E, -ncb);
+            const float uar = fmaf(a[i], ks, -nca), ubr = fmaf(b[i], ks, -ncb);
             F = fmaxf(F, uar - ubr);
             const float ua = fmaxf(uar, U_FLOOR), ub = fmaxf(ubr, U_FLOOR);
             ea[i] = ex2(ua);
@@ -74,11 +75,11 @@ struct OpKL1 {
 struct KLPart {
     float ma, za, mb, zb, A, F;
 };
-__device__ __forceinline__ KLPart kl_combine(KLPart x, KLPart y) {
+__device__ __forceinline__ KLPart kl_combine(KLPart x, KLPart y, float ks) {
     KLPart o;
     o.ma = fmaxf(x.ma, y.ma);
     o.mb = fmaxf(x.mb, y.mb);
-    const float ca = refc(o.ma), cb = refc(o.mb);
+    const float ca = refc(o.ma, ks), cb = refc(o.mb, ks);
     o.za = 0.0f;
     o.zb = 0.0f;
     o.A = 0.0f;
@@ -86,10 +87,10 @@ __device__ __forceinline__ KLPart kl_combine(KLPart x, KLPart y) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const KLPart &p = *in[q];
-        if (p.mb != NINF) o.zb += p.zb * ex2(refc(p.mb) - cb);
+        if (p.mb != NINF) o.zb += p.zb * ex2(refc(p.mb, ks) - cb);
         if (p.ma != NINF) {
-            const float da = refc(p.ma) - ca;
-            const float db = p.mb == NINF ? 0.0f : refc(p.mb) - cb;
+            const float da = refc(p.ma, ks) - ca;
+            const float db = p.mb == NINF ? 0.0f : refc(p.mb, ks) - cb;
             const float sc = ex2(da);
             o.za += p.za * sc;
             o.A += sc * fmaf(da - db, p.za, p.A);
@@ -101,15 +102,16 @@ __device__ __forceinline__ KLPart kl_combine(KLPart x, KLPart y) {
 
 template <class D, bool REV>
 __global__ __launch_bounds__(BLOCK) void k_kl1(RowView sv, RowView tv, int64_t w,
-                                               float *__restrict__ part_k) {
+                                               float *__restrict__ part_k, RowOpts ro) {
     using T = typename D::T;
     __shared__ float red[6 * NWAVE];
     const int64_t r = blockIdx.x;
     KLPart p{NINF, 0.0f, NINF, 0.0f, 0.0f, NINF};
-    if (w > 0) {
+    if (w > 0 && !row_dropped(ro, r)) {
         const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
         const T *a = REV ? s : t, *b = REV ? t : s;
         OpKL1 op;
+        op.ks = ro.ks;
         sweep<D, 4, true, BLOCK, true>(a, b, w, head_len<T>(w, a, b), op);
         p = {op.ma, op.za, op.mb, op.zb, op.A, op.F};
         // wave reduction in lane order, then waves in order
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(BLOCK) void k_kl1(RowView sv, RowView tv, int64_t w
         for (int o = 32; o >= 1; o >>= 1) {
             KLPart q{__shfl_xor(p.ma, o), __shfl_xor(p.za, o), __shfl_xor(p.mb, o),
                      __shfl_xor(p.zb, o), __shfl_xor(p.A, o),  __shfl_xor(p.F, o)};
-            p = (threadIdx.x & o) ? kl_combine(q, p) : kl_combine(p, q);
+            p = (threadIdx.x & o) ? kl_combine(q, p, ro.ks) : kl_combine(p, q, ro.ks);
         }
         const int wave = threadIdx.x >> 6;
         if ((threadIdx.x & 63) == 0) {
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(BLOCK) void k_kl1(RowView sv, RowView tv, int64_t w
             p = {red[0], red[1], red[2], red[3], red[4], red[5]};
             for (int q = 1; q < NWAVE; ++q) {
                 const float *d = red + 6 * q;
-                p = kl_combine(p, KLPart{d[0], d[1], d[2], d[3], d[4], d[5]});
+                p = kl_combine(p, KLPart{d[0], d[1], d[2], d[3], d[4], d[5]}, ro.ks);
             }
         }
     }
@@ -141,9 +143,16 @@ __global__ __launch_bounds__(BLOCK) void k_kl1(RowView sv, RowView tv, int64_t w
 
 __global__ void k_kl1_merge(int rev, const float *__restrict__ part, int S, int64_t N,
                             double *__restrict__ stats, float *__restrict__ kl,
-                            float *__restrict__ loss) {
+                            float *__restrict__ loss, RowOpts ro) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= N) return;
+    if (row_dropped(ro, r)) {
+        double *o = stats + r * 4;
+        o[0] = o[1] = o[2] = o[3] = -__builtin_inf();
+        masked_row(kl + 2 * r, loss + r);
+        return;
+    }
+    const float ks = ro.ks;
     float ma = NINF, mb = NINF, F = NINF;
     for (int k = 0; k < S; ++k) {
         const float *p = part + ((int64_t)k * N + r) * PART_STRIDE;
@@ -151,14 +160,14 @@ __global__ void k_kl1_merge(int rev, const float *__restrict__ part, int S, int6
         mb = fmaxf(mb, p[2]);
         F = fmaxf(F, p[5]);
     }
-    const double ca = refc(ma), cb = refc(mb);
+    const double ca = refc(ma, ks), cb = refc(mb, ks);
     double Za = 0.0, Zb = 0.0, A = 0.0;
     for (int k = 0; k < S; ++k) {
         const float *p = part + ((int64_t)k * N + r) * PART_STRIDE;
-        if (p[2] != NINF) Zb += (double)p[3] * exp2((double)refc(p[2]) - cb);
+        if (p[2] != NINF) Zb += (double)p[3] * exp2((double)refc(p[2], ks) - cb);
         if (p[0] != NINF) {
-            const double da = (double)refc(p[0]) - ca;
-            const double db = p[2] == NINF ? 0.0 : (double)refc(p[2]) - cb;
+            const double da = (double)refc(p[0], ks) - ca;
+            const double db = p[2] == NINF ? 0.0 : (double)refc(p[2], ks) - cb;
             const double sc = exp2(da);
             Za += (double)p[1] * sc;
             A += sc * ((double)p[4] + (da - db) * (double)p[1]);
@@ -175,13 +184,13 @@ __global__ void k_kl1_merge(int rev, const float *__restrict__ part, int S, int6
     const double Zs = rev ? Za : Zb, Zt = rev ? Zb : Za;
     double *o = stats + r * 4;
     o[0] = ms;
-    o[1] = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, Zs);
+    o[1] = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, Zs, ks);
     o[2] = mt;
-    o[3] = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, Zt);
+    o[3] = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, Zt, ks);
     kl[2 * r] = rev ? 0.0f : (float)v;
     kl[2 * r + 1] = rev ? (float)v : 0.0f;
     if (undefined) kl[2 * r] = kl[2 * r + 1] = __builtin_nanf("");
-    loss[r] = (float)v;
+    loss[r] = (float)(v * (double)ro.lscale);
 }
 
 // ---- single-pass entropy ------------------------------------------------------------
@@ -489,31 +498,32 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, 
 }
 
 template <class D>
-hipError_t kl1_dt(int rev, const Shard &sh, int64_t N, float *part_k, hipStream_t st) {
+hipError_t kl1_dt(int rev, const Shard &sh, int64_t N, float *part_k, hipStream_t st,
+                  const RowOpts &o) {
     if (rev)
         hipLaunchKernelGGL((k_kl1<D, true>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s, sh.t,
-                           sh.width, part_k);
+                           sh.width, part_k, o);
     else
         hipLaunchKernelGGL((k_kl1<D, false>), dim3((unsigned)N), dim3(BLOCK), 0, st, sh.s, sh.t,
-                           sh.width, part_k);
+                           sh.width, part_k, o);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_kl1(int dtype, int reverse, const Shard &sh, int64_t N, float *part_k,
-                      hipStream_t st) {
+                      hipStream_t st, const RowOpts &o) {
     switch (dtype) {
-        case 0: return kl1_dt<F32>(reverse, sh, N, part_k, st);
-        case 1: return kl1_dt<F16>(reverse, sh, N, part_k, st);
-        default: return kl1_dt<BF16>(reverse, sh, N, part_k, st);
+        case 0: return kl1_dt<F32>(reverse, sh, N, part_k, st, o);
+        case 1: return kl1_dt<F16>(reverse, sh, N, part_k, st, o);
+        default: return kl1_dt<BF16>(reverse, sh, N, part_k, st, o);
     }
 }
 
 hipError_t launch_kl1_merge(int reverse, const float *part, int S, int64_t N, double *stats,
-                            float *kl, float *loss, hipStream_t st) {
+                            float *kl, float *loss, hipStream_t st, const RowOpts &o) {
     hipLaunchKernelGGL(k_kl1_merge, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st,
-                       reverse, part, S, N, stats, kl, loss);
+                       reverse, part, S, N, stats, kl, loss, o);
     return hipGetLastError();
 }
 

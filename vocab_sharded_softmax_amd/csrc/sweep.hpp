@@ -82,10 +82,11 @@ __device__ __forceinline__ void zero_span(typename D::T *p, int64_t n) {
     for (int64_t i = h + nv * D::VEC + threadIdx.x; i < n; i += BLK) store1<D>(p + i, 0.0f);
 }
 
-// Online (max, sum of 2^(x*L2E - c)) of one input over a batch of n elements: one
+// Online (max, sum of 2^(x*ks - c)) of one input over a batch of n elements: one
 // rescale per batch, a tree sum of the batch's exponentials.
 struct Online {
     float m = NINF, c = 0.0f, z = 0.0f;
+    float ks = L2E;  // log2 e / temperature
 
     template <int N>
     __device__ __forceinline__ void add(const float *x) {
@@ -93,11 +94,11 @@ struct Online {
 #pragma unroll
         for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
         const float nm = fmaxf(m, bm);
-        const float nc = refc(nm);
+        const float nc = refc(nm, ks);
         const float scale = m == NINF ? 0.0f : ex2(c - nc);
         float e[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) e[i] = ex2(fmaf(x[i], L2E, -nc));
+        for (int i = 0; i < N; ++i) e[i] = ex2(fmaf(x[i], ks, -nc));
 #pragma unroll
         for (int st = N / 2; st >= 1; st /= 2)
 #pragma unroll
@@ -113,6 +114,10 @@ struct Online {
 template <int WHICH>
 struct OpStats {
     Online a, b;  // first and second swept input
+    __device__ explicit OpStats(float ks = L2E) {
+        a.ks = ks;
+        b.ks = ks;
+    }
     template <int NV, int W>
     __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
                                         const int64_t (&)[NV]) {
@@ -124,17 +129,17 @@ struct OpStats {
 // (max, sum-exp) over a BLK-lane workgroup, combined in wave order; red holds
 // 2 * (BLK / 64) floats.  Every lane returns the result.
 template <int BLK = BLOCK>
-__device__ __forceinline__ MZ block_mz(MZ v, float *red) {
+__device__ __forceinline__ MZ block_mz(MZ v, float *red, float ks = L2E) {
     constexpr int NW = BLK / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = wave_mz(v);
+    v = wave_mz(v, ks);
     if (lane == 0) {
         red[2 * wave] = v.m;
         red[2 * wave + 1] = v.z;
     }
     __syncthreads();
     MZ acc{red[0], red[1]};
-    for (int k = 1; k < NW; ++k) acc = mz_combine(acc, MZ{red[2 * k], red[2 * k + 1]});
+    for (int k = 1; k < NW; ++k) acc = mz_combine(acc, MZ{red[2 * k], red[2 * k + 1]}, ks);
     __syncthreads();
     return acc;
 }

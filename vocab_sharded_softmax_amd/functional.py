@@ -8,9 +8,10 @@ Logits are GPU tensors ``[N, V]`` or ``[B, T, V]`` (views with unit vocabulary
 stride, such as causal-shift slices, are taken without a copy), or a list of
 per-shard tensors ``[..., V_k]``; ``split`` cuts a whole tensor into logical
 vocabulary shards.  Outputs are fp32 per token, shaped like the leading
-dimensions.  Temperature, masking, reduction and T^2 scaling are the caller's
-[JSD-PR, Changes].  Only first-order gradients exist: a second backward raises
-[OPS-PR, Limitations].  Every step runs in libvjsd's HIP kernels.
+dimensions.  The per-token ops leave temperature, masking, reduction and T^2
+scaling to the caller [JSD-PR, Changes]; ``jsd_loss`` fuses them into the passes.
+Only first-order gradients exist: a second backward raises [OPS-PR, Limitations].
+Every step runs in libvjsd's HIP kernels.
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ from torch.autograd.function import once_differentiable
 from . import _abi
 from ._abi import ShardSet
 
-__all__ = ["jsd", "kl_div", "entropy", "logprobs"]
+__all__ = ["jsd", "jsd_loss", "kl_div", "entropy", "logprobs"]
 
 
 def _unpack(n_shards: int, tensors):
@@ -75,6 +76,47 @@ class _JSD(torch.autograd.Function):
         out_s = _flat(gs) if want_s else [None] * half
         out_t = _flat(gt) if want_t else [None] * half
         return (None, None, None, *out_s, *out_t)
+
+
+class _JSDLoss(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, beta, temperature, scale_t2, reduction, mask, split, n_shards, *tensors):
+        half = len(tensors) // 2
+        s = _unpack(n_shards, tensors[:half])
+        t = _unpack(n_shards, tensors[half:])
+        sh = ShardSet(s, t, widths=split)
+        dev = (s[0] if n_shards else s).device
+        N, S = sh.N, sh.S
+        opts = _abi.loss_opts(N, temperature, scale_t2, mask, reduction)
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
+        rows = torch.empty((N,), dtype=torch.float32, device=dev)
+        out = torch.empty((1,), dtype=torch.float32, device=dev) if reduction != "none" else None
+        _abi.vjsd_loss_forward(sh, beta, opts, part, stats, kl, rows, out)
+        ctx.args = (beta, temperature, scale_t2, reduction, split, n_shards)
+        ctx.save_for_backward(stats, kl, mask, *tensors)
+        return rows.view(sh.lead_shape) if out is None else out.view(())
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gout):
+        beta, temperature, scale_t2, reduction, split, n = ctx.args
+        stats, kl, mask, *tensors = ctx.saved_tensors
+        half = len(tensors) // 2
+        s = _unpack(n, tensors[:half])
+        t = _unpack(n, tensors[half:])
+        need = ctx.needs_input_grad[7:]
+        want_s, want_t = any(need[:half]), any(need[half:])
+        gs = _grads_like(s, bool(n)) if want_s else None
+        gt = _grads_like(t, bool(n)) if want_t else None
+        sh = ShardSet(s, t, widths=split, gs=gs, gt=gt)
+        opts = _abi.loss_opts(sh.N, temperature, scale_t2, mask, reduction)
+        g = gout.reshape(-1).to(torch.float32).contiguous()
+        _abi.vjsd_loss_backward(sh, beta, opts, stats, kl, g, _abi.new_part(sh.N, sh.S, stats.device))
+        out_s = _flat(gs) if want_s else [None] * half
+        out_t = _flat(gt) if want_t else [None] * half
+        return (None, None, None, None, None, None, None, *out_s, *out_t)
 
 
 class _KL(torch.autograd.Function):
@@ -199,6 +241,44 @@ def jsd(student, teacher, beta: float = 0.5, *, split=None) -> torch.Tensor:
     if ns != nt or len(s) != len(t):
         raise ValueError("student and teacher must be given the same way (tensor or shard list)")
     return _JSD.apply(beta, None if split is None else tuple(split), ns, *s, *t)
+
+
+def jsd_loss(student, teacher, beta: float = 0.5, *, temperature: float = 1.0,
+             scale_t2: bool = False, mask=None, reduction: str = "mean",
+             split=None) -> torch.Tensor:
+    """Distillation loss around the per-token JSD, fused into its passes.
+
+    Both logits are divided by ``temperature`` in registers (no fp32 copies); with
+    ``scale_t2`` the per-token losses carry T^2.  ``mask`` (bool or uint8, shaped
+    like the leading dimensions) drops tokens: their logits are never read and their
+    gradients are 0.  ``reduction``: "none" (per-token losses, 0 where dropped),
+    "sum", or "mean" over the kept tokens (0 when none is kept).  The pages leave all
+    of this to the caller [JSD-PR, Changes]; its teacher-cache caller divides by the
+    temperature in fp32 first and keeps the token mean and T^2 scaling
+    (DeepSpeedExamples PR #1019).
+    """
+    beta = float(beta)
+    if not (0.0 <= beta <= 1.0):
+        raise ValueError("beta must be in [0, 1]")
+    temperature = float(temperature)
+    if not (temperature > 0.0 and temperature < float("inf")):
+        raise ValueError("temperature must be a positive finite number")
+    if reduction not in _abi.REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(_abi.REDUCTIONS)}")
+    ns, s = _as_args(student)
+    nt, t = _as_args(teacher)
+    if ns != nt or len(s) != len(t):
+        raise ValueError("student and teacher must be given the same way (tensor or shard list)")
+    m = None
+    if mask is not None:
+        lead = s[0].shape[:-1]
+        if tuple(mask.shape) != tuple(lead):
+            raise ValueError(f"mask must have shape {tuple(lead)}, got {tuple(mask.shape)}")
+        m = mask.reshape(-1)
+        m = m.view(torch.uint8) if m.dtype == torch.bool else m.to(torch.uint8)
+        m = m.contiguous()
+    return _JSDLoss.apply(beta, temperature, bool(scale_t2), reduction, m,
+                          None if split is None else tuple(split), ns, *s, *t)
 
 
 def kl_div(student, teacher, reverse: bool = False, *, split=None) -> torch.Tensor:
