@@ -180,6 +180,38 @@ def jsd_loss(s, t, beta, temperature=1.0, scale_t2=False, mask=None, reduction="
     return res
 
 
+def topk_kl(x, ids, tlogp, ignore_index=-100, widths=None, rows=None, gout=None, grads=True):
+    """Teacher top-k forward KL per row, from the student's log-probabilities at the
+    teacher's top-k ids ([OPS-PR, What]: the verl forward_kl_topk pattern):
+        kl = sum_k exp(t_k) * (t_k - lp_s(id_k))
+    over the valid slots: id_k != ignore_index and t_k > -inf (an ignored slot is
+    padding; a -inf teacher log-probability has no mass).  A valid slot whose student
+    log-probability is -inf makes the row +inf, even when exp(t_k) underflows [OPS-PR,
+    Tests]; an undefined student row is NaN with zero gradient [OPS-PR, review].
+    ``tlogp`` is data (no gradient); gx is d(gout[q] * kl[q])/dx through the
+    log-probabilities' gradient with weights -gout * exp(t_k).
+    """
+    idv = np.asarray(ids, dtype=np.int64)
+    t = np.asarray(tlogp, dtype=np.float64).reshape(idv.shape)
+    n = idv.shape[0]
+    g = np.ones(n) if gout is None else np.asarray(gout, np.float64).reshape(n)
+    valid = (idv != ignore_index) & (t > -np.inf)
+    w = np.where(valid, -g[:, None] * np.exp(np.where(valid, t, 0.0)), 0.0)
+    lp = logprobs(x, idv, ignore_index, widths=widths, rows=rows, gout=w, grads=grads)
+    lps = lp["out"]
+    with np.errstate(invalid="ignore"):
+        terms = np.where(valid, np.exp(np.where(valid, t, 0.0)) * (t - lps), 0.0)
+        terms = np.where(valid & (lps == -np.inf), np.inf, terms)
+    kl = terms.sum(axis=1)
+    st = stats(x, widths=widths, rows=rows)[0]
+    undefined = st == -np.inf
+    kl = np.where(undefined, np.nan, kl)
+    gx = lp["gx"]
+    if grads:
+        gx = np.where(undefined[:, None], 0.0, gx)
+    return dict(kl=kl, gx=gx)
+
+
 def entropy(x, widths=None, rows=None, gout=None, grads=True):
     ptr, dt, ld = _mat(x)
     V, w, r = _common(x, widths, rows)
