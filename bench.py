@@ -432,6 +432,9 @@ def sibling_rows(torch, vj, synth, reps=3):
         shg = vj.ShardSet(b.s, b.t, gs=gs)
         sx = vj.ShardSet(b.s)
         sxg = vj.ShardSet(b.s, gs=gs)
+        # the teacher's top-K ids and log-probabilities, as a rollout would hand them over
+        tk_lp, tk_ids = torch.log_softmax(b.t.float(), dim=-1).topk(K, dim=-1)
+        tk_lp, tk_ids = tk_lp.contiguous(), tk_ids.contiguous()
         ops = {
             "fwd_kl": (lambda: (vj.vkl_fwd(sh, False, part, stats, kl, loss),
                                 vj.vkl_bwd(shg, False, stats, kl, b.gout, part)), 5 * tb),
@@ -442,6 +445,10 @@ def sibling_rows(torch, vj, synth, reps=3):
             "logprobs_top20": (lambda: (vj.vlogprobs_fwd(sx, V, b.ids, -100, part, stats, out, err),
                                         vj.vlogprobs_bwd(sxg, V, stats, b.ids, -100, b.gids, part)),
                                3 * tb),
+            "topk_fwd_kl_top20": (lambda: (vj.vtopk_kl_fwd(sx, V, tk_ids, tk_lp, -100, part, stats,
+                                                           loss, err),
+                                           vj.vtopk_kl_bwd(sxg, V, stats, tk_ids, tk_lp, -100,
+                                                           b.gout, part)), 3 * tb),
         }
         for op, (fn, nbytes) in ops.items():
             fn()
@@ -455,7 +462,7 @@ def sibling_rows(torch, vj, synth, reps=3):
             res[f"{op}_{name}"] = {"fwd_bwd_ms": round(ms, 4),
                                    "tokens_per_s": round(N / (ms * 1e-3), 1),
                                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-        del b, gs, sh, shg, sx, sxg
+        del b, gs, sh, shg, sx, sxg, tk_lp, tk_ids
         torch.cuda.empty_cache()
     return res
 

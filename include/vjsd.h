@@ -295,6 +295,34 @@ VJSD_API int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype
                   const float *grad, float *part, void *stream);
 
 /*
+ * Teacher top-k forward KL per token [OPS-PR, What: the teacher top-k forward KL
+ * pattern built on the log-probabilities of the teacher's top-k ids]:
+ *     kl[r] = sum_k exp(tlogp[r][k]) * (tlogp[r][k] - lp_s(r, ids[r][k]))
+ * with lp_s the student's log-softmax over the whole (sharded) vocabulary.  ids
+ * (device int64[N][K], global vocabulary ids) and tlogp (device float[N][K], the
+ * teacher's log-probabilities at those ids) are data.  A slot whose id equals
+ * ignore_index, or whose tlogp is -inf, is padding and adds nothing.  A valid slot
+ * on a student logit of -inf makes kl +inf (decided on the logits); an undefined
+ * student row gives NaN.  An id outside [0, vocab_global) that is not ignore_index
+ * sets *dev_err = 1 and makes its row NaN (the flag is never cleared by the library).
+ * The sum runs in fp64 per row (shards in groups of 16; more groups add in fp32).
+ * Writes stats (student half), kl[N].  Shard rules and errors as vlogprobs_fwd.
+ */
+VJSD_API int vtopk_kl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                          const int64_t *ids, const float *tlogp, int K, int64_t ignore_index,
+                          float *part, double *stats, float *kl, int32_t *dev_err, void *stream);
+
+/*
+ * Its backward, to the student logits only: d kl[r] / d lp_s(id_k) = -exp(tlogp[r][k])
+ * on valid slots, through the log-probability backward, so
+ *     d/dx_j = sum_k w_k [j == id_k] - (sum_k w_k) p_j,   w_k = -grad[r] exp(tlogp[r][k]).
+ * grad is float[N]; undefined rows get exactly 0.  Errors as vlogprobs_bwd.
+ */
+VJSD_API int vtopk_kl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                          const double *stats, const int64_t *ids, const float *tlogp, int K,
+                          int64_t ignore_index, const float *grad, float *part, void *stream);
+
+/*
  * Memory-bandwidth probe: the streaming ceiling the passes above are judged against
  * (their inputs and gradients move through HBM once per pass with 16-byte
  * streaming accesses, so a plain streaming read or copy of the same size bounds

@@ -28,13 +28,13 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
     out = os.popen(f"nm -D --defined-only {abi.LIB_PATH}").read().split("\n")
     own = {ln.split()[-1] for ln in out if ln.strip() and (" T " in ln)}
-    own = {n for n in own if n.startswith(("vjsd", "vkl", "ventropy", "vlogprobs"))}
+    own = {n for n in own if n.startswith(("vjsd", "vkl", "ventropy", "vlogprobs", "vtopk"))}
     assert own == set(names)
 
 
@@ -185,6 +185,22 @@ def test_loss_entry_points_check_their_options():
     assert lib.vjsd_loss_forward(a, 1, 4, 2, 1.5, None, FAKE, FAKE, FAKE, FAKE, None, None) == BETA
     assert lib.vjsd_loss_forward(a, 1, 4, 2, 0.5, None, None, FAKE, FAKE, FAKE, None, None) == ARG
     assert lib.vjsd_loss_backward(a, 1, 4, 2, 0.5, None, FAKE, FAKE, None, FAKE, None) == ARG
+
+
+def test_topk_kl_checks_its_arguments():
+    a = shards([5, 7])
+    f = lambda *x: lib.vtopk_kl_fwd(a, 2, 4, 2, 12, *x, None)
+    assert f(FAKE, None, 3, -100, FAKE, FAKE, FAKE, FAKE) == ARG  # no teacher log-probs
+    assert f(FAKE, FAKE, 3, -100, FAKE, FAKE, None, FAKE) == ARG  # no kl
+    assert f(FAKE, FAKE, 3, -100, FAKE, FAKE, FAKE, None) == ARG  # no error flag
+    assert lib.vtopk_kl_fwd(a, 2, 4, 7, 12, FAKE, FAKE, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == DTYPE
+    assert lib.vtopk_kl_fwd(a, 2, 4, 2, 13, FAKE, FAKE, 3, -100, FAKE, FAKE, FAKE, FAKE, None) == LAYOUT
+    assert lib.vtopk_kl_fwd(shards([5, 0, 7]), 3, 4, 2, 12, FAKE, FAKE, 3, -100, FAKE, FAKE, FAKE,
+                            FAKE, None) == EMPTY
+    b = lambda *x: lib.vtopk_kl_bwd(a, 2, 4, 2, 12, *x, None)
+    assert b(FAKE, FAKE, None, 3, -100, FAKE, FAKE) == ARG
+    assert b(FAKE, FAKE, FAKE, 3, -100, None, FAKE) == ARG
+    assert lib.vtopk_kl_fwd(a, 2, 0, 2, 12, None, None, 3, -100, None, None, None, None, None) == OK
 
 
 def test_membw_probe_checks_its_arguments():

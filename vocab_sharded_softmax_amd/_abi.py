@@ -73,6 +73,8 @@ def _load():
         "ventropy_bwd": ([SP, I, I64, I, P, P, P, P, P], I),
         "vlogprobs_fwd": ([SP, I, I64, I, I64, P, I, I64, P, P, P, P, P], I),
         "vlogprobs_bwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P, P], I),
+        "vtopk_kl_fwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P, P, P, P], I),
+        "vtopk_kl_bwd": ([SP, I, I64, I, I64, P, P, P, I, I64, P, P, P], I),
         "vjsd_membw_probe": ([P, P, ctypes.c_size_t, I, P], I),
         "vjsd_loss_forward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P, P], I),
         "vjsd_loss_backward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P], I),
@@ -343,6 +345,32 @@ def vlogprobs_fwd(sh: ShardSet, vocab_global: int, ids, ignore_index: int, part,
                              _ptr(stats, torch.float64, N * 4, "stats"),
                              _ptr(out, torch.float32, N * K, "out"),
                              _ptr(dev_err, torch.int32, 1, "dev_err"), _stream(stream)))
+
+
+def vtopk_kl_fwd(sh: ShardSet, vocab_global: int, ids, tlogp, ignore_index: int, part, stats,
+                 kl, dev_err, stream=None) -> None:
+    N = sh.N
+    K = ids.shape[-1] if ids is not None and ids.dim() else 0
+    _check(lib.vtopk_kl_fwd(sh.arr, sh.S, N, sh.dtype_code, int(vocab_global),
+                            _ptr(ids, torch.int64, N * K, "ids"),
+                            _ptr(tlogp, torch.float32, N * K, "tlogp"), K, int(ignore_index),
+                            _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                            _ptr(stats, torch.float64, N * 4, "stats"),
+                            _ptr(kl, torch.float32, N, "kl"),
+                            _ptr(dev_err, torch.int32, 1, "dev_err"), _stream(stream)))
+
+
+def vtopk_kl_bwd(sh: ShardSet, vocab_global: int, stats, ids, tlogp, ignore_index: int, grad,
+                 part, stream=None) -> None:
+    N = sh.N
+    K = ids.shape[-1] if ids is not None and ids.dim() else 0
+    _check(lib.vtopk_kl_bwd(sh.arr, sh.S, N, sh.dtype_code, int(vocab_global),
+                            _ptr(stats, torch.float64, N * 4, "stats"),
+                            _ptr(ids, torch.int64, N * K, "ids"),
+                            _ptr(tlogp, torch.float32, N * K, "tlogp"), K, int(ignore_index),
+                            _ptr(grad, torch.float32, N, "grad"),
+                            _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                            _stream(stream)))
 
 
 def vlogprobs_bwd(sh: ShardSet, vocab_global: int, stats, ids, ignore_index: int, grad, part,

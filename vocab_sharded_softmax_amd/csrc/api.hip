@@ -126,6 +126,37 @@ int mode_of(double beta) {
     return beta == 0.0 ? vjsd::FWD_KL : (beta == 1.0 ? vjsd::REV_KL : vjsd::INTERIOR);
 }
 
+// The student views of up to LP_TABLE shards starting at shard k0.
+vjsd::LpTable lp_table(const vjsd_shard *shards, int S, int k0) {
+    vjsd::LpTable tab;
+    memset(&tab, 0, sizeof tab);
+    tab.n = (S - k0) < vjsd::LP_TABLE ? (S - k0) : vjsd::LP_TABLE;
+    for (int q = 0; q < tab.n; ++q) {
+        const vjsd_shard &h = shards[k0 + q];
+        tab.start[q] = h.vocab_start;
+        tab.width[q] = h.width;
+        tab.x[q] = {h.s.p, h.s.row_stride, h.s.rows_per_batch, h.s.batch_stride};
+    }
+    return tab;
+}
+
+// Log-probability backward with per-slot upstream weights (validated arguments).
+int lp_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                const double *stats, const int64_t *ids, int K, int64_t ignore_index,
+                const vjsd::LpWeights &w, float *part, hipStream_t st) {
+    int e;
+    if ((e = hip_status(vjsd::launch_lp_bwd_prep(N, vocab_global, stats, ids, K, ignore_index, w,
+                                                 part, st))))
+        return e;
+    for (int k = 0; k < S; ++k) {
+        if (!shards[k].gs.p) continue;
+        Shard sh = convert(shards[k], false, true);
+        if ((e = hip_status(vjsd::launch_lp_bwd(dtype, sh, N, ids, K, ignore_index, w, part, st))))
+            return e;
+    }
+    return VJSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -422,15 +453,7 @@ int vlogprobs_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t
     if ((e = hip_status(vjsd::launch_merge(part_of(part, 0, N), S, N, 1, stats, st)))) return e;
     if (K == 0) return VJSD_OK;
     for (int k0 = 0; k0 < S; k0 += vjsd::LP_TABLE) {
-        vjsd::LpTable tab;
-        memset(&tab, 0, sizeof tab);
-        tab.n = (S - k0) < vjsd::LP_TABLE ? (S - k0) : vjsd::LP_TABLE;
-        for (int q = 0; q < tab.n; ++q) {
-            const vjsd_shard &h = shards[k0 + q];
-            tab.start[q] = h.vocab_start;
-            tab.width[q] = h.width;
-            tab.x[q] = {h.s.p, h.s.row_stride, h.s.rows_per_batch, h.s.batch_stride};
-        }
+        vjsd::LpTable tab = lp_table(shards, S, k0);
         if ((e = hip_status(vjsd::launch_lp_gather(dtype, tab, k0 == 0, N, vocab_global, ids, K,
                                                    ignore_index, stats, out, dev_err, st))))
             return e;
@@ -447,17 +470,47 @@ int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t
     if (N == 0) return VJSD_OK;
     if (!stats || !part || (K > 0 && !grad)) return VJSD_ERR_ARG;
     hipStream_t st = (hipStream_t)stream;
-    if ((e = hip_status(vjsd::launch_lp_bwd_prep(N, vocab_global, stats, ids, K, ignore_index,
-                                                 grad, part, st))))
-        return e;
+    vjsd::LpWeights w;
+    w.grad = grad;
+    return lp_backward(shards, S, N, dtype, vocab_global, stats, ids, K, ignore_index, w, part, st);
+}
+
+int vtopk_kl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                 const int64_t *ids, const float *tlogp, int K, int64_t ignore_index, float *part,
+                 double *stats, float *kl, int32_t *dev_err, void *stream) {
+    int e = check_logprobs(shards, S, N, dtype, vocab_global, ids, K);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, false))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!part || !stats || !kl || !dev_err || (K > 0 && !tlogp)) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
     for (int k = 0; k < S; ++k) {
-        if (!shards[k].gs.p) continue;
-        Shard sh = convert(shards[k], false, true);
-        if ((e = hip_status(vjsd::launch_lp_bwd(dtype, sh, N, ids, K, ignore_index, grad, part,
-                                                st))))
+        Shard sh = convert(shards[k], false, false);
+        if ((e = hip_status(vjsd::launch_stats(dtype, 1, sh, N, part_of(part, k, N), st)))) return e;
+    }
+    if ((e = hip_status(vjsd::launch_merge(part_of(part, 0, N), S, N, 1, stats, st)))) return e;
+    for (int k0 = 0; k0 < S; k0 += vjsd::LP_TABLE) {
+        vjsd::LpTable tab = lp_table(shards, S, k0);
+        if ((e = hip_status(vjsd::launch_topk_kl(dtype, tab, k0 == 0, N, vocab_global, ids, tlogp,
+                                                 K, ignore_index, stats, kl, dev_err, st))))
             return e;
     }
     return VJSD_OK;
+}
+
+int vtopk_kl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                 const double *stats, const int64_t *ids, const float *tlogp, int K,
+                 int64_t ignore_index, const float *grad, float *part, void *stream) {
+    int e = check_logprobs(shards, S, N, dtype, vocab_global, ids, K);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, true))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!stats || !part || !grad || (K > 0 && !tlogp)) return VJSD_ERR_ARG;
+    vjsd::LpWeights w;
+    w.tlogp = tlogp;
+    w.grow = grad;
+    return lp_backward(shards, S, N, dtype, vocab_global, stats, ids, K, ignore_index, w, part,
+                       (hipStream_t)stream);
 }
 
 }  // extern "C"

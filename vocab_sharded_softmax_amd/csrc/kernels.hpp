@@ -96,10 +96,30 @@ struct LpTable {
 hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N,
                             int64_t vocab_global, const int64_t *ids, int K, int64_t ignore,
                             const double *stats, float *out, int32_t *dev_err, hipStream_t st);
+// Upstream gradient of each (row, slot) of the log-probability backward: grad[r*K+k]
+// for log-probabilities; -grow[r] * exp(tlogp[r*K+k]) (0 where tlogp is -inf) for the
+// teacher top-k forward KL, whose value depends on lp_s(id_k) through that weight.
+struct LpWeights {
+    const float *grad = nullptr;
+    const float *tlogp = nullptr;
+    const float *grow = nullptr;
+};
+__device__ __forceinline__ float lp_weight(const LpWeights &w, int64_t r, int K, int k) {
+    if (w.tlogp == nullptr) return w.grad[r * K + k];
+    const float t = w.tlogp[r * K + k];
+    return t > -__builtin_huge_valf() ? -w.grow[r] * expf(t) : 0.0f;
+}
+
 hipError_t launch_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *stats,
-                              const int64_t *ids, int K, int64_t ignore, const float *grad,
+                              const int64_t *ids, int K, int64_t ignore, const LpWeights &w,
                               float *rowc, hipStream_t st);
 hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, const int64_t *ids, int K,
-                         int64_t ignore, const float *grad, const float *rowc, hipStream_t st);
+                         int64_t ignore, const LpWeights &w, const float *rowc, hipStream_t st);
+// teacher top-k forward KL: per row, sum over the ids this table of shards owns of
+// exp(t) (t - lp_s(id)); the first launch writes, later launches add
+hipError_t launch_topk_kl(int dtype, const LpTable &tab, bool first, int64_t N,
+                          int64_t vocab_global, const int64_t *ids, const float *tlogp, int K,
+                          int64_t ignore, const double *stats, float *kl, int32_t *dev_err,
+                          hipStream_t st);
 
 }  // namespace vjsd

@@ -415,6 +415,53 @@ __global__ void k_lp_gather(LpTable tab, int first, int64_t N, int64_t vocab_glo
     }
 }
 
+// Teacher top-k forward KL ([OPS-PR, What]: the teacher top-k forward KL built on the
+// log-probabilities of the teacher's top-k ids).  One thread per row sums, in fp64,
+// exp(t_k) (t_k - lp_s(id_k)) over the slots whose id this table of shards owns; a slot
+// is padding when id_k == ignore or t_k == -inf.  A student logit of -inf under
+// teacher mass makes the row +inf; an undefined student row is NaN; an id outside
+// [0, vocab_global) raises the error flag (first launch) and makes the row NaN.  The
+// first launch of a call writes kl, later launches (more shards) add to it.
+template <class D>
+__global__ void k_topk_kl(LpTable tab, int first, int64_t N, int64_t vocab_global,
+                          const int64_t *__restrict__ ids, const float *__restrict__ tlogp, int K,
+                          int64_t ignore, const double *__restrict__ stats,
+                          float *__restrict__ kl, int32_t *__restrict__ dev_err) {
+    using T = typename D::T;
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= N) return;
+    const double m = stats[r * 4], lz = stats[r * 4 + 1];
+    const bool undefined = m == -__builtin_inf();
+    double acc = 0.0;
+    bool bad = false, inf = false;
+    for (int k = 0; k < K; ++k) {
+        const int64_t id = ids[r * K + k];
+        if (id == ignore) continue;
+        if (id < 0 || id >= vocab_global) {
+            if (first) {
+                *dev_err = 1;
+                bad = true;
+            }
+            continue;
+        }
+        const float t = tlogp[r * K + k];
+        if (t == -__builtin_huge_valf()) continue;  // no teacher mass
+        if (t != t) bad = true;                     // NaN propagates
+        for (int q = 0; q < tab.n; ++q) {
+            if (id < tab.start[q] || id >= tab.start[q] + tab.width[q]) continue;
+            if (!undefined) {
+                const double x = load1<D>(row_ptr<T>(tab.x[q], r) + (id - tab.start[q]));
+                if (x == -__builtin_inf()) inf = true;
+                else acc += exp((double)t) * ((double)t - ((x - m) - lz));
+            }
+            break;
+        }
+    }
+    const float part = bad ? __builtin_nanf("") : (inf ? __builtin_huge_valf() : (float)acc);
+    if (first) kl[r] = undefined ? __builtin_nanf("") : part;
+    else kl[r] += part;
+}
+
 // d/dx_j = -G p_j everywhere (G = sum of the valid upstream gradients), then the ids a
 // chunk owns are rewritten as (sum of their g) - G p_j, rounded once.
 template <class D>
@@ -441,7 +488,7 @@ struct OpLpBwd {
 // rowc: c, C = -G / Z, 1 / Z, G and the undefined flag
 __global__ void k_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *__restrict__ stats,
                               const int64_t *__restrict__ ids, int K, int64_t ignore,
-                              const float *__restrict__ grad, float *__restrict__ rowc) {
+                              LpWeights wts, float *__restrict__ rowc) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= N) return;
     const float m = (float)stats[r * 4];
@@ -451,7 +498,7 @@ __global__ void k_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *__r
     double G = 0.0;
     for (int k = 0; k < K; ++k) {
         const int64_t id = ids[r * K + k];
-        if (id != ignore && id >= 0 && id < vocab_global) G += grad[r * K + k];
+        if (id != ignore && id >= 0 && id < vocab_global) G += lp_weight(wts, r, K, k);
     }
     const double Z = z_from_stats(m, stats[r * 4 + 1]);
     o[0] = refc(m);
@@ -464,7 +511,7 @@ template <class D>
 __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, int64_t start,
                                                        int64_t w, int64_t cw, int64_t nchunk,
                                                        const int64_t *__restrict__ ids, int K,
-                                                       int64_t ignore, const float *__restrict__ grad,
+                                                       int64_t ignore, LpWeights wts,
                                                        const float *__restrict__ rowc) {
     using T = typename D::T;
     const int64_t b = blockIdx.x;
@@ -485,13 +532,12 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, 
     sweep<D, 1, false, GRAD_BLOCK, true>(x, x, n, head_len<T>(n, x, gx), op);
     __syncthreads();  // this chunk's streamed values land before the id fix-ups
     const int64_t *id = ids + r * K;
-    const float *g = grad + r * K;
     for (int q = threadIdx.x; q < K; q += GRAD_BLOCK) {
         const int64_t j = id[q] - start - c0;
         if (id[q] == ignore || j < 0 || j >= n) continue;
         float gsum = 0.0f;
         for (int q2 = 0; q2 < K; ++q2)
-            if (id[q2] == id[q]) gsum += g[q2];
+            if (id[q2] == id[q]) gsum += lp_weight(wts, r, K, q2);
         const float p = ex2(fmaxf(fmaf(load1<D>(x + j), L2E, -op.c), U_FLOOR)) * k[2];
         store1<D>(gx + j, gsum - k[3] * p);
     }
@@ -579,22 +625,36 @@ hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N
 }
 
 hipError_t launch_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *stats,
-                              const int64_t *ids, int K, int64_t ignore, const float *grad,
+                              const int64_t *ids, int K, int64_t ignore, const LpWeights &w,
                               float *rowc, hipStream_t st) {
     hipLaunchKernelGGL(k_lp_bwd_prep, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, N,
-                       vocab_global, stats, ids, K, ignore, grad, rowc);
+                       vocab_global, stats, ids, K, ignore, w, rowc);
     return hipGetLastError();
 }
 
 hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, const int64_t *ids, int K,
-                         int64_t ignore, const float *grad, const float *rowc, hipStream_t st) {
+                         int64_t ignore, const LpWeights &w, const float *rowc, hipStream_t st) {
     const Chunks ch = grad_chunks(N, sh.width, dtype == 0 ? 4 : 2);
     if (ch.nchunk == 0) return hipSuccess;
     const dim3 grid((unsigned)(N * ch.nchunk)), block(GRAD_BLOCK);
     switch (dtype) {
-        case 0: hipLaunchKernelGGL(k_lp_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, grad, rowc); break;
-        case 1: hipLaunchKernelGGL(k_lp_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, grad, rowc); break;
-        default: hipLaunchKernelGGL(k_lp_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, grad, rowc);
+        case 0: hipLaunchKernelGGL(k_lp_bwd<F32>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, w, rowc); break;
+        case 1: hipLaunchKernelGGL(k_lp_bwd<F16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, w, rowc); break;
+        default: hipLaunchKernelGGL(k_lp_bwd<BF16>, grid, block, 0, st, sh.s, sh.gs, sh.start, sh.width, ch.cw, ch.nchunk, ids, K, ignore, w, rowc);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_kl(int dtype, const LpTable &tab, bool first, int64_t N,
+                          int64_t vocab_global, const int64_t *ids, const float *tlogp, int K,
+                          int64_t ignore, const double *stats, float *kl, int32_t *dev_err,
+                          hipStream_t st) {
+    const dim3 grid((unsigned)((N + 255) / 256)), block(256);
+    const int f = first ? 1 : 0;
+    switch (dtype) {
+        case 0: hipLaunchKernelGGL(k_topk_kl<F32>, grid, block, 0, st, tab, f, N, vocab_global, ids, tlogp, K, ignore, stats, kl, dev_err); break;
+        case 1: hipLaunchKernelGGL(k_topk_kl<F16>, grid, block, 0, st, tab, f, N, vocab_global, ids, tlogp, K, ignore, stats, kl, dev_err); break;
+        default: hipLaunchKernelGGL(k_topk_kl<BF16>, grid, block, 0, st, tab, f, N, vocab_global, ids, tlogp, K, ignore, stats, kl, dev_err);
     }
     return hipGetLastError();
 }

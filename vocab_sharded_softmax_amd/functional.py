@@ -21,7 +21,7 @@ from torch.autograd.function import once_differentiable
 from . import _abi
 from ._abi import ShardSet
 
-__all__ = ["jsd", "jsd_loss", "kl_div", "entropy", "logprobs"]
+__all__ = ["jsd", "jsd_loss", "kl_div", "entropy", "logprobs", "topk_kl"]
 
 
 def _unpack(n_shards: int, tensors):
@@ -220,6 +220,41 @@ class _Logprobs(torch.autograd.Function):
         return (None, None, None, None, *_flat(gx))
 
 
+class _TopkKL(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, ids, tlogp, ignore_index, split, n_shards, *tensors):
+        x = _unpack(n_shards, tensors)
+        sh = ShardSet(x, widths=split)
+        dev = (x[0] if n_shards else x).device
+        N, S = sh.N, sh.S
+        K = ids.shape[-1]
+        idv = ids.reshape(N, K).to(torch.int64).contiguous()
+        tl = tlogp.reshape(N, K).to(torch.float32).contiguous()
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        kl = torch.empty((N,), dtype=torch.float32, device=dev)
+        err = torch.zeros((1,), dtype=torch.int32, device=dev)
+        _abi.vtopk_kl_fwd(sh, sh.V, idv, tl, ignore_index, part, stats, kl, err)
+        if N and K and int(err.item()):
+            raise ValueError("topk_kl: an index is outside [0, V) and is not ignore_index")
+        ctx.ignore_index, ctx.split, ctx.n_shards, ctx.V = ignore_index, split, n_shards, sh.V
+        ctx.save_for_backward(stats, idv, tl, *tensors)
+        return kl.view(sh.lead_shape)
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gout):
+        stats, idv, tl, *tensors = ctx.saved_tensors
+        n = ctx.n_shards
+        x = _unpack(n, tensors)
+        gx = _grads_like(x, bool(n))
+        sh = ShardSet(x, widths=ctx.split, gs=gx)
+        g = gout.reshape(-1).to(torch.float32).contiguous()
+        _abi.vtopk_kl_bwd(sh, ctx.V, stats, idv, tl, ctx.ignore_index, g,
+                          _abi.new_part(sh.N, sh.S, stats.device))
+        return (None, None, None, None, None, *_flat(gx))
+
+
 def _as_args(x):
     if isinstance(x, (list, tuple)):
         return len(x), list(x)
@@ -295,6 +330,26 @@ def entropy(logits, *, split=None) -> torch.Tensor:
     """Per-token entropy of softmax(logits) [OPS-PR, What]; single input pass."""
     n, x = _as_args(logits)
     return _Entropy.apply(None if split is None else tuple(split), n, *x)
+
+
+def topk_kl(student, teacher_topk_ids, teacher_topk_logp, *, ignore_index: int = -100,
+            split=None) -> torch.Tensor:
+    """Teacher top-k forward KL per token [OPS-PR, What]:
+    sum_k exp(t_k) * (t_k - log p_student(id_k)) over the teacher's top-k ids
+    ``[..., K]`` (global) and log-probabilities ``[..., K]``.  Slots equal to
+    ``ignore_index`` or with t_k = -inf are padding.  The student's log-probabilities
+    are gathered and combined inside one kernel; gradients flow to the student
+    logits only (the teacher's log-probabilities are data).  An index outside the
+    vocabulary raises ValueError after a host synchronisation."""
+    if teacher_topk_logp.requires_grad:
+        raise ValueError("teacher_topk_logp is data: detach it")
+    if teacher_topk_ids.shape != teacher_topk_logp.shape:
+        raise ValueError("teacher_topk_ids and teacher_topk_logp must have the same shape")
+    n, x = _as_args(student)
+    if tuple(teacher_topk_ids.shape[:-1]) != tuple(x[0].shape[:-1]):
+        raise ValueError("the top-k tensors must be shaped [..., K] like the logits' leading dims")
+    return _TopkKL.apply(teacher_topk_ids, teacher_topk_logp, int(ignore_index),
+                         None if split is None else tuple(split), n, *x)
 
 
 def logprobs(logits, index, *, ignore_index: int = -100, split=None) -> torch.Tensor:
