@@ -212,6 +212,39 @@ def topk_kl(x, ids, tlogp, ignore_index=-100, widths=None, rows=None, gout=None,
     return dict(kl=kl, gx=gx)
 
 
+def cross_entropy(x, labels, ignore_index=-100, reduction="mean", grad=None, widths=None,
+                  grads=True):
+    """Cross-entropy of integer labels over a sharded vocabulary, the loss a
+    vocabulary-parallel causal-LM head installs (DeepSpeed PR #8309, "[AutoTP] vocab-
+    parallel LM head": vocab_parallel_cross_entropy), written out with the
+    log-probabilities:
+        rows_r = -lp(x_r)[label_r], exactly 0 where label_r == ignore_index
+        "sum": sum of rows over labelled tokens; "mean": that sum / max(labelled, 1)
+    (no labelled token gives 0 with zero gradients).  An undefined row with a label
+    is NaN with zero gradient.  ``grad``: [N] for "none", a scalar otherwise.
+    Returns dict(rows, out, gx) with gx = d(sum_r grad_r rows_r or grad * out)/dx.
+    """
+    lab = np.asarray(labels, dtype=np.int64).reshape(-1)
+    N = lab.size
+    valid = lab != ignore_index
+    count = int(valid.sum())
+    if reduction == "none":
+        g = np.zeros(N) if grad is None else np.asarray(grad, np.float64).reshape(N)
+    elif reduction == "sum":
+        g = np.full(N, 0.0 if grad is None else float(grad))
+    elif reduction == "mean":
+        g = np.full(N, (0.0 if grad is None else float(grad)) / max(count, 1))
+    else:
+        raise ValueError(reduction)
+    lp = logprobs(x, lab[:, None], ignore_index, widths=widths, gout=-g[:, None], grads=grads)
+    rows = np.where(valid, -lp["out"][:, 0], 0.0)
+    out = None
+    if reduction != "none":
+        tot = rows[valid].sum() if count else 0.0
+        out = tot / max(count, 1) if reduction == "mean" else tot
+    return dict(rows=rows, out=out, gx=lp["gx"])
+
+
 def entropy(x, widths=None, rows=None, gout=None, grads=True):
     ptr, dt, ld = _mat(x)
     V, w, r = _common(x, widths, rows)
