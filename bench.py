@@ -12,7 +12,8 @@ Printed: one JSON line with tokens/s, ms per step, the roofline of the dominant
 kernel (the backward), measured with HIP events on the stream the kernels run
 on, the fp64 CPU oracle's rate on a bounded sample of the same rows, and
 per-kernel and sibling-op timings (forward / reverse KL, entropy, top-k
-log-probabilities at N=16384, V=128256 in bf16 and fp16; the beta = 0 / 1 JSD
+log-probabilities, teacher top-k forward KL, cross-entropy at N=16384, V=128256 in
+bf16 and fp16; the beta = 0 / 1 JSD
 branches; the distillation-loss form at temperature 2 with a token mean, all tokens
 and 3% kept; the one-pass forward at one tensor-parallel rank's shard width).  The HBM traffic figure comes from committed rocprofv3 counters and
 is reported only while the kernel sources match the ones profiled.
@@ -435,6 +436,9 @@ def sibling_rows(torch, vj, synth, reps=3):
         # the teacher's top-K ids and log-probabilities, as a rollout would hand them over
         tk_lp, tk_ids = torch.log_softmax(b.t.float(), dim=-1).topk(K, dim=-1)
         tk_lp, tk_ids = tk_lp.contiguous(), tk_ids.contiguous()
+        ce_lab = b.ids[:, 0].contiguous()  # one label per token, 10% ignore_index
+        ce_out = torch.empty(1, dtype=torch.float32, device="cuda")
+        one = torch.ones(1, dtype=torch.float32, device="cuda")
         ops = {
             "fwd_kl": (lambda: (vj.vkl_fwd(sh, False, part, stats, kl, loss),
                                 vj.vkl_bwd(shg, False, stats, kl, b.gout, part)), 5 * tb),
@@ -449,6 +453,10 @@ def sibling_rows(torch, vj, synth, reps=3):
                                                            loss, err),
                                            vj.vtopk_kl_bwd(sxg, V, stats, tk_ids, tk_lp, -100,
                                                            b.gout, part)), 3 * tb),
+            "cross_entropy_mean": (lambda: (vj.vce_fwd(sx, V, ce_lab, -100, "mean", part, stats,
+                                                       loss, ce_out, err),
+                                            vj.vce_bwd(sxg, V, stats, ce_lab, -100, "mean", one,
+                                                       part)), 3 * tb),
         }
         for op, (fn, nbytes) in ops.items():
             fn()
@@ -462,7 +470,7 @@ def sibling_rows(torch, vj, synth, reps=3):
             res[f"{op}_{name}"] = {"fwd_bwd_ms": round(ms, 4),
                                    "tokens_per_s": round(N / (ms * 1e-3), 1),
                                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-        del b, gs, sh, shg, sx, sxg, tk_lp, tk_ids
+        del b, gs, sh, shg, sx, sxg, tk_lp, tk_ids, ce_lab
         torch.cuda.empty_cache()
     return res
 

@@ -295,6 +295,33 @@ VJSD_API int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype
                   const float *grad, float *part, void *stream);
 
 /*
+ * Cross-entropy of integer labels over the sharded vocabulary, the loss a
+ * vocabulary-parallel causal-LM head installs (DeepSpeed PR #8309, "[AutoTP]
+ * vocab-parallel LM head": vocab_parallel_cross_entropy):
+ *     rows[r] = -lp_s(r, labels[r]),  exactly 0 where labels[r] == ignore_index
+ * with lp_s the log-softmax of the shards' `s` views (labels: device int64[N],
+ * global ids).  A row whose label is ignore_index is never read.  reduction as in
+ * vjsd_loss_opts: out[0] = sum over labelled rows, or their mean (0 when none).
+ * An undefined labelled row is NaN; a label outside [0, vocab_global) that is not
+ * ignore_index sets *dev_err = 1 and makes its row NaN.  Writes stats (s half) and
+ * rows[N].  Shard rules and errors as vlogprobs_fwd, plus VJSD_ERR_ARG for a bad
+ * reduction or a NULL out with a reduction.  With N == 0 only out[0] = 0 is written.
+ */
+VJSD_API int vce_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                     const int64_t *labels, int64_t ignore_index, int reduction, float *part,
+                     double *stats, float *rows, float *out, int32_t *dev_err, void *stream);
+
+/*
+ * Its backward into each shard's gs view: d/dx_j = g_r (p_j - [j == label_r]) for
+ * labelled rows (g_r = grad[r] for VJSD_REDUCE_NONE, grad[0] for a sum, grad[0] /
+ * max(labelled, 1) for a mean), exactly 0 for ignored and undefined rows, which are
+ * not read.  Errors as vlogprobs_bwd.
+ */
+VJSD_API int vce_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+                     const double *stats, const int64_t *labels, int64_t ignore_index, int reduction,
+                     const float *grad, float *part, void *stream);
+
+/*
  * Teacher top-k forward KL per token [OPS-PR, What: the teacher top-k forward KL
  * pattern built on the log-probabilities of the teacher's top-k ids]:
  *     kl[r] = sum_k exp(tlogp[r][k]) * (tlogp[r][k] - lp_s(r, ids[r][k]))

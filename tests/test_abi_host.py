@@ -28,13 +28,13 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
     out = os.popen(f"nm -D --defined-only {abi.LIB_PATH}").read().split("\n")
     own = {ln.split()[-1] for ln in out if ln.strip() and (" T " in ln)}
-    own = {n for n in own if n.startswith(("vjsd", "vkl", "ventropy", "vlogprobs", "vtopk"))}
+    own = {n for n in own if n.startswith(("vjsd", "vkl", "ventropy", "vlogprobs", "vtopk", "vce"))}
     assert own == set(names)
 
 
@@ -201,6 +201,20 @@ def test_topk_kl_checks_its_arguments():
     assert b(FAKE, FAKE, None, 3, -100, FAKE, FAKE) == ARG
     assert b(FAKE, FAKE, FAKE, 3, -100, None, FAKE) == ARG
     assert lib.vtopk_kl_fwd(a, 2, 0, 2, 12, None, None, 3, -100, None, None, None, None, None) == OK
+
+
+def test_cross_entropy_checks_its_arguments():
+    a = shards([5, 7])
+    f = lambda red, *x: lib.vce_fwd(a, 2, 4, 2, 12, FAKE, -100, red, *x, None)
+    assert f(3, FAKE, FAKE, FAKE, FAKE, FAKE) == ARG  # bad reduction
+    assert f(2, FAKE, FAKE, FAKE, None, FAKE) == ARG  # a reduction needs out
+    assert f(0, FAKE, FAKE, None, None, FAKE) == ARG  # no rows
+    assert f(0, FAKE, FAKE, FAKE, None, None) == ARG  # no error flag
+    assert lib.vce_fwd(a, 2, 4, 2, 12, None, -100, 0, FAKE, FAKE, FAKE, None, FAKE, None) == ARG
+    assert lib.vce_fwd(a, 2, 4, 2, 13, FAKE, -100, 0, FAKE, FAKE, FAKE, None, FAKE, None) == LAYOUT
+    assert lib.vce_fwd(a, 2, 0, 2, 12, None, -100, 0, None, None, None, None, None, None) == OK
+    assert lib.vce_bwd(a, 2, 4, 2, 12, FAKE, FAKE, -100, 5, FAKE, FAKE, None) == ARG
+    assert lib.vce_bwd(a, 2, 4, 2, 12, FAKE, FAKE, -100, 0, None, FAKE, None) == ARG
 
 
 def test_membw_probe_checks_its_arguments():

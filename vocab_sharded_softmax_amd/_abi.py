@@ -74,6 +74,8 @@ def _load():
         "vlogprobs_fwd": ([SP, I, I64, I, I64, P, I, I64, P, P, P, P, P], I),
         "vlogprobs_bwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P, P], I),
         "vtopk_kl_fwd": ([SP, I, I64, I, I64, P, P, I, I64, P, P, P, P, P], I),
+        "vce_fwd": ([SP, I, I64, I, I64, P, I64, I, P, P, P, P, P, P], I),
+        "vce_bwd": ([SP, I, I64, I, I64, P, P, I64, I, P, P, P], I),
         "vtopk_kl_bwd": ([SP, I, I64, I, I64, P, P, P, I, I64, P, P, P], I),
         "vjsd_membw_probe": ([P, P, ctypes.c_size_t, I, P], I),
         "vjsd_loss_forward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P, P], I),
@@ -345,6 +347,33 @@ def vlogprobs_fwd(sh: ShardSet, vocab_global: int, ids, ignore_index: int, part,
                              _ptr(stats, torch.float64, N * 4, "stats"),
                              _ptr(out, torch.float32, N * K, "out"),
                              _ptr(dev_err, torch.int32, 1, "dev_err"), _stream(stream)))
+
+
+def vce_fwd(sh: ShardSet, vocab_global: int, labels, ignore_index: int, reduction: str, part,
+            stats, rows, out, dev_err, stream=None) -> None:
+    N = sh.N
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
+    _check(lib.vce_fwd(sh.arr, sh.S, N, sh.dtype_code, int(vocab_global),
+                       _ptr(labels, torch.int64, N, "labels"), int(ignore_index),
+                       REDUCTIONS[reduction],
+                       _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                       _ptr(stats, torch.float64, N * 4, "stats"),
+                       _ptr(rows, torch.float32, N, "rows"), _ptr(out, torch.float32, 1, "out"),
+                       _ptr(dev_err, torch.int32, 1, "dev_err"), _stream(stream)))
+
+
+def vce_bwd(sh: ShardSet, vocab_global: int, stats, labels, ignore_index: int, reduction: str,
+            grad, part, stream=None) -> None:
+    N = sh.N
+    if reduction not in REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(REDUCTIONS)}")
+    _check(lib.vce_bwd(sh.arr, sh.S, N, sh.dtype_code, int(vocab_global),
+                       _ptr(stats, torch.float64, N * 4, "stats"),
+                       _ptr(labels, torch.int64, N, "labels"), int(ignore_index),
+                       REDUCTIONS[reduction],
+                       _ptr(grad, torch.float32, N if reduction == "none" else 1, "grad"),
+                       _ptr(part, torch.float32, part_floats(N, sh.S), "part"), _stream(stream)))
 
 
 def vtopk_kl_fwd(sh: ShardSet, vocab_global: int, ids, tlogp, ignore_index: int, part, stats,

@@ -273,7 +273,8 @@ int vjsd_loss_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, dou
     hipStream_t st = (hipStream_t)stream;
     if (N == 0) {
         if (c.red != VJSD_REDUCE_NONE)
-            return hip_status(vjsd::launch_reduce_rows(nullptr, nullptr, 0, false, out, nullptr, st));
+            return hip_status(
+                vjsd::launch_reduce_rows(nullptr, vjsd::RowOpts(), 0, false, out, nullptr, st));
         return VJSD_OK;
     }
     if (!part || !stats || !kl || !rows) return VJSD_ERR_ARG;
@@ -312,7 +313,7 @@ int vjsd_loss_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, dou
             return e;
     }
     if (c.red == VJSD_REDUCE_NONE) return VJSD_OK;
-    return hip_status(vjsd::launch_reduce_rows(rows, c.mask, N, c.red == VJSD_REDUCE_MEAN, out,
+    return hip_status(vjsd::launch_reduce_rows(rows, ro, N, c.red == VJSD_REDUCE_MEAN, out,
                                                nullptr, st));
 }
 
@@ -336,7 +337,8 @@ int vjsd_loss_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, do
     go.mask = c.mask;
     if (c.red == VJSD_REDUCE_MEAN) {
         double *cnt = count_of(part, S, N);
-        if ((e = hip_status(vjsd::launch_reduce_rows(nullptr, c.mask, N, false, nullptr, cnt, st))))
+        if ((e = hip_status(
+                 vjsd::launch_reduce_rows(nullptr, row_opts(c), N, false, nullptr, cnt, st))))
             return e;
         go.count = cnt;
     }
@@ -473,6 +475,69 @@ int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t
     vjsd::LpWeights w;
     w.grad = grad;
     return lp_backward(shards, S, N, dtype, vocab_global, stats, ids, K, ignore_index, w, part, st);
+}
+
+int vce_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+            const int64_t *labels, int64_t ignore_index, int reduction, float *part,
+            double *stats, float *rows, float *out, int32_t *dev_err, void *stream) {
+    int e = check_logprobs(shards, S, N, dtype, vocab_global, labels, 1);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, false))) return e;
+    if (reduction < VJSD_REDUCE_NONE || reduction > VJSD_REDUCE_MEAN) return VJSD_ERR_ARG;
+    if (reduction != VJSD_REDUCE_NONE && !out) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (N == 0) {
+        if (reduction != VJSD_REDUCE_NONE)
+            return hip_status(
+                vjsd::launch_reduce_rows(nullptr, vjsd::RowOpts(), 0, false, out, nullptr, st));
+        return VJSD_OK;
+    }
+    if (!part || !stats || !rows || !dev_err) return VJSD_ERR_ARG;
+    vjsd::RowOpts sel;  // rows whose label is ignore_index are never read
+    sel.labels = labels;
+    sel.ignore = ignore_index;
+    for (int k = 0; k < S; ++k) {
+        Shard sh = convert(shards[k], false, false);
+        if ((e = hip_status(vjsd::launch_stats(dtype, 1, sh, N, part_of(part, k, N), st, sel))))
+            return e;
+    }
+    if ((e = hip_status(vjsd::launch_merge(part_of(part, 0, N), S, N, 1, stats, st)))) return e;
+    for (int k0 = 0; k0 < S; k0 += vjsd::LP_TABLE) {
+        vjsd::LpTable tab = lp_table(shards, S, k0);
+        if ((e = hip_status(vjsd::launch_lp_gather(dtype, tab, k0 == 0, N, vocab_global, labels, 1,
+                                                   ignore_index, stats, rows, dev_err, st,
+                                                   -1.0f))))
+            return e;
+    }
+    if (reduction == VJSD_REDUCE_NONE) return VJSD_OK;
+    return hip_status(vjsd::launch_reduce_rows(rows, sel, N, reduction == VJSD_REDUCE_MEAN, out,
+                                               nullptr, st));
+}
+
+int vce_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
+            const double *stats, const int64_t *labels, int64_t ignore_index, int reduction,
+            const float *grad, float *part, void *stream) {
+    int e = check_logprobs(shards, S, N, dtype, vocab_global, labels, 1);
+    if (e) return e;
+    if ((e = check_views(shards, S, N, dtype, false, true))) return e;
+    if (reduction < VJSD_REDUCE_NONE || reduction > VJSD_REDUCE_MEAN) return VJSD_ERR_ARG;
+    if (N == 0) return VJSD_OK;
+    if (!stats || !part || !grad) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    vjsd::LpWeights w;
+    w.grow = grad;
+    w.scalar = reduction != VJSD_REDUCE_NONE;
+    if (reduction == VJSD_REDUCE_MEAN) {
+        vjsd::RowOpts sel;
+        sel.labels = labels;
+        sel.ignore = ignore_index;
+        double *cnt = count_of(part, S, N);
+        if ((e = hip_status(vjsd::launch_reduce_rows(nullptr, sel, N, false, nullptr, cnt, st))))
+            return e;
+        w.count = cnt;
+    }
+    return lp_backward(shards, S, N, dtype, vocab_global, stats, labels, 1, ignore_index, w, part,
+                       st);
 }
 
 int vtopk_kl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,

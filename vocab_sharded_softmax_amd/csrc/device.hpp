@@ -239,13 +239,16 @@ __device__ __forceinline__ double lnz_from_z(float m, double Z, float ks = L2E) 
 // Per-call options of the distillation-loss form of the forward passes (kernel
 // argument, by value): the exponent scale, the loss multiplier and the row mask.
 struct RowOpts {
-    float ks = L2E;                 // log2 e / temperature
-    float lscale = 1.0f;            // T^2 when the loss is temperature-scaled, else 1
-    const uint8_t *mask = nullptr;  // [N]; a zero entry drops the row; null keeps all
+    float ks = L2E;                   // log2 e / temperature
+    float lscale = 1.0f;              // T^2 when the loss is temperature-scaled, else 1
+    const uint8_t *mask = nullptr;    // [N]; a zero entry drops the row; null keeps all
+    const int64_t *labels = nullptr;  // [N]; a label equal to `ignore` drops the row
+    int64_t ignore = 0;
 };
 // A dropped row is never read: its outputs are zeros.
 __device__ __forceinline__ bool row_dropped(const RowOpts &o, int64_t r) {
-    return o.mask != nullptr && o.mask[r] == 0;
+    return (o.mask != nullptr && o.mask[r] == 0) ||
+           (o.labels != nullptr && o.labels[r] == o.ignore);
 }
 
 // ---- workgroup reductions (fixed order: deterministic results) ----------------------

@@ -74,8 +74,8 @@ hipError_t launch_kl1_merge(int reverse, const float *part, int S, int64_t N, do
                             float *kl, float *loss, hipStream_t st, const RowOpts &o = RowOpts());
 
 // fixed-order masked reduction of per-row losses: out[0] = sum (mean: sum / max(count,
-// 1)) over the kept rows; *count = kept rows (rows may be null to count only)
-hipError_t launch_reduce_rows(const float *rows, const uint8_t *mask, int64_t N, bool mean,
+// 1)) over the rows `sel` keeps; *count = kept rows (rows may be null to count only)
+hipError_t launch_reduce_rows(const float *rows, const RowOpts &sel, int64_t N, bool mean,
                               float *out, double *count, hipStream_t st);
 // single-pass entropy forward and its backward
 hipError_t launch_ent1(int dtype, const Shard &sh, int64_t N, float *part_k, hipStream_t st);
@@ -93,21 +93,34 @@ struct LpTable {
     int64_t start[LP_TABLE], width[LP_TABLE];
     RowView x[LP_TABLE];
 };
+// out = sign * lp (sign -1: cross-entropy); ignored ids give exactly 0
 hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N,
                             int64_t vocab_global, const int64_t *ids, int K, int64_t ignore,
-                            const double *stats, float *out, int32_t *dev_err, hipStream_t st);
+                            const double *stats, float *out, int32_t *dev_err, hipStream_t st,
+                            float sign = 1.0f);
 // Upstream gradient of each (row, slot) of the log-probability backward: grad[r*K+k]
 // for log-probabilities; -grow[r] * exp(tlogp[r*K+k]) (0 where tlogp is -inf) for the
 // teacher top-k forward KL, whose value depends on lp_s(id_k) through that weight.
+// For cross-entropy (rows = -lp(label)): -g_r, g_r = grow[r] or grow[0] (scalar),
+// divided by max(*count, 1) for a mean.
 struct LpWeights {
     const float *grad = nullptr;
     const float *tlogp = nullptr;
     const float *grow = nullptr;
+    bool scalar = false;
+    const double *count = nullptr;
 };
 __device__ __forceinline__ float lp_weight(const LpWeights &w, int64_t r, int K, int k) {
-    if (w.tlogp == nullptr) return w.grad[r * K + k];
-    const float t = w.tlogp[r * K + k];
-    return t > -__builtin_huge_valf() ? -w.grow[r] * expf(t) : 0.0f;
+    if (w.tlogp != nullptr) {
+        const float t = w.tlogp[r * K + k];
+        return t > -__builtin_huge_valf() ? -w.grow[r] * expf(t) : 0.0f;
+    }
+    if (w.grow != nullptr) {
+        double g = w.scalar ? (double)w.grow[0] : (double)w.grow[r];
+        if (w.count) g /= fmax(*w.count, 1.0);
+        return (float)-g;
+    }
+    return w.grad[r * K + k];
 }
 
 hipError_t launch_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *stats,

@@ -21,17 +21,17 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 // out[0] = sum over kept rows (mean: / kept rows, 0 when none); *count = kept rows.
+// A row is kept unless the selector drops it (token mask, or ignored label).
 // rows may be null (count only); out and count may each be null.
 __global__ __launch_bounds__(RED_BLOCK) void k_reduce_rows(const float *__restrict__ rows,
-                                                           const uint8_t *__restrict__ mask,
-                                                           int64_t N, int mean,
+                                                           RowOpts sel, int64_t N, int mean,
                                                            float *__restrict__ out,
                                                            double *__restrict__ count) {
     constexpr int NW = RED_BLOCK / 64;
     __shared__ double red[2 * NW];
     double sum = 0.0, cnt = 0.0;
     for (int64_t r = threadIdx.x; r < N; r += RED_BLOCK) {
-        if (mask == nullptr || mask[r] != 0) {
+        if (!row_dropped(sel, r)) {
             cnt += 1.0;
             if (rows) sum += (double)rows[r];
         }
@@ -57,9 +57,9 @@ __global__ __launch_bounds__(RED_BLOCK) void k_reduce_rows(const float *__restri
 
 }  // namespace
 
-hipError_t launch_reduce_rows(const float *rows, const uint8_t *mask, int64_t N, bool mean,
+hipError_t launch_reduce_rows(const float *rows, const RowOpts &sel, int64_t N, bool mean,
                               float *out, double *count, hipStream_t st) {
-    hipLaunchKernelGGL(k_reduce_rows, dim3(1), dim3(RED_BLOCK), 0, st, rows, mask, N,
+    hipLaunchKernelGGL(k_reduce_rows, dim3(1), dim3(RED_BLOCK), 0, st, rows, sel, N,
                        mean ? 1 : 0, out, count);
     return hipGetLastError();
 }

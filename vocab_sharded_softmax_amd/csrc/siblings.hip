@@ -384,7 +384,7 @@ template <class D>
 __global__ void k_lp_gather(LpTable tab, int first, int64_t N, int64_t vocab_global,
                             const int64_t *__restrict__ ids, int K, int64_t ignore,
                             const double *__restrict__ stats, float *__restrict__ out,
-                            int32_t *__restrict__ dev_err) {
+                            int32_t *__restrict__ dev_err, float sign) {
     using T = typename D::T;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= N * K) return;
@@ -408,7 +408,7 @@ __global__ void k_lp_gather(LpTable tab, int first, int64_t N, int64_t vocab_glo
                 out[i] = __builtin_nanf("");
             } else {
                 const double x = load1<D>(row_ptr<T>(tab.x[q], r) + (id - tab.start[q]));
-                out[i] = (float)((x - m) - lz);
+                out[i] = (float)((double)sign * ((x - m) - lz));
             }
             return;
         }
@@ -493,13 +493,17 @@ __global__ void k_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *__r
     if (r >= N) return;
     const float m = (float)stats[r * 4];
     float *o = rowc + r * ROWC;
-    o[ROWC_UNDEFINED] = m == NINF ? 1.0f : 0.0f;
-    if (m == NINF) return;
     double G = 0.0;
+    bool any = false;  // a row with no valid slot gets exactly 0 without being read
     for (int k = 0; k < K; ++k) {
         const int64_t id = ids[r * K + k];
-        if (id != ignore && id >= 0 && id < vocab_global) G += lp_weight(wts, r, K, k);
+        if (id != ignore && id >= 0 && id < vocab_global) {
+            G += lp_weight(wts, r, K, k);
+            any = true;
+        }
     }
+    o[ROWC_UNDEFINED] = (m == NINF || !any) ? 1.0f : 0.0f;
+    if (m == NINF || !any) return;
     const double Z = z_from_stats(m, stats[r * 4 + 1]);
     o[0] = refc(m);
     o[1] = (float)(-G / Z);
@@ -612,14 +616,15 @@ hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const float *ro
 
 hipError_t launch_lp_gather(int dtype, const LpTable &tab, bool first, int64_t N,
                             int64_t vocab_global, const int64_t *ids, int K, int64_t ignore,
-                            const double *stats, float *out, int32_t *dev_err, hipStream_t st) {
+                            const double *stats, float *out, int32_t *dev_err, hipStream_t st,
+                            float sign) {
     const int64_t n = N * K;
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     const int f = first ? 1 : 0;
     switch (dtype) {
-        case 0: hipLaunchKernelGGL(k_lp_gather<F32>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err); break;
-        case 1: hipLaunchKernelGGL(k_lp_gather<F16>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err); break;
-        default: hipLaunchKernelGGL(k_lp_gather<BF16>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err);
+        case 0: hipLaunchKernelGGL(k_lp_gather<F32>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err, sign); break;
+        case 1: hipLaunchKernelGGL(k_lp_gather<F16>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err, sign); break;
+        default: hipLaunchKernelGGL(k_lp_gather<BF16>, grid, block, 0, st, tab, f, N, vocab_global, ids, K, ignore, stats, out, dev_err, sign);
     }
     return hipGetLastError();
 }

@@ -21,7 +21,7 @@ from torch.autograd.function import once_differentiable
 from . import _abi
 from ._abi import ShardSet
 
-__all__ = ["jsd", "jsd_loss", "kl_div", "entropy", "logprobs", "topk_kl"]
+__all__ = ["jsd", "jsd_loss", "kl_div", "entropy", "logprobs", "topk_kl", "cross_entropy"]
 
 
 def _unpack(n_shards: int, tensors):
@@ -255,6 +255,40 @@ class _TopkKL(torch.autograd.Function):
         return (None, None, None, None, None, *_flat(gx))
 
 
+class _CrossEntropy(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, labels, ignore_index, reduction, split, n_shards, *tensors):
+        x = _unpack(n_shards, tensors)
+        sh = ShardSet(x, widths=split)
+        dev = (x[0] if n_shards else x).device
+        N, S = sh.N, sh.S
+        lab = labels.reshape(N).to(torch.int64).contiguous()
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        rows = torch.empty((N,), dtype=torch.float32, device=dev)
+        out = torch.empty((1,), dtype=torch.float32, device=dev) if reduction != "none" else None
+        err = torch.zeros((1,), dtype=torch.int32, device=dev)
+        _abi.vce_fwd(sh, sh.V, lab, ignore_index, reduction, part, stats, rows, out, err)
+        if N and int(err.item()):
+            raise ValueError("cross_entropy: a label is outside [0, V) and is not ignore_index")
+        ctx.args = (ignore_index, reduction, split, n_shards, sh.V)
+        ctx.save_for_backward(stats, lab, *tensors)
+        return rows.view(sh.lead_shape) if out is None else out.view(())
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gout):
+        ignore_index, reduction, split, n, V = ctx.args
+        stats, lab, *tensors = ctx.saved_tensors
+        x = _unpack(n, tensors)
+        gx = _grads_like(x, bool(n))
+        sh = ShardSet(x, widths=split, gs=gx)
+        g = gout.reshape(-1).to(torch.float32).contiguous()
+        _abi.vce_bwd(sh, V, stats, lab, ignore_index, reduction, g,
+                     _abi.new_part(sh.N, sh.S, stats.device))
+        return (None, None, None, None, None, *_flat(gx))
+
+
 def _as_args(x):
     if isinstance(x, (list, tuple)):
         return len(x), list(x)
@@ -350,6 +384,23 @@ def topk_kl(student, teacher_topk_ids, teacher_topk_logp, *, ignore_index: int =
         raise ValueError("the top-k tensors must be shaped [..., K] like the logits' leading dims")
     return _TopkKL.apply(teacher_topk_ids, teacher_topk_logp, int(ignore_index),
                          None if split is None else tuple(split), n, *x)
+
+
+def cross_entropy(logits, labels, *, ignore_index: int = -100, reduction: str = "mean",
+                  split=None) -> torch.Tensor:
+    """Cross-entropy of integer ``labels`` (shaped like the leading dimensions, global
+    ids) over the sharded vocabulary, as ``torch.nn.functional.cross_entropy`` with
+    ``ignore_index`` and reduction "none" / "sum" / "mean" (a mean over no labelled
+    token is 0).  Rows whose label is ignored are never read (DeepSpeed PR #8309,
+    "[AutoTP] vocab-parallel LM head": vocab_parallel_cross_entropy).  A label outside
+    the vocabulary raises ValueError after a host synchronisation."""
+    if reduction not in _abi.REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(_abi.REDUCTIONS)}")
+    n, x = _as_args(logits)
+    if tuple(labels.shape) != tuple(x[0].shape[:-1]):
+        raise ValueError("labels must be shaped like the logits' leading dimensions")
+    return _CrossEntropy.apply(labels, int(ignore_index), reduction,
+                               None if split is None else tuple(split), n, *x)
 
 
 def logprobs(logits, index, *, ignore_index: int = -100, split=None) -> torch.Tensor:
