@@ -240,24 +240,9 @@ int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double
 
 int vjsd_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta, float *part,
                  double *stats, float *kl, float *loss, void *stream) {
-    int e = check_common(shards, S, N, dtype);
-    if (e) return e;
-    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
-    if ((e = check_views(shards, S, N, dtype, true, false))) return e;
-    if (N == 0) return VJSD_OK;
-    if (!part || !stats || !kl || !loss) return VJSD_ERR_ARG;
-    const int mode = mode_of(beta);
-    // the endpoints are plain KL divergences: one input pass
-    if (mode != vjsd::INTERIOR)
-        return vkl_fwd(shards, S, N, dtype, mode == vjsd::REV_KL, part, stats, kl, loss, stream);
-    if (S == 1) {
-        Shard sh = convert(shards[0], true, false);
-        return hip_status(vjsd::launch_fwd_fused(dtype, sh, N, beta, stats, kl, loss,
-                                                 (hipStream_t)stream));
-    }
-    if ((e = vjsd_stats(shards, S, N, dtype, 3, part, stream))) return e;
-    if ((e = vjsd_merge(part, S, N, 3, stats, stream))) return e;
-    return vjsd_fwd(shards, S, N, dtype, stats, beta, part, kl, loss, stream);
+    // the loss form without options: T = 1, no T^2, no mask, per-token losses
+    return vjsd_loss_forward(shards, S, N, dtype, beta, nullptr, part, stats, kl, loss, nullptr,
+                             stream);
 }
 
 int vjsd_loss_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,

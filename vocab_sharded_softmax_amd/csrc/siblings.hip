@@ -529,19 +529,23 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, 
         return;
     }
     const T *x = row_ptr<T>(xv, r) + c0;
+    // the first GRAD_BLOCK ids are loaded before the sweep, so their latency overlaps
+    // the chunk's loads instead of trailing them
+    const int64_t *id = ids + r * K;
+    const int64_t id0 = (int)threadIdx.x < K ? id[threadIdx.x] : ignore;
     OpLpBwd<D> op;
     op.gx = gx;
     op.c = k[0];
     op.C = k[1];
     sweep<D, 1, false, GRAD_BLOCK, true>(x, x, n, head_len<T>(n, x, gx), op);
     __syncthreads();  // this chunk's streamed values land before the id fix-ups
-    const int64_t *id = ids + r * K;
     for (int q = threadIdx.x; q < K; q += GRAD_BLOCK) {
-        const int64_t j = id[q] - start - c0;
-        if (id[q] == ignore || j < 0 || j >= n) continue;
+        const int64_t idq = q < GRAD_BLOCK ? id0 : id[q];
+        const int64_t j = idq - start - c0;
+        if (idq == ignore || j < 0 || j >= n) continue;
         float gsum = 0.0f;
         for (int q2 = 0; q2 < K; ++q2)
-            if (id[q2] == id[q]) gsum += lp_weight(wts, r, K, q2);
+            if (id[q2] == idq) gsum += lp_weight(wts, r, K, q2);
         const float p = ex2(fmaxf(fmaf(load1<D>(x + j), L2E, -op.c), U_FLOOR)) * k[2];
         store1<D>(gx + j, gsum - k[3] * p);
     }
