@@ -251,17 +251,86 @@ __device__ __forceinline__ bool row_dropped(const RowOpts &o, int64_t r) {
            (o.labels != nullptr && o.labels[r] == o.ignore);
 }
 
-// ---- workgroup reductions (fixed order: deterministic results) ----------------------
+// ---- wave reductions (fixed order: deterministic results) ---------------------------
+//
+// A butterfly over the 64 lanes of a wave that never touches LDS.  The first four
+// steps read the partner lane through a DPP modifier of the combining instruction:
+// quad permutations [1,0,3,2] and [2,3,0,1] for lane bits 0 and 1, the half-row mirror
+// (lane j of an 8-lane group reads lane 7 - j) for bit 2, and the rotation of each
+// 16-lane row by 8 for bit 3.  The last two steps use gfx950's v_permlane16_swap and
+// v_permlane32_swap with both operands equal, which leave in every lane the value of
+// the lower and of the upper row (half) of the pair it belongs to.  After the step
+// across bit k every aligned group of 2^(k+1) lanes holds the same value, which is
+// what makes the mirror a valid bit-2 partner.  ORDERED combines pass the lower lane's
+// operand first, so every lane computes the bit-identical result; unordered ones
+// (commutative combines: sum, max) let the DPP read fold into the combining
+// instruction.  All 64 lanes must be active.
+
+template <class T>
+struct Words {
+    static_assert(sizeof(T) % 4 == 0, "wave reductions move 32-bit words");
+    uint32_t w[sizeof(T) / 4];
+};
+
+// v read from the DPP partner given by CTRL (row and bank masks full).
+template <int CTRL, class T>
+__device__ __forceinline__ T dpp_read(const T &v) {
+    Words<T> a = __builtin_bit_cast(Words<T>, v);
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i)
+        a.w[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a.w[i], CTRL, 0xF, 0xF, true);
+    return __builtin_bit_cast(T, a);
+}
+
+template <int BIT, int CTRL, bool ORDERED, class T, class F>
+__device__ __forceinline__ T bfly_dpp(const T &v, F &&f) {
+    const T p = dpp_read<CTRL>(v);
+    if constexpr (!ORDERED) {
+        return f(v, p);
+    } else {
+        const bool upper = (threadIdx.x & BIT) != 0;
+        return upper ? f(p, v) : f(v, p);
+    }
+}
+
+// Step across lane bit 4 (ROW32 false) or 5 (true): f(lower value, upper value).
+template <bool ROW32, class T, class F>
+__device__ __forceinline__ T bfly_swap(const T &v, F &&f) {
+    const Words<T> a = __builtin_bit_cast(Words<T>, v);
+    Words<T> lo, hi;
+#pragma unroll
+    for (unsigned i = 0; i < sizeof(T) / 4; ++i) {
+        uint32_t r0, r1;
+        if constexpr (ROW32) {
+            const auto r = __builtin_amdgcn_permlane32_swap(a.w[i], a.w[i], false, false);
+            r0 = r[0];  // through scalars: a bit-cast vector element reads element 0
+            r1 = r[1];
+        } else {
+            const auto r = __builtin_amdgcn_permlane16_swap(a.w[i], a.w[i], false, false);
+            r0 = r[0];
+            r1 = r[1];
+        }
+        lo.w[i] = r0;
+        hi.w[i] = r1;
+    }
+    return f(__builtin_bit_cast(T, lo), __builtin_bit_cast(T, hi));
+}
+
+template <bool ORDERED, class T, class F>
+__device__ __forceinline__ T wave_reduce(T v, F &&f) {
+    v = bfly_dpp<1, 0xB1, ORDERED>(v, f);   // quad_perm [1,0,3,2]
+    v = bfly_dpp<2, 0x4E, ORDERED>(v, f);   // quad_perm [2,3,0,1]
+    v = bfly_dpp<4, 0x141, ORDERED>(v, f);  // row_half_mirror
+    v = bfly_dpp<8, 0x128, ORDERED>(v, f);  // row_ror:8
+    v = bfly_swap<false>(v, f);
+    return bfly_swap<true>(v, f);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce<false>(v, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return wave_reduce<false>(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // Online (max, sum of 2^(x*ks - refc(max))) pair.
@@ -276,14 +345,10 @@ __device__ __forceinline__ MZ mz_combine(MZ a, MZ b, float ks = L2E) {
     return {m, za + zb};
 }
 __device__ __forceinline__ MZ wave_mz(MZ v, float ks = L2E) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        MZ w{__shfl_xor(v.m, o), __shfl_xor(v.z, o)};
-        // combine in lane order so that both partners compute the same value
-        v = (threadIdx.x & o) ? mz_combine(w, v, ks) : mz_combine(v, w, ks);
-    }
-    return v;
+    return wave_reduce<true>(v, [ks](MZ a, MZ b) { return mz_combine(a, b, ks); });
 }
+
+// ---- workgroup reductions: waves as above, then the wave results in wave order ------
 
 // Sum of NV floats over a BLK-lane workgroup; result valid in thread 0.  `red` is LDS
 // of NV * (BLK / 64) floats.

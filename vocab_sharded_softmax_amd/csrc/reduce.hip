@@ -15,9 +15,7 @@ namespace {
 constexpr int RED_BLOCK = 1024;
 
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce<false>(v, [](double a, double b) { return a + b; });
 }
 
 // out[0] = sum over kept rows (mean: / kept rows, 0 when none); *count = kept rows.

@@ -115,12 +115,8 @@ __global__ __launch_bounds__(BLOCK) void k_kl1(RowView sv, RowView tv, int64_t w
         sweep<D, 4, true, BLOCK, true>(a, b, w, head_len<T>(w, a, b), op);
         p = {op.ma, op.za, op.mb, op.zb, op.A, op.F};
         // wave reduction in lane order, then waves in order
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            KLPart q{__shfl_xor(p.ma, o), __shfl_xor(p.za, o), __shfl_xor(p.mb, o),
-                     __shfl_xor(p.zb, o), __shfl_xor(p.A, o),  __shfl_xor(p.F, o)};
-            p = (threadIdx.x & o) ? kl_combine(q, p, ro.ks) : kl_combine(p, q, ro.ks);
-        }
+        const float ks = ro.ks;
+        p = wave_reduce<true>(p, [ks](const KLPart &x, const KLPart &y) { return kl_combine(x, y, ks); });
         const int wave = threadIdx.x >> 6;
         if ((threadIdx.x & 63) == 0) {
             float *d = red + 6 * wave;
@@ -258,11 +254,7 @@ __global__ __launch_bounds__(BLOCK) void k_ent1(RowView xv, int64_t w, float *__
         OpEnt1 op;
         sweep<D, 4, false, BLOCK, true>(x, x, w, head_len<T>(w, x), op);
         p = {op.m, op.z, op.B};
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            EntPart q{__shfl_xor(p.m, o), __shfl_xor(p.z, o), __shfl_xor(p.B, o)};
-            p = (threadIdx.x & o) ? ent_combine(q, p) : ent_combine(p, q);
-        }
+        p = wave_reduce<true>(p, [](const EntPart &x, const EntPart &y) { return ent_combine(x, y); });
         const int wave = threadIdx.x >> 6;
         if ((threadIdx.x & 63) == 0) {
             red[3 * wave] = p.m;
