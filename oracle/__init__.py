@@ -277,3 +277,39 @@ def logprobs(x, ids, ignore_index=-100, widths=None, rows=None, gout=None, grads
     if err.value:
         raise ValueError("logprobs: an id is outside [0, V) and is not ignore_index")
     return dict(out=out, gx=gx)
+
+
+def linear_jsd(hs, ws, ht, wt, beta, temperature=1.0, scale_t2=False, mask=None,
+               reduction="mean", grad=1.0, grads=True):
+    """The distillation loss of ``jsd_loss`` on LM-head projections, in fp64.
+
+    [JSD-PR, Motivation] names a route that evaluates the divergence from tiled
+    LM-head projections without materialising the full logits, and [JSD-PR, Scope and
+    limitations] / [OPS-PR, Limitations] leave such a fused-linear variant as future
+    work: the logits of a row are the products of its hidden state with every row of
+    the head weight.  Here, on the exact stored values:
+        logits_s = hs @ ws^T   ([N, Ds] x [V, Ds] -> [N, V]),  logits_t = ht @ wt^T
+        result   = jsd_loss(logits_s, logits_t, beta, temperature, scale_t2, mask,
+                            reduction, grad)
+    The teacher is a constant (no gradients).  With G = d(result)/d(logits_s) from
+    ``jsd_loss``, the chain rule through the product gives
+        gh = G @ ws   ([N, Ds], gradient of the student hidden states)
+        gw = G^T @ hs ([V, Ds], gradient of the student head weight)
+    Returns dict(out, rows, gh, gw) (``out`` None for reduction "none").
+    """
+    Hs, Ws = hs.double(), ws.double()
+    Ht, Wt = ht.double(), wt.double()
+    if Hs.shape[1] != Ws.shape[1] or Ht.shape[1] != Wt.shape[1]:
+        raise ValueError("hidden and head widths differ")
+    if Hs.shape[0] != Ht.shape[0] or Ws.shape[0] != Wt.shape[0]:
+        raise ValueError("student and teacher disagree on tokens or vocabulary")
+    ls = (Hs @ Ws.T).contiguous()
+    lt = (Ht @ Wt.T).contiguous()
+    ref = jsd_loss(ls, lt, beta, temperature=temperature, scale_t2=scale_t2, mask=mask,
+                   reduction=reduction, grad=grad, grads=grads)
+    res = dict(out=ref["out"], rows=ref["rows"], gh=None, gw=None)
+    if grads:
+        G = torch.from_numpy(ref["gs"])
+        res["gh"] = (G @ Ws).numpy()
+        res["gw"] = (G.T @ Hs).numpy()
+    return res
