@@ -363,6 +363,79 @@ VJSD_API int vtopk_kl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype,
  */
 VJSD_API int vjsd_membw_probe(const void *src, void *dst, size_t bytes, int op, void *stream);
 
+/* ---- fused linear + JSD ------------------------------------------------------------- */
+
+/*
+ * Matrix operand of vlin_gemm: element (row, k) at p[row*ld + k] when kmajor, else at
+ * p[k*ld + row].  dtype VJSD_BF16, or VJSD_F32 for the first operand only (each
+ * value rounded to bf16, nearest even, before its product).  p must be 16-byte
+ * aligned and ld a multiple of 8 elements (4 for VJSD_F32), at least the extent of
+ * the contiguous index.
+ */
+typedef struct {
+    const void *p;
+    int64_t ld;
+    int dtype;
+    int kmajor;
+} vlin_operand;
+
+enum { VLIN_OUT_F32 = 0, VLIN_OUT_F32_ACC = 1, VLIN_OUT_BF16 = 2 };
+
+/*
+ * The matrix-core product the fused-linear loss is built from ([JSD-PR, Motivation]:
+ * the divergence evaluated from tiled LM-head projections; [JSD-PR, Scope and
+ * limitations] / [OPS-PR, Limitations]: a fused-linear variant is future work):
+ *     C[i][j] = sum_k A(i, k) * B(j, k),   i < M, j < N, k < K
+ * bf16 products accumulated in fp32 (v_mfma_f32_32x32x16_bf16).  out selects fp32
+ * C (VLIN_OUT_F32), fp32 C += product (VLIN_OUT_F32_ACC) or bf16 C rounded to
+ * nearest even (VLIN_OUT_BF16); C row-major with row stride ldc >= N, element
+ * aligned, not overlapping A or B.  K == 0 gives C = 0 (or leaves C unchanged when
+ * accumulating).  VJSD_ERR_ARG for negative sizes, a NULL, misaligned or too-short
+ * operand, or a bad out; VJSD_ERR_DTYPE for another operand dtype.
+ */
+VJSD_API int vlin_gemm(int64_t M, int64_t N, int64_t K, vlin_operand a, vlin_operand b, void *c,
+                       int64_t ldc, int out, void *stream);
+
+/*
+ * One side of the fused-linear loss: hidden states h [N][dim] (row stride ldh) and
+ * LM-head weight w [V][dim] (row stride ldw), both bf16, 16-byte aligned, strides
+ * multiples of 8 elements.  The side's logits are h w^T [N][V].
+ */
+typedef struct {
+    const void *h;
+    int64_t ldh;
+    const void *w;
+    int64_t ldw;
+    int64_t dim;
+} vlin_head;
+
+/*
+ * Fused-linear distillation loss: the loss of vjsd_loss_forward on the logits
+ * h_s w_s^T (student) and h_t w_t^T (teacher), computed `chunk` tokens at a time, so
+ * that only chunk-row blocks of logits ever exist (in the workspace, fp32).  opts as
+ * vjsd_loss_opts (temperature, T^2, token mask, reduction).  out is float[N] for
+ * VJSD_REDUCE_NONE, else out[0] is the sum or the mean over the kept tokens.
+ * grad_h (bf16 [N][dim_s], row stride ldgh) and grad_w (bf16 [V][dim_s], row stride
+ * ldgw), each optional (NULL), receive d out[0] / d h_s and d out[0] / d w_s; they
+ * need a reduction (VJSD_ERR_ARG otherwise).  The teacher is a constant.  Gradients
+ * come from the bf16-rounded logit gradient (the operand precision of the products).
+ * Masked tokens get exactly zero rows of grad_h.  workspace: device memory of
+ * vljsd_workspace_bytes(N, V, dim_s, chunk) bytes, 256-byte aligned.  VJSD_ERR_ARG
+ * for a bad size, chunk, pointer, alignment or stride; VJSD_ERR_BETA as vjsd_fwd.
+ */
+VJSD_API size_t vljsd_workspace_bytes(int64_t N, int64_t V, int64_t dim_s, int64_t chunk);
+VJSD_API int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t V,
+                   double beta, const vjsd_loss_opts *opts, int64_t chunk, void *workspace,
+                   float *out, void *grad_h, int64_t ldgh, void *grad_w, int64_t ldgw,
+                   void *stream);
+
+/*
+ * Scales n values in place by a device scalar: p[i] *= g[0] (the upstream gradient
+ * of a reduced loss applied to gradients computed for a unit upstream gradient).
+ * dtype VJSD_F32 or VJSD_BF16 (nearest even); p 16-byte aligned.
+ */
+VJSD_API int vlin_scale(void *p, int64_t n, int dtype, const float *g, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -280,7 +280,7 @@ def logprobs(x, ids, ignore_index=-100, widths=None, rows=None, gout=None, grads
 
 
 def linear_jsd(hs, ws, ht, wt, beta, temperature=1.0, scale_t2=False, mask=None,
-               reduction="mean", grad=1.0, grads=True):
+               reduction="mean", grad=1.0, grads=True, head_grad=True):
     """The distillation loss of ``jsd_loss`` on LM-head projections, in fp64.
 
     [JSD-PR, Motivation] names a route that evaluates the divergence from tiled
@@ -295,7 +295,8 @@ def linear_jsd(hs, ws, ht, wt, beta, temperature=1.0, scale_t2=False, mask=None,
     ``jsd_loss``, the chain rule through the product gives
         gh = G @ ws   ([N, Ds], gradient of the student hidden states)
         gw = G^T @ hs ([V, Ds], gradient of the student head weight)
-    Returns dict(out, rows, gh, gw) (``out`` None for reduction "none").
+    Returns dict(out, rows, G, gh, gw) (``out`` None for reduction "none"); with
+    ``head_grad`` False the [V, Ds] head gradient is not formed (gw None).
     """
     Hs, Ws = hs.double(), ws.double()
     Ht, Wt = ht.double(), wt.double()
@@ -307,9 +308,11 @@ def linear_jsd(hs, ws, ht, wt, beta, temperature=1.0, scale_t2=False, mask=None,
     lt = (Ht @ Wt.T).contiguous()
     ref = jsd_loss(ls, lt, beta, temperature=temperature, scale_t2=scale_t2, mask=mask,
                    reduction=reduction, grad=grad, grads=grads)
-    res = dict(out=ref["out"], rows=ref["rows"], gh=None, gw=None)
+    res = dict(out=ref["out"], rows=ref["rows"], G=None, gh=None, gw=None)
     if grads:
+        res["G"] = ref["gs"]
         G = torch.from_numpy(ref["gs"])
         res["gh"] = (G @ Ws).numpy()
-        res["gw"] = (G.T @ Hs).numpy()
+        if head_grad:
+            res["gw"] = (G.T @ Hs).numpy()
     return res

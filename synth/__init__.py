@@ -25,6 +25,15 @@ logprobs, entropy and KL ops", section Memory, T = 8192 and V_local = 16032):
               drawn uniformly without replacement, 10% of all ids set to
               ignore_index (-100)
 
+  linear      N=8192, V=151936, Ds=Dt=3584 (a Qwen2.5-7B-sized hidden width), bf16:
+              hidden states and LM-head weights for the fused-linear loss (the
+              logits h W^T are never drawn).  Student hidden x ~ N(0, 1) with
+              feature 0 fixed at 1; head W_s ~ N(0, (3/sqrt(Ds))^2) with column 0
+              the Zipf bias b above, so the student logits are about N(0, 3^2) + b
+              as in full_vocab.  Teacher hidden y = 0.7 x + N(0, 0.71^2) (feature 0
+              again 1), head W_t = 0.7 W_s + N(0, (2/sqrt(Dt))^2) (column 0 = b);
+              with Dt != Ds the shared part uses the first min(Ds, Dt) features.
+
 Upstream per-token gradients are U(0.5, 1.5).  Any workload can be drawn at a
 reduced (N, V) with the same recipe for tests the oracle must finish quickly.
 """
@@ -154,6 +163,45 @@ def draw(name: str, device="cpu", N: int | None = None, V: int | None = None,
     return batch
 
 
+@dataclass
+class LinearBatch:
+    hs: torch.Tensor  # [N, Ds] student hidden states
+    ws: torch.Tensor  # [V, Ds] student LM-head weight
+    ht: torch.Tensor  # [N, Dt] teacher hidden states
+    wt: torch.Tensor  # [V, Dt] teacher LM-head weight
+    meta: dict = field(default_factory=dict)
+
+
+LINEAR = dict(N=8192, V=151936, Ds=3584, Dt=3584, seed=1005)
+
+
+def draw_linear(device="cpu", N: int | None = None, V: int | None = None,
+                Ds: int | None = None, Dt: int | None = None, seed: int | None = None,
+                dtype: torch.dtype = torch.bfloat16) -> LinearBatch:
+    """Hidden states and LM-head weights of the fused-linear workload (module doc)."""
+    N = LINEAR["N"] if N is None else N
+    V = LINEAR["V"] if V is None else V
+    Ds = LINEAR["Ds"] if Ds is None else Ds
+    Dt = LINEAR["Dt"] if Dt is None else Dt
+    gen = torch.Generator(device=device)
+    gen.manual_seed(LINEAR["seed"] if seed is None else seed)
+    b = zipf_bias(V, device)
+    x = _normal(gen, (N, Ds), 1.0, device)
+    x[:, 0] = 1.0
+    ws = _normal(gen, (V, Ds), 3.0 / Ds ** 0.5, device)
+    ws[:, 0] = b
+    d = min(Ds, Dt)
+    y = _normal(gen, (N, Dt), 0.71, device)
+    y[:, :d] += 0.7 * x[:, :d]
+    y[:, 0] = 1.0
+    wt = _normal(gen, (V, Dt), 2.0 / Dt ** 0.5, device)
+    wt[:, :d] += 0.7 * ws[:, :d]
+    wt[:, 0] = b
+    return LinearBatch(hs=x.to(dtype), ws=ws.to(dtype), ht=y.to(dtype), wt=wt.to(dtype),
+                       meta=dict(name="linear", N=N, V=V, Ds=Ds, Dt=Dt,
+                                 dtype=str(dtype).replace("torch.", "")))
+
+
 def default_split(V: int, parts: int) -> list[int]:
     """Even split of V columns into ``parts`` shards, remainder to the first shards
     (101 over two shards gives 51/50, as in DeepSpeed PR #8309's resume example)."""
@@ -166,4 +214,4 @@ def bytes_of(N: int, V: int, dtype: torch.dtype) -> int:
 
 
 __all__ = ["WORKLOADS", "Workload", "Batch", "draw", "zipf_bias", "default_split",
-           "bytes_of", "IGNORE_INDEX"]
+           "bytes_of", "IGNORE_INDEX", "LinearBatch", "LINEAR", "draw_linear"]

@@ -28,13 +28,14 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
     out = os.popen(f"nm -D --defined-only {abi.LIB_PATH}").read().split("\n")
     own = {ln.split()[-1] for ln in out if ln.strip() and (" T " in ln)}
-    own = {n for n in own if n.startswith(("vjsd", "vkl", "ventropy", "vlogprobs", "vtopk", "vce"))}
+    own = {n for n in own if n.startswith(("vjsd", "vkl", "ventropy", "vlogprobs", "vtopk", "vce",
+                                            "vlin", "vljsd"))}
     assert own == set(names)
 
 
@@ -235,3 +236,76 @@ def test_default_split_matches_the_pages_uneven_example():
     assert synth.default_split(101, 2) == [51, 50]
     assert synth.default_split(128256, 8) == [16032] * 8
     assert synth.default_split(5, 8) == [1, 1, 1, 1, 1, 0, 0, 0]
+
+
+def test_linear_gemm_validates_before_any_launch():
+    Op = abi.LinOperand
+    a, b = Op(FAKE, 64, 2, 1), Op(FAKE, 64, 2, 1)
+    g = lib.vlin_gemm
+    assert g(0, 5, 64, a, b, FAKE, 5, 0, None) == OK  # no rows: nothing to do
+    assert g(4, 0, 64, a, b, FAKE, 5, 0, None) == OK
+    assert g(-1, 5, 64, a, b, FAKE, 5, 0, None) == ARG
+    assert g(4, 5, -2, a, b, FAKE, 5, 0, None) == ARG
+    assert g(4, 5, 64, a, b, FAKE, 5, 3, None) == ARG  # no such output mode
+    assert g(4, 5, 64, Op(FAKE, 64, 1, 1), b, FAKE, 5, 0, None) == DTYPE  # fp16 operand
+    assert g(4, 5, 64, a, Op(FAKE, 64, 0, 1), FAKE, 5, 0, None) == DTYPE  # fp32 only for A
+    assert g(4, 5, 64, Op(FAKE + 8, 64, 2, 1), b, FAKE, 5, 0, None) == ARG  # not 16-byte aligned
+    assert g(4, 5, 64, Op(FAKE, 68, 2, 1), b, FAKE, 5, 0, None) == ARG  # ld not a multiple of 8
+    assert g(4, 5, 64, Op(FAKE, 56, 2, 1), b, FAKE, 5, 0, None) == ARG  # ld shorter than K
+    assert g(40, 5, 64, Op(FAKE, 32, 2, 0), b, FAKE, 5, 0, None) == ARG  # i-major: ld < M
+    assert g(4, 5, 64, Op(FAKE, 66, 0, 1), b, FAKE, 5, 0, None) == ARG  # fp32: ld % 4
+    assert g(4, 5, 64, Op(FAKE, 64, 2, 2), b, FAKE, 5, 0, None) == ARG  # kmajor is 0 or 1
+    assert g(4, 5, 64, a, b, FAKE, 4, 0, None) == ARG  # ldc < N
+    assert g(4, 5, 64, a, b, None, 5, 0, None) == ARG  # no C
+    assert g(4, 5, 64, a, b, FAKE + 2, 5, 0, None) == ARG  # fp32 C not element aligned
+
+
+def test_linear_jsd_validates_before_any_launch():
+    H = abi.LinHead
+    st, te = H(FAKE, 64, FAKE, 64, 64), H(FAKE, 64, FAKE, 64, 64)
+    f = lib.vljsd
+    opts = abi.LossOpts(1.0, 0, None, 2)
+    none = abi.LossOpts(1.0, 0, None, 0)
+    by = ctypes.byref
+
+    def call(N=16, V=100, beta=0.5, o=opts, chunk=8, ws=FAKE, out=FAKE, gh=None, ldgh=0,
+             gw=None, ldgw=0, s=st, t=te):
+        return f(by(s), by(t), N, V, beta, by(o), chunk, ws, out, gh, ldgh, gw, ldgw, None)
+
+    assert call(N=-1) == ARG
+    assert call(V=0) == ARG
+    assert call(chunk=0) == ARG
+    assert call(out=None) == ARG
+    assert call(beta=1.5) == BETA
+    assert call(beta=float("nan")) == BETA
+    assert call(o=abi.LossOpts(0.0, 0, None, 2)) == ARG  # temperature
+    assert call(s=H(FAKE + 8, 64, FAKE, 64, 64)) == ARG  # hidden not 16-byte aligned
+    assert call(s=H(FAKE, 60, FAKE, 64, 56)) == ARG  # ldh not a multiple of 8
+    assert call(t=H(FAKE, 64, FAKE, 56, 64)) == ARG  # ldw shorter than dim
+    assert call(s=H(FAKE, 64, FAKE, 64, 0)) == ARG  # no width
+    assert call(o=none, gh=FAKE, ldgh=64) == ARG  # gradients need a reduction
+    assert call(gh=FAKE, ldgh=32) == ARG  # grad_h row stride < dim
+    assert call(gw=FAKE + 1, ldgw=64) == ARG  # grad_w not element aligned
+    assert call(ws=None) == ARG
+    assert call(ws=FAKE + 16) == ARG  # workspace 256-byte aligned
+    # no tokens, no reduction, no gradients: nothing to enqueue
+    assert call(N=0, o=none, ws=None, s=H(None, 64, FAKE, 64, 64)) == OK
+
+
+def test_linear_workspace_and_scale():
+    w = lib.vljsd_workspace_bytes
+    assert w(16, 0, 8, 4) == 0 and w(16, 10, 0, 4) == 0 and w(16, 10, 8, 0) == 0
+    al = lambda x: (x + 255) // 256 * 256
+    N, V, D, C = 8192, 151936, 3584, 4096
+    expect = (3 * al(C * V * 4) + al(N * 4) + al(C * 32) + al(C * 8)
+              + al(lib.vjsd_workspace_bytes(C, 1)) + al(8) + al(V * D * 4))
+    assert w(N, V, D, C) == expect
+    # one block: no head-gradient accumulator; logit rows padded to a multiple of 4
+    assert w(100, 1001, 16, 128) == (3 * al(100 * 1004 * 4) + al(400) + al(3200) + al(800)
+                                     + al(lib.vjsd_workspace_bytes(100, 1)) + al(8))
+    s = lib.vlin_scale
+    assert s(FAKE, 10, 1, FAKE, None) == DTYPE
+    assert s(FAKE, 0, 2, FAKE, None) == OK
+    assert s(FAKE, -1, 2, FAKE, None) == ARG
+    assert s(FAKE + 4, 10, 0, FAKE, None) == ARG
+    assert s(FAKE, 10, 0, None, None) == ARG

@@ -49,7 +49,18 @@ class LossOpts(ctypes.Structure):
                 ("mask", ctypes.c_void_p), ("reduction", ctypes.c_int)]
 
 
+class LinOperand(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_void_p), ("ld", ctypes.c_int64), ("dtype", ctypes.c_int),
+                ("kmajor", ctypes.c_int)]
+
+
+class LinHead(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("ldh", ctypes.c_int64), ("w", ctypes.c_void_p),
+                ("ldw", ctypes.c_int64), ("dim", ctypes.c_int64)]
+
+
 REDUCTIONS = {"none": 0, "sum": 1, "mean": 2}
+LIN_OUT = {"f32": 0, "f32_acc": 1, "bf16": 2}
 
 
 def _load():
@@ -80,6 +91,11 @@ def _load():
         "vjsd_membw_probe": ([P, P, ctypes.c_size_t, I, P], I),
         "vjsd_loss_forward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P, P], I),
         "vjsd_loss_backward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P], I),
+        "vlin_gemm": ([I64, I64, I64, LinOperand, LinOperand, P, I64, I, P], I),
+        "vljsd_workspace_bytes": ([I64, I64, I64, I64], ctypes.c_size_t),
+        "vljsd": ([ctypes.POINTER(LinHead), ctypes.POINTER(LinHead), I64, I64, D,
+                   ctypes.POINTER(LossOpts), I64, P, P, P, I64, P, I64, P], I),
+        "vlin_scale": ([P, I64, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -412,3 +428,88 @@ def vlogprobs_bwd(sh: ShardSet, vocab_global: int, stats, ids, ignore_index: int
                              _ptr(grad, torch.float32, N * K, "grad"),
                              _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
                              _stream(stream)))
+
+
+# ---- fused linear + JSD ----------------------------------------------------------------
+
+def _matrix(x: torch.Tensor, name: str) -> None:
+    _require_gpu(x, name)
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+
+
+def lin_operand(x: torch.Tensor, kmajor: bool, name: str = "operand") -> LinOperand:
+    """Operand of vlin_gemm from a 2-D tensor with unit column stride: rows of x are the
+    operand's rows (kmajor) or its k index (not kmajor)."""
+    _matrix(x, name)
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"{name} must be bfloat16 or float32")
+    q = 4 if x.dtype == torch.float32 else 8
+    # a single row's stride is never used: any multiple of q covering the row will do
+    ld = x.stride(0) if x.shape[0] > 1 else -(-max(x.shape[1], 1) // q) * q
+    return LinOperand(x.data_ptr() if x.numel() else None, ld, DTYPES[x.dtype], int(kmajor))
+
+
+def vlin_gemm(M: int, N: int, K: int, a: LinOperand, b: LinOperand, c: torch.Tensor,
+              out: str = "f32", stream=None) -> None:
+    """C[i][j] (+)= sum_k A(i, k) B(j, k) into the 2-D tensor c (row stride >= N)."""
+    if out not in LIN_OUT:
+        raise ValueError(f"out must be one of {sorted(LIN_OUT)}")
+    _matrix(c, "c")
+    want = torch.bfloat16 if out == "bf16" else torch.float32
+    if c.dtype != want:
+        raise ValueError(f"c must be {want} for out={out!r}")
+    if c.shape[0] < M or c.shape[1] < N:
+        raise ValueError("c is smaller than M x N")
+    ldc = c.stride(0) if c.shape[0] > 1 else max(c.shape[1], 1)
+    _check(lib.vlin_gemm(M, N, K, a, b, c.data_ptr() if c.numel() else None, ldc, LIN_OUT[out],
+                         _stream(stream)))
+
+
+def lin_head(h: torch.Tensor, w: torch.Tensor, name: str) -> LinHead:
+    """One side of the fused-linear loss: hidden [N, dim] and head weight [V, dim], bf16."""
+    for x, nm in ((h, f"{name} hidden"), (w, f"{name} head")):
+        _matrix(x, nm)
+        if x.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    if h.shape[1] != w.shape[1]:
+        raise ValueError(f"{name} hidden and head widths differ")
+    ldh = h.stride(0) if h.shape[0] > 1 else -(-max(h.shape[1], 1) // 8) * 8
+    ldw = w.stride(0) if w.shape[0] > 1 else -(-max(w.shape[1], 1) // 8) * 8
+    return LinHead(h.data_ptr() if h.numel() else None, ldh, w.data_ptr(), ldw, w.shape[1])
+
+
+def vljsd_workspace_bytes(N: int, V: int, dim_s: int, chunk: int) -> int:
+    return lib.vljsd_workspace_bytes(N, V, dim_s, chunk)
+
+
+def vljsd(student: LinHead, teacher: LinHead, N: int, V: int, beta: float, opts: LossOpts,
+          chunk: int, workspace, out, grad_h=None, grad_w=None, stream=None) -> None:
+    nout = N if opts.reduction == 0 else 1
+    ws = _ptr(workspace, torch.uint8, vljsd_workspace_bytes(N, V, student.dim, chunk),
+              "workspace")
+    gh = gw = None
+    ldgh = ldgw = 0
+    if grad_h is not None:
+        _matrix(grad_h, "grad_h")
+        if grad_h.dtype != torch.bfloat16 or grad_h.shape[0] < N:
+            raise ValueError("grad_h must be bfloat16 [N, dim_s]")
+        gh = grad_h.data_ptr() if grad_h.numel() else None
+        ldgh = grad_h.stride(0) if grad_h.shape[0] > 1 else grad_h.shape[1]
+    if grad_w is not None:
+        _matrix(grad_w, "grad_w")
+        if grad_w.dtype != torch.bfloat16 or grad_w.shape[0] < V:
+            raise ValueError("grad_w must be bfloat16 [V, dim_s]")
+        gw = grad_w.data_ptr()
+        ldgw = grad_w.stride(0) if grad_w.shape[0] > 1 else grad_w.shape[1]
+    _check(lib.vljsd(ctypes.byref(student), ctypes.byref(teacher), N, V, float(beta),
+                     ctypes.byref(opts), int(chunk), ws, _ptr(out, torch.float32, nout, "out"),
+                     gh, ldgh, gw, ldgw, _stream(stream)))
+
+
+def vlin_scale(x: torch.Tensor, g: torch.Tensor, stream=None) -> None:
+    """x *= g[0] in place (x contiguous fp32 or bf16, g a GPU float32 scalar)."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    _check(lib.vlin_scale(_ptr(x, name="x"), x.numel(), DTYPES[x.dtype],
+                          _ptr(g, torch.float32, 1, "g"), _stream(stream)))

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvjsd.so")
-SOURCES = ["api.hip", "stats.hip", "jsd.hip", "fused.hip", "siblings.hip", "probe.hip", "reduce.hip"]
+SOURCES = ["api.hip", "stats.hip", "jsd.hip", "fused.hip", "siblings.hip", "probe.hip", "reduce.hip", "gemm.hip", "linear.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

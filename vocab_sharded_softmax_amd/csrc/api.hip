@@ -157,6 +157,77 @@ int lp_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t v
     return VJSD_OK;
 }
 
+
+// ---- fused linear + JSD ------------------------------------------------------------
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of vljsd: three logit-sized blocks of C rows (student logits, teacher
+// logits, the student logit gradient; fp32, row stride ldl), the per-token losses,
+// the block's statistics, KL pair and pass workspace, the kept-token count, and the
+// fp32 head-gradient accumulator when there is more than one block.
+struct LinLayout {
+    int64_t C = 0, ldl = 0;
+    size_t ls = 0, lt = 0, g = 0, rows = 0, stats = 0, kl = 0, part = 0, count = 0, gw = 0;
+    size_t total = 0;
+    bool has_gw = false;
+};
+LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk) {
+    LinLayout L;
+    L.C = chunk < N ? chunk : N;
+    L.ldl = (V + 3) / 4 * 4;
+    size_t o = 0;
+    auto take = [&o](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    const size_t blk = (size_t)L.C * (size_t)L.ldl * sizeof(float);
+    L.ls = take(blk);
+    L.lt = take(blk);
+    L.g = take(blk);
+    L.rows = take((size_t)N * sizeof(float));
+    L.stats = take((size_t)L.C * 4 * sizeof(double));
+    L.kl = take((size_t)L.C * 2 * sizeof(float));
+    L.part = take(vjsd_workspace_bytes(L.C > 0 ? L.C : 1, 1));
+    L.count = take(sizeof(double));
+    L.has_gw = L.C < N;
+    L.gw = take(L.has_gw ? (size_t)V * (size_t)dim * sizeof(float) : 0);
+    L.total = o;
+    return L;
+}
+
+// A vlin_gemm operand of `rows` rows and K reduction steps.
+int check_operand(const vlin_operand &o, int64_t rows, int64_t K, bool allow_f32) {
+    if (o.dtype != VJSD_BF16 && !(allow_f32 && o.dtype == VJSD_F32)) return VJSD_ERR_DTYPE;
+    if (o.kmajor != 0 && o.kmajor != 1) return VJSD_ERR_ARG;
+    if (rows == 0 || K == 0) return VJSD_OK;  // never read
+    if (!o.p || reinterpret_cast<uintptr_t>(o.p) % 16 != 0) return VJSD_ERR_ARG;
+    const int64_t q = o.dtype == VJSD_F32 ? 4 : 8;
+    if (o.ld <= 0 || o.ld % q != 0) return VJSD_ERR_ARG;
+    if (o.kmajor ? o.ld < K : o.ld < rows) return VJSD_ERR_ARG;
+    return VJSD_OK;
+}
+
+constexpr int64_t GEMM_TILES_MAX = 0x7fffff00LL;  // one workgroup per 128 x 128 tile
+
+bool gemm_size_ok(int64_t M, int64_t N) {
+    return ((M + 127) / 128) * ((N + 127) / 128) <= GEMM_TILES_MAX;
+}
+
+// One LM-head side: hidden [N][dim] and head [V][dim], bf16.
+int check_head(const vlin_head *h, int64_t N, int64_t V) {
+    if (!h || h->dim < 1) return VJSD_ERR_ARG;
+    if (N > 0 && (!h->h || reinterpret_cast<uintptr_t>(h->h) % 16 != 0 || h->ldh < h->dim ||
+                  h->ldh % 8 != 0))
+        return VJSD_ERR_ARG;
+    if (!h->w || reinterpret_cast<uintptr_t>(h->w) % 16 != 0 || h->ldw < h->dim ||
+        h->ldw % 8 != 0)
+        return VJSD_ERR_ARG;
+    (void)V;
+    return VJSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -561,6 +632,201 @@ int vtopk_kl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t 
     w.grow = grad;
     return lp_backward(shards, S, N, dtype, vocab_global, stats, ids, K, ignore_index, w, part,
                        (hipStream_t)stream);
+}
+
+int vlin_gemm(int64_t M, int64_t N, int64_t K, vlin_operand a, vlin_operand b, void *c,
+              int64_t ldc, int out, void *stream) {
+    if (M < 0 || N < 0 || K < 0 || !gemm_size_ok(M, N)) return VJSD_ERR_ARG;
+    if (out != VLIN_OUT_F32 && out != VLIN_OUT_F32_ACC && out != VLIN_OUT_BF16)
+        return VJSD_ERR_ARG;
+    int e = check_operand(a, M, K, true);
+    if (e) return e;
+    if ((e = check_operand(b, N, K, false))) return e;
+    if (M == 0 || N == 0) return VJSD_OK;
+    const size_t es = out == VLIN_OUT_BF16 ? 2 : 4;
+    if (!c || reinterpret_cast<uintptr_t>(c) % es != 0 || ldc < N) return VJSD_ERR_ARG;
+    vjsd::GemmArgs g;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.a = a.p;
+    g.lda = a.ld;
+    g.a_f32 = a.dtype == VJSD_F32;
+    g.a_kmajor = a.kmajor;
+    g.b = b.p;
+    g.ldb = b.ld;
+    g.b_kmajor = b.kmajor;
+    g.c = c;
+    g.ldc = ldc;
+    g.out = out == VLIN_OUT_F32 ? vjsd::GEMM_F32
+                                : (out == VLIN_OUT_F32_ACC ? vjsd::GEMM_F32_ACC : vjsd::GEMM_BF16);
+    return hip_status(vjsd::launch_gemm(g, (hipStream_t)stream));
+}
+
+size_t vljsd_workspace_bytes(int64_t N, int64_t V, int64_t dim_s, int64_t chunk) {
+    if (N < 0 || V < 1 || dim_s < 1 || chunk < 1) return 0;
+    return lin_layout(N, V, dim_s, chunk).total;
+}
+
+int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t V, double beta,
+          const vjsd_loss_opts *opts, int64_t chunk, void *workspace, float *out, void *grad_h,
+          int64_t ldgh, void *grad_w, int64_t ldgw, void *stream) {
+    if (N < 0 || N > MAX_ROWS || V < 1 || chunk < 1 || !out) return VJSD_ERR_ARG;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    LossCfg c;
+    int e = loss_cfg(opts, &c);
+    if (e) return e;
+    if ((e = check_head(student, N, V)) || (e = check_head(teacher, N, V))) return e;
+    const int64_t D = student->dim;
+    const bool grads = grad_h != nullptr || grad_w != nullptr;
+    if (grads && c.red == VJSD_REDUCE_NONE) return VJSD_ERR_ARG;
+    if (grad_h && (ldgh < D || reinterpret_cast<uintptr_t>(grad_h) % 2 != 0)) return VJSD_ERR_ARG;
+    if (grad_w && (ldgw < D || reinterpret_cast<uintptr_t>(grad_w) % 2 != 0)) return VJSD_ERR_ARG;
+    if (!gemm_size_ok(chunk < N ? chunk : N, V) || !gemm_size_ok(V, D)) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    const vjsd::RowOpts ro = row_opts(c);
+    if (N == 0) {
+        if (grad_w) {  // d out / d w = 0: a product over no tokens
+            vjsd::GemmArgs g;
+            g.M = V;
+            g.N = D;
+            g.K = 0;
+            g.c = grad_w;
+            g.ldc = ldgw;
+            g.out = vjsd::GEMM_BF16;
+            if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+        }
+        if (c.red != VJSD_REDUCE_NONE)
+            return hip_status(
+                vjsd::launch_reduce_rows(nullptr, vjsd::RowOpts(), 0, false, out, nullptr, st));
+        return VJSD_OK;
+    }
+    if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return VJSD_ERR_ARG;
+    const LinLayout L = lin_layout(N, V, D, chunk);
+    char *ws = static_cast<char *>(workspace);
+    float *ls = reinterpret_cast<float *>(ws + L.ls);
+    float *lt = reinterpret_cast<float *>(ws + L.lt);
+    float *G = reinterpret_cast<float *>(ws + L.g);
+    float *rows = reinterpret_cast<float *>(ws + L.rows);
+    double *stats = reinterpret_cast<double *>(ws + L.stats);
+    float *kl = reinterpret_cast<float *>(ws + L.kl);
+    float *part = reinterpret_cast<float *>(ws + L.part);
+    double *count = reinterpret_cast<double *>(ws + L.count);
+    float *gw = L.has_gw ? reinterpret_cast<float *>(ws + L.gw) : nullptr;
+    const bool mean = c.red == VJSD_REDUCE_MEAN;
+    if (grads && mean) {  // the kept-token count over all N, before any block's gradient
+        if ((e = hip_status(vjsd::launch_reduce_rows(nullptr, ro, N, false, nullptr, count, st))))
+            return e;
+    }
+    float *rows_out = c.red == VJSD_REDUCE_NONE ? out : rows;
+    const int mode = mode_of(beta);
+    const int64_t C = L.C, nblk = (N + C - 1) / C;
+    const uint16_t *hs = static_cast<const uint16_t *>(student->h);
+    const uint16_t *ht = static_cast<const uint16_t *>(teacher->h);
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+        const int64_t n0 = blk * C, nb = N - n0 < C ? N - n0 : C;
+        // the block's logits, student and teacher
+        for (int side = 0; side < 2; ++side) {
+            const vlin_head *hd = side == 0 ? student : teacher;
+            vjsd::GemmArgs g;
+            g.M = nb;
+            g.N = V;
+            g.K = hd->dim;
+            g.a = (side == 0 ? hs : ht) + n0 * hd->ldh;
+            g.lda = hd->ldh;
+            g.b = hd->w;
+            g.ldb = hd->ldw;
+            g.c = side == 0 ? ls : lt;
+            g.ldc = L.ldl;
+            g.out = vjsd::GEMM_F32;
+            if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+        }
+        // the block's per-token loss
+        Shard sh;
+        sh.start = 0;
+        sh.width = V;
+        sh.s = {ls, L.ldl, 0, 0};
+        sh.t = {lt, L.ldl, 0, 0};
+        sh.gs = {G, L.ldl, 0, 0};
+        sh.gt = {nullptr, 0, 0, 0};
+        vjsd::RowOpts rb = ro;
+        rb.mask = ro.mask ? ro.mask + n0 : nullptr;
+        if (mode != vjsd::INTERIOR) {
+            const int rev = mode == vjsd::REV_KL;
+            if ((e = hip_status(vjsd::launch_kl1(VJSD_F32, rev, sh, nb, part_of(part, 0, nb), st,
+                                                 rb))))
+                return e;
+            if ((e = hip_status(vjsd::launch_kl1_merge(rev, part_of(part, 0, nb), 1, nb, stats, kl,
+                                                       rows_out + n0, st, rb))))
+                return e;
+        } else if ((e = hip_status(vjsd::launch_fwd_fused(VJSD_F32, sh, nb, beta, stats, kl,
+                                                           rows_out + n0, st, rb)))) {
+            return e;
+        }
+        if (!grads) continue;
+        // the logit gradient of the block for a unit upstream gradient of out[0]
+        vjsd::GradOpts go;
+        go.ks = ro.ks;
+        go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
+        go.scalar = true;
+        go.mask = rb.mask;
+        go.count = mean ? count : nullptr;
+        if ((e = hip_status(vjsd::launch_bwd_prep(mode, nb, stats, kl, beta, nullptr, part, st,
+                                                  go))))
+            return e;
+        if ((e = hip_status(vjsd::launch_bwd(VJSD_F32, mode, sh, nb, part, st)))) return e;
+        if (grad_h) {  // G [nb][V] x w_s [V][D]
+            vjsd::GemmArgs g;
+            g.M = nb;
+            g.N = D;
+            g.K = V;
+            g.a = G;
+            g.lda = L.ldl;
+            g.a_f32 = 1;
+            g.b = student->w;
+            g.ldb = student->ldw;
+            g.b_kmajor = 0;
+            g.c = static_cast<uint16_t *>(grad_h) + n0 * ldgh;
+            g.ldc = ldgh;
+            g.out = vjsd::GEMM_BF16;
+            if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+        }
+        if (grad_w) {  // G^T [V][nb] x h_s [nb][D], summed over the blocks in fp32
+            vjsd::GemmArgs g;
+            g.M = V;
+            g.N = D;
+            g.K = nb;
+            g.a = G;
+            g.lda = L.ldl;
+            g.a_f32 = 1;
+            g.a_kmajor = 0;
+            g.b = hs + n0 * student->ldh;
+            g.ldb = student->ldh;
+            g.b_kmajor = 0;
+            if (nblk == 1 || blk == nblk - 1) {
+                g.c = grad_w;
+                g.ldc = ldgw;
+                g.out = nblk == 1 ? vjsd::GEMM_BF16 : vjsd::GEMM_BF16_ACC;
+                g.addend = gw;
+                g.ldadd = D;
+            } else {
+                g.c = gw;
+                g.ldc = D;
+                g.out = blk == 0 ? vjsd::GEMM_F32 : vjsd::GEMM_F32_ACC;
+            }
+            if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+        }
+    }
+    if (c.red == VJSD_REDUCE_NONE) return VJSD_OK;
+    return hip_status(vjsd::launch_reduce_rows(rows, ro, N, mean, out, nullptr, st));
+}
+
+int vlin_scale(void *p, int64_t n, int dtype, const float *g, void *stream) {
+    if (dtype != VJSD_F32 && dtype != VJSD_BF16) return VJSD_ERR_DTYPE;
+    if (n < 0) return VJSD_ERR_ARG;
+    if (n == 0) return VJSD_OK;
+    if (!p || !g || reinterpret_cast<uintptr_t>(p) % 16 != 0) return VJSD_ERR_ARG;
+    return hip_status(vjsd::launch_scale(dtype == VJSD_F32 ? 0 : 2, p, n, g, (hipStream_t)stream));
 }
 
 }  // extern "C"

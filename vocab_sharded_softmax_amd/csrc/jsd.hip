@@ -180,7 +180,7 @@ __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats
     if (r >= N) return;
     const RowConst k = row_const(stats, r, go.ks);
     const bool dropped = go.mask != nullptr && go.mask[r] == 0;
-    double g = go.scalar ? (double)grad[0] : (double)grad[r];
+    double g = grad == nullptr ? 1.0 : (go.scalar ? (double)grad[0] : (double)grad[r]);
     if (go.count) g /= fmax((double)*go.count, 1.0);
     g *= go.gmul;
     const double KT2 = (double)kl[2 * r] * L2E_D, KS2 = (double)kl[2 * r + 1] * L2E_D;

@@ -50,7 +50,8 @@ inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
 
 // Upstream-gradient options of the distillation-loss form of the backward: the row
 // r's gradient scale is g_r * gmul, g_r = grad[r] (per-row) or grad[0] (reduced;
-// divided by max(*count, 1) for a mean), and 0 for a row the mask drops.
+// divided by max(*count, 1) for a mean), and 0 for a row the mask drops.  A NULL
+// grad stands for a unit upstream gradient.
 struct GradOpts {
     float ks = L2E;                  // log2 e / temperature
     double gmul = 1.0;               // T^2 (if scaled) * (1/T): chain rule through x / T
@@ -134,5 +135,34 @@ hipError_t launch_topk_kl(int dtype, const LpTable &tab, bool first, int64_t N,
                           int64_t vocab_global, const int64_t *ids, const float *tlogp, int K,
                           int64_t ignore, const double *stats, float *kl, int32_t *dev_err,
                           hipStream_t st);
+
+// Matrix-core GEMM of the fused-linear loss: C[i][j] (+)= sum_k A(i, k) * B(j, k), bf16
+// products (fp32 A rounded to bf16 when staged), fp32 accumulation.  A(i, k) is at
+// a[i*lda + k] (a_kmajor) or a[k*lda + i]; B(j, k) at b[j*ldb + k] (b_kmajor) or
+// b[k*ldb + j], bf16.  Pointers 16-byte aligned, leading dimensions multiples of 8
+// elements (fp32 A: 4).
+enum GemmOut {
+    GEMM_F32 = 0,      // fp32 C = A B^T
+    GEMM_F32_ACC = 1,  // fp32 C += A B^T
+    GEMM_BF16 = 2,     // bf16 C = A B^T (nearest even)
+    GEMM_BF16_ACC = 3  // bf16 C = addend + A B^T (addend fp32)
+};
+struct GemmArgs {
+    int64_t M = 0, N = 0, K = 0;
+    const void *a = nullptr;
+    int64_t lda = 0;
+    int a_f32 = 0, a_kmajor = 1;
+    const void *b = nullptr;
+    int64_t ldb = 0;
+    int b_kmajor = 1;
+    void *c = nullptr;
+    int64_t ldc = 0;
+    int out = GEMM_F32;
+    const float *addend = nullptr;  // GEMM_BF16_ACC: fp32, element (i, j) at addend[i*ldadd + j]
+    int64_t ldadd = 0;
+};
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
+// p[i] *= g[0] over n values of dtype 0 (fp32) or 2 (bf16); p 16-byte aligned
+hipError_t launch_scale(int dtype, void *p, int64_t n, const float *g, hipStream_t st);
 
 }  // namespace vjsd

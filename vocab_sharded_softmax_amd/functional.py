@@ -21,7 +21,8 @@ from torch.autograd.function import once_differentiable
 from . import _abi
 from ._abi import ShardSet
 
-__all__ = ["jsd", "jsd_loss", "kl_div", "entropy", "logprobs", "topk_kl", "cross_entropy"]
+__all__ = ["jsd", "jsd_loss", "kl_div", "entropy", "logprobs", "topk_kl", "cross_entropy",
+           "linear_jsd"]
 
 
 def _unpack(n_shards: int, tensors):
@@ -412,3 +413,95 @@ def logprobs(logits, index, *, ignore_index: int = -100, split=None) -> torch.Te
     ids = index.unsqueeze(-1) if single else index
     out = _Logprobs.apply(ids, int(ignore_index), None if split is None else tuple(split), n, *x)
     return out.squeeze(-1) if single else out
+
+
+class _LinearJSD(torch.autograd.Function):
+    """Fused-linear loss: the gradients of a reduced loss are formed in the forward pass
+    for a unit upstream gradient (the logit blocks exist only there) and scaled by the
+    actual one in the backward."""
+
+    @staticmethod
+    def forward(ctx, beta, temperature, scale_t2, reduction, mask, chunk, hs, ws, ht, wt):
+        N, V = hs.shape[0], ws.shape[0]
+        dev = hs.device
+        want_h = ctx.needs_input_grad[6] and reduction != "none"
+        want_w = ctx.needs_input_grad[7] and reduction != "none"
+        student = _abi.lin_head(hs, ws, "student")
+        teacher = _abi.lin_head(ht, wt, "teacher")
+        opts = _abi.loss_opts(N, temperature, scale_t2, mask, reduction)
+        C = max(1, min(int(chunk), max(N, 1)))
+        nbytes = _abi.vljsd_workspace_bytes(N, V, hs.shape[1], C)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        out = torch.empty((N if reduction == "none" else 1,), dtype=torch.float32, device=dev)
+        gh = torch.empty(hs.shape, dtype=hs.dtype, device=dev) if want_h else None
+        gw = torch.empty(ws.shape, dtype=ws.dtype, device=dev) if want_w else None
+        _abi.vljsd(student, teacher, N, V, beta, opts, C, workspace, out, gh, gw)
+        del workspace
+        ctx.save_for_backward(gh, gw)
+        ctx.used = False
+        return out if reduction == "none" else out.view(())
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gout):
+        if ctx.used:
+            raise RuntimeError("linear_jsd: the backward scales its stored gradients in place "
+                               "and can run only once")
+        ctx.used = True
+        gh, gw = ctx.saved_tensors
+        g = gout.reshape(-1)[:1].to(torch.float32).contiguous()
+        if gh is not None:
+            _abi.vlin_scale(gh, g)
+        if gw is not None:
+            _abi.vlin_scale(gw, g)
+        return (None, None, None, None, None, None, gh, gw, None, None)
+
+
+def linear_jsd(student_hidden, student_head, teacher_hidden, teacher_head, beta: float = 0.5, *,
+               temperature: float = 1.0, scale_t2: bool = False, mask=None,
+               reduction: str = "mean", chunk: int = 4096) -> torch.Tensor:
+    """Fused-linear distillation loss: ``jsd_loss`` on the logits ``h @ W^T`` of the
+    student and the teacher, evaluated ``chunk`` tokens at a time so that the full
+    ``[N, V]`` logits never exist (the fused-linear divergence [JSD-PR, Scope and
+    limitations] and [OPS-PR, Limitations] leave as future work; [JSD-PR, Motivation]
+    describes the tiled LM-head projection it replaces materialised logits with).
+
+    Hidden states ``[N, D]`` or ``[B, T, D]`` and head weights ``[V, D]``, bfloat16,
+    with unit column stride; the teacher's width may differ from the student's.  The
+    teacher is a constant: pass it without ``requires_grad``.  Gradients flow to the
+    student's hidden states and head weight and need ``reduction`` "sum" or "mean";
+    "none" returns per-token losses without gradients.  The logit products run on the
+    matrix cores in bf16 with fp32 accumulation; the logit gradient is rounded to bf16
+    for the two gradient products, as a bf16 model's backward rounds it.
+    """
+    beta = float(beta)
+    if not (0.0 <= beta <= 1.0):
+        raise ValueError("beta must be in [0, 1]")
+    temperature = float(temperature)
+    if not (temperature > 0.0 and temperature < float("inf")):
+        raise ValueError("temperature must be a positive finite number")
+    if reduction not in _abi.REDUCTIONS:
+        raise ValueError(f"reduction must be one of {sorted(_abi.REDUCTIONS)}")
+    if int(chunk) < 1:
+        raise ValueError("chunk must be a positive number of tokens")
+    if teacher_hidden.requires_grad or teacher_head.requires_grad:
+        raise ValueError("the teacher is a constant: pass teacher tensors without requires_grad "
+                         "(detach them)")
+    if reduction == "none" and torch.is_grad_enabled() and (
+            student_hidden.requires_grad or student_head.requires_grad):
+        raise ValueError("gradients of linear_jsd need reduction 'sum' or 'mean'")
+    lead = student_hidden.shape[:-1]
+    if tuple(teacher_hidden.shape[:-1]) != tuple(lead):
+        raise ValueError("student and teacher hidden states must cover the same tokens")
+    hs = student_hidden.reshape(-1, student_hidden.shape[-1])
+    ht = teacher_hidden.reshape(-1, teacher_hidden.shape[-1])
+    m = None
+    if mask is not None:
+        if tuple(mask.shape) != tuple(lead):
+            raise ValueError(f"mask must have shape {tuple(lead)}, got {tuple(mask.shape)}")
+        m = mask.reshape(-1)
+        m = m.view(torch.uint8) if m.dtype == torch.bool else m.to(torch.uint8)
+        m = m.contiguous()
+    out = _LinearJSD.apply(beta, temperature, bool(scale_t2), reduction, m, int(chunk), hs,
+                           student_head, ht, teacher_head)
+    return out.view(lead) if reduction == "none" else out
