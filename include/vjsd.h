@@ -370,7 +370,9 @@ VJSD_API int vjsd_membw_probe(const void *src, void *dst, size_t bytes, int op, 
  * p[k*ld + row].  dtype VJSD_BF16, or VJSD_F32 for the first operand only (each
  * value rounded to bf16, nearest even, before its product).  p must be 16-byte
  * aligned and ld a multiple of 8 elements (4 for VJSD_F32), at least the extent of
- * the contiguous index.
+ * the contiguous index, and the operand readable over whole rows of ld elements
+ * (edge tiles read full 16-byte chunks up to a row's ld and discard what lies past
+ * the contiguous index).
  */
 typedef struct {
     const void *p;
@@ -417,17 +419,21 @@ typedef struct {
  * VJSD_REDUCE_NONE, else out[0] is the sum or the mean over the kept tokens.
  * grad_h (bf16 [N][dim_s], row stride ldgh) and grad_w (bf16 [V][dim_s], row stride
  * ldgw), each optional (NULL), receive d out[0] / d h_s and d out[0] / d w_s; they
- * need a reduction (VJSD_ERR_ARG otherwise).  The teacher is a constant.  Gradients
- * come from the bf16-rounded logit gradient (the operand precision of the products).
- * Masked tokens get exactly zero rows of grad_h.  workspace: device memory of
- * vljsd_workspace_bytes(N, V, dim_s, chunk) bytes, 256-byte aligned.  VJSD_ERR_ARG
- * for a bad size, chunk, pointer, alignment or stride; VJSD_ERR_BETA as vjsd_fwd.
+ * need a reduction (VJSD_ERR_ARG otherwise).  The teacher is a constant.  The logit
+ * gradient is rounded to bf16 (the operand precision of the products) and kept for
+ * `group` tokens at a time (rounded up to whole chunks; 0: as many as fit 4 GiB),
+ * whose two gradient products then run at once; with more than one group the head
+ * gradient is summed across groups in fp32.  Masked tokens get exactly zero rows of
+ * grad_h.  workspace: device memory of vljsd_workspace_bytes(N, V, dim_s, chunk,
+ * group) bytes, 256-byte aligned.  VJSD_ERR_ARG for a bad size, chunk, group,
+ * pointer, alignment or stride; VJSD_ERR_BETA as vjsd_fwd.
  */
-VJSD_API size_t vljsd_workspace_bytes(int64_t N, int64_t V, int64_t dim_s, int64_t chunk);
+VJSD_API size_t vljsd_workspace_bytes(int64_t N, int64_t V, int64_t dim_s, int64_t chunk,
+                                      int64_t group);
 VJSD_API int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t V,
-                   double beta, const vjsd_loss_opts *opts, int64_t chunk, void *workspace,
-                   float *out, void *grad_h, int64_t ldgh, void *grad_w, int64_t ldgw,
-                   void *stream);
+                   double beta, const vjsd_loss_opts *opts, int64_t chunk, int64_t group,
+                   void *workspace, float *out, void *grad_h, int64_t ldgh, void *grad_w,
+                   int64_t ldgw, void *stream);
 
 /*
  * Scales n values in place by a device scalar: p[i] *= g[0] (the upstream gradient

@@ -268,13 +268,15 @@ def test_linear_jsd_validates_before_any_launch():
     none = abi.LossOpts(1.0, 0, None, 0)
     by = ctypes.byref
 
-    def call(N=16, V=100, beta=0.5, o=opts, chunk=8, ws=FAKE, out=FAKE, gh=None, ldgh=0,
-             gw=None, ldgw=0, s=st, t=te):
-        return f(by(s), by(t), N, V, beta, by(o), chunk, ws, out, gh, ldgh, gw, ldgw, None)
+    def call(N=16, V=100, beta=0.5, o=opts, chunk=8, group=0, ws=FAKE, out=FAKE, gh=None,
+             ldgh=0, gw=None, ldgw=0, s=st, t=te):
+        return f(by(s), by(t), N, V, beta, by(o), chunk, group, ws, out, gh, ldgh, gw, ldgw,
+                 None)
 
     assert call(N=-1) == ARG
     assert call(V=0) == ARG
     assert call(chunk=0) == ARG
+    assert call(group=-1) == ARG
     assert call(out=None) == ARG
     assert call(beta=1.5) == BETA
     assert call(beta=float("nan")) == BETA
@@ -294,15 +296,23 @@ def test_linear_jsd_validates_before_any_launch():
 
 def test_linear_workspace_and_scale():
     w = lib.vljsd_workspace_bytes
-    assert w(16, 0, 8, 4) == 0 and w(16, 10, 0, 4) == 0 and w(16, 10, 8, 0) == 0
+    assert w(16, 0, 8, 4, 0) == 0 and w(16, 10, 0, 4, 0) == 0 and w(16, 10, 8, 0, 0) == 0
+    assert w(16, 10, 8, 4, -1) == 0
     al = lambda x: (x + 255) // 256 * 256
+    # two fp32 logit blocks of C rows (row stride V rounded up to 8), the bf16 logit
+    # gradient of a group (4 GiB worth of whole chunks by default), per-token losses,
+    # the block's statistics / KL pair / pass workspace, the count, and the fp32 head
+    # gradient accumulator only with more than one group
     N, V, D, C = 8192, 151936, 3584, 4096
-    expect = (3 * al(C * V * 4) + al(N * 4) + al(C * 32) + al(C * 8)
-              + al(lib.vjsd_workspace_bytes(C, 1)) + al(8) + al(V * D * 4))
-    assert w(N, V, D, C) == expect
-    # one block: no head-gradient accumulator; logit rows padded to a multiple of 4
-    assert w(100, 1001, 16, 128) == (3 * al(100 * 1004 * 4) + al(400) + al(3200) + al(800)
-                                     + al(lib.vjsd_workspace_bytes(100, 1)) + al(8))
+    ldl = V
+    expect = (2 * al(C * ldl * 4) + al(N * ldl * 2) + al(N * 4) + al(C * 32) + al(C * 8)
+              + al(lib.vjsd_workspace_bytes(C, 1)) + al(8))
+    assert w(N, V, D, C, 0) == expect
+    # groups of 2 chunks of 100 over 300 tokens: two groups, so an accumulator
+    ldl = 1008
+    expect = (2 * al(100 * ldl * 4) + al(200 * ldl * 2) + al(300 * 4) + al(3200) + al(800)
+              + al(lib.vjsd_workspace_bytes(100, 1)) + al(8) + al(1001 * 16 * 4))
+    assert w(300, 1001, 16, 100, 150) == expect
     s = lib.vlin_scale
     assert s(FAKE, 10, 1, FAKE, None) == DTYPE
     assert s(FAKE, 0, 2, FAKE, None) == OK

@@ -111,20 +111,20 @@ def _grad_tol(G, other, ref):
     return (2.0 ** -8 + 1e-4 + (K + 2) * U) * mag + 2.0 ** -8 * np.abs(ref) + 1e-7
 
 
-def _check_linear(b, beta, T=1.0, t2=False, mask=None, red="mean", chunk=4096):
+def _check_linear(b, beta, T=1.0, t2=False, mask=None, red="mean", chunk=4096, group=0):
     v = vj()
     N, V = b.hs.shape[0], b.ws.shape[0]
     st = v.lin_head(b.hs, b.ws, "student")
     te = v.lin_head(b.ht, b.wt, "teacher")
     opts = v.loss_opts(N, T, t2, mask, red)
-    ws = torch.empty(max(1, v.vljsd_workspace_bytes(N, V, b.hs.shape[1], chunk)),
+    ws = torch.empty(max(1, v.vljsd_workspace_bytes(N, V, b.hs.shape[1], chunk, group)),
                      dtype=torch.uint8, device="cuda")
     out = torch.full((N if red == "none" else 1,), float("nan"), device="cuda")
     gh = gw = None
     if red != "none":
         gh = torch.full_like(b.hs, float("nan"))
         gw = torch.full_like(b.ws, float("nan"))
-    v.vljsd(st, te, N, V, beta, opts, chunk, ws, out, gh, gw)
+    v.vljsd(st, te, N, V, beta, opts, chunk, ws, out, gh, gw, group=group)
     torch.cuda.synchronize()
     ref = _lin_ref(b, beta, T, t2, mask, red)
     want = ref["rows"] if red == "none" else np.array([ref["out"]])
@@ -147,10 +147,13 @@ def _check_linear(b, beta, T=1.0, t2=False, mask=None, red="mean", chunk=4096):
         assert not ghg[drop].any()
 
 
-@pytest.mark.parametrize("chunk", [10_000, 128, 100])
-def test_linear_jsd_chunks(chunk):
+@pytest.mark.parametrize("chunk,group", [(10_000, 0), (128, 0), (100, 0), (64, 128), (100, 100),
+                                         (128, 1)])
+def test_linear_jsd_chunks_and_groups(chunk, group):
+    # one block; several blocks in one group; three groups (the head gradient summed
+    # in fp32 across them: the store, accumulate and final convert epilogues)
     b = synth.draw_linear("cuda", N=300, V=1000, Ds=72, Dt=56, seed=7)
-    _check_linear(b, 0.5, chunk=chunk)
+    _check_linear(b, 0.5, chunk=chunk, group=group)
 
 
 @pytest.mark.parametrize("beta", [0.0, 0.3, 1.0])
@@ -158,7 +161,7 @@ def test_linear_jsd_betas_temperature_mask(beta):
     b = synth.draw_linear("cuda", N=257, V=777, Ds=64, Dt=96, seed=8)
     g = torch.Generator(device="cuda").manual_seed(3)
     mask = (torch.rand(257, generator=g, device="cuda") > 0.2).to(torch.uint8)
-    _check_linear(b, beta, T=2.0, t2=True, mask=mask, red="mean", chunk=128)
+    _check_linear(b, beta, T=2.0, t2=True, mask=mask, red="mean", chunk=128, group=128)
     _check_linear(b, beta, T=0.7, red="sum", chunk=1000)
     _check_linear(b, beta, red="none", chunk=64)
 
@@ -211,7 +214,7 @@ def test_linear_full_size_sampled():
     N, V, D = b.hs.shape[0], b.ws.shape[0], b.hs.shape[1]
     st = v.lin_head(b.hs, b.ws, "student")
     te = v.lin_head(b.ht, b.wt, "teacher")
-    ws = torch.empty(v.vljsd_workspace_bytes(N, V, D, 4096), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(v.vljsd_workspace_bytes(N, V, D, 4096, 0), dtype=torch.uint8, device="cuda")
     rows = torch.full((N,), float("nan"), device="cuda")
     v.vljsd(st, te, N, V, 0.5, v.loss_opts(N, 1.0, False, None, "none"), 4096, ws, rows)
     out = torch.full((1,), float("nan"), device="cuda")

@@ -92,9 +92,9 @@ def _load():
         "vjsd_loss_forward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P, P], I),
         "vjsd_loss_backward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P], I),
         "vlin_gemm": ([I64, I64, I64, LinOperand, LinOperand, P, I64, I, P], I),
-        "vljsd_workspace_bytes": ([I64, I64, I64, I64], ctypes.c_size_t),
+        "vljsd_workspace_bytes": ([I64, I64, I64, I64, I64], ctypes.c_size_t),
         "vljsd": ([ctypes.POINTER(LinHead), ctypes.POINTER(LinHead), I64, I64, D,
-                   ctypes.POINTER(LossOpts), I64, P, P, P, I64, P, I64, P], I),
+                   ctypes.POINTER(LossOpts), I64, I64, P, P, P, I64, P, I64, P], I),
         "vlin_scale": ([P, I64, I, P, P], I),
     }
     for name, (args, res) in sig.items():
@@ -447,7 +447,19 @@ def lin_operand(x: torch.Tensor, kmajor: bool, name: str = "operand") -> LinOper
     q = 4 if x.dtype == torch.float32 else 8
     # a single row's stride is never used: any multiple of q covering the row will do
     ld = x.stride(0) if x.shape[0] > 1 else -(-max(x.shape[1], 1) // q) * q
+    _whole_rows(x, ld, name)
     return LinOperand(x.data_ptr() if x.numel() else None, ld, DTYPES[x.dtype], int(kmajor))
+
+
+def _whole_rows(x: torch.Tensor, ld: int, name: str) -> None:
+    """The products read whole rows of ld elements: the storage must hold them."""
+    if x.numel() == 0:
+        return
+    have = x.untyped_storage().nbytes() // x.element_size() - x.storage_offset()
+    if have < x.shape[0] * ld:
+        raise ValueError(f"{name}: the storage must extend over whole rows of {ld} elements "
+                         f"(pad the last row, or pass a tensor whose row stride is a multiple "
+                         f"of {16 // x.element_size()})")
 
 
 def vlin_gemm(M: int, N: int, K: int, a: LinOperand, b: LinOperand, c: torch.Tensor,
@@ -476,17 +488,20 @@ def lin_head(h: torch.Tensor, w: torch.Tensor, name: str) -> LinHead:
         raise ValueError(f"{name} hidden and head widths differ")
     ldh = h.stride(0) if h.shape[0] > 1 else -(-max(h.shape[1], 1) // 8) * 8
     ldw = w.stride(0) if w.shape[0] > 1 else -(-max(w.shape[1], 1) // 8) * 8
+    _whole_rows(h, ldh, f"{name} hidden")
+    _whole_rows(w, ldw, f"{name} head")
     return LinHead(h.data_ptr() if h.numel() else None, ldh, w.data_ptr(), ldw, w.shape[1])
 
 
-def vljsd_workspace_bytes(N: int, V: int, dim_s: int, chunk: int) -> int:
-    return lib.vljsd_workspace_bytes(N, V, dim_s, chunk)
+def vljsd_workspace_bytes(N: int, V: int, dim_s: int, chunk: int, group: int = 0) -> int:
+    return lib.vljsd_workspace_bytes(N, V, dim_s, chunk, group)
 
 
 def vljsd(student: LinHead, teacher: LinHead, N: int, V: int, beta: float, opts: LossOpts,
-          chunk: int, workspace, out, grad_h=None, grad_w=None, stream=None) -> None:
+          chunk: int, workspace, out, grad_h=None, grad_w=None, stream=None,
+          group: int = 0) -> None:
     nout = N if opts.reduction == 0 else 1
-    ws = _ptr(workspace, torch.uint8, vljsd_workspace_bytes(N, V, student.dim, chunk),
+    ws = _ptr(workspace, torch.uint8, vljsd_workspace_bytes(N, V, student.dim, chunk, group),
               "workspace")
     gh = gw = None
     ldgh = ldgw = 0
@@ -503,8 +518,8 @@ def vljsd(student: LinHead, teacher: LinHead, N: int, V: int, beta: float, opts:
         gw = grad_w.data_ptr()
         ldgw = grad_w.stride(0) if grad_w.shape[0] > 1 else grad_w.shape[1]
     _check(lib.vljsd(ctypes.byref(student), ctypes.byref(teacher), N, V, float(beta),
-                     ctypes.byref(opts), int(chunk), ws, _ptr(out, torch.float32, nout, "out"),
-                     gh, ldgh, gw, ldgw, _stream(stream)))
+                     ctypes.byref(opts), int(chunk), int(group), ws,
+                     _ptr(out, torch.float32, nout, "out"), gh, ldgh, gw, ldgw, _stream(stream)))
 
 
 def vlin_scale(x: torch.Tensor, g: torch.Tensor, stream=None) -> None:

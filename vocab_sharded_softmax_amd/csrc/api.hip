@@ -162,20 +162,33 @@ int lp_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t v
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of vljsd: three logit-sized blocks of C rows (student logits, teacher
-// logits, the student logit gradient; fp32, row stride ldl), the per-token losses,
-// the block's statistics, KL pair and pass workspace, the kept-token count, and the
-// fp32 head-gradient accumulator when there is more than one block.
+// Workspace of vljsd.  Tokens go C = min(chunk, N) at a time through two fp32 logit
+// blocks (student, teacher; row stride ldl = V rounded up to 8); the bf16 logit
+// gradient G of a group of NG tokens (whole chunks: `group` rounded up, or with group 0
+// as many as fit LIN_G_BUDGET bytes, at least one) is kept for the two gradient
+// products of the group; then the
+// per-token losses, the block's statistics, KL pair and pass workspace, the kept-token
+// count, and the fp32 head-gradient accumulator when there is more than one group.
+constexpr size_t LIN_G_BUDGET = (size_t)4 << 30;
+
 struct LinLayout {
-    int64_t C = 0, ldl = 0;
+    int64_t C = 0, NG = 0, ldl = 0;
     size_t ls = 0, lt = 0, g = 0, rows = 0, stats = 0, kl = 0, part = 0, count = 0, gw = 0;
     size_t total = 0;
     bool has_gw = false;
 };
-LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk) {
+LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk, int64_t group) {
     LinLayout L;
     L.C = chunk < N ? chunk : N;
-    L.ldl = (V + 3) / 4 * 4;
+    L.ldl = (V + 7) / 8 * 8;
+    int64_t per = 1;  // chunks per group
+    if (L.C > 0) {
+        per = group > 0 ? (group + L.C - 1) / L.C
+                        : (int64_t)(LIN_G_BUDGET / ((size_t)L.ldl * 2)) / L.C;
+        if (per < 1) per = 1;
+    }
+    const int64_t ng = per * L.C;
+    L.NG = ng < N ? ng : N;
     size_t o = 0;
     auto take = [&o](size_t bytes) {
         const size_t at = o;
@@ -185,13 +198,13 @@ LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk) {
     const size_t blk = (size_t)L.C * (size_t)L.ldl * sizeof(float);
     L.ls = take(blk);
     L.lt = take(blk);
-    L.g = take(blk);
+    L.g = take((size_t)L.NG * (size_t)L.ldl * 2);
     L.rows = take((size_t)N * sizeof(float));
     L.stats = take((size_t)L.C * 4 * sizeof(double));
     L.kl = take((size_t)L.C * 2 * sizeof(float));
     L.part = take(vjsd_workspace_bytes(L.C > 0 ? L.C : 1, 1));
     L.count = take(sizeof(double));
-    L.has_gw = L.C < N;
+    L.has_gw = L.NG < N;
     L.gw = take(L.has_gw ? (size_t)V * (size_t)dim * sizeof(float) : 0);
     L.total = o;
     return L;
@@ -663,15 +676,15 @@ int vlin_gemm(int64_t M, int64_t N, int64_t K, vlin_operand a, vlin_operand b, v
     return hip_status(vjsd::launch_gemm(g, (hipStream_t)stream));
 }
 
-size_t vljsd_workspace_bytes(int64_t N, int64_t V, int64_t dim_s, int64_t chunk) {
-    if (N < 0 || V < 1 || dim_s < 1 || chunk < 1) return 0;
-    return lin_layout(N, V, dim_s, chunk).total;
+size_t vljsd_workspace_bytes(int64_t N, int64_t V, int64_t dim_s, int64_t chunk, int64_t group) {
+    if (N < 0 || V < 1 || dim_s < 1 || chunk < 1 || group < 0) return 0;
+    return lin_layout(N, V, dim_s, chunk, group).total;
 }
 
 int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t V, double beta,
-          const vjsd_loss_opts *opts, int64_t chunk, void *workspace, float *out, void *grad_h,
-          int64_t ldgh, void *grad_w, int64_t ldgw, void *stream) {
-    if (N < 0 || N > MAX_ROWS || V < 1 || chunk < 1 || !out) return VJSD_ERR_ARG;
+          const vjsd_loss_opts *opts, int64_t chunk, int64_t group, void *workspace, float *out,
+          void *grad_h, int64_t ldgh, void *grad_w, int64_t ldgw, void *stream) {
+    if (N < 0 || N > MAX_ROWS || V < 1 || chunk < 1 || group < 0 || !out) return VJSD_ERR_ARG;
     if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
     LossCfg c;
     int e = loss_cfg(opts, &c);
@@ -702,11 +715,11 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
         return VJSD_OK;
     }
     if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return VJSD_ERR_ARG;
-    const LinLayout L = lin_layout(N, V, D, chunk);
+    const LinLayout L = lin_layout(N, V, D, chunk, group);
     char *ws = static_cast<char *>(workspace);
     float *ls = reinterpret_cast<float *>(ws + L.ls);
     float *lt = reinterpret_cast<float *>(ws + L.lt);
-    float *G = reinterpret_cast<float *>(ws + L.g);
+    uint16_t *G = reinterpret_cast<uint16_t *>(ws + L.g);
     float *rows = reinterpret_cast<float *>(ws + L.rows);
     double *stats = reinterpret_cast<double *>(ws + L.stats);
     float *kl = reinterpret_cast<float *>(ws + L.kl);
@@ -720,99 +733,101 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
     }
     float *rows_out = c.red == VJSD_REDUCE_NONE ? out : rows;
     const int mode = mode_of(beta);
-    const int64_t C = L.C, nblk = (N + C - 1) / C;
+    const int64_t C = L.C, NG = L.NG, ngroups = (N + NG - 1) / NG;
     const uint16_t *hs = static_cast<const uint16_t *>(student->h);
     const uint16_t *ht = static_cast<const uint16_t *>(teacher->h);
-    for (int64_t blk = 0; blk < nblk; ++blk) {
-        const int64_t n0 = blk * C, nb = N - n0 < C ? N - n0 : C;
-        // the block's logits, student and teacher
-        for (int side = 0; side < 2; ++side) {
-            const vlin_head *hd = side == 0 ? student : teacher;
-            vjsd::GemmArgs g;
-            g.M = nb;
-            g.N = V;
-            g.K = hd->dim;
-            g.a = (side == 0 ? hs : ht) + n0 * hd->ldh;
-            g.lda = hd->ldh;
-            g.b = hd->w;
-            g.ldb = hd->ldw;
-            g.c = side == 0 ? ls : lt;
-            g.ldc = L.ldl;
-            g.out = vjsd::GEMM_F32;
-            if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
-        }
-        // the block's per-token loss
-        Shard sh;
-        sh.start = 0;
-        sh.width = V;
-        sh.s = {ls, L.ldl, 0, 0};
-        sh.t = {lt, L.ldl, 0, 0};
-        sh.gs = {G, L.ldl, 0, 0};
-        sh.gt = {nullptr, 0, 0, 0};
-        vjsd::RowOpts rb = ro;
-        rb.mask = ro.mask ? ro.mask + n0 : nullptr;
-        if (mode != vjsd::INTERIOR) {
-            const int rev = mode == vjsd::REV_KL;
-            if ((e = hip_status(vjsd::launch_kl1(VJSD_F32, rev, sh, nb, part_of(part, 0, nb), st,
-                                                 rb))))
+    for (int64_t grp = 0; grp < ngroups; ++grp) {
+        const int64_t g0 = grp * NG, gn = N - g0 < NG ? N - g0 : NG;
+        for (int64_t n0 = g0; n0 < g0 + gn; n0 += C) {
+            const int64_t nb = g0 + gn - n0 < C ? g0 + gn - n0 : C;
+            // the block's logits, student and teacher
+            for (int side = 0; side < 2; ++side) {
+                const vlin_head *hd = side == 0 ? student : teacher;
+                vjsd::GemmArgs g;
+                g.M = nb;
+                g.N = V;
+                g.K = hd->dim;
+                g.a = (side == 0 ? hs : ht) + n0 * hd->ldh;
+                g.lda = hd->ldh;
+                g.b = hd->w;
+                g.ldb = hd->ldw;
+                g.c = side == 0 ? ls : lt;
+                g.ldc = L.ldl;
+                g.out = vjsd::GEMM_F32;
+                if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+            }
+            // the block's per-token loss
+            Shard sh;
+            sh.start = 0;
+            sh.width = V;
+            sh.s = {ls, L.ldl, 0, 0};
+            sh.t = {lt, L.ldl, 0, 0};
+            sh.gs = {G + (n0 - g0) * L.ldl, L.ldl, 0, 0};
+            sh.gt = {nullptr, 0, 0, 0};
+            vjsd::RowOpts rb = ro;
+            rb.mask = ro.mask ? ro.mask + n0 : nullptr;
+            if (mode != vjsd::INTERIOR) {
+                const int rev = mode == vjsd::REV_KL;
+                if ((e = hip_status(vjsd::launch_kl1(VJSD_F32, rev, sh, nb, part_of(part, 0, nb),
+                                                     st, rb))))
+                    return e;
+                if ((e = hip_status(vjsd::launch_kl1_merge(rev, part_of(part, 0, nb), 1, nb,
+                                                           stats, kl, rows_out + n0, st, rb))))
+                    return e;
+            } else if ((e = hip_status(vjsd::launch_fwd_fused(VJSD_F32, sh, nb, beta, stats, kl,
+                                                               rows_out + n0, st, rb)))) {
                 return e;
-            if ((e = hip_status(vjsd::launch_kl1_merge(rev, part_of(part, 0, nb), 1, nb, stats, kl,
-                                                       rows_out + n0, st, rb))))
+            }
+            if (!grads) continue;
+            // the block's logit gradient (bf16) for a unit upstream gradient of out[0]
+            vjsd::GradOpts go;
+            go.ks = ro.ks;
+            go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
+            go.scalar = true;
+            go.mask = rb.mask;
+            go.count = mean ? count : nullptr;
+            if ((e = hip_status(vjsd::launch_bwd_prep(mode, nb, stats, kl, beta, nullptr, part, st,
+                                                      go))))
                 return e;
-        } else if ((e = hip_status(vjsd::launch_fwd_fused(VJSD_F32, sh, nb, beta, stats, kl,
-                                                           rows_out + n0, st, rb)))) {
-            return e;
+            if ((e = hip_status(vjsd::launch_bwd_f32_to_bf16(mode, sh, nb, part, st)))) return e;
         }
         if (!grads) continue;
-        // the logit gradient of the block for a unit upstream gradient of out[0]
-        vjsd::GradOpts go;
-        go.ks = ro.ks;
-        go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
-        go.scalar = true;
-        go.mask = rb.mask;
-        go.count = mean ? count : nullptr;
-        if ((e = hip_status(vjsd::launch_bwd_prep(mode, nb, stats, kl, beta, nullptr, part, st,
-                                                  go))))
-            return e;
-        if ((e = hip_status(vjsd::launch_bwd(VJSD_F32, mode, sh, nb, part, st)))) return e;
-        if (grad_h) {  // G [nb][V] x w_s [V][D]
+        if (grad_h) {  // G [gn][V] x w_s [V][D]
             vjsd::GemmArgs g;
-            g.M = nb;
+            g.M = gn;
             g.N = D;
             g.K = V;
             g.a = G;
             g.lda = L.ldl;
-            g.a_f32 = 1;
             g.b = student->w;
             g.ldb = student->ldw;
             g.b_kmajor = 0;
-            g.c = static_cast<uint16_t *>(grad_h) + n0 * ldgh;
+            g.c = static_cast<uint16_t *>(grad_h) + g0 * ldgh;
             g.ldc = ldgh;
             g.out = vjsd::GEMM_BF16;
             if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
         }
-        if (grad_w) {  // G^T [V][nb] x h_s [nb][D], summed over the blocks in fp32
+        if (grad_w) {  // G^T [V][gn] x h_s [gn][D], summed over the groups in fp32
             vjsd::GemmArgs g;
             g.M = V;
             g.N = D;
-            g.K = nb;
+            g.K = gn;
             g.a = G;
             g.lda = L.ldl;
-            g.a_f32 = 1;
             g.a_kmajor = 0;
-            g.b = hs + n0 * student->ldh;
+            g.b = hs + g0 * student->ldh;
             g.ldb = student->ldh;
             g.b_kmajor = 0;
-            if (nblk == 1 || blk == nblk - 1) {
+            if (ngroups == 1 || grp == ngroups - 1) {
                 g.c = grad_w;
                 g.ldc = ldgw;
-                g.out = nblk == 1 ? vjsd::GEMM_BF16 : vjsd::GEMM_BF16_ACC;
+                g.out = ngroups == 1 ? vjsd::GEMM_BF16 : vjsd::GEMM_BF16_ACC;
                 g.addend = gw;
                 g.ldadd = D;
             } else {
                 g.c = gw;
                 g.ldc = D;
-                g.out = blk == 0 ? vjsd::GEMM_F32 : vjsd::GEMM_F32_ACC;
+                g.out = grp == 0 ? vjsd::GEMM_F32 : vjsd::GEMM_F32_ACC;
             }
             if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
         }

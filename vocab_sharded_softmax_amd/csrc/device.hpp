@@ -158,6 +158,14 @@ __device__ __forceinline__ void store_vec(typename D::T *p, const float (&x)[D::
     st16<STREAM>(p, narrow<D>(x));
 }
 
+// four fp32 values as four bf16 (nearest even) in 8 bytes; p 8-byte aligned
+__device__ __forceinline__ void st_bf16x4(uint16_t *p, const float (&x)[4]) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[0], x[1]}, bf16x2));
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[2], x[3]}, bf16x2));
+    *reinterpret_cast<u32x2 *>(p) = u32x2{lo, hi};
+}
+
 // Round-to-nearest-even stores of fp32 results in the storage format.
 template <class D>
 __device__ __forceinline__ void store1(typename D::T *p, float v);

@@ -11,213 +11,350 @@
 //
 // Operands: A(i, k) at a[i*lda + k] ("k-major") or a[k*lda + i] ("i-major"), bf16 or
 // fp32; B(j, k) at b[j*ldb + k] or b[k*ldb + j], bf16.  Every operand pointer is 16-byte
-// aligned and every leading dimension a multiple of 8 elements (4 for fp32), checked
-// by the host.
+// aligned, every leading dimension a multiple of 8 elements (4 for fp32), and every
+// operand readable over whole rows of ld elements (checked by the host).
 //
-// Tiling: a 128 x 128 output tile per workgroup of four waves (2 x 2, 64 x 64 each,
-// 2 x 2 MFMA tiles of 32 x 32), k in steps of 64 through double-buffered LDS.  A
-// k-major operand is stored k-major in LDS (rows padded to 144 bytes, so the 16-byte
-// fragment reads of eight consecutive rows hit disjoint banks); an i/j-major operand
-// is stored as loaded (rows of 128 elements padded to 264 bytes) and its fragments
-// are gathered element by element.  The workgroup -> tile map gives each of the eight
-// XCDs a contiguous range of tiles in i-fastest order, so the tiles that share a
-// panel of B run on one XCD, close in time, out of its L2.
+// Tiling: a 256 x 256 output tile per workgroup of four waves (2 x 2, 128 x 128 each,
+// 4 x 4 MFMA tiles of 32 x 32, 256 fp32 accumulators per lane in AGPRs), k in steps
+// of 64 through double-buffered LDS (144 KiB: one workgroup per CU).  When an operand
+// has its rows contiguous (and both are bf16) the global loads run two k-steps ahead
+// (two register stages), so a load has two steps of products to arrive in.  Every operand is
+// stored k-major in LDS, rows padded to 144 bytes, so each MFMA fragment is one
+// 16-byte read and the reads of eight consecutive rows hit disjoint banks.  A k-major
+// operand is staged in 16-byte chunks along k; an operand whose rows are contiguous
+// (k strided) is staged as 8 (k) x 8 (rows) blocks and transposed in registers into
+// 16-byte k-major rows.  Tiles are ordered so that
+// consecutive ones share a panel of the larger operand (that panel is then read from
+// HBM once), and the workgroup -> tile map gives each of the eight XCDs a contiguous
+// range of that order, so the sharing happens inside one XCD's L2.
 #include "kernels.hpp"
 
 namespace vjsd {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TM = 128, TN = 128, TK = 64;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int GTHREADS = 256;
-constexpr int LDK = TK + 8;    // k-major LDS row: 72 bf16 = 144 bytes
-constexpr int LDI = 128 + 4;   // i/j-major LDS row: 132 bf16 = 264 bytes
-constexpr int KM_ELEMS = TM * LDK;  // 9216
-constexpr int IM_ELEMS = TK * LDI;  // 8448
-constexpr int OP_ELEMS = KM_ELEMS > IM_ELEMS ? KM_ELEMS : IM_ELEMS;
+constexpr int LDR = BK + 8;               // LDS row: 72 bf16 = 144 bytes
+constexpr int OP_ELEMS = 256 * LDR;       // one operand's stage
+constexpr int WTM = 4, WTN = 4;           // MFMA tiles per wave (rows, columns)
 
-// bf16 bits of an fp32 value, round to nearest even (NaN kept quiet)
-__device__ __forceinline__ unsigned short bf16_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
-    return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+// two fp32 values as a bf16 pair (nearest even), the first in the low half
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// One operand's tile: ROWS = 128 rows (i or j) by TK = 64 k, loaded into registers,
-// then stored to LDS in bf16.  F32: fp32 storage; KMAJ: k contiguous in memory.
+__device__ __forceinline__ unsigned short bf16_bits(float f) {
+    return (unsigned short)(pack_bf16(f, 0.0f) & 0xffffu);
+}
+
+// One operand's 256 (rows) x 64 (k) tile, loaded into registers, then written to LDS
+// in bf16, k-major.  Primary template: k contiguous in memory.
 template <bool F32, bool KMAJ>
-struct Tile {
-    // elements per 16-byte chunk, chunks per thread
-    static constexpr int EPC = F32 ? 4 : 8;
-    static constexpr int NCH = TM * TK / EPC / GTHREADS;
+struct Stage {
+    static constexpr int EPC = F32 ? 4 : 8;      // elements per 16-byte chunk
+    static constexpr int CPR = BK / EPC;         // chunks per row
+    static constexpr int NCH = 256 * CPR / GTHREADS;
     u32x4 r[NCH];
-    bool full[NCH];
 
-    // chunk q of the tile: (row, k) of its first element (k-major) or (k, row)
-    __device__ __forceinline__ static void coords(int q, int &row, int &k) {
-        if (KMAJ) {
-            constexpr int CPR = TK / EPC;  // chunks per row
-            row = q / CPR;
-            k = (q % CPR) * EPC;
-        } else {
-            constexpr int CPR = TM / EPC;
-            k = q / CPR;
-            row = (q % CPR) * EPC;
-        }
-    }
-
-    // rows [r0, r0 + 128) (of R) and k [k0, k0 + 64) (of K); zeros outside
+    // CHECKED false: the whole 256 x 64 tile is inside the operand.  Chunk c of a
+    // thread sits 256 / CPR rows below chunk c - 1: a wave-uniform base plus one
+    // per-lane offset.  CHECKED true: a row past the operand reads row R - 1 and a
+    // chunk at or past K reads the last chunk of its row (a chunk starts at a multiple
+    // of EPC < ld, so it never leaves its row's ld elements); elements outside the
+    // operand are then zeroed.
+    template <bool CHECKED>
     __device__ __forceinline__ void load(const void *p, int64_t ld, int64_t r0, int64_t R,
                                          int64_t k0, int64_t K) {
+        constexpr int ES = F32 ? 4 : 2;
+        const int64_t lr = threadIdx.x / CPR, lk = (threadIdx.x % CPR) * EPC;
+        if (!CHECKED) {
+            const uint32_t lane_off = (uint32_t)((lr * ld + lk) * ES);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const char *base = static_cast<const char *>(p) +
+                                   ((r0 + (int64_t)c * (GTHREADS / CPR)) * ld + k0) * ES;
+                r[c] = ld16<false>(base + lane_off);
+            }
+            return;
+        }
+        const int64_t klast = (K - 1) / EPC * EPC;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            int row, k;
-            coords(threadIdx.x + c * GTHREADS, row, k);
-            const int64_t gr = r0 + row, gk = k0 + k;
-            // a chunk runs along k (k-major) or along the rows (i/j-major)
-            const int64_t lim = KMAJ ? K - gk : R - gr;
-            const bool inb = KMAJ ? gr < R : gk < K;
-            const int64_t off = KMAJ ? gr * ld + gk : gk * ld + gr;
-            full[c] = inb && lim >= EPC;
-            if (full[c]) {
-                r[c] = F32 ? ld16<false>(static_cast<const float *>(p) + off)
-                           : ld16<false>(static_cast<const unsigned short *>(p) + off);
-            } else {
-                uint32_t w[4] = {0, 0, 0, 0};
-                if (inb && lim > 0) {
-                    for (int e = 0; e < EPC && e < lim; ++e) {
-                        if (F32) {
-                            w[e] = __float_as_uint(static_cast<const float *>(p)[off + e]);
-                        } else {
-                            const uint32_t h = static_cast<const unsigned short *>(p)[off + e];
-                            w[e >> 1] |= h << (16 * (e & 1));
-                        }
-                    }
+            const int64_t gr = r0 + lr + (int64_t)c * (GTHREADS / CPR), gk = k0 + lk;
+            const int64_t ar = gr < R ? gr : R - 1, ak = gk < klast ? gk : klast;
+            u32x4 v = ld16<false>(static_cast<const char *>(p) + (ar * ld + ak) * ES);
+            const bool rok = gr < R;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (F32) {
+                    if (!(rok && gk + i < K)) v[i] = 0u;
+                } else {
+                    const uint32_t m = ((rok && gk + 2 * i < K) ? 0x0000ffffu : 0u) |
+                                       ((rok && gk + 2 * i + 1 < K) ? 0xffff0000u : 0u);
+                    v[i] &= m;
                 }
-                r[c] = u32x4{w[0], w[1], w[2], w[3]};
             }
+            r[c] = v;
         }
     }
 
-    // bf16 into the LDS tile s (k-major rows of LDK, or k rows of LDI)
     __device__ __forceinline__ void store(unsigned short *s) const {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            int row, k;
-            coords(threadIdx.x + c * GTHREADS, row, k);
-            unsigned short *d = KMAJ ? s + row * LDK + k : s + k * LDI + row;
+            const int q = threadIdx.x + c * GTHREADS;
+            unsigned short *d = s + (q / CPR) * LDR + (q % CPR) * EPC;
             if (F32) {
-                u16x4 h;
-                h[0] = bf16_bits(__uint_as_float(r[c][0]));
-                h[1] = bf16_bits(__uint_as_float(r[c][1]));
-                h[2] = bf16_bits(__uint_as_float(r[c][2]));
-                h[3] = bf16_bits(__uint_as_float(r[c][3]));
-                *reinterpret_cast<u16x4 *>(d) = h;  // 8-byte aligned in both layouts
-            } else if (KMAJ) {
-                *reinterpret_cast<u32x4 *>(d) = r[c];  // 16-byte aligned
-            } else {
-                // i/j-major rows are 264 bytes: 8-byte aligned only
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                reinterpret_cast<u32x2 *>(d)[0] = u32x2{r[c][0], r[c][1]};
-                reinterpret_cast<u32x2 *>(d)[1] = u32x2{r[c][2], r[c][3]};
+                *reinterpret_cast<u32x2 *>(d) =
+                    u32x2{pack_bf16(__uint_as_float(r[c][0]), __uint_as_float(r[c][1])),
+                          pack_bf16(__uint_as_float(r[c][2]), __uint_as_float(r[c][3]))};
+            } else {
+                *reinterpret_cast<u32x4 *>(d) = r[c];
             }
+        }
+    }
+};
+
+// Rows contiguous in memory, k strided: thread t owns the block k in
+// [8 (t % 8), + 8) x rows [8 (t / 8), + 8) of the tile.
+template <bool F32>
+struct Stage<F32, false> {
+    static constexpr int EPC = F32 ? 4 : 8;
+    static constexpr int W = 8 / EPC;  // 16-byte loads per k-row of the block
+    static_assert((BK / 8) * (256 / 8) == GTHREADS, "one block per thread");
+    u32x4 r[8][W];
+
+    // CHECKED as for the k-major stage, with the roles of rows and k swapped: a k-row
+    // at or past K reads k-row K - 1, a chunk at or past R the last chunk of its k-row.
+    template <bool CHECKED>
+    __device__ __forceinline__ void load(const void *p, int64_t ld, int64_t r0, int64_t R,
+                                         int64_t k0, int64_t K) {
+        const int kb = threadIdx.x & 7, rb = threadIdx.x >> 3;
+        constexpr int ES = F32 ? 4 : 2;
+        if (!CHECKED) {  // wave-uniform base per load plus one per-lane offset
+            const uint32_t lane_off = (uint32_t)((8 * kb * ld + 8 * rb) * ES);
+#pragma unroll
+            for (int kr = 0; kr < 8; ++kr)
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const char *base = static_cast<const char *>(p) +
+                                       ((k0 + kr) * ld + r0 + w * EPC) * ES;
+                    r[kr][w] = ld16<false>(base + lane_off);
+                }
+            return;
+        }
+        const int64_t rlast = (R - 1) / EPC * EPC;
+#pragma unroll
+        for (int kr = 0; kr < 8; ++kr) {
+            const int64_t gk = k0 + 8 * kb + kr;
+            const int64_t ak = gk < K ? gk : K - 1;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const int64_t gr = r0 + 8 * rb + w * EPC;
+                const int64_t ar = gr < rlast ? gr : rlast;
+                u32x4 v = ld16<false>(static_cast<const char *>(p) + (ak * ld + ar) * ES);
+                const bool kok = gk < K;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (F32) {
+                        if (!(kok && gr + i < R)) v[i] = 0u;
+                    } else {
+                        const uint32_t m = ((kok && gr + 2 * i < R) ? 0x0000ffffu : 0u) |
+                                           ((kok && gr + 2 * i + 1 < R) ? 0xffff0000u : 0u);
+                        v[i] &= m;
+                    }
+                }
+                r[kr][w] = v;
+            }
+        }
+    }
+
+    // element (k = kr, row = j) of the block as fp32 / bf16 bits
+    __device__ __forceinline__ float f32_at(int kr, int j) const {
+        const uint32_t u = r[kr][j / 4][j % 4];
+        return __uint_as_float(u);
+    }
+    __device__ __forceinline__ uint32_t half_at(int kr, int j) const {
+        const uint32_t u = r[kr][0][j / 2];
+        return (j & 1) ? (u >> 16) : (u & 0xffffu);
+    }
+
+    __device__ __forceinline__ void store(unsigned short *s) const {
+        const int kb = threadIdx.x & 7, rb = threadIdx.x >> 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (F32) o[q] = pack_bf16(f32_at(2 * q, j), f32_at(2 * q + 1, j));
+                else o[q] = half_at(2 * q, j) | (half_at(2 * q + 1, j) << 16);
+            }
+            *reinterpret_cast<u32x4 *>(s + (8 * rb + j) * LDR + 8 * kb) =
+                u32x4{o[0], o[1], o[2], o[3]};
         }
     }
 };
 
 // MFMA operand of rows [base, base + 32), k [kk, kk + 16): lane l holds row
 // base + l % 32, k = kk + 8 * (l / 32) + e, e = 0..7.
-template <bool KMAJ>
 __device__ __forceinline__ bf16x8 frag(const unsigned short *s, int base, int kk) {
     const int l = threadIdx.x & 63;
-    const int row = base + (l & 31), k = kk + 8 * (l >> 5);
-    if (KMAJ) {
-        const u16x8 v = *reinterpret_cast<const u16x8 *>(s + row * LDK + k);
-        return __builtin_bit_cast(bf16x8, v);
-    } else {
-        u16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = s[(k + e) * LDI + row];
-        return __builtin_bit_cast(bf16x8, v);
-    }
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(s + (base + (l & 31)) * LDR + kk + 8 * (l >> 5));
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Tile (m0, n0) at position t of the order.  The larger operand's panels are taken
+// GL at a time (the outer group), and within that group the other operand's panels GS
+// at a time, so the 32 tiles an XCD runs at once form a GS x GL block: each of its
+// panels is fetched once for the block, and each of the larger operand's panels once
+// from HBM for all of the other operand.
+__device__ __forceinline__ void tile_of(int64_t t, int64_t mt, int64_t nt, int a_larger,
+                                        int64_t &m0, int64_t &n0) {
+    constexpr int64_t GL = 8, GS = 4;
+    const int64_t nl = a_larger ? mt : nt, ns = a_larger ? nt : mt;  // larger / smaller
+    const int64_t gi = t / (ns * GL), lb = gi * GL;
+    const int64_t gl = nl - lb < GL ? nl - lb : GL;
+    const int64_t u = t - gi * ns * GL;
+    const int64_t si = u / (GS * gl), sb = si * GS;
+    const int64_t gs = ns - sb < GS ? ns - sb : GS;
+    const int64_t v = u - si * GS * gl;
+    const int64_t is = sb + v % gs, il = lb + v / gs;
+    m0 = (a_larger ? il : is) * BM;
+    n0 = (a_larger ? is : il) * BN;
 }
 
 template <bool AF32, bool AKM, bool BKM, int OUT>
-__global__ __launch_bounds__(GTHREADS) void k_gemm(GemmArgs g) {
+__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) unsigned short lds[2][2][OP_ELEMS];
     // tile of this workgroup: XCD x = blockIdx % 8 owns tiles [x * per, (x + 1) * per)
-    const int64_t mt = (g.M + TM - 1) / TM, nt = (g.N + TN - 1) / TN, T = mt * nt;
+    // of an order in which consecutive tiles share a panel of the larger operand
+    const int64_t mt = (g.M + BM - 1) / BM, nt = (g.N + BN - 1) / BN, T = mt * nt;
     const int64_t per = (T + 7) / 8;
     const int64_t t = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (t >= T) return;
-    const int64_t m0 = (t % mt) * TM, n0 = (t / mt) * TN;
+    int64_t m0, n0;
+    tile_of(t, mt, nt, g.n_fastest, m0, n0);
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    f32x16 acc[2][2];
+    const int wm = (wave >> 1) * (32 * WTM), wn = (wave & 1) * (32 * WTN);
+    f32x16 acc[WTM][WTN];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < WTM; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < WTN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    Tile<AF32, AKM> ta;
-    Tile<false, BKM> tb;
-    const int64_t nk = (g.K + TK - 1) / TK;
-    if (nk > 0) {
-        ta.load(g.a, g.lda, m0, g.M, 0, g.K);
-        tb.load(g.b, g.ldb, n0, g.N, 0, g.K);
-        ta.store(lds[0][0]);
-        tb.store(lds[0][1]);
-    }
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {  // next stage in flight during this stage's products
-            ta.load(g.a, g.lda, m0, g.M, (kt + 1) * TK, g.K);
-            tb.load(g.b, g.ldb, n0, g.N, (kt + 1) * TK, g.K);
+    const int64_t nk = (g.K + BK - 1) / BK;
+    const bool rows_in = m0 + BM <= g.M && n0 + BN <= g.N;
+    // a stage with every element inside both operands is loaded without tests
+    auto load_stage = [&](auto &sa, auto &sb, int64_t k0) {
+        if (rows_in && k0 + BK <= g.K) {
+            sa.template load<false>(g.a, g.lda, m0, g.M, k0, g.K);
+            sb.template load<false>(g.b, g.ldb, n0, g.N, k0, g.K);
+        } else {
+            sa.template load<true>(g.a, g.lda, m0, g.M, k0, g.K);
+            sb.template load<true>(g.b, g.ldb, n0, g.N, k0, g.K);
         }
-        const unsigned short *sa = lds[cur][0], *sb = lds[cur][1];
+    };
+    bf16x8 fa[2][WTM], fb[2][WTN];
+    auto read_frags = [&](int buf, const unsigned short *la, const unsigned short *lb, int kk) {
 #pragma unroll
-        for (int kk = 0; kk < TK; kk += 16) {
-            bf16x8 fa[2], fb[2];
+        for (int a = 0; a < WTM; ++a) fa[buf][a] = frag(la, wm + 32 * a, kk);
 #pragma unroll
-            for (int a = 0; a < 2; ++a) fa[a] = frag<AKM>(sa, wm + 32 * a, kk);
+        for (int b = 0; b < WTN; ++b) fb[buf][b] = frag(lb, wn + 32 * b, kk);
+    };
+    // the products of one LDS stage; sub-step 0's fragments are already in fa/fb[0]
+    auto products = [&](const unsigned short *la, const unsigned short *lb) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b) fb[b] = frag<BKM>(sb, wn + 32 * b, kk);
+        for (int s = 0; s < BK / 16; ++s) {
+            // the next sub-step's fragments are read while this one's products run
+            if (s + 1 < BK / 16) read_frags((s + 1) & 1, la, lb, 16 * (s + 1));
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < WTM; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b],
-                                                                         0, 0, 0);
+                for (int b = 0; b < WTN; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][a], fb[s & 1][b],
+                                                                         acc[a][b], 0, 0, 0);
         }
-        if (more) {
-            ta.store(lds[cur ^ 1][0]);
-            tb.store(lds[cur ^ 1][1]);
+    };
+    // one register stage when an operand is fp32 or both are k-major (their staging
+    // registers leave no room for a second); two otherwise
+    if constexpr (AF32 || (AKM && BKM)) {
+        Stage<AF32, AKM> sa;
+        Stage<false, BKM> sb;
+        if (nk > 0) {
+            load_stage(sa, sb, 0);
+            sa.store(lds[0][0]);
+            sb.store(lds[0][1]);
         }
         __syncthreads();
+        if (nk > 0) read_frags(0, lds[0][0], lds[0][1], 0);
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < nk;
+            if (more) load_stage(sa, sb, (kt + 1) * BK);  // in flight during the products
+            products(lds[cur][0], lds[cur][1]);
+            if (more) {
+                sa.store(lds[cur ^ 1][0]);
+                sb.store(lds[cur ^ 1][1]);
+            }
+            __syncthreads();
+            if (more) read_frags(0, lds[cur ^ 1][0], lds[cur ^ 1][1], 0);
+        }
+    } else {  // two register stages: stage s is loaded two steps before its products
+        Stage<false, AKM> sa0, sa1;
+        Stage<false, BKM> sb0, sb1;
+        if (nk > 0) load_stage(sa0, sb0, 0);
+        if (nk > 1) load_stage(sa1, sb1, BK);
+        if (nk > 0) {
+            sa0.store(lds[0][0]);
+            sb0.store(lds[0][1]);
+        }
+        __syncthreads();
+        if (nk > 0) read_frags(0, lds[0][0], lds[0][1], 0);
+        // step kt: its data is in lds[P]; register set P (free since its store) takes
+        // stage kt + 2; set 1 - P (stage kt + 1) goes to lds[1 - P]
+        auto step = [&](auto &sa_p, auto &sb_p, auto &sa_q, auto &sb_q, int P, int64_t kt) {
+            if (kt + 2 < nk) load_stage(sa_p, sb_p, (kt + 2) * BK);
+            products(lds[P][0], lds[P][1]);
+            if (kt + 1 < nk) {
+                sa_q.store(lds[P ^ 1][0]);
+                sb_q.store(lds[P ^ 1][1]);
+            }
+            __syncthreads();
+            if (kt + 1 < nk) read_frags(0, lds[P ^ 1][0], lds[P ^ 1][1], 0);
+        };
+        int64_t kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            step(sa0, sb0, sa1, sb1, 0, kt);
+            step(sa1, sb1, sa0, sb0, 1, kt + 1);
+        }
+        if (kt < nk) step(sa0, sb0, sa1, sb1, 0, kt);
     }
 
     // result element r of MFMA tile (a, b): row 8 (r / 4) + 4 (lane / 32) + r % 4,
-    // column lane % 32
+    // column lane % 32; one row pointer per output row
+    const int64_t jl = n0 + wn + (lane & 31);
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < WTM; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int r = 0; r < 16; ++r) {
+            const int64_t i = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (!rows_in && i >= g.M) continue;
+            const int64_t row = i * g.ldc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t i = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int64_t j = n0 + wn + 32 * b + (lane & 31);
-                if (i >= g.M || j >= g.N) continue;
+            for (int b = 0; b < WTN; ++b) {
+                const int64_t j = jl + 32 * b;
+                if (!rows_in && j >= g.N) continue;
                 const float v = acc[a][b][r];
-                const int64_t o = i * g.ldc + j;
+                const int64_t o = row + j;
                 if (OUT == GEMM_F32) {
                     static_cast<float *>(g.c)[o] = v;
                 } else if (OUT == GEMM_F32_ACC) {
@@ -228,11 +365,12 @@ __global__ __launch_bounds__(GTHREADS) void k_gemm(GemmArgs g) {
                     static_cast<unsigned short *>(g.c)[o] = bf16_bits(g.addend[i * g.ldadd + j] + v);
                 }
             }
+        }
 }
 
 template <bool AF32, bool AKM, bool BKM>
 hipError_t gemm_out(const GemmArgs &g, hipStream_t st) {
-    const int64_t T = ((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
+    const int64_t T = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     const dim3 grid((unsigned)(8 * ((T + 7) / 8)));
     switch (g.out) {
         case GEMM_F32:
@@ -255,8 +393,11 @@ hipError_t gemm_out(const GemmArgs &g, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs &g, hipStream_t st) {
-    if (g.M == 0 || g.N == 0) return hipSuccess;
+hipError_t launch_gemm(const GemmArgs &gin, hipStream_t st) {
+    if (gin.M == 0 || gin.N == 0) return hipSuccess;
+    GemmArgs g = gin;
+    // consecutive tiles share a panel of the operand with more bytes
+    g.n_fastest = (double)g.M * (g.a_f32 ? 4 : 2) > (double)g.N * 2;
     if (g.a_f32) {
         if (g.a_kmajor) return g.b_kmajor ? gemm_out<true, true, true>(g, st)
                                           : gemm_out<true, true, false>(g, st);

@@ -18,6 +18,8 @@
 // so the per-element work touches only O(1)-sized quantities, never log Z; u - L and
 // (u_s - L) - r are differences of nearby numbers and come out (nearly) exact.
 #include "divergence.hpp"
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "sweep.hpp"
 
@@ -121,10 +123,13 @@ __global__ void k_div_finalize(int mode, const float *__restrict__ part, int S, 
 
 // ---- backward ---------------------------------------------------------------------
 
-template <class D, int MODE, bool WS, bool WT>
+// DG: storage of the gradients (the input's, or bf16 for fp32 input: the logit
+// gradient the fused-linear products consume)
+template <class D, int MODE, bool WS, bool WT, class DG = D>
 struct OpBwd {
     using T = typename D::T;
-    T *gs, *gt;
+    using TG = typename DG::T;
+    TG *gs, *gt;
     float ks;  // log2 e / temperature
     float cs, ct, bf, gam;
     float Cs, Ct;  // gradient scales
@@ -154,14 +159,17 @@ struct OpBwd {
                     ot[i] = fmaf(Gt, et, -(Gs * es));
                 }
             }
-            if constexpr (W == D::VEC) {
+            if constexpr (W == D::VEC && std::is_same<D, DG>::value) {
                 if (WS) store_vec<D, true>(gs + col[j], os);
                 if (WT) store_vec<D, true>(gt + col[j], ot);
+            } else if constexpr (W == D::VEC) {  // four fp32 values as 8 bytes of bf16
+                if (WS) st_bf16x4(gs + col[j], os);
+                if (WT) st_bf16x4(gt + col[j], ot);
             } else {
 #pragma unroll
                 for (int i = 0; i < W; ++i) {
-                    if (WS) store1<D>(gs + col[j] + i, os[i]);
-                    if (WT) store1<D>(gt + col[j] + i, ot[i]);
+                    if (WS) store1<DG>(gs + col[j] + i, os[i]);
+                    if (WT) store1<DG>(gt + col[j] + i, ot[i]);
                 }
             }
         }
@@ -214,25 +222,26 @@ __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats
 
 // One wave per row chunk of cw columns; the chunks of a row are consecutive workgroups,
 // so the whole grid streams through memory in order.
-template <class D, int MODE, bool WS, bool WT>
+template <class D, int MODE, bool WS, bool WT, class DG = D>
 __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowMView gsv,
                                                     RowMView gtv, int64_t w, int64_t cw,
                                                     int64_t nchunk, const float *__restrict__ rowc) {
     using T = typename D::T;
+    using TG = typename DG::T;
     const int64_t b = blockIdx.x;
     const int64_t r = b / nchunk;
     const int64_t c0 = (b - r * nchunk) * cw;
     const int64_t n = w - c0 < cw ? w - c0 : cw;
     const float *k = rowc + r * ROWC;
-    T *gs = WS ? row_ptr<T>(gsv, r) + c0 : nullptr;
-    T *gt = WT ? row_ptr<T>(gtv, r) + c0 : nullptr;
+    TG *gs = WS ? row_ptr<TG>(gsv, r) + c0 : nullptr;
+    TG *gt = WT ? row_ptr<TG>(gtv, r) + c0 : nullptr;
     if (k[ROWC_UNDEFINED] != 0.0f) {  // no distribution, or dropped: exactly zero gradient
-        if (WS) zero_span<D, GRAD_BLOCK>(gs, n);
-        if (WT) zero_span<D, GRAD_BLOCK>(gt, n);
+        if (WS) zero_span<DG, GRAD_BLOCK>(gs, n);
+        if (WT) zero_span<DG, GRAD_BLOCK>(gt, n);
         return;
     }
     const T *s = row_ptr<T>(sv, r) + c0, *t = row_ptr<T>(tv, r) + c0;
-    OpBwd<D, MODE, WS, WT> op;
+    OpBwd<D, MODE, WS, WT, DG> op;
     op.gs = gs;
     op.gt = gt;
     op.ks = k[ROWC_KS];
@@ -248,7 +257,11 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
     op.Gt = k[9];
     // the vector path needs every view of the chunk at the same offset inside 16 bytes;
     // inputs and gradients are touched once, so loads and stores stream
-    sweep<D, 1, true, GRAD_BLOCK, true>(s, t, n, head_len<T>(n, s, t, gs, gt), op);
+    // (a bf16 gradient of fp32 input sits at the same element offsets, 8-byte aligned
+    // where the input is 16-byte aligned: the inputs alone fix the head)
+    const int64_t h = std::is_same<D, DG>::value ? head_len<T>(n, s, t, gs, gt)
+                                                 : head_len<T>(n, s, t);
+    sweep<D, 1, true, GRAD_BLOCK, true>(s, t, n, h, op);
 }
 
 template <class D, int MODE>
@@ -272,6 +285,16 @@ hipError_t bwd_k(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) 
     const Chunks ch = grad_chunks(N, sh.width, sizeof(typename D::T));
     if (ch.nchunk == 0) return hipSuccess;
     hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)(N * ch.nchunk)),
+                       dim3(GRAD_BLOCK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
+                       ch.nchunk, rowc);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t bwd_g16(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
+    const Chunks ch = grad_chunks(N, sh.width, sizeof(float));
+    if (ch.nchunk == 0) return hipSuccess;
+    hipLaunchKernelGGL((k_bwd<F32, MODE, true, false, BF16>), dim3((unsigned)(N * ch.nchunk)),
                        dim3(GRAD_BLOCK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
                        ch.nchunk, rowc);
     return hipGetLastError();
@@ -320,6 +343,13 @@ hipError_t launch_bwd_prep(int mode, int64_t N, const double *stats, const float
     hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, mode, N,
                        stats, kl, beta, grad, rowc, g);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32_to_bf16(int mode, const Shard &sh, int64_t N, const float *rowc,
+                                  hipStream_t st) {
+    if (mode == INTERIOR) return bwd_g16<INTERIOR>(sh, N, rowc, st);
+    if (mode == FWD_KL) return bwd_g16<FWD_KL>(sh, N, rowc, st);
+    return bwd_g16<REV_KL>(sh, N, rowc, st);
 }
 
 hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const float *rowc,

@@ -67,6 +67,10 @@ hipError_t launch_bwd_prep(int mode, int64_t N, const double *stats, const float
                            const GradOpts &g = GradOpts());
 hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const float *rowc,
                       hipStream_t st);
+// the same for fp32 logits, writing only the student gradient, in bf16 (nearest even);
+// the gradient view must be 8-byte aligned wherever the input view is 16-byte aligned
+hipError_t launch_bwd_f32_to_bf16(int mode, const Shard &sh, int64_t N, const float *rowc,
+                                  hipStream_t st);
 
 // single-pass KL forward: per-shard online partials, then the merge into stats/kl/loss
 hipError_t launch_kl1(int dtype, int reverse, const Shard &sh, int64_t N, float *part_k,
@@ -160,6 +164,7 @@ struct GemmArgs {
     int out = GEMM_F32;
     const float *addend = nullptr;  // GEMM_BF16_ACC: fp32, element (i, j) at addend[i*ldadd + j]
     int64_t ldadd = 0;
+    int n_fastest = 0;  // tile order (set by launch_gemm)
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
 // p[i] *= g[0] over n values of dtype 0 (fp32) or 2 (bf16); p 16-byte aligned

@@ -421,21 +421,21 @@ class _LinearJSD(torch.autograd.Function):
     actual one in the backward."""
 
     @staticmethod
-    def forward(ctx, beta, temperature, scale_t2, reduction, mask, chunk, hs, ws, ht, wt):
+    def forward(ctx, beta, temperature, scale_t2, reduction, mask, chunk, group, hs, ws, ht, wt):
         N, V = hs.shape[0], ws.shape[0]
         dev = hs.device
-        want_h = ctx.needs_input_grad[6] and reduction != "none"
-        want_w = ctx.needs_input_grad[7] and reduction != "none"
+        want_h = ctx.needs_input_grad[7] and reduction != "none"
+        want_w = ctx.needs_input_grad[8] and reduction != "none"
         student = _abi.lin_head(hs, ws, "student")
         teacher = _abi.lin_head(ht, wt, "teacher")
         opts = _abi.loss_opts(N, temperature, scale_t2, mask, reduction)
         C = max(1, min(int(chunk), max(N, 1)))
-        nbytes = _abi.vljsd_workspace_bytes(N, V, hs.shape[1], C)
+        nbytes = _abi.vljsd_workspace_bytes(N, V, hs.shape[1], C, group)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
         out = torch.empty((N if reduction == "none" else 1,), dtype=torch.float32, device=dev)
         gh = torch.empty(hs.shape, dtype=hs.dtype, device=dev) if want_h else None
         gw = torch.empty(ws.shape, dtype=ws.dtype, device=dev) if want_w else None
-        _abi.vljsd(student, teacher, N, V, beta, opts, C, workspace, out, gh, gw)
+        _abi.vljsd(student, teacher, N, V, beta, opts, C, workspace, out, gh, gw, group=group)
         del workspace
         ctx.save_for_backward(gh, gw)
         ctx.used = False
@@ -454,12 +454,12 @@ class _LinearJSD(torch.autograd.Function):
             _abi.vlin_scale(gh, g)
         if gw is not None:
             _abi.vlin_scale(gw, g)
-        return (None, None, None, None, None, None, gh, gw, None, None)
+        return (None, None, None, None, None, None, None, gh, gw, None, None)
 
 
 def linear_jsd(student_hidden, student_head, teacher_hidden, teacher_head, beta: float = 0.5, *,
                temperature: float = 1.0, scale_t2: bool = False, mask=None,
-               reduction: str = "mean", chunk: int = 4096) -> torch.Tensor:
+               reduction: str = "mean", chunk: int = 4096, group: int = 0) -> torch.Tensor:
     """Fused-linear distillation loss: ``jsd_loss`` on the logits ``h @ W^T`` of the
     student and the teacher, evaluated ``chunk`` tokens at a time so that the full
     ``[N, V]`` logits never exist (the fused-linear divergence [JSD-PR, Scope and
@@ -472,7 +472,8 @@ def linear_jsd(student_hidden, student_head, teacher_hidden, teacher_head, beta:
     student's hidden states and head weight and need ``reduction`` "sum" or "mean";
     "none" returns per-token losses without gradients.  The logit products run on the
     matrix cores in bf16 with fp32 accumulation; the logit gradient is rounded to bf16
-    for the two gradient products, as a bf16 model's backward rounds it.
+    for the two gradient products, as a bf16 model's backward rounds it, and kept for
+    ``group`` tokens at a time (whole chunks; 0: as many as fit 4 GiB).
     """
     beta = float(beta)
     if not (0.0 <= beta <= 1.0):
@@ -484,6 +485,8 @@ def linear_jsd(student_hidden, student_head, teacher_hidden, teacher_head, beta:
         raise ValueError(f"reduction must be one of {sorted(_abi.REDUCTIONS)}")
     if int(chunk) < 1:
         raise ValueError("chunk must be a positive number of tokens")
+    if int(group) < 0:
+        raise ValueError("group must be a number of tokens (0: automatic)")
     if teacher_hidden.requires_grad or teacher_head.requires_grad:
         raise ValueError("the teacher is a constant: pass teacher tensors without requires_grad "
                          "(detach them)")
@@ -502,6 +505,6 @@ def linear_jsd(student_hidden, student_head, teacher_hidden, teacher_head, beta:
         m = mask.reshape(-1)
         m = m.view(torch.uint8) if m.dtype == torch.bool else m.to(torch.uint8)
         m = m.contiguous()
-    out = _LinearJSD.apply(beta, temperature, bool(scale_t2), reduction, m, int(chunk), hs,
-                           student_head, ht, teacher_head)
+    out = _LinearJSD.apply(beta, temperature, bool(scale_t2), reduction, m, int(chunk), int(group),
+                           hs, student_head, ht, teacher_head)
     return out.view(lead) if reduction == "none" else out
