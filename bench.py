@@ -64,6 +64,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-siblings", action="store_true")
+    p.add_argument("--no-linear", action="store_true", help="skip the fused-linear row")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="wall-clock budget of the oracle sample")
     p.add_argument("--no-extras", action="store_true",
@@ -265,7 +266,7 @@ def main():
     per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas}
     log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
 
-    three = branches = siblings = tp8 = None
+    three = branches = siblings = tp8 = linear = None
     if not args.no_extras:
         # the same forward as three separate launches (statistics, merge, divergence),
         # timed one by one for comparison with the one-launch forward above
@@ -331,6 +332,7 @@ def main():
     if not args.no_extras:
         siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
         tp8 = tp8_forward(torch, vj, synth)
+        linear = None if args.no_linear else fused_linear_row(torch, vj, synth)
 
     out = {
         "metric": METRIC,
@@ -370,8 +372,53 @@ def main():
         "step_ms_by_beta": per_beta,
         "branches": branches,
         "siblings": siblings,
+        "fused_linear": linear,
     }
     print(json.dumps(out), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def fused_linear_row(torch, vj, synth, reps=3, chunk=4096):
+    """The fused-linear loss (hidden states and LM heads -> JSD loss, mean over tokens,
+    gradients of the student's hidden states and head) on the linear workload: N=8192,
+    V=151936, Ds=Dt=3584 bf16, `chunk` tokens per logit block."""
+    log("fused linear")
+    b = synth.draw_linear("cuda")
+    N, V, Ds = b.hs.shape[0], b.ws.shape[0], b.hs.shape[1]
+    Dt = b.ht.shape[1]
+    st, te = vj.lin_head(b.hs, b.ws, "student"), vj.lin_head(b.ht, b.wt, "teacher")
+    wsb = vj.vljsd_workspace_bytes(N, V, Ds, chunk, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    gh, gw = torch.empty_like(b.hs), torch.empty_like(b.ws)
+    opts = vj.loss_opts(N, 1.0, False, None, "mean")
+    fn = lambda: vj.vljsd(st, te, N, V, 0.5, opts, chunk, ws, out, gh, gw)
+    fn()
+    tm = Timer(torch)
+    for _ in range(reps):
+        a = tm.mark()
+        fn()
+        tm.add("x", a, tm.mark())
+    torch.cuda.synchronize()
+    ms = tm.ms("x")
+    # the four products: student and teacher logits, hidden and head gradients
+    flops = 2 * N * V * (Ds + Dt + 2 * Ds)
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": f"linear N={N} V={V} Ds={Ds} Dt={Dt} bf16, chunk {chunk}, beta 0.5, mean",
+           "fwd_bwd_ms": round(ms, 4), "tokens_per_s": round(N / (ms * 1e-3), 1),
+           "spread": tm.spread("x"),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "flops_per_call": flops},
+           "workspace_bytes": wsb,
+           # what the unfused route holds at once: bf16 logits of both sides and the
+           # student's logit gradient, [N, V] each
+           "materialized_logits_bytes": 3 * N * V * 2}
+    del ws, gh, gw, b
+    torch.cuda.empty_cache()
+    return res
 
 
 def tp8_forward(torch, vj, synth, reps=10):
