@@ -94,6 +94,15 @@ def test_gemm_edge_shapes(M, N, K):
     gemm_case(M, N, K, 0, 1, 1, "bf16", seed=5)
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 200, 128), (257, 513, 192), (1, 1, 64), (129, 300, 3584),
+                                   (256, 256, 64)])
+@pytest.mark.parametrize("out", ["f32", "f32_acc", "bf16"])
+def test_gemm_direct_to_lds_path(M, N, K, out):
+    # both operands bf16 and k-major with K a multiple of 64: the kernel whose global
+    # loads go straight into LDS (two stages of k = 64); ragged M and N
+    gemm_case(M, N, K, 0, 1, 1, out, seed=M * 7 + N + K, pad=1)
+
+
 def test_gemm_long_reduction():
     # the gradient-of-hidden shape: a long reduction over a vocabulary-sized K
     gemm_case(96, 136, 20000, 1, 1, 0, "bf16", seed=3)

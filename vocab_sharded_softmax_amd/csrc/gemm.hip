@@ -228,6 +228,39 @@ __device__ __forceinline__ void tile_of(int64_t t, int64_t mt, int64_t nt, int a
     n0 = (a_larger ? is : il) * BN;
 }
 
+// The accumulators to C: result element r of MFMA tile (a, b) is row
+// 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32; one row pointer per output row.
+template <int OUT>
+__device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc)[WTM][WTN],
+                                           int64_t m0, int64_t n0, int wm, int wn, int lane) {
+    const bool rows_in = m0 + BM <= g.M && n0 + BN <= g.N;
+    const int64_t jl = n0 + wn + (lane & 31);
+#pragma unroll
+    for (int a = 0; a < WTM; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t i = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (!rows_in && i >= g.M) continue;
+            const int64_t row = i * g.ldc;
+#pragma unroll
+            for (int b = 0; b < WTN; ++b) {
+                const int64_t j = jl + 32 * b;
+                if (!rows_in && j >= g.N) continue;
+                const float v = acc[a][b][r];
+                const int64_t o = row + j;
+                if (OUT == GEMM_F32) {
+                    static_cast<float *>(g.c)[o] = v;
+                } else if (OUT == GEMM_F32_ACC) {
+                    static_cast<float *>(g.c)[o] += v;
+                } else if (OUT == GEMM_BF16) {
+                    static_cast<unsigned short *>(g.c)[o] = bf16_bits(v);
+                } else {  // GEMM_BF16_ACC: bf16(addend + v)
+                    static_cast<unsigned short *>(g.c)[o] = bf16_bits(g.addend[i * g.ldadd + j] + v);
+                }
+            }
+        }
+}
+
 template <bool AF32, bool AKM, bool BKM, int OUT>
 __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm(GemmArgs g) {
@@ -339,33 +372,151 @@ void k_gemm(GemmArgs g) {
         if (kt < nk) step(sa0, sb0, sa1, sb1, 0, kt);
     }
 
-    // result element r of MFMA tile (a, b): row 8 (r / 4) + 4 (lane / 32) + r % 4,
-    // column lane % 32; one row pointer per output row
-    const int64_t jl = n0 + wn + (lane & 31);
+    store_tile<OUT>(g, acc, m0, n0, wm, wn, lane);
+}
+
+// ---- both operands bf16 and k-major, K a multiple of 64: global loads straight into LDS
+//
+// gfx950's global_load_lds_dwordx4 writes each lane's 16 bytes at consecutive LDS
+// addresses (no staging registers).  A stage is k = 64, so each LDS row is one full
+// 128-byte line of its operand row: the eight lanes of a row load the whole line
+// (loads of half lines fetch every line twice from L2, and that bound the earlier
+// stage of k = 32).  Two stages of 64 KiB: the loads of stage kt + 1 run during stage
+// kt's products.  The chunk c of row r sits at slot c ^ dswz(r): sixteen consecutive
+// rows' 16-byte reads of one chunk fall on distinct banks whether the LDS serves eight
+// or sixteen lanes a cycle.  A row past the edge loads row M - 1 (N - 1): it feeds only
+// outputs that are not stored.
+constexpr int DBK = 64, DST = 2;
+constexpr int DSTAGE = 2 * 256 * DBK;  // bf16 elements of one stage (A rows, then B rows)
+
+__device__ __forceinline__ int dswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ bf16x8 dfrag(const unsigned short *s, int base, int chunk) {
+    const int l = threadIdx.x & 63;
+    const int row = base + (l & 31), c = chunk + (l >> 5);
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(s + row * DBK + 8 * (c ^ dswz(row)));
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_dl(GemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) unsigned short lds[DST][DSTAGE];
+    const int64_t mt = (g.M + BM - 1) / BM, nt = (g.N + BN - 1) / BN, T = mt * nt;
+    const int64_t per = (T + 7) / 8;
+    const int64_t t = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (t >= T) return;
+    int64_t m0, n0;
+    tile_of(t, mt, nt, g.n_fastest, m0, n0);
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = (wave >> 1) * (32 * WTM), wn = (wave & 1) * (32 * WTN);
+    f32x16 acc[WTM][WTN];
 #pragma unroll
     for (int a = 0; a < WTM; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t i = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (!rows_in && i >= g.M) continue;
-            const int64_t row = i * g.ldc;
+        for (int b = 0; b < WTN; ++b)
 #pragma unroll
-            for (int b = 0; b < WTN; ++b) {
-                const int64_t j = jl + 32 * b;
-                if (!rows_in && j >= g.N) continue;
-                const float v = acc[a][b][r];
-                const int64_t o = row + j;
-                if (OUT == GEMM_F32) {
-                    static_cast<float *>(g.c)[o] = v;
-                } else if (OUT == GEMM_F32_ACC) {
-                    static_cast<float *>(g.c)[o] += v;
-                } else if (OUT == GEMM_BF16) {
-                    static_cast<unsigned short *>(g.c)[o] = bf16_bits(v);
-                } else {  // GEMM_BF16_ACC: bf16(addend + v)
-                    static_cast<unsigned short *>(g.c)[o] = bf16_bits(g.addend[i * g.ldadd + j] + v);
-                }
-            }
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    // this wave loads rows [64 wave, + 64) of A and of B: eight instructions of 8 rows
+    // each; lane i of an instruction covers row + i / 8, slot i % 8
+    constexpr int NI = 8;  // load instructions per operand per wave and stage
+    const int64_t rl = lane >> 3;
+    const int cl = lane & 7;
+    const uint16_t *pa = static_cast<const uint16_t *>(g.a);
+    const uint16_t *pb = static_cast<const uint16_t *>(g.b);
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto issue = [&](int64_t s) {
+        unsigned short *st = lds[s % DST];
+        const int64_t k0 = s * DBK;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int r = 64 * wave + 8 * j + (int)rl;
+            const int c = cl ^ dswz(r);
+            const int64_t ra = m0 + r < g.M ? m0 + r : g.M - 1;
+            const int64_t rb = n0 + r < g.N ? n0 + r : g.N - 1;
+            const int row0 = 64 * wave + 8 * j;
+            __builtin_amdgcn_global_load_lds(pa + ra * g.lda + k0 + 8 * c,
+                                             (lds_void *)(st + row0 * DBK), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(pb + rb * g.ldb + k0 + 8 * c,
+                                             (lds_void *)(st + 256 * DBK + row0 * DBK), 16, 0, 0);
         }
+    };
+
+    // Software pipeline over the four MFMA sub-steps F0..F3 of a stage: F(i + 1)'s
+    // fragments are read while F(i)'s products run; after F2, the wait and barrier for
+    // the next stage, whose loads then go into the buffer this stage leaves, and whose
+    // F0 is read while F3's products run.
+    const int64_t nk = g.K / DBK;
+    bf16x8 fa[2][WTM], fb[2][WTN];
+    auto read = [&](int buf, int64_t s, int sub) {
+        const unsigned short *la = lds[s % DST], *lb = la + 256 * DBK;
+#pragma unroll
+        for (int a = 0; a < WTM; ++a) fa[buf][a] = dfrag(la, wm + 32 * a, 2 * sub);
+#pragma unroll
+        for (int b = 0; b < WTN; ++b) fb[buf][b] = dfrag(lb, wn + 32 * b, 2 * sub);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int a = 0; a < WTM; ++a)
+#pragma unroll
+            for (int b = 0; b < WTN; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][a], fb[buf][b],
+                                                                     acc[a][b], 0, 0, 0);
+    };
+    if (nk > 0) {
+        issue(0);
+        if (nk > 1) {
+            issue(1);
+            wait_vm<2 * NI>();  // stage 0 landed; stage 1 may be in flight
+        } else {
+            wait_vm<0>();
+        }
+        // plain barriers: the waits cover this wave's loads, and __syncthreads()'s fence
+        // would also wait for the stage still in flight
+        __builtin_amdgcn_s_barrier();
+        read(0, 0, 0);
+    }
+    // (the last stage is peeled off, so that no branch separates the next stage's
+    // fragment reads from the products they overlap)
+    for (int64_t kt = 0; kt + 1 < nk; ++kt) {
+        read(1, kt, 1);
+        mma(0);
+        read(0, kt, 2);
+        mma(1);
+        read(1, kt, 3);
+        mma(0);
+        // every wave's reads of stage kt are complete before the barrier (F3 is waited
+        // for here), and stage kt + 1 has landed for this wave; after the barrier the
+        // next issue may overwrite stage kt's buffer
+        wait_lgkm0();
+        wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 2 < nk) issue(kt + 2);
+        read(0, kt + 1, 0);
+        mma(1);
+    }
+    if (nk > 0) {
+        read(1, nk - 1, 1);
+        mma(0);
+        read(0, nk - 1, 2);
+        mma(1);
+        read(1, nk - 1, 3);
+        mma(0);
+        mma(1);
+    }
+    store_tile<OUT>(g, acc, m0, n0, wm, wn, lane);
 }
 
 template <bool AF32, bool AKM, bool BKM>
@@ -398,6 +549,25 @@ hipError_t launch_gemm(const GemmArgs &gin, hipStream_t st) {
     GemmArgs g = gin;
     // consecutive tiles share a panel of the operand with more bytes
     g.n_fastest = (double)g.M * (g.a_f32 ? 4 : 2) > (double)g.N * 2;
+    if (!g.a_f32 && g.a_kmajor && g.b_kmajor && g.K > 0 && g.K % DBK == 0) {
+        const int64_t T = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+        const dim3 grid((unsigned)(8 * ((T + 7) / 8)));
+        switch (g.out) {
+            case GEMM_F32:
+                hipLaunchKernelGGL(k_gemm_dl<GEMM_F32>, grid, dim3(GTHREADS), 0, st, g);
+                break;
+            case GEMM_F32_ACC:
+                hipLaunchKernelGGL(k_gemm_dl<GEMM_F32_ACC>, grid, dim3(GTHREADS), 0, st, g);
+                break;
+            case GEMM_BF16:
+                hipLaunchKernelGGL(k_gemm_dl<GEMM_BF16>, grid, dim3(GTHREADS), 0, st, g);
+                break;
+            default:
+                hipLaunchKernelGGL(k_gemm_dl<GEMM_BF16_ACC>, grid, dim3(GTHREADS), 0, st, g);
+                break;
+        }
+        return hipGetLastError();
+    }
     if (g.a_f32) {
         if (g.a_kmajor) return g.b_kmajor ? gemm_out<true, true, true>(g, st)
                                           : gemm_out<true, true, false>(g, st);
