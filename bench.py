@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-siblings", action="store_true")
     p.add_argument("--no-linear", action="store_true", help="skip the fused-linear row")
+    p.add_argument("--linear-only", action="store_true",
+                   help="only the fused-linear row, printed as its own JSON line (for profiling)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="wall-clock budget of the oracle sample")
     p.add_argument("--no-extras", action="store_true",
@@ -192,6 +194,12 @@ def traffic_entry(kernel_key):
 
 def main():
     args = parse()
+    if args.linear_only:
+        import torch
+        import synth
+        import vocab_sharded_softmax_amd as vj
+        print(json.dumps(fused_linear_row(torch, vj, synth)), flush=True)
+        return
     if args.gpus != 1:
         log(f"bench.py measures one GPU: the op runs on one GPU's vocabulary shards with an "
             f"on-device merge, and no multi-GPU path exists (asked for --gpus {args.gpus}).")
