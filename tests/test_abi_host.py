@@ -303,14 +303,20 @@ def test_linear_workspace_and_scale():
     # gradient of a group (4 GiB worth of whole chunks by default), per-token losses,
     # the block's statistics / KL pair / pass workspace, the count, and the fp32 head
     # gradient accumulator only with more than one group
+    # (plus G and the group's hidden states transposed, token rows padded to 8)
     N, V, D, C = 8192, 151936, 3584, 4096
     ldl = V
-    expect = (2 * al(C * ldl * 4) + al(N * ldl * 2) + al(N * 4) + al(C * 32) + al(C * 8)
-              + al(lib.vjsd_workspace_bytes(C, 1)) + al(8))
+    # (and the student head transposed, with the fp32 partials of the hidden-gradient
+    # product's K split: 32 x 14 tiles -> 3 splits)
+    expect = (2 * al(C * ldl * 4) + al(N * ldl * 2) + al(V * N * 2) + al(D * N * 2)
+              + al(D * V * 2) + al(3 * N * D * 4) + al(N * 4)
+              + al(C * 32) + al(C * 8) + al(lib.vjsd_workspace_bytes(C, 1)) + al(8))
     assert w(N, V, D, C, 0) == expect
     # groups of 2 chunks of 100 over 300 tokens: two groups, so an accumulator
     ldl = 1008
-    expect = (2 * al(100 * ldl * 4) + al(200 * ldl * 2) + al(300 * 4) + al(3200) + al(800)
+    # (V = 1001 is no multiple of 64: no K split)
+    expect = (2 * al(100 * ldl * 4) + al(200 * ldl * 2) + al(1001 * 200 * 2) + al(16 * 200 * 2)
+              + al(16 * 1008 * 2) + al(300 * 4) + al(3200) + al(800)
               + al(lib.vjsd_workspace_bytes(100, 1)) + al(8) + al(1001 * 16 * 4))
     assert w(300, 1001, 16, 100, 150) == expect
     s = lib.vlin_scale

@@ -165,6 +165,14 @@ def test_linear_jsd_chunks_and_groups(chunk, group):
     _check_linear(b, 0.5, chunk=chunk, group=group)
 
 
+@pytest.mark.parametrize("chunk,group", [(300, 0), (128, 128)])
+def test_linear_jsd_vocabulary_multiple_of_64(chunk, group):
+    # V a multiple of 64: the hidden-gradient product runs on the direct-to-LDS kernel
+    # with its K (the vocabulary) split over work items and the fp32 partials summed
+    b = synth.draw_linear("cuda", N=300, V=1024, Ds=64, Dt=48, seed=12)
+    _check_linear(b, 0.5, T=1.5, t2=True, red="mean", chunk=chunk, group=group)
+
+
 @pytest.mark.parametrize("beta", [0.0, 0.3, 1.0])
 def test_linear_jsd_betas_temperature_mask(beta):
     b = synth.draw_linear("cuda", N=257, V=777, Ds=64, Dt=96, seed=8)

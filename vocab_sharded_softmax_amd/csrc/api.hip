@@ -169,14 +169,29 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // products of the group; then the
 // per-token losses, the block's statistics, KL pair and pass workspace, the kept-token
 // count, and the fp32 head-gradient accumulator when there is more than one group.
+// G and the group's hidden states are also kept transposed (for the head gradient).
 constexpr size_t LIN_G_BUDGET = (size_t)4 << 30;
 
 struct LinLayout {
-    int64_t C = 0, NG = 0, ldl = 0;
-    size_t ls = 0, lt = 0, g = 0, rows = 0, stats = 0, kl = 0, part = 0, count = 0, gw = 0;
+    int64_t C = 0, NG = 0, ldl = 0, ldt = 0, ldv = 0;
+    int splits = 1;  // K split of the hidden-gradient product
+    size_t ls = 0, lt = 0, g = 0, gt = 0, ht = 0, wt = 0, hp = 0, rows = 0, stats = 0, kl = 0,
+           part = 0, count = 0, gw = 0;
     size_t total = 0;
     bool has_gw = false;
 };
+
+// The hidden-gradient product of a group (gn x dim tiles of 256 x 256 over a K of V) has
+// few tiles for 256 CUs: its K is split so that there are about four work items per CU,
+// when V allows the direct-to-LDS kernel (V a multiple of 64).
+int lin_splits(int64_t ng, int64_t V, int64_t dim) {
+    if (V % 64 != 0 || ng <= 0) return 1;
+    const int64_t tiles = ((ng + 255) / 256) * ((dim + 255) / 256);
+    int64_t s = (1024 + tiles - 1) / tiles;
+    const int64_t stages = V / 64;
+    while (s > 1 && stages / s < 8) --s;  // at least 8 stages of k per item
+    return (int)(s < 1 ? 1 : (s > 8 ? 8 : s));
+}
 LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk, int64_t group) {
     LinLayout L;
     L.C = chunk < N ? chunk : N;
@@ -199,6 +214,17 @@ LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk, int64_t g
     L.ls = take(blk);
     L.lt = take(blk);
     L.g = take((size_t)L.NG * (size_t)L.ldl * 2);
+    // the group's G and student hidden states transposed (tokens contiguous), so that the
+    // head-gradient product reads both operands k-major
+    L.ldt = (L.NG + 7) / 8 * 8;
+    L.gt = take((size_t)V * (size_t)L.ldt * 2);
+    L.ht = take((size_t)dim * (size_t)L.ldt * 2);
+    // the student head transposed (vocabulary contiguous) for the hidden-gradient
+    // product, and that product's fp32 partials when its K is split
+    L.ldv = (V + 7) / 8 * 8;
+    L.wt = take((size_t)dim * (size_t)L.ldv * 2);
+    L.splits = lin_splits(L.NG, V, dim);
+    L.hp = take(L.splits > 1 ? (size_t)L.splits * (size_t)L.NG * (size_t)dim * 4 : 0);
     L.rows = take((size_t)N * sizeof(float));
     L.stats = take((size_t)L.C * 4 * sizeof(double));
     L.kl = take((size_t)L.C * 2 * sizeof(float));
@@ -720,6 +746,10 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
     float *ls = reinterpret_cast<float *>(ws + L.ls);
     float *lt = reinterpret_cast<float *>(ws + L.lt);
     uint16_t *G = reinterpret_cast<uint16_t *>(ws + L.g);
+    uint16_t *Gt = reinterpret_cast<uint16_t *>(ws + L.gt);
+    uint16_t *Ht = reinterpret_cast<uint16_t *>(ws + L.ht);
+    uint16_t *Wt = reinterpret_cast<uint16_t *>(ws + L.wt);
+    float *Hp = reinterpret_cast<float *>(ws + L.hp);
     float *rows = reinterpret_cast<float *>(ws + L.rows);
     double *stats = reinterpret_cast<double *>(ws + L.stats);
     float *kl = reinterpret_cast<float *>(ws + L.kl);
@@ -734,6 +764,11 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
     float *rows_out = c.red == VJSD_REDUCE_NONE ? out : rows;
     const int mode = mode_of(beta);
     const int64_t C = L.C, NG = L.NG, ngroups = (N + NG - 1) / NG;
+    if (grad_h) {  // w_s^T [D][V], once: the hidden-gradient products read it k-major
+        if ((e = hip_status(vjsd::launch_transpose16(static_cast<const uint16_t *>(student->w),
+                                                      student->ldw, V, D, Wt, L.ldv, st))))
+            return e;
+    }
     const uint16_t *hs = static_cast<const uint16_t *>(student->h);
     const uint16_t *ht = static_cast<const uint16_t *>(teacher->h);
     for (int64_t grp = 0; grp < ngroups; ++grp) {
@@ -792,32 +827,49 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
             if ((e = hip_status(vjsd::launch_bwd_f32_to_bf16(mode, sh, nb, part, st)))) return e;
         }
         if (!grads) continue;
-        if (grad_h) {  // G [gn][V] x w_s [V][D]
+        if (grad_h) {  // G [gn][V] x (w_s^T)^T: both operands k-major
             vjsd::GemmArgs g;
             g.M = gn;
             g.N = D;
             g.K = V;
             g.a = G;
             g.lda = L.ldl;
-            g.b = student->w;
-            g.ldb = student->ldw;
-            g.b_kmajor = 0;
-            g.c = static_cast<uint16_t *>(grad_h) + g0 * ldgh;
-            g.ldc = ldgh;
-            g.out = vjsd::GEMM_BF16;
-            if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+            g.b = Wt;
+            g.ldb = L.ldv;
+            uint16_t *dst = static_cast<uint16_t *>(grad_h) + g0 * ldgh;
+            const int S = lin_splits(gn, V, D) < L.splits ? lin_splits(gn, V, D) : L.splits;
+            if (S > 1) {  // fp32 partials of the K split, then their sum in split order
+                g.ksplit = S;
+                g.split_stride = gn * D;
+                g.c = Hp;
+                g.ldc = D;
+                g.out = vjsd::GEMM_F32;
+                if ((e = hip_status(vjsd::launch_gemm(g, st))) ||
+                    (e = hip_status(vjsd::launch_sum_partials(Hp, S, gn * D, gn, D, D, dst, ldgh,
+                                                              st))))
+                    return e;
+            } else {
+                g.c = dst;
+                g.ldc = ldgh;
+                g.out = vjsd::GEMM_BF16;
+                if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+            }
         }
         if (grad_w) {  // G^T [V][gn] x h_s [gn][D], summed over the groups in fp32
+            // both operands transposed first (tokens contiguous): the product then runs on
+            // k-major operands
+            if ((e = hip_status(vjsd::launch_transpose16(G, L.ldl, gn, V, Gt, L.ldt, st))) ||
+                (e = hip_status(vjsd::launch_transpose16(hs + g0 * student->ldh, student->ldh,
+                                                          gn, D, Ht, L.ldt, st))))
+                return e;
             vjsd::GemmArgs g;
             g.M = V;
             g.N = D;
             g.K = gn;
-            g.a = G;
-            g.lda = L.ldl;
-            g.a_kmajor = 0;
-            g.b = hs + g0 * student->ldh;
-            g.ldb = student->ldh;
-            g.b_kmajor = 0;
+            g.a = Gt;
+            g.lda = L.ldt;
+            g.b = Ht;
+            g.ldb = L.ldt;
             if (ngroups == 1 || grp == ngroups - 1) {
                 g.c = grad_w;
                 g.ldc = ldgw;

@@ -413,11 +413,18 @@ __global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1))
 void k_gemm_dl(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) unsigned short lds[DST][DSTAGE];
     const int64_t mt = (g.M + BM - 1) / BM, nt = (g.N + BN - 1) / BN, T = mt * nt;
-    const int64_t per = (T + 7) / 8;
-    const int64_t t = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (t >= T) return;
+    // work items: ksplit per tile, split-major (each split runs the whole tile order)
+    const int64_t items = T * g.ksplit;
+    const int64_t per = (items + 7) / 8;
+    const int64_t it = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (it >= items) return;
+    const int64_t split = it / T, t = it - split * T;
     int64_t m0, n0;
     tile_of(t, mt, nt, g.n_fastest, m0, n0);
+    // this item's stages of k = 64
+    const int64_t nk_all = g.K / DBK, nk_per = (nk_all + g.ksplit - 1) / g.ksplit;
+    const int64_t kb = split * nk_per;
+    const int64_t nk = nk_all - kb < nk_per ? (nk_all - kb > 0 ? nk_all - kb : 0) : nk_per;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = (wave >> 1) * (32 * WTM), wn = (wave & 1) * (32 * WTN);
@@ -439,7 +446,7 @@ void k_gemm_dl(GemmArgs g) {
     typedef __attribute__((address_space(3))) void lds_void;
     auto issue = [&](int64_t s) {
         unsigned short *st = lds[s % DST];
-        const int64_t k0 = s * DBK;
+        const int64_t k0 = (kb + s) * DBK;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
             const int r = 64 * wave + 8 * j + (int)rl;
@@ -458,7 +465,6 @@ void k_gemm_dl(GemmArgs g) {
     // fragments are read while F(i)'s products run; after F2, the wait and barrier for
     // the next stage, whose loads then go into the buffer this stage leaves, and whose
     // F0 is read while F3's products run.
-    const int64_t nk = g.K / DBK;
     bf16x8 fa[2][WTM], fb[2][WTN];
     auto read = [&](int buf, int64_t s, int sub) {
         const unsigned short *la = lds[s % DST], *lb = la + 256 * DBK;
@@ -516,6 +522,12 @@ void k_gemm_dl(GemmArgs g) {
         mma(0);
         mma(1);
     }
+    if (g.ksplit > 1) {  // this split's partial product, fp32
+        GemmArgs gp = g;
+        gp.c = static_cast<float *>(g.c) + split * g.split_stride;
+        store_tile<GEMM_F32>(gp, acc, m0, n0, wm, wn, lane);
+        return;
+    }
     store_tile<OUT>(g, acc, m0, n0, wm, wn, lane);
 }
 
@@ -546,11 +558,15 @@ hipError_t gemm_out(const GemmArgs &g, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs &gin, hipStream_t st) {
     if (gin.M == 0 || gin.N == 0) return hipSuccess;
+    // a K split needs the direct-to-LDS kernel (both operands bf16, k-major, K % 64 == 0)
+    if (gin.ksplit > 1 && (gin.a_f32 || !gin.a_kmajor || !gin.b_kmajor || gin.K % DBK != 0 ||
+                           gin.K == 0))
+        return hipErrorInvalidValue;
     GemmArgs g = gin;
     // consecutive tiles share a panel of the operand with more bytes
     g.n_fastest = (double)g.M * (g.a_f32 ? 4 : 2) > (double)g.N * 2;
     if (!g.a_f32 && g.a_kmajor && g.b_kmajor && g.K > 0 && g.K % DBK == 0) {
-        const int64_t T = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+        const int64_t T = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.ksplit;
         const dim3 grid((unsigned)(8 * ((T + 7) / 8)));
         switch (g.out) {
             case GEMM_F32:

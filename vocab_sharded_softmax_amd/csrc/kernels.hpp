@@ -165,8 +165,19 @@ struct GemmArgs {
     const float *addend = nullptr;  // GEMM_BF16_ACC: fp32, element (i, j) at addend[i*ldadd + j]
     int64_t ldadd = 0;
     int n_fastest = 0;  // tile order (set by launch_gemm)
+    // split of K over `ksplit` work items per tile (the direct-to-LDS kernel only): item s
+    // writes the fp32 product of its K range to c + s * split_stride (out GEMM_F32)
+    int ksplit = 1;
+    int64_t split_stride = 0;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
+// out[i][j] = bf16(sum_{s < S} part[s * stride + i * ldp + j]) (fixed order), i < M, j < N
+hipError_t launch_sum_partials(const float *part, int S, int64_t stride, int64_t M, int64_t N,
+                               int64_t ldp, uint16_t *out, int64_t ldo, hipStream_t st);
+// dst[c][r] = src[r][c], 16-bit elements, r < R, c < C; row strides multiples of 8
+// elements, bases 16-byte aligned
+hipError_t launch_transpose16(const uint16_t *src, int64_t lds, int64_t R, int64_t C,
+                              uint16_t *dst, int64_t ldd, hipStream_t st);
 // p[i] *= g[0] over n values of dtype 0 (fp32) or 2 (bf16); p 16-byte aligned
 hipError_t launch_scale(int dtype, void *p, int64_t n, const float *g, hipStream_t st);
 

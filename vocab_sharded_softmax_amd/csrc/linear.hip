@@ -26,7 +26,100 @@ __global__ __launch_bounds__(SCALE_BLOCK) void k_scale(typename D::T *p, int64_t
         store1<D>(p + i, load1<D>(p + i) * s);
 }
 
+// dst[c][r] = src[r][c] for 16-bit elements, r < R, c < C: one 64 x 64 tile per
+// workgroup through LDS (rows padded by 2 elements).  Interior tiles move 16-byte
+// vectors (row strides multiples of 8 elements, bases 16-byte aligned); edge tiles
+// move single elements.
+constexpr int TT = 64, TT_BLOCK = 256;
+
+__global__ __launch_bounds__(TT_BLOCK) void k_transpose16(const uint16_t *__restrict__ src,
+                                                          int64_t lds_, int64_t R, int64_t C,
+                                                          uint16_t *__restrict__ dst,
+                                                          int64_t ldd) {
+    __shared__ uint16_t tile[TT][TT + 2];
+    const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
+    const bool full = r0 + TT <= R && c0 + TT <= C;
+    const int t = threadIdx.x;
+    if (full) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {  // 64 rows x 8 vectors of 8
+            const int q = t + TT_BLOCK * i, r = q >> 3, cv = (q & 7) * 8;
+            const u32x4 v = ld16<false>(src + (r0 + r) * lds_ + c0 + cv);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = v[e];
+                tile[r][cv + 2 * e] = (uint16_t)(w & 0xffffu);
+                tile[r][cv + 2 * e + 1] = (uint16_t)(w >> 16);
+            }
+        }
+    } else {
+        for (int q = t; q < TT * TT; q += TT_BLOCK) {
+            const int r = q / TT, c = q % TT;
+            if (r0 + r < R && c0 + c < C) tile[r][c] = src[(r0 + r) * lds_ + c0 + c];
+        }
+    }
+    __syncthreads();
+    if (full) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {  // 64 output rows (source columns) x 8 vectors
+            const int q = t + TT_BLOCK * i, c = q >> 3, rv = (q & 7) * 8;
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = (uint32_t)tile[rv + 2 * e][c] | ((uint32_t)tile[rv + 2 * e + 1][c] << 16);
+            st16<false>(dst + (c0 + c) * ldd + r0 + rv, u32x4{w[0], w[1], w[2], w[3]});
+        }
+    } else {
+        for (int q = t; q < TT * TT; q += TT_BLOCK) {
+            const int c = q / TT, r = q % TT;
+            if (r0 + r < R && c0 + c < C) dst[(c0 + c) * ldd + r0 + r] = tile[r][c];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_sum_partials(const float *__restrict__ part, int S,
+                                                     int64_t stride, int64_t M, int64_t N,
+                                                     int64_t ldp, uint16_t *__restrict__ out,
+                                                     int64_t ldo) {
+    const int64_t total = M * N;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total;
+         q += (int64_t)gridDim.x * 256) {
+        const int64_t i = q / N, j = q - i * N;
+        float v = part[i * ldp + j];
+        for (int s = 1; s < S; ++s) v += part[s * stride + i * ldp + j];
+        out[i * ldo + j] = (uint16_t)(__builtin_bit_cast(
+                                          uint32_t, __builtin_convertvector((f32x2){v, 0.0f},
+                                                                            bf16x2)) &
+                                      0xffffu);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_sum_partials(const float *part, int S, int64_t stride, int64_t M, int64_t N,
+                               int64_t ldp, uint16_t *out, int64_t ldo, hipStream_t st) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const int64_t want = (M * N + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 16384 ? want : 16384);
+    hipLaunchKernelGGL(k_sum_partials, dim3(blocks), dim3(256), 0, st, part, S, stride, M, N, ldp,
+                       out, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose16(const uint16_t *src, int64_t lds_, int64_t R, int64_t C,
+                              uint16_t *dst, int64_t ldd, hipStream_t st) {
+    constexpr int64_t RMAX = (int64_t)65535 * TT;  // rows one launch covers (grid.y)
+    for (int64_t rb = 0; rb < R; rb += RMAX) {
+        const int64_t rn = R - rb < RMAX ? R - rb : RMAX;
+        if (C == 0) break;
+        const dim3 grid((unsigned)((C + TT - 1) / TT), (unsigned)((rn + TT - 1) / TT));
+        hipLaunchKernelGGL(k_transpose16, grid, dim3(TT_BLOCK), 0, st, src + rb * lds_, lds_, rn,
+                           C, dst + rb, ldd);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
 
 hipError_t launch_scale(int dtype, void *p, int64_t n, const float *g, hipStream_t st) {
     if (n == 0) return hipSuccess;
