@@ -306,10 +306,10 @@ def test_linear_workspace_and_scale():
     # (plus G and the group's hidden states transposed, token rows padded to 8)
     N, V, D, C = 8192, 151936, 3584, 4096
     ldl = V
-    # (and the student head transposed, with the fp32 partials of the hidden-gradient
-    # product's K split: 32 x 14 tiles -> 3 splits)
+    # (and the student head transposed; 32 x 14 tiles fill the CUs, so the
+    # hidden-gradient product is not split and needs no partials)
     expect = (2 * al(C * ldl * 4) + al(N * ldl * 2) + al(V * N * 2) + al(D * N * 2)
-              + al(D * V * 2) + al(3 * N * D * 4) + al(N * 4)
+              + al(D * V * 2) + al(N * 4)
               + al(C * 32) + al(C * 8) + al(lib.vjsd_workspace_bytes(C, 1)) + al(8))
     assert w(N, V, D, C, 0) == expect
     # groups of 2 chunks of 100 over 300 tokens: two groups, so an accumulator

@@ -26,24 +26,28 @@ __global__ __launch_bounds__(SCALE_BLOCK) void k_scale(typename D::T *p, int64_t
         store1<D>(p + i, load1<D>(p + i) * s);
 }
 
-// dst[c][r] = src[r][c] for 16-bit elements, r < R, c < C: one 64 x 64 tile per
-// workgroup through LDS (rows padded by 2 elements).  Interior tiles move 16-byte
+// dst[c][r] = src[r][c] for 16-bit elements, r < R, c < C: one 128 x 128 tile per
+// workgroup through LDS (rows padded by 2 elements), so every row segment read or
+// written is 256 bytes.  Interior tiles move 16-byte
 // vectors (row strides multiples of 8 elements, bases 16-byte aligned); edge tiles
 // move single elements.
-constexpr int TT = 64, TT_BLOCK = 256;
+constexpr int TT = 128, TT_BLOCK = 256;
+constexpr int TT_VEC = TT * TT / 8 / TT_BLOCK;  // 16-byte vectors per thread
 
 __global__ __launch_bounds__(TT_BLOCK) void k_transpose16(const uint16_t *__restrict__ src,
                                                           int64_t lds_, int64_t R, int64_t C,
                                                           uint16_t *__restrict__ dst,
-                                                          int64_t ldd) {
+                                                          int64_t ldd, int rows_fast) {
     __shared__ uint16_t tile[TT][TT + 2];
-    const int64_t r0 = (int64_t)blockIdx.y * TT, c0 = (int64_t)blockIdx.x * TT;
+    // consecutive workgroups step along the longer dimension
+    const int64_t r0 = (int64_t)(rows_fast ? blockIdx.x : blockIdx.y) * TT;
+    const int64_t c0 = (int64_t)(rows_fast ? blockIdx.y : blockIdx.x) * TT;
     const bool full = r0 + TT <= R && c0 + TT <= C;
     const int t = threadIdx.x;
     if (full) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {  // 64 rows x 8 vectors of 8
-            const int q = t + TT_BLOCK * i, r = q >> 3, cv = (q & 7) * 8;
+        for (int i = 0; i < TT_VEC; ++i) {  // TT rows x TT / 8 vectors of 8
+            const int q = t + TT_BLOCK * i, r = q / (TT / 8), cv = (q % (TT / 8)) * 8;
             const u32x4 v = ld16<false>(src + (r0 + r) * lds_ + c0 + cv);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -61,8 +65,8 @@ __global__ __launch_bounds__(TT_BLOCK) void k_transpose16(const uint16_t *__rest
     __syncthreads();
     if (full) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {  // 64 output rows (source columns) x 8 vectors
-            const int q = t + TT_BLOCK * i, c = q >> 3, rv = (q & 7) * 8;
+        for (int i = 0; i < TT_VEC; ++i) {  // TT output rows (source columns) x TT / 8 vectors
+            const int q = t + TT_BLOCK * i, c = q / (TT / 8), rv = (q % (TT / 8)) * 8;
             uint32_t w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -108,13 +112,21 @@ hipError_t launch_sum_partials(const float *part, int S, int64_t stride, int64_t
 
 hipError_t launch_transpose16(const uint16_t *src, int64_t lds_, int64_t R, int64_t C,
                               uint16_t *dst, int64_t ldd, hipStream_t st) {
-    constexpr int64_t RMAX = (int64_t)65535 * TT;  // rows one launch covers (grid.y)
-    for (int64_t rb = 0; rb < R; rb += RMAX) {
-        const int64_t rn = R - rb < RMAX ? R - rb : RMAX;
-        if (C == 0) break;
-        const dim3 grid((unsigned)((C + TT - 1) / TT), (unsigned)((rn + TT - 1) / TT));
-        hipLaunchKernelGGL(k_transpose16, grid, dim3(TT_BLOCK), 0, st, src + rb * lds_, lds_, rn,
-                           C, dst + rb, ldd);
+    if (R == 0 || C == 0) return hipSuccess;
+    // grid.x runs along the longer dimension; the shorter one (grid.y, at most 65535
+    // tiles a launch) is cut into launches
+    const int rows_fast = R >= C;
+    const int64_t ylen = rows_fast ? C : R, xlen = rows_fast ? R : C;
+    constexpr int64_t YMAX = (int64_t)65535 * TT;
+    for (int64_t yb = 0; yb < ylen; yb += YMAX) {
+        const int64_t yn = ylen - yb < YMAX ? ylen - yb : YMAX;
+        const dim3 grid((unsigned)((xlen + TT - 1) / TT), (unsigned)((yn + TT - 1) / TT));
+        if (rows_fast)  // columns [yb, yb + yn) of src are rows [yb, yb + yn) of dst
+            hipLaunchKernelGGL(k_transpose16, grid, dim3(TT_BLOCK), 0, st, src + yb, lds_, R, yn,
+                               dst + yb * ldd, ldd, 1);
+        else  // rows [yb, yb + yn) of src are columns of dst
+            hipLaunchKernelGGL(k_transpose16, grid, dim3(TT_BLOCK), 0, st, src + yb * lds_, lds_,
+                               yn, C, dst + yb, ldd, 0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
