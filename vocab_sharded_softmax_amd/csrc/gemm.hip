@@ -248,14 +248,18 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc
                 if (!rows_in && j >= g.N) continue;
                 const float v = acc[a][b][r];
                 const int64_t o = row + j;
+                // results are written with the streaming policy: they are read much
+                // later, and through the L2 they would evict the operand panels the
+                // tiles running beside this one still share
                 if (OUT == GEMM_F32) {
-                    static_cast<float *>(g.c)[o] = v;
+                    __builtin_nontemporal_store(v, static_cast<float *>(g.c) + o);
                 } else if (OUT == GEMM_F32_ACC) {
                     static_cast<float *>(g.c)[o] += v;
                 } else if (OUT == GEMM_BF16) {
-                    static_cast<unsigned short *>(g.c)[o] = bf16_bits(v);
+                    __builtin_nontemporal_store(bf16_bits(v), static_cast<unsigned short *>(g.c) + o);
                 } else {  // GEMM_BF16_ACC: bf16(addend + v)
-                    static_cast<unsigned short *>(g.c)[o] = bf16_bits(g.addend[i * g.ldadd + j] + v);
+                    __builtin_nontemporal_store(bf16_bits(g.addend[i * g.ldadd + j] + v),
+                                                static_cast<unsigned short *>(g.c) + o);
                 }
             }
         }
