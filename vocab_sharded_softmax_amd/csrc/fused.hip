@@ -9,9 +9,8 @@
 //                FUSED_NVT_MAX 16-byte vectors per input: up to 16384 bf16 / fp16 or
 //                8192 fp32 columns, 16-byte aligned rows): one HBM read per logit
 //   k_fwd_twice  wider rows: the workgroup sweeps its row for the statistics, then
-//                sweeps it again for the divergence terms; part of the second read
-//                is served by the caches, and the merge launch and two kernel
-//                boundaries go away
+//                sweeps it again for the divergence terms; the merge launch and two
+//                kernel boundaries go away, the second read stays
 // The row constants are rebuilt from the fp64 statistics exactly as the separate
 // passes rebuild them.  Splitting a row over several workgroups would need a
 // device-wide exchange per row; on MI355X the cache write-back and invalidation that a
@@ -80,6 +79,43 @@ __device__ __forceinline__ void block_sum2(float &a, float &b, float *red) {
     a = x;
     b = y;
     __syncthreads();
+}
+
+// Constants of a row's divergence pass, derived from the row's (max, sum) pairs.
+struct RowK {
+    float cs, ct, gam, rf, izs, izt;  // references, mixture weight, log2(Zs/Zt), 1/Z
+    int undefined;                    // a side has no distribution (all -inf)
+};
+
+// Run by one whole wave: the fp64 steps are the costliest part of a row's finish, so
+// one wave takes them and the others read the result from LDS.  Lane 0 stores the
+// row's statistics and the constants.
+__device__ __forceinline__ void row_constants(float ms, float zs, float mt, float zt,
+                                              double beta, float ks, double *st, RowK *out) {
+    const bool undefined = ms == NINF || mt == NINF;
+    const double lzs = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, (double)zs, ks);
+    const double lzt = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, (double)zt, ks);
+    RowK k;
+    k.cs = refc(ms, ks);
+    k.ct = refc(mt, ks);
+    k.undefined = undefined;
+    double Zs = 1.0, Zt = 1.0;
+    k.gam = k.rf = 0.0f;
+    if (!undefined) {
+        Zs = z_from_stats(ms, lzs, ks);
+        Zt = z_from_stats(mt, lzt, ks);
+        k.gam = (float)((1.0 - beta) * Zt / Zs);
+        k.rf = (float)log2(Zs / Zt);
+    }
+    k.izs = (float)(1.0 / Zs);
+    k.izt = (float)(1.0 / Zt);
+    if ((threadIdx.x & 63) == 0) {
+        st[0] = ms;
+        st[1] = lzs;
+        st[2] = mt;
+        st[3] = lzt;
+        *out = k;
+    }
 }
 
 // One workgroup per row.  Lane l holds vectors l, l + FB, ... of each input; slots past
@@ -154,29 +190,20 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
         zt += eb[0];
     }
     block_sum2(zs, zt, red);
-    const bool undefined = ms == NINF || mt == NINF;
-    const double lzs = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, (double)zs, o.ks);
-    const double lzt = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, (double)zt, o.ks);
-    if (threadIdx.x == 0) {
-        double *o = stats + r * 4;
-        o[0] = ms;
-        o[1] = lzs;
-        o[2] = mt;
-        o[3] = lzt;
-    }
-    // ---- divergence: row constants from the stored statistics, terms from registers
+    __shared__ RowK rk;
+    if (threadIdx.x < 64) row_constants(ms, zs, mt, zt, beta, o.ks, stats + r * 4, &rk);
+    __syncthreads();
+    const RowK k = rk;
+    // ---- divergence: terms from registers
     float pt = 0.0f, ps = 0.0f;
-    double Zs = 1.0, Zt = 1.0;
-    if (!undefined) {
-        Zs = z_from_stats(ms, lzs, o.ks);
-        Zt = z_from_stats(mt, lzt, o.ks);
+    if (!k.undefined) {
         OpDivRegs<INTERIOR> op;
         op.ks = o.ks;
-        op.cs = cs;
-        op.ct = ct;
+        op.cs = k.cs;
+        op.ct = k.ct;
         op.bf = (float)beta;
-        op.gam = (float)((1.0 - beta) * Zt / Zs);
-        op.rf = (float)log2(Zs / Zt);
+        op.gam = k.gam;
+        op.rf = k.rf;
 #pragma unroll
         for (int i = 0; i < NVT; ++i) {
             opaque(xs[i]);
@@ -194,14 +221,15 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
     }
     block_sum2(pt, ps, red);
     if (threadIdx.x == 0)
-        finalize_row(INTERIOR, beta, undefined, pt * (float)(1.0 / Zt), ps * (float)(1.0 / Zs),
-                     NINF, kl + 2 * r, loss + r, o.lscale);
+        finalize_row(INTERIOR, beta, k.undefined, pt * k.izt, ps * k.izs, NINF, kl + 2 * r,
+                     loss + r, o.lscale);
 }
 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
-// TWICE_BLK lanes, so that two workgroups fill a CU: about 512 rows are in flight, few
-// enough that much of the second sweep is served by the caches.  The first sweep reads
-// with the default cache policy (its data is wanted again), the second streams.
+// TWICE_BLK lanes, two workgroups per CU (about 512 rows in flight); 256- and
+// 1024-lane workgroups measured slower.  Both sweeps are bound by HBM reads: the
+// arithmetic alone takes a sixth of the time.  The first sweep reads with the default
+// cache policy, the second streams.
 constexpr int TWICE_BLK = 512;
 
 template <class D>
@@ -211,7 +239,7 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
                                                          float *__restrict__ kl,
                                                          float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
-    __shared__ float red[2 * (TWICE_BLK / 64)];
+    __shared__ float red[4 * (TWICE_BLK / 64)];
     const int64_t r = blockIdx.x;
     if (row_dropped(o, r)) {
         dropped_row(stats + r * 4, kl + 2 * r, loss + r);
@@ -221,38 +249,48 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
     const int64_t h = head_len<T>(w, s, t);
     OpStats<3> o1(o.ks);
     sweep<D, 4, true, TWICE_BLK>(s, t, w, h, o1);
-    const MZ ms = block_mz<TWICE_BLK>(MZ{o1.a.m, o1.a.z}, red, o.ks);
-    const MZ mt = block_mz<TWICE_BLK>(MZ{o1.b.m, o1.b.z}, red, o.ks);
-    const bool undefined = ms.m == NINF || mt.m == NINF;
-    const double lzs = ms.m == NINF ? -__builtin_inf() : lnz_from_z(ms.m, (double)ms.z, o.ks);
-    const double lzt = mt.m == NINF ? -__builtin_inf() : lnz_from_z(mt.m, (double)mt.z, o.ks);
-    if (threadIdx.x == 0) {
-        double *o = stats + r * 4;
-        o[0] = ms.m;
-        o[1] = lzs;
-        o[2] = mt.m;
-        o[3] = lzt;
+    // wave partials, then wave 0 combines them in wave order and derives the constants
+    constexpr int NW = TWICE_BLK / 64;
+    __shared__ RowK rk;
+    {
+        const MZ ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
+        const MZ wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) {
+            red[2 * wave] = ws.m;
+            red[2 * wave + 1] = ws.z;
+            red[2 * NW + 2 * wave] = wt.m;
+            red[2 * NW + 2 * wave + 1] = wt.z;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            MZ ms{red[0], red[1]}, mt{red[2 * NW], red[2 * NW + 1]};
+            for (int k = 1; k < NW; ++k) {
+                ms = mz_combine(ms, MZ{red[2 * k], red[2 * k + 1]}, o.ks);
+                mt = mz_combine(mt, MZ{red[2 * NW + 2 * k], red[2 * NW + 2 * k + 1]}, o.ks);
+            }
+            row_constants(ms.m, ms.z, mt.m, mt.z, beta, o.ks, stats + r * 4, &rk);
+        }
+        __syncthreads();
     }
+    const RowK k = rk;
     float v[2] = {0.0f, 0.0f};
-    double Zs = 1.0, Zt = 1.0;
-    if (!undefined) {
-        Zs = z_from_stats(ms.m, lzs, o.ks);
-        Zt = z_from_stats(mt.m, lzt, o.ks);
+    if (!k.undefined) {
         OpDiv<INTERIOR> op;
         op.ks = o.ks;
-        op.cs = refc(ms.m, o.ks);
-        op.ct = refc(mt.m, o.ks);
+        op.cs = k.cs;
+        op.ct = k.ct;
         op.bf = (float)beta;
-        op.gam = (float)((1.0 - beta) * Zt / Zs);
-        op.rf = (float)log2(Zs / Zt);
+        op.gam = k.gam;
+        op.rf = k.rf;
         sweep<D, 4, true, TWICE_BLK, true>(s, t, w, h, op);
         v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
         v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
     }
     block_sum<2, TWICE_BLK>(v, red);
     if (threadIdx.x == 0)
-        finalize_row(INTERIOR, beta, undefined, v[0] * (float)(1.0 / Zt),
-                     v[1] * (float)(1.0 / Zs), NINF, kl + 2 * r, loss + r, o.lscale);
+        finalize_row(INTERIOR, beta, k.undefined, v[0] * k.izt, v[1] * k.izs, NINF, kl + 2 * r,
+                     loss + r, o.lscale);
 }
 
 template <class D, int NVT>
