@@ -59,8 +59,11 @@ def check(s, t, beta, widths=None):
 
 
 # 1000 / 4096 / 8192 / 16032 / 16384: the row held in registers (1, 2, 4, 8 vectors
-# per lane); 16392 and wider: the row swept twice
-@pytest.mark.parametrize("V", [1000, 4096, 8192, 16032, 16384, 16392, 151936])
+# per lane); 16392 and wider: the row swept twice (135160 / 135168 / 135176 leave 511,
+# 512 and 513 vectors after the last whole step of 4 vectors per lane of the 512-lane
+# workgroup)
+@pytest.mark.parametrize("V", [1000, 4096, 8192, 16032, 16384, 16392, 135160, 135168, 135176,
+                               151936])
 @pytest.mark.parametrize("beta", [0.5, 0.0, 1.0])
 def test_one_pass_forward_bf16(V, beta):
     b = synth.draw("full_vocab", device="cuda", N=40, V=V)
@@ -78,6 +81,29 @@ def test_one_pass_forward_other_dtypes(dtype, V):
 def test_one_pass_forward_batch_sizes(N):
     b = synth.draw("full_vocab", device="cuda", N=N, V=16032)
     check(b.s, b.t, 0.9)
+
+
+# wide rows in batches larger than the number of CUs
+@pytest.mark.parametrize("N,V", [(700, 20000), (300, 140000)])
+def test_swept_twice_forward_large_batches(N, V):
+    b = synth.draw("full_vocab", device="cuda", N=N, V=V)
+    check(b.s, b.t, 0.7)
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.float32, 40000), (torch.bfloat16, 140000)])
+def test_swept_twice_forward_masks_and_undefined_rows(dtype, V):
+    b = synth.draw("robust", device="cuda", N=20, V=V)
+    s, t = b.s.to(dtype), b.t.to(dtype)
+    s[7] = NINF  # student undefined
+    t[8] = NINF  # teacher undefined
+    s[9, 50:] = NINF  # partly masked
+    s[10, :V - 3] = NINF  # mass only in the last three columns (the sweeps' scalar tail)
+    s[11, 123] = NINF  # forward KL of row 11 infinite
+    t[11, 123] = 1.0
+    loss = check(s, t, 0.5)
+    assert np.isnan(loss.numpy()[[7, 8]]).all()
+    lf = check(s, t, 0.0)
+    assert np.isinf(lf.numpy()[11])
 
 
 def test_one_pass_forward_masks_offsets_undefined_rows():
