@@ -227,9 +227,9 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
 // TWICE_BLK lanes, two workgroups per CU (about 512 rows in flight); 256- and
-// 1024-lane workgroups measured slower.  Both sweeps are bound by HBM reads: the
-// arithmetic alone takes a sixth of the time.  The first sweep reads with the default
-// cache policy, the second streams.
+// 1024-lane workgroups measured slower.  The arithmetic and the two reads take about
+// as long as each other, so the kernel is bound by both.  The first sweep reads with
+// the default cache policy, the second streams.
 constexpr int TWICE_BLK = 512;
 
 template <class D>
