@@ -274,7 +274,7 @@ def main():
     per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas}
     log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
 
-    three = branches = siblings = tp8 = linear = None
+    three = branches = siblings = tp8 = linear = configs = None
     if not args.no_extras:
         # the same forward as three separate launches (statistics, merge, divergence),
         # timed one by one for comparison with the one-launch forward above
@@ -340,6 +340,7 @@ def main():
     if not args.no_extras:
         siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
         tp8 = tp8_forward(torch, vj, synth)
+        configs = config_rows(torch, vj, synth)
         linear = None if args.no_linear else fused_linear_row(torch, vj, synth)
 
     out = {
@@ -377,6 +378,7 @@ def main():
         "clocks": clock_state(),
         "forward_parts_ms": three,
         "tp8_shard": tp8,
+        "other_configs": configs,
         "step_ms_by_beta": per_beta,
         "branches": branches,
         "siblings": siblings,
@@ -465,6 +467,66 @@ def tp8_forward(torch, vj, synth, reps=10):
     res["bwd_gbps"] = round(4 * tb / (res["bwd_ms"] * 1e-3) / 1e9, 1)
     res["tokens_per_s"] = round(N / ((res["one_pass_forward_ms"] + res["bwd_ms"]) * 1e-3), 1)
     return res
+
+
+def config_rows(torch, vj, synth, reps=10):
+    """The other configurations of the path, each fwd+bwd with both gradients unless
+    stated: the tiny fp32 case (launch-latency bound, no roofline meaning), one
+    tensor-parallel rank's width with the teacher detached (student gradient only),
+    and the robustness mix (fp32, four column-slice shards of widths 60000/0/40000/28256
+    merged on the device, masked columns and rows, offset rows) beside the same data
+    as one shard.  Bytes as the pages count them: 3 input passes over s and t plus
+    the gradient writes."""
+    def timed(fn):
+        fn()
+        fn()
+        tm = Timer(torch)
+        for _ in range(reps):
+            a = tm.mark()
+            fn()
+            tm.add("x", a, tm.mark())
+        torch.cuda.synchronize()
+        return tm.ms("x")
+
+    def run(b, widths, beta, student_only=False):
+        N, V = b.s.shape
+        S = 1 if widths is None else len(widths)
+        part = vj.new_part(N, S, "cuda")
+        stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
+        kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
+        loss = torch.empty((N,), dtype=torch.float32, device="cuda")
+        gs = torch.empty_like(b.s)
+        gt = None if student_only else torch.empty_like(b.t)
+        sh = vj.ShardSet(b.s, b.t, widths=widths)
+        shg = vj.ShardSet(b.s, b.t, widths=widths, gs=gs, gt=gt)
+        fwd = lambda: vj.vjsd_forward(sh, beta, part, stats, kl, loss)
+        bwd = lambda: vj.vjsd_bwd(shg, stats, kl, beta, b.gout, part)
+        f_ms = timed(fwd)
+        b_ms = timed(bwd)
+        step = timed(lambda: (fwd(), bwd()))
+        tb = N * V * b.s.element_size()
+        nbytes = 6 * tb + (1 if student_only else 2) * tb
+        return {"N": N, "V": V, "shards": S, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+                "fwd_bwd_ms": round(step, 4), "tokens_per_s": round(N / (step * 1e-3), 1),
+                "bytes_alg": nbytes, "hbm_gbps": round(nbytes / (step * 1e-3) / 1e9, 1),
+                "hbm_frac": round(nbytes / (step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+
+    rows = {}
+    b = synth.draw("tiny", device="cuda")
+    r = run(b, None, 0.5)
+    rows["tiny_fp32"] = {k: r[k] for k in ("N", "V", "fwd_ms", "bwd_ms", "fwd_bwd_ms",
+                                           "tokens_per_s")}
+    b = synth.draw("tp8_shard", device="cuda")
+    rows["tp8_shard_teacher_detached"] = run(b, None, 0.5, student_only=True)
+    del b
+    torch.cuda.empty_cache()
+    w = synth.WORKLOADS["robust"]
+    b = synth.draw("robust", device="cuda")
+    rows["robust_fp32_4_shards"] = run(b, list(w.widths), 0.5)
+    rows["robust_fp32_1_shard"] = run(b, None, 0.5)
+    del b
+    torch.cuda.empty_cache()
+    return rows
 
 
 def sibling_rows(torch, vj, synth, reps=3):
