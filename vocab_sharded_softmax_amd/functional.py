@@ -53,11 +53,11 @@ class _JSD(torch.autograd.Function):
         part = _abi.new_part(N, S, dev)
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
         kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
-        loss = torch.empty((N,), dtype=torch.float32, device=dev)
+        loss = torch.empty(sh.lead_shape, dtype=torch.float32, device=dev)
         _abi.vjsd_forward(sh, beta, part, stats, kl, loss)
         ctx.beta, ctx.split, ctx.n_shards = beta, split, n_shards
         ctx.save_for_backward(stats, kl, *tensors)
-        return loss.view(sh.lead_shape)
+        return loss
 
     @staticmethod
     @once_differentiable
@@ -92,12 +92,12 @@ class _JSDLoss(torch.autograd.Function):
         part = _abi.new_part(N, S, dev)
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
         kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
-        rows = torch.empty((N,), dtype=torch.float32, device=dev)
-        out = torch.empty((1,), dtype=torch.float32, device=dev) if reduction != "none" else None
+        rows = torch.empty(sh.lead_shape, dtype=torch.float32, device=dev)
+        out = torch.empty((), dtype=torch.float32, device=dev) if reduction != "none" else None
         _abi.vjsd_loss_forward(sh, beta, opts, part, stats, kl, rows, out)
         ctx.args = (beta, temperature, scale_t2, reduction, split, n_shards)
         ctx.save_for_backward(stats, kl, mask, *tensors)
-        return rows.view(sh.lead_shape) if out is None else out.view(())
+        return rows if out is None else out
 
     @staticmethod
     @once_differentiable
@@ -132,11 +132,11 @@ class _KL(torch.autograd.Function):
         part = _abi.new_part(N, S, dev)
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
         kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
-        loss = torch.empty((N,), dtype=torch.float32, device=dev)
+        loss = torch.empty(sh.lead_shape, dtype=torch.float32, device=dev)
         _abi.vkl_fwd(sh, reverse, part, stats, kl, loss)
         ctx.reverse, ctx.split, ctx.n_shards = reverse, split, n_shards
         ctx.save_for_backward(stats, kl, *tensors)
-        return loss.view(sh.lead_shape)
+        return loss
 
     @staticmethod
     @once_differentiable
@@ -167,11 +167,12 @@ class _Entropy(torch.autograd.Function):
         N, S = sh.N, sh.S
         part = _abi.new_part(N, S, dev)
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
-        ent = torch.empty((N,), dtype=torch.float32, device=dev)
+        ent = torch.empty(sh.lead_shape, dtype=torch.float32, device=dev)
         _abi.ventropy_fwd(sh, part, stats, ent)
         ctx.split, ctx.n_shards = split, n_shards
-        ctx.save_for_backward(stats, ent, *tensors)
-        return ent.view(sh.lead_shape)
+        # the backward reads H from its own copy: the caller may overwrite the output
+        ctx.save_for_backward(stats, ent.clone(), *tensors)
+        return ent
 
     @staticmethod
     @once_differentiable
@@ -197,7 +198,7 @@ class _Logprobs(torch.autograd.Function):
         idv = ids.reshape(N, K).to(torch.int64).contiguous()
         part = _abi.new_part(N, S, dev)
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
-        out = torch.empty((N, K), dtype=torch.float32, device=dev)
+        out = torch.empty((*sh.lead_shape, K), dtype=torch.float32, device=dev)
         err = torch.zeros((1,), dtype=torch.int32, device=dev)
         _abi.vlogprobs_fwd(sh, sh.V, idv, ignore_index, part, stats, out, err)
         # the range check runs every call; it needs this host synchronisation
@@ -205,7 +206,7 @@ class _Logprobs(torch.autograd.Function):
             raise ValueError("logprobs: an index is outside [0, V) and is not ignore_index")
         ctx.ignore_index, ctx.split, ctx.n_shards, ctx.V = ignore_index, split, n_shards, sh.V
         ctx.save_for_backward(stats, idv, *tensors)
-        return out.view(*sh.lead_shape, K)
+        return out
 
     @staticmethod
     @once_differentiable
@@ -233,14 +234,14 @@ class _TopkKL(torch.autograd.Function):
         tl = tlogp.reshape(N, K).to(torch.float32).contiguous()
         part = _abi.new_part(N, S, dev)
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
-        kl = torch.empty((N,), dtype=torch.float32, device=dev)
+        kl = torch.empty(sh.lead_shape, dtype=torch.float32, device=dev)
         err = torch.zeros((1,), dtype=torch.int32, device=dev)
         _abi.vtopk_kl_fwd(sh, sh.V, idv, tl, ignore_index, part, stats, kl, err)
         if N and K and int(err.item()):
             raise ValueError("topk_kl: an index is outside [0, V) and is not ignore_index")
         ctx.ignore_index, ctx.split, ctx.n_shards, ctx.V = ignore_index, split, n_shards, sh.V
         ctx.save_for_backward(stats, idv, tl, *tensors)
-        return kl.view(sh.lead_shape)
+        return kl
 
     @staticmethod
     @once_differentiable
@@ -266,15 +267,15 @@ class _CrossEntropy(torch.autograd.Function):
         lab = labels.reshape(N).to(torch.int64).contiguous()
         part = _abi.new_part(N, S, dev)
         stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
-        rows = torch.empty((N,), dtype=torch.float32, device=dev)
-        out = torch.empty((1,), dtype=torch.float32, device=dev) if reduction != "none" else None
+        rows = torch.empty(sh.lead_shape, dtype=torch.float32, device=dev)
+        out = torch.empty((), dtype=torch.float32, device=dev) if reduction != "none" else None
         err = torch.zeros((1,), dtype=torch.int32, device=dev)
         _abi.vce_fwd(sh, sh.V, lab, ignore_index, reduction, part, stats, rows, out, err)
         if N and int(err.item()):
             raise ValueError("cross_entropy: a label is outside [0, V) and is not ignore_index")
         ctx.args = (ignore_index, reduction, split, n_shards, sh.V)
         ctx.save_for_backward(stats, lab, *tensors)
-        return rows.view(sh.lead_shape) if out is None else out.view(())
+        return rows if out is None else out
 
     @staticmethod
     @once_differentiable
@@ -432,14 +433,14 @@ class _LinearJSD(torch.autograd.Function):
         C = max(1, min(int(chunk), max(N, 1)))
         nbytes = _abi.vljsd_workspace_bytes(N, V, hs.shape[1], C, group)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        out = torch.empty((N if reduction == "none" else 1,), dtype=torch.float32, device=dev)
+        out = torch.empty((N,) if reduction == "none" else (), dtype=torch.float32, device=dev)
         gh = torch.empty(hs.shape, dtype=hs.dtype, device=dev) if want_h else None
         gw = torch.empty(ws.shape, dtype=ws.dtype, device=dev) if want_w else None
         _abi.vljsd(student, teacher, N, V, beta, opts, C, workspace, out, gh, gw, group=group)
         del workspace
         ctx.save_for_backward(gh, gw)
         ctx.used = False
-        return out if reduction == "none" else out.view(())
+        return out
 
     @staticmethod
     @once_differentiable
