@@ -255,6 +255,34 @@ def test_large_offset_rows():
     assert_values(g["loss"][::2], ref0["loss"], torch.float32, "offset rows vs unshifted")
 
 
+
+@pytest.mark.parametrize("beta", [0.0, 0.4, 1.0])
+@pytest.mark.parametrize("widths", [None, [1700, 0, 3300]])
+def test_independent_large_shifts(beta, widths):
+    """[JSD-PR, Validation]: independent large logit shifts.  Every row of each input
+    gets its own offset (+-1e4, 3e3, -5e3 or none), so student and teacher rows sit
+    far apart; each softmax is shift-invariant, so the oracle is the unshifted rows
+    (recovered exactly: fl32(x + a) - a is exact by Sterbenz for |x| << |a|), for the
+    loss and both gradients, on the pass-by-pass route, and for the loss on the
+    one-call forward of the autograd op."""
+    v = vj()
+    b = synth.draw("tiny", device="cuda", N=16, V=5000)
+    gen = torch.Generator().manual_seed(31)
+    offs = torch.tensor([1e4, -1e4, 3e3, -5e3, 0.0])
+    a = offs[torch.randint(0, 5, (16,), generator=gen)].cuda()[:, None]
+    c = offs[torch.randint(0, 5, (16,), generator=gen)].cuda()[:, None]
+    assert not torch.equal(a, c)
+    s, t = b.s + a, b.t + c
+    s0, t0 = s - a, t - c
+    assert torch.equal(s0 + a, s) and torch.equal(t0 + c, t)
+    g = run_jsd(s, t, beta, widths, b.gout)
+    ref = oracle.jsd(s0.cpu(), t0.cpu(), beta, widths=widths, gout=b.gout.cpu().double().numpy())
+    assert_values(g["loss"], ref["loss"], torch.float32, "shifted rows vs unshifted")
+    assert_grads(g["gs"], ref["gs"], torch.float32, "d/ds of shifted rows")
+    assert_grads(g["gt"], ref["gt"], torch.float32, "d/dt of shifted rows")
+    loss = v.jsd(s, t, beta, split=widths)
+    assert_values(loss, ref["loss"], torch.float32, "one-call forward of shifted rows")
+
 def test_reruns_are_bitwise_identical():
     b = synth.draw("full_vocab", device="cuda", N=64, V=30011)
     g1 = run_jsd(b.s, b.t, 0.5, None, b.gout)
