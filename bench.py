@@ -271,7 +271,9 @@ def main():
     bwd_ms = timer.ms("bwd")
     achieved = bytes_bwd / (bwd_ms * 1e-3) / 1e9
     per_kernel = {k: round(timer.ms(k), 4) for k in ("forward", "bwd", "step")}
-    per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas}
+    # betas that no timed step reached (fewer steps than betas) are left out
+    per_beta = {str(bt): round(timer.ms(f"step_beta{bt}"), 4) for bt in betas
+                if timer.spans.get(f"step_beta{bt}")}
     log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
 
     three = branches = siblings = tp8 = linear = configs = None
