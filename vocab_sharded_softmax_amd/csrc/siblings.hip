@@ -503,6 +503,13 @@ __global__ void k_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *__r
     o[3] = (float)G;
 }
 
+// The value v holds in lane q (q uniform across the wave).
+__device__ __forceinline__ int64_t lane_value(int64_t v, int q) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, q);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), q);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 template <class D>
 __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, int64_t start,
                                                        int64_t w, int64_t cw, int64_t nchunk,
@@ -525,6 +532,40 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, 
     // the chunk's loads instead of trailing them
     const int64_t *id = ids + r * K;
     const int64_t id0 = (int)threadIdx.x < K ? id[threadIdx.x] : ignore;
+    constexpr int VEC = D::VEC;
+    if (K <= GRAD_BLOCK && n == (int64_t)GRAD_BLOCK * VEC && head_len<T>(n, x, gx) == 0) {
+        // A whole chunk of aligned vectors (every chunk but a row's last): one vector
+        // per lane, every id in one lane.  A ballot over the ids finds the few this
+        // chunk owns, their values are written into the registers, and the chunk is
+        // stored once: no fix-up store has to wait for the streamed one to land.
+        const int lane = threadIdx.x;
+        const u32x4 raw = ld16<true>(x + lane * VEC);
+        const int64_t j0 = id0 - start - c0;
+        uint64_t hits = __ballot(lane < K && id0 != ignore && j0 >= 0 && j0 < n);
+        float xv[VEC], o[VEC];
+        widen<D>(raw, xv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = k[1] * ex2(fmaxf(fmaf(xv[e], L2E, -k[0]), U_FLOOR));
+        while (hits) {  // uniform: the ids this chunk owns, usually none
+            const int q = __builtin_ctzll(hits);
+            hits &= hits - 1;
+            const int64_t idq = lane_value(id0, q);
+            float gsum = 0.0f;  // repeated ids accumulate, in slot order
+            for (int q2 = 0; q2 < K; ++q2)
+                if (lane_value(id0, q2) == idq) gsum += lp_weight(wts, r, K, q2);
+            const int64_t j = idq - start - c0;
+            if (lane == (int)(j / VEC)) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    if (e == (int)(j % VEC)) {
+                        const float p = ex2(fmaxf(fmaf(xv[e], L2E, -k[0]), U_FLOOR)) * k[2];
+                        o[e] = gsum - k[3] * p;
+                    }
+            }
+        }
+        store_vec<D, true>(gx + lane * VEC, o);
+        return;
+    }
     OpLpBwd<D> op;
     op.gx = gx;
     op.c = k[0];
