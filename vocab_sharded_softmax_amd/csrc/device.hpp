@@ -219,6 +219,24 @@ __device__ __forceinline__ int64_t head_len(int64_t w, const void *a, const void
     return h < w ? h : w;
 }
 
+// Chunk q of a row of w elements: columns [c0, c0 + n); n <= 0 past the row's end.
+// ALIGNED puts chunk boundaries at multiples of cw elements of the address space of
+// `row` (the first chunk runs from the row start to the first boundary), so that no
+// wave's 1 KiB request straddles two 1 KiB blocks where a row's size is not a multiple
+// of 1 KiB (a 151936-wide bf16 row is 296.75 KiB).  On MI355X that made the two-read,
+// two-write JSD backward 2-4 % faster and the one-read, one-write backwards 2-3 %
+// slower, so each kernel chooses.  cw is a power of two (a mask, not a 64-bit
+// division, finds the row's offset inside a chunk).
+template <bool ALIGNED, class T>
+__device__ __forceinline__ void chunk_span(const T *row, int64_t w, int64_t cw, int64_t q,
+                                           int64_t &c0, int64_t &n) {
+    const int64_t lead =
+        ALIGNED ? (int64_t)((reinterpret_cast<uintptr_t>(row) / sizeof(T)) & (uint64_t)(cw - 1)) : 0;
+    const int64_t a = q * cw - lead;
+    c0 = a > 0 ? a : 0;
+    n = (a + cw < w ? a + cw : w) - c0;
+}
+
 // ---- hardware exp2 / log2 and the base-2 reference point ---------------------------
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -220,8 +220,8 @@ __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats
     o[ROWC_UNDEFINED] = (k.undefined || dropped) ? 1.0f : 0.0f;
 }
 
-// One wave per row chunk of cw columns; the chunks of a row are consecutive workgroups,
-// so the whole grid streams through memory in order.
+// One wave per row chunk of up to cw columns (chunk_span); the chunks of a row are
+// consecutive workgroups, so the whole grid streams through memory in order.
 template <class D, int MODE, bool WS, bool WT, class DG = D>
 __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowMView gsv,
                                                     RowMView gtv, int64_t w, int64_t cw,
@@ -230,8 +230,10 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
     using TG = typename DG::T;
     const int64_t b = blockIdx.x;
     const int64_t r = b / nchunk;
-    const int64_t c0 = (b - r * nchunk) * cw;
-    const int64_t n = w - c0 < cw ? w - c0 : cw;
+    const T *srow = row_ptr<T>(sv, r);
+    int64_t c0, n;
+    chunk_span<true>(srow, w, cw, b - r * nchunk, c0, n);
+    if (n <= 0) return;
     const float *k = rowc + r * ROWC;
     TG *gs = WS ? row_ptr<TG>(gsv, r) + c0 : nullptr;
     TG *gt = WT ? row_ptr<TG>(gtv, r) + c0 : nullptr;
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
         if (WT) zero_span<DG, GRAD_BLOCK>(gt, n);
         return;
     }
-    const T *s = row_ptr<T>(sv, r) + c0, *t = row_ptr<T>(tv, r) + c0;
+    const T *s = srow + c0, *t = row_ptr<T>(tv, r) + c0;
     OpBwd<D, MODE, WS, WT, DG> op;
     op.gs = gs;
     op.gt = gt;
@@ -282,7 +284,7 @@ hipError_t div_mode(int mode, const Shard &sh, int64_t N, const double *stats, d
 
 template <class D, int MODE, bool WS, bool WT>
 hipError_t bwd_k(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
-    const Chunks ch = grad_chunks(N, sh.width, sizeof(typename D::T));
+    const Chunks ch = grad_chunks<true>(N, sh.width, sizeof(typename D::T));
     if (ch.nchunk == 0) return hipSuccess;
     hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)(N * ch.nchunk)),
                        dim3(GRAD_BLOCK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
@@ -292,7 +294,7 @@ hipError_t bwd_k(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) 
 
 template <int MODE>
 hipError_t bwd_g16(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
-    const Chunks ch = grad_chunks(N, sh.width, sizeof(float));
+    const Chunks ch = grad_chunks<true>(N, sh.width, sizeof(float));
     if (ch.nchunk == 0) return hipSuccess;
     hipLaunchKernelGGL((k_bwd<F32, MODE, true, false, BF16>), dim3((unsigned)(N * ch.nchunk)),
                        dim3(GRAD_BLOCK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,

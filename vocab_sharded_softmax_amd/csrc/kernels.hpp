@@ -36,16 +36,23 @@ hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
 hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
                             float *kl, float *loss, hipStream_t st, const RowOpts &o = RowOpts());
 
-// Row chunks of the streaming gradient kernels: cw columns per workgroup (a multiple
-// of GRAD_BLOCK vectors), nchunk chunks per row, N * nchunk workgroups in all.
+// Row chunks of the streaming gradient kernels: cw columns per workgroup (GRAD_BLOCK
+// vectors times a power of two, so a power of two), nchunk chunks per row, N * nchunk
+// workgroups in all.  With ALIGNED, chunk boundaries sit at multiples of cw elements of
+// the address space (chunk_span), not of the row start, so a row may need one chunk
+// more than ceil(w / cw); a chunk past a row's end is empty.
 struct Chunks {
     int64_t cw, nchunk;
 };
+template <bool ALIGNED>
 inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
     const int64_t vec = 16 / esize;
     int64_t cw = GRAD_BLOCK * vec;
-    while (N * ((w + cw - 1) / cw) > 0x7fffffffLL) cw *= 2;  // grid.x limit
-    return {cw, w > 0 ? (w + cw - 1) / cw : 0};
+    auto count = [w](int64_t c) {
+        return w <= 0 ? (int64_t)0 : ALIGNED ? (w + 2 * c - 2) / c : (w + c - 1) / c;
+    };
+    while (N * count(cw) > 0x7fffffffLL) cw *= 2;  // grid.x limit
+    return {cw, count(cw)};
 }
 
 // Upstream-gradient options of the distillation-loss form of the backward: the row

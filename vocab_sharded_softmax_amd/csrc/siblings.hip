@@ -350,15 +350,17 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_ent_bwd(RowView xv, RowMView gv,
     using T = typename D::T;
     const int64_t b = blockIdx.x;
     const int64_t r = b / nchunk;
-    const int64_t c0 = (b - r * nchunk) * cw;
-    const int64_t n = w - c0 < cw ? w - c0 : cw;
+    const T *xrow = row_ptr<T>(xv, r);
+    int64_t c0, n;
+    chunk_span<false>(xrow, w, cw, b - r * nchunk, c0, n);
+    if (n <= 0) return;
     const float *k = rowc + r * ROWC;
     T *gx = row_ptr<T>(gv, r) + c0;
     if (k[ROWC_UNDEFINED] != 0.0f) {
         zero_span<D, GRAD_BLOCK>(gx, n);
         return;
     }
-    const T *x = row_ptr<T>(xv, r) + c0;
+    const T *x = xrow + c0;
     OpEntBwd<D> op;
     op.gx = gx;
     op.c = k[0];
@@ -519,15 +521,17 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_lp_bwd(RowView xv, RowMView gv, 
     using T = typename D::T;
     const int64_t b = blockIdx.x;
     const int64_t r = b / nchunk;
-    const int64_t c0 = (b - r * nchunk) * cw;
-    const int64_t n = w - c0 < cw ? w - c0 : cw;
+    const T *xrow = row_ptr<T>(xv, r);
+    int64_t c0, n;
+    chunk_span<false>(xrow, w, cw, b - r * nchunk, c0, n);
+    if (n <= 0) return;
     const float *k = rowc + r * ROWC;
     T *gx = row_ptr<T>(gv, r) + c0;
     if (k[ROWC_UNDEFINED] != 0.0f) {
         zero_span<D, GRAD_BLOCK>(gx, n);
         return;
     }
-    const T *x = row_ptr<T>(xv, r) + c0;
+    const T *x = xrow + c0;
     // the first GRAD_BLOCK ids are loaded before the sweep, so their latency overlaps
     // the chunk's loads instead of trailing them
     const int64_t *id = ids + r * K;
@@ -640,7 +644,7 @@ hipError_t launch_ent_bwd_prep(int64_t N, const double *stats, const float *ent,
 
 hipError_t launch_ent_bwd(int dtype, const Shard &sh, int64_t N, const float *rowc,
                           hipStream_t st) {
-    const Chunks ch = grad_chunks(N, sh.width, dtype == 0 ? 4 : 2);
+    const Chunks ch = grad_chunks<false>(N, sh.width, dtype == 0 ? 4 : 2);
     if (ch.nchunk == 0) return hipSuccess;
     const dim3 grid((unsigned)(N * ch.nchunk)), block(GRAD_BLOCK);
     switch (dtype) {
@@ -676,7 +680,7 @@ hipError_t launch_lp_bwd_prep(int64_t N, int64_t vocab_global, const double *sta
 
 hipError_t launch_lp_bwd(int dtype, const Shard &sh, int64_t N, const int64_t *ids, int K,
                          int64_t ignore, const LpWeights &w, const float *rowc, hipStream_t st) {
-    const Chunks ch = grad_chunks(N, sh.width, dtype == 0 ? 4 : 2);
+    const Chunks ch = grad_chunks<false>(N, sh.width, dtype == 0 ? 4 : 2);
     if (ch.nchunk == 0) return hipSuccess;
     const dim3 grid((unsigned)(N * ch.nchunk)), block(GRAD_BLOCK);
     switch (dtype) {
