@@ -168,7 +168,11 @@ VJSD_API int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, con
  *                   Rows 16-byte aligned, a multiple of 16 bytes and at most
  *                   32 KiB wide (16384 bf16 / fp16 or 8192 fp32 columns) are held
  *                   in registers and read from HBM once; wider rows are swept twice
- *   several shards  the three separate launches
+ *   2 to 8 shards   one launch, a workgroup per row: each shard's slice is swept for
+ *                   its (max, sum-exp) pairs, the pairs are merged in shard order as
+ *                   vjsd_merge merges them, then the slices are swept for the
+ *                   divergence; `part` is not written
+ *   more shards     the three separate launches
  * Results agree with the separate calls within rounding (the reduction order
  * differs) and are deterministic for a given layout and device.  Errors as vjsd_fwd.
  */

@@ -2,7 +2,8 @@
 against the three separate launches, over dtypes, the beta = 0 / 1 branches (one-pass
 KL), row widths on both sides of the held-in-registers limit (16384 16-bit or 8192
 fp32 columns) and at each register-tile size below it, batch sizes, masks, offsets,
-unaligned rows (swept twice) and several shards (three launches)."""
+unaligned rows (swept twice) and several shards (one launch up to eight, three
+launches beyond)."""
 import numpy as np
 import pytest
 import torch
@@ -151,3 +152,57 @@ def test_autograd_uses_the_one_pass_forward():
     assert torch.equal(loss.detach().cpu(), ref)
     loss.sum().backward()
     assert torch.isfinite(s.grad.float()).all()
+
+
+# 2 to 8 shards run as one launch (per-shard statistics merged in the workgroup), 9
+# and more as the three launches; single-column, empty and all-but-one-empty shards
+@pytest.mark.parametrize("widths", [[9000, 11000], [1, 0, 19999], [2500] * 8,
+                                    [2000] * 8 + [4000], [0, 0, 20000, 0],
+                                    [7, 3, 5000, 0, 14990]])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_sharded_forward(dtype, widths):
+    V = sum(widths)
+    b = synth.draw("robust", device="cuda", N=37, V=V)
+    s, t = b.s.to(dtype).clone(), b.t.to(dtype).clone()
+    s[5] = NINF  # student undefined
+    t[6] = NINF  # teacher undefined
+    s[7, 100:] = NINF  # partly masked, across shard boundaries
+    t[8, 2000:2600] = NINF
+    loss = check(s, t, 0.4, widths=widths)
+    assert np.isnan(loss.numpy()[[5, 6]]).all()
+    assert np.isfinite(np.delete(loss.numpy(), [5, 6])).all()
+
+
+def test_sharded_forward_separate_tensors():
+    """Per-shard tensors with their own allocations and alignments (one shard's rows
+    start 2 bytes past a 16-byte boundary), against the oracle on the concatenation."""
+    v = vj()
+    b = synth.draw("full_vocab", device="cuda", N=29, V=30001)
+    cuts = [0, 7001, 7001, 19000, 30001]
+    ws = [cuts[i + 1] - cuts[i] for i in range(4)]
+    ss, ts = [], []
+    for i in range(4):
+        a, c = cuts[i], cuts[i + 1]
+        if i == 2:  # an unaligned view of a wider buffer
+            bs = torch.empty((29, c - a + 1), dtype=b.s.dtype, device="cuda")
+            bt = torch.empty((29, c - a + 1), dtype=b.t.dtype, device="cuda")
+            bs[:, 1:] = b.s[:, a:c]
+            bt[:, 1:] = b.t[:, a:c]
+            ss.append(bs[:, 1:])
+            ts.append(bt[:, 1:])
+        else:
+            ss.append(b.s[:, a:c].contiguous())
+            ts.append(b.t[:, a:c].contiguous())
+    sh = v.ShardSet(ss, ts)
+    N = 29
+    part = v.new_part(N, 4, "cuda")
+    stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
+    kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
+    loss = torch.empty((N,), dtype=torch.float32, device="cuda")
+    v.vjsd_forward(sh, 0.6, part, stats, kl, loss)
+    torch.cuda.synchronize()
+    sc, tc = b.s.cpu(), b.t.cpu()
+    ref = oracle.jsd(sc, tc, 0.6, widths=ws, grads=False)
+    assert_values(loss.cpu(), ref["loss"], b.s.dtype, "loss")
+    assert_stats(stats.cpu(), *oracle.stats(sc, widths=ws), 0, "student stats")
+    assert_stats(stats.cpu(), *oracle.stats(tc, widths=ws), 1, "teacher stats")

@@ -392,6 +392,11 @@ int vjsd_loss_forward(const vjsd_shard *shards, int S, int64_t N, int dtype, dou
         Shard sh = convert(shards[0], true, false);
         if ((e = hip_status(vjsd::launch_fwd_fused(dtype, sh, N, beta, stats, kl, rows, st, ro))))
             return e;
+    } else if (S <= vjsd::FUSED_SHARDS) {
+        Shard sh[vjsd::FUSED_SHARDS];
+        for (int k = 0; k < S; ++k) sh[k] = convert(shards[k], true, false);
+        if ((e = hip_status(vjsd::launch_fwd_shards(dtype, sh, S, N, beta, stats, kl, rows, st, ro))))
+            return e;
     } else {
         for (int k = 0; k < S; ++k) {
             Shard sh = convert(shards[k], true, false);

@@ -1,4 +1,4 @@
-// fused.hip -- the interior JSD forward of a single shard in one launch.
+// fused.hip -- the interior JSD forward in one launch.
 //
 // [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel generalized JSD with
 // Triton kernels", section Scope and limitations: the JSD needs the global normaliser
@@ -11,6 +11,8 @@
 //   k_fwd_twice  wider rows: the workgroup sweeps its row for the statistics, then
 //                sweeps it again for the divergence terms; the merge launch and two
 //                kernel boundaries go away, the second read stays
+//   k_fwd_shards the same for a row split into up to FUSED_SHARDS logical shards:
+//                per-shard statistics merged in the workgroup, then the divergence
 // The row constants are rebuilt from the fp64 statistics exactly as the separate
 // passes rebuild them.  Splitting a row over several workgroups would need a
 // device-wide exchange per row; on MI355X the cache write-back and invalidation that a
@@ -90,11 +92,11 @@ struct RowK {
 // Run by one whole wave: the fp64 steps are the costliest part of a row's finish, so
 // one wave takes them and the others read the result from LDS.  Lane 0 stores the
 // row's statistics and the constants.
-__device__ __forceinline__ void row_constants(float ms, float zs, float mt, float zt,
+__device__ __forceinline__ void row_constants(float ms, double zs, float mt, double zt,
                                               double beta, float ks, double *st, RowK *out) {
     const bool undefined = ms == NINF || mt == NINF;
-    const double lzs = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, (double)zs, ks);
-    const double lzt = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, (double)zt, ks);
+    const double lzs = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, zs, ks);
+    const double lzt = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, zt, ks);
     RowK k;
     k.cs = refc(ms, ks);
     k.ct = refc(mt, ks);
@@ -293,6 +295,98 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
                      loss + r, o.lscale);
 }
 
+
+// Several logical shards of a row, one launch: the workgroup sweeps each shard's slice
+// for that shard's (max, sum-exp) pair of each input, merges the pairs in shard order
+// exactly as the merge launch does (maximum of the maxima, then the rescaled sums in
+// fp64; an empty shard adds nothing), then sweeps the slices again for the divergence
+// terms.  The pages' cross-rank reductions of [N] statistics become this in-workgroup
+// merge when all shards sit on one device [JSD-PR, Changes; OPS-PR, How].
+template <class D>
+__global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double beta,
+                                                          double *__restrict__ stats,
+                                                          float *__restrict__ kl,
+                                                          float *__restrict__ loss, RowOpts o) {
+    using T = typename D::T;
+    constexpr int NW = TWICE_BLK / 64;
+    __shared__ float red[4 * NW];
+    __shared__ float sp[FUSED_SHARDS][4];  // per shard: (m_s, z_s, m_t, z_t)
+    const int64_t r = blockIdx.x;
+    if (row_dropped(o, r)) {
+        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
+        return;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int q = 0; q < sr.S; ++q) {
+        OpStats<3> o1(o.ks);
+        const int64_t w = sr.w[q];
+        if (w > 0) {
+            const T *s = row_ptr<T>(sr.s[q], r), *t = row_ptr<T>(sr.t[q], r);
+            sweep<D, 4, true, TWICE_BLK>(s, t, w, head_len<T>(w, s, t), o1);
+        }
+        const MZ ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
+        const MZ wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
+        if (lane == 0) {
+            red[2 * wave] = ws.m;
+            red[2 * wave + 1] = ws.z;
+            red[2 * NW + 2 * wave] = wt.m;
+            red[2 * NW + 2 * wave + 1] = wt.z;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            MZ ms{red[0], red[1]}, mt{red[2 * NW], red[2 * NW + 1]};
+            for (int k = 1; k < NW; ++k) {
+                ms = mz_combine(ms, MZ{red[2 * k], red[2 * k + 1]}, o.ks);
+                mt = mz_combine(mt, MZ{red[2 * NW + 2 * k], red[2 * NW + 2 * k + 1]}, o.ks);
+            }
+            sp[q][0] = ms.m;
+            sp[q][1] = ms.z;
+            sp[q][2] = mt.m;
+            sp[q][3] = mt.z;
+        }
+        __syncthreads();
+    }
+    __shared__ RowK rk;
+    if (wave == 0) {
+        float ms = NINF, mt = NINF;
+        for (int q = 0; q < sr.S; ++q) {
+            ms = fmaxf(ms, sp[q][0]);
+            mt = fmaxf(mt, sp[q][2]);
+        }
+        const double cs = refc(ms, o.ks), ct = refc(mt, o.ks);
+        double zs = 0.0, zt = 0.0;
+        for (int q = 0; q < sr.S; ++q) {
+            if (sp[q][0] != NINF) zs += (double)sp[q][1] * exp2((double)refc(sp[q][0], o.ks) - cs);
+            if (sp[q][2] != NINF) zt += (double)sp[q][3] * exp2((double)refc(sp[q][2], o.ks) - ct);
+        }
+        row_constants(ms, zs, mt, zt, beta, o.ks, stats + r * 4, &rk);
+    }
+    __syncthreads();
+    const RowK k = rk;
+    float v[2] = {0.0f, 0.0f};
+    if (!k.undefined) {
+        OpDiv<INTERIOR> op;
+        op.ks = o.ks;
+        op.cs = k.cs;
+        op.ct = k.ct;
+        op.bf = (float)beta;
+        op.gam = k.gam;
+        op.rf = k.rf;
+        for (int q = 0; q < sr.S; ++q) {
+            const int64_t w = sr.w[q];
+            if (w == 0) continue;
+            const T *s = row_ptr<T>(sr.s[q], r), *t = row_ptr<T>(sr.t[q], r);
+            sweep<D, 4, true, TWICE_BLK, true>(s, t, w, head_len<T>(w, s, t), op);
+        }
+        v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
+        v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
+    }
+    block_sum<2, TWICE_BLK>(v, red);
+    if (threadIdx.x == 0)
+        finalize_row(INTERIOR, beta, k.undefined, v[0] * k.izt, v[1] * k.izs, NINF, kl + 2 * r,
+                     loss + r, o.lscale);
+}
+
 template <class D, int NVT>
 hipError_t row_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
                       float *loss, hipStream_t st, const RowOpts &o) {
@@ -328,6 +422,26 @@ hipError_t fused_launch(const Shard &sh, int64_t N, double beta, double *stats, 
 }
 
 }  // namespace
+
+hipError_t launch_fwd_shards(int dtype, const Shard *sh, int S, int64_t N, double beta,
+                             double *stats, float *kl, float *loss, hipStream_t st,
+                             const RowOpts &o) {
+    if (S < 1 || S > FUSED_SHARDS) return hipErrorInvalidValue;
+    ShardRows sr{};
+    sr.S = S;
+    for (int q = 0; q < S; ++q) {
+        sr.w[q] = sh[q].width;
+        sr.s[q] = sh[q].s;
+        sr.t[q] = sh[q].t;
+    }
+    const dim3 grid((unsigned)N), block(TWICE_BLK);
+    switch (dtype) {
+        case 0: hipLaunchKernelGGL(k_fwd_shards<F32>, grid, block, 0, st, sr, beta, stats, kl, loss, o); break;
+        case 1: hipLaunchKernelGGL(k_fwd_shards<F16>, grid, block, 0, st, sr, beta, stats, kl, loss, o); break;
+        default: hipLaunchKernelGGL(k_fwd_shards<BF16>, grid, block, 0, st, sr, beta, stats, kl, loss, o);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
                             float *kl, float *loss, hipStream_t st, const RowOpts &o) {

@@ -35,6 +35,16 @@ hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
 // then divergence, one workgroup per row (held in registers when the row fits).
 hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
                             float *kl, float *loss, hipStream_t st, const RowOpts &o = RowOpts());
+// interior JSD forward of 2..FUSED_SHARDS shards in one launch (stats, merge, divergence)
+constexpr int FUSED_SHARDS = 8;
+struct ShardRows {
+    int S;
+    int64_t w[FUSED_SHARDS];
+    RowView s[FUSED_SHARDS], t[FUSED_SHARDS];
+};
+hipError_t launch_fwd_shards(int dtype, const Shard *sh, int S, int64_t N, double beta,
+                             double *stats, float *kl, float *loss, hipStream_t st,
+                             const RowOpts &o = RowOpts());
 
 // Row chunks of the streaming gradient kernels: cw columns per workgroup (GRAD_BLOCK
 // vectors times a power of two, so a power of two), nchunk chunks per row, N * nchunk
