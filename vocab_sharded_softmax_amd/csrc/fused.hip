@@ -91,7 +91,10 @@ struct RowK {
 
 // Run by one whole wave: the fp64 steps are the costliest part of a row's finish, so
 // one wave takes them and the others read the result from LDS.  Lane 0 stores the
-// row's statistics and the constants.
+// row's statistics and the constants.  The constants come from the sums themselves
+// (the stored ln Z gives them back to within 1e-16 relative), with one fp64 division
+// and one fp64 log2 besides the two logs of the statistics; at one tensor-parallel
+// rank's width the finish is a visible part of a row's time.
 __device__ __forceinline__ void row_constants(float ms, double zs, float mt, double zt,
                                               double beta, float ks, double *st, RowK *out) {
     const bool undefined = ms == NINF || mt == NINF;
@@ -101,16 +104,15 @@ __device__ __forceinline__ void row_constants(float ms, double zs, float mt, dou
     k.cs = refc(ms, ks);
     k.ct = refc(mt, ks);
     k.undefined = undefined;
-    double Zs = 1.0, Zt = 1.0;
     k.gam = k.rf = 0.0f;
+    k.izs = k.izt = 1.0f;
     if (!undefined) {
-        Zs = z_from_stats(ms, lzs, ks);
-        Zt = z_from_stats(mt, lzt, ks);
-        k.gam = (float)((1.0 - beta) * Zt / Zs);
-        k.rf = (float)log2(Zs / Zt);
+        const double q = zt / zs;  // Z_t / Z_s
+        k.gam = (float)((1.0 - beta) * q);
+        k.rf = (float)-log2(q);
+        k.izs = (float)(1.0 / zs);
+        k.izt = (float)(1.0 / zt);
     }
-    k.izs = (float)(1.0 / Zs);
-    k.izt = (float)(1.0 / Zt);
     if ((threadIdx.x & 63) == 0) {
         st[0] = ms;
         st[1] = lzs;
