@@ -276,7 +276,7 @@ def main():
                 if timer.spans.get(f"step_beta{bt}")}
     log(f"step {ms_step:.3f} ms (events {per_kernel['step']:.3f}); kernels {per_kernel}")
 
-    three = branches = siblings = tp8 = linear = configs = None
+    three = branches = siblings = tp8 = linear = configs = pages_shape = None
     if not args.no_extras:
         # the same forward as three separate launches (statistics, merge, divergence),
         # timed one by one for comparison with the one-launch forward above
@@ -343,6 +343,7 @@ def main():
         siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
         tp8 = tp8_forward(torch, vj, synth)
         configs = config_rows(torch, vj, synth)
+        pages_shape = pages_shape_siblings(torch, vj, synth)
         linear = None if args.no_linear else fused_linear_row(torch, vj, synth)
 
     out = {
@@ -381,6 +382,7 @@ def main():
         "forward_parts_ms": three,
         "tp8_shard": tp8,
         "other_configs": configs,
+        "pages_shape_siblings": pages_shape,
         "step_ms_by_beta": per_beta,
         "branches": branches,
         "siblings": siblings,
@@ -529,6 +531,58 @@ def config_rows(torch, vj, synth, reps=10):
     del b
     torch.cuda.empty_cache()
     return rows
+
+
+# The sibling ops' fwd+bwd time and peak memory the pages print for one Intel Arc Pro
+# B70 at T=8192, V_local=16032, bf16 ([OPS-PR, Memory]: naive PyTorch -> the eager
+# vocabulary-parallel ops), quoted as context beside ours at the same shape.
+PAGES_B70_SIBLINGS = {
+    "logprobs": {"naive_ms": 7.5, "eager_ms": 21.4, "naive_mib": 1506, "eager_mib": 443},
+    "entropy": {"naive_ms": 30.7, "eager_ms": 41.5, "naive_mib": 3012, "eager_mib": 586},
+    "reverse_kl": {"naive_ms": 37.2, "eager_ms": 70.2, "naive_mib": 3012, "eager_mib": 698},
+    "forward_kl": {"naive_ms": 24.8, "eager_ms": 64.3, "naive_mib": 2510, "eager_mib": 634},
+}
+
+
+def pages_shape_siblings(torch, vj, synth, reps=10):
+    """The autograd ops at the shape of the pages' memory table (T=8192, V=16032 bf16,
+    one id per token, teacher detached): fwd+bwd ms and the peak device memory of the
+    forward and backward beyond the inputs (the student gradient included)."""
+    b = synth.draw("tp8_shard", device="cuda")
+    N, V = b.s.shape
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    ids = torch.randint(0, V, (N,), generator=gen, device="cuda")
+    t = b.t
+    ops = {
+        "logprobs": lambda x: vj.logprobs(x, ids),
+        "entropy": lambda x: vj.entropy(x),
+        "reverse_kl": lambda x: vj.kl_div(x, t, reverse=True),
+        "forward_kl": lambda x: vj.kl_div(x, t),
+    }
+    rows = {}
+    for name, fn in ops.items():
+        x = b.s.detach().clone().requires_grad_()
+
+        def once():
+            fn(x).sum().backward()
+            x.grad = None
+        once()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        once()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        tm = Timer(torch)
+        for _ in range(reps):
+            a = tm.mark()
+            once()
+            tm.add("x", a, tm.mark())
+        torch.cuda.synchronize()
+        rows[name] = {"fwd_bwd_ms": round(tm.ms("x"), 4), "peak_mib": round(peak / 2**20, 1),
+                      "pages_b70": PAGES_B70_SIBLINGS[name]}
+        del x
+    return {"shape": f"T={N} V={V} bf16, teacher detached", "ops": rows}
 
 
 def sibling_rows(torch, vj, synth, reps=3):
