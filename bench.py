@@ -343,7 +343,8 @@ def main():
         siblings = None if args.no_siblings else sibling_rows(torch, vj, synth)
         tp8 = tp8_forward(torch, vj, synth)
         configs = config_rows(torch, vj, synth)
-        pages_shape = pages_shape_siblings(torch, vj, synth)
+        pages_shape = {"siblings": pages_shape_siblings(torch, vj, synth),
+                       "jsd_rank_share": pages_shape_jsd(torch, vj, synth)}
         linear = None if args.no_linear else fused_linear_row(torch, vj, synth)
 
     out = {
@@ -382,7 +383,7 @@ def main():
         "forward_parts_ms": three,
         "tp8_shard": tp8,
         "other_configs": configs,
-        "pages_shape_siblings": pages_shape,
+        "pages_shapes": pages_shape,
         "step_ms_by_beta": per_beta,
         "branches": branches,
         "siblings": siblings,
@@ -583,6 +584,46 @@ def pages_shape_siblings(torch, vj, synth, reps=10):
                       "pages_b70": PAGES_B70_SIBLINGS[name]}
         del x
     return {"shape": f"T={N} V={V} bf16, teacher detached", "ops": rows}
+
+
+# The pages' JSD fwd+bwd per TP rank at N=1024, global V=151936, bf16, beta=0.3, frozen
+# teacher ([JSD-PR, Validation]: median ms with collectives, peak GiB per rank), quoted
+# as context beside one rank's share computed here with no exchange.
+PAGES_JSD_RANKS = {
+    75968: {"tp": 2, "b70_triton_ms": 3.08, "l20_triton_ms": 1.95, "peak_gib_per_rank": 0.435},
+    37984: {"tp": 4, "b70_triton_ms": 3.41, "l20_triton_ms": 1.57, "peak_gib_per_rank": 0.217},
+}
+
+
+def pages_shape_jsd(torch, vj, synth, reps=10):
+    """One tensor-parallel rank's share of the pages' JSD benchmark: the autograd jsd
+    op at N=1024 and V_local = 151936 / TP, beta 0.3, student gradient only."""
+    rows = {}
+    for V, ref in PAGES_JSD_RANKS.items():
+        b = synth.draw("full_vocab", device="cuda", N=1024, V=V)
+        t = b.t.detach()
+        x = b.s.detach().clone().requires_grad_()
+
+        def once():
+            vj.jsd(x, t, 0.3).sum().backward()
+            x.grad = None
+        once()
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        once()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        tm = Timer(torch)
+        for _ in range(reps):
+            a = tm.mark()
+            once()
+            tm.add("x", a, tm.mark())
+        torch.cuda.synchronize()
+        rows[f"V_local={V}"] = {"fwd_bwd_ms": round(tm.ms("x"), 4),
+                                "peak_gib_beyond_inputs": round(peak / 2**30, 3), "pages": ref}
+        del x, b
+    return rows
 
 
 def sibling_rows(torch, vj, synth, reps=3):
