@@ -220,10 +220,17 @@ __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats
     o[ROWC_UNDEFINED] = (k.undefined || dropped) ? 1.0f : 0.0f;
 }
 
-// One wave per row chunk of up to cw columns (chunk_span); the chunks of a row are
-// consecutive workgroups, so the whole grid streams through memory in order.
-template <class D, int MODE, bool WS, bool WT, class DG = D>
-__global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowMView gsv,
+// One workgroup of LANES lanes per row chunk of up to cw columns (chunk_span), one
+// 16-byte vector per lane; the chunks of a row are consecutive workgroups, so the whole
+// grid streams through memory in order.  Measured on MI355X: one wave per chunk when
+// both gradients are written (two waves: 1.68-1.69 against 1.63-1.69 ms at full
+// vocabulary), two waves when one is (0.131-0.133 against 0.142-0.145 ms at 16032
+// columns; even at full vocabulary).
+template <int WS, int WT>
+constexpr int bwd_lanes() { return WS && WT ? GRAD_BLOCK : 2 * GRAD_BLOCK; }
+
+template <class D, int MODE, bool WS, bool WT, class DG = D, int LANES = bwd_lanes<WS, WT>()>
+__global__ __launch_bounds__(LANES) void k_bwd(RowView sv, RowView tv, RowMView gsv,
                                                     RowMView gtv, int64_t w, int64_t cw,
                                                     int64_t nchunk, const float *__restrict__ rowc) {
     using T = typename D::T;
@@ -238,8 +245,8 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
     TG *gs = WS ? row_ptr<TG>(gsv, r) + c0 : nullptr;
     TG *gt = WT ? row_ptr<TG>(gtv, r) + c0 : nullptr;
     if (k[ROWC_UNDEFINED] != 0.0f) {  // no distribution, or dropped: exactly zero gradient
-        if (WS) zero_span<DG, GRAD_BLOCK>(gs, n);
-        if (WT) zero_span<DG, GRAD_BLOCK>(gt, n);
+        if (WS) zero_span<DG, LANES>(gs, n);
+        if (WT) zero_span<DG, LANES>(gt, n);
         return;
     }
     const T *s = srow + c0, *t = row_ptr<T>(tv, r) + c0;
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(GRAD_BLOCK) void k_bwd(RowView sv, RowView tv, RowM
     // where the input is 16-byte aligned: the inputs alone fix the head)
     const int64_t h = std::is_same<D, DG>::value ? head_len<T>(n, s, t, gs, gt)
                                                  : head_len<T>(n, s, t);
-    sweep<D, 1, true, GRAD_BLOCK, true>(s, t, n, h, op);
+    sweep<D, 1, true, LANES, true>(s, t, n, h, op);
 }
 
 template <class D, int MODE>
@@ -284,20 +291,22 @@ hipError_t div_mode(int mode, const Shard &sh, int64_t N, const double *stats, d
 
 template <class D, int MODE, bool WS, bool WT>
 hipError_t bwd_k(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
-    const Chunks ch = grad_chunks<true>(N, sh.width, sizeof(typename D::T));
+    constexpr int L = bwd_lanes<WS, WT>();
+    const Chunks ch = grad_chunks<true, L>(N, sh.width, sizeof(typename D::T));
     if (ch.nchunk == 0) return hipSuccess;
     hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)(N * ch.nchunk)),
-                       dim3(GRAD_BLOCK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
+                       dim3(L), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
                        ch.nchunk, rowc);
     return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t bwd_g16(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) {
-    const Chunks ch = grad_chunks<true>(N, sh.width, sizeof(float));
+    constexpr int L = bwd_lanes<true, false>();
+    const Chunks ch = grad_chunks<true, L>(N, sh.width, sizeof(float));
     if (ch.nchunk == 0) return hipSuccess;
     hipLaunchKernelGGL((k_bwd<F32, MODE, true, false, BF16>), dim3((unsigned)(N * ch.nchunk)),
-                       dim3(GRAD_BLOCK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
+                       dim3(L), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
                        ch.nchunk, rowc);
     return hipGetLastError();
 }

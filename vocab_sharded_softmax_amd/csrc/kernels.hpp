@@ -54,10 +54,10 @@ hipError_t launch_fwd_shards(int dtype, const Shard *sh, int S, int64_t N, doubl
 struct Chunks {
     int64_t cw, nchunk;
 };
-template <bool ALIGNED>
+template <bool ALIGNED, int LANES = GRAD_BLOCK>
 inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
     const int64_t vec = 16 / esize;
-    int64_t cw = GRAD_BLOCK * vec;
+    int64_t cw = LANES * vec;
     auto count = [w](int64_t c) {
         return w <= 0 ? (int64_t)0 : ALIGNED ? (w + 2 * c - 2) / c : (w + c - 1) / c;
     };
