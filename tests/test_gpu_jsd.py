@@ -321,3 +321,18 @@ def test_bad_arguments_raise_before_any_launch():
         v.jsd(s, s.half(), 0.5)
     with pytest.raises(ValueError):
         v.jsd(s, torch.randn(4, 11, device="cuda"), 0.5)
+
+
+# The backward of 2 to 8 shards runs as one launch whose chunks walk each row's shards
+# in order, more shards one launch each; empty and one-column shards, each gradient alone
+@pytest.mark.parametrize("widths", [[2500] * 8, [2000] * 8 + [4000], [1, 0, 19999],
+                                    [7, 3, 5000, 0, 14990]])
+@pytest.mark.parametrize("want", [(True, True), (True, False), (False, True)])
+@pytest.mark.parametrize("beta", [0.4, 0.0, 1.0])
+def test_sharded_backward(widths, want, beta):
+    b = synth.draw("robust", device="cuda", N=23, V=sum(widths))
+    s, t = b.s.clone(), b.t.clone()
+    s[4] = NINF  # undefined row: exact-zero gradients in every shard
+    t[6, 3000:3500] = NINF
+    check_against_oracle(s, t, beta, widths=widths, gout=b.gout, want_s=want[0],
+                         want_t=want[1])

@@ -270,6 +270,22 @@ int check_head(const vlin_head *h, int64_t N, int64_t V) {
     return VJSD_OK;
 }
 
+// The backward of every shard of a call (one launch for up to eight shards).
+int bwd_all(const vjsd_shard *shards, int S, int64_t N, int dtype, int mode, const float *rowc,
+            hipStream_t st) {
+    Shard sh[vjsd::FUSED_SHARDS];
+    if (S <= vjsd::FUSED_SHARDS) {
+        for (int k = 0; k < S; ++k) sh[k] = convert(shards[k], true, true);
+        return hip_status(vjsd::launch_bwd_shards(dtype, mode, sh, S, N, rowc, st));
+    }
+    for (int k = 0; k < S; ++k) {
+        Shard one = convert(shards[k], true, true);
+        const int e = hip_status(vjsd::launch_bwd(dtype, mode, one, N, rowc, st));
+        if (e) return e;
+    }
+    return VJSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,11 +463,7 @@ int vjsd_loss_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, do
     }
     if ((e = hip_status(vjsd::launch_bwd_prep(mode, N, stats, kl, beta, grad, part, st, go))))
         return e;
-    for (int k = 0; k < S; ++k) {
-        Shard sh = convert(shards[k], true, true);
-        if ((e = hip_status(vjsd::launch_bwd(dtype, mode, sh, N, part, st)))) return e;
-    }
-    return VJSD_OK;
+    return bwd_all(shards, S, N, dtype, mode, part, st);
 }
 
 int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
@@ -466,11 +478,7 @@ int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double
     hipStream_t st = (hipStream_t)stream;
     if ((e = hip_status(vjsd::launch_bwd_prep(mode, N, stats, kl, beta, grad_loss, part, st))))
         return e;
-    for (int k = 0; k < S; ++k) {
-        Shard sh = convert(shards[k], true, true);
-        if ((e = hip_status(vjsd::launch_bwd(dtype, mode, sh, N, part, st)))) return e;
-    }
-    return VJSD_OK;
+    return bwd_all(shards, S, N, dtype, mode, part, st);
 }
 
 int vkl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse, float *part,

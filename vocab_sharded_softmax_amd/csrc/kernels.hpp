@@ -84,6 +84,10 @@ hipError_t launch_bwd_prep(int mode, int64_t N, const double *stats, const float
                            const GradOpts &g = GradOpts());
 hipError_t launch_bwd(int dtype, int mode, const Shard &sh, int64_t N, const float *rowc,
                       hipStream_t st);
+// the same over all S shards of a call: one launch for 2..FUSED_SHARDS shards that ask
+// for the same gradients, else launch_bwd per shard
+hipError_t launch_bwd_shards(int dtype, int mode, const Shard *sh, int S, int64_t N,
+                             const float *rowc, hipStream_t st);
 // the same for fp32 logits, writing only the student gradient, in bf16 (nearest even);
 // the gradient view must be 8-byte aligned wherever the input view is 16-byte aligned
 hipError_t launch_bwd_f32_to_bf16(int mode, const Shard &sh, int64_t N, const float *rowc,
