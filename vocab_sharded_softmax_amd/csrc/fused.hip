@@ -231,18 +231,39 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
 // TWICE_BLK lanes, two workgroups per CU (about 512 rows in flight); 256- and
-// 1024-lane workgroups measured slower.  The arithmetic and the two reads take about
-// as long as each other, so the kernel is bound by both.  The first sweep reads with
-// the default cache policy, the second streams.
+// 1024-lane workgroups measured slower.  The kernel is bound by its reads (with the
+// arithmetic close behind), so the last full step of the statistics sweep (TWICE_BLK x
+// TW_U vectors per input, 11 % of a 151936-wide bf16 row) stays in registers and
+// starts the divergence sweep instead of being read again: 1.36 -> 1.30 ms at
+// 8192 x 151936 bf16.  That takes the 16-bit kernels to 126 VGPRs, still two workgroups
+// per CU (at most 128); holding two steps (167) left one and ran at 1.43 ms, and asking
+// the compiler for four waves per SIMD made it spill.  The first sweep reads with the
+// default cache policy, the second streams.
 constexpr int TWICE_BLK = 512;
+constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sweep step
+
+// The held step's vectors through a sweep op, as the sweep would pass them.
+template <class D, class Op>
+__device__ __forceinline__ void run_held(const u32x4 (&hs)[TW_U], const u32x4 (&ht)[TW_U],
+                                         Op &op) {
+    float a[TW_U][D::VEC], b[TW_U][D::VEC];
+    int64_t c[TW_U];
+#pragma unroll
+    for (int u = 0; u < TW_U; ++u) {
+        widen<D>(hs[u], a[u]);
+        widen<D>(ht[u], b[u]);
+        c[u] = 0;  // the statistics and divergence ops take no column
+    }
+    op.template run<TW_U, D::VEC>(a, b, c);
+}
 
 template <class D>
-__global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv, int64_t w,
-                                                         double beta,
-                                                         double *__restrict__ stats,
-                                                         float *__restrict__ kl,
-                                                         float *__restrict__ loss, RowOpts o) {
+__global__ __launch_bounds__(TWICE_BLK)
+void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restrict__ stats,
+                 float *__restrict__ kl, float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
+    constexpr int VEC = D::VEC;
+    constexpr int64_t STEP = (int64_t)TW_U * TWICE_BLK;  // vectors per input per sweep step
     __shared__ float red[4 * (TWICE_BLK / 64)];
     const int64_t r = blockIdx.x;
     if (row_dropped(o, r)) {
@@ -252,7 +273,26 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const int64_t h = head_len<T>(w, s, t);
     OpStats<3> o1(o.ks);
-    sweep<D, 4, true, TWICE_BLK>(s, t, w, h, o1);
+    // Held step: the last full step of the 16-byte body, elements [P, Q).  Rows whose two
+    // inputs sit at different offsets inside 16 bytes (h == w) are swept whole.
+    const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
+    const bool hold = nfull >= 1;
+    const int64_t P = hold ? h + (nfull - 1) * STEP * VEC : w;
+    const int64_t Q = hold ? P + STEP * VEC : w;
+    u32x4 hs[TW_U], ht[TW_U];
+    if (hold) {
+        sweep<D, TW_U, true, TWICE_BLK>(s, t, P, h, o1);
+#pragma unroll
+        for (int u = 0; u < TW_U; ++u) {
+            const int64_t q = P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+            hs[u] = ld16<true>(s + q);
+            ht[u] = ld16<true>(t + q);
+        }
+        run_held<D>(hs, ht, o1);
+        sweep<D, TW_U, true, TWICE_BLK>(s + Q, t + Q, w - Q, 0, o1);
+    } else {
+        sweep<D, TW_U, true, TWICE_BLK>(s, t, w, h, o1);
+    }
     // wave partials, then wave 0 combines them in wave order and derives the constants
     constexpr int NW = TWICE_BLK / 64;
     __shared__ RowK rk;
@@ -287,7 +327,13 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_twice(RowView sv, RowView tv,
         op.bf = (float)beta;
         op.gam = k.gam;
         op.rf = k.rf;
-        sweep<D, 4, true, TWICE_BLK, true>(s, t, w, h, op);
+        if (hold) {  // the held step first, then the rest of the row streamed again
+            run_held<D>(hs, ht, op);
+            sweep<D, TW_U, true, TWICE_BLK, true>(s, t, P, h, op);
+            sweep<D, TW_U, true, TWICE_BLK, true>(s + Q, t + Q, w - Q, 0, op);
+        } else {
+            sweep<D, TW_U, true, TWICE_BLK, true>(s, t, w, h, op);
+        }
         v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
         v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
     }
