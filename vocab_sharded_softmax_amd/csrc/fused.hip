@@ -232,17 +232,22 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
 // TWICE_BLK lanes, two workgroups per CU (about 512 rows in flight); 256- and
 // 1024-lane workgroups measured slower.  The kernel is bound by its reads (with the
-// arithmetic close behind), so the last full step of the statistics sweep (TWICE_BLK x
-// TW_U vectors per input, 11 % of a 151936-wide bf16 row) stays in registers and
-// starts the divergence sweep instead of being read again: 1.36 -> 1.30 ms at
-// 8192 x 151936 bf16.  That takes the 16-bit kernels to 126 VGPRs, still two workgroups
+// arithmetic close behind), so the last full steps of the statistics sweep (TWICE_BLK x
+// TW_U vectors per input each, 11 % of a 151936-wide bf16 row per step) stay in
+// registers and start the divergence sweep instead of being read again: 1.35 -> 1.30 ms
+// at 8192 x 151936 bf16 (one step), 1.18 -> 1.08 ms at 4096 x 128256 fp32 (two).  That takes the 16-bit kernels to 126 VGPRs, still two workgroups
 // per CU (at most 128); holding two steps (167) left one and ran at 1.43 ms, and asking
 // the compiler for four waves per SIMD made it spill.  The first sweep reads with the
 // default cache policy, the second streams.
 constexpr int TWICE_BLK = 512;
 constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sweep step
 
-// The held step's vectors through a sweep op, as the sweep would pass them.
+// Sweep steps held in registers: one for 16-bit inputs (126 VGPRs), two for fp32 (whose
+// widening needs fewer registers).
+template <class D>
+constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 2 : 1; }
+
+// A held step's vectors through a sweep op, as the sweep would pass them.
 template <class D, class Op>
 __device__ __forceinline__ void run_held(const u32x4 (&hs)[TW_U], const u32x4 (&ht)[TW_U],
                                          Op &op) {
@@ -275,20 +280,25 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
     OpStats<3> o1(o.ks);
     // Held step: the last full step of the 16-byte body, elements [P, Q).  Rows whose two
     // inputs sit at different offsets inside 16 bytes (h == w) are swept whole.
+    constexpr int HOLD = held_steps<D>();
     const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
-    const bool hold = nfull >= 1;
-    const int64_t P = hold ? h + (nfull - 1) * STEP * VEC : w;
-    const int64_t Q = hold ? P + STEP * VEC : w;
-    u32x4 hs[TW_U], ht[TW_U];
+    const bool hold = nfull >= HOLD;
+    const int64_t P = hold ? h + (nfull - HOLD) * STEP * VEC : w;
+    const int64_t Q = hold ? P + HOLD * STEP * VEC : w;
+    u32x4 hs[HOLD][TW_U], ht[HOLD][TW_U];
     if (hold) {
         sweep<D, TW_U, true, TWICE_BLK>(s, t, P, h, o1);
 #pragma unroll
-        for (int u = 0; u < TW_U; ++u) {
-            const int64_t q = P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
-            hs[u] = ld16<true>(s + q);
-            ht[u] = ld16<true>(t + q);
+        for (int k = 0; k < HOLD; ++k) {
+#pragma unroll
+            for (int u = 0; u < TW_U; ++u) {
+                const int64_t q =
+                    P + ((int64_t)k * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+                hs[k][u] = ld16<true>(s + q);
+                ht[k][u] = ld16<true>(t + q);
+            }
+            run_held<D>(hs[k], ht[k], o1);
         }
-        run_held<D>(hs, ht, o1);
         sweep<D, TW_U, true, TWICE_BLK>(s + Q, t + Q, w - Q, 0, o1);
     } else {
         sweep<D, TW_U, true, TWICE_BLK>(s, t, w, h, o1);
@@ -327,8 +337,9 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
         op.bf = (float)beta;
         op.gam = k.gam;
         op.rf = k.rf;
-        if (hold) {  // the held step first, then the rest of the row streamed again
-            run_held<D>(hs, ht, op);
+        if (hold) {  // the held steps first, then the rest of the row streamed again
+#pragma unroll
+            for (int k = 0; k < HOLD; ++k) run_held<D>(hs[k], ht[k], op);
             sweep<D, TW_U, true, TWICE_BLK, true>(s, t, P, h, op);
             sweep<D, TW_U, true, TWICE_BLK, true>(s + Q, t + Q, w - Q, 0, op);
         } else {
