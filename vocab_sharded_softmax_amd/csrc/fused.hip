@@ -20,6 +20,8 @@
 #include "kernels.hpp"
 #include "sweep.hpp"
 
+#include <type_traits>
+
 namespace vjsd {
 
 namespace {
@@ -243,9 +245,14 @@ constexpr int TWICE_BLK = 512;
 constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sweep step
 
 // Sweep steps held in registers: one for 16-bit inputs (126 VGPRs), two for fp32 (whose
-// widening needs fewer registers).
+// widening needs fewer registers).  One more step (64 KiB per workgroup) is held in LDS
+// for bf16 and fp32: 1.30 -> 1.26 ms at 8192 x 151936 bf16, 1.08 -> 1.04 ms at
+// 4096 x 128256 fp32.  fp16 compiled to 167 VGPRs with it and ran 8 % slower, so it
+// holds the register step only.
 template <class D>
 constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 2 : 1; }
+template <class D>
+constexpr int lds_steps() { return std::is_same<D, F16>::value ? 0 : 1; }
 
 // A held step's vectors through a sweep op, as the sweep would pass them.
 template <class D, class Op>
@@ -280,20 +287,38 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
     OpStats<3> o1(o.ks);
     // Held step: the last full step of the 16-byte body, elements [P, Q).  Rows whose two
     // inputs sit at different offsets inside 16 bytes (h == w) are swept whole.
-    constexpr int HOLD = held_steps<D>();
+    constexpr int HOLD = held_steps<D>(), LHOLD = lds_steps<D>();
     const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
-    const bool hold = nfull >= HOLD;
-    const int64_t P = hold ? h + (nfull - HOLD) * STEP * VEC : w;
-    const int64_t Q = hold ? P + HOLD * STEP * VEC : w;
+    const bool hold = nfull >= HOLD + LHOLD;
+    // [P, PR): the step held in LDS (if any); [PR, Q): the steps held in registers
+    const int64_t P = hold ? h + (nfull - HOLD - LHOLD) * STEP * VEC : w;
+    const int64_t PR = P + LHOLD * STEP * VEC;
+    const int64_t Q = hold ? PR + HOLD * STEP * VEC : w;
+    __shared__ u32x4 lds_step[2][TW_U][LHOLD ? TWICE_BLK : 1];  // each lane's own vectors
     u32x4 hs[HOLD][TW_U], ht[HOLD][TW_U];
     if (hold) {
         sweep<D, TW_U, true, TWICE_BLK>(s, t, P, h, o1);
+        if constexpr (LHOLD > 0) {
+            u32x4 ls[TW_U], lt[TW_U];
+#pragma unroll
+            for (int u = 0; u < TW_U; ++u) {
+                const int64_t q = P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+                ls[u] = ld16<true>(s + q);
+                lt[u] = ld16<true>(t + q);
+            }
+#pragma unroll
+            for (int u = 0; u < TW_U; ++u) {
+                lds_step[0][u][threadIdx.x] = ls[u];
+                lds_step[1][u][threadIdx.x] = lt[u];
+            }
+            run_held<D>(ls, lt, o1);
+        }
 #pragma unroll
         for (int k = 0; k < HOLD; ++k) {
 #pragma unroll
             for (int u = 0; u < TW_U; ++u) {
                 const int64_t q =
-                    P + ((int64_t)k * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+                    PR + ((int64_t)k * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
                 hs[k][u] = ld16<true>(s + q);
                 ht[k][u] = ld16<true>(t + q);
             }
@@ -340,6 +365,15 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
         if (hold) {  // the held steps first, then the rest of the row streamed again
 #pragma unroll
             for (int k = 0; k < HOLD; ++k) run_held<D>(hs[k], ht[k], op);
+            if constexpr (LHOLD > 0) {
+                u32x4 ls[TW_U], lt[TW_U];
+#pragma unroll
+                for (int u = 0; u < TW_U; ++u) {
+                    ls[u] = lds_step[0][u][threadIdx.x];
+                    lt[u] = lds_step[1][u][threadIdx.x];
+                }
+                run_held<D>(ls, lt, op);
+            }
             sweep<D, TW_U, true, TWICE_BLK, true>(s, t, P, h, op);
             sweep<D, TW_U, true, TWICE_BLK, true>(s + Q, t + Q, w - Q, 0, op);
         } else {
