@@ -285,8 +285,10 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const int64_t h = head_len<T>(w, s, t);
     OpStats<3> o1(o.ks);
-    // Held step: the last full step of the 16-byte body, elements [P, Q).  Rows whose two
-    // inputs sit at different offsets inside 16 bytes (h == w) are swept whole.
+    // Held steps: the last HOLD + LHOLD full steps of the 16-byte body, elements [P, Q).
+    // Rows whose two inputs sit at different offsets inside 16 bytes (h == w), or that
+    // are too short, are swept whole.  A lane reads back from LDS only the vectors it
+    // wrote there itself, so the LDS step needs no barrier of its own.
     constexpr int HOLD = held_steps<D>(), LHOLD = lds_steps<D>();
     const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
     const bool hold = nfull >= HOLD + LHOLD;
