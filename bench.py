@@ -329,6 +329,8 @@ def main():
     ceil = ceilings(torch, vj, s, t, gs)
     ceil["bwd_frac_of_copy"] = round(achieved / ceil["copy_gbps"], 4)
     fwd_ms = timer.ms("forward")
+    # the forward as if it read both sweeps in full (the pages' count); it holds the
+    # statistics sweep's last steps on chip, so it fetches less and this can exceed 1
     ceil["fwd_two_reads_frac_of_read"] = round(
         4 * tensor_bytes / (fwd_ms * 1e-3) / 1e9 / ceil["read_gbps"], 4)
 
