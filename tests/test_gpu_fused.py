@@ -206,3 +206,20 @@ def test_sharded_forward_separate_tensors():
     assert_values(loss.cpu(), ref["loss"], b.s.dtype, "loss")
     assert_stats(stats.cpu(), *oracle.stats(sc, widths=ws), 0, "student stats")
     assert_stats(stats.cpu(), *oracle.stats(tc, widths=ws), 1, "teacher stats")
+
+
+# The two-sweep forward holds the statistics sweep's last full steps on chip (a step is
+# 512 lanes x 4 vectors: 16384 16-bit or 8192 fp32 columns; bf16 holds 2 steps, fp16 1,
+# fp32 3).  Widths where the held steps take the whole body (empty prefix and rest), one
+# column more or fewer, and rows 2 bytes past a 16-byte boundary (a scalar head before
+# the held body).
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 32768), (torch.bfloat16, 32769),
+                                     (torch.bfloat16, 32767), (torch.bfloat16, 49160),
+                                     (torch.float16, 16392), (torch.float16, 32768),
+                                     (torch.float32, 24576), (torch.float32, 24580),
+                                     (torch.float32, 24575)])
+def test_held_steps_boundaries(dtype, V):
+    b = synth.draw("tiny", device="cuda", N=9, V=V + 9, dtype=dtype)
+    check(b.s[:, :V], b.t[:, :V], 0.5)  # rows 16-byte aligned when V + 9 allows it
+    check(b.s[:, 1:V + 1], b.t[:, 1:V + 1], 0.5)  # a scalar head before the body
+    check(b.s[:, 8:V + 8], b.t[:, 8:V + 8], 0.3)
