@@ -210,14 +210,14 @@ def test_sharded_forward_separate_tensors():
 
 # The two-sweep forward holds the statistics sweep's last full steps on chip (a step is
 # 512 lanes x 4 vectors: 16384 16-bit or 8192 fp32 columns; bf16 holds 2 steps, fp16 1,
-# fp32 3).  Widths where the held steps take the whole body (empty prefix and rest), one
+# fp32 5).  Widths where the held steps take the whole body (empty prefix and rest), one
 # column more or fewer, and rows 2 bytes past a 16-byte boundary (a scalar head before
 # the held body).
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 32768), (torch.bfloat16, 32769),
                                      (torch.bfloat16, 32767), (torch.bfloat16, 49160),
                                      (torch.float16, 16392), (torch.float16, 32768),
-                                     (torch.float32, 24576), (torch.float32, 24580),
-                                     (torch.float32, 24575)])
+                                     (torch.float32, 40960), (torch.float32, 40964),
+                                     (torch.float32, 40959), (torch.float32, 57344)])
 def test_held_steps_boundaries(dtype, V):
     b = synth.draw("tiny", device="cuda", N=9, V=V + 9, dtype=dtype)
     check(b.s[:, :V], b.t[:, :V], 0.5)  # rows 16-byte aligned when V + 9 allows it

@@ -235,22 +235,24 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
 // TWICE_BLK lanes, two workgroups per CU (about 512 rows in flight); 256- and
 // 1024-lane workgroups measured slower.  The kernel is bound by its reads (with the
 // arithmetic close behind), so the last full steps of the statistics sweep (TWICE_BLK x
-// TW_U vectors per input each, 11 % of a 151936-wide bf16 row per step) stay in
-// registers and start the divergence sweep instead of being read again: 1.35 -> 1.30 ms
-// at 8192 x 151936 bf16 (one step), 1.18 -> 1.08 ms at 4096 x 128256 fp32 (two).  That takes the 16-bit kernels to 126 VGPRs, still two workgroups
-// per CU (at most 128); holding two steps (167) left one and ran at 1.43 ms, and asking
-// the compiler for four waves per SIMD made it spill.  The first sweep reads with the
-// default cache policy, the second streams.
+// TW_U vectors per input each: 16384 16-bit or 8192 fp32 columns) stay on chip, in
+// registers and LDS, and open the divergence sweep instead of being read again.  The
+// first sweep reads with the default cache policy, the second streams.
 constexpr int TWICE_BLK = 512;
 constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sweep step
 
-// Sweep steps held in registers: one for 16-bit inputs (126 VGPRs), two for fp32 (whose
-// widening needs fewer registers).  One more step (64 KiB per workgroup) is held in LDS
-// for bf16 and fp32: 1.30 -> 1.26 ms at 8192 x 151936 bf16, 1.08 -> 1.04 ms at
-// 4096 x 128256 fp32.  fp16 compiled to 167 VGPRs with it and ran 8 % slower, so it
-// holds the register step only.
+// Sweep steps held in registers, and one more (64 KiB per workgroup) in LDS for bf16 and
+// fp32.  Measured on MI355X (forward at 8192 x 151936 bf16 / 4096 x 128256 fp32):
+//   bf16  1 step + LDS (125 VGPRs, two workgroups per CU): 1.35 -> 1.25 ms; 2 steps +
+//         LDS (247 VGPRs) 1.44 ms; asking the compiler for four waves per SIMD made it
+//         spill
+//   fp16  1 step (126 VGPRs); with the LDS step it compiled to 167 VGPRs and ran 8 %
+//         slower, with 2 steps 1.39 ms
+//   fp32  4 steps + LDS (236 VGPRs, one workgroup per CU): 1.18 -> 0.99 ms; an fp32
+//         step holds half the columns of a 16-bit one, and holding more beat occupancy
+//         here (1 / 2 / 3 steps + LDS: 1.08 / 1.05 / 1.02 ms; 5 steps spilled)
 template <class D>
-constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 2 : 1; }
+constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 4 : 1; }
 template <class D>
 constexpr int lds_steps() { return std::is_same<D, F16>::value ? 0 : 1; }
 
