@@ -336,3 +336,20 @@ def test_sharded_backward(widths, want, beta):
     t[6, 3000:3500] = NINF
     check_against_oracle(s, t, beta, widths=widths, gout=b.gout, want_s=want[0],
                          want_t=want[1])
+
+
+# ---- the backward's work-item numbering: each XCD takes runs of 256 consecutive row
+# chunks and the grid is padded to whole rounds of 8 x 256 items, so item counts just
+# below, at and above a round must still write every gradient element exactly once
+# (the gradient buffers start as NaN) -------------------------------------------------
+
+@pytest.mark.parametrize("N,V,detached", [
+    (23, 44800, False),   # 23 rows x 89 chunks of 512 columns = 2047 items
+    (32, 32000, False),   # 32 x 64 = 2048
+    (683, 800, False),    # 683 x 3 = 2049
+    (17, 122500, False),  # 17 x 241 = 4097
+    (683, 1500, True),    # student gradient alone: 683 x 3 chunks of 1024 = 2049
+])
+def test_backward_item_rounds(N, V, detached):
+    b = synth.draw("tp8_shard", device="cuda", N=N, V=V, dtype=torch.bfloat16)
+    check_against_oracle(b.s, b.t, 0.5, gout=b.gout, want_t=not detached)
