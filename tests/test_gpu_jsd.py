@@ -340,8 +340,8 @@ def test_sharded_backward(widths, want, beta):
 
 # ---- the backward's work-item numbering: each XCD takes runs of 256 consecutive row
 # chunks and the grid is padded to whole rounds of 8 x 256 items, so item counts just
-# below, at and above a round must still write every gradient element exactly once
-# (the gradient buffers start as NaN) -------------------------------------------------
+# below, at and above a round must still write every gradient element (the gradient
+# buffers start as NaN, so an element left unwritten fails) ----------------------------
 
 @pytest.mark.parametrize("N,V,detached", [
     (23, 44800, False),   # 23 rows x 89 chunks of 512 columns = 2047 items
