@@ -1,8 +1,12 @@
-"""Full-size workloads on the GPU, in the launch configuration the benchmark times.
+"""Full-size workloads on the GPU.
 
-The GPU path runs over every row; the fp64 oracle checks a sample of rows element
-by element (always including the first and last rows and the workload's special
-rows), and properties that hold at any size are checked on all rows.
+Each workload runs over every row through the route the benchmark times: the
+one-call forward (``vjsd_forward``: one launch that holds the row in registers,
+sweeps it twice, or merges its shards in the workgroup) followed by ``vjsd_bwd``.
+The fp64 oracle checks a sample of rows element by element (always including the
+first and last rows and the workload's special rows); every row is compared with
+the three-launch route (``vjsd_stats``, ``vjsd_merge``, ``vjsd_fwd``), and
+properties that hold at any size are checked on all rows.
 """
 import math
 
@@ -16,28 +20,75 @@ from parity import assert_grads, assert_stats, assert_values, sample_rows
 
 pytestmark = pytest.mark.gpu
 
+NAN = float("nan")
+
 
 def vj():
     import vocab_sharded_softmax_amd as v
     return v
 
 
-def jsd_all(s, t, beta, widths=None, gout=None, want_t=True):
+def jsd_all(s, t, beta, widths=None, gout=None, want_t=True, timed=True):
+    """Statistics, KL pair, loss and gradients of every row.  ``timed``: the one-call
+    forward then the backward, as the benchmark's step runs them; else the three
+    separate forward launches then the backward.  Outputs start as NaN, so a row or
+    element left unwritten shows."""
     v = vj()
     sh = v.ShardSet(s, t, widths=widths)
     N, S = sh.N, sh.S
-    part = v.new_part(N, S, s.device)
-    stats = torch.empty((N, 4), dtype=torch.float64, device=s.device)
-    kl = torch.empty((N, 2), dtype=torch.float32, device=s.device)
-    loss = torch.empty((N,), dtype=torch.float32, device=s.device)
-    v.vjsd_stats(sh, 3, part)
-    v.vjsd_merge(part, S, N, 3, stats)
-    v.vjsd_fwd(sh, stats, beta, part, kl, loss)
-    gs = torch.empty_like(s)
-    gt = torch.empty_like(t) if want_t else None
+    dev = s.device
+    part = v.new_part(N, S, dev)
+    stats = torch.full((N, 4), NAN, dtype=torch.float64, device=dev)
+    kl = torch.full((N, 2), NAN, dtype=torch.float32, device=dev)
+    loss = torch.full((N,), NAN, dtype=torch.float32, device=dev)
+    if timed:
+        v.vjsd_forward(sh, beta, part, stats, kl, loss)
+    else:
+        v.vjsd_stats(sh, 3, part)
+        v.vjsd_merge(part, S, N, 3, stats)
+        v.vjsd_fwd(sh, stats, beta, part, kl, loss)
+    gs = torch.full_like(s, NAN)
+    gt = torch.full_like(t, NAN) if want_t else None
     v.vjsd_bwd(v.ShardSet(s, t, widths=widths, gs=gs, gt=gt), stats, kl, beta, gout, part)
     torch.cuda.synchronize()
     return stats, kl, loss, gs, gt
+
+
+def same_as_three_launch(out, ref, dtype):
+    """Every row of the timed route against the three-launch route on the same data:
+    row maxima bit-exact, ln sum exp and the per-token values within rounding, NaN
+    and infinity patterns identical, gradients within one unit in the last place of
+    the storage format (both routes feed the same backward kernel; their statistics
+    differ only in summation order)."""
+    st, kl, loss, gs, gt = out
+    st3, kl3, loss3, gs3, gt3 = ref
+    m, m3 = st[:, 0::2], st3[:, 0::2]
+    assert torch.equal(torch.isnan(m), torch.isnan(m3))
+    assert torch.equal(m.nan_to_num(), m3.nan_to_num()), "row maxima differ"
+    lz, lz3 = st[:, 1::2], st3[:, 1::2]
+    fin = torch.isfinite(lz3)
+    assert torch.equal(torch.isfinite(lz), fin)
+    assert (lz[fin] - lz3[fin]).abs().max().item() <= 4e-6
+    # each route sums a row's V terms in fp32 in its own order: the two sums differ by
+    # rounding of order sqrt(V) * 2^-24 relative; four times that, plus the fp32
+    # value tolerance's absolute part
+    V = gs.shape[-1]
+    rtol = 4.0 * math.sqrt(V) * 2.0 ** -24
+    for a, b in ((loss, loss3), (kl, kl3)):
+        a, b = a.cpu().numpy(), b.cpu().numpy()
+        assert np.array_equal(np.isnan(a), np.isnan(b))
+        assert np.array_equal(np.isinf(a), np.isinf(b))
+        f = np.isfinite(b)
+        np.testing.assert_allclose(a[f], b[f], rtol=rtol, atol=1e-6)
+    eps = 2.0 ** -7 if dtype == torch.bfloat16 else (2.0 ** -10 if dtype == torch.float16 else 1e-4)
+    for a, b in ((gs, gs3), (gt, gt3)):
+        if a is None:
+            continue
+        for r0 in range(0, a.shape[0], 1024):  # row blocks: bounded fp32 temporaries
+            x, y = a[r0:r0 + 1024].float(), b[r0:r0 + 1024].float()
+            assert not torch.isnan(x).any() and not torch.isnan(y).any()
+            bound = eps * torch.maximum(x.abs(), y.abs()) + 1e-6
+            assert ((x - y).abs() <= bound).all(), f"gradients differ in rows from {r0}"
 
 
 def check_rows(rows, s, t, beta, widths, gout, stats, kl, loss, gs, gt):
@@ -67,24 +118,32 @@ def H(beta):
 
 @pytest.mark.parametrize("detached", [False, True])
 def test_tp8_shard_full(detached):
+    """One tensor-parallel rank's width (8192 x 16032 bf16, beta 0.5): the one-call
+    forward holds each row in registers."""
     b = synth.draw("tp8_shard", device="cuda")
     out = jsd_all(b.s, b.t, 0.5, None, b.gout, want_t=not detached)
     rows = sample_rows(b.s.shape[0], 24, 11)
     check_rows(rows, b.s, b.t, 0.5, None, b.gout, *out)
     loss = out[2]
     assert torch.isfinite(loss).all() and (loss >= -1e-5).all() and (loss <= H(0.5) + 1e-5).all()
+    same_as_three_launch(out, jsd_all(b.s, b.t, 0.5, None, b.gout, want_t=not detached,
+                                      timed=False), b.s.dtype)
 
 
-def test_full_vocab_full_size_three_betas():
+@pytest.mark.parametrize("beta", [0.1, 0.5, 0.9])
+def test_full_vocab_timed_step(beta):
+    """The benchmark's step at its full size (8192 x 151936 bf16, both gradients) at
+    each of its three betas: the two-sweep forward with held steps, then the
+    backward."""
     b = synth.draw("full_vocab", device="cuda")
-    for i, beta in enumerate(synth.WORKLOADS["full_vocab"].betas):
-        out = jsd_all(b.s, b.t, beta, None, b.gout)
-        rows = sample_rows(b.s.shape[0], 10, 20 + i)
-        check_rows(rows, b.s, b.t, beta, None, b.gout, *out)
-        loss = out[2]
-        assert torch.isfinite(loss).all()
-        assert (loss >= -1e-5).all() and (loss <= H(beta) + 1e-5).all()
-        del out
+    assert beta in synth.WORKLOADS["full_vocab"].betas
+    out = jsd_all(b.s, b.t, beta, None, b.gout)
+    rows = sample_rows(b.s.shape[0], 10, 20 + int(beta * 10))
+    check_rows(rows, b.s, b.t, beta, None, b.gout, *out)
+    loss = out[2]
+    assert torch.isfinite(loss).all()
+    assert (loss >= -1e-5).all() and (loss <= H(beta) + 1e-5).all()
+    same_as_three_launch(out, jsd_all(b.s, b.t, beta, None, b.gout, timed=False), b.s.dtype)
 
 
 def test_robust_full_size_sharded_and_split_independent():
@@ -99,6 +158,9 @@ def test_robust_full_size_sharded_and_split_independent():
     assert np.isnan(loss4[masked]).all()
     assert np.isfinite(np.delete(loss4, masked)).all()
     assert torch.all(out4[3][b.rows_masked] == 0) and torch.all(out4[4][b.rows_masked] == 0)
+    same_as_three_launch(out4, jsd_all(b.s, b.t, 0.5, list(w.widths), b.gout, timed=False),
+                         b.s.dtype)
+    del out4
     loss1 = jsd_all(b.s, b.t, 0.5, None, b.gout)[2].cpu().numpy()
     fin = np.isfinite(loss4)
     np.testing.assert_allclose(loss1[fin], loss4[fin], rtol=5e-6, atol=5e-7)

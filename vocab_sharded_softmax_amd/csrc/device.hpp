@@ -358,6 +358,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ float wave_max(float v) {
     return wave_reduce<false>(v, [](float a, float b) { return fmaxf(a, b); });
 }
+__device__ __forceinline__ float wave_min(float v) {
+    return wave_reduce<false>(v, [](float a, float b) { return fminf(a, b); });
+}
 
 // Online (max, sum of 2^(x*ks - refc(max))) pair.
 struct MZ {

@@ -51,6 +51,100 @@ struct DivTerm {
     }
 };
 
+// ---- the interior divergence, 0 < beta < 1 -------------------------------------------
+//
+// With u = x ks - c (c the statistics' reference point of that side) and e = 2^u, the
+// mixture scaled by Z_t is M Z_t = beta e_t + (1 - beta) (Z_t / Z_s) e_s.  The ratio
+// Z_t / Z_s goes into the student's exponent reference: v_s = x_s ks - c'_s with
+// c'_s = fl32(c_s + r), r = log2(Z_s / Z_t), so f_s = 2^v_s = 2^(c_s - c'_s) e_s, and
+//   delta = (c_s - c'_s) + r          (the rounding of c'_s: at most half its ulp)
+//   W = beta e_t + k_s f_s = M Z_t,   k_s = fl32((1 - beta) 2^-delta),   L = log2 W
+//   u_t - L = log2(p_t / M),          v_s - L = log2(p_s / M) + delta
+//   KL(p_t || M) / ln 2 = (1 / Z_t) sum e_t (u_t - L)
+//   KL(p_s || M) / ln 2 = (1 / (2^delta Z_t)) sum f_s (v_s - L) - delta
+// (2^(c_s - c'_s) Z_s = 2^delta Z_t).  Both log-ratios come out of one subtraction of
+// nearby numbers, free of any row offset.  Per element pair: two FMAs for the
+// exponents, two exp2, a multiply and an FMA for the mixture, one log2, two
+// subtractions and two FMAs into the sums.  SAFE adds what a row with masked (-inf)
+// tokens, or with logits so spread that both exponentials of a pair underflow, needs: u
+// and v clamped at U_FLOOR (so 0 * -inf never forms) and W_FLOOR inside the logarithm
+// (so log2 never sees 0).  A row takes the plain form when its statistics sweep found
+// every logit of both sides within FAST_RANGE (base 2) of the row's maximum: then
+// e_t >= 2^-FAST_RANGE and W > 0, and every term is finite.
+constexpr float FAST_RANGE = 96.0f;
+
+template <bool SAFE>
+struct MixTerm {
+    float ks = L2E;  // log2 e / temperature
+    float ct, cs, bt, ksc;  // references (c_t, c'_s) and mixture weights (beta, k_s)
+
+    __device__ __forceinline__ void add(float xs, float xt, float &at, float &as) const {
+        float ut = fmaf(xt, ks, -ct);
+        float vs = fmaf(xs, ks, -cs);
+        if constexpr (SAFE) {
+            ut = fmaxf(ut, U_FLOOR);
+            vs = fmaxf(vs, U_FLOOR);
+        }
+        const float et = ex2(ut), fs = ex2(vs);
+        const float L = lg2(fmaf(bt, et, SAFE ? fmaf(ksc, fs, W_FLOOR) : ksc * fs));
+        at = fmaf(et, ut - L, at);
+        as = fmaf(fs, vs - L, as);
+    }
+};
+
+// Row constants of the interior divergence, from the row's statistics: reference
+// points and sums of 2^u relative to them (both sides defined: zs, zt > 0).
+struct MixRow {
+    float ct, cs, ksc;   // c_t, c'_s, k_s
+    double izt, izs;     // 1 / Z_t and 1 / (2^delta Z_t)
+    double delta;
+};
+
+__device__ __forceinline__ MixRow mix_row(double beta, float cs, double zs, float ct,
+                                          double zt) {
+    MixRow k;
+    const double r = log2(zs / zt);
+    k.ct = ct;
+    k.cs = (float)((double)cs + r);
+    k.delta = ((double)cs - (double)k.cs) + r;
+    const double e = exp2(k.delta);
+    k.ksc = (float)((1.0 - beta) / e);
+    k.izt = 1.0 / zt;
+    k.izs = 1.0 / (e * zt);
+    return k;
+}
+
+// KL(p_t || M) / ln 2 and KL(p_s || M) / ln 2 from the row's two sums.
+__device__ __forceinline__ void mix_finish(const MixRow &k, double at, double as, double &kt2,
+                                           double &ks2) {
+    kt2 = at * k.izt;
+    ks2 = as * k.izs - k.delta;
+}
+
+// Sweep op of the interior divergence: four independent accumulators per side.
+template <bool SAFE>
+struct OpMix : MixTerm<SAFE> {
+    float at[4] = {0, 0, 0, 0}, as[4] = {0, 0, 0, 0};
+
+    __device__ __forceinline__ void set(const MixRow &k, float beta, float ks) {
+        this->ks = ks;
+        this->ct = k.ct;
+        this->cs = k.cs;
+        this->bt = beta;
+        this->ksc = k.ksc;
+    }
+    template <int NV, int W>
+    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
+                                        const int64_t (&)[NV]) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int i = 0; i < W; ++i) this->add(x[j][i], y[j][i], at[j], as[j]);
+    }
+    __device__ __forceinline__ float sum_t() const { return (at[0] + at[1]) + (at[2] + at[3]); }
+    __device__ __forceinline__ float sum_s() const { return (as[0] + as[1]) + (as[2] + as[3]); }
+};
+
 // Sweep op of the two-pass divergence kernel: four independent accumulators.
 template <int MODE>
 struct OpDiv : DivTerm<MODE> {

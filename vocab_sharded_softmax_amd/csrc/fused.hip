@@ -13,10 +13,13 @@
 //                kernel boundaries go away, the second read stays
 //   k_fwd_shards the same for a row split into up to FUSED_SHARDS logical shards:
 //                per-shard statistics merged in the workgroup, then the divergence
-// The row constants are rebuilt from the fp64 statistics exactly as the separate
-// passes rebuild them.  Splitting a row over several workgroups would need a
-// device-wide exchange per row; on MI355X the cache write-back and invalidation that a
-// correct device-scope release/acquire costs exceeds the second read it would save.
+// The divergence terms are those of MixTerm (divergence.hpp).  The statistics sweep
+// also finds each side's smallest logit: a row whose logits all lie within FAST_RANGE
+// of its maximum (no masked token, no underflow) takes the divergence without the
+// clamps and the floor that masked tokens need.  Splitting a row over several
+// workgroups would need a device-wide exchange per row; on MI355X the cache write-back
+// and invalidation that a correct device-scope release/acquire costs exceeds the
+// second read it would save.
 #include "kernels.hpp"
 #include "sweep.hpp"
 
@@ -45,23 +48,33 @@ __device__ __forceinline__ void opaque(u32x4 &v) {
     asm volatile("" : "+v"(v));
 }
 
-__device__ __forceinline__ void block_max2(float &a, float &b, float *red) {
+// Row maxima (a, b) and minima (na, nb) over the workgroup; red holds 4 * FNW floats.
+__device__ __forceinline__ void block_minmax2(float &a, float &b, float &na, float &nb,
+                                              float *red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     a = wave_max(a);
     b = wave_max(b);
+    na = wave_min(na);
+    nb = wave_min(nb);
     if (lane == 0) {
         red[wave] = a;
         red[FNW + wave] = b;
+        red[2 * FNW + wave] = na;
+        red[3 * FNW + wave] = nb;
     }
     __syncthreads();
-    float x = red[0], y = red[FNW];
+    float x = red[0], y = red[FNW], nx = red[2 * FNW], ny = red[3 * FNW];
 #pragma unroll
     for (int k = 1; k < FNW; ++k) {
         x = fmaxf(x, red[k]);
         y = fmaxf(y, red[FNW + k]);
+        nx = fminf(nx, red[2 * FNW + k]);
+        ny = fminf(ny, red[3 * FNW + k]);
     }
     a = x;
     b = y;
+    na = nx;
+    nb = ny;
     __syncthreads();
 }
 
@@ -85,42 +98,68 @@ __device__ __forceinline__ void block_sum2(float &a, float &b, float *red) {
     __syncthreads();
 }
 
-// Constants of a row's divergence pass, derived from the row's (max, sum) pairs.
+// Constants of a row's divergence pass, derived from the row's statistics.
 struct RowK {
-    float cs, ct, gam, rf, izs, izt;  // references, mixture weight, log2(Zs/Zt), 1/Z
-    int undefined;                    // a side has no distribution (all -inf)
+    MixRow mx;
+    int undefined;  // a side has no distribution (all -inf)
+    int fast;       // every logit of both sides within FAST_RANGE of its row maximum
 };
 
 // Run by one whole wave: the fp64 steps are the costliest part of a row's finish, so
 // one wave takes them and the others read the result from LDS.  Lane 0 stores the
-// row's statistics and the constants.  The constants come from the sums themselves
-// (the stored ln Z gives them back to within 1e-16 relative), with one fp64 division
-// and one fp64 log2 besides the two logs of the statistics; at one tensor-parallel
-// rank's width the finish is a visible part of a row's time.
-__device__ __forceinline__ void row_constants(float ms, double zs, float mt, double zt,
-                                              double beta, float ks, double *st, RowK *out) {
+// row's statistics and the constants.  (ms, zs), (mt, zt): row maxima and sums of
+// 2^(x ks - refc(max)); ns, nt: row minima.
+__device__ __forceinline__ void row_constants(float ms, double zs, float mt, double zt, float ns,
+                                              float nt, double beta, float ks, double *st,
+                                              RowK *out) {
     const bool undefined = ms == NINF || mt == NINF;
-    const double lzs = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, zs, ks);
-    const double lzt = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, zt, ks);
     RowK k;
-    k.cs = refc(ms, ks);
-    k.ct = refc(mt, ks);
     k.undefined = undefined;
-    k.gam = k.rf = 0.0f;
-    k.izs = k.izt = 1.0f;
+    k.fast = 0;
+    k.mx = MixRow{0.0f, 0.0f, 0.0f, 1.0, 1.0, 0.0};
     if (!undefined) {
-        const double q = zt / zs;  // Z_t / Z_s
-        k.gam = (float)((1.0 - beta) * q);
-        k.rf = (float)-log2(q);
-        k.izs = (float)(1.0 / zs);
-        k.izt = (float)(1.0 / zt);
+        k.mx = mix_row(beta, refc(ms, ks), zs, refc(mt, ks), zt);
+        k.fast = (ms - ns) * ks <= FAST_RANGE && (mt - nt) * ks <= FAST_RANGE;
     }
     if ((threadIdx.x & 63) == 0) {
         st[0] = ms;
-        st[1] = lzs;
+        st[1] = ms == NINF ? -__builtin_inf() : lnz_from_z(ms, zs, ks);
         st[2] = mt;
-        st[3] = lzt;
+        st[3] = mt == NINF ? -__builtin_inf() : lnz_from_z(mt, zt, ks);
         *out = k;
+    }
+}
+
+// The row's per-token values from its two divergence sums (thread 0).
+__device__ __forceinline__ void finish_row(const RowK &k, double beta, float at, float as,
+                                           float *kl, float *loss, float lscale) {
+    double kt2 = 0.0, ks2 = 0.0;
+    if (!k.undefined) mix_finish(k.mx, at, as, kt2, ks2);
+    finalize_row(INTERIOR, beta, k.undefined, kt2, ks2, NINF, kl, loss, lscale);
+}
+
+// Divergence terms of a row held in registers; slots past the row's end (they hold
+// -inf) are skipped.
+template <class D, int NVT, bool SAFE>
+__device__ __forceinline__ void regs_div(const u32x4 (&xs)[NVT], const u32x4 (&xt)[NVT],
+                                         int64_t nv, const MixRow &mx, float beta, float ks,
+                                         float &at, float &as) {
+    constexpr int VEC = D::VEC;
+    MixTerm<SAFE> op;
+    op.ks = ks;
+    op.ct = mx.ct;
+    op.cs = mx.cs;
+    op.bt = beta;
+    op.ksc = mx.ksc;
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) {
+        if (threadIdx.x + (int64_t)i * FB < nv) {
+            float a[VEC], b[VEC];
+            widen<D>(xs[i], a);
+            widen<D>(xt[i], b);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) op.add(a[e], b[e], at, as);
+        }
     }
 }
 
@@ -133,7 +172,7 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
                                                 float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
     constexpr int VEC = D::VEC;
-    __shared__ float red[2 * FNW];
+    __shared__ float red[4 * FNW];
     const int64_t r = blockIdx.x;
     if (row_dropped(o, r)) {
         dropped_row(stats + r * 4, kl + 2 * r, loss + r);
@@ -154,20 +193,28 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
             xt[i] = u32x4{q, q, q, q};
         }
     }
-    // ---- statistics: row max, then sum of 2^(x ks - c)
-    float ms = NINF, mt = NINF;
+    // ---- statistics: row max and min, then sum of 2^(x ks - c)
+    float ms = NINF, mt = NINF, ns = __builtin_huge_valf(), nt = __builtin_huge_valf();
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
         float a[VEC], b[VEC];
         widen<D>(xs[i], a);
         widen<D>(xt[i], b);
+        float na = a[0], nb = b[0];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             ms = fmaxf(ms, a[e]);
             mt = fmaxf(mt, b[e]);
+            na = fminf(na, a[e]);
+            nb = fminf(nb, b[e]);
         }
+        // a -inf filled slot past the row's end is left out of the minima (a select, not
+        // a branch: a branch here keeps every widened value of the row alive)
+        const bool real = threadIdx.x + (int64_t)i * FB < nv;
+        ns = fminf(ns, real ? na : __builtin_huge_valf());
+        nt = fminf(nt, real ? nb : __builtin_huge_valf());
     }
-    block_max2(ms, mt, red);
+    block_minmax2(ms, mt, ns, nt, red);
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
         opaque(xs[i]);
@@ -197,38 +244,23 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
     }
     block_sum2(zs, zt, red);
     __shared__ RowK rk;
-    if (threadIdx.x < 64) row_constants(ms, zs, mt, zt, beta, o.ks, stats + r * 4, &rk);
+    if (threadIdx.x < 64)
+        row_constants(ms, zs, mt, zt, ns, nt, beta, o.ks, stats + r * 4, &rk);
     __syncthreads();
     const RowK k = rk;
     // ---- divergence: terms from registers
     float pt = 0.0f, ps = 0.0f;
     if (!k.undefined) {
-        OpDivRegs<INTERIOR> op;
-        op.ks = o.ks;
-        op.cs = k.cs;
-        op.ct = k.ct;
-        op.bf = (float)beta;
-        op.gam = k.gam;
-        op.rf = k.rf;
 #pragma unroll
         for (int i = 0; i < NVT; ++i) {
             opaque(xs[i]);
             opaque(xt[i]);
         }
-#pragma unroll
-        for (int i = 0; i < NVT; ++i) {
-            float a[VEC], b[VEC];
-            widen<D>(xs[i], a);
-            widen<D>(xt[i], b);
-            op.template add<VEC>(a, b);
-        }
-        pt = op.At;
-        ps = op.As;
+        if (k.fast) regs_div<D, NVT, false>(xs, xt, nv, k.mx, (float)beta, o.ks, pt, ps);
+        else regs_div<D, NVT, true>(xs, xt, nv, k.mx, (float)beta, o.ks, pt, ps);
     }
     block_sum2(pt, ps, red);
-    if (threadIdx.x == 0)
-        finalize_row(INTERIOR, beta, k.undefined, pt * k.izt, ps * k.izs, NINF, kl + 2 * r,
-                     loss + r, o.lscale);
+    if (threadIdx.x == 0) finish_row(k, beta, pt, ps, kl + 2 * r, loss + r, o.lscale);
 }
 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
@@ -271,6 +303,65 @@ __device__ __forceinline__ void run_held(const u32x4 (&hs)[TW_U], const u32x4 (&
     op.template run<TW_U, D::VEC>(a, b, c);
 }
 
+// The streamed part of k_fwd_twice's divergence sweep, continuing the sums `acc`
+// (t, s) of the held steps.
+template <class D, bool SAFE>
+__device__ __forceinline__ void twice_stream(const MixRow &mx, float beta, float ks, bool hold,
+                                             const typename D::T *s, const typename D::T *t,
+                                             int64_t w, int64_t h, int64_t P, int64_t Q,
+                                             float (&acc)[2]) {
+    OpMix<SAFE> op;
+    op.set(mx, beta, ks);
+    op.at[0] = acc[0];
+    op.as[0] = acc[1];
+    if (hold) {
+        sweep<D, TW_U, true, TWICE_BLK, true>(s, t, P, h, op);
+        sweep<D, TW_U, true, TWICE_BLK, true>(s + Q, t + Q, w - Q, 0, op);
+    } else {
+        sweep<D, TW_U, true, TWICE_BLK, true>(s, t, w, h, op);
+    }
+    acc[0] = op.sum_t();
+    acc[1] = op.sum_s();
+}
+
+// The held vectors through the statistics op one at a time (one online batch per
+// vector), chained like held_div below.
+template <class D, class Op>
+__device__ __forceinline__ void held_stats(const u32x4 (&hs)[TW_U], const u32x4 (&ht)[TW_U],
+                                           Op &op) {
+    constexpr int VEC = D::VEC;
+#pragma unroll
+    for (int u = 0; u < TW_U; ++u) {
+        u32x4 xs = hs[u], xt = ht[u];
+        if (u > 0) asm volatile("" : "+v"(xs), "+v"(xt), "+v"(op.a.z), "+v"(op.b.z));
+        float a[1][VEC], b[1][VEC];
+        widen<D>(xs, a[0]);
+        widen<D>(xt, b[0]);
+        const int64_t c[1] = {0};
+        op.template run<1, VEC>(a, b, c);
+    }
+}
+
+// The held vectors through the divergence op one at a time, vector u into accumulator
+// u: the empty asm ties the next vector to the sums of the one before, so only one
+// vector's widened values are live at once (all of them at once spill the 16-bit
+// kernels out of two workgroups per CU).
+template <class D, bool SAFE>
+__device__ __forceinline__ void held_div(const u32x4 (&hs)[TW_U], const u32x4 (&ht)[TW_U],
+                                         OpMix<SAFE> &op) {
+    constexpr int VEC = D::VEC;
+#pragma unroll
+    for (int u = 0; u < TW_U; ++u) {
+        u32x4 xs = hs[u], xt = ht[u];
+        if (u > 0) asm volatile("" : "+v"(xs), "+v"(xt), "+v"(op.at[u - 1]), "+v"(op.as[u - 1]));
+        float a[VEC], b[VEC];
+        widen<D>(xs, a);
+        widen<D>(xt, b);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) op.add(a[e], b[e], op.at[u], op.as[u]);
+    }
+}
+
 template <class D>
 __global__ __launch_bounds__(TWICE_BLK)
 void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restrict__ stats,
@@ -278,7 +369,7 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
     using T = typename D::T;
     constexpr int VEC = D::VEC;
     constexpr int64_t STEP = (int64_t)TW_U * TWICE_BLK;  // vectors per input per sweep step
-    __shared__ float red[4 * (TWICE_BLK / 64)];
+    __shared__ float red[6 * (TWICE_BLK / 64)];
     const int64_t r = blockIdx.x;
     if (row_dropped(o, r)) {
         dropped_row(stats + r * 4, kl + 2 * r, loss + r);
@@ -286,7 +377,11 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
     }
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const int64_t h = head_len<T>(w, s, t);
-    OpStats<3> o1(o.ks);
+    // fp16 rows take the divergence form that admits masked tokens without the range
+    // test: tracking the minima costs the fp16 kernel 26 VGPRs and its second workgroup
+    // per CU
+    constexpr bool RANGE = !std::is_same<D, F16>::value;
+    OpStats<3, RANGE> o1(o.ks);
     // Held steps: the last HOLD + LHOLD full steps of the 16-byte body, elements [P, Q).
     // Rows whose two inputs sit at different offsets inside 16 bytes (h == w), or that
     // are too short, are swept whole.  A lane reads back from LDS only the vectors it
@@ -315,7 +410,7 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
                 lds_step[0][u][threadIdx.x] = ls[u];
                 lds_step[1][u][threadIdx.x] = lt[u];
             }
-            run_held<D>(ls, lt, o1);
+            held_stats<D>(ls, lt, o1);
         }
 #pragma unroll
         for (int k = 0; k < HOLD; ++k) {
@@ -326,7 +421,7 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
                 hs[k][u] = ld16<true>(s + q);
                 ht[k][u] = ld16<true>(t + q);
             }
-            run_held<D>(hs[k], ht[k], o1);
+            held_stats<D>(hs[k], ht[k], o1);
         }
         sweep<D, TW_U, true, TWICE_BLK>(s + Q, t + Q, w - Q, 0, o1);
     } else {
@@ -338,37 +433,41 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
     {
         const MZ ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
         const MZ wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
+        const float ns = RANGE ? wave_min(o1.a.mn) : NINF;
+        const float nt = RANGE ? wave_min(o1.b.mn) : NINF;
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         if (lane == 0) {
             red[2 * wave] = ws.m;
             red[2 * wave + 1] = ws.z;
             red[2 * NW + 2 * wave] = wt.m;
             red[2 * NW + 2 * wave + 1] = wt.z;
+            red[4 * NW + 2 * wave] = ns;
+            red[4 * NW + 2 * wave + 1] = nt;
         }
         __syncthreads();
         if (wave == 0) {
             MZ ms{red[0], red[1]}, mt{red[2 * NW], red[2 * NW + 1]};
+            float mns = red[4 * NW], mnt = red[4 * NW + 1];
             for (int k = 1; k < NW; ++k) {
                 ms = mz_combine(ms, MZ{red[2 * k], red[2 * k + 1]}, o.ks);
                 mt = mz_combine(mt, MZ{red[2 * NW + 2 * k], red[2 * NW + 2 * k + 1]}, o.ks);
+                mns = fminf(mns, red[4 * NW + 2 * k]);
+                mnt = fminf(mnt, red[4 * NW + 2 * k + 1]);
             }
-            row_constants(ms.m, ms.z, mt.m, mt.z, beta, o.ks, stats + r * 4, &rk);
+            row_constants(ms.m, ms.z, mt.m, mt.z, mns, mnt, beta, o.ks, stats + r * 4, &rk);
         }
         __syncthreads();
     }
     const RowK k = rk;
     float v[2] = {0.0f, 0.0f};
     if (!k.undefined) {
-        OpDiv<INTERIOR> op;
-        op.ks = o.ks;
-        op.cs = k.cs;
-        op.ct = k.ct;
-        op.bf = (float)beta;
-        op.gam = k.gam;
-        op.rf = k.rf;
-        if (hold) {  // the held steps first, then the rest of the row streamed again
+        // the held steps (a small part of the row) always take the form that admits
+        // masked tokens: one copy of them keeps the held registers' live range short
+        if (hold) {
+            OpMix<true> oh;
+            oh.set(k.mx, (float)beta, o.ks);
 #pragma unroll
-            for (int k = 0; k < HOLD; ++k) run_held<D>(hs[k], ht[k], op);
+            for (int j = 0; j < HOLD; ++j) held_div<D>(hs[j], ht[j], oh);
             if constexpr (LHOLD > 0) {
                 u32x4 ls[TW_U], lt[TW_U];
 #pragma unroll
@@ -376,20 +475,18 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
                     ls[u] = lds_step[0][u][threadIdx.x];
                     lt[u] = lds_step[1][u][threadIdx.x];
                 }
-                run_held<D>(ls, lt, op);
+                held_div<D>(ls, lt, oh);
             }
-            sweep<D, TW_U, true, TWICE_BLK, true>(s, t, P, h, op);
-            sweep<D, TW_U, true, TWICE_BLK, true>(s + Q, t + Q, w - Q, 0, op);
-        } else {
-            sweep<D, TW_U, true, TWICE_BLK, true>(s, t, w, h, op);
+            v[0] = oh.sum_t();
+            v[1] = oh.sum_s();
         }
-        v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
-        v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
+        if (RANGE && k.fast)
+            twice_stream<D, false>(k.mx, (float)beta, o.ks, hold, s, t, w, h, P, Q, v);
+        else
+            twice_stream<D, true>(k.mx, (float)beta, o.ks, hold, s, t, w, h, P, Q, v);
     }
     block_sum<2, TWICE_BLK>(v, red);
-    if (threadIdx.x == 0)
-        finalize_row(INTERIOR, beta, k.undefined, v[0] * k.izt, v[1] * k.izs, NINF, kl + 2 * r,
-                     loss + r, o.lscale);
+    if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], kl + 2 * r, loss + r, o.lscale);
 }
 
 
@@ -399,6 +496,23 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
 // fp64; an empty shard adds nothing), then sweeps the slices again for the divergence
 // terms.  The pages' cross-rank reductions of [N] statistics become this in-workgroup
 // merge when all shards sit on one device [JSD-PR, Changes; OPS-PR, How].
+// The divergence sweep of k_fwd_shards over every non-empty shard's slice in order.
+template <class D, bool SAFE>
+__device__ __forceinline__ void shards_div(const ShardRows &sr, int64_t r, const MixRow &mx,
+                                           float beta, float ks, float (&v)[2]) {
+    using T = typename D::T;
+    OpMix<SAFE> op;
+    op.set(mx, beta, ks);
+    for (int q = 0; q < sr.S; ++q) {
+        const int64_t w = sr.w[q];
+        if (w == 0) continue;
+        const T *s = row_ptr<T>(sr.s[q], r), *t = row_ptr<T>(sr.t[q], r);
+        sweep<D, 4, true, TWICE_BLK, true>(s, t, w, head_len<T>(w, s, t), op);
+    }
+    v[0] = op.sum_t();
+    v[1] = op.sum_s();
+}
+
 template <class D>
 __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double beta,
                                                           double *__restrict__ stats,
@@ -406,8 +520,8 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
                                                           float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
     constexpr int NW = TWICE_BLK / 64;
-    __shared__ float red[4 * NW];
-    __shared__ float sp[FUSED_SHARDS][4];  // per shard: (m_s, z_s, m_t, z_t)
+    __shared__ float red[6 * NW];
+    __shared__ float sp[FUSED_SHARDS][6];  // per shard: (m_s, z_s, m_t, z_t, min_s, min_t)
     const int64_t r = blockIdx.x;
     if (row_dropped(o, r)) {
         dropped_row(stats + r * 4, kl + 2 * r, loss + r);
@@ -415,7 +529,7 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int q = 0; q < sr.S; ++q) {
-        OpStats<3> o1(o.ks);
+        OpStats<3, true> o1(o.ks);
         const int64_t w = sr.w[q];
         if (w > 0) {
             const T *s = row_ptr<T>(sr.s[q], r), *t = row_ptr<T>(sr.t[q], r);
@@ -423,32 +537,42 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
         }
         const MZ ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
         const MZ wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
+        const float ns = wave_min(o1.a.mn), nt = wave_min(o1.b.mn);
         if (lane == 0) {
             red[2 * wave] = ws.m;
             red[2 * wave + 1] = ws.z;
             red[2 * NW + 2 * wave] = wt.m;
             red[2 * NW + 2 * wave + 1] = wt.z;
+            red[4 * NW + 2 * wave] = ns;
+            red[4 * NW + 2 * wave + 1] = nt;
         }
         __syncthreads();
         if (threadIdx.x == 0) {
             MZ ms{red[0], red[1]}, mt{red[2 * NW], red[2 * NW + 1]};
+            float mns = red[4 * NW], mnt = red[4 * NW + 1];
             for (int k = 1; k < NW; ++k) {
                 ms = mz_combine(ms, MZ{red[2 * k], red[2 * k + 1]}, o.ks);
                 mt = mz_combine(mt, MZ{red[2 * NW + 2 * k], red[2 * NW + 2 * k + 1]}, o.ks);
+                mns = fminf(mns, red[4 * NW + 2 * k]);
+                mnt = fminf(mnt, red[4 * NW + 2 * k + 1]);
             }
             sp[q][0] = ms.m;
             sp[q][1] = ms.z;
             sp[q][2] = mt.m;
             sp[q][3] = mt.z;
+            sp[q][4] = mns;
+            sp[q][5] = mnt;
         }
         __syncthreads();
     }
     __shared__ RowK rk;
     if (wave == 0) {
-        float ms = NINF, mt = NINF;
+        float ms = NINF, mt = NINF, ns = __builtin_huge_valf(), nt = __builtin_huge_valf();
         for (int q = 0; q < sr.S; ++q) {
             ms = fmaxf(ms, sp[q][0]);
             mt = fmaxf(mt, sp[q][2]);
+            ns = fminf(ns, sp[q][4]);
+            nt = fminf(nt, sp[q][5]);
         }
         const double cs = refc(ms, o.ks), ct = refc(mt, o.ks);
         double zs = 0.0, zt = 0.0;
@@ -456,32 +580,17 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
             if (sp[q][0] != NINF) zs += (double)sp[q][1] * exp2((double)refc(sp[q][0], o.ks) - cs);
             if (sp[q][2] != NINF) zt += (double)sp[q][3] * exp2((double)refc(sp[q][2], o.ks) - ct);
         }
-        row_constants(ms, zs, mt, zt, beta, o.ks, stats + r * 4, &rk);
+        row_constants(ms, zs, mt, zt, ns, nt, beta, o.ks, stats + r * 4, &rk);
     }
     __syncthreads();
     const RowK k = rk;
     float v[2] = {0.0f, 0.0f};
     if (!k.undefined) {
-        OpDiv<INTERIOR> op;
-        op.ks = o.ks;
-        op.cs = k.cs;
-        op.ct = k.ct;
-        op.bf = (float)beta;
-        op.gam = k.gam;
-        op.rf = k.rf;
-        for (int q = 0; q < sr.S; ++q) {
-            const int64_t w = sr.w[q];
-            if (w == 0) continue;
-            const T *s = row_ptr<T>(sr.s[q], r), *t = row_ptr<T>(sr.t[q], r);
-            sweep<D, 4, true, TWICE_BLK, true>(s, t, w, head_len<T>(w, s, t), op);
-        }
-        v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
-        v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
+        if (k.fast) shards_div<D, false>(sr, r, k.mx, (float)beta, o.ks, v);
+        else shards_div<D, true>(sr, r, k.mx, (float)beta, o.ks, v);
     }
     block_sum<2, TWICE_BLK>(v, red);
-    if (threadIdx.x == 0)
-        finalize_row(INTERIOR, beta, k.undefined, v[0] * k.izt, v[1] * k.izs, NINF, kl + 2 * r,
-                     loss + r, o.lscale);
+    if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], kl + 2 * r, loss + r, o.lscale);
 }
 
 template <class D, int NVT>

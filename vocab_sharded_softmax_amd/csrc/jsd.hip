@@ -61,40 +61,65 @@ __global__ __launch_bounds__(BLOCK) void k_div(RowView sv, RowView tv, int64_t w
     __shared__ float red[3 * NWAVE];
     const int64_t r = blockIdx.x;
     const RowConst k = row_const(stats, r, o.ks);
-    float pt = 0.0f, ps = 0.0f, F = NINF;
+    // interior: (KL(p_t||M), KL(p_s||M)) / ln 2 of this shard before the row's offset
+    // (mix_finish); endpoints: base-2 partial KL sums scaled by 1 / Z
+    double pt = 0.0, ps = 0.0;
+    float F = NINF;
+    MixRow mx{};
     // a dropped row has statistics (-inf, ...) and so counts as undefined here
+    if (!k.undefined) {
+        if constexpr (MODE == INTERIOR) mx = mix_row(beta, k.cs, k.Zs, k.ct, k.Zt);
+    }
     if (!k.undefined && w > 0) {
         const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
-        OpDiv<MODE> op;
-        op.ks = o.ks;
-        op.cs = k.cs;
-        op.ct = k.ct;
-        op.bf = (float)beta;
-        op.gam = (float)((1.0 - beta) * k.Zt / k.Zs);
-        op.rf = (float)k.r;
-        sweep<D, 4, true, BLOCK, true>(s, t, w, head_len<T>(w, s, t), op);
-        float v[2] = {(op.At[0] + op.At[1]) + (op.At[2] + op.At[3]),
-                      (op.As[0] + op.As[1]) + (op.As[2] + op.As[3])};
+        float v[2];
+        if constexpr (MODE == INTERIOR) {
+            // no row minimum in this pass: masked tokens admitted throughout
+            OpMix<true> op;
+            op.set(mx, (float)beta, o.ks);
+            sweep<D, 4, true, BLOCK, true>(s, t, w, head_len<T>(w, s, t), op);
+            v[0] = op.sum_t();
+            v[1] = op.sum_s();
+        } else {
+            OpDiv<MODE> op;
+            op.ks = o.ks;
+            op.cs = k.cs;
+            op.ct = k.ct;
+            op.bf = (float)beta;
+            op.gam = (float)((1.0 - beta) * k.Zt / k.Zs);
+            op.rf = (float)k.r;
+            sweep<D, 4, true, BLOCK, true>(s, t, w, head_len<T>(w, s, t), op);
+            v[0] = (op.At[0] + op.At[1]) + (op.At[2] + op.At[3]);
+            v[1] = (op.As[0] + op.As[1]) + (op.As[2] + op.As[3]);
+            F = op.F;
+        }
         block_sum<2>(v, red);
-        const float f = wave_max(op.F);
+        const float f = wave_max(F);
         if ((threadIdx.x & 63) == 0) red[2 * NWAVE + (threadIdx.x >> 6)] = f;
         __syncthreads();
         if (threadIdx.x == 0) {
-            pt = v[0] * k.izt;
-            ps = v[1] * k.izs;
+            if constexpr (MODE == INTERIOR) {
+                pt = v[0] * mx.izt;
+                ps = v[1] * mx.izs;
+            } else {
+                pt = v[0] * k.izt;
+                ps = v[1] * k.izs;
+            }
             for (int q = 0; q < NWAVE; ++q) F = fmaxf(F, red[2 * NWAVE + q]);
         }
     }
     if (threadIdx.x == 0) {
         if (loss) {
-            if (row_dropped(o, r))
+            if (row_dropped(o, r)) {
                 masked_row(kl + 2 * r, loss + r);
-            else
+            } else {
+                if (MODE == INTERIOR && !k.undefined) ps -= mx.delta;
                 finalize_row(MODE, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r, o.lscale);
+            }
         } else {
             float *o = part_k + r * PART_STRIDE;
-            o[0] = pt;
-            o[1] = ps;
+            o[0] = (float)pt;
+            o[1] = (float)ps;
             o[2] = F;
         }
     }
@@ -118,6 +143,7 @@ __global__ void k_div_finalize(int mode, const float *__restrict__ part, int S, 
         ps += p[1];
         F = fmaxf(F, p[2]);
     }
+    if (mode == INTERIOR && !k.undefined) ps -= mix_row(beta, k.cs, k.Zs, k.ct, k.Zt).delta;
     finalize_row(mode, beta, k.undefined, pt, ps, F, kl + 2 * r, loss + r, o.lscale);
 }
 

@@ -83,9 +83,12 @@ __device__ __forceinline__ void zero_span(typename D::T *p, int64_t n) {
 }
 
 // Online (max, sum of 2^(x*ks - c)) of one input over a batch of n elements: one
-// rescale per batch, a tree sum of the batch's exponentials.
+// rescale per batch, a tree sum of the batch's exponentials.  With MIN it also keeps
+// the smallest element (the range test of the interior divergence's plain form).
+template <bool MIN = false>
 struct Online {
     float m = NINF, c = 0.0f, z = 0.0f;
+    float mn = __builtin_huge_valf();  // MIN only
     float ks = L2E;  // log2 e / temperature
 
     template <int N>
@@ -93,6 +96,12 @@ struct Online {
         float bm = x[0];
 #pragma unroll
         for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
+        if constexpr (MIN) {
+            float bn = x[0];
+#pragma unroll
+            for (int i = 1; i < N; ++i) bn = fminf(bn, x[i]);
+            mn = fminf(mn, bn);
+        }
         const float nm = fmaxf(m, bm);
         const float nc = refc(nm, ks);
         const float scale = m == NINF ? 0.0f : ex2(c - nc);
@@ -110,10 +119,10 @@ struct Online {
 };
 
 // Sweep op of the statistics pass: online (max, sum-exp) of the first input, and of
-// the second when WHICH == 3.
-template <int WHICH>
+// the second when WHICH == 3; MIN also tracks each input's smallest element.
+template <int WHICH, bool MIN = false>
 struct OpStats {
-    Online a, b;  // first and second swept input
+    Online<MIN> a, b;  // first and second swept input
     __device__ explicit OpStats(float ks = L2E) {
         a.ks = ks;
         b.ks = ks;
@@ -121,8 +130,8 @@ struct OpStats {
     template <int NV, int W>
     __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
                                         const int64_t (&)[NV]) {
-        a.add<NV * W>(&x[0][0]);
-        if (WHICH == 3) b.add<NV * W>(&y[0][0]);
+        a.template add<NV * W>(&x[0][0]);
+        if (WHICH == 3) b.template add<NV * W>(&y[0][0]);
     }
 };
 
