@@ -90,7 +90,8 @@ enum {
     VJSD_ERR_BETA = -3,        /* beta NaN or outside [0, 1] */
     VJSD_ERR_LAYOUT = -4,      /* shards not ordered/contiguous, or vocabulary size mismatch */
     VJSD_ERR_EMPTY_SHARD = -5, /* a shard of width 0 given to the log-probability op */
-    VJSD_ERR_HIP = -6          /* the HIP runtime refused a launch */
+    VJSD_ERR_HIP = -6,         /* the HIP runtime refused a launch */
+    VJSD_ERR_SCRATCH = -7      /* more rows than the no-allocation scratch holds */
 };
 
 /* Read-only view of one shard of one input (see "Views"). */
@@ -248,6 +249,27 @@ VJSD_API int vjsd_loss_backward(const vjsd_shard *shards, int S, int64_t N, int 
  */
 VJSD_API int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
              const float *kl, double beta, const float *grad_loss, float *part, void *stream);
+
+/*
+ * vjsd_bwd without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The per-row constants that vjsd_bwd writes into `part` go instead to an
+ * array the library owns in device memory, VJSD_NOALLOC_MAX_ROWS rows of 64 bytes
+ * (4 MiB), which each device the library runs on holds until the process ends.  Its
+ * address on a device is looked up once, on the first call there.  The call itself
+ * allocates nothing; every other argument, the results and the errors are those of
+ * vjsd_bwd, which shares its kernels.  Every call on one device uses that device's one
+ * array, and a call fully rewrites the rows it reads before reading them: calls that
+ * overlap on one device (concurrent streams, or threads) race on the array, so the
+ * caller must serialise them.  `stream` must belong to the current device (NULL: the
+ * current device's null stream).  Extra errors: VJSD_ERR_SCRATCH when N exceeds
+ * VJSD_NOALLOC_MAX_ROWS; VJSD_ERR_ARG when the stream belongs to another device;
+ * VJSD_ERR_HIP when the array's address cannot be obtained.
+ */
+#define VJSD_NOALLOC_MAX_ROWS 65536
+VJSD_API int vjsd_bwd_noalloc(const vjsd_shard *shards, int S, int64_t N, int dtype,
+                              const double *stats, const float *kl, double beta,
+                              const float *grad_loss, void *stream);
 
 /*
  * KL divergence [OPS-PR, What]: KL(p_t || p_s), or KL(p_s || p_t) when reverse != 0,

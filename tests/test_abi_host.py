@@ -17,7 +17,7 @@ abi = pytest.importorskip("vocab_sharded_softmax_amd._abi")
 lib = abi.lib
 Shard, View = abi.Shard, abi.View
 
-OK, ARG, DTYPE, BETA, LAYOUT, EMPTY = 0, -1, -2, -3, -4, -5
+OK, ARG, DTYPE, BETA, LAYOUT, EMPTY, SCRATCH = 0, -1, -2, -3, -4, -5, -7
 FAKE = 0x10000  # a well-aligned address that is never dereferenced here
 
 
@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
@@ -325,3 +325,16 @@ def test_linear_workspace_and_scale():
     assert s(FAKE, -1, 2, FAKE, None) == ARG
     assert s(FAKE + 4, 10, 0, FAKE, None) == ARG
     assert s(FAKE, 10, 0, None, None) == ARG
+
+
+def test_noalloc_backward_checks_before_any_device_call():
+    """vjsd_bwd_noalloc validates like vjsd_bwd and refuses more rows than its scratch
+    holds, all on the host (no device is touched here)."""
+    a = shards([8], grads=True)
+    assert lib.vjsd_bwd_noalloc(a, 1, 0, 2, None, None, 0.5, None, None) == OK
+    assert lib.vjsd_bwd_noalloc(a, 1, 4, 2, FAKE, FAKE, 1.5, FAKE, None) == BETA
+    assert lib.vjsd_bwd_noalloc(a, 1, 4, 7, FAKE, FAKE, 0.5, FAKE, None) == DTYPE
+    assert lib.vjsd_bwd_noalloc(a, 1, 4, 2, FAKE, None, 0.5, FAKE, None) == ARG
+    big = 65536 + 1
+    assert lib.vjsd_bwd_noalloc(a, 1, big, 2, FAKE, FAKE, 0.5, FAKE, None) == SCRATCH
+    assert b"65536" in lib.vjsd_strerror(SCRATCH)

@@ -6,6 +6,7 @@ The compute path is libvjsd.so (hand-written HIP kernels for gfx950, C ABI in
 library has not been built.
 """
 from ._abi import (ShardSet, VjsdArgumentError, VjsdError, loss_opts, new_part, vjsd_bwd,
+                   vjsd_bwd_noalloc,
                    vjsd_forward, vjsd_fwd, vjsd_loss_backward, vjsd_loss_forward,
                    vjsd_membw_probe, vjsd_merge, vjsd_stats, vjsd_strerror, vjsd_workspace_bytes,
                    ventropy_bwd, ventropy_fwd, vkl_bwd, vkl_fwd, vlogprobs_bwd, vlogprobs_fwd,
@@ -19,7 +20,8 @@ __all__ = [
     "jsd", "jsd_loss", "kl_div", "entropy", "logprobs", "topk_kl", "cross_entropy", "linear_jsd",
     "vlin_gemm", "vljsd", "vljsd_workspace_bytes", "vlin_scale", "lin_operand", "lin_head",
     "vtopk_kl_fwd", "vtopk_kl_bwd", "vce_fwd", "vce_bwd", "ShardSet", "VjsdError", "VjsdArgumentError",
-    "vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vkl_fwd", "vkl_bwd", "ventropy_fwd",
+    "vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vjsd_bwd_noalloc",
+    "vkl_fwd", "vkl_bwd", "ventropy_fwd",
     "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd", "vjsd_strerror", "vjsd_workspace_bytes",
     "vjsd_membw_probe", "vjsd_loss_forward", "vjsd_loss_backward", "loss_opts", "new_part",
     "LIB_PATH",

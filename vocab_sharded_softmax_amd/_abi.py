@@ -78,6 +78,7 @@ def _load():
         "vjsd_fwd": ([SP, I, I64, I, P, D, P, P, P, P], I),
         "vjsd_forward": ([SP, I, I64, I, D, P, P, P, P, P], I),
         "vjsd_bwd": ([SP, I, I64, I, P, P, D, P, P, P], I),
+        "vjsd_bwd_noalloc": ([SP, I, I64, I, P, P, D, P, P], I),
         "vkl_fwd": ([SP, I, I64, I, I, P, P, P, P, P], I),
         "vkl_bwd": ([SP, I, I64, I, I, P, P, P, P, P], I),
         "ventropy_fwd": ([SP, I, I64, I, P, P, P, P], I),
@@ -282,6 +283,14 @@ def vjsd_bwd(sh: ShardSet, stats, kl, beta: float, grad_loss, part, stream=None)
                         _ptr(kl, torch.float32, N * 2, "kl"), float(beta),
                         _ptr(grad_loss, torch.float32, N, "grad_loss"),
                         _ptr(part, torch.float32, part_floats(N, sh.S), "part"), _stream(stream)))
+
+
+def vjsd_bwd_noalloc(sh: ShardSet, stats, kl, beta: float, grad_loss, stream=None) -> None:
+    N = sh.N
+    _check(lib.vjsd_bwd_noalloc(sh.arr, sh.S, N, sh.dtype_code,
+                                _ptr(stats, torch.float64, N * 4, "stats"),
+                                _ptr(kl, torch.float32, N * 2, "kl"), float(beta),
+                                _ptr(grad_loss, torch.float32, N, "grad_loss"), _stream(stream)))
 
 
 def loss_opts(N: int, temperature: float = 1.0, scale_t2: bool = False, mask=None,

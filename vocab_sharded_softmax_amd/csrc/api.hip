@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kernels.hpp"
 #include "vjsd.h"
 
@@ -286,6 +288,36 @@ int bwd_all(const vjsd_shard *shards, int S, int64_t N, int dtype, int mode, con
     return VJSD_OK;
 }
 
+// Per-row constants of vjsd_bwd_noalloc: a file-scope device array.  In host code the
+// name `scratch` is a host-side stand-in; kernels get the per-device address that
+// hipGetSymbolAddress returns, kept in scratch_ptr.
+static __device__ __align__(256) float scratch[(size_t)VJSD_NOALLOC_MAX_ROWS * vjsd::ROWC];
+constexpr int SCRATCH_DEVICES = 64;
+std::atomic<float *> scratch_ptr[SCRATCH_DEVICES];
+
+// This device's address of `scratch`, looked up on the first call on the device (a
+// second thread racing through the lookup stores the same address).  The stream must
+// belong to the current device.
+int scratch_of(hipStream_t st, float **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return VJSD_ERR_HIP;
+    if (dev < 0 || dev >= SCRATCH_DEVICES) return VJSD_ERR_ARG;
+    if (st) {
+        hipDevice_t sd = 0;
+        if (hipStreamGetDevice(st, &sd) != hipSuccess) return VJSD_ERR_HIP;
+        if (sd != dev) return VJSD_ERR_ARG;
+    }
+    float *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return VJSD_ERR_HIP;
+        p = static_cast<float *>(q);
+        scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return VJSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -299,6 +331,9 @@ const char *vjsd_strerror(int code) {
         case VJSD_ERR_LAYOUT: return "shards must be ordered and contiguous in the vocabulary";
         case VJSD_ERR_EMPTY_SHARD: return "log-probabilities need every vocabulary shard non-empty";
         case VJSD_ERR_HIP: return "HIP kernel launch failed";
+        case VJSD_ERR_SCRATCH:
+            return "more rows than the no-allocation backward's scratch holds "
+                   "(VJSD_NOALLOC_MAX_ROWS = 65536)";
         default: return "unknown vjsd status";
     }
 }
@@ -479,6 +514,25 @@ int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double
     if ((e = hip_status(vjsd::launch_bwd_prep(mode, N, stats, kl, beta, grad_loss, part, st))))
         return e;
     return bwd_all(shards, S, N, dtype, mode, part, st);
+}
+
+int vjsd_bwd_noalloc(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
+                     const float *kl, double beta, const float *grad_loss, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    if ((e = check_views(shards, S, N, dtype, true, true))) return e;
+    if (N == 0) return VJSD_OK;
+    if (!stats || !kl || !grad_loss) return VJSD_ERR_ARG;
+    if (N > VJSD_NOALLOC_MAX_ROWS) return VJSD_ERR_SCRATCH;
+    hipStream_t st = (hipStream_t)stream;
+    float *rowc = nullptr;
+    if ((e = scratch_of(st, &rowc))) return e;
+    const int mode = mode_of(beta);
+    // k_bwd_prep writes every constant of rows [0, N) that the gradient kernels read
+    if ((e = hip_status(vjsd::launch_bwd_prep(mode, N, stats, kl, beta, grad_loss, rowc, st))))
+        return e;
+    return bwd_all(shards, S, N, dtype, mode, rowc, st);
 }
 
 int vkl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse, float *part,
