@@ -51,7 +51,8 @@
  * overlap in time.
  *
  * Ownership and streams.  The caller owns every buffer.  The library allocates no
- * memory, keeps no state between calls and is reentrant; every call only enqueues
+ * memory, keeps no state between calls (vjsd_bwd_noalloc's device array aside) and is
+ * reentrant; every call only enqueues
  * kernels on `stream` (a hipStream_t; NULL is the null stream) and returns without
  * synchronising.  Buffers must stay valid until the enqueued work completes.
  * Outputs must not alias inputs.

@@ -1,6 +1,6 @@
 // api.hip -- the extern "C" entry points of libvjsd: argument validation on the host,
 // then one launch per shard per pass on the caller's stream.  The library allocates
-// nothing and keeps no state.  The operations and their citations are documented in
+// nothing and keeps no state, except the device array of vjsd_bwd_noalloc (below).  The operations and their citations are documented in
 // include/vjsd.h.
 #include <math.h>
 #include <string.h>
