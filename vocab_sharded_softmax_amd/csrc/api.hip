@@ -1,7 +1,7 @@
 // api.hip -- the extern "C" entry points of libvjsd: argument validation on the host,
 // then one launch per shard per pass on the caller's stream.  The library allocates
-// nothing and keeps no state, except the device array of vjsd_bwd_noalloc (below).  The operations and their citations are documented in
-// include/vjsd.h.
+// nothing and keeps no state, except the device array of vjsd_bwd_noalloc (below).
+// The operations and their citations are documented in include/vjsd.h.
 #include <math.h>
 #include <string.h>
 
