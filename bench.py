@@ -33,27 +33,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+# Transcendental results per second: 1024 SIMDs x 2.4 GHz x 8 lanes per cycle.  The
+# 157.3 TFLOP/s FP32 vector peak is 32 FMA lanes per SIMD per cycle; v_exp_f32 and
+# v_log_f32 issue at a quarter of that rate (a wave64 instruction every 8 cycles,
+# measured on MI355X against 2.2 cycles for v_add_f32 / v_fma_f32).
+PEAK_TRANS_PER_S = 1024 * 2.4e9 * 8
 METRIC = "JSD fwd+bwd tokens/s and HBM GB/s (% peak), N=8192 V=151936 bf16, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CSRC = os.path.join(ROOT, "vocab_sharded_softmax_amd", "csrc")
-# the sources each profiled kernel is compiled from: its counters stay valid while
-# these files are unchanged
-HEADERS = ["device.hpp", "sweep.hpp", "divergence.hpp", "kernels.hpp"]
-KERNEL_SOURCES = {
-    "bwd_bf16_interior_both": ["jsd.hip"] + HEADERS,
-    "fwd_twice_bf16": ["fused.hip"] + HEADERS,
-}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def sources_digest(names) -> str:
+def sources_digest() -> str:
+    """Digest of every kernel source: committed counters are used only while it matches
+    the digest recorded with them."""
     h = hashlib.sha256()
-    for name in sorted(names):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -73,6 +74,8 @@ def parse():
                    help="time the step only (no per-part, branch, shard-width or sibling rows)")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a streaming 2 GiB device copy (counter calibration for rocprofv3)")
+    p.add_argument("--counter-set", action="store_true",
+                   help="only run the forward and backward of each counted workload (rocprofv3 --pmc)")
     return p.parse_args()
 
 
@@ -181,15 +184,125 @@ def cpu_baseline(torch, s, t, gout, budget_s):
                       f"{rows_done} of {N} rows of the same workload, {elapsed:.1f} s"}
 
 
-def traffic_entry(kernel_key):
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    with open(TRAFFIC_FILE) as f:
-        rec = json.load(f)
-    k = rec.get("kernels", {}).get(kernel_key)
-    if k is None or k.get("sources_sha") != sources_digest(KERNEL_SOURCES[kernel_key]):
-        return None  # the kernel changed since the counters were taken
-    return k.get("bytes_per_launch")
+_COUNTERS = None
+
+
+def counters(workload):
+    """The committed rocprofv3 counters of a workload's forward and backward (bytes
+    fetched and written per step, scaled by the copy calibration; VALU and
+    transcendental instructions), or None when the kernel sources changed since they
+    were taken."""
+    global _COUNTERS
+    if _COUNTERS is None:
+        _COUNTERS = {}
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                rec = json.load(f)
+            if rec.get("sources_sha") == sources_digest():
+                _COUNTERS = rec.get("workloads", {})
+    return _COUNTERS.get(workload)
+
+
+def traffic_fields(workload, ms_fwd, ms_bwd, ms_step, compulsory_bytes, pages_bytes):
+    """HBM rate and fraction of a step on the bytes its kernels move: the counters'
+    fetch + write bytes when they match the sources ("bytes_basis": "counters"), else the
+    compulsory bytes (one forward read of the inputs, the backward's read and its
+    gradient writes), which are a lower bound of the traffic.  The pages' count (three
+    input passes plus the gradient writes) is reported beside, labelled as such; the
+    held steps and caches let it exceed what the kernels fetch.  With counters, the
+    transcendental utilisation of the forward and backward: their transcendental
+    results per second against PEAK_TRANS_PER_S."""
+    c = counters(workload)
+    if c is not None:
+        nbytes, basis = c["fwd"]["bytes"] + c["bwd"]["bytes"], "counters"
+    else:
+        nbytes, basis = compulsory_bytes, "compulsory"
+    gbps = nbytes / (ms_step * 1e-3) / 1e9
+    out = {"bytes_per_step": nbytes, "bytes_basis": basis, "hbm_gbps": round(gbps, 1),
+           "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "pages_equivalent_bytes": pages_bytes,
+           "pages_equivalent_frac": round(pages_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    if c is not None:
+        out["counter_bytes"] = {"fwd": c["fwd"]["bytes"], "bwd": c["bwd"]["bytes"]}
+        out["trans_util"] = {
+            "fwd": round(c["fwd"]["trans_lane_insts"] / (ms_fwd * 1e-3) / PEAK_TRANS_PER_S, 4),
+            "bwd": round(c["bwd"]["trans_lane_insts"] / (ms_bwd * 1e-3) / PEAK_TRANS_PER_S, 4)}
+        out["valu_busy_pct"] = {"fwd": c["fwd"].get("valu_busy_pct"),
+                                "bwd": c["bwd"].get("valu_busy_pct")}
+    return out
+
+
+# The workloads whose forward and backward the committed counters cover, in the order
+# `--counter-set` runs them: name -> (draw arguments, beta, shard widths, student only).
+COUNTER_WORKLOADS = {
+    "full_vocab": (("full_vocab",), {}, 0.5, None, False),
+    "tp8_shard": (("tp8_shard",), {}, 0.5, None, False),
+    "tp8_shard_teacher_detached": (("tp8_shard",), {}, 0.5, None, True),
+    "robust_fp32_4_shards": (("robust",), {}, 0.5, "robust", False),
+    "robust_fp32_1_shard": (("robust",), {}, 0.5, None, False),
+    "rank_share_75968": (("full_vocab",), {"N": 1024, "V": 75968}, 0.3, None, True),
+    "rank_share_37984": (("full_vocab",), {"N": 1024, "V": 37984}, 0.3, None, True),
+}
+
+
+class Workload:
+    """Inputs, outputs and workspace of one JSD workload through the C ABI, preallocated:
+    fwd() is vjsd_forward, bwd() vjsd_bwd (both gradients, or the student's alone)."""
+
+    def __init__(self, torch, vj, synth, name, batch=None):
+        draw, kw, self.beta, widths, student_only = COUNTER_WORKLOADS[name]
+        self.name = name
+        b = batch if batch is not None else synth.draw(*draw, device="cuda", **kw)
+        if widths == "robust":
+            widths = list(synth.WORKLOADS["robust"].widths)
+        self.b = b
+        N, V = b.s.shape
+        self.N, self.V, self.S = N, V, 1 if widths is None else len(widths)
+        self.tensor_bytes = N * V * b.s.element_size()
+        self.ngrads = 1 if student_only else 2
+        self.part = vj.new_part(N, self.S, "cuda")
+        self.stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
+        self.kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
+        self.loss = torch.empty((N,), dtype=torch.float32, device="cuda")
+        self.gs = torch.empty_like(b.s)
+        self.gt = None if student_only else torch.empty_like(b.t)
+        self.sh = vj.ShardSet(b.s, b.t, widths=widths)
+        self.shg = vj.ShardSet(b.s, b.t, widths=widths, gs=self.gs, gt=self.gt)
+        self.vj = vj
+
+    def fwd(self):
+        self.vj.vjsd_forward(self.sh, self.beta, self.part, self.stats, self.kl, self.loss)
+
+    def bwd(self):
+        self.vj.vjsd_bwd(self.shg, self.stats, self.kl, self.beta, self.b.gout, self.part)
+
+    def compulsory_bytes(self):
+        """One forward read and one backward read of both inputs, and the gradients."""
+        return (4 + self.ngrads) * self.tensor_bytes
+
+    def pages_bytes(self):
+        """The pages' count: three input passes over both inputs, and the gradients."""
+        return (6 + self.ngrads) * self.tensor_bytes
+
+
+def counter_set(torch, vj, synth, reps=3):
+    """Each of COUNTER_WORKLOADS in turn, for rocprofv3 --pmc runs: a one-page read with
+    the bandwidth probe (a marker dispatch that opens the workload's dispatches), then
+    1 + reps steps of the forward and the backward."""
+    marker_src = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    marker_dst = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    for name in COUNTER_WORKLOADS:
+        w = Workload(torch, vj, synth, name)
+        torch.cuda.synchronize()
+        vj.vjsd_membw_probe(marker_src, marker_dst, 0)
+        for _ in range(1 + reps):
+            w.fwd()
+            w.bwd()
+        torch.cuda.synchronize()
+        log(f"counter set: {name} ({1 + reps} steps)")
+        del w
+        torch.cuda.empty_cache()
+    print(json.dumps({"counter_set": list(COUNTER_WORKLOADS), "steps": 1 + reps}))
 
 
 def main():
@@ -208,6 +321,11 @@ def main():
 
     if args.calib_copy:
         calib_copy(torch)
+        return
+    if args.counter_set:
+        import synth
+        import vocab_sharded_softmax_amd as vj
+        counter_set(torch, vj, synth)
         return
 
     import synth
@@ -266,8 +384,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     tensor_bytes = N * V * el
-    bytes_alg = 8 * tensor_bytes  # 3 input passes over s and t + 2 gradient writes
-    bytes_bwd = 4 * tensor_bytes  # read s, t; write gs, gt
+    bytes_bwd = 4 * tensor_bytes  # read s, t; write gs, gt: the backward's algorithmic bytes
     bwd_ms = timer.ms("bwd")
     achieved = bytes_bwd / (bwd_ms * 1e-3) / 1e9
     per_kernel = {k: round(timer.ms(k), 4) for k in ("forward", "bwd", "step")}
@@ -329,10 +446,11 @@ def main():
     ceil = ceilings(torch, vj, s, t, gs)
     ceil["bwd_frac_of_copy"] = round(achieved / ceil["copy_gbps"], 4)
     fwd_ms = timer.ms("forward")
-    # the forward as if it read both sweeps in full (the pages' count); it holds the
-    # statistics sweep's last steps on chip, so it fetches less and this can exceed 1
-    ceil["fwd_two_reads_frac_of_read"] = round(
-        4 * tensor_bytes / (fwd_ms * 1e-3) / 1e9 / ceil["read_gbps"], 4)
+    # the forward's fetched bytes (counters) against the measured read ceiling
+    cfv = counters("full_vocab")
+    if cfv is not None:
+        ceil["fwd_frac_of_read"] = round(
+            cfv["fwd"]["bytes"] / (fwd_ms * 1e-3) / 1e9 / ceil["read_gbps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -365,16 +483,12 @@ def main():
         "config": {"workload": "full_vocab N=8192 V=151936 bf16 logits, Zipf column bias",
                    "global_batch": N, "vocab": V, "storage_dtype": "bf16",
                    "betas": betas, "grads": "student and teacher", "shards": 1},
-        "hbm_gbps": round(bytes_alg / (ms_step * 1e-3) / 1e9, 1),
-        "hbm_frac": round(bytes_alg / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "bytes_alg_per_step": bytes_alg,
-        # one forward read and one backward read of s and t, plus the gradient writes
-        "bytes_compulsory_per_step": 6 * tensor_bytes,
-        "hbm_frac_compulsory": round(6 * tensor_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        **traffic_fields("full_vocab", timer.ms("forward"), bwd_ms, ms_step, 6 * tensor_bytes,
+                         8 * tensor_bytes),
         "roofline": {"kernel": "k_bwd<BF16, interior, both grads>", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic_entry("bwd_bf16_interior_both"),
+                     "traffic": (counters("full_vocab") or {}).get("bwd", {}).get("bytes"),
                      "bytes_per_launch": bytes_bwd, "avg_launch_ms": round(bwd_ms, 4)},
         "cpu_baseline": cpu,
         "step_ms_spread": timer.spread("step"),
@@ -440,99 +554,63 @@ def fused_linear_row(torch, vj, synth, reps=3, chunk=4096):
 
 def tp8_forward(torch, vj, synth, reps=10):
     """JSD at one tensor-parallel rank's vocabulary shard (N=8192, V=16032 bf16, one
-    shard, beta=0.5): the one-pass forward (a row per workgroup, held in registers)
-    against the same forward as three launches, and the backward."""
-    b = synth.draw("tp8_shard", device="cuda")
-    N, V = b.s.shape
-    tb = N * V * b.s.element_size()
-    part = vj.new_part(N, 1, "cuda")
-    stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
-    kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
-    loss = torch.empty((N,), dtype=torch.float32, device="cuda")
-    gs, gt = torch.empty_like(b.s), torch.empty_like(b.t)
-    sh = vj.ShardSet(b.s, b.t)
-    shg = vj.ShardSet(b.s, b.t, gs=gs, gt=gt)
-    ops = {
-        "one_pass_forward": lambda: vj.vjsd_forward(sh, 0.5, part, stats, kl, loss),
-        "three_launch_forward": lambda: (vj.vjsd_stats(sh, 3, part),
-                                         vj.vjsd_merge(part, 1, N, 3, stats),
-                                         vj.vjsd_fwd(sh, stats, 0.5, part, kl, loss)),
-        "bwd": lambda: vj.vjsd_bwd(shg, stats, kl, 0.5, b.gout, part),
-    }
-    res = {}
-    for name, fn in ops.items():
-        fn()
-        fn()
-        tm = Timer(torch)
-        for _ in range(reps):
-            a = tm.mark()
-            fn()
-            tm.add("x", a, tm.mark())
-        torch.cuda.synchronize()
-        res[name + "_ms"] = round(tm.ms("x"), 4)
-    res["one_pass_forward_gbps"] = round(2 * tb / (res["one_pass_forward_ms"] * 1e-3) / 1e9, 1)
-    res["bwd_gbps"] = round(4 * tb / (res["bwd_ms"] * 1e-3) / 1e9, 1)
-    res["tokens_per_s"] = round(N / ((res["one_pass_forward_ms"] + res["bwd_ms"]) * 1e-3), 1)
+    shard, beta=0.5, both gradients) through the C ABI: the one-pass forward (a row per
+    workgroup, held in registers) against the same forward as three launches, the
+    backward, and the step's traffic."""
+    w = Workload(torch, vj, synth, "tp8_shard")
+    three = lambda: (vj.vjsd_stats(w.sh, 3, w.part), vj.vjsd_merge(w.part, 1, w.N, 3, w.stats),
+                     vj.vjsd_fwd(w.sh, w.stats, 0.5, w.part, w.kl, w.loss))
+    res = {"one_pass_forward_ms": round(timed(torch, w.fwd, reps), 4),
+           "three_launch_forward_ms": round(timed(torch, three, reps), 4)}
+    row = workload_row(torch, w, reps)
+    res.update({k: row[k] for k in row if k not in ("N", "V", "shards", "fwd_ms")})
+    del w
+    torch.cuda.empty_cache()
     return res
 
 
+def timed(torch, fn, reps=10):
+    """Mean HIP-event time of fn after two untimed calls."""
+    fn()
+    fn()
+    tm = Timer(torch)
+    for _ in range(reps):
+        a = tm.mark()
+        fn()
+        tm.add("x", a, tm.mark())
+    torch.cuda.synchronize()
+    return tm.ms("x")
+
+
+def workload_row(torch, w, reps=10):
+    """Forward, backward and step of a Workload, with its traffic fields."""
+    f_ms = timed(torch, w.fwd, reps)
+    b_ms = timed(torch, w.bwd, reps)
+    step = timed(torch, lambda: (w.fwd(), w.bwd()), reps)
+    return {"N": w.N, "V": w.V, "shards": w.S, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "fwd_bwd_ms": round(step, 4), "tokens_per_s": round(w.N / (step * 1e-3), 1),
+            **traffic_fields(w.name, f_ms, b_ms, step, w.compulsory_bytes(), w.pages_bytes())}
+
+
 def config_rows(torch, vj, synth, reps=10):
-    """The other configurations of the path, each fwd+bwd with both gradients unless
-    stated: the tiny fp32 case (launch-latency bound, no roofline meaning), one
-    tensor-parallel rank's width with the teacher detached (student gradient only),
-    and the robustness mix (fp32, four column-slice shards of widths 60000/0/40000/28256
-    merged on the device, masked columns and rows, offset rows) beside the same data
-    as one shard.  Bytes as the pages count them: 3 input passes over s and t plus
-    the gradient writes."""
-    def timed(fn):
-        fn()
-        fn()
-        tm = Timer(torch)
-        for _ in range(reps):
-            a = tm.mark()
-            fn()
-            tm.add("x", a, tm.mark())
-        torch.cuda.synchronize()
-        return tm.ms("x")
-
-    def run(b, widths, beta, student_only=False):
-        N, V = b.s.shape
-        S = 1 if widths is None else len(widths)
-        part = vj.new_part(N, S, "cuda")
-        stats = torch.empty((N, 4), dtype=torch.float64, device="cuda")
-        kl = torch.empty((N, 2), dtype=torch.float32, device="cuda")
-        loss = torch.empty((N,), dtype=torch.float32, device="cuda")
-        gs = torch.empty_like(b.s)
-        gt = None if student_only else torch.empty_like(b.t)
-        sh = vj.ShardSet(b.s, b.t, widths=widths)
-        shg = vj.ShardSet(b.s, b.t, widths=widths, gs=gs, gt=gt)
-        fwd = lambda: vj.vjsd_forward(sh, beta, part, stats, kl, loss)
-        bwd = lambda: vj.vjsd_bwd(shg, stats, kl, beta, b.gout, part)
-        f_ms = timed(fwd)
-        b_ms = timed(bwd)
-        step = timed(lambda: (fwd(), bwd()))
-        tb = N * V * b.s.element_size()
-        nbytes = 6 * tb + (1 if student_only else 2) * tb
-        return {"N": N, "V": V, "shards": S, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
-                "fwd_bwd_ms": round(step, 4), "tokens_per_s": round(N / (step * 1e-3), 1),
-                "bytes_alg": nbytes, "hbm_gbps": round(nbytes / (step * 1e-3) / 1e9, 1),
-                "hbm_frac": round(nbytes / (step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
-
+    """The other configurations of the path, each fwd+bwd through the C ABI with both
+    gradients unless stated: the tiny fp32 case (launch-latency bound, no roofline
+    meaning), one tensor-parallel rank's width with the teacher detached (student
+    gradient only), and the robustness mix (fp32, four column-slice shards of widths
+    60000/0/40000/28256 merged on the device, masked columns and rows, offset rows)
+    beside the same data as one shard."""
     rows = {}
     b = synth.draw("tiny", device="cuda")
-    r = run(b, None, 0.5)
+    w = Workload(torch, vj, synth, "full_vocab", batch=b)  # the full_vocab route, tiny data
+    w.name = "tiny_fp32"
+    r = workload_row(torch, w, reps)
     rows["tiny_fp32"] = {k: r[k] for k in ("N", "V", "fwd_ms", "bwd_ms", "fwd_bwd_ms",
                                            "tokens_per_s")}
-    b = synth.draw("tp8_shard", device="cuda")
-    rows["tp8_shard_teacher_detached"] = run(b, None, 0.5, student_only=True)
-    del b
-    torch.cuda.empty_cache()
-    w = synth.WORKLOADS["robust"]
-    b = synth.draw("robust", device="cuda")
-    rows["robust_fp32_4_shards"] = run(b, list(w.widths), 0.5)
-    rows["robust_fp32_1_shard"] = run(b, None, 0.5)
-    del b
-    torch.cuda.empty_cache()
+    for name in ("tp8_shard_teacher_detached", "robust_fp32_4_shards", "robust_fp32_1_shard"):
+        w = Workload(torch, vj, synth, name)
+        rows[name] = workload_row(torch, w, reps)
+        del w
+        torch.cuda.empty_cache()
     return rows
 
 
@@ -598,11 +676,17 @@ PAGES_JSD_RANKS = {
 
 
 def pages_shape_jsd(torch, vj, synth, reps=10):
-    """One tensor-parallel rank's share of the pages' JSD benchmark: the autograd jsd
-    op at N=1024 and V_local = 151936 / TP, beta 0.3, student gradient only."""
+    """One tensor-parallel rank's share of the pages' JSD benchmark: N=1024 and V_local =
+    151936 / TP, beta 0.3, student gradient only.  Through the C ABI with preallocated
+    buffers (kernel time, with the step's traffic), and through the autograd jsd op
+    (which adds the framework's allocations and launches: context for the pages'
+    op-level medians), with the op's peak device memory beyond the inputs."""
     rows = {}
     for V, ref in PAGES_JSD_RANKS.items():
-        b = synth.draw("full_vocab", device="cuda", N=1024, V=V)
+        w = Workload(torch, vj, synth, f"rank_share_{V}")
+        row = workload_row(torch, w, reps)
+        b = w.b
+        del w
         t = b.t.detach()
         x = b.s.detach().clone().requires_grad_()
 
@@ -622,9 +706,11 @@ def pages_shape_jsd(torch, vj, synth, reps=10):
             once()
             tm.add("x", a, tm.mark())
         torch.cuda.synchronize()
-        rows[f"V_local={V}"] = {"fwd_bwd_ms": round(tm.ms("x"), 4),
-                                "peak_gib_beyond_inputs": round(peak / 2**30, 3), "pages": ref}
+        row.update({"autograd_fwd_bwd_ms": round(tm.ms("x"), 4),
+                    "peak_gib_beyond_inputs": round(peak / 2**30, 3), "pages": ref})
+        rows[f"V_local={V}"] = row
         del x, b
+        torch.cuda.empty_cache()
     return rows
 
 
@@ -685,6 +771,7 @@ def sibling_rows(torch, vj, synth, reps=3):
             ms = tm.ms("x")
             res[f"{op}_{name}"] = {"fwd_bwd_ms": round(ms, 4),
                                    "tokens_per_s": round(N / (ms * 1e-3), 1),
+                                   "bytes_per_step": nbytes, "bytes_basis": "compulsory",
                                    "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
         del b, gs, sh, shg, sx, sxg, tk_lp, tk_ids, ce_lab
         torch.cuda.empty_cache()
