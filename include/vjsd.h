@@ -168,7 +168,7 @@ VJSD_API int vjsd_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, con
  *   beta = 0 or 1   the forward / reverse KL, in one input pass (as vkl_fwd)
  *   one shard       one launch, a workgroup per row: statistics, then divergence.
  *                   Rows 16-byte aligned, a multiple of 16 bytes and at most
- *                   32 KiB wide (16384 bf16 / fp16 or 8192 fp32 columns) are held
+ *                   80 KiB wide (40960 bf16 / fp16 or 20480 fp32 columns) are held
  *                   in registers and read from HBM once; wider rows are swept twice
  *   2 to 8 shards   one launch, a workgroup per row: each shard's slice is swept for
  *                   its (max, sum-exp) pairs, the pairs are merged in shard order as

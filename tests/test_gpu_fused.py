@@ -1,9 +1,9 @@
 """GPU parity of the whole-forward call (vjsd_forward): against the fp64 oracle and
 against the three separate launches, over dtypes, the beta = 0 / 1 branches (one-pass
-KL), row widths on both sides of the held-in-registers limit (16384 16-bit or 8192
-fp32 columns) and at each register-tile size below it, batch sizes, masks, offsets,
-unaligned rows (swept twice) and several shards (one launch up to eight, three
-launches beyond)."""
+KL), row widths at each register-tile size of the rows held in registers (256 lanes up
+to 16384 16-bit / 8192 fp32 columns, 512 lanes up to 40960 / 20480) and on both sides of
+each limit, batch sizes, masks, offsets, unaligned rows (swept twice) and several
+shards (one launch up to eight, three launches beyond)."""
 import numpy as np
 import pytest
 import torch
@@ -60,9 +60,9 @@ def check(s, t, beta, widths=None):
 
 
 # 1000 / 4096 / 8192 / 16032 / 16384: the row held in registers (1, 2, 4, 8 vectors
-# per lane); 16392 and wider: the row swept twice (135160 / 135168 / 135176 leave 511,
-# 512 and 513 vectors after the last whole step of 4 vectors per lane of the 512-lane
-# workgroup)
+# per lane of 256); 16392: 6 vectors per lane of 512; 135160 and wider: the row swept
+# twice (135160 / 135168 / 135176 leave 511, 512 and 513 vectors after the last whole
+# step of 4 vectors per lane of the 512-lane workgroup)
 @pytest.mark.parametrize("V", [1000, 4096, 8192, 16032, 16384, 16392, 135160, 135168, 135176,
                                151936])
 @pytest.mark.parametrize("beta", [0.5, 0.0, 1.0])
@@ -78,14 +78,65 @@ def test_one_pass_forward_other_dtypes(dtype, V):
     check(b.s, b.t, 0.3)
 
 
+# 512-lane workgroups holding 6, 8 or 10 vectors per lane of each input: the widths at
+# and one vector past each tile (16-bit: 24576 / 32768 / 40960 columns; fp32: 12288 /
+# 16384 / 20480), a ragged last tile, and one vector past the last (swept twice); the
+# one-rank shares of the pages' short batch (N=1024 rows at 37984 columns) sampled
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 16392), (torch.bfloat16, 24576),
+                                     (torch.bfloat16, 24584), (torch.bfloat16, 32768),
+                                     (torch.bfloat16, 32776), (torch.bfloat16, 37984),
+                                     (torch.bfloat16, 40960), (torch.bfloat16, 40968),
+                                     (torch.float16, 20000), (torch.float16, 40960),
+                                     (torch.float32, 8196), (torch.float32, 12288),
+                                     (torch.float32, 16388), (torch.float32, 20480),
+                                     (torch.float32, 20484)])
+def test_wide_register_rows(dtype, V):
+    b = synth.draw("full_vocab", device="cuda", N=21, V=V, dtype=dtype)
+    check(b.s, b.t, 0.5)
+    check(b.s, b.t, 0.1)
+
+
+def test_wide_register_rows_masks_and_undefined_rows():
+    b = synth.draw("robust", device="cuda", N=30, V=30000)  # fp32 -> bf16 below
+    s, t = b.s.to(torch.bfloat16), b.t.to(torch.bfloat16)
+    s[7] = NINF  # student undefined
+    t[8] = NINF  # teacher undefined
+    s[9, 50:] = NINF  # partly masked
+    s[10, :29997] = NINF  # mass only in the last three columns (the ragged last tile)
+    s[11, 123] = NINF  # forward KL of row 11 infinite
+    t[11, 123] = 1.0
+    loss = check(s, t, 0.5)
+    assert np.isnan(loss.numpy()[[7, 8]]).all()
+    lf = check(s, t, 0.0)
+    assert np.isinf(lf.numpy()[11])
+
+
+def test_wide_register_rows_pages_short_batch_sampled():
+    b = synth.draw("full_vocab", device="cuda", N=1024, V=37984)
+    for beta in (0.3, 0.9):
+        st, kl, loss = forward(b.s, b.t, beta)
+        rows = np.array([0, 1, 511, 512, 1022, 1023])
+        ref = oracle.jsd(b.s[rows].cpu(), b.t[rows].cpu(), beta, grads=False)
+        assert_values(loss[rows], ref["loss"], torch.bfloat16, "loss")
+        assert_values(kl[rows, 0], ref["kt"], torch.bfloat16, "KL(p_t||M)")
+        assert_values(kl[rows, 1], ref["ks"], torch.bfloat16, "KL(p_s||M)")
+        # each route sums a row's V terms in fp32 in its own order: rounding of order
+        # sqrt(V) * 2^-24 relative; four times that, plus the fp32 tolerance's absolute part
+        st3, kl3, loss3 = forward(b.s, b.t, beta, fused=False)
+        rtol = 4.0 * np.sqrt(b.s.shape[1]) * 2.0 ** -24
+        np.testing.assert_allclose(loss.numpy(), loss3.numpy(), rtol=rtol, atol=1e-6)
+        np.testing.assert_allclose(kl.numpy(), kl3.numpy(), rtol=rtol, atol=1e-6)
+
+
 @pytest.mark.parametrize("N", [1, 7, 100, 4097])
 def test_one_pass_forward_batch_sizes(N):
     b = synth.draw("full_vocab", device="cuda", N=N, V=16032)
     check(b.s, b.t, 0.9)
 
 
-# wide rows in batches larger than the number of CUs
-@pytest.mark.parametrize("N,V", [(700, 20000), (300, 140000)])
+# wide rows in batches larger than the number of CUs (41000: just past the rows held in
+# registers)
+@pytest.mark.parametrize("N,V", [(700, 41000), (300, 140000)])
 def test_swept_twice_forward_large_batches(N, V):
     b = synth.draw("full_vocab", device="cuda", N=N, V=V)
     check(b.s, b.t, 0.7)

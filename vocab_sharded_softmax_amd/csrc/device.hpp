@@ -40,9 +40,6 @@ constexpr int ROWC_UNDEFINED = 15;  // slot holding 1.0f for a row with no distr
 // Streaming gradient kernels: one wave per workgroup, each lane one 16-byte vector of
 // a row chunk, consecutive workgroups on consecutive chunks of a row.
 constexpr int GRAD_BLOCK = 64;
-// One-pass forward: 16-byte vectors per lane per input at most (a row of up to
-// 256 * FUSED_NVT_MAX vectors is held in one workgroup's registers).
-constexpr int FUSED_NVT_MAX = 8;
 
 // ---- storage formats -------------------------------------------------------------
 

@@ -5,9 +5,10 @@
 // before the nonlinear mixture, so statistics and divergence are two passes over the
 // input.  With a single shard one workgroup owns a whole row, so both passes can run
 // in one workgroup with nothing exchanged between workgroups:
-//   k_fwd_row    a row of both inputs fits the workgroup's registers (256 lanes x
-//                FUSED_NVT_MAX 16-byte vectors per input: up to 16384 bf16 / fp16 or
-//                8192 fp32 columns, 16-byte aligned rows): one HBM read per logit
+//   k_fwd_row    a row of both inputs fits the workgroup's registers (16-byte aligned
+//                rows; 256 lanes x up to 8 16-byte vectors per input, 16384 bf16 / fp16
+//                or 8192 fp32 columns, and 512 lanes x up to 10, 40960 / 20480 columns):
+//                one HBM read per logit
 //   k_fwd_twice  wider rows: the workgroup sweeps its row for the statistics, then
 //                sweeps it again for the divergence terms; the merge launch and two
 //                kernel boundaries go away, the second read stays
@@ -29,8 +30,16 @@ namespace vjsd {
 
 namespace {
 
+// Register-held rows: 256-lane workgroups with 1, 2, 4 or 8 vectors per lane, then
+// 512-lane workgroups with 6, 8 or 10 (ROW_WIDE_NVT_MAX).  At 16384 < V <= 40960 bf16 the
+// wider workgroup (124 VGPRs at 10 vectors, two workgroups per CU) beat the two sweeps
+// by 8-15 % on MI355X (1024 x 37984: 0.063 -> 0.056 ms; 1024 x 32000: 0.061 -> 0.052;
+// 8192 x 20000: 0.26 -> 0.24); 1024-lane workgroups spilled at 8 vectors and ran slower
+// at 5.  Keeping the statistics' exponentials for the divergence (238 VGPRs at 256 x 8,
+// one workgroup per SIMD pair) ran slower too: 0.170 against 0.148 ms at 8192 x 16032.
 constexpr int FB = 256;
-constexpr int FNW = FB / 64;
+constexpr int FB_WIDE = 512;
+constexpr int ROW_WIDE_NVT_MAX = 10;
 
 // raw 32-bit word of -inf in each storage format (two halves for 16-bit formats)
 template <class D>
@@ -48,9 +57,12 @@ __device__ __forceinline__ void opaque(u32x4 &v) {
     asm volatile("" : "+v"(v));
 }
 
-// Row maxima (a, b) and minima (na, nb) over the workgroup; red holds 4 * FNW floats.
+// Row maxima (a, b) and minima (na, nb) over the B-lane workgroup; red holds B / 16
+// floats.
+template <int B>
 __device__ __forceinline__ void block_minmax2(float &a, float &b, float &na, float &nb,
                                               float *red) {
+    constexpr int FNW = B / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     a = wave_max(a);
     b = wave_max(b);
@@ -78,7 +90,9 @@ __device__ __forceinline__ void block_minmax2(float &a, float &b, float &na, flo
     __syncthreads();
 }
 
+template <int B>
 __device__ __forceinline__ void block_sum2(float &a, float &b, float *red) {
+    constexpr int FNW = B / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     a = wave_sum(a);
     b = wave_sum(b);
@@ -140,7 +154,7 @@ __device__ __forceinline__ void finish_row(const RowK &k, double beta, float at,
 
 // Divergence terms of a row held in registers; slots past the row's end (they hold
 // -inf) are skipped.
-template <class D, int NVT, bool SAFE>
+template <class D, int NVT, int B, bool SAFE>
 __device__ __forceinline__ void regs_div(const u32x4 (&xs)[NVT], const u32x4 (&xt)[NVT],
                                          int64_t nv, const MixRow &mx, float beta, float ks,
                                          float &at, float &as) {
@@ -153,7 +167,7 @@ __device__ __forceinline__ void regs_div(const u32x4 (&xs)[NVT], const u32x4 (&x
     op.ksc = mx.ksc;
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
-        if (threadIdx.x + (int64_t)i * FB < nv) {
+        if (threadIdx.x + (int64_t)i * B < nv) {
             float a[VEC], b[VEC];
             widen<D>(xs[i], a);
             widen<D>(xt[i], b);
@@ -163,16 +177,16 @@ __device__ __forceinline__ void regs_div(const u32x4 (&xs)[NVT], const u32x4 (&x
     }
 }
 
-// One workgroup per row.  Lane l holds vectors l, l + FB, ... of each input; slots past
+// One B-lane workgroup per row.  Lane l holds vectors l, l + B, ... of each input; slots past
 // the row's end hold -inf, which adds exactly nothing to any sum below.
-template <class D, int NVT>
-__global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t w, double beta,
+template <class D, int NVT, int B>
+__global__ __launch_bounds__(B) void k_fwd_row(RowView sv, RowView tv, int64_t w, double beta,
                                                 double *__restrict__ stats,
                                                 float *__restrict__ kl,
                                                 float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
     constexpr int VEC = D::VEC;
-    __shared__ float red[4 * FNW];
+    __shared__ float red[4 * (B / 64)];
     const int64_t r = blockIdx.x;
     if (row_dropped(o, r)) {
         dropped_row(stats + r * 4, kl + 2 * r, loss + r);
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
     u32x4 xs[NVT], xt[NVT];
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
-        const int64_t j = threadIdx.x + (int64_t)i * FB;
+        const int64_t j = threadIdx.x + (int64_t)i * B;
         if (j < nv) {
             xs[i] = ld16<true>(s + j * VEC);
             xt[i] = ld16<true>(t + j * VEC);
@@ -210,11 +224,11 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
         }
         // a -inf filled slot past the row's end is left out of the minima (a select, not
         // a branch: a branch here keeps every widened value of the row alive)
-        const bool real = threadIdx.x + (int64_t)i * FB < nv;
+        const bool real = threadIdx.x + (int64_t)i * B < nv;
         ns = fminf(ns, real ? na : __builtin_huge_valf());
         nt = fminf(nt, real ? nb : __builtin_huge_valf());
     }
-    block_minmax2(ms, mt, ns, nt, red);
+    block_minmax2<B>(ms, mt, ns, nt, red);
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
         opaque(xs[i]);
@@ -242,7 +256,7 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
         zs += ea[0];
         zt += eb[0];
     }
-    block_sum2(zs, zt, red);
+    block_sum2<B>(zs, zt, red);
     __shared__ RowK rk;
     if (threadIdx.x < 64)
         row_constants(ms, zs, mt, zt, ns, nt, beta, o.ks, stats + r * 4, &rk);
@@ -256,10 +270,10 @@ __global__ __launch_bounds__(FB) void k_fwd_row(RowView sv, RowView tv, int64_t 
             opaque(xs[i]);
             opaque(xt[i]);
         }
-        if (k.fast) regs_div<D, NVT, false>(xs, xt, nv, k.mx, (float)beta, o.ks, pt, ps);
-        else regs_div<D, NVT, true>(xs, xt, nv, k.mx, (float)beta, o.ks, pt, ps);
+        if (k.fast) regs_div<D, NVT, B, false>(xs, xt, nv, k.mx, (float)beta, o.ks, pt, ps);
+        else regs_div<D, NVT, B, true>(xs, xt, nv, k.mx, (float)beta, o.ks, pt, ps);
     }
-    block_sum2(pt, ps, red);
+    block_sum2<B>(pt, ps, red);
     if (threadIdx.x == 0) finish_row(k, beta, pt, ps, kl + 2 * r, loss + r, o.lscale);
 }
 
@@ -593,10 +607,10 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
     if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], kl + 2 * r, loss + r, o.lscale);
 }
 
-template <class D, int NVT>
+template <class D, int NVT, int B>
 hipError_t row_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
                       float *loss, hipStream_t st, const RowOpts &o) {
-    hipLaunchKernelGGL((k_fwd_row<D, NVT>), dim3((unsigned)N), dim3(FB), 0, st, sh.s, sh.t,
+    hipLaunchKernelGGL((k_fwd_row<D, NVT, B>), dim3((unsigned)N), dim3(B), 0, st, sh.s, sh.t,
                        sh.width, beta, stats, kl, loss, o);
     return hipGetLastError();
 }
@@ -608,7 +622,7 @@ hipError_t fused_launch(const Shard &sh, int64_t N, double beta, double *stats, 
     constexpr int VEC = D::VEC;
     const int64_t w = sh.width;
     const int64_t nv = w / VEC;
-    bool regs = w > 0 && w % VEC == 0 && nv <= (int64_t)FB * FUSED_NVT_MAX;
+    bool regs = w > 0 && w % VEC == 0 && nv <= (int64_t)FB_WIDE * ROW_WIDE_NVT_MAX;
     const int esize = (int)sizeof(typename D::T);
     const RowView *views[2] = {&sh.s, &sh.t};
     for (const RowView *v : views) {  // every row must start on a 16-byte boundary
@@ -621,10 +635,13 @@ hipError_t fused_launch(const Shard &sh, int64_t N, double beta, double *stats, 
                            sh.t, w, beta, stats, kl, loss, o);
         return hipGetLastError();
     }
-    if (nv <= FB) return row_launch<D, 1>(sh, N, beta, stats, kl, loss, st, o);
-    if (nv <= 2 * FB) return row_launch<D, 2>(sh, N, beta, stats, kl, loss, st, o);
-    if (nv <= 4 * FB) return row_launch<D, 4>(sh, N, beta, stats, kl, loss, st, o);
-    return row_launch<D, FUSED_NVT_MAX>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= FB) return row_launch<D, 1, FB>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= 2 * FB) return row_launch<D, 2, FB>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= 4 * FB) return row_launch<D, 4, FB>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= 8 * FB) return row_launch<D, 8, FB>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= 6 * FB_WIDE) return row_launch<D, 6, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
+    if (nv <= 8 * FB_WIDE) return row_launch<D, 8, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
+    return row_launch<D, ROW_WIDE_NVT_MAX, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
 }
 
 }  // namespace
