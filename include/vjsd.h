@@ -282,7 +282,11 @@ VJSD_API int vjsd_bwd_noalloc(const vjsd_shard *shards, int S, int64_t N, int dt
 VJSD_API int vkl_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse, float *part,
             double *stats, float *kl, float *loss, void *stream);
 
-/* KL backward: vjsd_bwd at beta = 0 (reverse = 0) or beta = 1 (reverse != 0). */
+/*
+ * KL backward: vjsd_bwd at beta = 0 (reverse = 0) or beta = 1 (reverse != 0); closed
+ * form from the saved [N] statistics and the inputs, probabilities recomputed, and a
+ * row with no distribution gets exactly zero gradients [OPS-PR, How].
+ */
 VJSD_API int vkl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int reverse,
             const double *stats, const float *kl, const float *grad_loss, float *part,
             void *stream);
@@ -294,7 +298,11 @@ VJSD_API int vkl_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int 
 VJSD_API int ventropy_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype, float *part,
                  double *stats, float *ent, void *stream);
 
-/* Entropy backward: d/dx_j = -g p_j (lp_j + H), into each shard's gs view. */
+/*
+ * Entropy backward: d/dx_j = -g p_j (lp_j + H), into each shard's gs view; closed form
+ * from the saved statistics and ent, a -inf token and an undefined row get exactly
+ * zero [OPS-PR, How].
+ */
 VJSD_API int ventropy_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,
                  const float *ent, const float *grad, float *part, void *stream);
 
@@ -313,9 +321,10 @@ VJSD_API int vlogprobs_fwd(const vjsd_shard *shards, int S, int64_t N, int dtype
                   float *out, int32_t *dev_err, void *stream);
 
 /*
- * Log-probabilities backward: d/dx_j = sum_{k valid} g_k [j == ids_k]
- *   - (sum_{k valid} g_k) p_j, with g = grad[N][K]; repeated ids accumulate.  Writes
- * each shard's gs view.  Out-of-range ids are skipped (the forward reported them).
+ * Log-probabilities backward [OPS-PR, How: closed form, local, from the saved
+ * statistics]: d/dx_j = sum_{k valid} g_k [j == ids_k] - (sum_{k valid} g_k) p_j, with
+ * g = grad[N][K]; repeated ids accumulate.  Writes each shard's gs view.  Out-of-range
+ * ids are skipped (the forward reported them).
  */
 VJSD_API int vlogprobs_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t vocab_global,
                   const double *stats, const int64_t *ids, int K, int64_t ignore_index,

@@ -45,6 +45,18 @@ def build() -> str:
     return _LIB
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The same source under gcc's AddressSanitizer and UndefinedBehaviorSanitizer
+    (into out_dir/liboracle_san.so; load it with VJSD_ORACLE_LIB and gcc's libasan
+    preloaded).  Checks the checker's own memory and arithmetic safety."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "liboracle_san.so")
+    subprocess.run(["gcc", "-std=gnu11", "-O1", "-g", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                    "-Wextra", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                    "-fno-omit-frame-pointer", "-o", lib, _SRC, "-lm"], check=True)
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:

@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libvjsd.so")
+# VJSD_LIB points the loader at another build of the same sources (the host-sanitizer
+# build that the CPU tests load); by default the in-tree library.
+LIB_PATH = os.environ.get("VJSD_LIB") or os.path.join(_HERE, "libvjsd.so")
 
 VJSD_OK = 0
 ERRORS = {-1: "ERR_ARG", -2: "ERR_DTYPE", -3: "ERR_BETA", -4: "ERR_LAYOUT",

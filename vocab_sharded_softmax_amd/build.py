@@ -67,5 +67,50 @@ def build(jobs: int = 4) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C ABI's argument
+# checks (csrc/api.hip): each sanitizer flag applies to the host pass only, the device
+# code is compiled as usual.  Loaded with the clang ASan runtime preloaded (it carries
+# the UBSan handlers too).
+SAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+             "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_DIR = os.path.join(OBJ, "san")
+
+
+def build_host_sanitized() -> str:
+    """libvjsd with api.hip's host code under ASan + UBSan (the other objects as built
+    by build()); returns the library's path, _build/san/libvjsd_san.so."""
+    if not all(os.path.exists(os.path.join(OBJ, os.path.splitext(x)[0] + ".o")) for x in SOURCES):
+        build()
+    os.makedirs(SAN_DIR, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-O3"] + SAN_FLAGS
+    api_o = os.path.join(SAN_DIR, "api.o")
+    r = subprocess.run([hipcc(), *flags, "-c", os.path.join(CSRC, "api.hip"), "-o", api_o],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitized build of api.hip failed:\n" + r.stdout + r.stderr)
+    objs = [os.path.join(OBJ, os.path.splitext(x)[0] + ".o") for x in SOURCES if x != "api.hip"]
+    lib = os.path.join(SAN_DIR, "libvjsd_san.so")
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", lib, *objs,
+                        api_o], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link of libvjsd_san.so failed:\n" + r.stdout + r.stderr)
+    return lib
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime of the HIP toolchain (to preload for build_host_sanitized's
+    library)."""
+    import glob
+
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for pat in ("llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so",
+                "llvm/lib/clang/*/lib/x86_64-unknown-linux-gnu/libclang_rt.asan.so"):
+        hits = sorted(glob.glob(os.path.join(root, pat)))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("clang ASan runtime not found under " + root)
+
+
 if __name__ == "__main__":
     print(build())
