@@ -2,8 +2,8 @@
 against the same training run done densely by the fp64 oracle.
 
 [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel generalized JSD with
-Triton kernels", section Validation: three SGD updates of a sharded head match the
-dense reference at tensor-parallel degrees 1, 2 and 4 (a head-only training test).
+Triton kernels", section Validation: the pages check a head-only training run, a few
+SGD steps with the head split over 1, 2 and 4 ranks, against the same run unsplit.
 Here the ranks are S logical shards on one GPU: shard k owns rows [v_k, v_k+1) of
 the student head W, computes its own logit slice h W_k^T, and is paired with the
 teacher's logits over the same columns; the per-token JSD merges the shards on the

@@ -303,7 +303,7 @@ __global__ __launch_bounds__(LANES) void k_bwd(RowView sv, RowView tv, RowMView 
                                                     RowMView gtv, int64_t w, int64_t cw,
                                                     int64_t nchunk, const float *__restrict__ rowc,
                                                     int64_t items) {
-    const int64_t b = xcd_item(blockIdx.x);
+    const int64_t b = xcd_item(blockIdx.x, items);
     if (b >= items) return;
     const int64_t r = b / nchunk;
     bwd_chunk<D, MODE, WS, WT, DG, LANES>(row_ptr<typename D::T>(sv, r), tv, gsv, gtv, w, cw,
@@ -327,7 +327,7 @@ template <class D, int MODE, bool WS, bool WT, int LANES = bwd_lanes<WS, WT>()>
 __global__ __launch_bounds__(LANES) void k_bwd_shards(ShardGrads g, int64_t cw, int64_t nchunk,
                                                        const float *__restrict__ rowc,
                                                        int64_t items) {
-    const int64_t b = xcd_item(blockIdx.x);
+    const int64_t b = xcd_item(blockIdx.x, items);
     if (b >= items) return;
     const int64_t r = b / nchunk;
     const int64_t j = b - r * nchunk;
@@ -358,7 +358,7 @@ hipError_t bwd_k(const Shard &sh, int64_t N, const float *rowc, hipStream_t st) 
     constexpr int L = bwd_lanes<WS, WT>();
     const Chunks ch = grad_chunks<true, L>(N, sh.width, sizeof(typename D::T));
     if (ch.nchunk == 0) return hipSuccess;
-    hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)xcd_grid(N * ch.nchunk)),
+    hipLaunchKernelGGL((k_bwd<D, MODE, WS, WT>), dim3((unsigned)(N * ch.nchunk)),
                        dim3(L), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, ch.cw,
                        ch.nchunk, rowc, N * ch.nchunk);
     return hipGetLastError();
@@ -370,7 +370,7 @@ hipError_t bwd_g16(const Shard &sh, int64_t N, const float *rowc, hipStream_t st
     const Chunks ch = grad_chunks<true, L>(N, sh.width, sizeof(float));
     if (ch.nchunk == 0) return hipSuccess;
     hipLaunchKernelGGL((k_bwd<F32, MODE, true, false, BF16>),
-                       dim3((unsigned)xcd_grid(N * ch.nchunk)), dim3(L), 0, st, sh.s, sh.t, sh.gs,
+                       dim3((unsigned)(N * ch.nchunk)), dim3(L), 0, st, sh.s, sh.t, sh.gs,
                        sh.gt, sh.width, ch.cw, ch.nchunk, rowc, N * ch.nchunk);
     return hipGetLastError();
 }
@@ -400,7 +400,7 @@ hipError_t bwd_shards_k(const Shard *sh, int S, int64_t N, const float *rowc, hi
     for (;;) {  // the chunk width of grad_chunks, over all shards' chunks of a row
         total = 0;
         for (int k = 0; k < S; ++k) total += count(sh[k].width, cw);
-        if (N * total <= 0x7fffffffLL - 8 * XCD_RUN) break;
+        if (N * total <= 0x7fffffffLL) break;
         cw *= 2;
     }
     if (total == 0) return hipSuccess;
@@ -415,7 +415,7 @@ hipError_t bwd_shards_k(const Shard *sh, int S, int64_t N, const float *rowc, hi
         g.gs[k] = sh[k].gs;
         g.gt[k] = sh[k].gt;
     }
-    hipLaunchKernelGGL((k_bwd_shards<D, MODE, WS, WT>), dim3((unsigned)xcd_grid(N * total)),
+    hipLaunchKernelGGL((k_bwd_shards<D, MODE, WS, WT>), dim3((unsigned)(N * total)),
                        dim3(L), 0, st, g, cw, total, rowc, N * total);
     return hipGetLastError();
 }

@@ -60,15 +60,15 @@ struct Chunks {
 // XCD_RUN consecutive row chunks: on MI355X the both-gradient backward at 8192 x 151936
 // bf16 ran 1-2 % faster than with consecutive chunks on eight XCDs, the student-only
 // one 6 %, and at 16032 columns 3 % (runs of 32 chunks lost 5 % at full width; runs
-// of 1024 gained more there but lost 3 % at 16032 columns).  The grid is padded to
-// whole rounds of 8 * XCD_RUN; padding items exit at once.
+// of 1024 gained more there but lost 3 % at 16032 columns).  Only whole rounds of
+// 8 * XCD_RUN items are renumbered; the items of a last partial round keep their
+// order, so they spread over all eight XCDs (a small batch is all partial round).
 constexpr int64_t XCD_RUN = 256;
-inline int64_t xcd_grid(int64_t items) {
-    return (items + 8 * XCD_RUN - 1) / (8 * XCD_RUN) * (8 * XCD_RUN);
-}
-__device__ __forceinline__ int64_t xcd_item(int64_t i) {
-    const int64_t round = i / (8 * XCD_RUN), k = i - round * (8 * XCD_RUN);
-    return round * (8 * XCD_RUN) + (k & 7) * XCD_RUN + (k >> 3);
+__device__ __forceinline__ int64_t xcd_item(int64_t i, int64_t items) {
+    constexpr int64_t R = 8 * XCD_RUN;
+    if (i >= items / R * R) return i;
+    const int64_t round = i / R, k = i - round * R;
+    return round * R + (k & 7) * XCD_RUN + (k >> 3);
 }
 template <bool ALIGNED, int LANES = GRAD_BLOCK>
 inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
@@ -77,7 +77,7 @@ inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
     auto count = [w](int64_t c) {
         return w <= 0 ? (int64_t)0 : ALIGNED ? (w + 2 * c - 2) / c : (w + c - 1) / c;
     };
-    while (N * count(cw) > 0x7fffffffLL - 8 * XCD_RUN) cw *= 2;  // grid.x limit, padded
+    while (N * count(cw) > 0x7fffffffLL) cw *= 2;  // grid.x limit
     return {cw, count(cw)};
 }
 
