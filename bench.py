@@ -511,10 +511,11 @@ def main():
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
-def fused_linear_row(torch, vj, synth, reps=3, chunk=4096):
+def fused_linear_row(torch, vj, synth, reps=3, chunk=1024):
     """The fused-linear loss (hidden states and LM heads -> JSD loss, mean over tokens,
     gradients of the student's hidden states and head) on the linear workload: N=8192,
-    V=151936, Ds=Dt=3584 bf16, `chunk` tokens per logit block."""
+    V=151936, Ds=Dt=3584 bf16, `chunk` tokens per logit block (the library's default
+    plan), with its workspace against what the unfused route holds."""
     log("fused linear")
     b = synth.draw_linear("cuda")
     N, V, Ds = b.hs.shape[0], b.ws.shape[0], b.hs.shape[1]
@@ -546,7 +547,8 @@ def fused_linear_row(torch, vj, synth, reps=3, chunk=4096):
            "workspace_bytes": wsb,
            # what the unfused route holds at once: bf16 logits of both sides and the
            # student's logit gradient, [N, V] each
-           "materialized_logits_bytes": 3 * N * V * 2}
+           "unfused_bytes": 3 * N * V * 2,
+           "workspace_frac_of_unfused": round(wsb / (3 * N * V * 2), 4)}
     del ws, gh, gw, b
     torch.cuda.empty_cache()
     return res

@@ -450,19 +450,21 @@ typedef struct {
 /*
  * Fused-linear distillation loss: the loss of vjsd_loss_forward on the logits
  * h_s w_s^T (student) and h_t w_t^T (teacher), computed `chunk` tokens at a time, so
- * that only chunk-row blocks of logits ever exist (in the workspace, fp32).  opts as
+ * that only chunk-row blocks of logits ever exist (in the workspace, fp32); with more
+ * than one chunk, chunk is rounded down to a multiple of 8 (at least 8).  opts as
  * vjsd_loss_opts (temperature, T^2, token mask, reduction).  out is float[N] for
  * VJSD_REDUCE_NONE, else out[0] is the sum or the mean over the kept tokens.
  * grad_h (bf16 [N][dim_s], row stride ldgh) and grad_w (bf16 [V][dim_s], row stride
  * ldgw), each optional (NULL), receive d out[0] / d h_s and d out[0] / d w_s; they
  * need a reduction (VJSD_ERR_ARG otherwise).  The teacher is a constant.  The logit
- * gradient is rounded to bf16 (the operand precision of the products) and kept for
- * `group` tokens at a time (rounded up to whole chunks; 0: as many as fit 4 GiB),
- * whose two gradient products then run at once; with more than one group the head
- * gradient is summed across groups in fp32.  Masked tokens get exactly zero rows of
- * grad_h.  workspace: device memory of vljsd_workspace_bytes(N, V, dim_s, chunk,
- * group) bytes, 256-byte aligned.  VJSD_ERR_ARG for a bad size, chunk, group,
- * pointer, alignment or stride; VJSD_ERR_BETA as vjsd_fwd.
+ * gradient is rounded to bf16 (the operand precision of the products); each chunk's
+ * goes into its grad_h rows at once, and, transposed, it is kept for `group` tokens
+ * at a time (rounded up to whole chunks; 0: as many as fit 4 GiB) for the head
+ * gradient's product; with more than one group the head gradient is summed across
+ * groups in fp32.  Masked tokens get exactly zero rows of grad_h.  workspace: device
+ * memory of vljsd_workspace_bytes(N, V, dim_s, chunk, group) bytes, 256-byte aligned
+ * (for a fixed group it does not grow with N).  VJSD_ERR_ARG for a bad size, chunk,
+ * group, pointer, alignment or stride; VJSD_ERR_BETA as vjsd_fwd.
  */
 VJSD_API size_t vljsd_workspace_bytes(int64_t N, int64_t V, int64_t dim_s, int64_t chunk,
                                       int64_t group);

@@ -299,25 +299,38 @@ def test_linear_workspace_and_scale():
     assert w(16, 0, 8, 4, 0) == 0 and w(16, 10, 0, 4, 0) == 0 and w(16, 10, 8, 0, 0) == 0
     assert w(16, 10, 8, 4, -1) == 0
     al = lambda x: (x + 255) // 256 * 256
-    # two fp32 logit blocks of C rows (row stride V rounded up to 8), the bf16 logit
-    # gradient of a group (4 GiB worth of whole chunks by default), per-token losses,
-    # the block's statistics / KL pair / pass workspace, the count, and the fp32 head
-    # gradient accumulator only with more than one group
-    # (plus G and the group's hidden states transposed, token rows padded to 8)
+    # two fp32 logit blocks of C rows (row stride V rounded up to 8) and the chunk's bf16
+    # logit gradient; the group's logit gradient and hidden states transposed (token rows
+    # padded to 8; a group is 4 GiB worth of whole chunks by default); the student head
+    # transposed; the hidden-gradient product's fp32 partials when its K is split; the
+    # per-token losses, the chunk's statistics / KL pair / pass workspace, the count, and
+    # the fp32 head-gradient accumulator only with more than one group
     N, V, D, C = 8192, 151936, 3584, 4096
     ldl = V
-    # (and the student head transposed; 32 x 14 tiles fill the CUs, so the
-    # hidden-gradient product is not split and needs no partials)
-    expect = (2 * al(C * ldl * 4) + al(N * ldl * 2) + al(V * N * 2) + al(D * N * 2)
+    # (16 x 14 tiles of the hidden-gradient product: not split)
+    expect = (2 * al(C * ldl * 4) + al(C * ldl * 2) + al(V * N * 2) + al(D * N * 2)
               + al(D * V * 2) + al(N * 4)
               + al(C * 32) + al(C * 8) + al(lib.vjsd_workspace_bytes(C, 1)) + al(8))
     assert w(N, V, D, C, 0) == expect
-    # groups of 2 chunks of 100 over 300 tokens: two groups, so an accumulator
+    C = 1024  # 4 x 14 tiles: K split 4 ways
+    expect = (2 * al(C * ldl * 4) + al(C * ldl * 2) + al(V * N * 2) + al(D * N * 2)
+              + al(D * V * 2) + al(4 * C * D * 4) + al(N * 4)
+              + al(C * 32) + al(C * 8) + al(lib.vjsd_workspace_bytes(C, 1)) + al(8))
+    assert w(N, V, D, C, 0) == expect
+    # the default plan at that size holds less than the unfused route's bf16 logits of
+    # both sides and the student's logit gradient
+    assert w(N, V, D, 1024, 0) < 3 * N * V * 2
+    # with a fixed group the workspace does not grow with N past one group, but for the
+    # per-token losses (4 bytes a token)
+    assert (w(16384, V, D, 1024, 4096) - al(16384 * 4)
+            == w(65536, V, D, 1024, 4096) - al(65536 * 4))
+    # chunks of 100 over 300 tokens are taken 96 at a time (whole multiples of 8); groups
+    # of 150 tokens are 2 chunks, 192 tokens: two groups, so an accumulator
     ldl = 1008
     # (V = 1001 is no multiple of 64: no K split)
-    expect = (2 * al(100 * ldl * 4) + al(200 * ldl * 2) + al(1001 * 200 * 2) + al(16 * 200 * 2)
-              + al(16 * 1008 * 2) + al(300 * 4) + al(3200) + al(800)
-              + al(lib.vjsd_workspace_bytes(100, 1)) + al(8) + al(1001 * 16 * 4))
+    expect = (2 * al(96 * ldl * 4) + al(96 * ldl * 2) + al(1001 * 192 * 2) + al(16 * 192 * 2)
+              + al(16 * 1008 * 2) + al(300 * 4) + al(96 * 32) + al(96 * 8)
+              + al(lib.vjsd_workspace_bytes(96, 1)) + al(8) + al(1001 * 16 * 4))
     assert w(300, 1001, 16, 100, 150) == expect
     s = lib.vlin_scale
     assert s(FAKE, 10, 1, FAKE, None) == DTYPE

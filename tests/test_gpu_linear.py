@@ -157,10 +157,12 @@ def _check_linear(b, beta, T=1.0, t2=False, mask=None, red="mean", chunk=4096, g
 
 
 @pytest.mark.parametrize("chunk,group", [(10_000, 0), (128, 0), (100, 0), (64, 128), (100, 100),
-                                         (128, 1)])
+                                         (128, 1), (3, 0), (7, 20)])
 def test_linear_jsd_chunks_and_groups(chunk, group):
     # one block; several blocks in one group; three groups (the head gradient summed
-    # in fp32 across them: the store, accumulate and final convert epilogues)
+    # in fp32 across them: the store, accumulate and final convert epilogues); chunks
+    # below 8 tokens taken 8 at a time (each chunk's columns of the transposed logit
+    # gradient start 8 tokens apart), in one group and in thirteen
     b = synth.draw_linear("cuda", N=300, V=1000, Ds=72, Dt=56, seed=7)
     _check_linear(b, 0.5, chunk=chunk, group=group)
 
@@ -224,22 +226,22 @@ def test_linear_jsd_autograd():
 
 def test_linear_full_size_sampled():
     """The fused-linear workload at its full size (N=8192, V=151936, D=3584, chunk
-    4096, as the benchmark runs it): per-token losses of sampled rows, and the
+    1024, as the benchmark runs it): per-token losses of sampled rows, and the
     hidden-state gradient rows of those tokens, against the oracle on those rows."""
     v = vj()
     b = synth.draw_linear("cuda")
     N, V, D = b.hs.shape[0], b.ws.shape[0], b.hs.shape[1]
     st = v.lin_head(b.hs, b.ws, "student")
     te = v.lin_head(b.ht, b.wt, "teacher")
-    ws = torch.empty(v.vljsd_workspace_bytes(N, V, D, 4096, 0), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(v.vljsd_workspace_bytes(N, V, D, 1024, 0), dtype=torch.uint8, device="cuda")
     rows = torch.full((N,), float("nan"), device="cuda")
-    v.vljsd(st, te, N, V, 0.5, v.loss_opts(N, 1.0, False, None, "none"), 4096, ws, rows)
+    v.vljsd(st, te, N, V, 0.5, v.loss_opts(N, 1.0, False, None, "none"), 1024, ws, rows)
     out = torch.full((1,), float("nan"), device="cuda")
     gh = torch.full_like(b.hs, float("nan"))
-    v.vljsd(st, te, N, V, 0.5, v.loss_opts(N, 1.0, False, None, "sum"), 4096, ws, out, gh, None)
+    v.vljsd(st, te, N, V, 0.5, v.loss_opts(N, 1.0, False, None, "sum"), 1024, ws, out, gh, None)
     torch.cuda.synchronize()
     del ws
-    sample = np.array([0, 1, 4095, 4096, 5000, N - 1])
+    sample = np.array([0, 1, 1023, 1024, 4095, 4096, 5000, N - 1])
     hs_s, ht_s = b.hs[sample].cpu(), b.ht[sample].cpu()
     ref = oracle.linear_jsd(hs_s, b.ws.cpu(), ht_s, b.wt.cpu(), 0.5, reduction="sum", grad=1.0,
                             head_grad=False)

@@ -164,14 +164,20 @@ int lp_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, int64_t v
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace of vljsd.  Tokens go C = min(chunk, N) at a time through two fp32 logit
-// blocks (student, teacher; row stride ldl = V rounded up to 8); the bf16 logit
-// gradient G of a group of NG tokens (whole chunks: `group` rounded up, or with group 0
-// as many as fit LIN_G_BUDGET bytes, at least one) is kept for the two gradient
-// products of the group; then the
-// per-token losses, the block's statistics, KL pair and pass workspace, the kept-token
-// count, and the fp32 head-gradient accumulator when there is more than one group.
-// G and the group's hidden states are also kept transposed (for the head gradient).
+// Workspace of vljsd.  Tokens go C at a time (C = min(chunk, N); when that leaves more
+// than one chunk, rounded down to a multiple of 8, at least 8, so that each chunk's
+// columns of the transposed buffers below start 16 bytes apart) through two fp32 logit
+// blocks (student, teacher; row stride ldl = V rounded up to 8) and the chunk's bf16
+// logit gradient G, which feeds the chunk's hidden-gradient product at once.  For the
+// head gradient, G and the student hidden states of a group of NG tokens (whole chunks:
+// `group` rounded up, or with group 0 as many as fit LIN_G_BUDGET bytes, at least one
+// chunk) are kept transposed, tokens contiguous; the group's product then runs at once,
+// summed across groups in an fp32 accumulator when there is more than one.  Then the
+// per-token losses, the chunk's statistics, KL pair and pass workspace, the kept-token
+// count.  Measured on MI355X at N=8192, V=151936, D=3584 (fp32 logit blocks 8 C V bytes,
+// G 2 C V, the group's transposed G 2 NG V, the transposed head 2 D V): C = 4096 held
+// 11.1 GB when G was kept for the whole group; now C = 2048 with one group holds 6.8 GB,
+// against 7.5 GB for the bf16 logits and logit gradient of the unfused route.
 constexpr size_t LIN_G_BUDGET = (size_t)4 << 30;
 
 struct LinLayout {
@@ -183,23 +189,37 @@ struct LinLayout {
     bool has_gw = false;
 };
 
-// The hidden-gradient product of a group (gn x dim tiles of 256 x 256 over a K of V) may
-// have fewer tiles than the 256 CUs (a small group): then its K is split so that every
-// CU gets a work item, when V allows the direct-to-LDS kernel (V a multiple of 64).
-// With a round of tiles or more it is not split (measured: 448 tiles split three ways
-// ran 11 % slower than unsplit).
+// The hidden-gradient product of a chunk (c x dim tiles of 256 x 256 over a K of V) may
+// have fewer tiles than the 256 CUs: then its K is split, when V allows the
+// direct-to-LDS kernel (V a multiple of 64), into the number of parts s that minimises
+// the time, taken as (rounds of 256 work items) / s plus 2 % per extra part for the
+// fp32 partials' write and sum.  112 tiles (2048 tokens at D = 3584) split 2 ways: one
+// round at half the K, where 3 ways needed two rounds of a third each.  A round of
+// tiles or more is not split (measured: 448 tiles split three ways ran 11 % slower than
+// unsplit).
 int lin_splits(int64_t ng, int64_t V, int64_t dim) {
     if (V % 64 != 0 || ng <= 0) return 1;
     const int64_t tiles = ((ng + 255) / 256) * ((dim + 255) / 256);
     if (tiles >= 256) return 1;
-    int64_t s = (256 + tiles - 1) / tiles;
     const int64_t stages = V / 64;
-    while (s > 1 && stages / s < 8) --s;  // at least 8 stages of k per item
-    return (int)(s < 1 ? 1 : (s > 8 ? 8 : s));
+    int best = 1;
+    double best_t = 1.0;
+    for (int s = 2; s <= 8 && stages / s >= 8; ++s) {  // at least 8 stages of k per item
+        const double t = (double)((tiles * s + 255) / 256) / s + 0.02 * (s - 1);
+        if (t < best_t - 1e-12) {
+            best = s;
+            best_t = t;
+        }
+    }
+    return best;
 }
 LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk, int64_t group) {
     LinLayout L;
     L.C = chunk < N ? chunk : N;
+    if (L.C < N) {  // several chunks: whole multiples of 8 tokens
+        L.C = L.C >= 8 ? L.C / 8 * 8 : 8;
+        if (L.C > N) L.C = N;
+    }
     L.ldl = (V + 7) / 8 * 8;
     int64_t per = 1;  // chunks per group
     if (L.C > 0) {
@@ -218,7 +238,7 @@ LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk, int64_t g
     const size_t blk = (size_t)L.C * (size_t)L.ldl * sizeof(float);
     L.ls = take(blk);
     L.lt = take(blk);
-    L.g = take((size_t)L.NG * (size_t)L.ldl * 2);
+    L.g = take((size_t)L.C * (size_t)L.ldl * 2);
     // the group's G and student hidden states transposed (tokens contiguous), so that the
     // head-gradient product reads both operands k-major
     L.ldt = (L.NG + 7) / 8 * 8;
@@ -228,8 +248,8 @@ LinLayout lin_layout(int64_t N, int64_t V, int64_t dim, int64_t chunk, int64_t g
     // product, and that product's fp32 partials when its K is split
     L.ldv = (V + 7) / 8 * 8;
     L.wt = take((size_t)dim * (size_t)L.ldv * 2);
-    L.splits = lin_splits(L.NG, V, dim);
-    L.hp = take(L.splits > 1 ? (size_t)L.splits * (size_t)L.NG * (size_t)dim * 4 : 0);
+    L.splits = lin_splits(L.C, V, dim);
+    L.hp = take(L.splits > 1 ? (size_t)L.splits * (size_t)L.C * (size_t)dim * 4 : 0);
     L.rows = take((size_t)N * sizeof(float));
     L.stats = take((size_t)L.C * 4 * sizeof(double));
     L.kl = take((size_t)L.C * 2 * sizeof(float));
@@ -867,7 +887,7 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
             sh.width = V;
             sh.s = {ls, L.ldl, 0, 0};
             sh.t = {lt, L.ldl, 0, 0};
-            sh.gs = {G + (n0 - g0) * L.ldl, L.ldl, 0, 0};
+            sh.gs = {G, L.ldl, 0, 0};
             sh.gt = {nullptr, 0, 0, 0};
             vjsd::RowOpts rb = ro;
             rb.mask = ro.mask ? ro.mask + n0 : nullptr;
@@ -895,43 +915,46 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
                                                       go))))
                 return e;
             if ((e = hip_status(vjsd::launch_bwd_f32_to_bf16(mode, sh, nb, part, st)))) return e;
-        }
-        if (!grads) continue;
-        if (grad_h) {  // G [gn][V] x (w_s^T)^T: both operands k-major
-            vjsd::GemmArgs g;
-            g.M = gn;
-            g.N = D;
-            g.K = V;
-            g.a = G;
-            g.lda = L.ldl;
-            g.b = Wt;
-            g.ldb = L.ldv;
-            uint16_t *dst = static_cast<uint16_t *>(grad_h) + g0 * ldgh;
-            const int S = lin_splits(gn, V, D) < L.splits ? lin_splits(gn, V, D) : L.splits;
-            if (S > 1) {  // fp32 partials of the K split, then their sum in split order
-                g.ksplit = S;
-                g.split_stride = gn * D;
-                g.c = Hp;
-                g.ldc = D;
-                g.out = vjsd::GEMM_F32;
-                if ((e = hip_status(vjsd::launch_gemm(g, st))) ||
-                    (e = hip_status(vjsd::launch_sum_partials(Hp, S, gn * D, gn, D, D, dst, ldgh,
-                                                              st))))
+            if (grad_h) {  // G [nb][V] x (w_s^T)^T: both operands k-major
+                vjsd::GemmArgs g;
+                g.M = nb;
+                g.N = D;
+                g.K = V;
+                g.a = G;
+                g.lda = L.ldl;
+                g.b = Wt;
+                g.ldb = L.ldv;
+                uint16_t *dst = static_cast<uint16_t *>(grad_h) + n0 * ldgh;
+                const int S = lin_splits(nb, V, D) < L.splits ? lin_splits(nb, V, D) : L.splits;
+                if (S > 1) {  // fp32 partials of the K split, then their sum in split order
+                    g.ksplit = S;
+                    g.split_stride = nb * D;
+                    g.c = Hp;
+                    g.ldc = D;
+                    g.out = vjsd::GEMM_F32;
+                    if ((e = hip_status(vjsd::launch_gemm(g, st))) ||
+                        (e = hip_status(vjsd::launch_sum_partials(Hp, S, nb * D, nb, D, D, dst,
+                                                                  ldgh, st))))
+                        return e;
+                } else {
+                    g.c = dst;
+                    g.ldc = ldgh;
+                    g.out = vjsd::GEMM_BF16;
+                    if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
+                }
+            }
+            if (grad_w) {  // the chunk's G and hidden states into the group's transposes
+                const int64_t off = n0 - g0;  // a multiple of 8 (lin_layout)
+                if ((e = hip_status(vjsd::launch_transpose16(G, L.ldl, nb, V, Gt + off, L.ldt,
+                                                              st))) ||
+                    (e = hip_status(vjsd::launch_transpose16(hs + n0 * student->ldh,
+                                                              student->ldh, nb, D, Ht + off,
+                                                              L.ldt, st))))
                     return e;
-            } else {
-                g.c = dst;
-                g.ldc = ldgh;
-                g.out = vjsd::GEMM_BF16;
-                if ((e = hip_status(vjsd::launch_gemm(g, st)))) return e;
             }
         }
-        if (grad_w) {  // G^T [V][gn] x h_s [gn][D], summed over the groups in fp32
-            // both operands transposed first (tokens contiguous): the product then runs on
-            // k-major operands
-            if ((e = hip_status(vjsd::launch_transpose16(G, L.ldl, gn, V, Gt, L.ldt, st))) ||
-                (e = hip_status(vjsd::launch_transpose16(hs + g0 * student->ldh, student->ldh,
-                                                          gn, D, Ht, L.ldt, st))))
-                return e;
+        if (!grads || !grad_w) continue;
+        {  // G^T [V][gn] x h_s [gn][D], summed over the groups in fp32
             vjsd::GemmArgs g;
             g.M = V;
             g.N = D;
