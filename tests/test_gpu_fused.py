@@ -224,6 +224,32 @@ def test_sharded_forward(dtype, widths):
     assert np.isfinite(np.delete(loss.numpy(), [5, 6])).all()
 
 
+# fp32 rows in 2 to 8 shards hold the widest shard's last five full steps (four in
+# registers, one in LDS: 40960 columns) on chip through the merge: the widest shard with
+# exactly five full steps (an empty prefix) and one column short of them (no hold); the
+# widest shard first, in the middle (after shards that leave it 4 bytes past a 16-byte
+# boundary: a scalar head before its held steps) and last; two equally wide shards (the
+# first holds); masked tokens inside the held columns
+@pytest.mark.parametrize("widths", [[40960, 100], [40959, 100], [60000, 0, 40000, 28256],
+                                    [3000, 50001, 7], [40960, 40960],
+                                    [1, 2, 45000, 3, 0, 5, 6, 7]])
+def test_sharded_forward_held_steps(widths):
+    V = sum(widths)
+    b = synth.draw("robust", device="cuda", N=23, V=V)  # fp32
+    s, t = b.s.clone(), b.t.clone()
+    s[5] = NINF  # student undefined
+    t[6] = NINF  # teacher undefined
+    s[7, 100:] = NINF  # partly masked, across shard boundaries
+    q = int(np.argmax(widths))
+    end = sum(widths[:q + 1])
+    t[8, end - 9000:end - 8000] = NINF  # inside the widest shard's held columns
+    loss = check(s, t, 0.4, widths=widths)
+    assert np.isnan(loss.numpy()[[5, 6]]).all()
+    assert np.isfinite(np.delete(loss.numpy(), [5, 6])).all()
+    lf = check(s, t, 0.0, widths=widths)  # forward KL: teacher mass on row 7's masked tokens
+    assert np.isinf(lf.numpy()[7])
+
+
 def test_sharded_forward_separate_tensors():
     """Per-shard tensors with their own allocations and alignments (one shard's rows
     start 2 bytes past a 16-byte boundary), against the oracle on the concatenation."""

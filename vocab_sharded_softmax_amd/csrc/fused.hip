@@ -302,21 +302,6 @@ constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 4 : 1; }
 template <class D>
 constexpr int lds_steps() { return std::is_same<D, F16>::value ? 0 : 1; }
 
-// A held step's vectors through a sweep op, as the sweep would pass them.
-template <class D, class Op>
-__device__ __forceinline__ void run_held(const u32x4 (&hs)[TW_U], const u32x4 (&ht)[TW_U],
-                                         Op &op) {
-    float a[TW_U][D::VEC], b[TW_U][D::VEC];
-    int64_t c[TW_U];
-#pragma unroll
-    for (int u = 0; u < TW_U; ++u) {
-        widen<D>(hs[u], a[u]);
-        widen<D>(ht[u], b[u]);
-        c[u] = 0;  // the statistics and divergence ops take no column
-    }
-    op.template run<TW_U, D::VEC>(a, b, c);
-}
-
 // The streamed part of k_fwd_twice's divergence sweep, continuing the sums `acc`
 // (t, s) of the held steps.
 template <class D, bool SAFE>
@@ -504,27 +489,51 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
 }
 
 
+// Orders one wave's LDS writes before that wave's later LDS reads of other lanes'
+// values (wavefront-scope release, the wave's barrier, acquire).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Steps of the widest shard's slice that k_fwd_shards holds on chip, as k_fwd_twice
+// holds a row's: fp32 four in registers and one in LDS (232 VGPRs, one workgroup per
+// CU, as the fp32 two-sweep kernel), 16-bit formats none.  Measured on MI355X (4096 x
+// 128256 fp32 in shards 60000/0/40000/28256; 8192 x 151936 bf16 in 40000/40000/0/71936):
+// fp32 1.16 -> 1.03 ms with the held steps, the merge behind one barrier and the sweeps'
+// partial steps loaded at once (one shard: 1.00 ms); a bf16 LDS step ran 6 % slower
+// (1.37 -> 1.45 ms), and a register step in the 16-bit kernels, live across the loop
+// over shards, costs them their second workgroup per CU.
+template <class D>
+constexpr int shard_held_steps() { return sizeof(typename D::T) == 4 ? 4 : 0; }
+template <class D>
+constexpr int shard_lds_steps() { return sizeof(typename D::T) == 4 ? 1 : 0; }
+
 // Several logical shards of a row, one launch: the workgroup sweeps each shard's slice
 // for that shard's (max, sum-exp) pair of each input, merges the pairs in shard order
 // exactly as the merge launch does (maximum of the maxima, then the rescaled sums in
 // fp64; an empty shard adds nothing), then sweeps the slices again for the divergence
 // terms.  The pages' cross-rank reductions of [N] statistics become this in-workgroup
-// merge when all shards sit on one device [JSD-PR, Changes; OPS-PR, How].
-// The divergence sweep of k_fwd_shards over every non-empty shard's slice in order.
+// merge when all shards sit on one device [JSD-PR, Changes; OPS-PR, How].  Each wave's
+// pairs of every shard are combined after the last shard's sweep, behind one barrier;
+// in fp32 the widest shard's last full steps stay on chip for the divergence sweep.
+
+// The divergence sweep of k_fwd_shards over every non-empty shard's slice in order,
+// continuing the sums v of the held steps: the held shard qh's slice skips its held
+// columns [P, Q).
 template <class D, bool SAFE>
 __device__ __forceinline__ void shards_div(const ShardRows &sr, int64_t r, const MixRow &mx,
-                                           float beta, float ks, float (&v)[2]) {
+                                           float beta, float ks, int qh, bool hold, int64_t P,
+                                           int64_t Q, float (&v)[2]) {
     using T = typename D::T;
-    OpMix<SAFE> op;
-    op.set(mx, beta, ks);
     for (int q = 0; q < sr.S; ++q) {
         const int64_t w = sr.w[q];
         if (w == 0) continue;
         const T *s = row_ptr<T>(sr.s[q], r), *t = row_ptr<T>(sr.t[q], r);
-        sweep<D, 4, true, TWICE_BLK, true>(s, t, w, head_len<T>(w, s, t), op);
+        const int64_t h = head_len<T>(w, s, t);
+        twice_stream<D, SAFE>(mx, beta, ks, hold && q == qh, s, t, w, h, P, Q, v);
     }
-    v[0] = op.sum_t();
-    v[1] = op.sum_s();
 }
 
 template <class D>
@@ -533,42 +542,107 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
                                                           float *__restrict__ kl,
                                                           float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
+    constexpr int VEC = D::VEC;
     constexpr int NW = TWICE_BLK / 64;
+    constexpr int64_t STEP = (int64_t)TW_U * TWICE_BLK;  // vectors per input per sweep step
+    constexpr int HOLD = shard_held_steps<D>(), LHOLD = shard_lds_steps<D>();
     __shared__ float red[6 * NW];
     __shared__ float sp[FUSED_SHARDS][6];  // per shard: (m_s, z_s, m_t, z_t, min_s, min_t)
+    __shared__ float wp[FUSED_SHARDS][NW][6];  // the same per shard and wave
     const int64_t r = blockIdx.x;
     if (row_dropped(o, r)) {
         dropped_row(stats + r * 4, kl + 2 * r, loss + r);
         return;
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the widest shard (the first of equals) holds its statistics sweep's last full
+    // steps, [P, Q) of its slice ([P, PR) in LDS, [PR, Q) in registers), when it has
+    // that many
+    int qh = -1;
+    for (int q = 0; q < sr.S; ++q)
+        if (sr.w[q] > 0 && (qh < 0 || sr.w[q] > sr.w[qh])) qh = q;
+    bool hold = false;
+    int64_t P = 0, PR = 0, Q = 0;
+    if (qh >= 0 && HOLD + LHOLD > 0) {
+        const int64_t w = sr.w[qh];
+        const T *s = row_ptr<T>(sr.s[qh], r), *t = row_ptr<T>(sr.t[qh], r);
+        const int64_t h = head_len<T>(w, s, t);
+        const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
+        hold = nfull >= HOLD + LHOLD;
+        P = hold ? h + (nfull - HOLD - LHOLD) * STEP * VEC : w;
+        PR = P + LHOLD * STEP * VEC;
+        Q = hold ? PR + HOLD * STEP * VEC : w;
+    }
+    __shared__ u32x4 lds_step[2][TW_U][LHOLD ? TWICE_BLK : 1];  // each lane's own vectors
+    u32x4 hs[HOLD ? HOLD : 1][TW_U], ht[HOLD ? HOLD : 1][TW_U];
     for (int q = 0; q < sr.S; ++q) {
         OpStats<3, true> o1(o.ks);
         const int64_t w = sr.w[q];
         if (w > 0) {
             const T *s = row_ptr<T>(sr.s[q], r), *t = row_ptr<T>(sr.t[q], r);
-            sweep<D, 4, true, TWICE_BLK>(s, t, w, head_len<T>(w, s, t), o1);
+            const int64_t h = head_len<T>(w, s, t);
+            if (hold && q == qh) {
+                sweep<D, TW_U, true, TWICE_BLK>(s, t, P, h, o1);
+                if constexpr (LHOLD > 0) {
+                    u32x4 ls[TW_U], lt[TW_U];
+#pragma unroll
+                    for (int u = 0; u < TW_U; ++u) {
+                        const int64_t c = P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+                        ls[u] = ld16<true>(s + c);
+                        lt[u] = ld16<true>(t + c);
+                    }
+#pragma unroll
+                    for (int u = 0; u < TW_U; ++u) {
+                        lds_step[0][u][threadIdx.x] = ls[u];
+                        lds_step[1][u][threadIdx.x] = lt[u];
+                    }
+                    held_stats<D>(ls, lt, o1);
+                }
+#pragma unroll
+                for (int k = 0; k < HOLD; ++k) {
+#pragma unroll
+                    for (int u = 0; u < TW_U; ++u) {
+                        const int64_t c =
+                            PR + ((int64_t)k * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+                        hs[k][u] = ld16<true>(s + c);
+                        ht[k][u] = ld16<true>(t + c);
+                    }
+                    held_stats<D>(hs[k], ht[k], o1);
+                }
+                sweep<D, TW_U, true, TWICE_BLK>(s + Q, t + Q, w - Q, 0, o1);
+            } else {
+                sweep<D, TW_U, true, TWICE_BLK>(s, t, w, h, o1);
+            }
         }
+        // this wave's pair for the shard; the waves are combined after the last shard,
+        // behind one barrier for all shards
         const MZ ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
         const MZ wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
         const float ns = wave_min(o1.a.mn), nt = wave_min(o1.b.mn);
         if (lane == 0) {
-            red[2 * wave] = ws.m;
-            red[2 * wave + 1] = ws.z;
-            red[2 * NW + 2 * wave] = wt.m;
-            red[2 * NW + 2 * wave + 1] = wt.z;
-            red[4 * NW + 2 * wave] = ns;
-            red[4 * NW + 2 * wave + 1] = nt;
+            float *d = wp[q][wave];
+            d[0] = ws.m;
+            d[1] = ws.z;
+            d[2] = wt.m;
+            d[3] = wt.z;
+            d[4] = ns;
+            d[5] = nt;
         }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            MZ ms{red[0], red[1]}, mt{red[2 * NW], red[2 * NW + 1]};
-            float mns = red[4 * NW], mnt = red[4 * NW + 1];
+    }
+    __syncthreads();
+    __shared__ RowK rk;
+    if (wave == 0) {
+        // lane q combines shard q's wave pairs in wave order (as one shard's workgroup
+        // combines them), then the whole wave merges the shards
+        if (lane < sr.S) {
+            const int q = lane;
+            MZ ms{wp[q][0][0], wp[q][0][1]}, mt{wp[q][0][2], wp[q][0][3]};
+            float mns = wp[q][0][4], mnt = wp[q][0][5];
             for (int k = 1; k < NW; ++k) {
-                ms = mz_combine(ms, MZ{red[2 * k], red[2 * k + 1]}, o.ks);
-                mt = mz_combine(mt, MZ{red[2 * NW + 2 * k], red[2 * NW + 2 * k + 1]}, o.ks);
-                mns = fminf(mns, red[4 * NW + 2 * k]);
-                mnt = fminf(mnt, red[4 * NW + 2 * k + 1]);
+                ms = mz_combine(ms, MZ{wp[q][k][0], wp[q][k][1]}, o.ks);
+                mt = mz_combine(mt, MZ{wp[q][k][2], wp[q][k][3]}, o.ks);
+                mns = fminf(mns, wp[q][k][4]);
+                mnt = fminf(mnt, wp[q][k][5]);
             }
             sp[q][0] = ms.m;
             sp[q][1] = ms.z;
@@ -577,10 +651,8 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
             sp[q][4] = mns;
             sp[q][5] = mnt;
         }
-        __syncthreads();
-    }
-    __shared__ RowK rk;
-    if (wave == 0) {
+        // the lanes' LDS writes above come before the reads below
+        wave_lds_sync();
         float ms = NINF, mt = NINF, ns = __builtin_huge_valf(), nt = __builtin_huge_valf();
         for (int q = 0; q < sr.S; ++q) {
             ms = fmaxf(ms, sp[q][0]);
@@ -600,8 +672,26 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
     const RowK k = rk;
     float v[2] = {0.0f, 0.0f};
     if (!k.undefined) {
-        if (k.fast) shards_div<D, false>(sr, r, k.mx, (float)beta, o.ks, v);
-        else shards_div<D, true>(sr, r, k.mx, (float)beta, o.ks, v);
+        // the held steps first, in the form that admits masked tokens (as k_fwd_twice)
+        if (hold) {
+            OpMix<true> oh;
+            oh.set(k.mx, (float)beta, o.ks);
+#pragma unroll
+            for (int j = 0; j < HOLD; ++j) held_div<D>(hs[j], ht[j], oh);
+            if constexpr (LHOLD > 0) {
+                u32x4 ls[TW_U], lt[TW_U];
+#pragma unroll
+                for (int u = 0; u < TW_U; ++u) {
+                    ls[u] = lds_step[0][u][threadIdx.x];
+                    lt[u] = lds_step[1][u][threadIdx.x];
+                }
+                held_div<D>(ls, lt, oh);
+            }
+            v[0] = oh.sum_t();
+            v[1] = oh.sum_s();
+        }
+        if (k.fast) shards_div<D, false>(sr, r, k.mx, (float)beta, o.ks, qh, hold, P, Q, v);
+        else shards_div<D, true>(sr, r, k.mx, (float)beta, o.ks, qh, hold, P, Q, v);
     }
     block_sum<2, TWICE_BLK>(v, red);
     if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], kl + 2 * r, loss + r, o.lscale);

@@ -48,16 +48,47 @@ __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
         }
         op.template run<U, VEC>(a, b, c);
     }
-    for (; v < nv; v += BLOCK) {
-        float a[1][VEC], b[1][VEC];
-        const int64_t q = v * VEC;
-        const int64_t c[1] = {h + q};
-        load_vec<D, STREAM>(sb + q, a[0]);
-        if (TWO) load_vec<D, STREAM>(tb + q, b[0]);
-        else
+    if constexpr (U > 1) {
+        // the last partial step: a lane's (at most U - 1) vectors are loaded together,
+        // then run one by one in the same order (one memory round trip instead of up to
+        // U - 1: the several-shard fp32 forward at 4096 x 128256 in four shards, with a
+        // partial step per shard and sweep, 1.057 -> 1.034 ms)
+        u32x4 ra[U - 1], rb[U - 1];
+        bool ok[U - 1];
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) b[0][i] = 0.0f;
-        op.template run<1, VEC>(a, b, c);
+        for (int u = 0; u < U - 1; ++u) {
+            const int64_t vu = v + (int64_t)u * BLOCK;
+            ok[u] = vu < nv;
+            if (ok[u]) {
+                ra[u] = ld16<STREAM>(sb + vu * VEC);
+                if (TWO) rb[u] = ld16<STREAM>(tb + vu * VEC);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u) {
+            if (ok[u]) {
+                float a[1][VEC], b[1][VEC];
+                widen<D>(ra[u], a[0]);
+                if (TWO) widen<D>(rb[u], b[0]);
+                else
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) b[0][i] = 0.0f;
+                const int64_t c[1] = {h + (v + (int64_t)u * BLOCK) * VEC};
+                op.template run<1, VEC>(a, b, c);
+            }
+        }
+    } else {
+        for (; v < nv; v += BLOCK) {
+            float a[1][VEC], b[1][VEC];
+            const int64_t q = v * VEC;
+            const int64_t c[1] = {h + q};
+            load_vec<D, STREAM>(sb + q, a[0]);
+            if (TWO) load_vec<D, STREAM>(tb + q, b[0]);
+            else
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) b[0][i] = 0.0f;
+            op.template run<1, VEC>(a, b, c);
+        }
     }
     for (int64_t i = h + nv * VEC + tid; i < w; i += BLOCK) {
         float a[1][1], b[1][1] = {{0.0f}};
