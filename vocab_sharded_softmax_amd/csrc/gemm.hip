@@ -14,9 +14,11 @@
 // aligned, every leading dimension a multiple of 8 elements (4 for fp32), and every
 // operand readable over whole rows of ld elements (checked by the host).
 //
-// Tiling: a 256 x 256 output tile per workgroup of four waves (2 x 2, 128 x 128 each,
-// 4 x 4 MFMA tiles of 32 x 32, 256 fp32 accumulators per lane in AGPRs), k in steps
-// of 64 through double-buffered LDS (144 KiB: one workgroup per CU).  When an operand
+// Tiling: a 256 x 256 output tile per workgroup, k in steps of 64 through
+// double-buffered LDS (one workgroup per CU).  The general kernel (k_gemm) runs four
+// waves (2 x 2, 128 x 128 each, 4 x 4 MFMA tiles of 32 x 32, 256 fp32 accumulators per
+// lane in AGPRs; 144 KiB of LDS); the direct-to-LDS kernel (k_gemm_dl, below), which
+// every product of the loss runs on, eight (4 x 2, 64 x 128 each).  When an operand
 // has its rows contiguous (and both are bf16) the global loads run two k-steps ahead
 // (two register stages), so a load has two steps of products to arrive in.  Every operand is
 // stored k-major in LDS, rows padded to 144 bytes, so each MFMA fragment is one
@@ -234,8 +236,8 @@ __device__ __forceinline__ void tile_of(int64_t t, int64_t mt, int64_t nt, int a
 // together, then store that block: an add per element made each load wait behind the
 // store before it (an fp32 accumulate of a 151936 x 3584 head gradient over 2048 tokens
 // took 5.8 ms against 2.6 ms stored), and all 256 at once would not fit the registers.
-template <int OUT>
-__device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc)[WTM][WTN],
+template <int OUT, int TM = WTM, int TN = WTN>
+__device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc)[TM][TN],
                                            int64_t m0, int64_t n0, int wm, int wn, int lane) {
     const bool rows_in = m0 + BM <= g.M && n0 + BN <= g.N;
     const int64_t jl = n0 + wn + (lane & 31);
@@ -243,14 +245,14 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc
     const float *src = OUT == GEMM_F32_ACC ? static_cast<const float *>(g.c) : g.addend;
     const int64_t lds_ = OUT == GEMM_F32_ACC ? g.ldc : g.ldadd;
 #pragma unroll
-    for (int a = 0; a < WTM; ++a) {
-        float add[WTN][16];
+    for (int a = 0; a < TM; ++a) {
+        float add[TN][16];
         if constexpr (ACC) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t i = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 #pragma unroll
-                for (int b = 0; b < WTN; ++b) {
+                for (int b = 0; b < TN; ++b) {
                     const int64_t j = jl + 32 * b;
                     add[b][r] = (rows_in || (i < g.M && j < g.N)) ? src[i * lds_ + j] : 0.0f;
                 }
@@ -262,7 +264,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &g, const f32x16 (&acc
             if (!rows_in && i >= g.M) continue;
             const int64_t row = i * g.ldc;
 #pragma unroll
-            for (int b = 0; b < WTN; ++b) {
+            for (int b = 0; b < TN; ++b) {
                 const int64_t j = jl + 32 * b;
                 if (!rows_in && j >= g.N) continue;
                 const float v = acc[a][b][r];
@@ -412,6 +414,13 @@ void k_gemm(GemmArgs g) {
 // or sixteen lanes a cycle.  A row past the edge loads row M - 1 (N - 1): it feeds only
 // outputs that are not stored.
 constexpr int DBK = 64, DST = 2;
+// eight waves of 64 x 128 each (2 x 4 MFMA tiles, 128 accumulators), two per SIMD: one
+// wave's products run while the other waits on its fragment reads or loads.  Measured
+// on MI355X against four waves of 128 x 128: logits of 1024 tokens (1024 x 151936 x
+// 3584, fp32 out) 1.25 -> 1.10 ms, of 4096 tokens 4.75 -> 4.40 ms, the head gradient
+// over 8192 tokens 8.8-9.0 -> 8.0 ms; sixteen waves of 64 x 64 ran as eight; loading
+// through registers instead of straight into LDS ran as eight.
+constexpr int DL_WAVES = 8, DL_TM = 2, DL_TN = 4;
 constexpr int DSTAGE = 2 * 256 * DBK;  // bf16 elements of one stage (A rows, then B rows)
 
 __device__ __forceinline__ int dswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -433,9 +442,12 @@ __device__ __forceinline__ bf16x8 dfrag(const unsigned short *s, int base, int c
     return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int OUT>
-__global__ __launch_bounds__(GTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int OUT, int NWV, int TM, int TN>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void k_gemm_dl(GemmArgs g) {
+    static_assert((BM / (32 * TM)) * (BN / (32 * TN)) == NWV, "waves tile the workgroup tile");
+    constexpr int WGN = BN / (32 * TN);  // waves along N
+    constexpr int RPW = 256 / NWV;       // operand rows each wave loads per stage
     __shared__ __attribute__((aligned(1024))) unsigned short lds[DST][DSTAGE];
     const int64_t mt = (g.M + BM - 1) / BM, nt = (g.N + BN - 1) / BN, T = mt * nt;
     // work items: ksplit per tile, split-major (each split runs the whole tile order)
@@ -452,18 +464,18 @@ void k_gemm_dl(GemmArgs g) {
     const int64_t nk = nk_all - kb < nk_per ? (nk_all - kb > 0 ? nk_all - kb : 0) : nk_per;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = (wave >> 1) * (32 * WTM), wn = (wave & 1) * (32 * WTN);
-    f32x16 acc[WTM][WTN];
+    const int wm = (wave / WGN) * (32 * TM), wn = (wave % WGN) * (32 * TN);
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int a = 0; a < WTM; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < WTN; ++b)
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    // this wave loads rows [64 wave, + 64) of A and of B: eight instructions of 8 rows
-    // each; lane i of an instruction covers row + i / 8, slot i % 8
-    constexpr int NI = 8;  // load instructions per operand per wave and stage
+    // this wave loads rows [RPW wave, + RPW) of A and of B: instructions of 8 rows each;
+    // lane i of an instruction covers row + i / 8, slot i % 8
+    constexpr int NI = RPW / 8;  // load instructions per operand per wave and stage
     const int64_t rl = lane >> 3;
     const int cl = lane & 7;
     const uint16_t *pa = static_cast<const uint16_t *>(g.a);
@@ -474,11 +486,11 @@ void k_gemm_dl(GemmArgs g) {
         const int64_t k0 = (kb + s) * DBK;
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
-            const int r = 64 * wave + 8 * j + (int)rl;
+            const int r = RPW * wave + 8 * j + (int)rl;
             const int c = cl ^ dswz(r);
             const int64_t ra = m0 + r < g.M ? m0 + r : g.M - 1;
             const int64_t rb = n0 + r < g.N ? n0 + r : g.N - 1;
-            const int row0 = 64 * wave + 8 * j;
+            const int row0 = RPW * wave + 8 * j;
             __builtin_amdgcn_global_load_lds(pa + ra * g.lda + k0 + 8 * c,
                                              (lds_void *)(st + row0 * DBK), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(pb + rb * g.ldb + k0 + 8 * c,
@@ -490,19 +502,19 @@ void k_gemm_dl(GemmArgs g) {
     // fragments are read while F(i)'s products run; after F2, the wait and barrier for
     // the next stage, whose loads then go into the buffer this stage leaves, and whose
     // F0 is read while F3's products run.
-    bf16x8 fa[2][WTM], fb[2][WTN];
+    bf16x8 fa[2][TM], fb[2][TN];
     auto read = [&](int buf, int64_t s, int sub) {
         const unsigned short *la = lds[s % DST], *lb = la + 256 * DBK;
 #pragma unroll
-        for (int a = 0; a < WTM; ++a) fa[buf][a] = dfrag(la, wm + 32 * a, 2 * sub);
+        for (int a = 0; a < TM; ++a) fa[buf][a] = dfrag(la, wm + 32 * a, 2 * sub);
 #pragma unroll
-        for (int b = 0; b < WTN; ++b) fb[buf][b] = dfrag(lb, wn + 32 * b, 2 * sub);
+        for (int b = 0; b < TN; ++b) fb[buf][b] = dfrag(lb, wn + 32 * b, 2 * sub);
     };
     auto mma = [&](int buf) {
 #pragma unroll
-        for (int a = 0; a < WTM; ++a)
+        for (int a = 0; a < TM; ++a)
 #pragma unroll
-            for (int b = 0; b < WTN; ++b)
+            for (int b = 0; b < TN; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][a], fb[buf][b],
                                                                      acc[a][b], 0, 0, 0);
     };
@@ -550,10 +562,10 @@ void k_gemm_dl(GemmArgs g) {
     if (g.ksplit > 1) {  // this split's partial product, fp32
         GemmArgs gp = g;
         gp.c = static_cast<float *>(g.c) + split * g.split_stride;
-        store_tile<GEMM_F32>(gp, acc, m0, n0, wm, wn, lane);
+        store_tile<GEMM_F32, TM, TN>(gp, acc, m0, n0, wm, wn, lane);
         return;
     }
-    store_tile<OUT>(g, acc, m0, n0, wm, wn, lane);
+    store_tile<OUT, TM, TN>(g, acc, m0, n0, wm, wn, lane);
 }
 
 template <bool AF32, bool AKM, bool BKM>
@@ -593,18 +605,19 @@ hipError_t launch_gemm(const GemmArgs &gin, hipStream_t st) {
     if (!g.a_f32 && g.a_kmajor && g.b_kmajor && g.K > 0 && g.K % DBK == 0) {
         const int64_t T = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.ksplit;
         const dim3 grid((unsigned)(8 * ((T + 7) / 8)));
+        const dim3 block(64 * DL_WAVES);
         switch (g.out) {
             case GEMM_F32:
-                hipLaunchKernelGGL(k_gemm_dl<GEMM_F32>, grid, dim3(GTHREADS), 0, st, g);
+                hipLaunchKernelGGL((k_gemm_dl<GEMM_F32, DL_WAVES, DL_TM, DL_TN>), grid, block, 0, st, g);
                 break;
             case GEMM_F32_ACC:
-                hipLaunchKernelGGL(k_gemm_dl<GEMM_F32_ACC>, grid, dim3(GTHREADS), 0, st, g);
+                hipLaunchKernelGGL((k_gemm_dl<GEMM_F32_ACC, DL_WAVES, DL_TM, DL_TN>), grid, block, 0, st, g);
                 break;
             case GEMM_BF16:
-                hipLaunchKernelGGL(k_gemm_dl<GEMM_BF16>, grid, dim3(GTHREADS), 0, st, g);
+                hipLaunchKernelGGL((k_gemm_dl<GEMM_BF16, DL_WAVES, DL_TM, DL_TN>), grid, block, 0, st, g);
                 break;
             default:
-                hipLaunchKernelGGL(k_gemm_dl<GEMM_BF16_ACC>, grid, dim3(GTHREADS), 0, st, g);
+                hipLaunchKernelGGL((k_gemm_dl<GEMM_BF16_ACC, DL_WAVES, DL_TM, DL_TN>), grid, block, 0, st, g);
                 break;
         }
         return hipGetLastError();
