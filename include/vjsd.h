@@ -273,6 +273,41 @@ VJSD_API int vjsd_bwd_noalloc(const vjsd_shard *shards, int S, int64_t N, int dt
                               const float *grad_loss, void *stream);
 
 /*
+ * Forward and backward of the distillation loss in one call, for callers that know
+ * the upstream gradient before the forward (a per-token weight, or the reduction's
+ * scale of a loss that is itself the objective): the outputs of vjsd_loss_forward
+ * (stats, kl, rows, out) and the gradients of vjsd_loss_backward for `grad`, into
+ * each shard's gs / gt views, bit for bit [JSD-PR, Changes: the backward reuses the
+ * forward's global statistics and recomputes probabilities from the logits].  Same
+ * arguments as those two calls, same meaning and ownership; `part` as there.  How it
+ * runs:
+ *   one shard, 0 < beta < 1   one launch, a workgroup per row: the forward of
+ *                   vjsd_forward's single-shard route, then that row's gradients in
+ *                   the same workgroup.  A row held in registers is read from HBM
+ *                   once for both passes (its gradient views must start on 16-byte
+ *                   boundaries like the inputs', else the two calls run); a wider row
+ *                   reuses the sweep steps it holds on chip and reads the rest a
+ *                   third time.  With VJSD_REDUCE_MEAN a short launch counts the kept
+ *                   rows first.
+ *   otherwise       vjsd_loss_forward, then vjsd_loss_backward.
+ * Errors as vjsd_loss_forward and vjsd_loss_backward; on an error nothing is
+ * launched, except a VJSD_ERR_HIP from a launch.
+ */
+VJSD_API int vjsd_loss_forward_backward(const vjsd_shard *shards, int S, int64_t N, int dtype,
+                                        double beta, const vjsd_loss_opts *opts,
+                                        const float *grad, float *part, double *stats,
+                                        float *kl, float *rows, float *out, void *stream);
+
+/*
+ * vjsd_forward, then vjsd_bwd with the upstream gradient grad_loss[N], in one call:
+ * vjsd_loss_forward_backward with NULL opts (T = 1, no mask, per-token losses into
+ * `loss`).  Outputs equal those of the two calls bit for bit [JSD-PR, Changes].
+ */
+VJSD_API int vjsd_forward_backward(const vjsd_shard *shards, int S, int64_t N, int dtype,
+                                   double beta, const float *grad_loss, float *part,
+                                   double *stats, float *kl, float *loss, void *stream);
+
+/*
  * KL divergence [OPS-PR, What]: KL(p_t || p_s), or KL(p_s || p_t) when reverse != 0,
  * with the forward computed in a single input pass by online accumulation (as the
  * single-pass KL forward of [JSD-PR, Scope and limitations]).  Writes stats[N][4]

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_every_declared_entry_point_is_exported():
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     # and nothing else of the library's own code is exported
@@ -351,3 +351,40 @@ def test_noalloc_backward_checks_before_any_device_call():
     big = 65536 + 1
     assert lib.vjsd_bwd_noalloc(a, 1, big, 2, FAKE, FAKE, 0.5, FAKE, None) == SCRATCH
     assert b"65536" in lib.vjsd_strerror(SCRATCH)
+
+
+def fb(arr, S, N, dt=2, beta=0.5, grad=FAKE, part=FAKE, stats=FAKE, kl=FAKE, loss=FAKE):
+    return lib.vjsd_forward_backward(arr, S, N, dt, beta, grad, part, stats, kl, loss, None)
+
+
+def test_forward_backward_arguments_are_checked_before_any_launch():
+    a = shards([10], grads=True)
+    assert fb(a, 1, 0, grad=None, part=None, stats=None, kl=None, loss=None) == OK
+    for beta in (-0.1, 1.5, math.nan):
+        assert fb(a, 1, 4, beta=beta) == BETA
+    assert fb(a, 1, 4, dt=3) == DTYPE
+    for k in ("grad", "part", "stats", "kl", "loss"):
+        assert fb(a, 1, 4, **{k: None}) == ARG, k
+    bad = shards([10], grads=True)
+    bad[0].gs.p = bad[0].gs.p + 1  # a gradient view that is not element-aligned
+    assert fb(bad, 1, 4) == ARG
+    over = shards([10], grads=True)
+    over[0].gt.row_stride = 9  # overlapping gradient rows
+    assert fb(over, 1, 4) == ARG
+    lay = shards([4, 6], grads=True)
+    lay[1].vocab_start = 5
+    assert fb(lay, 2, 4) == LAYOUT
+
+
+def test_loss_forward_backward_options_are_checked():
+    a = shards([10], grads=True)
+    LossOpts = abi.LossOpts
+
+    def call(opts, out=FAKE, N=4):
+        return lib.vjsd_loss_forward_backward(a, 1, N, 2, 0.5, ctypes.byref(opts), FAKE, FAKE,
+                                              FAKE, FAKE, FAKE, out, None)
+    assert call(LossOpts(0.0, 0, None, 0)) == ARG  # temperature must be > 0
+    assert call(LossOpts(math.nan, 0, None, 0)) == ARG
+    assert call(LossOpts(1.0, 0, None, 3)) == ARG  # no such reduction
+    assert call(LossOpts(1.0, 0, None, 2), out=None) == ARG  # a reduction needs out
+    assert call(LossOpts(1.0, 0, None, 0), N=0, out=None) == OK

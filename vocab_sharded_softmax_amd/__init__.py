@@ -6,7 +6,7 @@ The compute path is libvjsd.so (hand-written HIP kernels for gfx950, C ABI in
 library has not been built.
 """
 from ._abi import (ShardSet, VjsdArgumentError, VjsdError, loss_opts, new_part, vjsd_bwd,
-                   vjsd_bwd_noalloc,
+                   vjsd_bwd_noalloc, vjsd_forward_backward, vjsd_loss_forward_backward,
                    vjsd_forward, vjsd_fwd, vjsd_loss_backward, vjsd_loss_forward,
                    vjsd_membw_probe, vjsd_merge, vjsd_stats, vjsd_strerror, vjsd_workspace_bytes,
                    ventropy_bwd, ventropy_fwd, vkl_bwd, vkl_fwd, vlogprobs_bwd, vlogprobs_fwd,
@@ -24,5 +24,6 @@ __all__ = [
     "vkl_fwd", "vkl_bwd", "ventropy_fwd",
     "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd", "vjsd_strerror", "vjsd_workspace_bytes",
     "vjsd_membw_probe", "vjsd_loss_forward", "vjsd_loss_backward", "loss_opts", "new_part",
+    "vjsd_forward_backward", "vjsd_loss_forward_backward",
     "LIB_PATH",
 ]

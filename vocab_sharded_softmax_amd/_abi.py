@@ -94,6 +94,9 @@ def _load():
         "vjsd_membw_probe": ([P, P, ctypes.c_size_t, I, P], I),
         "vjsd_loss_forward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P, P], I),
         "vjsd_loss_backward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P, P], I),
+        "vjsd_forward_backward": ([SP, I, I64, I, D, P, P, P, P, P, P], I),
+        "vjsd_loss_forward_backward": ([SP, I, I64, I, D, ctypes.POINTER(LossOpts), P, P, P, P,
+                                        P, P, P], I),
         "vlin_gemm": ([I64, I64, I64, LinOperand, LinOperand, P, I64, I, P], I),
         "vljsd_workspace_bytes": ([I64, I64, I64, I64, I64], ctypes.c_size_t),
         "vljsd": ([ctypes.POINTER(LinHead), ctypes.POINTER(LinHead), I64, I64, D,
@@ -326,6 +329,30 @@ def vjsd_loss_backward(sh: ShardSet, beta: float, opts: LossOpts, stats, kl, gra
                                   _ptr(grad, torch.float32, ng, "grad"),
                                   _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
                                   _stream(stream)))
+
+
+def vjsd_forward_backward(sh: ShardSet, beta: float, grad_loss, part, stats, kl, loss,
+                          stream=None) -> None:
+    N = sh.N
+    _check(lib.vjsd_forward_backward(sh.arr, sh.S, N, sh.dtype_code, float(beta),
+                                     _ptr(grad_loss, torch.float32, N, "grad_loss"),
+                                     _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                                     _ptr(stats, torch.float64, N * 4, "stats"),
+                                     _ptr(kl, torch.float32, N * 2, "kl"),
+                                     _ptr(loss, torch.float32, N, "loss"), _stream(stream)))
+
+
+def vjsd_loss_forward_backward(sh: ShardSet, beta: float, opts: LossOpts, grad, part, stats, kl,
+                               rows, out=None, stream=None) -> None:
+    N = sh.N
+    ng = N if opts.reduction == 0 else 1
+    _check(lib.vjsd_loss_forward_backward(sh.arr, sh.S, N, sh.dtype_code, float(beta),
+                                          ctypes.byref(opts), _ptr(grad, torch.float32, ng, "grad"),
+                                          _ptr(part, torch.float32, part_floats(N, sh.S), "part"),
+                                          _ptr(stats, torch.float64, N * 4, "stats"),
+                                          _ptr(kl, torch.float32, N * 2, "kl"),
+                                          _ptr(rows, torch.float32, N, "rows"),
+                                          _ptr(out, torch.float32, 1, "out"), _stream(stream)))
 
 
 def vkl_fwd(sh: ShardSet, reverse: bool, part, stats, kl, loss, stream=None) -> None:

@@ -124,6 +124,16 @@ vjsd::RowOpts row_opts(const LossCfg &c) {
     return o;
 }
 
+// The backward's upstream-gradient options for the loss form c.
+vjsd::GradOpts grad_opts(const LossCfg &c) {
+    vjsd::GradOpts go;
+    go.ks = row_opts(c).ks;
+    go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
+    go.scalar = c.red != VJSD_REDUCE_NONE;
+    go.mask = c.mask;
+    return go;
+}
+
 int mode_of(double beta) {
     return beta == 0.0 ? vjsd::FWD_KL : (beta == 1.0 ? vjsd::REV_KL : vjsd::INTERIOR);
 }
@@ -504,11 +514,7 @@ int vjsd_loss_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, do
     if (!stats || !kl || !grad || !part) return VJSD_ERR_ARG;
     const int mode = mode_of(beta);
     hipStream_t st = (hipStream_t)stream;
-    vjsd::GradOpts go;
-    go.ks = row_opts(c).ks;
-    go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
-    go.scalar = c.red != VJSD_REDUCE_NONE;
-    go.mask = c.mask;
+    vjsd::GradOpts go = grad_opts(c);
     if (c.red == VJSD_REDUCE_MEAN) {
         double *cnt = count_of(part, S, N);
         if ((e = hip_status(
@@ -519,6 +525,54 @@ int vjsd_loss_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, do
     if ((e = hip_status(vjsd::launch_bwd_prep(mode, N, stats, kl, beta, grad, part, st, go))))
         return e;
     return bwd_all(shards, S, N, dtype, mode, part, st);
+}
+
+int vjsd_loss_forward_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
+                               const vjsd_loss_opts *opts, const float *grad, float *part,
+                               double *stats, float *kl, float *rows, float *out, void *stream) {
+    int e = check_common(shards, S, N, dtype);
+    if (e) return e;
+    if (!(beta >= 0.0 && beta <= 1.0)) return VJSD_ERR_BETA;
+    LossCfg c;
+    if ((e = loss_cfg(opts, &c))) return e;
+    if ((e = check_views(shards, S, N, dtype, true, true))) return e;
+    if (c.red != VJSD_REDUCE_NONE && !out) return VJSD_ERR_ARG;
+    if (N == 0)  // nothing to differentiate; a reduction's out is still written
+        return vjsd_loss_forward(shards, S, N, dtype, beta, opts, part, stats, kl, rows, out,
+                                 stream);
+    if (!part || !stats || !kl || !rows || !grad) return VJSD_ERR_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    if (S == 1 && mode_of(beta) == vjsd::INTERIOR) {
+        const vjsd::RowOpts ro = row_opts(c);
+        vjsd::GradOpts go = grad_opts(c);
+        if (c.red == VJSD_REDUCE_MEAN) {  // the kept-row count, before any gradient
+            double *cnt = count_of(part, S, N);
+            if ((e = hip_status(vjsd::launch_reduce_rows(nullptr, ro, N, false, nullptr, cnt, st))))
+                return e;
+            go.count = cnt;
+        }
+        const Shard sh = convert(shards[0], true, true);
+        const hipError_t he =
+            vjsd::launch_fwd_bwd_fused(dtype, sh, N, beta, grad, stats, kl, rows, st, ro, go);
+        if (he == hipSuccess) {
+            if (c.red == VJSD_REDUCE_NONE) return VJSD_OK;
+            return hip_status(vjsd::launch_reduce_rows(rows, ro, N, c.red == VJSD_REDUCE_MEAN,
+                                                       out, nullptr, st));
+        }
+        if (he != hipErrorNotSupported) return VJSD_ERR_HIP;
+    }
+    // every other case: the two entry points, which compute the same outputs
+    if ((e = vjsd_loss_forward(shards, S, N, dtype, beta, opts, part, stats, kl, rows, out,
+                               stream)))
+        return e;
+    return vjsd_loss_backward(shards, S, N, dtype, beta, opts, stats, kl, grad, part, stream);
+}
+
+int vjsd_forward_backward(const vjsd_shard *shards, int S, int64_t N, int dtype, double beta,
+                          const float *grad_loss, float *part, double *stats, float *kl,
+                          float *loss, void *stream) {
+    return vjsd_loss_forward_backward(shards, S, N, dtype, beta, nullptr, grad_loss, part, stats,
+                                      kl, loss, nullptr, stream);
 }
 
 int vjsd_bwd(const vjsd_shard *shards, int S, int64_t N, int dtype, const double *stats,

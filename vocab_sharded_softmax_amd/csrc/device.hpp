@@ -274,6 +274,18 @@ __device__ __forceinline__ bool row_dropped(const RowOpts &o, int64_t r) {
            (o.labels != nullptr && o.labels[r] == o.ignore);
 }
 
+// Upstream-gradient options of the distillation-loss form of the backward: the row
+// r's gradient scale is g_r * gmul, g_r = grad[r] (per-row) or grad[0] (reduced;
+// divided by max(*count, 1) for a mean), and 0 for a row the mask drops.  A NULL
+// grad stands for a unit upstream gradient.
+struct GradOpts {
+    float ks = L2E;                  // log2 e / temperature
+    double gmul = 1.0;               // T^2 (if scaled) * (1/T): chain rule through x / T
+    bool scalar = false;             // grad is one value for all rows
+    const uint8_t *mask = nullptr;   // [N]; zero drops the row
+    const double *count = nullptr;   // device: kept rows, for a mean (null: no division)
+};
+
 // ---- wave reductions (fixed order: deterministic results) ---------------------------
 //
 // A butterfly over the 64 lanes of a wave that never touches LDS.  The first four

@@ -1,4 +1,5 @@
-// fused.hip -- the interior JSD forward in one launch.
+// fused.hip -- the interior JSD forward in one launch, and the forward and backward in
+// one launch.
 //
 // [JSD-PR] DeepSpeed PR #8958 "[VocabTP] Add vocabulary-parallel generalized JSD with
 // Triton kernels", section Scope and limitations: the JSD needs the global normaliser
@@ -14,6 +15,8 @@
 //                kernel boundaries go away, the second read stays
 //   k_fwd_shards the same for a row split into up to FUSED_SHARDS logical shards:
 //                per-shard statistics merged in the workgroup, then the divergence
+//   k_fwdbwd_row / k_fwdbwd_twice   k_fwd_row / k_fwd_twice, then the row's gradients
+//                in the same workgroup (below)
 // The divergence terms are those of MixTerm (divergence.hpp).  The statistics sweep
 // also finds each side's smallest logit: a row whose logits all lie within FAST_RANGE
 // of its maximum (no masked token, no underflow) takes the divergence without the
@@ -21,6 +24,7 @@
 // workgroups would need a device-wide exchange per row; on MI355X the cache write-back
 // and invalidation that a correct device-scope release/acquire costs exceeds the
 // second read it would save.
+#include "backward.hpp"
 #include "kernels.hpp"
 #include "sweep.hpp"
 
@@ -177,24 +181,17 @@ __device__ __forceinline__ void regs_div(const u32x4 (&xs)[NVT], const u32x4 (&x
     }
 }
 
-// One B-lane workgroup per row.  Lane l holds vectors l, l + B, ... of each input; slots past
-// the row's end hold -inf, which adds exactly nothing to any sum below.
+// The forward of one row held in registers by a B-lane workgroup: the body of k_fwd_row
+// and k_fwdbwd_row.  Lane l loads vectors l, l + B, ... of each input into xs / xt;
+// slots past the row's end hold -inf, which adds exactly nothing to any sum below.
+// Thread 0 writes the row's statistics (st), KL pair (klr) and loss; the row stays in
+// xs / xt.  nv: the row's 16-byte vectors (the host requires whole vectors).
 template <class D, int NVT, int B>
-__global__ __launch_bounds__(B) void k_fwd_row(RowView sv, RowView tv, int64_t w, double beta,
-                                                double *__restrict__ stats,
-                                                float *__restrict__ kl,
-                                                float *__restrict__ loss, RowOpts o) {
-    using T = typename D::T;
+__device__ __forceinline__ void row_forward(const typename D::T *s, const typename D::T *t,
+                                            int64_t nv, double beta, double *st, float *klr,
+                                            float *lossr, const RowOpts &o, float *red,
+                                            RowK &rk, u32x4 (&xs)[NVT], u32x4 (&xt)[NVT]) {
     constexpr int VEC = D::VEC;
-    __shared__ float red[4 * (B / 64)];
-    const int64_t r = blockIdx.x;
-    if (row_dropped(o, r)) {
-        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
-        return;
-    }
-    const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
-    const int64_t nv = w / VEC;  // whole vectors: the host requires w % VEC == 0
-    u32x4 xs[NVT], xt[NVT];
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
         const int64_t j = threadIdx.x + (int64_t)i * B;
@@ -257,9 +254,7 @@ __global__ __launch_bounds__(B) void k_fwd_row(RowView sv, RowView tv, int64_t w
         zt += eb[0];
     }
     block_sum2<B>(zs, zt, red);
-    __shared__ RowK rk;
-    if (threadIdx.x < 64)
-        row_constants(ms, zs, mt, zt, ns, nt, beta, o.ks, stats + r * 4, &rk);
+    if (threadIdx.x < 64) row_constants(ms, zs, mt, zt, ns, nt, beta, o.ks, st, &rk);
     __syncthreads();
     const RowK k = rk;
     // ---- divergence: terms from registers
@@ -274,7 +269,27 @@ __global__ __launch_bounds__(B) void k_fwd_row(RowView sv, RowView tv, int64_t w
         else regs_div<D, NVT, B, true>(xs, xt, nv, k.mx, (float)beta, o.ks, pt, ps);
     }
     block_sum2<B>(pt, ps, red);
-    if (threadIdx.x == 0) finish_row(k, beta, pt, ps, kl + 2 * r, loss + r, o.lscale);
+    if (threadIdx.x == 0) finish_row(k, beta, pt, ps, klr, lossr, o.lscale);
+}
+
+
+// One B-lane workgroup per row.
+template <class D, int NVT, int B>
+__global__ __launch_bounds__(B) void k_fwd_row(RowView sv, RowView tv, int64_t w, double beta,
+                                                double *__restrict__ stats,
+                                                float *__restrict__ kl,
+                                                float *__restrict__ loss, RowOpts o) {
+    using T = typename D::T;
+    __shared__ float red[4 * (B / 64)];
+    __shared__ RowK rk;
+    const int64_t r = blockIdx.x;
+    if (row_dropped(o, r)) {
+        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
+        return;
+    }
+    u32x4 xs[NVT], xt[NVT];
+    row_forward<D, NVT, B>(row_ptr<T>(sv, r), row_ptr<T>(tv, r), w / D::VEC, beta, stats + r * 4,
+                           kl + 2 * r, loss + r, o, red, rk, xs, xt);
 }
 
 // One workgroup per row, any alignment: statistics sweep, then divergence sweep.
@@ -361,39 +376,57 @@ __device__ __forceinline__ void held_div(const u32x4 (&hs)[TW_U], const u32x4 (&
     }
 }
 
+// The part of a row that the statistics sweep of k_fwd_twice keeps on chip: the last
+// HOLD + LHOLD full sweep steps of the row's 16-byte body, elements [P, Q) ([P, PR) in
+// LDS, [PR, Q) in registers).  Rows whose two inputs sit at different offsets inside 16
+// bytes (h == w), or that are too short, hold nothing and are swept whole.
+struct TwiceSpan {
+    int64_t h, P, PR, Q;
+    bool hold;
+};
 template <class D>
-__global__ __launch_bounds__(TWICE_BLK)
-void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restrict__ stats,
-                 float *__restrict__ kl, float *__restrict__ loss, RowOpts o) {
-    using T = typename D::T;
+__device__ __forceinline__ TwiceSpan twice_span(int64_t w, int64_t h) {
     constexpr int VEC = D::VEC;
     constexpr int64_t STEP = (int64_t)TW_U * TWICE_BLK;  // vectors per input per sweep step
-    __shared__ float red[6 * (TWICE_BLK / 64)];
-    const int64_t r = blockIdx.x;
-    if (row_dropped(o, r)) {
-        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
-        return;
-    }
-    const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
-    const int64_t h = head_len<T>(w, s, t);
+    constexpr int HOLD = held_steps<D>(), LHOLD = lds_steps<D>();
+    TwiceSpan sp;
+    sp.h = h;
+    const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
+    sp.hold = nfull >= HOLD + LHOLD;
+    sp.P = sp.hold ? h + (nfull - HOLD - LHOLD) * STEP * VEC : w;
+    sp.PR = sp.P + LHOLD * STEP * VEC;
+    sp.Q = sp.hold ? sp.PR + HOLD * STEP * VEC : w;
+    return sp;
+}
+// The held steps: LDS (each lane's own vectors) and registers.
+template <class D>
+using LdsStep = u32x4[2][TW_U][lds_steps<D>() ? TWICE_BLK : 1];
+template <class D>
+using HeldRegs = u32x4[held_steps<D>()][TW_U];
+
+// The forward of one row by a TWICE_BLK-lane workgroup, the body of k_fwd_twice and
+// k_fwdbwd_twice: the statistics sweep, keeping the span sp on chip, the row's
+// constants (into rk), then the divergence sweep.  Thread 0 writes the row's
+// statistics (st), KL pair (klr) and loss; the held steps stay in lds_step / hs / ht.
+template <class D>
+__device__ __forceinline__ void twice_forward(const typename D::T *s, const typename D::T *t,
+                                              int64_t w, const TwiceSpan &sp, double beta,
+                                              double *st, float *klr, float *lossr,
+                                              const RowOpts &o, float *red, RowK &rk,
+                                              LdsStep<D> &lds_step, HeldRegs<D> &hs,
+                                              HeldRegs<D> &ht) {
+    constexpr int VEC = D::VEC;
+    constexpr int64_t STEP = (int64_t)TW_U * TWICE_BLK;  // vectors per input per sweep step
     // fp16 rows take the divergence form that admits masked tokens without the range
     // test: tracking the minima costs the fp16 kernel 26 VGPRs and its second workgroup
     // per CU
     constexpr bool RANGE = !std::is_same<D, F16>::value;
     OpStats<3, RANGE> o1(o.ks);
-    // Held steps: the last HOLD + LHOLD full steps of the 16-byte body, elements [P, Q).
-    // Rows whose two inputs sit at different offsets inside 16 bytes (h == w), or that
-    // are too short, are swept whole.  A lane reads back from LDS only the vectors it
-    // wrote there itself, so the LDS step needs no barrier of its own.
+    // A lane reads back from LDS only the vectors it wrote there itself, so the LDS step
+    // needs no barrier of its own.
     constexpr int HOLD = held_steps<D>(), LHOLD = lds_steps<D>();
-    const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
-    const bool hold = nfull >= HOLD + LHOLD;
-    // [P, PR): the step held in LDS (if any); [PR, Q): the steps held in registers
-    const int64_t P = hold ? h + (nfull - HOLD - LHOLD) * STEP * VEC : w;
-    const int64_t PR = P + LHOLD * STEP * VEC;
-    const int64_t Q = hold ? PR + HOLD * STEP * VEC : w;
-    __shared__ u32x4 lds_step[2][TW_U][LHOLD ? TWICE_BLK : 1];  // each lane's own vectors
-    u32x4 hs[HOLD][TW_U], ht[HOLD][TW_U];
+    const int64_t h = sp.h, P = sp.P, PR = sp.PR, Q = sp.Q;
+    const bool hold = sp.hold;
     if (hold) {
         sweep<D, TW_U, true, TWICE_BLK>(s, t, P, h, o1);
         if constexpr (LHOLD > 0) {
@@ -428,7 +461,6 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
     }
     // wave partials, then wave 0 combines them in wave order and derives the constants
     constexpr int NW = TWICE_BLK / 64;
-    __shared__ RowK rk;
     {
         const MZ ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
         const MZ wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
@@ -453,7 +485,7 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
                 mns = fminf(mns, red[4 * NW + 2 * k]);
                 mnt = fminf(mnt, red[4 * NW + 2 * k + 1]);
             }
-            row_constants(ms.m, ms.z, mt.m, mt.z, mns, mnt, beta, o.ks, stats + r * 4, &rk);
+            row_constants(ms.m, ms.z, mt.m, mt.z, mns, mnt, beta, o.ks, st, &rk);
         }
         __syncthreads();
     }
@@ -485,9 +517,207 @@ void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restr
             twice_stream<D, true>(k.mx, (float)beta, o.ks, hold, s, t, w, h, P, Q, v);
     }
     block_sum<2, TWICE_BLK>(v, red);
-    if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], kl + 2 * r, loss + r, o.lscale);
+    if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], klr, lossr, o.lscale);
 }
 
+template <class D>
+__global__ __launch_bounds__(TWICE_BLK)
+void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restrict__ stats,
+                 float *__restrict__ kl, float *__restrict__ loss, RowOpts o) {
+    using T = typename D::T;
+    __shared__ float red[6 * (TWICE_BLK / 64)];
+    __shared__ RowK rk;
+    __shared__ LdsStep<D> lds_step;
+    const int64_t r = blockIdx.x;
+    if (row_dropped(o, r)) {
+        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
+        return;
+    }
+    const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
+    const TwiceSpan sp = twice_span<D>(w, head_len<T>(w, s, t));
+    HeldRegs<D> hs, ht;
+    twice_forward<D>(s, t, w, sp, beta, stats + r * 4, kl + 2 * r, loss + r, o, red, rk, lds_step,
+                     hs, ht);
+}
+
+// ---- forward and backward in one launch ---------------------------------------------
+//
+// [JSD-PR, Changes] The backward needs the forward's statistics and KL pair, which a
+// single-shard row's workgroup has just produced: with the upstream gradient known
+// before the forward (a per-token weight, or a reduction's scale), the same workgroup
+// goes on to the row's gradients.  The register-held row is then read from HBM once for
+// both passes; the two-sweep row reuses the steps it holds on chip, and the separate
+// backward's constants launch and kernel boundary go away.  Each output is the one the
+// forward and backward entry points compute, bit for bit: the forward is the same code,
+// and the gradients are element-wise with the same constants (backward.hpp).
+
+// Thread 0, after its row's forward: the backward's constants of row r from the
+// statistics and KL pair it has just written to global memory (a thread reads back its
+// own writes), as k_bwd_prep derives them.
+__device__ __forceinline__ void fused_bwd_constants(const double *stats, const float *kl,
+                                                    int64_t r, double beta, const float *grad,
+                                                    const GradOpts &go, float *rc) {
+    const RowConst k = row_const(stats, r, go.ks);
+    bwd_constants(INTERIOR, k, kl + 2 * r, beta, upstream_g(grad, go, r), go.ks, k.undefined, rc);
+}
+
+template <class D, int BLK, bool WS, bool WT>
+__device__ __forceinline__ void zero_grads(typename D::T *gs, typename D::T *gt, int64_t w) {
+    if (WS) zero_span<D, BLK>(gs, w);
+    if (WT) zero_span<D, BLK>(gt, w);
+}
+
+// Shape of the fused kernels, measured on MI355X against the forward and backward
+// launches (kernel time, two calls -> one call):
+//   two-sweep rows: waves per SIMD held at 4 for 16-bit inputs (128 VGPRs, two
+//     workgroups per CU as the forward alone; bf16 spills 12 bytes, fp16 68), 2 for
+//     fp32 (one workgroup per CU, 244 VGPRs); one vector per lane in flight in the
+//     gradient sweep (two: 8192 x 151936 bf16 2.82 against 2.75 ms).  8192 x 151936
+//     bf16: 2.83-2.87 -> 2.73-2.75 ms; 4096 x 151936 fp16: 1.45-1.46 -> 1.41-1.43 ms;
+//     4096 x 128256 fp32: 2.29-2.30 -> 2.29 ms, where the backward part runs at one
+//     workgroup per CU (reading the four register steps again instead of keeping
+//     them: 2.38-2.44 ms)
+//   512-lane register rows: held to 128 VGPRs, two workgroups per CU (1024 x 37984
+//     bf16, student gradient: 0.0916 ms at 134 VGPRs and one workgroup per CU, 0.0815
+//     ms with a 20-byte spill; the two calls 0.092-0.096 ms); 8192 x 16032 bf16 (256
+//     lanes, 8 vectors): 0.304 -> 0.235 ms; 8192 x 32000: 0.60 -> 0.46-0.49 ms
+template <class D>
+constexpr int fb_waves() { return sizeof(typename D::T) == 4 ? 2 : 4; }
+template <class D>
+constexpr int fb_sweep_u() { return 1; }
+template <int B>
+constexpr int fb_row_waves() { return B == 512 ? 4 : 1; }
+
+// A row held in registers: k_fwd_row's forward, then the gradients from the same
+// registers.  The gradient rows start on 16-byte boundaries like the inputs' (the host
+// checks).
+template <class D, int NVT, int B, bool WS, bool WT>
+__global__ __launch_bounds__(B) __attribute__((amdgpu_waves_per_eu(fb_row_waves<B>())))
+void k_fwdbwd_row(RowView sv, RowView tv, RowMView gsv,
+                                                   RowMView gtv, int64_t w, double beta,
+                                                   const float *__restrict__ grad,
+                                                   double *stats, float *kl,
+                                                   float *__restrict__ loss, RowOpts o,
+                                                   GradOpts go) {
+    using T = typename D::T;
+    constexpr int VEC = D::VEC;
+    __shared__ float red[4 * (B / 64)];
+    __shared__ RowK rk;
+    __shared__ float rc[ROWC];
+    const int64_t r = blockIdx.x;
+    T *gs = WS ? row_ptr<T>(gsv, r) : nullptr;
+    T *gt = WT ? row_ptr<T>(gtv, r) : nullptr;
+    if (row_dropped(o, r)) {
+        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
+        zero_grads<D, B, WS, WT>(gs, gt, w);
+        return;
+    }
+    const int64_t nv = w / VEC;
+    u32x4 xs[NVT], xt[NVT];
+    row_forward<D, NVT, B>(row_ptr<T>(sv, r), row_ptr<T>(tv, r), nv, beta, stats + r * 4,
+                           kl + 2 * r, loss + r, o, red, rk, xs, xt);
+    if (threadIdx.x == 0) fused_bwd_constants(stats, kl, r, beta, grad, go, rc);
+    __syncthreads();
+    if (rc[ROWC_UNDEFINED] != 0.0f) {  // no distribution: exactly zero gradients
+        zero_grads<D, B, WS, WT>(gs, gt, w);
+        return;
+    }
+    OpBwd<D, INTERIOR, WS, WT> op;
+    op.gs = gs;
+    op.gt = gt;
+    op.set(rc);
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) {
+        const int64_t j = threadIdx.x + (int64_t)i * B;
+        if (j < nv) {
+            float a[1][VEC], b[1][VEC];
+            widen<D>(xs[i], a[0]);
+            widen<D>(xt[i], b[0]);
+            const int64_t c[1] = {j * VEC};
+            op.template run<1, VEC>(a, b, c);
+        }
+    }
+}
+
+// The two-sweep row: k_fwd_twice's forward, then the gradients, the held steps first
+// (registers, then LDS), then the rest of the row read a third time.  Gradient views at
+// another offset inside 16 bytes than the inputs' take the whole row from memory.
+// Measured on MI355X at 8192 x 151936 bf16, both gradients: 2.73-2.75 ms against
+// 2.83-2.87 ms for the forward and backward launches.
+
+template <class D, bool WS, bool WT>
+__global__ __launch_bounds__(TWICE_BLK)
+__attribute__((amdgpu_waves_per_eu(fb_waves<D>(), fb_waves<D>())))
+void k_fwdbwd_twice(RowView sv, RowView tv, RowMView gsv, RowMView gtv, int64_t w, double beta,
+                    const float *__restrict__ grad, double *stats, float *kl,
+                    float *__restrict__ loss, RowOpts o, GradOpts go) {
+    using T = typename D::T;
+    constexpr int VEC = D::VEC;
+    constexpr int64_t STEP = (int64_t)TW_U * TWICE_BLK;  // vectors per input per sweep step
+    constexpr int HOLD = held_steps<D>(), LHOLD = lds_steps<D>();
+    constexpr int U = fb_sweep_u<D>();
+    __shared__ float red[6 * (TWICE_BLK / 64)];
+    __shared__ RowK rk;
+    __shared__ LdsStep<D> lds_step;
+    __shared__ float rc[ROWC];
+    const int64_t r = blockIdx.x;
+    T *gs = WS ? row_ptr<T>(gsv, r) : nullptr;
+    T *gt = WT ? row_ptr<T>(gtv, r) : nullptr;
+    if (row_dropped(o, r)) {
+        dropped_row(stats + r * 4, kl + 2 * r, loss + r);
+        zero_grads<D, TWICE_BLK, WS, WT>(gs, gt, w);
+        return;
+    }
+    const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
+    const TwiceSpan sp = twice_span<D>(w, head_len<T>(w, s, t));
+    HeldRegs<D> hs, ht;
+    twice_forward<D>(s, t, w, sp, beta, stats + r * 4, kl + 2 * r, loss + r, o, red, rk, lds_step,
+                     hs, ht);
+    if (threadIdx.x == 0) fused_bwd_constants(stats, kl, r, beta, grad, go, rc);
+    __syncthreads();
+    if (rc[ROWC_UNDEFINED] != 0.0f) {  // no distribution: exactly zero gradients
+        zero_grads<D, TWICE_BLK, WS, WT>(gs, gt, w);
+        return;
+    }
+    OpBwd<D, INTERIOR, WS, WT> op;
+    op.gs = gs;
+    op.gt = gt;
+    op.set(rc);
+    const int64_t hg = head_len<T>(w, s, t, gs, gt);
+    if (!sp.hold || hg != sp.h) {
+        sweep<D, U, true, TWICE_BLK, true>(s, t, w, hg, op);
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < HOLD; ++j) {
+#pragma unroll
+        for (int u = 0; u < TW_U; ++u) {
+            // one held vector's widened values live at a time (as held_div)
+            u32x4 xs = hs[j][u], xt = ht[j][u];
+            if (u > 0) asm volatile("" : "+v"(xs), "+v"(xt));
+            float a[1][VEC], b[1][VEC];
+            widen<D>(xs, a[0]);
+            widen<D>(xt, b[0]);
+            const int64_t c[1] = {
+                sp.PR + ((int64_t)j * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC};
+            op.template run<1, VEC>(a, b, c);
+        }
+    }
+    if constexpr (LHOLD > 0) {
+#pragma unroll
+        for (int u = 0; u < TW_U; ++u) {
+            float a[1][VEC], b[1][VEC];
+            widen<D>(lds_step[0][u][threadIdx.x], a[0]);
+            widen<D>(lds_step[1][u][threadIdx.x], b[0]);
+            const int64_t c[1] = {sp.P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC};
+            op.template run<1, VEC>(a, b, c);
+        }
+    }
+    sweep<D, U, true, TWICE_BLK, true>(s, t, sp.P, sp.h, op);
+    if (WS) op.gs = gs + sp.Q;
+    if (WT) op.gt = gt + sp.Q;
+    sweep<D, U, true, TWICE_BLK, true>(s + sp.Q, t + sp.Q, w - sp.Q, 0, op);
+}
 
 // Orders one wave's LDS writes before that wave's later LDS reads of other lanes'
 // values (wavefront-scope release, the wave's barrier, acquire).
@@ -697,6 +927,40 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
     if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], kl + 2 * r, loss + r, o.lscale);
 }
 
+// Every row of the view starts on a 16-byte boundary.
+template <class V>
+bool rows16(const V &v, int64_t N, int esize) {
+    if (reinterpret_cast<uintptr_t>(v.p) % 16 != 0) return false;
+    if ((v.rs * esize) % 16 != 0 && N > 1) return false;
+    if (v.rpb > 0 && (v.bs * esize) % 16 != 0) return false;
+    return true;
+}
+
+// The register-held row's workgroup shape for rows of nv 16-byte vectors (nv <=
+// FB_WIDE * ROW_WIDE_NVT_MAX): 256 lanes with 1, 2, 4 or 8 vectors, then 512 lanes with
+// 6, 8 or 10.
+enum RowShape { R1, R2, R4, R8, W6, W8, W10 };
+RowShape row_shape(int64_t nv) {
+    if (nv <= FB) return R1;
+    if (nv <= 2 * FB) return R2;
+    if (nv <= 4 * FB) return R4;
+    if (nv <= 8 * FB) return R8;
+    if (nv <= 6 * FB_WIDE) return W6;
+    if (nv <= 8 * FB_WIDE) return W8;
+    return W10;
+}
+
+// Rows of shard sh fit the register-held kernels: whole vectors, at most
+// FB_WIDE * ROW_WIDE_NVT_MAX of them, every row of both inputs 16-byte aligned.
+template <class D>
+bool row_fits(const Shard &sh, int64_t N) {
+    constexpr int VEC = D::VEC;
+    const int64_t w = sh.width;
+    const int esize = (int)sizeof(typename D::T);
+    return w > 0 && w % VEC == 0 && w / VEC <= (int64_t)FB_WIDE * ROW_WIDE_NVT_MAX &&
+           rows16(sh.s, N, esize) && rows16(sh.t, N, esize);
+}
+
 template <class D, int NVT, int B>
 hipError_t row_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
                       float *loss, hipStream_t st, const RowOpts &o) {
@@ -709,29 +973,73 @@ hipError_t row_launch(const Shard &sh, int64_t N, double beta, double *stats, fl
 template <class D>
 hipError_t fused_launch(const Shard &sh, int64_t N, double beta, double *stats, float *kl,
                         float *loss, hipStream_t st, const RowOpts &o) {
-    constexpr int VEC = D::VEC;
-    const int64_t w = sh.width;
-    const int64_t nv = w / VEC;
-    bool regs = w > 0 && w % VEC == 0 && nv <= (int64_t)FB_WIDE * ROW_WIDE_NVT_MAX;
-    const int esize = (int)sizeof(typename D::T);
-    const RowView *views[2] = {&sh.s, &sh.t};
-    for (const RowView *v : views) {  // every row must start on a 16-byte boundary
-        if (reinterpret_cast<uintptr_t>(v->p) % 16 != 0) regs = false;
-        if ((v->rs * esize) % 16 != 0 && N > 1) regs = false;
-        if (v->rpb > 0 && (v->bs * esize) % 16 != 0) regs = false;
-    }
-    if (!regs) {
+    if (!row_fits<D>(sh, N)) {
         hipLaunchKernelGGL(k_fwd_twice<D>, dim3((unsigned)N), dim3(TWICE_BLK), 0, st, sh.s,
-                           sh.t, w, beta, stats, kl, loss, o);
+                           sh.t, sh.width, beta, stats, kl, loss, o);
         return hipGetLastError();
     }
-    if (nv <= FB) return row_launch<D, 1, FB>(sh, N, beta, stats, kl, loss, st, o);
-    if (nv <= 2 * FB) return row_launch<D, 2, FB>(sh, N, beta, stats, kl, loss, st, o);
-    if (nv <= 4 * FB) return row_launch<D, 4, FB>(sh, N, beta, stats, kl, loss, st, o);
-    if (nv <= 8 * FB) return row_launch<D, 8, FB>(sh, N, beta, stats, kl, loss, st, o);
-    if (nv <= 6 * FB_WIDE) return row_launch<D, 6, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
-    if (nv <= 8 * FB_WIDE) return row_launch<D, 8, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
-    return row_launch<D, ROW_WIDE_NVT_MAX, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
+    switch (row_shape(sh.width / D::VEC)) {
+        case R1: return row_launch<D, 1, FB>(sh, N, beta, stats, kl, loss, st, o);
+        case R2: return row_launch<D, 2, FB>(sh, N, beta, stats, kl, loss, st, o);
+        case R4: return row_launch<D, 4, FB>(sh, N, beta, stats, kl, loss, st, o);
+        case R8: return row_launch<D, 8, FB>(sh, N, beta, stats, kl, loss, st, o);
+        case W6: return row_launch<D, 6, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
+        case W8: return row_launch<D, 8, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
+        default: return row_launch<D, ROW_WIDE_NVT_MAX, FB_WIDE>(sh, N, beta, stats, kl, loss, st, o);
+    }
+}
+
+// Arguments of a forward-and-backward launch.
+struct FbArgs {
+    double beta;
+    const float *grad;
+    double *stats;
+    float *kl, *loss;
+    RowOpts o;
+    GradOpts go;
+};
+
+template <class D, int NVT, int B, bool WS, bool WT>
+hipError_t fb_row_launch(const Shard &sh, int64_t N, const FbArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL((k_fwdbwd_row<D, NVT, B, WS, WT>), dim3((unsigned)N), dim3(B), 0, st,
+                       sh.s, sh.t, sh.gs, sh.gt, sh.width, a.beta, a.grad, a.stats, a.kl, a.loss,
+                       a.o, a.go);
+    return hipGetLastError();
+}
+
+// The register-held row when the inputs fit it and the wanted gradient views are
+// 16-byte aligned too; the two sweeps for rows the register kernels do not take.  Rows
+// the forward alone would hold in registers but whose gradient views are not aligned
+// are not fused: hipErrorNotSupported, and the caller runs the two entry points.
+template <class D, bool WS, bool WT>
+hipError_t fb_launch(const Shard &sh, int64_t N, const FbArgs &a, hipStream_t st) {
+    const int esize = (int)sizeof(typename D::T);
+    if (!row_fits<D>(sh, N)) {
+        hipLaunchKernelGGL((k_fwdbwd_twice<D, WS, WT>), dim3((unsigned)N), dim3(TWICE_BLK), 0, st,
+                           sh.s, sh.t, sh.gs, sh.gt, sh.width, a.beta, a.grad, a.stats, a.kl,
+                           a.loss, a.o, a.go);
+        return hipGetLastError();
+    }
+    if ((WS && !rows16(sh.gs, N, esize)) || (WT && !rows16(sh.gt, N, esize)))
+        return hipErrorNotSupported;
+    switch (row_shape(sh.width / D::VEC)) {
+        case R1: return fb_row_launch<D, 1, FB, WS, WT>(sh, N, a, st);
+        case R2: return fb_row_launch<D, 2, FB, WS, WT>(sh, N, a, st);
+        case R4: return fb_row_launch<D, 4, FB, WS, WT>(sh, N, a, st);
+        case R8: return fb_row_launch<D, 8, FB, WS, WT>(sh, N, a, st);
+        case W6: return fb_row_launch<D, 6, FB_WIDE, WS, WT>(sh, N, a, st);
+        case W8: return fb_row_launch<D, 8, FB_WIDE, WS, WT>(sh, N, a, st);
+        default: return fb_row_launch<D, ROW_WIDE_NVT_MAX, FB_WIDE, WS, WT>(sh, N, a, st);
+    }
+}
+
+template <class D>
+hipError_t fb_want(const Shard &sh, int64_t N, const FbArgs &a, hipStream_t st) {
+    const bool ws = sh.gs.p != nullptr, wt = sh.gt.p != nullptr;
+    if (ws && wt) return fb_launch<D, true, true>(sh, N, a, st);
+    if (ws) return fb_launch<D, true, false>(sh, N, a, st);
+    if (wt) return fb_launch<D, false, true>(sh, N, a, st);
+    return fused_launch<D>(sh, N, a.beta, a.stats, a.kl, a.loss, st, a.o);
 }
 
 }  // namespace
@@ -762,6 +1070,17 @@ hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, 
         case 0: return fused_launch<F32>(sh, N, beta, stats, kl, loss, st, o);
         case 1: return fused_launch<F16>(sh, N, beta, stats, kl, loss, st, o);
         default: return fused_launch<BF16>(sh, N, beta, stats, kl, loss, st, o);
+    }
+}
+
+hipError_t launch_fwd_bwd_fused(int dtype, const Shard &sh, int64_t N, double beta,
+                                const float *grad, double *stats, float *kl, float *loss,
+                                hipStream_t st, const RowOpts &o, const GradOpts &go) {
+    const FbArgs a{beta, grad, stats, kl, loss, o, go};
+    switch (dtype) {
+        case 0: return fb_want<F32>(sh, N, a, st);
+        case 1: return fb_want<F16>(sh, N, a, st);
+        default: return fb_want<BF16>(sh, N, a, st);
     }
 }
 

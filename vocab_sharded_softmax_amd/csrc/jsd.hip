@@ -17,6 +17,7 @@
 //   KT / ln2 = (1/Z_t) sum e_t (u_t - L),  KS / ln2 = (1/Z_s) sum e_s ((u_s - L) - r)
 // so the per-element work touches only O(1)-sized quantities, never log Z; u - L and
 // (u_s - L) - r are differences of nearby numbers and come out (nearly) exact.
+#include "backward.hpp"
 #include "divergence.hpp"
 #include <type_traits>
 
@@ -26,31 +27,6 @@
 namespace vjsd {
 
 namespace {
-
-// Per-row constants of a two-input pass, rebuilt from the fp64 statistics.
-struct RowConst {
-    bool undefined;
-    float cs, ct;    // reference points
-    float izs, izt;  // 1 / Z
-    double Zs, Zt;
-    double r;        // log2(Z_s / Z_t)
-};
-
-__device__ __forceinline__ RowConst row_const(const double *__restrict__ stats, int64_t r,
-                                              float ks = L2E) {
-    RowConst k;
-    const double *st = stats + r * 4;
-    const float ms = (float)st[0], mt = (float)st[2];
-    k.undefined = (ms == NINF) || (mt == NINF);
-    k.cs = refc(ms, ks);
-    k.ct = refc(mt, ks);
-    k.Zs = k.undefined ? 1.0 : z_from_stats(ms, st[1], ks);
-    k.Zt = k.undefined ? 1.0 : z_from_stats(mt, st[3], ks);
-    k.izs = (float)(1.0 / k.Zs);
-    k.izt = (float)(1.0 / k.Zt);
-    k.r = log2(k.Zs / k.Zt);
-    return k;
-}
 
 template <class D, int MODE>
 __global__ __launch_bounds__(BLOCK) void k_div(RowView sv, RowView tv, int64_t w,
@@ -148,64 +124,14 @@ __global__ void k_div_finalize(int mode, const float *__restrict__ part, int S, 
 }
 
 // ---- backward ---------------------------------------------------------------------
+//
+// The constants and the element op are those of backward.hpp, which the one-launch
+// forward and backward (fused.hip) shares.
 
-// DG: storage of the gradients (the input's, or bf16 for fp32 input: the logit
-// gradient the fused-linear products consume)
-template <class D, int MODE, bool WS, bool WT, class DG = D>
-struct OpBwd {
-    using T = typename D::T;
-    using TG = typename DG::T;
-    TG *gs, *gt;
-    float ks;  // log2 e / temperature
-    float cs, ct, bf, gam;
-    float Cs, Ct;  // gradient scales
-    float Hs, Ht;  // per-side offsets subtracted from the log-ratio
-    float Gs, Gt;  // g / Z for the p_s - p_t terms of the endpoints
-
-    template <int NV, int W>
-    __device__ __forceinline__ void run(const float (&x)[NV][W], const float (&y)[NV][W],
-                                        const int64_t (&col)[NV]) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            float os[W], ot[W];
-#pragma unroll
-            for (int i = 0; i < W; ++i) {
-                const float us = fmaxf(fmaf(x[j][i], ks, -cs), U_FLOOR);
-                const float ut = fmaxf(fmaf(y[j][i], ks, -ct), U_FLOOR);
-                const float es = ex2(us), et = ex2(ut);
-                if constexpr (MODE == INTERIOR) {
-                    const float L = lg2(fmaf(bf, et, fmaf(gam, es, W_FLOOR)));
-                    os[i] = (Cs * es) * ((us - L) - Hs);
-                    ot[i] = (Ct * et) * ((ut - L) - Ht);
-                } else if constexpr (MODE == FWD_KL) {
-                    os[i] = fmaf(Gs, es, -(Gt * et));
-                    ot[i] = (Ct * et) * ((ut - us) - Ht);
-                } else {
-                    os[i] = (Cs * es) * ((us - ut) - Hs);
-                    ot[i] = fmaf(Gt, et, -(Gs * es));
-                }
-            }
-            if constexpr (W == D::VEC && std::is_same<D, DG>::value) {
-                if (WS) store_vec<D, true>(gs + col[j], os);
-                if (WT) store_vec<D, true>(gt + col[j], ot);
-            } else if constexpr (W == D::VEC) {  // four fp32 values as 8 bytes of bf16
-                if (WS) st_bf16x4(gs + col[j], os);
-                if (WT) st_bf16x4(gt + col[j], ot);
-            } else {
-#pragma unroll
-                for (int i = 0; i < W; ++i) {
-                    if (WS) store1<DG>(gs + col[j] + i, os[i]);
-                    if (WT) store1<DG>(gt + col[j] + i, ot[i]);
-                }
-            }
-        }
-    }
-};
-
-// Per-row constants of the backward, computed once per call from the fp64 statistics:
-// rowc[r*ROWC + i] = cs, ct, beta, gamma, Cs, Ct, Hs, Ht, Gs, Gt (i = 0..9), the
-// exponent scale in slot ROWC_KS and the zero-gradient flag (no distribution, or a
-// row the mask drops) in slot ROWC_UNDEFINED.
+// Per-row constants of the backward, computed once per call from the fp64 statistics
+// (bwd_constants: rowc[r*ROWC + i] = cs, ct, beta, gamma, Cs, Ct, Hs, Ht, Gs, Gt for
+// i = 0..9, the exponent scale in slot ROWC_KS and the zero-gradient flag, no
+// distribution or a row the mask drops, in slot ROWC_UNDEFINED).
 __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats,
                            const float *__restrict__ kl, double beta,
                            const float *__restrict__ grad, float *__restrict__ rowc,
@@ -214,36 +140,8 @@ __global__ void k_bwd_prep(int mode, int64_t N, const double *__restrict__ stats
     if (r >= N) return;
     const RowConst k = row_const(stats, r, go.ks);
     const bool dropped = go.mask != nullptr && go.mask[r] == 0;
-    double g = grad == nullptr ? 1.0 : (go.scalar ? (double)grad[0] : (double)grad[r]);
-    if (go.count) g /= fmax((double)*go.count, 1.0);
-    g *= go.gmul;
-    const double KT2 = (double)kl[2 * r] * L2E_D, KS2 = (double)kl[2 * r + 1] * L2E_D;
-    double Cs = 0.0, Ct = 0.0, Hs = 0.0, Ht = 0.0;
-    if (mode == INTERIOR) {
-        Cs = g * (1.0 - beta) * LN2_D / k.Zs;
-        Ct = g * beta * LN2_D / k.Zt;
-        Hs = k.r + KS2;
-        Ht = KT2;
-    } else if (mode == FWD_KL) {  // d/dt = g p_t (lp_t - lp_s - KT), lp2_t - lp2_s = u_t - u_s + r
-        Ct = g * LN2_D / k.Zt;
-        Ht = KT2 - k.r;
-    } else {  // d/ds = g p_s (lp_s - lp_t - KS), lp2_s - lp2_t = u_s - u_t - r
-        Cs = g * LN2_D / k.Zs;
-        Hs = KS2 + k.r;
-    }
-    float *o = rowc + r * ROWC;
-    o[0] = k.cs;
-    o[1] = k.ct;
-    o[2] = (float)beta;
-    o[3] = (float)((1.0 - beta) * k.Zt / k.Zs);
-    o[4] = (float)Cs;
-    o[5] = (float)Ct;
-    o[6] = (float)Hs;
-    o[7] = (float)Ht;
-    o[8] = (float)(g / k.Zs);
-    o[9] = (float)(g / k.Zt);
-    o[ROWC_KS] = go.ks;
-    o[ROWC_UNDEFINED] = (k.undefined || dropped) ? 1.0f : 0.0f;
+    bwd_constants(mode, k, kl + 2 * r, beta, upstream_g(grad, go, r), go.ks,
+                  k.undefined || dropped, rowc + r * ROWC);
 }
 
 // One workgroup of LANES lanes per row chunk of up to cw columns (chunk_span), one
@@ -278,17 +176,7 @@ __device__ __forceinline__ void bwd_chunk(const typename D::T *srow, const RowVi
     OpBwd<D, MODE, WS, WT, DG> op;
     op.gs = gs;
     op.gt = gt;
-    op.ks = k[ROWC_KS];
-    op.cs = k[0];
-    op.ct = k[1];
-    op.bf = k[2];
-    op.gam = k[3];
-    op.Cs = k[4];
-    op.Ct = k[5];
-    op.Hs = k[6];
-    op.Ht = k[7];
-    op.Gs = k[8];
-    op.Gt = k[9];
+    op.set(k);
     // the vector path needs every view of the chunk at the same offset inside 16 bytes;
     // inputs and gradients are touched once, so loads and stores stream
     // (a bf16 gradient of fp32 input sits at the same element offsets, 8-byte aligned

@@ -35,6 +35,14 @@ hipError_t launch_div_finalize(int mode, const float *part, int S, int64_t N,
 // then divergence, one workgroup per row (held in registers when the row fits).
 hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, double *stats,
                             float *kl, float *loss, hipStream_t st, const RowOpts &o = RowOpts());
+// Interior JSD forward and backward of a single shard in one launch: launch_fwd_fused's
+// outputs, then the gradients into sh.gs / sh.gt (a NULL view is not written) for the
+// upstream gradient grad under go, as launch_bwd_prep + launch_bwd compute them.
+// hipErrorNotSupported (nothing launched) for register-held rows whose gradient views
+// are not 16-byte aligned like the inputs.
+hipError_t launch_fwd_bwd_fused(int dtype, const Shard &sh, int64_t N, double beta,
+                                const float *grad, double *stats, float *kl, float *loss,
+                                hipStream_t st, const RowOpts &o, const GradOpts &go);
 // interior JSD forward of 2..FUSED_SHARDS shards in one launch (stats, merge, divergence)
 constexpr int FUSED_SHARDS = 8;
 struct ShardRows {
@@ -80,18 +88,6 @@ inline Chunks grad_chunks(int64_t N, int64_t w, int esize) {
     while (N * count(cw) > 0x7fffffffLL) cw *= 2;  // grid.x limit
     return {cw, count(cw)};
 }
-
-// Upstream-gradient options of the distillation-loss form of the backward: the row
-// r's gradient scale is g_r * gmul, g_r = grad[r] (per-row) or grad[0] (reduced;
-// divided by max(*count, 1) for a mean), and 0 for a row the mask drops.  A NULL
-// grad stands for a unit upstream gradient.
-struct GradOpts {
-    float ks = L2E;                  // log2 e / temperature
-    double gmul = 1.0;               // T^2 (if scaled) * (1/T): chain rule through x / T
-    bool scalar = false;             // grad is one value for all rows
-    const uint8_t *mask = nullptr;   // [N]; zero drops the row
-    const double *count = nullptr;   // device: kept rows, for a mean (null: no division)
-};
 
 // pass 3: per-row constants of the backward (once per call), then the closed-form
 // gradients of the JSD / KL for one shard
