@@ -214,8 +214,9 @@ def traffic_fields(workload, parts, ms, fallback_bytes, fallback_basis, pages_by
     fallback_bytes, a lower bound of the route's traffic ("compulsory": one forward and
     one backward read of the inputs and the gradient writes, for the two calls;
     "minimum": one read and the gradient writes, for the one call).  The pages' count
-    (three input passes plus the gradient writes) is reported beside, labelled as such;
-    held steps, register-held rows and caches let it exceed what the kernels fetch.
+    (three input passes plus the gradient writes) is reported beside as bytes only: held
+    steps and register-held rows let it exceed what the kernels fetch, so no fraction is
+    quoted on it.
     With counters, the transcendental utilisation of each part: its transcendental
     results per second (time part_ms[part], else ms) against PEAK_TRANS_PER_S."""
     c = counters(workload)
@@ -227,9 +228,7 @@ def traffic_fields(workload, parts, ms, fallback_bytes, fallback_basis, pages_by
         nbytes, basis = fallback_bytes, fallback_basis
     gbps = nbytes / (ms * 1e-3) / 1e9
     out = {"bytes_per_step": nbytes, "bytes_basis": basis, "hbm_gbps": round(gbps, 1),
-           "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-           "pages_equivalent_bytes": pages_bytes,
-           "pages_equivalent_frac": round(pages_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+           "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4), "pages_equivalent_bytes": pages_bytes}
     if c is not None:
         pm = part_ms or {}
         out["counter_bytes"] = {p: c[p]["bytes"] for p in parts}
@@ -472,7 +471,9 @@ def main():
         gen = torch.Generator(device="cuda").manual_seed(5)
         for name, frac in (("all_tokens", 1.0), ("3pct_tokens", 0.03)):
             keep = (torch.rand(N, generator=gen, device="cuda") < frac).to(torch.uint8)
-            opts = vj.loss_opts(N, 2.0, True, keep, "mean")
+            # every token kept is no mask at all (the one call applies); a mask runs the
+            # forward and backward launches (one launch would end on the kept rows' tail)
+            opts = vj.loss_opts(N, 2.0, True, None if frac == 1.0 else keep, "mean")
 
             def lstep():
                 vj.vjsd_loss_forward(sh, 0.5, opts, part, stats, kl, loss, out1)
@@ -484,6 +485,22 @@ def main():
                                "fwd_bwd_ms": round(timed(torch, lone, 5), 4),
                                "two_calls_ms": round(timed(torch, lstep, 5), 4)}
         branches["jsd_loss_T2_mean"] = loss_rows
+
+        # the same loss through the autograd op (all tokens kept): its gradients in the
+        # backward (two calls), and in the forward (one call, then a unit-scale no-op)
+        auto = {}
+        for gif in (False, True):
+            xs = s.detach().clone().requires_grad_()
+            xt = t.detach().clone().requires_grad_()
+
+            def astep():
+                vj.jsd_loss(xs, xt, 0.5, temperature=2.0, scale_t2=True, reduction="mean",
+                            grad_in_forward=gif).backward()
+                xs.grad = xt.grad = None
+            auto["grad_in_forward" if gif else "grad_in_backward"] = round(
+                timed(torch, astep, 5), 4)
+            del xs, xt
+        branches["jsd_loss_T2_mean_autograd_ms"] = auto
 
     # streaming read and copy ceilings measured on the same buffers
     ceil = ceilings(torch, vj, s, t, gs)

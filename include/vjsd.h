@@ -281,15 +281,16 @@ VJSD_API int vjsd_bwd_noalloc(const vjsd_shard *shards, int S, int64_t N, int dt
  * forward's global statistics and recomputes probabilities from the logits].  Same
  * arguments as those two calls, same meaning and ownership; `part` as there.  How it
  * runs:
- *   one shard, 0 < beta < 1   one launch, a workgroup per row: the forward of
+ *   one shard, 0 < beta < 1, no mask   one launch, a workgroup per row: the forward of
  *                   vjsd_forward's single-shard route, then that row's gradients in
  *                   the same workgroup.  A row held in registers is read from HBM
  *                   once for both passes (its gradient views must start on 16-byte
  *                   boundaries like the inputs', else the two calls run); a wider row
  *                   reuses the sweep steps it holds on chip and reads the rest a
- *                   third time.  With VJSD_REDUCE_MEAN a short launch counts the kept
- *                   rows first.
- *   otherwise       vjsd_loss_forward, then vjsd_loss_backward.
+ *                   third time.
+ *   otherwise       vjsd_loss_forward, then vjsd_loss_backward (with a mask too: when
+ *                   few tokens are kept, the kept rows' whole work in one workgroup
+ *                   each would end the launch on a tail).
  * Errors as vjsd_loss_forward and vjsd_loss_backward; on an error nothing is
  * launched, except a VJSD_ERR_HIP from a launch.
  */
@@ -510,8 +511,11 @@ VJSD_API int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N
 
 /*
  * Scales n values in place by a device scalar: p[i] *= g[0] (the upstream gradient
- * of a reduced loss applied to gradients computed for a unit upstream gradient).
- * dtype VJSD_F32 or VJSD_BF16 (nearest even); p 16-byte aligned.
+ * of a reduced loss applied to gradients computed for a unit upstream gradient: the
+ * fused-linear loss, or vjsd_loss_forward_backward with a unit grad).  dtype VJSD_F32,
+ * VJSD_F16 or VJSD_BF16 (nearest even); p 16-byte aligned.  When g[0] is exactly 1
+ * the launched kernel returns at once and p is neither read nor written (x * 1 == x
+ * in every format), so applying a unit upstream gradient costs one short launch.
  */
 VJSD_API int vlin_scale(void *p, int64_t n, int dtype, const float *g, void *stream);
 

@@ -333,8 +333,10 @@ def test_linear_workspace_and_scale():
               + al(lib.vjsd_workspace_bytes(96, 1)) + al(8) + al(1001 * 16 * 4))
     assert w(300, 1001, 16, 100, 150) == expect
     s = lib.vlin_scale
-    assert s(FAKE, 10, 1, FAKE, None) == DTYPE
+    assert s(FAKE, 10, 3, FAKE, None) == DTYPE
+    assert s(FAKE, 10, -1, FAKE, None) == DTYPE
     assert s(FAKE, 0, 2, FAKE, None) == OK
+    assert s(FAKE + 2, 10, 1, FAKE, None) == ARG  # fp16 accepted, alignment still checked
     assert s(FAKE, -1, 2, FAKE, None) == ARG
     assert s(FAKE + 4, 10, 0, FAKE, None) == ARG
     assert s(FAKE, 10, 0, None, None) == ARG

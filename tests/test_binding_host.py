@@ -88,6 +88,12 @@ def test_wrappers_pass_sizes_and_shards(rec):
     assert (opts.temperature, opts.scale_t2, opts.mask, opts.reduction) == (2.0, 1, mask.data_ptr(), 2)
     vj.vjsd_loss_forward(sh, 0.25, opts, part, stats, kl, loss, torch.empty(1))
     vj.vjsd_loss_backward(shg, 0.25, opts, stats, kl, torch.empty(1), part)
+    vj.vjsd_forward_backward(shg, 0.25, g, part, stats, kl, loss)
+    vj.vjsd_loss_forward_backward(shg, 0.25, opts, torch.empty(1), part, stats, kl, loss,
+                                  torch.empty(1))
+    with pytest.raises(ValueError):  # per-token losses need N upstream gradients
+        vj.vjsd_loss_forward_backward(shg, 0.25, abi.loss_opts(N), torch.empty(1), part, stats,
+                                      kl, loss)
     with pytest.raises(ValueError):  # a per-token backward needs N upstream gradients
         vj.vjsd_loss_backward(shg, 0.25, abi.loss_opts(N), stats, kl, torch.empty(1), part)
     with pytest.raises(ValueError):
@@ -95,10 +101,13 @@ def test_wrappers_pass_sizes_and_shards(rec):
     names = [c[0] for c in rec.calls]
     assert names == ["vjsd_stats", "vjsd_merge", "vjsd_fwd", "vjsd_forward", "vjsd_bwd", "vkl_fwd", "vkl_bwd",
                      "ventropy_fwd", "ventropy_bwd", "vlogprobs_fwd", "vlogprobs_bwd",
-                     "vjsd_loss_forward", "vjsd_loss_backward"]
+                     "vjsd_loss_forward", "vjsd_loss_backward", "vjsd_forward_backward",
+                     "vjsd_loss_forward_backward"]
     args = dict(rec.calls)
     assert args["vjsd_stats"][1:5] == (3, N, 2, 3)
     assert args["vjsd_fwd"][5] == 0.25 and args["vjsd_bwd"][6] == 0.25
+    fb = args["vjsd_forward_backward"]
+    assert fb[1:6] == (3, N, 2, 0.25, g.data_ptr()) and fb[9] == loss.data_ptr()
     assert args["vlogprobs_fwd"][4:8] == (V, ids.data_ptr(), 3, -100)
     for name, a in rec.calls:  # every pointer argument is set
         assert all(v is not None for v in a if not isinstance(v, (int, float))), name
@@ -123,6 +132,14 @@ def test_autograd_ops_marshal_forward_and_backward(rec):
         functional.jsd_loss(s, t, 0.5, mask=torch.ones(3, dtype=torch.bool))
     with pytest.raises(ValueError):
         functional.jsd_loss(s, t, 0.5, temperature=0.0)
+    # gradients in the forward: one call, then one scale per wanted gradient
+    n0 = len(rec.calls)
+    dl = functional.jsd_loss(s, t.detach(), 0.5, reduction="sum", grad_in_forward=True)
+    dl.backward()
+    assert [c[0] for c in rec.calls[n0:]] == ["vjsd_loss_forward_backward", "vlin_scale"]
+    assert rec.calls[n0 + 1][1][1:3] == (s.numel(), 0)  # the student gradient, fp32
+    with pytest.raises(ValueError):
+        functional.jsd_loss(s, t, 0.5, reduction="none", grad_in_forward=True)
     e = functional.entropy([s[:, :4], s[:, 4:]])
     assert e.shape == (4,)
     lp = functional.logprobs(s, torch.tensor([0, 1, 2, -100]))

@@ -10,8 +10,8 @@ checked against the fp64 oracle.  Cases covered:
 - gradient views at the inputs' offset inside 16 bytes and at another one;
 - one gradient or both;
 - masks and undefined rows, and the loss options;
-- the cases that run the two calls: beta = 0 / 1, several shards, and register-held
-  rows whose gradient views are not aligned.
+- the cases that run the two calls: beta = 0 / 1, several shards, a token mask, and
+  register-held rows whose gradient views are not aligned.
 """
 import numpy as np
 import pytest
@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from parity import assert_grads, assert_values, sample_rows
+from parity import assert_grads, assert_values, sample_rows, ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -189,7 +189,7 @@ def test_masked_tokens_and_undefined_rows(dtype, V):
 @pytest.mark.parametrize("opts", [
     dict(temperature=2.0), dict(temperature=0.7, scale_t2=True),
     dict(mask=True, reduction="sum"), dict(mask=True, reduction="mean", temperature=1.5),
-    dict(reduction="mean")])
+    dict(reduction="mean"), dict(reduction="sum", temperature=3.0, scale_t2=True)])
 def test_loss_options(V, opts):
     b = synth.draw("full_vocab", device="cuda", N=32, V=V)
     opts = dict(opts)
@@ -260,3 +260,59 @@ def test_empty_batch_and_bad_arguments():
         v.vjsd_forward_backward(sh, 1.5, g, part, st, kl, loss)
     with pytest.raises(v.VjsdError):
         v.vjsd_forward_backward(sh, float("nan"), g, part, st, kl, loss)
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 16032), (torch.bfloat16, 151936),
+                                     (torch.float16, 37984), (torch.float32, 20000)])
+@pytest.mark.parametrize("reduction,upstream", [("mean", 1.0), ("sum", 0.5), ("mean", 4.0)])
+def test_autograd_loss_with_gradients_in_the_forward(dtype, V, reduction, upstream):
+    """jsd_loss(grad_in_forward=True): the loss and, for upstream gradients 1 and powers
+    of two (which scale exactly), the gradients bit-identical to the default autograd
+    path.  fp16 gradients reach the subnormal range (below 2^-14), where a power of two
+    rounds again: there the two paths may differ by one rounding of the output."""
+    v = vj()
+    b = synth.draw("full_vocab", device="cuda", N=24, V=V, dtype=dtype)
+    res = []
+    for gif in (False, True):
+        s = b.s.clone().requires_grad_()
+        t = b.t.clone().requires_grad_()
+        loss = v.jsd_loss(s, t, 0.4, temperature=1.5, scale_t2=True, reduction=reduction,
+                          grad_in_forward=gif)
+        (loss * upstream).backward()
+        torch.cuda.synchronize()
+        res.append((loss.detach(), s.grad, t.grad))
+    same_bits(res[0][0], res[1][0], "loss")
+    for a, c, what in zip(res[0][1:], res[1][1:], ("d/ds", "d/dt")):
+        if dtype == torch.float16 and upstream != 1.0:
+            a64, c64 = a.double().cpu().numpy(), c.double().cpu().numpy()
+            err = np.abs(a64 - c64)
+            assert np.all(err <= ulp(a64, dtype) + 2.0 ** -24), (what, float(err.max()))
+        else:
+            same_bits(a, c, what)
+
+
+def test_autograd_loss_with_gradients_in_the_forward_other_scales_and_masks():
+    """An upstream gradient that is not a power of two rounds twice (the unit gradient,
+    then the product): within the oracle's bound in fp32; a mask (two calls inside)
+    and teacher-only gradients go through the same op."""
+    v = vj()
+    b = synth.draw("robust", device="cuda", N=40, V=3000)
+    mask = torch.rand(40, device="cuda") > 0.4
+    s = b.s.clone().requires_grad_()
+    t = b.t.clone().requires_grad_()
+    loss = v.jsd_loss(s, t, 0.7, temperature=2.0, mask=mask, reduction="mean",
+                      grad_in_forward=True)
+    (loss * 0.3).backward()
+    torch.cuda.synchronize()
+    ref = oracle.jsd_loss(b.s.cpu(), b.t.cpu(), 0.7, temperature=2.0,
+                          mask=mask.cpu().numpy(), reduction="mean", grad=0.3)
+    assert_values(loss.detach().cpu().reshape(1), np.array([ref["out"]]), torch.float32, "loss")
+    assert_grads(s.grad.cpu(), ref["gs"], torch.float32, "d/ds")
+    assert_grads(t.grad.cpu(), ref["gt"], torch.float32, "d/dt")
+    t2 = b.t.clone().requires_grad_()
+    l2 = v.jsd_loss(b.s, t2, 0.7, reduction="sum", grad_in_forward=True)
+    l2.backward()
+    r2 = oracle.jsd_loss(b.s.cpu(), b.t.cpu(), 0.7, reduction="sum", grad=1.0)
+    assert_grads(t2.grad.cpu(), r2["gt"], torch.float32, "d/dt")
+    with pytest.raises(RuntimeError):
+        l2.backward()  # the stored gradients were consumed

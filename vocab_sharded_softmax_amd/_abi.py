@@ -561,8 +561,8 @@ def vljsd(student: LinHead, teacher: LinHead, N: int, V: int, beta: float, opts:
 
 
 def vlin_scale(x: torch.Tensor, g: torch.Tensor, stream=None) -> None:
-    """x *= g[0] in place (x contiguous fp32 or bf16, g a GPU float32 scalar)."""
-    if x.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("x must be float32 or bfloat16")
+    """x *= g[0] in place (x contiguous fp32, fp16 or bf16, g a GPU float32 scalar)."""
+    if x.dtype not in DTYPES:
+        raise ValueError("x must be float32, float16 or bfloat16")
     _check(lib.vlin_scale(_ptr(x, name="x"), x.numel(), DTYPES[x.dtype],
                           _ptr(g, torch.float32, 1, "g"), _stream(stream)))

@@ -211,7 +211,8 @@ hipError_t launch_sum_partials(const float *part, int S, int64_t stride, int64_t
 // elements, bases 16-byte aligned
 hipError_t launch_transpose16(const uint16_t *src, int64_t lds, int64_t R, int64_t C,
                               uint16_t *dst, int64_t ldd, hipStream_t st);
-// p[i] *= g[0] over n values of dtype 0 (fp32) or 2 (bf16); p 16-byte aligned
+// p[i] *= g[0] over n values of dtype 0 (fp32), 1 (fp16) or 2 (bf16); p 16-byte aligned;
+// nothing is read or written past g[0] when g[0] == 1
 hipError_t launch_scale(int dtype, void *p, int64_t n, const float *g, hipStream_t st);
 
 }  // namespace vjsd

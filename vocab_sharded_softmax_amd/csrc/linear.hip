@@ -1,6 +1,7 @@
-// linear.hip -- the element-wise helper of the fused-linear loss: scaling gradients
-// computed for a unit upstream gradient by the actual one (a device scalar), so the
-// caller's backward needs no host synchronisation.
+// linear.hip -- the element-wise helper of the losses that compute their gradients in
+// the forward (the fused-linear loss, the distillation loss with its gradients in the
+// forward): scaling gradients computed for a unit upstream gradient by the actual one (a
+// device scalar), so the caller's backward needs no host synchronisation.
 #include "kernels.hpp"
 
 namespace vjsd {
@@ -12,6 +13,7 @@ template <class D>
 __global__ __launch_bounds__(SCALE_BLOCK) void k_scale(typename D::T *p, int64_t n,
                                                        const float *__restrict__ g) {
     const float s = g[0];
+    if (s == 1.0f) return;  // x * 1 is x in every format: nothing to read or write
     const int64_t nv = n / D::VEC;
     const int64_t stride = (int64_t)gridDim.x * SCALE_BLOCK;
     for (int64_t v = (int64_t)blockIdx.x * SCALE_BLOCK + threadIdx.x; v < nv; v += stride) {
@@ -140,6 +142,9 @@ hipError_t launch_scale(int dtype, void *p, int64_t n, const float *g, hipStream
     if (dtype == 0)
         hipLaunchKernelGGL(k_scale<F32>, dim3(blocks), dim3(SCALE_BLOCK), 0, st,
                            static_cast<float *>(p), n, g);
+    else if (dtype == 1)
+        hipLaunchKernelGGL(k_scale<F16>, dim3(blocks), dim3(SCALE_BLOCK), 0, st,
+                           static_cast<typename F16::T *>(p), n, g);
     else
         hipLaunchKernelGGL(k_scale<BF16>, dim3(blocks), dim3(SCALE_BLOCK), 0, st,
                            static_cast<typename BF16::T *>(p), n, g);

@@ -314,9 +314,55 @@ def jsd(student, teacher, beta: float = 0.5, *, split=None) -> torch.Tensor:
     return _JSD.apply(beta, None if split is None else tuple(split), ns, *s, *t)
 
 
+class _JSDLossInForward(torch.autograd.Function):
+    """jsd_loss of a reduced (scalar) loss with its gradients computed in the forward, in
+    one call (vjsd_loss_forward_backward for a unit upstream gradient); the backward
+    scales them by the actual upstream gradient in place, which leaves them untouched
+    on the device when it is exactly 1."""
+
+    @staticmethod
+    def forward(ctx, beta, temperature, scale_t2, reduction, mask, split, n_shards, *tensors):
+        half = len(tensors) // 2
+        s = _unpack(n_shards, tensors[:half])
+        t = _unpack(n_shards, tensors[half:])
+        need = ctx.needs_input_grad[7:]
+        want_s, want_t = any(need[:half]), any(need[half:])
+        gs = _grads_like(s, bool(n_shards)) if want_s else None
+        gt = _grads_like(t, bool(n_shards)) if want_t else None
+        sh = ShardSet(s, t, widths=split, gs=gs, gt=gt)
+        dev = (s[0] if n_shards else s).device
+        N, S = sh.N, sh.S
+        opts = _abi.loss_opts(N, temperature, scale_t2, mask, reduction)
+        part = _abi.new_part(N, S, dev)
+        stats = torch.empty((N, 4), dtype=torch.float64, device=dev)
+        kl = torch.empty((N, 2), dtype=torch.float32, device=dev)
+        rows = torch.empty(sh.lead_shape, dtype=torch.float32, device=dev)
+        out = torch.empty((), dtype=torch.float32, device=dev)
+        one = torch.ones(1, dtype=torch.float32, device=dev)
+        _abi.vjsd_loss_forward_backward(sh, beta, opts, one, part, stats, kl, rows, out)
+        ctx.grads = (_flat(gs) if want_s else [None] * half, _flat(gt) if want_t else [None] * half)
+        ctx.used = False
+        return out
+
+    @staticmethod
+    @once_differentiable
+    def backward(ctx, gout):
+        if ctx.used:
+            raise RuntimeError("jsd_loss(grad_in_forward=True): the backward scales its stored "
+                               "gradients in place and can run only once")
+        ctx.used = True
+        g = gout.reshape(-1)[:1].to(torch.float32).contiguous()
+        out_s, out_t = ctx.grads
+        ctx.grads = None
+        for x in (*out_s, *out_t):
+            if x is not None:
+                _abi.vlin_scale(x, g)
+        return (None, None, None, None, None, None, None, *out_s, *out_t)
+
+
 def jsd_loss(student, teacher, beta: float = 0.5, *, temperature: float = 1.0,
              scale_t2: bool = False, mask=None, reduction: str = "mean",
-             split=None) -> torch.Tensor:
+             split=None, grad_in_forward: bool = False) -> torch.Tensor:
     """Distillation loss around the per-token JSD, fused into its passes.
 
     Both logits are divided by ``temperature`` in registers (no fp32 copies); with
@@ -327,6 +373,13 @@ def jsd_loss(student, teacher, beta: float = 0.5, *, temperature: float = 1.0,
     of this to the caller [JSD-PR, Changes]; its teacher-cache caller divides by the
     temperature in fp32 first and keeps the token mean and T^2 scaling
     (DeepSpeedExamples PR #1019).
+
+    ``grad_in_forward`` (a "sum" or "mean" loss only): the forward computes the
+    gradients too, in one call with the loss (vjsd_loss_forward_backward, one launch
+    per row set for one shard without a mask); the backward multiplies them by the
+    upstream gradient in place, a device-side no-op when it is exactly 1 (a plain
+    ``loss.backward()``).  The gradients are held from the forward on, and the backward
+    can run once.
     """
     beta = float(beta)
     if not (0.0 <= beta <= 1.0):
@@ -348,8 +401,14 @@ def jsd_loss(student, teacher, beta: float = 0.5, *, temperature: float = 1.0,
         m = mask.reshape(-1)
         m = m.view(torch.uint8) if m.dtype == torch.bool else m.to(torch.uint8)
         m = m.contiguous()
-    return _JSDLoss.apply(beta, temperature, bool(scale_t2), reduction, m,
-                          None if split is None else tuple(split), ns, *s, *t)
+    fn = _JSDLoss
+    if grad_in_forward:
+        if reduction == "none":
+            raise ValueError("grad_in_forward needs a reduced loss ('sum' or 'mean'): "
+                             "per-token upstream gradients are not known in the forward")
+        fn = _JSDLossInForward
+    return fn.apply(beta, temperature, bool(scale_t2), reduction, m,
+                    None if split is None else tuple(split), ns, *s, *t)
 
 
 def kl_div(student, teacher, reverse: bool = False, *, split=None) -> torch.Tensor:
