@@ -228,20 +228,21 @@ def test_cases_that_run_the_two_calls(beta, widths):
     assert_grads(res["gt"].cpu(), ref["gt"], torch.float32, "d/dt")
 
 
-@pytest.mark.parametrize("name", ["full_vocab", "tp8_shard"])
-def test_full_size(name):
-    """The step's sizes (8192 x 151936 bf16, two sweeps; 8192 x 16032 bf16, register-held
-    rows): every output bit-identical to the two calls, sampled rows against the
-    oracle."""
+@pytest.mark.parametrize("name,beta", [("full_vocab", 0.1), ("full_vocab", 0.5),
+                                       ("full_vocab", 0.9), ("tp8_shard", 0.5)])
+def test_full_size(name, beta):
+    """The route and sizes the benchmark times (8192 x 151936 bf16 at each of its betas,
+    two sweeps; 8192 x 16032 bf16, register-held rows), with the workload's own upstream
+    gradient: every output bit-identical to the two calls, sampled rows (the first and
+    last among them) against the oracle."""
     b = synth.draw(name, device="cuda")
-    gout = torch.rand(b.s.shape[0], device="cuda") + 0.5
-    one = run(b.s, b.t, 0.5, gout, fused=True)
-    two = run(b.s, b.t, 0.5, gout, fused=False)
+    one = run(b.s, b.t, beta, b.gout, fused=True)
+    two = run(b.s, b.t, beta, b.gout, fused=False)
     assert_same(one, two)
     del two
     torch.cuda.empty_cache()
     rows = sample_rows(b.s.shape[0], 6, seed=17, must=(4095, 4096))
-    check_oracle(b.s, b.t, 0.5, gout, one, rows=rows)
+    check_oracle(b.s, b.t, beta, b.gout, one, rows=rows)
 
 
 def test_empty_batch_and_bad_arguments():
