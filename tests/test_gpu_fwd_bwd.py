@@ -317,3 +317,39 @@ def test_autograd_loss_with_gradients_in_the_forward_other_scales_and_masks():
     assert_grads(t2.grad.cpu(), r2["gt"], torch.float32, "d/dt")
     with pytest.raises(RuntimeError):
         l2.backward()  # the stored gradients were consumed
+
+
+@pytest.mark.parametrize("V", [16032, 50000])
+def test_causal_shift_views(V):
+    """[B, T-1, V] slices of [B, T, V] tensors (rows through a batch stride, as the pages'
+    callers shift logits against labels), with gradients into [B, T-1, V] slices of
+    their own: the one call against the two calls bit for bit and against the oracle."""
+    v = vj()
+    B, T = 3, 9
+    b = synth.draw("full_vocab", device="cuda", N=B * T, V=V)
+    s = b.s.reshape(B, T, V)[:, :-1, :]
+    t = b.t.reshape(B, T, V)[:, 1:, :]
+    N = B * (T - 1)
+    gout = torch.rand(N, device="cuda") + 0.5
+    res = []
+    for fused in (True, False):
+        gbuf_s = torch.full((B, T, V), NAN, dtype=s.dtype, device="cuda")
+        gbuf_t = torch.full((B, T, V), NAN, dtype=s.dtype, device="cuda")
+        gs, gt = gbuf_s[:, :-1, :], gbuf_t[:, 1:, :]
+        sh = v.ShardSet(s, t, gs=gs, gt=gt)
+        part = v.new_part(N, 1, "cuda")
+        st = torch.full((N, 4), NAN, dtype=torch.float64, device="cuda")
+        kl = torch.full((N, 2), NAN, device="cuda")
+        lo = torch.full((N,), NAN, device="cuda")
+        if fused:
+            v.vjsd_forward_backward(sh, 0.3, gout, part, st, kl, lo)
+        else:
+            v.vjsd_forward(sh, 0.3, part, st, kl, lo)
+            v.vjsd_bwd(sh, st, kl, 0.3, gout, part)
+        torch.cuda.synchronize()
+        res.append(dict(stats=st, kl=kl, loss=lo, gs=gs.reshape(N, V), gt=gt.reshape(N, V),
+                        out=torch.zeros(1, device="cuda")))
+        # the rows outside the views are never written
+        assert torch.isnan(gbuf_s[:, -1, :]).all() and torch.isnan(gbuf_t[:, 0, :]).all()
+    assert_same(res[0], res[1])
+    check_oracle(s.reshape(N, V), t.reshape(N, V), 0.3, gout, res[0], rows=np.array([0, 7, 8, N - 1]))
