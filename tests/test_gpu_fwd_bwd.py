@@ -251,6 +251,12 @@ def test_empty_batch_and_bad_arguments():
     e = torch.empty((0, 1000), dtype=b.s.dtype, device="cuda")
     r = run(e, e.clone(), 0.5, torch.empty(0, device="cuda"))
     assert r["loss"].numel() == 0
+    # one shard of width 0: every row undefined (NaN loss), nothing to write, as two calls
+    z = torch.empty((4, 0), dtype=b.s.dtype, device="cuda")
+    one = run(z, z.clone(), 0.5, torch.ones(4, device="cuda"), fused=True)
+    two = run(z, z.clone(), 0.5, torch.ones(4, device="cuda"), fused=False)
+    assert torch.isnan(one["loss"]).all()
+    assert_same(one, two)
     sh = v.ShardSet(b.s, b.t, gs=torch.empty_like(b.s))
     part = v.new_part(4, 1, "cuda")
     st = torch.empty((4, 4), dtype=torch.float64, device="cuda")
