@@ -97,8 +97,11 @@ __device__ __forceinline__ void bwd_constants(int mode, const RowConst &k, const
 
 // The element op of the gradient sweeps: both gradients of NV vectors (or single
 // elements) of W values.  DG: storage of the gradients (the input's, or bf16 for fp32
-// input: the logit gradient the fused-linear products consume).
-template <class D, int MODE, bool WS, bool WT, class DG = D>
+// input: the logit gradient the fused-linear products consume).  CLAMP = false drops the
+// U_FLOOR clamps, for rows whose every logit lies within FAST_RANGE of its maximum:
+// there u >= -FAST_RANGE > U_FLOOR, the clamps return u unchanged and the results are
+// the same bit for bit.
+template <class D, int MODE, bool WS, bool WT, class DG = D, bool CLAMP = true>
 struct OpBwd {
     using T = typename D::T;
     using TG = typename DG::T;
@@ -132,8 +135,10 @@ struct OpBwd {
             float os[W], ot[W];
 #pragma unroll
             for (int i = 0; i < W; ++i) {
-                const float us = fmaxf(fmaf(x[j][i], ks, -cs), U_FLOOR);
-                const float ut = fmaxf(fmaf(y[j][i], ks, -ct), U_FLOOR);
+                const float us = CLAMP ? fmaxf(fmaf(x[j][i], ks, -cs), U_FLOOR)
+                                       : fmaf(x[j][i], ks, -cs);
+                const float ut = CLAMP ? fmaxf(fmaf(y[j][i], ks, -ct), U_FLOOR)
+                                       : fmaf(y[j][i], ks, -ct);
                 const float es = ex2(us), et = ex2(ut);
                 if constexpr (MODE == INTERIOR) {
                     const float L = lg2(fmaf(bf, et, fmaf(gam, es, W_FLOOR)));
