@@ -224,15 +224,16 @@ def test_sharded_forward(dtype, widths):
     assert np.isfinite(np.delete(loss.numpy(), [5, 6])).all()
 
 
-# fp32 rows in 2 to 8 shards hold the widest shard's last five full steps (four in
-# registers, one in LDS: 40960 columns) on chip through the merge: the widest shard with
-# exactly five full steps (an empty prefix) and one column short of them (no hold); the
-# widest shard first, in the middle (after shards that leave it 4 bytes past a 16-byte
-# boundary: a scalar head before its held steps) and last; two equally wide shards (the
-# first holds); masked tokens inside the held columns
-@pytest.mark.parametrize("widths", [[40960, 100], [40959, 100], [60000, 0, 40000, 28256],
-                                    [3000, 50001, 7], [40960, 40960],
-                                    [1, 2, 45000, 3, 0, 5, 6, 7]])
+# fp32 rows in 2 to 8 shards hold the widest shard's last five or six full steps (four in
+# registers, one or two in LDS: 40960 or 49152 columns) on chip through the merge: the
+# widest shard with exactly five or six full steps (an empty prefix) and one column short
+# of them (no hold; one LDS step); the widest shard first, in the middle (after shards
+# that leave it 4 bytes past a 16-byte boundary: a scalar head before its held steps)
+# and last; two equally wide shards (the first holds); masked tokens inside the held
+# columns
+@pytest.mark.parametrize("widths", [[40960, 100], [40959, 100], [49152, 100], [49151, 100],
+                                    [60000, 0, 40000, 28256], [3000, 50001, 7],
+                                    [40960, 40960], [1, 2, 45000, 3, 0, 5, 6, 7]])
 def test_sharded_forward_held_steps(widths):
     V = sum(widths)
     b = synth.draw("robust", device="cuda", N=23, V=V)  # fp32
@@ -287,14 +288,17 @@ def test_sharded_forward_separate_tensors():
 
 # The two-sweep forward holds the statistics sweep's last full steps on chip (a step is
 # 512 lanes x 4 vectors: 16384 16-bit or 8192 fp32 columns; bf16 holds 2 steps, fp16 1,
-# fp32 5).  Widths where the held steps take the whole body (empty prefix and rest), one
-# column more or fewer, and rows 2 bytes past a 16-byte boundary (a scalar head before
-# the held body).
+# fp32 4 in registers and 1 or 2 in LDS, as many as the row has past the 4).  Widths
+# where the held steps take the whole body (empty prefix and rest), one column more or
+# fewer, and rows 2 bytes past a 16-byte boundary (a scalar head before the held body);
+# fp32 at 5 steps (one in LDS), between 5 and 6, and at 6 (two in LDS).
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 32768), (torch.bfloat16, 32769),
                                      (torch.bfloat16, 32767), (torch.bfloat16, 49160),
                                      (torch.float16, 16392), (torch.float16, 32768),
                                      (torch.float32, 40960), (torch.float32, 40964),
-                                     (torch.float32, 40959), (torch.float32, 57344)])
+                                     (torch.float32, 40959), (torch.float32, 45000),
+                                     (torch.float32, 49152), (torch.float32, 49156),
+                                     (torch.float32, 49151), (torch.float32, 57344)])
 def test_held_steps_boundaries(dtype, V):
     b = synth.draw("tiny", device="cuda", N=9, V=V + 9, dtype=dtype)
     check(b.s[:, :V], b.t[:, :V], 0.5)  # rows 16-byte aligned when V + 9 allows it

@@ -142,12 +142,14 @@ def test_one_gradient_or_none(want, V):
 
 
 # Held-step boundaries of the two sweeps (a step: 512 lanes x 4 vectors, 16384 16-bit or
-# 8192 fp32 columns), with rows 16-byte aligned, 2 bytes past a boundary (a scalar head),
-# and gradient views at the inputs' offset or 1 element off it.
+# 8192 fp32 columns; fp32 holds one LDS step from 40960 columns, two from 49152), with
+# rows 16-byte aligned, 2 bytes past a boundary (a scalar head), and gradient views at
+# the inputs' offset or 1 element off it.
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 49152), (torch.bfloat16, 49153),
                                      (torch.bfloat16, 49151), (torch.float16, 49160),
                                      (torch.float32, 40960), (torch.float32, 40964),
-                                     (torch.float32, 40959)])
+                                     (torch.float32, 40959), (torch.float32, 49152),
+                                     (torch.float32, 49156), (torch.float32, 49151)])
 @pytest.mark.parametrize("off", [0, 1])
 def test_held_steps_and_gradient_offsets(dtype, V, off):
     b = synth.draw("tiny", device="cuda", N=9, V=V + 9, dtype=dtype)

@@ -302,8 +302,9 @@ __global__ __launch_bounds__(B) void k_fwd_row(RowView sv, RowView tv, int64_t w
 constexpr int TWICE_BLK = 512;
 constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sweep step
 
-// Sweep steps held in registers, and one more (64 KiB per workgroup) in LDS for bf16 and
-// fp32.  Measured on MI355X (forward at 8192 x 151936 bf16 / 4096 x 128256 fp32):
+// Sweep steps held in registers, and in LDS (64 KiB per workgroup each) one more for
+// bf16 and up to two more for fp32.  Measured on MI355X (forward at 8192 x 151936 bf16 /
+// 4096 x 128256 fp32):
 //   bf16  1 step + LDS (125 VGPRs, two workgroups per CU): 1.35 -> 1.25 ms; 2 steps +
 //         LDS (247 VGPRs) 1.44 ms; asking the compiler for four waves per SIMD made it
 //         spill
@@ -311,11 +312,16 @@ constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sw
 //         slower, with 2 steps 1.39 ms
 //   fp32  4 steps + LDS (236 VGPRs, one workgroup per CU): 1.18 -> 0.99 ms; an fp32
 //         step holds half the columns of a 16-bit one, and holding more beat occupancy
-//         here (1 / 2 / 3 steps + LDS: 1.08 / 1.05 / 1.02 ms; 5 steps spilled)
+//         here (1 / 2 / 3 steps + LDS: 1.08 / 1.05 / 1.02 ms; 5 steps spilled).  The one
+//         workgroup per CU leaves LDS for a second step (128 KiB): forward 1.014-1.023 ->
+//         1.006-1.014 ms, forward and backward in one launch 2.265-2.268 -> 2.193-2.198
+//         ms (three alternating runs on one box)
 template <class D>
 constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 4 : 1; }
 template <class D>
-constexpr int lds_steps() { return std::is_same<D, F16>::value ? 0 : 1; }
+constexpr int lds_steps() {
+    return std::is_same<D, F16>::value ? 0 : sizeof(typename D::T) == 4 ? 2 : 1;
+}
 
 // The streamed part of k_fwd_twice's divergence sweep, continuing the sums `acc`
 // (t, s) of the held steps.
@@ -377,11 +383,14 @@ __device__ __forceinline__ void held_div(const u32x4 (&hs)[TW_U], const u32x4 (&
 }
 
 // The part of a row that the statistics sweep of k_fwd_twice keeps on chip: the last
-// HOLD + LHOLD full sweep steps of the row's 16-byte body, elements [P, Q) ([P, PR) in
-// LDS, [PR, Q) in registers).  Rows whose two inputs sit at different offsets inside 16
-// bytes (h == w), or that are too short, hold nothing and are swept whole.
+// HOLD + lh full sweep steps of the row's 16-byte body, elements [P, Q) ([P, PR) in LDS,
+// lh <= LHOLD steps, as many as the row has beyond the HOLD register steps; [PR, Q) in
+// registers).  Rows whose two inputs sit at different offsets inside 16 bytes (h == w),
+// or that are too short for the register steps and one LDS step, hold nothing and are
+// swept whole.
 struct TwiceSpan {
     int64_t h, P, PR, Q;
+    int lh;
     bool hold;
 };
 template <class D>
@@ -392,15 +401,16 @@ __device__ __forceinline__ TwiceSpan twice_span(int64_t w, int64_t h) {
     TwiceSpan sp;
     sp.h = h;
     const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
-    sp.hold = nfull >= HOLD + LHOLD;
-    sp.P = sp.hold ? h + (nfull - HOLD - LHOLD) * STEP * VEC : w;
-    sp.PR = sp.P + LHOLD * STEP * VEC;
+    sp.hold = nfull >= HOLD + (LHOLD > 0 ? 1 : 0);
+    sp.lh = sp.hold ? (int)(nfull - HOLD < LHOLD ? nfull - HOLD : LHOLD) : 0;
+    sp.P = sp.hold ? h + (nfull - HOLD - sp.lh) * STEP * VEC : w;
+    sp.PR = sp.P + sp.lh * STEP * VEC;
     sp.Q = sp.hold ? sp.PR + HOLD * STEP * VEC : w;
     return sp;
 }
 // The held steps: LDS (each lane's own vectors) and registers.
 template <class D>
-using LdsStep = u32x4[2][TW_U][lds_steps<D>() ? TWICE_BLK : 1];
+using LdsStep = u32x4[lds_steps<D>() ? lds_steps<D>() : 1][2][TW_U][lds_steps<D>() ? TWICE_BLK : 1];
 template <class D>
 using HeldRegs = u32x4[held_steps<D>()][TW_U];
 
@@ -429,18 +439,21 @@ __device__ __forceinline__ void twice_forward(const typename D::T *s, const type
     const bool hold = sp.hold;
     if (hold) {
         sweep<D, TW_U, true, TWICE_BLK>(s, t, P, h, o1);
-        if constexpr (LHOLD > 0) {
+#pragma unroll
+        for (int l = 0; l < LHOLD; ++l) {
+            if (l >= sp.lh) break;
             u32x4 ls[TW_U], lt[TW_U];
 #pragma unroll
             for (int u = 0; u < TW_U; ++u) {
-                const int64_t q = P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+                const int64_t q =
+                    P + ((int64_t)l * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
                 ls[u] = ld16<true>(s + q);
                 lt[u] = ld16<true>(t + q);
             }
 #pragma unroll
             for (int u = 0; u < TW_U; ++u) {
-                lds_step[0][u][threadIdx.x] = ls[u];
-                lds_step[1][u][threadIdx.x] = lt[u];
+                lds_step[l][0][u][threadIdx.x] = ls[u];
+                lds_step[l][1][u][threadIdx.x] = lt[u];
             }
             held_stats<D>(ls, lt, o1);
         }
@@ -499,12 +512,14 @@ __device__ __forceinline__ void twice_forward(const typename D::T *s, const type
             oh.set(k.mx, (float)beta, o.ks);
 #pragma unroll
             for (int j = 0; j < HOLD; ++j) held_div<D>(hs[j], ht[j], oh);
-            if constexpr (LHOLD > 0) {
+#pragma unroll
+            for (int l = 0; l < LHOLD; ++l) {
+                if (l >= sp.lh) break;
                 u32x4 ls[TW_U], lt[TW_U];
 #pragma unroll
                 for (int u = 0; u < TW_U; ++u) {
-                    ls[u] = lds_step[0][u][threadIdx.x];
-                    lt[u] = lds_step[1][u][threadIdx.x];
+                    ls[u] = lds_step[l][0][u][threadIdx.x];
+                    lt[u] = lds_step[l][1][u][threadIdx.x];
                 }
                 held_div<D>(ls, lt, oh);
             }
@@ -571,12 +586,13 @@ __device__ __forceinline__ void zero_grads(typename D::T *gs, typename D::T *gt,
 // launches (kernel time, two calls -> one call):
 //   two-sweep rows: waves per SIMD held at 4 for 16-bit inputs (128 VGPRs, two
 //     workgroups per CU as the forward alone; bf16 spills 12 bytes, fp16 68), 2 for
-//     fp32 (one workgroup per CU, 244 VGPRs); one vector per lane in flight in the
-//     gradient sweep (two: 8192 x 151936 bf16 2.82 against 2.75 ms).  8192 x 151936
-//     bf16: 2.83-2.87 -> 2.73-2.75 ms; 4096 x 151936 fp16: 1.45-1.46 -> 1.41-1.43 ms;
-//     4096 x 128256 fp32: 2.29-2.30 -> 2.29 ms, where the backward part runs at one
-//     workgroup per CU (reading the four register steps again instead of keeping
-//     them: 2.38-2.44 ms)
+//     fp32 (one workgroup per CU, 232 VGPRs); one vector per lane in flight in the
+//     gradient sweep (two: 8192 x 151936 bf16 2.82 against 2.75 ms; fp32 ran no faster
+//     with two or four, or with the next vector's loads issued before the current
+//     one's arithmetic).  8192 x 151936 bf16: 2.83-2.87 -> 2.73-2.75 ms; 4096 x 151936
+//     fp16: 1.45-1.46 -> 1.41-1.43 ms; 4096 x 128256 fp32: 2.27-2.29 -> 2.25 ms with two
+//     held LDS steps, where the backward part runs at one workgroup per CU (reading the
+//     four register steps again instead of keeping them: 2.38-2.44 ms)
 //   512-lane register rows: held to 128 VGPRs, two workgroups per CU (1024 x 37984
 //     bf16, student gradient: 0.0916 ms at 134 VGPRs and one workgroup per CU, 0.0815
 //     ms with a 20-byte spill; the two calls 0.092-0.096 ms); 8192 x 16032 bf16 (256
@@ -738,13 +754,16 @@ void k_fwdbwd_twice(RowView sv, RowView tv, RowMView gsv, RowMView gtv, int64_t 
             op.template run<1, VEC>(a, b, c);
         }
     }
-    if constexpr (LHOLD > 0) {
+#pragma unroll
+    for (int l = 0; l < LHOLD; ++l) {
+        if (l >= sp.lh) break;
 #pragma unroll
         for (int u = 0; u < TW_U; ++u) {
             float a[1][VEC], b[1][VEC];
-            widen<D>(lds_step[0][u][threadIdx.x], a[0]);
-            widen<D>(lds_step[1][u][threadIdx.x], b[0]);
-            const int64_t c[1] = {sp.P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC};
+            widen<D>(lds_step[l][0][u][threadIdx.x], a[0]);
+            widen<D>(lds_step[l][1][u][threadIdx.x], b[0]);
+            const int64_t c[1] = {
+                sp.P + ((int64_t)l * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC};
             op.template run<1, VEC>(a, b, c);
         }
     }
@@ -763,17 +782,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Steps of the widest shard's slice that k_fwd_shards holds on chip, as k_fwd_twice
-// holds a row's: fp32 four in registers and one in LDS (232 VGPRs, one workgroup per
-// CU, as the fp32 two-sweep kernel), 16-bit formats none.  Measured on MI355X (4096 x
-// 128256 fp32 in shards 60000/0/40000/28256; 8192 x 151936 bf16 in 40000/40000/0/71936):
-// fp32 1.16 -> 1.03 ms with the held steps, the merge behind one barrier and the sweeps'
-// partial steps loaded at once (one shard: 1.00 ms); a bf16 LDS step ran 6 % slower
-// (1.37 -> 1.45 ms), and a register step in the 16-bit kernels, live across the loop
-// over shards, costs them their second workgroup per CU.
+// holds a row's: fp32 four in registers and up to two in LDS (one workgroup per CU, as
+// the fp32 two-sweep kernel), 16-bit formats none.  Measured on MI355X (4096 x 128256
+// fp32 in shards 60000/0/40000/28256; 8192 x 151936 bf16 in 40000/40000/0/71936): fp32
+// 1.16 -> 1.03 ms with four register steps and one LDS step, the merge behind one
+// barrier and the sweeps' partial steps loaded at once (one shard: 1.00 ms); a bf16 LDS
+// step ran 6 % slower (1.37 -> 1.45 ms), and a register step in the 16-bit kernels, live
+// across the loop over shards, costs them their second workgroup per CU.
 template <class D>
 constexpr int shard_held_steps() { return sizeof(typename D::T) == 4 ? 4 : 0; }
 template <class D>
-constexpr int shard_lds_steps() { return sizeof(typename D::T) == 4 ? 1 : 0; }
+constexpr int shard_lds_steps() { return sizeof(typename D::T) == 4 ? 2 : 0; }
 
 // Several logical shards of a row, one launch: the workgroup sweeps each shard's slice
 // for that shard's (max, sum-exp) pair of each input, merges the pairs in shard order
@@ -821,24 +840,27 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // the widest shard (the first of equals) holds its statistics sweep's last full
-    // steps, [P, Q) of its slice ([P, PR) in LDS, [PR, Q) in registers), when it has
-    // that many
+    // steps, [P, Q) of its slice ([P, PR) in LDS, lh of them, [PR, Q) in registers),
+    // when it has the register steps and one LDS step
     int qh = -1;
     for (int q = 0; q < sr.S; ++q)
         if (sr.w[q] > 0 && (qh < 0 || sr.w[q] > sr.w[qh])) qh = q;
     bool hold = false;
+    int lh = 0;
     int64_t P = 0, PR = 0, Q = 0;
     if (qh >= 0 && HOLD + LHOLD > 0) {
         const int64_t w = sr.w[qh];
         const T *s = row_ptr<T>(sr.s[qh], r), *t = row_ptr<T>(sr.t[qh], r);
         const int64_t h = head_len<T>(w, s, t);
         const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
-        hold = nfull >= HOLD + LHOLD;
-        P = hold ? h + (nfull - HOLD - LHOLD) * STEP * VEC : w;
-        PR = P + LHOLD * STEP * VEC;
+        hold = nfull >= HOLD + (LHOLD > 0 ? 1 : 0);
+        lh = hold ? (int)(nfull - HOLD < LHOLD ? nfull - HOLD : LHOLD) : 0;
+        P = hold ? h + (nfull - HOLD - lh) * STEP * VEC : w;
+        PR = P + lh * STEP * VEC;
         Q = hold ? PR + HOLD * STEP * VEC : w;
     }
-    __shared__ u32x4 lds_step[2][TW_U][LHOLD ? TWICE_BLK : 1];  // each lane's own vectors
+    // each lane's own vectors
+    __shared__ u32x4 lds_step[LHOLD ? LHOLD : 1][2][TW_U][LHOLD ? TWICE_BLK : 1];
     u32x4 hs[HOLD ? HOLD : 1][TW_U], ht[HOLD ? HOLD : 1][TW_U];
     for (int q = 0; q < sr.S; ++q) {
         OpStats<3, true> o1(o.ks);
@@ -848,18 +870,21 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
             const int64_t h = head_len<T>(w, s, t);
             if (hold && q == qh) {
                 sweep<D, TW_U, true, TWICE_BLK>(s, t, P, h, o1);
-                if constexpr (LHOLD > 0) {
+#pragma unroll
+                for (int l = 0; l < LHOLD; ++l) {
+                    if (l >= lh) break;
                     u32x4 ls[TW_U], lt[TW_U];
 #pragma unroll
                     for (int u = 0; u < TW_U; ++u) {
-                        const int64_t c = P + ((int64_t)threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
+                        const int64_t c =
+                            P + ((int64_t)l * STEP + threadIdx.x + (int64_t)u * TWICE_BLK) * VEC;
                         ls[u] = ld16<true>(s + c);
                         lt[u] = ld16<true>(t + c);
                     }
 #pragma unroll
                     for (int u = 0; u < TW_U; ++u) {
-                        lds_step[0][u][threadIdx.x] = ls[u];
-                        lds_step[1][u][threadIdx.x] = lt[u];
+                        lds_step[l][0][u][threadIdx.x] = ls[u];
+                        lds_step[l][1][u][threadIdx.x] = lt[u];
                     }
                     held_stats<D>(ls, lt, o1);
                 }
@@ -943,12 +968,14 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
             oh.set(k.mx, (float)beta, o.ks);
 #pragma unroll
             for (int j = 0; j < HOLD; ++j) held_div<D>(hs[j], ht[j], oh);
-            if constexpr (LHOLD > 0) {
+#pragma unroll
+            for (int l = 0; l < LHOLD; ++l) {
+                if (l >= lh) break;
                 u32x4 ls[TW_U], lt[TW_U];
 #pragma unroll
                 for (int u = 0; u < TW_U; ++u) {
-                    ls[u] = lds_step[0][u][threadIdx.x];
-                    lt[u] = lds_step[1][u][threadIdx.x];
+                    ls[u] = lds_step[l][0][u][threadIdx.x];
+                    lt[u] = lds_step[l][1][u][threadIdx.x];
                 }
                 held_div<D>(ls, lt, oh);
             }
