@@ -1,4 +1,4 @@
-"""Facts the pages print (tests/golden/pages_facts.json), checked against this build."""
+"""Facts the pages print (tests/golden/pages_facts.json), checked against this library."""
 import json
 import os
 
