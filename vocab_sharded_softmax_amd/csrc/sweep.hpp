@@ -99,6 +99,76 @@ __device__ __forceinline__ void sweep(const typename D::T *__restrict__ s,
     }
 }
 
+// The same elements as sweep, in the opposite order: the scalar tail first, then each
+// lane's 16-byte vectors from its last down to its first (its top n % U vectors
+// together, then groups of U), then the scalar head.  A sweep that follows a forward
+// one starts where that one ended.
+template <class D, int U, bool TWO, int BLK = BLOCK, bool STREAM = false, class Op>
+__device__ __forceinline__ void sweep_rev(const typename D::T *__restrict__ s,
+                                          const typename D::T *__restrict__ t, int64_t w,
+                                          int64_t h, Op &op) {
+    using T = typename D::T;
+    constexpr int VEC = D::VEC;
+    constexpr int BLOCK = BLK;
+    const int tid = threadIdx.x;
+    const int64_t nv = (w - h) / VEC;
+    for (int64_t i = h + nv * VEC + tid; i < w; i += BLOCK) {
+        float a[1][1], b[1][1] = {{0.0f}};
+        const int64_t c[1] = {i};
+        a[0][0] = load1<D>(s + i);
+        if (TWO) b[0][0] = load1<D>(t + i);
+        op.template run<1, 1>(a, b, c);
+    }
+    const T *sb = s + h;
+    const T *tb = TWO ? t + h : s + h;
+    const int64_t nl = nv > tid ? (nv - tid + BLOCK - 1) / BLOCK : 0;  // this lane's vectors
+    const int64_t r = nl % U;
+    int64_t j0 = nl - r;  // first of the top r
+    if (U > 1 && r > 0) {
+        u32x4 ra[U > 1 ? U - 1 : 1], rb[U > 1 ? U - 1 : 1];
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u) {
+            if (u < r) {
+                const int64_t v = tid + (j0 + u) * BLOCK;
+                ra[u] = ld16<STREAM>(sb + v * VEC);
+                if (TWO) rb[u] = ld16<STREAM>(tb + v * VEC);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U - 1; ++u) {
+            if (u < r) {
+                float a[1][VEC], b[1][VEC];
+                widen<D>(ra[u], a[0]);
+                if (TWO) widen<D>(rb[u], b[0]);
+                else
+#pragma unroll
+                    for (int i = 0; i < VEC; ++i) b[0][i] = 0.0f;
+                const int64_t c[1] = {h + (tid + (j0 + u) * BLOCK) * VEC};
+                op.template run<1, VEC>(a, b, c);
+            }
+        }
+    }
+    for (j0 -= U; j0 >= 0; j0 -= U) {
+        float a[U][VEC], b[U][VEC];
+        int64_t c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t q = (tid + (j0 + u) * BLOCK) * VEC;
+            c[u] = h + q;
+            load_vec<D, STREAM>(sb + q, a[u]);
+            if (TWO) load_vec<D, STREAM>(tb + q, b[u]);
+        }
+        op.template run<U, VEC>(a, b, c);
+    }
+    for (int64_t i = tid; i < h; i += BLOCK) {
+        float a[1][1], b[1][1] = {{0.0f}};
+        const int64_t c[1] = {i};
+        a[0][0] = load1<D>(s + i);
+        if (TWO) b[0][0] = load1<D>(t + i);
+        op.template run<1, 1>(a, b, c);
+    }
+}
+
 // Writes n zeros of the storage format (head / 16-byte body / tail), BLK lanes; the
 // body with streaming stores.
 template <class D, int BLK>
