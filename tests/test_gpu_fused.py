@@ -287,7 +287,7 @@ def test_sharded_forward_separate_tensors():
 
 
 # The two-sweep forward holds the statistics sweep's last full steps on chip (a step is
-# 512 lanes x 4 vectors: 16384 16-bit or 8192 fp32 columns; bf16 holds 2 steps, fp16 1,
+# 512 lanes x 4 vectors: 16384 16-bit or 8192 fp32 columns; 16-bit formats hold 2 steps,
 # fp32 4 in registers and 1 or 2 in LDS, as many as the row has past the 4).  Widths
 # where the held steps take the whole body (empty prefix and rest), one column more or
 # fewer, and rows 2 bytes past a 16-byte boundary (a scalar head before the held body);
@@ -295,6 +295,7 @@ def test_sharded_forward_separate_tensors():
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 32768), (torch.bfloat16, 32769),
                                      (torch.bfloat16, 32767), (torch.bfloat16, 49160),
                                      (torch.float16, 16392), (torch.float16, 32768),
+                                     (torch.float16, 32769), (torch.float16, 32767),
                                      (torch.float32, 40960), (torch.float32, 40964),
                                      (torch.float32, 40959), (torch.float32, 45000),
                                      (torch.float32, 49152), (torch.float32, 49156),

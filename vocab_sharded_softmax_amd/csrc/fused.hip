@@ -305,13 +305,16 @@ constexpr int TWICE_BLK = 512;
 constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sweep step
 
 // Sweep steps held in registers, and in LDS (64 KiB per workgroup each) one more for
-// bf16 and up to two more for fp32.  Measured on MI355X (forward at 8192 x 151936 bf16 /
-// 4096 x 128256 fp32):
+// 16-bit inputs and up to two more for fp32.  Measured on MI355X (forward at 8192 x
+// 151936 bf16 / 4096 x 151936 fp16 / 4096 x 128256 fp32):
 //   bf16  1 step + LDS (125 VGPRs, two workgroups per CU): 1.35 -> 1.25 ms; 2 steps +
 //         LDS (247 VGPRs) 1.44 ms; asking the compiler for four waves per SIMD made it
 //         spill
 //   fp16  1 step (126 VGPRs); with the LDS step it compiled to 167 VGPRs and ran 8 %
-//         slower, with 2 steps 1.39 ms
+//         slower, with 2 steps 1.39 ms; the LDS step with the kernel held to four
+//         waves per SIMD (128 VGPRs, a 68-byte spill) runs the forward as fast as
+//         without it and the one-launch forward and backward 1.375-1.381 -> 1.323-1.327
+//         ms (three alternating runs on one box)
 //   fp32  4 steps + LDS (236 VGPRs, one workgroup per CU): 1.18 -> 0.99 ms; an fp32
 //         step holds half the columns of a 16-bit one, and holding more beat occupancy
 //         here (1 / 2 / 3 steps + LDS: 1.08 / 1.05 / 1.02 ms; 5 steps spilled).  The one
@@ -322,7 +325,7 @@ template <class D>
 constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 4 : 1; }
 template <class D>
 constexpr int lds_steps() {
-    return std::is_same<D, F16>::value ? 0 : sizeof(typename D::T) == 4 ? 2 : 1;
+    return sizeof(typename D::T) == 4 ? 2 : 1;
 }
 
 // The streamed part of k_fwd_twice's divergence sweep, continuing the sums `acc`
@@ -545,6 +548,7 @@ __device__ __forceinline__ void twice_forward(const typename D::T *s, const type
 
 template <class D>
 __global__ __launch_bounds__(TWICE_BLK)
+__attribute__((amdgpu_waves_per_eu(sizeof(typename D::T) == 4 ? 2 : 4)))
 void k_fwd_twice(RowView sv, RowView tv, int64_t w, double beta, double *__restrict__ stats,
                  float *__restrict__ kl, float *__restrict__ loss, RowOpts o) {
     using T = typename D::T;
