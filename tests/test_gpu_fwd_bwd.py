@@ -147,6 +147,7 @@ def test_one_gradient_or_none(want, V):
 # the inputs' offset or 1 element off it.
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 49152), (torch.bfloat16, 49153),
                                      (torch.bfloat16, 49151), (torch.float16, 49160),
+                                     (torch.float16, 32768), (torch.float16, 32767),
                                      (torch.float32, 40960), (torch.float32, 40964),
                                      (torch.float32, 40959), (torch.float32, 49152),
                                      (torch.float32, 49156), (torch.float32, 49151)])
