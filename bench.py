@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -51,13 +52,17 @@ def log(*a):
 
 
 def sources_digest() -> str:
-    """Digest of every kernel source: committed counters are used only while it matches
-    the digest recorded with them."""
+    """Digest of every kernel source, comments and layout left out (the kernel sources
+    hold no comment markers inside string literals): committed counters are used only
+    while it matches the digest recorded with them."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                code = f.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
+            h.update(name.encode() + b"\0" + " ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -602,7 +602,8 @@ __device__ __forceinline__ void zero_grads(typename D::T *gs, typename D::T *gt,
 //     gradient sweep (two: 8192 x 151936 bf16 2.82 against 2.75 ms; fp32 ran no faster
 //     with two or four, or with the next vector's loads issued before the current
 //     one's arithmetic).  8192 x 151936 bf16: 2.83-2.87 -> 2.73-2.75 ms; 4096 x 151936
-//     fp16: 1.45-1.46 -> 1.41-1.43 ms; 4096 x 128256 fp32: 2.27-2.29 -> 2.25 ms with two
+//     fp16: 1.45-1.46 -> 1.41-1.43 ms (1.32-1.33 ms after the backward divergence
+//     sweep and the fp16 LDS step); 4096 x 128256 fp32: 2.27-2.29 -> 2.25 ms with two
 //     held LDS steps, where the backward part runs at one workgroup per CU (reading the
 //     four register steps again instead of keeping them: 2.38-2.44 ms)
 //   512-lane register rows: held to 128 VGPRs, two workgroups per CU (1024 x 37984
