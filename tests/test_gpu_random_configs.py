@@ -1,0 +1,146 @@
+"""Seeded random configurations of the JSD forward and backward: dtype, batch size, row
+width (register-held rows, two-sweep rows, ragged tails), the rows' offset inside 16
+bytes, logical shard splits, beta (endpoints and near them included), which gradients
+are wanted, tokens masked on both sides, undefined rows and zero upstream gradients.
+Each configuration runs the one call (vjsd_forward_backward) and the two calls
+(vjsd_forward + vjsd_bwd) on the same inputs: every output bit-identical, and sampled
+rows (first and last included) against the fp64 oracle.  The distillation-loss form
+(temperature, T^2, token mask, reduction) is drawn the same way.  The configurations
+are drawn once, from a fixed seed, so the list and its test names do not change between
+runs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import assert_grads, assert_values
+from test_gpu_fwd_bwd import assert_same, check_oracle, check_two_calls, run
+
+pytestmark = pytest.mark.gpu
+
+NINF = float("-inf")
+DTYPES = [torch.bfloat16, torch.float16, torch.float32]
+
+
+def _configs(n=40, seed=20261203):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = DTYPES[i % 3]
+        kind = rng.choice(["small", "register", "two_sweep"], p=[0.3, 0.35, 0.35])
+        if kind == "small":
+            V = int(rng.integers(1, 2000))
+        elif kind == "register":
+            V = int(rng.integers(2000, 20480 if dt == torch.float32 else 40960))
+        else:
+            V = int(rng.integers(41000, 140000))
+        N = int(rng.integers(1, max(2, min(33, 2_500_000 // V))))
+        off = int(rng.integers(0, 8))
+        u = rng.random()
+        beta = (0.0 if u < 0.1 else 1.0 if u < 0.2 else 1e-6 if u < 0.25
+                else 1.0 - 1e-6 if u < 0.3 else float(np.round(rng.random(), 3)))
+        S = 1 if rng.random() < 0.7 or V < 8 else int(rng.integers(2, 5))
+        widths = None
+        if S > 1:
+            cuts = np.sort(rng.choice(np.arange(1, V), size=S - 1, replace=False))
+            widths = [int(w) for w in np.diff(np.concatenate([[0], cuts, [V]]))]
+        want = [(True, True), (True, False), (False, True)][int(rng.integers(0, 3))]
+        mask = float(rng.choice([0.0, 0.0, 0.02, 0.3]))
+        undefined = bool(rng.random() < 0.2) and N > 1
+        zero_g = bool(rng.random() < 0.2)
+        out.append(dict(dtype=dt, N=N, V=V, off=off, beta=beta, widths=widths, want=want,
+                        mask=mask, undefined=undefined, zero_g=zero_g, seed=1000 + i))
+    return out
+
+
+CONFIGS = _configs()
+
+
+def _name(c):
+    w = "" if c["widths"] is None else f"-S{len(c['widths'])}"
+    return (f"{str(c['dtype'])[6:]}-N{c['N']}-V{c['V']}-o{c['off']}-b{c['beta']:g}{w}"
+            f"-g{int(c['want'][0])}{int(c['want'][1])}")
+
+
+@pytest.mark.parametrize("c", CONFIGS, ids=[_name(c) for c in CONFIGS])
+def test_random_config(c):
+    N, V, off = c["N"], c["V"], c["off"]
+    b = synth.draw("full_vocab", device="cuda", N=N, V=V + off, dtype=c["dtype"],
+                   seed=c["seed"])
+    s = b.s[:, off:off + V].clone() if c["mask"] or c["undefined"] else b.s[:, off:off + V]
+    t = b.t[:, off:off + V].clone() if c["mask"] or c["undefined"] else b.t[:, off:off + V]
+    if c["mask"] or c["undefined"]:
+        # clone() made the rows contiguous: take them back at the same offset
+        bs = torch.empty((N, V + off), dtype=s.dtype, device=s.device)
+        bt = torch.empty_like(bs)
+        bs[:, off:] = s
+        bt[:, off:] = t
+        s, t = bs[:, off:], bt[:, off:]
+    gen = torch.Generator(device="cuda").manual_seed(c["seed"])
+    if c["mask"]:
+        m = torch.rand((N, V), generator=gen, device="cuda") < c["mask"]
+        s.masked_fill_(m, NINF)  # the same tokens on both sides
+        t.masked_fill_(m, NINF)
+    if c["undefined"]:
+        s[N // 2] = NINF
+    gout = torch.rand(N, generator=gen, device="cuda") + 0.5
+    if c["zero_g"]:
+        gout[0] = 0.0
+    res, _ = check_two_calls(s, t, c["beta"], gout=gout, want=c["want"], widths=c["widths"])
+    rows = np.unique(np.array([0, N // 2, N - 1]))
+    check_oracle(s, t, c["beta"], gout, res, rows=rows, want=c["want"])
+
+
+def _loss_configs(n=20, seed=20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = DTYPES[i % 3]
+        V = int(rng.choice([int(rng.integers(100, 16384)), int(rng.integers(41000, 131072))]))
+        N = int(rng.integers(2, max(3, min(33, 2_000_000 // V))))
+        u = rng.random()
+        beta = 0.0 if u < 0.15 else 1.0 if u < 0.3 else float(np.round(rng.random(), 3))
+        out.append(dict(dtype=dt, N=N, V=V, beta=beta,
+                        temperature=float(rng.choice([0.5, 1.0, 1.7, 3.0])),
+                        scale_t2=bool(rng.random() < 0.5),
+                        reduction=str(rng.choice(["none", "sum", "mean"])),
+                        mask=bool(rng.random() < 0.5), seed=2000 + i))
+    return out
+
+
+LOSS_CONFIGS = _loss_configs()
+
+
+@pytest.mark.parametrize("c", LOSS_CONFIGS, ids=[
+    f"{str(c['dtype'])[6:]}-N{c['N']}-V{c['V']}-b{c['beta']:g}-T{c['temperature']:g}"
+    f"{'-t2' if c['scale_t2'] else ''}-{c['reduction']}{'-mask' if c['mask'] else ''}"
+    for c in LOSS_CONFIGS])
+def test_random_loss_config(c):
+    """The distillation loss form (vjsd_loss_forward_backward against the loss forward
+    and backward calls, and against oracle.jsd_loss)."""
+    N, V = c["N"], c["V"]
+    b = synth.draw("full_vocab", device="cuda", N=N, V=V, dtype=c["dtype"], seed=c["seed"])
+    gen = torch.Generator(device="cuda").manual_seed(c["seed"])
+    opts = dict(temperature=c["temperature"], scale_t2=c["scale_t2"],
+                reduction=c["reduction"])
+    if c["mask"]:
+        opts["mask"] = (torch.rand(N, generator=gen, device="cuda") > 0.3).to(torch.uint8)
+    if c["reduction"] == "none":
+        grad = torch.rand(N, generator=gen, device="cuda") + 0.5
+    else:
+        grad = torch.tensor([0.75], device="cuda")
+    one = run(b.s, b.t, c["beta"], None, fused=True, opts=opts, grad=grad)
+    two = run(b.s, b.t, c["beta"], None, fused=False, opts=opts, grad=grad)
+    assert_same(one, two)
+    mask = opts.get("mask")
+    ref = oracle.jsd_loss(b.s.cpu(), b.t.cpu(), c["beta"], temperature=c["temperature"],
+                          scale_t2=c["scale_t2"],
+                          mask=None if mask is None else mask.cpu().numpy(),
+                          reduction=c["reduction"],
+                          grad=grad.cpu().double().numpy() if grad.numel() > 1
+                          else float(grad.item()))
+    assert_values(one["loss"].cpu(), ref["rows"], b.s.dtype, "rows")
+    scale = max(1.0, 1.0 / c["temperature"])
+    assert_grads(one["gs"].cpu(), ref["gs"], b.s.dtype, "d/ds", scale=scale)
+    assert_grads(one["gt"].cpu(), ref["gt"], b.s.dtype, "d/dt", scale=scale)
