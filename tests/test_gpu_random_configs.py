@@ -5,7 +5,9 @@ are wanted, tokens masked on both sides, undefined rows and zero upstream gradie
 Each configuration runs the one call (vjsd_forward_backward) and the two calls
 (vjsd_forward + vjsd_bwd) on the same inputs: every output bit-identical, and sampled
 rows (first and last included) against the fp64 oracle.  The distillation-loss form
-(temperature, T^2, token mask, reduction) is drawn the same way.  The configurations
+(temperature, T^2, token mask, reduction) is drawn the same way, and so are the sibling
+ops (KL both ways, entropy, log-probabilities, teacher top-k KL, cross-entropy) against
+the oracle alone.  The configurations
 are drawn once, from a fixed seed, so the list and its test names do not change between
 runs."""
 import numpy as np
@@ -14,6 +16,9 @@ import torch
 
 import oracle
 import synth
+import test_gpu_ce
+import test_gpu_siblings as sib
+import test_gpu_topk
 from parity import assert_grads, assert_values
 from test_gpu_fwd_bwd import assert_same, check_oracle, check_two_calls, run
 
@@ -144,3 +149,69 @@ def test_random_loss_config(c):
     scale = max(1.0, 1.0 / c["temperature"])
     assert_grads(one["gs"].cpu(), ref["gs"], b.s.dtype, "d/ds", scale=scale)
     assert_grads(one["gt"].cpu(), ref["gt"], b.s.dtype, "d/dt", scale=scale)
+
+
+SIBLING_OPS = ["kl", "reverse_kl", "entropy", "logprobs", "topk_kl", "cross_entropy"]
+
+
+def _sibling_configs(n=24, seed=20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dt = DTYPES[i % 3]
+        op = SIBLING_OPS[(i // 3) % len(SIBLING_OPS)]
+        V = int(rng.choice([int(rng.integers(64, 4096)), int(rng.integers(4096, 140000))]))
+        N = int(rng.integers(2, max(3, min(25, 2_000_000 // V))))
+        off = int(rng.integers(0, 8))
+        S = 1 if rng.random() < 0.6 else int(rng.integers(2, 5))
+        widths = None
+        if S > 1:
+            cuts = np.sort(rng.choice(np.arange(1, V), size=S - 1, replace=False))
+            widths = [int(w) for w in np.diff(np.concatenate([[0], cuts, [V]]))]
+        out.append(dict(op=op, dtype=dt, N=N, V=V, off=off, widths=widths,
+                        K=int(rng.integers(1, 9)),
+                        red=str(rng.choice(["none", "sum", "mean"])), seed=3000 + i))
+    return out
+
+
+SIBLING_CONFIGS = _sibling_configs()
+
+
+@pytest.mark.parametrize("c", SIBLING_CONFIGS, ids=[
+    f"{c['op']}-{str(c['dtype'])[6:]}-N{c['N']}-V{c['V']}-o{c['off']}"
+    f"{'' if c['widths'] is None else '-S%d' % len(c['widths'])}" for c in SIBLING_CONFIGS])
+def test_random_sibling_config(c):
+    """The sibling ops through the C ABI (forward and backward) against the fp64 oracle,
+    on seeded random shapes, offsets and shard splits."""
+    N, V, off, widths = c["N"], c["V"], c["off"], c["widths"]
+    b = synth.draw("full_vocab", device="cuda", N=N, V=V + off, dtype=c["dtype"],
+                   seed=c["seed"])
+    s, t = b.s[:, off:off + V], b.t[:, off:off + V]
+    gen = torch.Generator(device="cuda").manual_seed(c["seed"])
+    op = c["op"]
+    if op in ("kl", "reverse_kl"):
+        gout = torch.rand(N, generator=gen, device="cuda") + 0.5
+        sib.check_kl(s, t, op == "reverse_kl", widths=widths, gout=gout, want_t=True)
+    elif op == "entropy":
+        gout = torch.rand(N, generator=gen, device="cuda") + 0.5
+        g = sib.run_entropy(s, widths, gout)
+        ref = oracle.entropy(s.cpu(), widths=widths, gout=gout.cpu().double().numpy())
+        assert_values(g["ent"], ref["ent"], s.dtype, "entropy")
+        assert_grads(g["gx"], ref["gx"], s.dtype, "d/dx")
+    elif op == "logprobs":
+        K = c["K"]
+        ids = torch.randint(0, V, (N, K), generator=gen, device="cuda")
+        ids[torch.rand((N, K), generator=gen, device="cuda") < 0.15] = -100
+        gout = torch.rand((N, K), generator=gen, device="cuda") + 0.5
+        g = sib.run_logprobs(s, ids, -100, widths, gout)
+        assert g["err"] == 0
+        ref = oracle.logprobs(s.cpu(), ids.cpu().numpy(), -100, widths=widths,
+                              gout=gout.cpu().double().numpy())
+        assert_values(g["out"], ref["out"], s.dtype, "logprobs")
+        assert_grads(g["gx"], ref["gx"], s.dtype, "d/dx")
+    elif op == "topk_kl":
+        ids, tl = test_gpu_topk.teacher_topk(t, min(c["K"], V), c["seed"])
+        test_gpu_topk.check(s, ids, tl, widths=widths, seed=c["seed"])
+    else:
+        labels = test_gpu_ce.labels_for(N, V, c["seed"])
+        test_gpu_ce.check(s, labels, c["red"], widths=widths, seed=c["seed"])
