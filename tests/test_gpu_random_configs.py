@@ -7,9 +7,9 @@ Each configuration runs the one call (vjsd_forward_backward) and the two calls
 rows (first and last included) against the fp64 oracle.  The distillation-loss form
 (temperature, T^2, token mask, reduction) is drawn the same way, and so are the sibling
 ops (KL both ways, entropy, log-probabilities, teacher top-k KL, cross-entropy) against
-the oracle alone.  The configurations
-are drawn once, from a fixed seed, so the list and its test names do not change between
-runs."""
+the oracle alone, and the fused-linear loss's GEMM against an fp64 product.  The
+configurations are drawn once, from a fixed seed, so the list and its test names do not
+change between runs."""
 import numpy as np
 import pytest
 import torch
@@ -17,6 +17,7 @@ import torch
 import oracle
 import synth
 import test_gpu_ce
+import test_gpu_linear
 import test_gpu_siblings as sib
 import test_gpu_topk
 from parity import assert_grads, assert_values
@@ -215,3 +216,33 @@ def test_random_sibling_config(c):
     else:
         labels = test_gpu_ce.labels_for(N, V, c["seed"])
         test_gpu_ce.check(s, labels, c["red"], widths=widths, seed=c["seed"])
+
+
+def _gemm_configs(n=30, seed=20261206):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, N = (int(x) for x in rng.integers(1, 600, size=2))
+        K = int(64 * rng.integers(1, 12)) if rng.random() < 0.4 else int(rng.integers(0, 700))
+        a_f32, a_km, b_km = (int(x) for x in rng.integers(0, 2, size=3))
+        if rng.random() < 0.3:  # the direct-to-LDS kernel's layout
+            a_f32, a_km, b_km = 0, 1, 1
+        out.append(dict(M=M, N=N, K=K, a_f32=a_f32, a_km=a_km, b_km=b_km,
+                        out=str(rng.choice(["f32", "f32_acc", "bf16"])),
+                        pad=int(rng.integers(0, 3)), seed=4000 + i))
+    return out
+
+
+GEMM_CONFIGS = _gemm_configs()
+
+
+@pytest.mark.parametrize("c", GEMM_CONFIGS, ids=[
+    f"M{c['M']}-N{c['N']}-K{c['K']}-a{'f32' if c['a_f32'] else 'bf16'}"
+    f"{'k' if c['a_km'] else 'r'}-b{'k' if c['b_km'] else 'r'}-{c['out']}-p{c['pad']}"
+    for c in GEMM_CONFIGS])
+def test_random_gemm_config(c):
+    """The fused-linear loss's GEMM (vlin_gemm) on seeded random shapes, operand layouts,
+    padded leading dimensions and output modes, against an fp64 product of the same
+    bf16 operands within the accumulation bound."""
+    test_gpu_linear.gemm_case(c["M"], c["N"], c["K"], c["a_f32"], c["a_km"], c["b_km"],
+                              c["out"], seed=c["seed"], pad=c["pad"])
