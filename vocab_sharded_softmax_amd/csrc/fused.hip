@@ -324,9 +324,7 @@ constexpr int TW_U = 4;  // 16-byte vectors per lane per input in flight in a sw
 template <class D>
 constexpr int held_steps() { return sizeof(typename D::T) == 4 ? 4 : 1; }
 template <class D>
-constexpr int lds_steps() {
-    return sizeof(typename D::T) == 4 ? 2 : 1;
-}
+constexpr int lds_steps() { return sizeof(typename D::T) == 4 ? 2 : 1; }
 
 // The streamed part of k_fwd_twice's divergence sweep, continuing the sums `acc`
 // (t, s) of the held steps.  It runs backwards, from the row's end, where the statistics
@@ -413,7 +411,9 @@ __device__ __forceinline__ TwiceSpan twice_span(int64_t w, int64_t h) {
     const int64_t nfull = h < w ? (w - h) / VEC / STEP : 0;
     sp.hold = nfull >= HOLD + (LHOLD > 0 ? 1 : 0);
     // (a constant for one LDS step: the row then holds it whenever it holds at all)
-    sp.lh = LHOLD <= 1 ? LHOLD : sp.hold ? (int)(nfull - HOLD < LHOLD ? nfull - HOLD : LHOLD) : 0;
+    sp.lh = LHOLD <= 1 ? LHOLD
+            : sp.hold  ? (int)(nfull - HOLD < LHOLD ? nfull - HOLD : LHOLD)
+                       : 0;
     sp.P = sp.hold ? h + (nfull - HOLD - sp.lh) * STEP * VEC : w;
     sp.PR = sp.P + sp.lh * STEP * VEC;
     sp.Q = sp.hold ? sp.PR + HOLD * STEP * VEC : w;
@@ -421,7 +421,8 @@ __device__ __forceinline__ TwiceSpan twice_span(int64_t w, int64_t h) {
 }
 // The held steps: LDS (each lane's own vectors) and registers.
 template <class D>
-using LdsStep = u32x4[lds_steps<D>() ? lds_steps<D>() : 1][2][TW_U][lds_steps<D>() ? TWICE_BLK : 1];
+using LdsStep =
+    u32x4[lds_steps<D>() ? lds_steps<D>() : 1][2][TW_U][lds_steps<D>() ? TWICE_BLK : 1];
 template <class D>
 using HeldRegs = u32x4[held_steps<D>()][TW_U];
 
