@@ -920,9 +920,15 @@ __global__ __launch_bounds__(TWICE_BLK) void k_fwd_shards(ShardRows sr, double b
         }
         // this wave's pair for the shard; the waves are combined after the last shard,
         // behind one barrier for all shards
-        const MZ ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
-        const MZ wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
-        const float ns = wave_min(o1.a.mn), nt = wave_min(o1.b.mn);
+        // (an empty shard's pair is the identity, exactly what its reductions give)
+        MZ ws{NINF, 0.0f}, wt{NINF, 0.0f};
+        float ns = __builtin_huge_valf(), nt = __builtin_huge_valf();
+        if (w > 0) {
+            ws = wave_mz(MZ{o1.a.m, o1.a.z}, o.ks);
+            wt = wave_mz(MZ{o1.b.m, o1.b.z}, o.ks);
+            ns = wave_min(o1.a.mn);
+            nt = wave_min(o1.b.mn);
+        }
         if (lane == 0) {
             float *d = wp[q][wave];
             d[0] = ws.m;
