@@ -333,7 +333,14 @@ constexpr int lds_steps() { return sizeof(typename D::T) == 4 ? 2 : 1; }
 // Measured on MI355X against the forward order, three alternating runs: 4096 x 151936
 // fp16 forward and backward in one launch 1.431-1.440 -> 1.398-1.408 ms; bf16 at 8192 x
 // 151936 and fp32 at 4096 x 128256 unchanged.
-template <class D, bool SAFE>
+// STREAM: the nontemporal load policy, for a forward whose row is not read again.  The
+// one-launch kernel reads the row a third time, for the gradients, and loads this
+// sweep with the default policy, which keeps the columns in the caches for that
+// sweep: forward and backward in one launch (three alternating runs on one box) at
+// 8192 x 151936 bf16 2.771-2.802 -> 2.699-2.724 ms, at 4096 x 151936 fp16 1.340-1.351
+// -> 1.279-1.285 ms, at 4096 x 128256 fp32 2.255-2.257 -> 1.975-2.008 ms; the same
+// policy in the forward alone made it 3-8 % slower.
+template <class D, bool SAFE, bool STREAM = true>
 __device__ __forceinline__ void twice_stream(const MixRow &mx, float beta, float ks, bool hold,
                                              const typename D::T *s, const typename D::T *t,
                                              int64_t w, int64_t h, int64_t P, int64_t Q,
@@ -343,10 +350,10 @@ __device__ __forceinline__ void twice_stream(const MixRow &mx, float beta, float
     op.at[0] = acc[0];
     op.as[0] = acc[1];
     if (hold) {
-        sweep_rev<D, TW_U, true, TWICE_BLK, true>(s + Q, t + Q, w - Q, 0, op);
-        sweep_rev<D, TW_U, true, TWICE_BLK, true>(s, t, P, h, op);
+        sweep_rev<D, TW_U, true, TWICE_BLK, STREAM>(s + Q, t + Q, w - Q, 0, op);
+        sweep_rev<D, TW_U, true, TWICE_BLK, STREAM>(s, t, P, h, op);
     } else {
-        sweep_rev<D, TW_U, true, TWICE_BLK, true>(s, t, w, h, op);
+        sweep_rev<D, TW_U, true, TWICE_BLK, STREAM>(s, t, w, h, op);
     }
     acc[0] = op.sum_t();
     acc[1] = op.sum_s();
@@ -430,7 +437,8 @@ using HeldRegs = u32x4[held_steps<D>()][TW_U];
 // k_fwdbwd_twice: the statistics sweep, keeping the span sp on chip, the row's
 // constants (into rk), then the divergence sweep.  Thread 0 writes the row's
 // statistics (st), KL pair (klr) and loss; the held steps stay in lds_step / hs / ht.
-template <class D>
+// STREAM: the divergence sweep's load policy (twice_stream).
+template <class D, bool STREAM = true>
 __device__ __forceinline__ void twice_forward(const typename D::T *s, const typename D::T *t,
                                               int64_t w, const TwiceSpan &sp, double beta,
                                               double *st, float *klr, float *lossr,
@@ -539,9 +547,9 @@ __device__ __forceinline__ void twice_forward(const typename D::T *s, const type
             v[1] = oh.sum_s();
         }
         if (RANGE && k.fast)
-            twice_stream<D, false>(k.mx, (float)beta, o.ks, hold, s, t, w, h, P, Q, v);
+            twice_stream<D, false, STREAM>(k.mx, (float)beta, o.ks, hold, s, t, w, h, P, Q, v);
         else
-            twice_stream<D, true>(k.mx, (float)beta, o.ks, hold, s, t, w, h, P, Q, v);
+            twice_stream<D, true, STREAM>(k.mx, (float)beta, o.ks, hold, s, t, w, h, P, Q, v);
     }
     block_sum<2, TWICE_BLK>(v, red);
     if (threadIdx.x == 0) finish_row(k, beta, v[0], v[1], klr, lossr, o.lscale);
@@ -736,8 +744,9 @@ void k_fwdbwd_twice(RowView sv, RowView tv, RowMView gsv, RowMView gtv, int64_t 
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
     const TwiceSpan sp = twice_span<D>(w, head_len<T>(w, s, t));
     HeldRegs<D> hs, ht;
-    twice_forward<D>(s, t, w, sp, beta, stats + r * 4, kl + 2 * r, loss + r, o, red, rk, lds_step,
-                     hs, ht);
+    // (the divergence sweep with the default load policy: the gradients read the row again)
+    twice_forward<D, false>(s, t, w, sp, beta, stats + r * 4, kl + 2 * r, loss + r, o, red, rk,
+                            lds_step, hs, ht);
     if (threadIdx.x == 0) fused_bwd_constants(stats, kl, r, beta, grad, go, rc);
     __syncthreads();
     if (rc[ROWC_UNDEFINED] != 0.0f) {  // no distribution: exactly zero gradients
