@@ -949,7 +949,20 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
             sh.gt = {nullptr, 0, 0, 0};
             vjsd::RowOpts rb = ro;
             rb.mask = ro.mask ? ro.mask + n0 : nullptr;
-            if (mode != vjsd::INTERIOR) {
+            // the logit gradient (bf16) for a unit upstream gradient of out[0]
+            vjsd::GradOpts go;
+            go.ks = ro.ks;
+            go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
+            go.scalar = true;
+            go.mask = rb.mask;
+            go.count = mean ? count : nullptr;
+            if (grads && mode == vjsd::INTERIOR && !rb.mask) {
+                // forward and G in one launch: the block's gradient sweep re-reads what the
+                // divergence sweep left in the caches
+                if ((e = hip_status(vjsd::launch_fwd_bwd_f32_bf16(sh, nb, beta, stats, kl,
+                                                                  rows_out + n0, st, rb, go))))
+                    return e;
+            } else if (mode != vjsd::INTERIOR) {
                 const int rev = mode == vjsd::REV_KL;
                 if ((e = hip_status(vjsd::launch_kl1(VJSD_F32, rev, sh, nb, part_of(part, 0, nb),
                                                      st, rb))))
@@ -962,17 +975,13 @@ int vljsd(const vlin_head *student, const vlin_head *teacher, int64_t N, int64_t
                 return e;
             }
             if (!grads) continue;
-            // the block's logit gradient (bf16) for a unit upstream gradient of out[0]
-            vjsd::GradOpts go;
-            go.ks = ro.ks;
-            go.gmul = (c.t2 ? c.T * c.T : 1.0) / c.T;
-            go.scalar = true;
-            go.mask = rb.mask;
-            go.count = mean ? count : nullptr;
-            if ((e = hip_status(vjsd::launch_bwd_prep(mode, nb, stats, kl, beta, nullptr, part, st,
-                                                      go))))
-                return e;
-            if ((e = hip_status(vjsd::launch_bwd_f32_to_bf16(mode, sh, nb, part, st)))) return e;
+            if (mode != vjsd::INTERIOR || rb.mask) {
+                if ((e = hip_status(vjsd::launch_bwd_prep(mode, nb, stats, kl, beta, nullptr,
+                                                          part, st, go))))
+                    return e;
+                if ((e = hip_status(vjsd::launch_bwd_f32_to_bf16(mode, sh, nb, part, st))))
+                    return e;
+            }
             if (grad_h) {  // G [nb][V] x (w_s^T)^T: both operands k-major
                 vjsd::GemmArgs g;
                 g.M = nb;

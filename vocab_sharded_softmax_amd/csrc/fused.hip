@@ -718,13 +718,16 @@ void k_fwdbwd_row(RowView sv, RowView tv, RowMView gsv,
 // Measured on MI355X at 8192 x 151936 bf16, both gradients: 2.73-2.75 ms against
 // 2.83-2.87 ms for the forward and backward launches.
 
-template <class D, bool WS, bool WT>
+// DG: the gradients' storage, the input's or bf16 for fp32 input (the fused-linear
+// loss's logit gradient; its rows at the inputs' element offsets).
+template <class D, bool WS, bool WT, class DG = D>
 __global__ __launch_bounds__(TWICE_BLK)
 __attribute__((amdgpu_waves_per_eu(fb_waves<D>(), fb_waves<D>())))
 void k_fwdbwd_twice(RowView sv, RowView tv, RowMView gsv, RowMView gtv, int64_t w, double beta,
                     const float *__restrict__ grad, double *stats, float *kl,
                     float *__restrict__ loss, RowOpts o, GradOpts go) {
     using T = typename D::T;
+    using TG = typename DG::T;
     constexpr int VEC = D::VEC;
     constexpr int64_t STEP = (int64_t)TW_U * TWICE_BLK;  // vectors per input per sweep step
     constexpr int HOLD = held_steps<D>(), LHOLD = lds_steps<D>();
@@ -734,11 +737,11 @@ void k_fwdbwd_twice(RowView sv, RowView tv, RowMView gsv, RowMView gtv, int64_t 
     __shared__ LdsStep<D> lds_step;
     __shared__ float rc[ROWC];
     const int64_t r = blockIdx.x;
-    T *gs = WS ? row_ptr<T>(gsv, r) : nullptr;
-    T *gt = WT ? row_ptr<T>(gtv, r) : nullptr;
+    TG *gs = WS ? row_ptr<TG>(gsv, r) : nullptr;
+    TG *gt = WT ? row_ptr<TG>(gtv, r) : nullptr;
     if (row_dropped(o, r)) {
         dropped_row(stats + r * 4, kl + 2 * r, loss + r);
-        zero_grads<D, TWICE_BLK, WS, WT>(gs, gt, w);
+        zero_grads<DG, TWICE_BLK, WS, WT>(gs, gt, w);
         return;
     }
     const T *s = row_ptr<T>(sv, r), *t = row_ptr<T>(tv, r);
@@ -750,14 +753,15 @@ void k_fwdbwd_twice(RowView sv, RowView tv, RowMView gsv, RowMView gtv, int64_t 
     if (threadIdx.x == 0) fused_bwd_constants(stats, kl, r, beta, grad, go, rc);
     __syncthreads();
     if (rc[ROWC_UNDEFINED] != 0.0f) {  // no distribution: exactly zero gradients
-        zero_grads<D, TWICE_BLK, WS, WT>(gs, gt, w);
+        zero_grads<DG, TWICE_BLK, WS, WT>(gs, gt, w);
         return;
     }
-    OpBwd<D, INTERIOR, WS, WT> op;
+    OpBwd<D, INTERIOR, WS, WT, DG> op;
     op.gs = gs;
     op.gt = gt;
     op.set(rc);
-    const int64_t hg = head_len<T>(w, s, t, gs, gt);
+    // (a bf16 gradient of fp32 input: the inputs alone fix the head, as in k_bwd)
+    const int64_t hg = std::is_same<D, DG>::value ? head_len<T>(w, s, t, gs, gt) : sp.h;
     if (!sp.hold || hg != sp.h) {
         sweep<D, U, true, TWICE_BLK, true>(s, t, w, hg, op);
         return;
@@ -1162,6 +1166,16 @@ hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, 
         case 1: return fused_launch<F16>(sh, N, beta, stats, kl, loss, st, o);
         default: return fused_launch<BF16>(sh, N, beta, stats, kl, loss, st, o);
     }
+}
+
+hipError_t launch_fwd_bwd_f32_bf16(const Shard &sh, int64_t N, double beta, double *stats,
+                                   float *kl, float *loss, hipStream_t st, const RowOpts &o,
+                                   const GradOpts &go) {
+    if (sh.gs.p == nullptr || sh.gt.p != nullptr) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_fwdbwd_twice<F32, true, false, BF16>), dim3((unsigned)N),
+                       dim3(TWICE_BLK), 0, st, sh.s, sh.t, sh.gs, sh.gt, sh.width, beta,
+                       (const float *)nullptr, stats, kl, loss, o, go);
+    return hipGetLastError();
 }
 
 hipError_t launch_fwd_bwd_fused(int dtype, const Shard &sh, int64_t N, double beta,

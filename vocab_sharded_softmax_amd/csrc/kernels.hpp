@@ -43,6 +43,13 @@ hipError_t launch_fwd_fused(int dtype, const Shard &sh, int64_t N, double beta, 
 hipError_t launch_fwd_bwd_fused(int dtype, const Shard &sh, int64_t N, double beta,
                                 const float *grad, double *stats, float *kl, float *loss,
                                 hipStream_t st, const RowOpts &o, const GradOpts &go);
+// The same for fp32 rows and their student gradient stored in bf16 (sh.gs; sh.gt NULL),
+// always the two-sweep kernel, with a unit upstream gradient under go: the fused-linear
+// loss's logit block and its gradient G in one launch.  The gradient rows sit at the
+// inputs' element offsets.
+hipError_t launch_fwd_bwd_f32_bf16(const Shard &sh, int64_t N, double beta, double *stats,
+                                   float *kl, float *loss, hipStream_t st, const RowOpts &o,
+                                   const GradOpts &go);
 // interior JSD forward of 2..FUSED_SHARDS shards in one launch (stats, merge, divergence)
 constexpr int FUSED_SHARDS = 8;
 struct ShardRows {
