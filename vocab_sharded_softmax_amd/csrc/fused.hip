@@ -612,9 +612,11 @@ __device__ __forceinline__ void zero_grads(typename D::T *gs, typename D::T *gt,
 //     with two or four, or with the next vector's loads issued before the current
 //     one's arithmetic).  8192 x 151936 bf16: 2.83-2.87 -> 2.73-2.75 ms; 4096 x 151936
 //     fp16: 1.45-1.46 -> 1.41-1.43 ms (1.32-1.33 ms after the backward divergence
-//     sweep and the fp16 LDS step); 4096 x 128256 fp32: 2.27-2.29 -> 2.25 ms with two
-//     held LDS steps, where the backward part runs at one workgroup per CU (reading the
-//     four register steps again instead of keeping them: 2.38-2.44 ms)
+//     sweep and the fp16 LDS step, 1.27-1.28 ms with the default load policy in the
+//     divergence sweep); 4096 x 128256 fp32: 2.27-2.29 -> 2.25 ms with two held LDS
+//     steps, where the backward part runs at one workgroup per CU (reading the four
+//     register steps again instead of keeping them: 2.38-2.44 ms), 1.94-1.95 ms with
+//     the default load policy in the divergence sweep
 //   512-lane register rows: held to 128 VGPRs, two workgroups per CU (1024 x 37984
 //     bf16, student gradient: 0.0916 ms at 134 VGPRs and one workgroup per CU, 0.0815
 //     ms with a 20-byte spill; the two calls 0.092-0.096 ms); 8192 x 16032 bf16 (256
